@@ -1,0 +1,208 @@
+"""Python binding of libwushkv, the MI355X (gfx950) WUSH-KV online path.
+
+Argument marshalling only: torch provides device memory and the stream, and
+every step of the path (append, flush with the key transform and quantization,
+query transform, split-K GQA decode with its merge) runs in the library's HIP
+kernels through the C ABI declared in include/wushkv.h.  There is no CPU
+fallback: without the built library every call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwushkv.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_ALIGN, ERR_HIP = range(8)
+DT_F32, DT_BF16, DT_F16 = 0, 1, 2
+Q_QUEST, Q_AFFINE = 0, 1
+PLANES = ("sink_k", "sink_v", "ring_k", "ring_v", "codes_k", "codes_v", "par_k", "par_v")
+EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "wushkv_plane_bytes",
+           "wushkv_decode_num_splits", "wushkv_decode_workspace_bytes", "wushkv_append_flush",
+           "wushkv_query_transform", "wushkv_decode_attention")
+
+
+class WushKVError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of wushkv_cache (include/wushkv.h)."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("sink", ctypes.c_int32), ("recent", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("capacity", ctypes.c_int64),
+        ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32),
+        ("quant_k", ctypes.c_int32), ("quant_v", ctypes.c_int32),
+        ("clip_mult", ctypes.c_float), ("pct_lo", ctypes.c_float), ("pct_hi", ctypes.c_float),
+    ] + [(p, ctypes.c_void_p) for p in PLANES]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libwushkv (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_kv_cache_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(CacheDesc)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sig = {
+            "wushkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "wushkv_abi_version": (ctypes.c_int, []),
+            "wushkv_cache_check": (ctypes.c_int, [P]),
+            "wushkv_plane_bytes": (sz, [P, ctypes.c_int]),
+            "wushkv_decode_num_splits": (i32, [P, i64, i32, i32]),
+            "wushkv_decode_workspace_bytes": (sz, [P, i64, i32, i32]),
+            "wushkv_append_flush": (ctypes.c_int, [P, i64, i32, vp, vp, i32, vp, vp]),
+            "wushkv_query_transform": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+            "wushkv_decode_attention": (ctypes.c_int, [P, i64, vp, i32, vp, i32, i32, vp, sz, vp, vp]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().wushkv_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != OK:
+        raise WushKVError(status, what)
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}[t.dtype]
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libwushkv must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class CacheSpec:
+    batch: int
+    num_kv_heads: int
+    head_dim: int
+    capacity: int
+    sink: int = 64
+    recent: int = 256
+    chunk: int = 8
+    bits_k: int = 2
+    bits_v: int = 2
+    quant_k: int = Q_QUEST
+    quant_v: int = Q_QUEST
+    clip_mult: float = 2.5
+    pct_lo: float = 0.5
+    pct_hi: float = 99.5
+
+    def desc(self, planes=None):
+        d = CacheDesc(self.batch, self.num_kv_heads, self.head_dim, self.sink, self.recent, self.chunk,
+                      self.capacity, self.bits_k, self.bits_v, self.quant_k, self.quant_v,
+                      self.clip_mult, self.pct_lo, self.pct_hi)
+        if planes:
+            for p in PLANES:
+                setattr(d, p, planes[p].data_ptr())
+        return d
+
+    def plane_bytes(self):
+        d = self.desc()
+        out = {p: int(lib().wushkv_plane_bytes(ctypes.byref(d), i)) for i, p in enumerate(PLANES)}
+        if any(v == 0 and not p.startswith("sink") for p, v in out.items()):
+            _check(lib().wushkv_cache_check(ctypes.byref(d)), "cache descriptor")
+        return out
+
+
+class KVCache:
+    """Caller-owned cache planes (torch device memory) plus the token count."""
+
+    def __init__(self, spec: CacheSpec, device="cuda"):
+        import torch
+        self.spec = spec
+        self.planes = {p: torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+                       for p, n in spec.plane_bytes().items()}
+        self.desc = spec.desc(self.planes)
+        self.n = 0
+
+    def view(self, plane, dtype=None):
+        import torch
+        t = self.planes[plane]
+        return t.view(dtype) if dtype is not None else t
+
+    def snapshot(self):
+        return {p: t.clone() for p, t in self.planes.items()}, self.n
+
+    def restore(self, snap):
+        planes, n = snap
+        for p, t in planes.items():
+            self.planes[p].copy_(t)
+        self.n = n
+
+
+def append_flush(cache: KVCache, k_new, v_new, t_k16, n_before=None, stream=None):
+    """Append [B, Hkv, n_new, d] keys/values (f32/bf16/f16) and run due flushes."""
+    import torch
+    n_before = cache.n if n_before is None else n_before
+    n_new = k_new.shape[2]
+    if k_new.dtype != v_new.dtype or t_k16.dtype != torch.float16:
+        raise ValueError("k_new/v_new must share a dtype and t_k16 must be float16")
+    _check(lib().wushkv_append_flush(ctypes.byref(cache.desc), n_before, n_new, _ptr(k_new), _ptr(v_new),
+                                     _dtype_code(k_new), _ptr(t_k16), _stream(stream)), "append_flush")
+    cache.n = n_before + n_new
+
+
+def query_transform(t_inv_t, q, num_kv_heads, out=None, stream=None):
+    """q~ = T^{-T} q: t_inv_t fp32 [Hkv, d, d], q [B, Hq, d] -> fp32 [B, Hq, d]."""
+    import torch
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_query_transform(_ptr(t_inv_t), _ptr(q), _dtype_code(q), B, Hq, num_kv_heads, d,
+                                        _ptr(out), _stream(stream)), "query_transform")
+    return out
+
+
+def decode_num_splits(cache: KVCache, n_tokens, num_q_heads, num_splits=0):
+    return int(lib().wushkv_decode_num_splits(ctypes.byref(cache.desc), n_tokens, num_q_heads, num_splits))
+
+
+def decode_workspace(cache: KVCache, n_tokens, num_q_heads, num_splits=0):
+    """A zero-filled workspace large enough for this decode (counters start at zero)."""
+    import torch
+    n = lib().wushkv_decode_workspace_bytes(ctypes.byref(cache.desc), n_tokens, num_q_heads, num_splits)
+    if n == 0:
+        raise WushKVError(ERR_SHAPE, "decode_workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=cache.planes["sink_k"].device)
+
+
+def decode_attention(cache: KVCache, q, q_t, n_tokens=None, num_splits=0, workspace=None, out=None, stream=None):
+    """GQA decode over the cache's first n_tokens tokens -> fp32 [B, Hq, d]."""
+    import torch
+    n_tokens = cache.n if n_tokens is None else n_tokens
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(cache, n_tokens, Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention(ctypes.byref(cache.desc), n_tokens, _ptr(q), _dtype_code(q), _ptr(q_t),
+                                         Hq, num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
+                                         _stream(stream)), "decode_attention")
+    return out

@@ -1,0 +1,271 @@
+// Host side of libwushkv: argument validation, plane geometry and dispatch of the
+// gfx950 kernels.  Every check runs before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "wushkv_internal.h"
+
+using namespace wushkv;
+
+namespace {
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+int check_dtype(int dt) { return (dt == WUSHKV_DT_F32 || dt == WUSHKV_DT_BF16 || dt == WUSHKV_DT_F16); }
+
+size_t dtype_size(int dt) { return dt == WUSHKV_DT_F32 ? 4 : 2; }
+
+// Order statistics needed for the linear-interpolation percentile at pct.
+void pct_index(int d, double pct, int *i, float *t) {
+  double h = (d - 1) * (pct / 100.0);
+  int fi = (int)floor(h);
+  if (fi >= d - 1) { *i = d - 1; *t = 0.0f; return; }
+  *i = fi;
+  *t = (float)(h - fi);
+}
+
+}  // namespace
+
+namespace wushkv {
+
+int make_geom(const wushkv_cache *c, Geom *g) {
+  if (!c) return WUSHKV_ERR_NULL;
+  if (c->batch < 1 || c->num_kv_heads < 1) return WUSHKV_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return WUSHKV_ERR_SHAPE;
+  if (c->sink < 0 || c->recent < 0 || c->chunk < 1 || c->recent % c->chunk != 0) return WUSHKV_ERR_SHAPE;
+  if (c->capacity < 1 || c->capacity > ((int64_t)1 << 40)) return WUSHKV_ERR_SHAPE;
+  for (int b : {c->bits_k, c->bits_v})
+    if (b < 2 || b > 4) return WUSHKV_ERR_SHAPE;
+  for (int q : {c->quant_k, c->quant_v})
+    if (q != WUSHKV_Q_QUEST && q != WUSHKV_Q_AFFINE_PCT) return WUSHKV_ERR_SHAPE;
+  bool any_quest = c->quant_k == WUSHKV_Q_QUEST || c->quant_v == WUSHKV_Q_QUEST;
+  bool any_aff = c->quant_k == WUSHKV_Q_AFFINE_PCT || c->quant_v == WUSHKV_Q_AFFINE_PCT;
+  if (any_quest && !(c->clip_mult > 0.0f && isfinite(c->clip_mult))) return WUSHKV_ERR_SHAPE;
+  if (any_aff && !(c->pct_lo >= 0.0f && c->pct_hi <= 100.0f && c->pct_lo < c->pct_hi)) return WUSHKV_ERR_SHAPE;
+  if (c->batch > 65535 || c->num_kv_heads > 4096) return WUSHKV_ERR_SHAPE;
+
+  Geom &G = *g;
+  G.B = c->batch; G.Hkv = c->num_kv_heads; G.d = c->head_dim;
+  G.S = c->sink; G.R = c->recent; G.C = c->chunk;
+  G.cap = c->capacity;
+  int64_t body = c->capacity - c->sink;
+  if (body < 0) body = 0;
+  G.body_cap = (body + kSet - 1) / kSet * kSet;
+  G.bits_k = c->bits_k; G.bits_v = c->bits_v;
+  G.quant_k = c->quant_k; G.quant_v = c->quant_v;
+  G.clip = c->clip_mult;
+  G.lo_i = G.hi_i = 0; G.lo_t = G.hi_t = 0.0f; G.need_lo = G.need_hi = 0;
+  if (any_aff) {
+    pct_index(G.d, c->pct_lo, &G.lo_i, &G.lo_t);
+    pct_index(G.d, c->pct_hi, &G.hi_i, &G.hi_t);
+    G.need_lo = (G.lo_i + 2 < G.d) ? G.lo_i + 2 : G.d;
+    G.need_hi = G.d - G.hi_i;
+    if (G.need_lo > kMaxOrderStats || G.need_hi > kMaxOrderStats) return WUSHKV_ERR_UNSUPPORTED;
+  }
+  G.sink_bytes = (size_t)G.S * G.d * 2;
+  G.ring_bytes = (size_t)(G.R + G.C) * G.d * 2;
+  G.kcode_row = (size_t)G.d * G.bits_k / 8;
+  G.kcode_bytes = (size_t)G.body_cap * G.kcode_row;
+  G.vset_bytes = (size_t)kSet * G.d * G.bits_v / 8;
+  G.vcode_bytes = (size_t)(G.body_cap / kSet) * G.vset_bytes;
+  G.kpar_n = c->quant_k == WUSHKV_Q_QUEST ? 1 : 2;
+  G.vpar_n = c->quant_v == WUSHKV_Q_QUEST ? 1 : 2;
+  G.kpar_bytes = (size_t)G.body_cap * G.kpar_n * 2;
+  G.vpar_bytes = (size_t)G.body_cap * G.vpar_n * 2;
+  return WUSHKV_OK;
+}
+
+}  // namespace wushkv
+
+namespace {
+
+int check_planes(const wushkv_cache *c) {
+  const void *ps[] = {c->sink_k, c->sink_v, c->ring_k, c->ring_v, c->codes_k, c->codes_v, c->par_k, c->par_v};
+  for (const void *p : ps)
+    if (!p) return WUSHKV_ERR_NULL;
+  for (const void *p : ps)
+    if (misaligned(p)) return WUSHKV_ERR_ALIGN;
+  return WUSHKV_OK;
+}
+
+int hip_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? WUSHKV_OK : WUSHKV_ERR_HIP;
+}
+
+// Body partitions for a decode: the caller's count, or enough waves to fill the
+// chip (about 2048 resident waves) with at least one 64-token set each.
+int32_t choose_splits(const Geom &g, int64_t nq, int32_t requested) {
+  int64_t nsets = (nq + kSet - 1) / kSet;
+  if (requested > 0) {
+    return requested;
+  }
+  int64_t heads = (int64_t)g.B * g.Hkv;
+  int64_t want = (2048 + heads - 1) / heads;
+  if (want < 1) want = 1;
+  if (want > nsets) want = nsets > 0 ? nsets : 1;
+  if (want > 1024) want = 1024;
+  return (int32_t)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *wushkv_status_string(int s) {
+  switch (s) {
+    case WUSHKV_OK: return "ok";
+    case WUSHKV_ERR_NULL: return "null pointer";
+    case WUSHKV_ERR_SHAPE: return "invalid shape or option";
+    case WUSHKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case WUSHKV_ERR_CAPACITY: return "token count exceeds cache capacity";
+    case WUSHKV_ERR_WORKSPACE: return "decode workspace missing or too small";
+    case WUSHKV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case WUSHKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int wushkv_abi_version(void) { return WUSHKV_ABI_VERSION; }
+
+int wushkv_cache_check(const wushkv_cache *c) {
+  Geom g;
+  return make_geom(c, &g);
+}
+
+size_t wushkv_plane_bytes(const wushkv_cache *c, int plane) {
+  Geom g;
+  if (make_geom(c, &g) != WUSHKV_OK) return 0;
+  size_t heads = (size_t)g.B * g.Hkv;
+  switch (plane) {
+    case WUSHKV_PLANE_SINK_K: case WUSHKV_PLANE_SINK_V: return heads * g.sink_bytes;
+    case WUSHKV_PLANE_RING_K: case WUSHKV_PLANE_RING_V: return heads * g.ring_bytes;
+    case WUSHKV_PLANE_CODES_K: return heads * g.kcode_bytes;
+    case WUSHKV_PLANE_CODES_V: return heads * g.vcode_bytes;
+    case WUSHKV_PLANE_PAR_K: return heads * g.kpar_bytes;
+    case WUSHKV_PLANE_PAR_V: return heads * g.vpar_bytes;
+    default: return 0;
+  }
+}
+
+int32_t wushkv_decode_num_splits(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads, int32_t num_splits) {
+  Geom g;
+  if (make_geom(c, &g) != WUSHKV_OK) return 0;
+  if (n_tokens < 1 || n_tokens > g.cap || num_q_heads < 1 || num_q_heads % g.Hkv || num_splits < 0) return 0;
+  return choose_splits(g, n_quantized(n_tokens, g.S, g.R, g.C), num_splits);
+}
+
+size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads, int32_t num_splits) {
+  Geom g;
+  int32_t P = wushkv_decode_num_splits(c, n_tokens, num_q_heads, num_splits);
+  if (P <= 0 || make_geom(c, &g) != WUSHKV_OK) return 0;
+  size_t rows = (size_t)g.B * num_q_heads * (P + 1);
+  size_t bytes = rows * g.d * 4 + rows * 2 * 4;
+  bytes = (bytes + 255) / 256 * 256;
+  bytes += (size_t)g.B * g.Hkv * 4;
+  return (bytes + 255) / 256 * 256;
+}
+
+int wushkv_append_flush(const wushkv_cache *c, int64_t n_before, int32_t n_new, const void *k_new,
+                        const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
+  Geom g;
+  int st = make_geom(c, &g);
+  if (st != WUSHKV_OK) return st;
+  if (n_before < 0 || n_new < 0 || !check_dtype(in_dtype)) return WUSHKV_ERR_SHAPE;
+  if (n_before + n_new > g.cap) return WUSHKV_ERR_CAPACITY;
+  if ((st = check_planes(c)) != WUSHKV_OK) return st;
+  if (n_new == 0) return WUSHKV_OK;
+  if (!k_new || !v_new || !t_k_f16) return WUSHKV_ERR_NULL;
+  if (misaligned(k_new) || misaligned(v_new) || misaligned(t_k_f16)) return WUSHKV_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  int64_t n_after = n_before + n_new;
+  int64_t qb = n_quantized(n_before, g.S, g.R, g.C), qa = n_quantized(n_after, g.S, g.R, g.C);
+  hipGetLastError();
+  if (qa > qb) {
+    // The flush reads ring rows written by earlier calls, so it runs before this
+    // call's ring writes (same stream, in order).
+    FlushArgs f;
+    memset(&f, 0, sizeof f);
+    f.B = g.B; f.Hkv = g.Hkv; f.d = g.d; f.S = g.S; f.R = g.R; f.C = g.C;
+    f.n_before = n_before; f.n_new = n_new; f.u0 = qb; f.u1 = qa; f.in_dtype = in_dtype;
+    f.k_new = k_new; f.v_new = v_new; f.tk = (const _Float16 *)t_k_f16;
+    f.ring_k = (const _Float16 *)c->ring_k; f.ring_v = (const _Float16 *)c->ring_v;
+    f.codes_k = (uint8_t *)c->codes_k; f.codes_v = (uint8_t *)c->codes_v;
+    f.par_k = (_Float16 *)c->par_k; f.par_v = (_Float16 *)c->par_v;
+    f.ring_bytes = g.ring_bytes; f.kcode_row = g.kcode_row; f.kcode_bytes = g.kcode_bytes;
+    f.vset_bytes = g.vset_bytes; f.vcode_bytes = g.vcode_bytes; f.kpar_bytes = g.kpar_bytes; f.vpar_bytes = g.vpar_bytes;
+    f.bits_k = g.bits_k; f.bits_v = g.bits_v; f.quant_k = g.quant_k; f.quant_v = g.quant_v;
+    f.kpar_n = g.kpar_n; f.vpar_n = g.vpar_n; f.clip = g.clip;
+    f.lo_i = g.lo_i; f.hi_i = g.hi_i; f.lo_t = g.lo_t; f.hi_t = g.hi_t; f.need_lo = g.need_lo; f.need_hi = g.need_hi;
+    if (launch_flush(f, s) != hipSuccess) return WUSHKV_ERR_HIP;
+  }
+  AppendArgs a;
+  memset(&a, 0, sizeof a);
+  a.B = g.B; a.Hkv = g.Hkv; a.d = g.d; a.S = g.S; a.R = g.R; a.C = g.C;
+  a.n_before = n_before; a.n_new = n_new; a.q_after = qa; a.in_dtype = in_dtype;
+  a.k_new = k_new; a.v_new = v_new;
+  a.sink_k = (_Float16 *)c->sink_k; a.sink_v = (_Float16 *)c->sink_v;
+  a.ring_k = (_Float16 *)c->ring_k; a.ring_v = (_Float16 *)c->ring_v;
+  a.sink_bytes = g.sink_bytes; a.ring_bytes = g.ring_bytes;
+  if (launch_append(a, s) != hipSuccess) return WUSHKV_ERR_HIP;
+  return hip_status();
+}
+
+int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtype, int32_t batch,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float *q_t,
+                           void *stream) {
+  if (batch < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads) return WUSHKV_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return WUSHKV_ERR_SHAPE;
+  if (!check_dtype(q_dtype)) return WUSHKV_ERR_SHAPE;
+  if (!t_k_inv_t || !q || !q_t) return WUSHKV_ERR_NULL;
+  if (misaligned(t_k_inv_t) || misaligned(q) || misaligned(q_t)) return WUSHKV_ERR_ALIGN;
+  QtArgs a{t_k_inv_t, q, q_t, q_dtype, batch, num_q_heads, num_kv_heads, head_dim};
+  hipGetLastError();
+  if (launch_qtransform(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
+  return hip_status();
+}
+
+int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
+                            const float *q_t, int32_t num_q_heads, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, float *out, void *stream) {
+  Geom g;
+  int st = make_geom(c, &g);
+  if (st != WUSHKV_OK) return st;
+  if (num_q_heads < 1 || num_q_heads % g.Hkv || num_splits < 0 || !check_dtype(q_dtype)) return WUSHKV_ERR_SHAPE;
+  int G = num_q_heads / g.Hkv;
+  if (G > 16) return WUSHKV_ERR_SHAPE;
+  if (n_tokens < 1) return WUSHKV_ERR_SHAPE;
+  if (n_tokens > g.cap) return WUSHKV_ERR_CAPACITY;
+  if ((st = check_planes(c)) != WUSHKV_OK) return st;
+  if (!q || !q_t || !out) return WUSHKV_ERR_NULL;
+  if (misaligned(q) || misaligned(q_t) || misaligned(out)) return WUSHKV_ERR_ALIGN;
+  size_t need = wushkv_decode_workspace_bytes(c, n_tokens, num_q_heads, num_splits);
+  if (!workspace || need == 0 || workspace_bytes < need) return WUSHKV_ERR_WORKSPACE;
+  if (misaligned(workspace)) return WUSHKV_ERR_ALIGN;
+  int32_t P = wushkv_decode_num_splits(c, n_tokens, num_q_heads, num_splits);
+
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.B = g.B; a.Hkv = g.Hkv; a.Hq = num_q_heads; a.G = G; a.d = g.d; a.S = g.S; a.R = g.R; a.C = g.C;
+  a.n = n_tokens; a.nq = n_quantized(n_tokens, g.S, g.R, g.C); a.P = P;
+  a.q = q; a.q_dtype = q_dtype; a.qt = q_t;
+  a.sink_k = (const _Float16 *)c->sink_k; a.sink_v = (const _Float16 *)c->sink_v;
+  a.ring_k = (const _Float16 *)c->ring_k; a.ring_v = (const _Float16 *)c->ring_v;
+  a.codes_k = (const uint8_t *)c->codes_k; a.codes_v = (const uint8_t *)c->codes_v;
+  a.par_k = (const _Float16 *)c->par_k; a.par_v = (const _Float16 *)c->par_v;
+  a.sink_bytes = g.sink_bytes; a.ring_bytes = g.ring_bytes; a.kcode_row = g.kcode_row; a.kcode_bytes = g.kcode_bytes;
+  a.vset_bytes = g.vset_bytes; a.vcode_bytes = g.vcode_bytes; a.kpar_bytes = g.kpar_bytes; a.vpar_bytes = g.vpar_bytes;
+  a.bits_k = g.bits_k; a.bits_v = g.bits_v; a.quant_k = g.quant_k; a.quant_v = g.quant_v;
+  a.kpar_n = g.kpar_n; a.vpar_n = g.vpar_n;
+  size_t rows = (size_t)g.B * num_q_heads * (P + 1);
+  a.part_o = (float *)workspace;
+  a.part_ml = a.part_o + rows * g.d;
+  size_t cnt_off = (rows * g.d * 4 + rows * 2 * 4 + 255) / 256 * 256;
+  a.counters = (unsigned *)((char *)workspace + cnt_off);
+  a.out = out;
+  hipGetLastError();
+  if (launch_decode(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
+  return hip_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,245 @@
+// Generic GQA decode attention over the mixed-precision cache (all shapes the ABI
+// accepts).  It favours plain indexing over speed; decode_fast.hip holds the
+// MFMA kernel used for the common shapes.
+//
+// Grid (P + 1, B * Hkv): workgroups 0..P-1 take contiguous ranges of 64-token body
+// sets, workgroup P takes the FP16 tokens (sink + recent window).  Each computes
+// scores for the G query heads of its KV head (raw q on FP16 keys, q~ = T^{-T} q on
+// transformed body keys; WUSH-KV digest, "method key points"), an online softmax
+// in the exp2 domain, and the weighted value sum, and writes a partial
+// (m, l, o).  The last workgroup of each (b, g) to finish -- found with an
+// agent-scope acquire/release counter -- merges the P + 1 partials in fixed order
+// and resets the counter.
+#include "wushkv_internal.h"
+
+namespace wushkv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxG = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct GenSmem {
+  float q[kMaxG][128];
+  float qt[kMaxG][128];
+  float sq[kMaxG];             // sum of q~ per head
+  float s[kMaxG][kSet];        // scores, then probabilities
+  float m[kMaxG], l[kMaxG], alpha[kMaxG];
+  float pv[kSet][2];           // value parameters of the tile's tokens
+  int is_body;
+};
+
+__device__ __forceinline__ int k_code(const uint8_t *row, int d, int bits, int j) {
+  const unsigned *w = (const unsigned *)row;
+  int c = (w[j / 16] >> (2 * (j % 16))) & 3;
+  if (bits == 3) c |= ((w[d / 16 + j / 32] >> (j % 32)) & 1) << 2;
+  if (bits == 4) c |= ((w[d / 16 + j / 16] >> (2 * (j % 16))) & 3) << 2;
+  return c;
+}
+
+__device__ __forceinline__ int v_code(const uint8_t *set, int d, int bits, int u, int j) {
+  const int a = u / 16, c = (u / 4) % 4, e = u % 4;
+  const int lane = 16 * c + (j % 16), t = j / 16;
+  const int f = 4 * a + e;
+  const int idx = lane * (d / 16) + t;
+  int code = (((const unsigned *)set)[idx] >> (2 * f)) & 3;
+  if (bits == 3) code |= ((((const unsigned short *)(set + 64 * (d / 16) * 4))[idx] >> f) & 1) << 2;
+  if (bits == 4) code |= ((((const unsigned *)(set + 64 * (d / 16) * 4))[idx] >> (2 * f)) & 3) << 2;
+  return code;
+}
+
+__global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) {
+  __shared__ GenSmem sm;
+  const int tid = threadIdx.x;
+  const int part = blockIdx.x;
+  const int bg = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.G, d = a.d;
+  const float qk_scale = kLog2e / sqrtf((float)d);
+  const int h0 = g * G;  // first query head of this group
+
+  for (int i = tid; i < G * d; i += kThreads) {
+    const int hh = i / d, j = i % d;
+    const size_t off = ((size_t)b * a.Hq + h0 + hh) * d + j;
+    sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
+    sm.qt[hh][j] = a.qt[off];
+  }
+  if (tid < G) { sm.m[tid] = -INFINITY; sm.l[tid] = 0.f; }
+  __syncthreads();
+  if (tid < G) {
+    float s = 0.f;
+    for (int j = 0; j < d; ++j) s += sm.qt[tid][j];
+    sm.sq[tid] = s;
+  }
+
+  // token range of this workgroup
+  const int64_t nsets = (a.nq + kSet - 1) / kSet;
+  const bool window = (part == a.P);
+  int64_t t_begin, t_end;  // body indices, or window list indices
+  const int64_t ns = a.n < a.S ? a.n : a.S;
+  if (!window) {
+    t_begin = nsets * part / a.P * kSet;
+    t_end = nsets * (part + 1) / a.P * kSet;
+    if (t_end > a.nq) t_end = a.nq;
+  } else {
+    t_begin = 0;
+    t_end = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+  }
+  const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
+  const uint8_t *kplane = a.codes_k + bg * a.kcode_bytes;
+  const uint8_t *vplane = a.codes_v + bg * a.vcode_bytes;
+  const _Float16 *kpar = (const _Float16 *)((const char *)a.par_k + bg * a.kpar_bytes);
+  const _Float16 *vpar = (const _Float16 *)((const char *)a.par_v + bg * a.vpar_bytes);
+  const _Float16 *sink_k = (const _Float16 *)((const char *)a.sink_k + bg * a.sink_bytes);
+  const _Float16 *sink_v = (const _Float16 *)((const char *)a.sink_v + bg * a.sink_bytes);
+  const _Float16 *ring_k = (const _Float16 *)((const char *)a.ring_k + bg * a.ring_bytes);
+  const _Float16 *ring_v = (const _Float16 *)((const char *)a.ring_v + bg * a.ring_bytes);
+
+  constexpr int kMaxOut = kMaxG * 128 / kThreads;
+  float acc[kMaxOut];
+#pragma unroll
+  for (int i = 0; i < kMaxOut; ++i) acc[i] = 0.f;
+
+  __syncthreads();
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kSet) {
+    const int cnt = (int)((t_end - t0) < kSet ? (t_end - t0) : kSet);
+    // scores: thread (token tt, head group hg)
+    {
+      const int tt = tid % kSet, hg = tid / kSet;
+      if (tt < cnt) {
+        const int64_t ti = t0 + tt;
+        if (!window) {
+          const uint8_t *row = kplane + ti * a.kcode_row;
+          float kp0 = (float)kpar[ti * a.kpar_n];
+          float kp1 = a.kpar_n == 2 ? (float)kpar[ti * a.kpar_n + 1] : 0.f;
+          for (int hh = hg; hh < G; hh += kThreads / kSet) {
+            float dot = 0.f;
+            for (int j = 0; j < d; ++j) dot = fmaf(sm.qt[hh][j], (float)k_code(row, d, a.bits_k, j), dot);
+            float sc;
+            if (a.quant_k == WUSHKV_Q_QUEST) sc = kp0 * (dot - 0.5f * (Lk - 1) * sm.sq[hh]);
+            else sc = kp0 * dot + kp1 * sm.sq[hh];
+            sm.s[hh][tt] = sc * qk_scale;
+          }
+          if (hg == 0) {
+            sm.pv[tt][0] = (float)vpar[ti * a.vpar_n];
+            sm.pv[tt][1] = a.vpar_n == 2 ? (float)vpar[ti * a.vpar_n + 1] : 0.f;
+          }
+        } else {
+          const int64_t p = ti < ns ? ti : a.S + a.nq + (ti - ns);
+          const _Float16 *krow = p < a.S ? sink_k + p * d : ring_k + ((p - a.S) % (a.R + a.C)) * d;
+          for (int hh = hg; hh < G; hh += kThreads / kSet) {
+            float dot = 0.f;
+            for (int j = 0; j < d; ++j) dot = fmaf(sm.q[hh][j], (float)krow[j], dot);
+            sm.s[hh][tt] = dot * qk_scale;
+          }
+        }
+      } else {
+        for (int hh = hg; hh < G; hh += kThreads / kSet) sm.s[hh][tt] = -INFINITY;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      float mx = sm.m[tid];
+      for (int t = 0; t < cnt; ++t) mx = fmaxf(mx, sm.s[tid][t]);
+      sm.alpha[tid] = __builtin_amdgcn_exp2f(sm.m[tid] - mx);
+      sm.m[tid] = mx;
+    }
+    __syncthreads();
+    {
+      const int tt = tid % kSet, hg = tid / kSet;
+      for (int hh = hg; hh < G; hh += kThreads / kSet)
+        sm.s[hh][tt] = tt < cnt ? __builtin_amdgcn_exp2f(sm.s[hh][tt] - sm.m[hh]) : 0.f;
+    }
+    __syncthreads();
+    if (tid < G) {
+      float sum = 0.f;
+      for (int t = 0; t < cnt; ++t) sum += sm.s[tid][t];
+      sm.l[tid] = sm.l[tid] * sm.alpha[tid] + sum;
+    }
+    // weighted values: thread handles outputs o = tid + k*256 -> (head, channel)
+#pragma unroll
+    for (int k = 0; k < kMaxOut; ++k) {
+      const int o = tid + k * kThreads;
+      if (o >= G * d) break;
+      const int hh = o / d, j = o % d;
+      float s = 0.f;
+      for (int t = 0; t < cnt; ++t) {
+        const float p = sm.s[hh][t];
+        float v;
+        if (!window) {
+          const int64_t ti = t0 + t;
+          const int64_t set = ti / kSet;
+          const int code = v_code(vplane + set * a.vset_bytes, d, a.bits_v, (int)(ti % kSet), j);
+          if (a.quant_v == WUSHKV_Q_QUEST) v = ((float)code - 0.5f * (Lv - 1)) * sm.pv[t][0];
+          else v = fmaf((float)code, sm.pv[t][0], sm.pv[t][1]);
+        } else {
+          const int64_t ti = t0 + t;
+          const int64_t p = ti < ns ? ti : a.S + a.nq + (ti - ns);
+          const _Float16 *vrow = p < a.S ? sink_v + p * d : ring_v + ((p - a.S) % (a.R + a.C)) * d;
+          v = (float)vrow[j];
+        }
+        s = fmaf(p, v, s);
+      }
+      acc[k] = acc[k] * sm.alpha[hh] + s;
+    }
+    __syncthreads();
+  }
+
+  // partial out: [B][Hq][P+1][d], (m, l)
+  const int P1 = a.P + 1;
+#pragma unroll
+  for (int k = 0; k < kMaxOut; ++k) {
+    const int o = tid + k * kThreads;
+    if (o >= G * d) break;
+    const int hh = o / d, j = o % d;
+    a.part_o[(((size_t)b * a.Hq + h0 + hh) * P1 + part) * d + j] = acc[k];
+  }
+  if (tid < G) {
+    float *ml = a.part_ml + (((size_t)b * a.Hq + h0 + tid) * P1 + part) * 2;
+    ml[0] = sm.m[tid];
+    ml[1] = sm.l[tid];
+  }
+  // publish, count arrivals; the last workgroup of this (b, g) merges
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    unsigned prev = __hip_atomic_fetch_add(&a.counters[bg], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sm.is_body = (prev == (unsigned)a.P);
+  }
+  __syncthreads();
+  if (!sm.is_body) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int o = tid; o < G * d; o += kThreads) {
+    const int hh = o / d, j = o % d;
+    const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1;
+    float mstar = -INFINITY;
+    for (int p = 0; p < P1; ++p) {
+      const float *ml = a.part_ml + (row + p) * 2;
+      if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
+    }
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < P1; ++p) {
+      const float *ml = a.part_ml + (row + p) * 2;
+      if (!(ml[1] > 0.f)) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[0] - mstar);
+      num = fmaf(w, a.part_o[(row + p) * d + j], num);
+      den = fmaf(w, ml[1], den);
+    }
+    a.out[((size_t)b * a.Hq + h0 + hh) * d + j] = num / den;
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
+  dim3 grid(a.P + 1, a.B * a.Hkv);
+  hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+  return launch_decode_generic(a, s);
+}
+
+}  // namespace wushkv

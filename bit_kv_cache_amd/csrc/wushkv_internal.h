@@ -1,0 +1,105 @@
+// Internal definitions shared by the host ABI layer and the HIP kernels of
+// libwushkv.  Nothing here is part of the public ABI (include/wushkv.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/wushkv.h"
+
+namespace wushkv {
+
+constexpr int kSet = 64;           // tokens per V-code set
+constexpr int kMaxOrderStats = 8;  // order statistics kept per end for percentiles
+
+// Geometry derived from a cache descriptor (host side, validated).
+struct Geom {
+  int B, Hkv, d, S, R, C;
+  int64_t cap, body_cap;
+  int bits_k, bits_v, quant_k, quant_v;
+  float clip;
+  // percentile interpolation: value = xs[i] + t * (xs[i+1] - xs[i]) with xs sorted ascending;
+  // lo uses (lo_i, lo_t) counted from the bottom, hi uses (hi_i, hi_t) counted from the bottom.
+  int lo_i, hi_i;
+  float lo_t, hi_t;
+  int need_lo, need_hi;  // smallest / largest order statistics a row needs
+  // per-(b, g) sizes in bytes
+  size_t sink_bytes, ring_bytes, kcode_row, kcode_bytes, vset_bytes, vcode_bytes, kpar_bytes, vpar_bytes;
+  int kpar_n, vpar_n;    // fp16 parameters per token (1 QuEST, 2 affine)
+};
+
+int make_geom(const wushkv_cache *c, Geom *g);
+
+inline int64_t n_quantized(int64_t n, int S, int R, int C) {
+  int64_t e = n - S - R;
+  return e > 0 ? (int64_t)C * (e / C) : 0;
+}
+
+// Plain-old-data argument blocks handed to kernels by value.
+struct FlushArgs {
+  int B, Hkv, d, S, R, C;
+  int64_t n_before, n_new;
+  int64_t u0, u1;                 // body rows [u0, u1) flushed by this call
+  int in_dtype;
+  const void *k_new, *v_new;      // [B][Hkv][n_new][d]
+  const _Float16 *tk;             // [Hkv][d][d]
+  const _Float16 *ring_k, *ring_v;
+  uint8_t *codes_k, *codes_v;
+  _Float16 *par_k, *par_v;
+  size_t ring_bytes, kcode_row, kcode_bytes, vset_bytes, vcode_bytes, kpar_bytes, vpar_bytes;
+  int bits_k, bits_v, quant_k, quant_v, kpar_n, vpar_n;
+  float clip;
+  int lo_i, hi_i, need_lo, need_hi;
+  float lo_t, hi_t;
+};
+
+struct AppendArgs {
+  int B, Hkv, d, S, R, C;
+  int64_t n_before, n_new, q_after;
+  int in_dtype;
+  const void *k_new, *v_new;
+  _Float16 *sink_k, *sink_v, *ring_k, *ring_v;
+  size_t sink_bytes, ring_bytes;
+};
+
+struct QtArgs {
+  const float *tinvt;
+  const void *q;
+  float *qt;
+  int q_dtype, B, Hq, Hkv, d;
+};
+
+struct DecodeArgs {
+  int B, Hkv, Hq, G, d, S, R, C;
+  int64_t n, nq;                  // tokens attended, body tokens Q(n)
+  int P;                          // body partitions
+  const void *q;
+  int q_dtype;
+  const float *qt;
+  const _Float16 *sink_k, *sink_v, *ring_k, *ring_v;
+  const uint8_t *codes_k, *codes_v;
+  const _Float16 *par_k, *par_v;
+  size_t sink_bytes, ring_bytes, kcode_row, kcode_bytes, vset_bytes, vcode_bytes, kpar_bytes, vpar_bytes;
+  int bits_k, bits_v, quant_k, quant_v, kpar_n, vpar_n;
+  float *part_o, *part_ml;        // workspace: [B][Hq][P+1][d], [B][Hq][P+1][2]
+  unsigned *counters;             // [B][Hkv]
+  float *out;                     // [B][Hq][d]
+};
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_flush(const FlushArgs &a, hipStream_t s);
+hipError_t launch_qtransform(const QtArgs &a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+
+// Device helpers ------------------------------------------------------------
+
+__device__ __forceinline__ float load_in(const void *p, int dtype, size_t i) {
+  if (dtype == WUSHKV_DT_F32) return ((const float *)p)[i];
+  if (dtype == WUSHKV_DT_BF16) {
+    unsigned short b = ((const unsigned short *)p)[i];
+    return __uint_as_float(((unsigned)b) << 16);
+  }
+  return (float)((const _Float16 *)p)[i];
+}
+
+}  // namespace wushkv

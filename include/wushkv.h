@@ -1,0 +1,203 @@
+/*
+ * wushkv.h -- C ABI of the WUSH-KV online hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method (WUSH-KV: KV Cache Quantization with Data-Adaptive Transforms):
+ *   - keys pass through a per-KV-head invertible d x d transform T_K applied
+ *     after RMSNorm and RoPE, one d x d product per new token, and each query
+ *     takes the matching inverse-transpose so that q . k is unchanged
+ *     (WUSH-KV digest, slinene.github.io, section "method key points");
+ *   - values need no online transform: their transform is folded into the
+ *     value and output projection weights (same section);
+ *   - the cache keeps an FP16 sink window and an FP16 recent window and
+ *     quantizes tokens leaving the recent window in chunks of 8 or 16 (digest,
+ *     sections "takeaways" and "method key points");
+ *   - the per-token quantizer is QuEST INT (RMS-based scaling, bin-centre
+ *     reconstruction; review blog "[논문리뷰] WUSH-KV", Key Terms) or an
+ *     OSCAR-style percentile-clipped affine quantizer (digest, "takeaways").
+ *   - several query heads share one KV head (grouped-query attention; review
+ *     blog, Key Terms); query head h reads KV head h / G, G = Hq / Hkv.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are device pointers (hipMalloc / torch CUDA memory)
+ *     owned by the caller; the library allocates nothing, keeps no state
+ *     between calls and never synchronizes the stream.  It is thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work of a call is enqueued on that stream, in order.
+ *   - Tensors are dense, row-major, in the shapes documented; every pointer
+ *     must be 16-byte aligned (WUSHKV_ERR_ALIGN otherwise).
+ *   - Every argument check runs on the host before any launch; a failing call
+ *     enqueues nothing.  After launching, hipGetLastError() is checked and
+ *     mapped to WUSHKV_ERR_HIP.  Faults inside kernels surface at the
+ *     caller's next synchronization.  No C++ exception crosses the ABI.
+ *   - Inputs must be finite with |x| < 65504 (the fp16 range); anything else
+ *     gives unspecified (but memory-safe) results.
+ */
+#ifndef WUSHKV_H
+#define WUSHKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WUSHKV_ABI_VERSION 1
+
+typedef enum {
+  WUSHKV_OK = 0,
+  WUSHKV_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  WUSHKV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent           */
+  WUSHKV_ERR_UNSUPPORTED = 3, /* valid request this build does not implement      */
+  WUSHKV_ERR_CAPACITY = 4,    /* token count beyond the cache capacity            */
+  WUSHKV_ERR_WORKSPACE = 5,   /* decode workspace missing or too small            */
+  WUSHKV_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                 */
+  WUSHKV_ERR_HIP = 7          /* the HIP runtime reported an error at launch time */
+} wushkv_status;
+
+typedef enum { WUSHKV_DT_F32 = 0, WUSHKV_DT_BF16 = 1, WUSHKV_DT_F16 = 2 } wushkv_dtype;
+
+/* QUEST: per-token step s = fp16(2 * clip_mult * rms(x) / L), L = 2^bits, code
+ *   q = clamp(floor(x / s + L/2), 0, L-1), reconstruction (q - (L-1)/2) * s; a zero
+ *   step gives code L/2.  AFFINE_PCT: lo / hi = the pct_lo / pct_hi percentiles of
+ *   the token's d values (linear interpolation between order statistics at virtual
+ *   index (d-1)*pct/100), scale s = fp16((hi - lo)/(L-1)), zero z = fp16(lo), code
+ *   q = clamp(rint((x - z)/s), 0, L-1) (half to even), reconstruction z + q*s; a
+ *   zero scale gives code 0.  Keys are quantized after the transform T_K, values
+ *   as they are; the quantizer input is always the token's fp16 value. */
+typedef enum { WUSHKV_Q_QUEST = 0, WUSHKV_Q_AFFINE_PCT = 1 } wushkv_quant;
+
+enum {
+  WUSHKV_PLANE_SINK_K = 0, WUSHKV_PLANE_SINK_V = 1,
+  WUSHKV_PLANE_RING_K = 2, WUSHKV_PLANE_RING_V = 3,
+  WUSHKV_PLANE_CODES_K = 4, WUSHKV_PLANE_CODES_V = 5,
+  WUSHKV_PLANE_PAR_K = 6, WUSHKV_PLANE_PAR_V = 7,
+  WUSHKV_NUM_PLANES = 8
+};
+
+/*
+ * Cache descriptor: a host struct read at call time.  The planes are caller-owned
+ * device buffers, each laid out [batch][num_kv_heads][...] with the per-(b, g)
+ * part below; wushkv_plane_bytes() gives each plane's total size.
+ *   S = sink, R = recent, C = chunk, body_cap = round_up(capacity - S, 64)
+ *   sink_k/v   fp16 [S][d]        first S tokens (raw post-RoPE keys / values)
+ *   ring_k/v   fp16 [R + C][d]    recent tokens; token p sits in slot (p - S) mod (R + C);
+ *                                 keys are raw (untransformed) post-RoPE keys
+ *   codes_k    u8   [body_cap][d*bits_k/8]   token-major rows of transformed-key codes
+ *   codes_v    u8   [body_cap/64][8*d*bits_v] sets of 64 value-code tokens
+ *   par_k/v    fp16 [body_cap][1 (QuEST step) | 2 (affine scale, zero)]
+ * Code bit layout (body index u = p - S):
+ *   K row:  plane 0 = d/16 u32 words, word w bits 2f..2f+1 = low 2 bits of channel 16w+f;
+ *           plane 1 (bits 3) = d/32 u32, word w bit f = bit 2 of channel 32w+f;
+ *           plane 1 (bits 4) = d/16 u32, word w bits 2f..2f+1 = bits 2..3 of channel 16w+f.
+ *   V set:  token u = 64*sigma + 16*a + 4*c + e, channel j = 16*t + m go to lane 16*c+m,
+ *           field f = 4*a + e.  plane 0 = u32 word [lane*(d/16) + t], bits 2f..2f+1 = low
+ *           2 bits; plane 1 (bits 3) = u16 [lane*(d/16) + t] after plane 0, bit f = bit 2;
+ *           plane 1 (bits 4) = u32 [lane*(d/16) + t] after plane 0, bits 2f..2f+1 = bits 2..3.
+ * Token p of an n-token cache is a sink token if p < S, a body token if
+ * S <= p < S + Q(n) with Q(n) = C * floor(max(0, n - S - R) / C), and a recent
+ * token otherwise: the ring holds up to R + C tokens and flushes its oldest C
+ * when it fills.
+ * Supported: head_dim in {64, 128}; bits in {2, 3, 4}; chunk >= 1; recent % chunk == 0;
+ * sink >= 0; 0 <= pct_lo < pct_hi <= 100; clip_mult > 0.
+ */
+typedef struct {
+  int32_t batch, num_kv_heads, head_dim;
+  int32_t sink, recent, chunk;
+  int64_t capacity;                 /* max tokens per sequence */
+  int32_t bits_k, bits_v;           /* 2 | 3 | 4 */
+  int32_t quant_k, quant_v;         /* wushkv_quant */
+  float clip_mult;                  /* QuEST clip multiplier c (2.5) */
+  float pct_lo, pct_hi;             /* affine percentiles (0.5, 99.5) */
+  void *sink_k, *sink_v;
+  void *ring_k, *ring_v;
+  void *codes_k, *codes_v;
+  void *par_k, *par_v;
+} wushkv_cache;
+
+/* Human-readable name of a status code (static string). */
+const char *wushkv_status_string(int status);
+
+/* ABI version (WUSHKV_ABI_VERSION) of the loaded library. */
+int wushkv_abi_version(void);
+
+/* Check a descriptor's sizes and options (pointers are not inspected).  Host only. */
+int wushkv_cache_check(const wushkv_cache *c);
+
+/* Total bytes of plane `plane` (WUSHKV_PLANE_*) over [batch][num_kv_heads]; 0 when
+ * the descriptor fails wushkv_cache_check or the plane id is unknown. */
+size_t wushkv_plane_bytes(const wushkv_cache *c, int plane);
+
+/* The number of KV partitions wushkv_decode_attention will use for these arguments
+ * (num_splits = 0 asks the library to choose); 0 when the arguments are invalid. */
+int32_t wushkv_decode_num_splits(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads,
+                                 int32_t num_splits);
+
+/* Bytes of decode workspace needed for these arguments (0 when invalid).  The
+ * workspace holds split-K partials and per-(b, g) arrival counters; its counter
+ * region must be zero before its first use (allocate it zero-filled) and every
+ * completed call leaves it zero again.  Calls that overlap in time must not share
+ * a workspace. */
+size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads,
+                                     int32_t num_splits);
+
+/*
+ * Append n_new tokens to every sequence of the cache, all of which hold n_before
+ * tokens, and quantize every token the window policy flushes as a result
+ * (WUSH-KV digest, "takeaways" and "method key points": FP16 sink/recent windows,
+ * chunked flush; the key transform after RoPE).
+ *   k_new, v_new  [batch][num_kv_heads][n_new][d] in in_dtype (F32, BF16 or F16):
+ *                 post-RoPE keys and values (values already in the folded basis).
+ *   t_k_f16       fp16 [num_kv_heads][d][d], row-major: the key transform, applied
+ *                 as x = T_K k to each flushed key's fp16 value.
+ * Sink tokens and tokens that end in the recent window are stored as fp16
+ * (round-to-nearest-even); body tokens get codes and parameters.  Tokens that were
+ * in the ring before the call and are flushed by it are read back from the ring.
+ * Errors: NULL pointer -> ERR_NULL; bad descriptor or n_new < 0 or n_before < 0 ->
+ * ERR_SHAPE; n_before + n_new > capacity -> ERR_CAPACITY; a percentile needing more
+ * than 8 order statistics from either end -> ERR_UNSUPPORTED; misaligned -> ERR_ALIGN.
+ * n_new == 0 is a no-op.
+ */
+int wushkv_append_flush(const wushkv_cache *c, int64_t n_before, int32_t n_new,
+                        const void *k_new, const void *v_new, int32_t in_dtype,
+                        const void *t_k_f16, void *stream);
+
+/*
+ * Query transform q~[b][h] = T_{h/G}^{-T} q[b][h] (WUSH-KV digest, "method key
+ * points": the query side takes one d x d product so that q~ . (T k) = q . k).
+ *   t_k_inv_t  fp32 [num_kv_heads][d][d], row-major: T^{-T} itself, i.e. element
+ *              [i][j] multiplies q[j] into q~[i]; the caller computes it (offline,
+ *              like T_K) from the fp16 T_K actually used.
+ *   q          [batch][num_q_heads][d] in q_dtype;  q_t  fp32 [batch][num_q_heads][d].
+ * Errors: ERR_NULL, ERR_SHAPE (num_q_heads % num_kv_heads != 0, d not in {64, 128},
+ * non-positive sizes), ERR_ALIGN.
+ */
+int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtype,
+                           int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, float *q_t, void *stream);
+
+/*
+ * GQA decode attention over the first n_tokens tokens of every sequence:
+ *   out[b][h] = sum_p softmax_p(s_p) v_p,  s_p = (q . k_p) / sqrt(d) on the FP16 sink
+ *   and recent tokens (raw q, raw keys) and s_p = (q~ . x^_p) / sqrt(d) on the body
+ *   (q~ from wushkv_query_transform, x^ the dequantized transformed key), v_p the
+ *   fp16 value or the dequantized value.  Each KV head's data is read once for all
+ *   G query heads of its group.  The body is split into num_splits KV partitions
+ *   (0 = library's choice) whose partial (max, sum, weighted values) are merged with
+ *   the online-softmax rule inside the same launch.
+ *   q      [batch][num_q_heads][d] in q_dtype;  q_t  fp32 [batch][num_q_heads][d]
+ *   out    fp32 [batch][num_q_heads][d]
+ *   workspace  device buffer of at least wushkv_decode_workspace_bytes() bytes.
+ * Errors: ERR_NULL, ERR_SHAPE (including n_tokens < 1 and group sizes G > 16),
+ * ERR_CAPACITY (n_tokens > capacity), ERR_WORKSPACE, ERR_ALIGN.
+ */
+int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens,
+                            const void *q, int32_t q_dtype, const float *q_t,
+                            int32_t num_q_heads, int32_t num_splits,
+                            void *workspace, size_t workspace_bytes,
+                            float *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WUSHKV_H */

@@ -68,6 +68,8 @@ def pack_k(codes, bits):
 
 def unpack_k(raw, bits, d, T):
     """uint8 rows [T, d*bits/8] (any buffer of at least that size) -> codes [T, d]."""
+    if T == 0:
+        return np.zeros((0, d), dtype=np.int64)
     raw = np.ascontiguousarray(np.asarray(raw, dtype=np.uint8).reshape(-1)[: T * k_row_bytes(d, bits)])
     words = _words(raw).reshape(T, -1).astype(np.int64)
     nw0 = d // 16
@@ -127,6 +129,8 @@ def pack_v(codes, bits):
 
 def unpack_v(raw, bits, d, T):
     """uint8 sets (any buffer holding ceil(T/64) sets) -> codes [T, d]."""
+    if T == 0:
+        return np.zeros((0, d), dtype=np.int64)
     nset = -(-T // SET)
     sb = v_set_bytes(d, bits)
     raw = np.ascontiguousarray(np.asarray(raw, dtype=np.uint8).reshape(-1)[: nset * sb]).reshape(nset, sb)

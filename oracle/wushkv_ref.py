@@ -102,10 +102,15 @@ def quest_params(x, bits, clip_mult):
     Review blog, Key Terms: RMS-based scaling and bin-centre reconstruction.
     Reading: L = 2**bits equal bins over [-c*r, c*r] (c = clip multiplier,
     2.5 in the workloads), one fp16 step per token."""
+    return f16(quest_step_exact(x, bits, clip_mult))
+
+
+def quest_step_exact(x, bits, clip_mult):
+    """The QuEST step 2*c*r/L before its fp16 rounding."""
     L = 2 ** bits
     x = np.asarray(x, dtype=np.float64)
     r = np.sqrt(np.mean(x * x, axis=-1))
-    return f16(2.0 * clip_mult * r / L)
+    return 2.0 * clip_mult * r / L
 
 
 def quest_codes(x, step, bits):
@@ -150,11 +155,17 @@ def affine_params(x, bits, pct_lo, pct_hi):
     affine quantizer.  Reading: lo/hi are the pct_lo / pct_hi percentiles of
     the row's d values, scale s = (hi - lo)/(L - 1) and zero z = lo, both
     stored fp16."""
+    s, lo = affine_params_exact(x, bits, pct_lo, pct_hi)
+    return f16(s), f16(lo)
+
+
+def affine_params_exact(x, bits, pct_lo, pct_hi):
+    """(scale, zero) of the affine quantizer before their fp16 rounding."""
     L = 2 ** bits
     xs = np.sort(np.asarray(x, dtype=np.float64), axis=-1)
     lo = percentile_linear(xs, pct_lo)
     hi = percentile_linear(xs, pct_hi)
-    return f16((hi - lo) / (L - 1)), f16(lo)
+    return (hi - lo) / (L - 1), lo
 
 
 def affine_codes(x, scale, zero, bits):
@@ -186,6 +197,14 @@ def quantize(x, quant, bits, clip_mult=2.5, pct_lo=0.5, pct_hi=99.5):
         s, z = affine_params(x, bits, pct_lo, pct_hi)
         return affine_codes(x, s, z, bits), np.stack([s, z], axis=-1)
     raise ValueError(quant)
+
+
+def params_exact(x, quant, bits, clip_mult=2.5, pct_lo=0.5, pct_hi=99.5):
+    """Parameters before fp16 rounding, shaped like quantize()'s params."""
+    if quant == QUEST:
+        return quest_step_exact(x, bits, clip_mult)[..., None]
+    s, z = affine_params_exact(x, bits, pct_lo, pct_hi)
+    return np.stack([s, z], axis=-1)
 
 
 def codes_from_params(x, quant, bits, params):

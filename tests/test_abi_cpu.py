@@ -1,0 +1,145 @@
+"""The C ABI library loads, exports every symbol include/wushkv.h declares, and
+rejects bad arguments on the host with the documented status codes before
+anything is launched.  No GPU needed: every call here fails validation (fake
+pointers are never dereferenced), or only computes sizes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_kv_cache_amd as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wushkv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(W.LIB_PATH):
+        pytest.skip("libwushkv.so not built (run __graft_entry__.build())")
+    return W.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wushkv_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(W.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", W.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (wushkv_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings_and_version(lib):
+    assert W.status_string(0) == "ok"
+    assert "capacity" in W.status_string(W.ERR_CAPACITY)
+    assert W.status_string(99) == "unknown status"
+    assert lib.wushkv_abi_version() == 1
+
+
+def _spec(**kw):
+    base = dict(batch=2, num_kv_heads=8, head_dim=128, capacity=8256, sink=64, recent=256, chunk=8,
+                bits_k=2, bits_v=3, quant_k=W.Q_AFFINE, quant_v=W.Q_QUEST)
+    base.update(kw)
+    return W.CacheSpec(**base)
+
+
+def test_plane_bytes_follow_the_layout(lib):
+    s = _spec()
+    pb = s.plane_bytes()
+    heads = 2 * 8
+    body_cap = -(-(8256 - 64) // 64) * 64
+    assert pb["sink_k"] == heads * 64 * 128 * 2
+    assert pb["ring_v"] == heads * (256 + 8) * 128 * 2
+    assert pb["codes_k"] == heads * body_cap * 128 * 2 // 8
+    assert pb["codes_v"] == heads * (body_cap // 64) * 64 * 128 * 3 // 8
+    assert pb["par_k"] == heads * body_cap * 2 * 2
+    assert pb["par_v"] == heads * body_cap * 1 * 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), W.ERR_SHAPE),
+    (dict(bits_k=5), W.ERR_SHAPE),
+    (dict(bits_v=1), W.ERR_SHAPE),
+    (dict(chunk=0), W.ERR_SHAPE),
+    (dict(recent=250), W.ERR_SHAPE),          # recent must be a multiple of chunk
+    (dict(quant_k=7), W.ERR_SHAPE),
+    (dict(pct_lo=60.0, pct_hi=40.0), W.ERR_SHAPE),
+    (dict(pct_lo=10.0), W.ERR_UNSUPPORTED),    # needs 14 order statistics from the bottom
+    (dict(clip_mult=0.0, quant_v=W.Q_QUEST), W.ERR_SHAPE),
+    (dict(batch=0), W.ERR_SHAPE),
+    (dict(), W.OK),
+])
+def test_descriptor_checks(lib, kw, status):
+    d = _spec(**kw).desc()
+    assert lib.wushkv_cache_check(ctypes.byref(d)) == status
+
+
+def _fake_planes(d, align=16):
+    for i, p in enumerate(W.PLANES):
+        setattr(d, p, 0x10000 * (i + 1) + (0 if align == 16 else 4))
+
+
+def test_append_flush_validation(lib):
+    d = _spec().desc()
+    f = lib.wushkv_append_flush
+    kv = ctypes.c_void_p(0x900000)
+    # null planes
+    assert f(ctypes.byref(d), 0, 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    _fake_planes(d)
+    assert f(ctypes.byref(d), 0, 1, None, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    assert f(ctypes.byref(d), 0, 1, kv, kv, 9, kv, None) == W.ERR_SHAPE
+    assert f(ctypes.byref(d), -1, 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_SHAPE
+    assert f(ctypes.byref(d), 8000, 257, kv, kv, W.DT_BF16, kv, None) == W.ERR_CAPACITY
+    assert f(ctypes.byref(d), 0, 1, ctypes.c_void_p(0x900004), kv, W.DT_BF16, kv, None) == W.ERR_ALIGN
+    assert f(ctypes.byref(d), 5, 0, None, None, W.DT_BF16, None, None) == W.OK  # no-op
+    _fake_planes(d, align=4)
+    assert f(ctypes.byref(d), 0, 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_ALIGN
+
+
+def test_query_transform_validation(lib):
+    f = lib.wushkv_query_transform
+    p = ctypes.c_void_p(0x900000)
+    assert f(p, p, W.DT_BF16, 1, 30, 8, 128, p, None) == W.ERR_SHAPE   # 30 % 8 != 0
+    assert f(p, p, W.DT_BF16, 1, 32, 8, 80, p, None) == W.ERR_SHAPE
+    assert f(None, p, W.DT_BF16, 1, 32, 8, 128, p, None) == W.ERR_NULL
+    assert f(p, ctypes.c_void_p(0x900002), W.DT_BF16, 1, 32, 8, 128, p, None) == W.ERR_ALIGN
+
+
+def test_decode_validation_and_workspace(lib):
+    d = _spec().desc()
+    _fake_planes(d)
+    f = lib.wushkv_decode_attention
+    p = ctypes.c_void_p(0x900000)
+    ws_need = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    P = lib.wushkv_decode_num_splits(ctypes.byref(d), 8000, 32, 0)
+    assert P >= 1
+    rows = 2 * 32 * (P + 1)
+    assert ws_need >= rows * 128 * 4 + rows * 8 + 2 * 8 * 4
+    assert lib.wushkv_decode_num_splits(ctypes.byref(d), 8000, 32, 7) == 7
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, 32, 0, p, ws_need - 1, p, None) == W.ERR_WORKSPACE
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, 32, 0, None, ws_need, p, None) == W.ERR_WORKSPACE
+    assert f(ctypes.byref(d), 9000, p, W.DT_BF16, p, 32, 0, p, ws_need, p, None) == W.ERR_CAPACITY
+    assert f(ctypes.byref(d), 0, p, W.DT_BF16, p, 32, 0, p, ws_need, p, None) == W.ERR_SHAPE
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, 30, 0, p, ws_need, p, None) == W.ERR_SHAPE
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, 8 * 17, 0, p, ws_need, p, None) == W.ERR_SHAPE  # G = 17
+    assert f(ctypes.byref(d), 8000, None, W.DT_BF16, p, 32, 0, p, ws_need, p, None) == W.ERR_NULL
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, 32, -1, p, ws_need, p, None) == W.ERR_SHAPE
+    assert lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 0, 32, 0) == 0
+
+
+def test_product_package_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "bit_kv_cache_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.replace("oracle of", ""), fn

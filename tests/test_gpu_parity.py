@@ -1,0 +1,156 @@
+"""GPU parity of the HIP path against the CPU oracle (run on an MI355X).
+
+Each test names its workload, shape and seed in its printed lines.  Sizes are
+chosen so the oracle finishes in seconds while spanning several 64-token sets,
+flush boundaries and a ragged tail; the full-size workloads are checked on
+sampled (batch row, KV head) pairs."""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_amd as W
+from synth import configs
+from tests.parity_util import Run, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_c0_tiny_full():
+    w = configs.TINY
+    r = Run(w, n_total=w.capacity)
+    r.append(w.context)
+    r.check_cache()
+    r.append(1)
+    q, qt, out = r.decode(0)
+    r.check_cache()
+    r.check_decode(q, qt, out)
+
+
+def test_c1_layer_decode_steps():
+    w = configs.LAYER_8B
+    r = Run(w)
+    r.append(w.context)
+    _, stats = r.check_cache()
+    say(f"[c1 prefill] {stats}")
+    for step in range(w.decode_steps):
+        r.append(1)
+        q, qt, out = r.decode(step)
+        if step % 8 == 7 or step in (0, 63):
+            r.check_decode(q, qt, out)
+    _, stats = r.check_cache()
+    say(f"[c1 after 64 steps] {stats}")
+
+
+def test_c2_serving_scaled():
+    w = configs.SERVING.scaled(batch=2, context=4000)
+    r = Run(w)
+    r.append(w.context)
+    r.check_cache()
+    r.append(1)
+    q, qt, out = r.decode(0)
+    r.check_decode(q, qt, out)
+
+
+def test_c4_long_context_scaled_empty_partitions():
+    # 128 partitions over fewer than 128 sets leaves some partitions empty
+    w = configs.LONG_CONTEXT.scaled(batch=1, context=6000)
+    r = Run(w)
+    r.append(w.context)
+    r.check_cache()
+    r.append(1)
+    q, qt, out = r.decode(0, num_splits=128)
+    r.check_decode(q, qt, out)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_c3_bulk_flush_scaled(bits):
+    w = configs.BULK_FLUSH.scaled(num_kv_heads=2, num_q_heads=8, context=4096 + 37, bits_k=bits, bits_v=bits)
+    r = Run(w, n_total=w.context)
+    r.append(w.context)
+    _, stats = r.check_cache()
+    say(f"[c3 bits={bits}] {stats}")
+
+
+FUZZ = [
+    # d, bits_k, bits_v, quant_k, quant_v, chunk, n_prefill, steps, G
+    (64, 2, 2, "quest", "quest", 8, 10, 3, 4),
+    (64, 3, 4, "affine", "quest", 16, 70, 5, 2),
+    (128, 4, 3, "quest", "affine", 8, 319, 12, 1),
+    (128, 2, 3, "affine", "affine", 16, 600, 20, 8),
+    (64, 4, 4, "affine", "affine", 8, 1000, 9, 16),
+    (128, 3, 2, "quest", "quest", 16, 333, 17, 4),
+]
+
+
+@pytest.mark.parametrize("case", FUZZ, ids=[f"d{c[0]}k{c[1]}v{c[2]}{c[3][0]}{c[4][0]}C{c[5]}n{c[6]}G{c[8]}" for c in FUZZ])
+def test_fuzz_shapes_and_flush_boundaries(case):
+    d, bk, bv, qk, qv, C, n0, steps, G = case
+    w = configs.SERVING.scaled(name="fuzz", seed=100 + n0, batch=2, num_kv_heads=2, num_q_heads=2 * G, head_dim=d,
+                               context=n0, decode_steps=steps, bits_k=bk, bits_v=bv, quant_k=qk, quant_v=qv,
+                               chunk=C, k_dist="gauss", v_dist="t3")
+    r = Run(w)
+    r.append(n0)
+    r.check_cache()
+    for s in range(steps):
+        r.append(1)
+        q, qt, out = r.decode(s, num_splits=(s % 3))
+        r.check_decode(q, qt, out)
+    r.check_cache()
+
+
+def test_token_by_token_equals_prefill():
+    """A 420-token prefill and 420 single-token appends leave bitwise-equal live
+    cache contents (ring slots of flushed tokens are stale and not compared)."""
+    from oracle import layout as LY
+    from oracle import wushkv_ref as R
+    from tests.parity_util import plane_arrays
+    w = configs.SERVING.scaled(name="tok", seed=7, batch=1, num_kv_heads=2, num_q_heads=8, context=420,
+                               decode_steps=0, chunk=8)
+    a = Run(w)
+    a.append(420)
+    b = Run(w)
+    for _ in range(420):
+        b.append(1)
+    torch.cuda.synchronize()
+    pa, pb = plane_arrays(a.cache), plane_arrays(b.cache)
+    nb = R.n_quantized(420, 64, 256, 8)
+    live = (np.arange(64 + nb, 420) - 64) % (256 + 8)
+    for g in range(2):
+        for p in ("sink_k", "sink_v"):
+            assert np.array_equal(pa[p][0, g].view(np.uint16), pb[p][0, g].view(np.uint16)), p
+        for p in ("ring_k", "ring_v"):
+            assert np.array_equal(pa[p][0, g, live].view(np.uint16), pb[p][0, g, live].view(np.uint16)), p
+        for p in ("par_k", "par_v"):
+            assert np.array_equal(pa[p][0, g, :nb].view(np.uint16), pb[p][0, g, :nb].view(np.uint16)), p
+        assert np.array_equal(LY.unpack_k(pa["codes_k"][0, g], 2, 128, nb), LY.unpack_k(pb["codes_k"][0, g], 2, 128, nb))
+        assert np.array_equal(LY.unpack_v(pa["codes_v"][0, g], 2, 128, nb), LY.unpack_v(pb["codes_v"][0, g], 2, 128, nb))
+    a.check_cache()
+    b.check_cache()
+
+
+def test_decode_deterministic_and_split_invariant():
+    w = configs.SERVING.scaled(name="det", seed=9, batch=2, context=3000)
+    r = Run(w)
+    r.append(w.context)
+    q, qt, o1 = r.decode(0, num_splits=5)
+    _, _, o2 = r.decode(0, num_splits=5)
+    assert torch.equal(o1, o2)
+    for P in (1, 2, 17, 47):
+        _, _, o3 = r.decode(0, num_splits=P)
+        rel = float((o3 - o1).norm() / o1.norm())
+        assert rel < 1e-5, (P, rel)
+
+
+def test_snapshot_restore_continues_bitwise():
+    w = configs.LAYER_8B.scaled(name="snap", context=1000, decode_steps=20)
+    r = Run(w)
+    r.append(1000)
+    snap = r.cache.snapshot()
+    outs = []
+    for s in range(20):
+        r.append(1)
+        outs.append(r.decode(s)[2].clone())
+    r.cache.restore(snap)
+    for s in range(20):
+        r.append(1)
+        assert torch.equal(r.decode(s)[2], outs[s]), s

@@ -275,6 +275,8 @@ def test_pack_v_worked_words():
 @pytest.mark.parametrize("d", [64, 128])
 def test_pack_roundtrip(bits, d):
     rng = np.random.default_rng(bits * d)
+    assert LY.unpack_k(np.zeros(0, np.uint8), bits, d, 0).shape == (0, d)
+    assert LY.unpack_v(np.zeros(0, np.uint8), bits, d, 0).shape == (0, d)
     for T in (1, 63, 64, 65, 200):
         c = rng.integers(0, 2 ** bits, (T, d))
         assert np.array_equal(LY.unpack_k(LY.pack_k(c, bits), bits, d, T), c)
