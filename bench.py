@@ -1,0 +1,290 @@
+"""Benchmark of the WUSH-KV online path on one MI355X.
+
+A step is one decode step of the batched-serving workload (32 sequences of
+32768 tokens, 32 query / 8 KV heads, head_dim 128, 2-bit percentile-clipped
+affine K and V, sink 64 / recent 256 / chunk 16): append one token to every
+sequence (flushing 16 tokens every 16th step), transform the queries, and run
+GQA decode attention over the whole cache.  The headline value is decode
+attention GB/s: algorithmic bytes the decode must move (codes, parameters, FP16
+windows, q, q~, out) per step over the step time.  A second leg times the bulk
+prefill flush (36 layers x 8 KV heads x 65536 tokens) at 2, 3 and 4 bits, and a
+third times the CPU oracle on a bounded sample of the decode step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-flush] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_kv_cache_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(w, n):
+    """Algorithmic bytes of one decode over n cached tokens."""
+    from synth.configs import QUEST
+    S, R, C, d = w.sink, w.recent, w.chunk, w.head_dim
+    nq = C * (max(0, n - S - R) // C)
+    pk = 1 if w.quant_k == QUEST else 2
+    pv = 1 if w.quant_v == QUEST else 2
+    heads = w.batch * w.num_kv_heads
+    body = nq * (d * w.bits_k // 8 + d * w.bits_v // 8 + 2 * pk + 2 * pv)
+    window = (n - nq) * d * 2 * 2
+    qio = w.batch * w.num_q_heads * d * (2 + 4 + 4)  # q bf16, q~ f32, out f32
+    return heads * (body + window) + qio
+
+
+def flush_bytes(w, bits, n):
+    """Algorithmic bytes of one bulk prefill flush call (one layer)."""
+    S, R, C, d = w.sink, w.recent, w.chunk, w.head_dim
+    nq = C * (max(0, n - S - R) // C)
+    heads = w.batch * w.num_kv_heads
+    read = n * d * 2 * 2
+    write = nq * (2 * d * bits // 8 + 2 * 2) + (n - nq) * d * 2 * 2
+    return heads * (read + write) + w.num_kv_heads * d * d * 2
+
+
+def traffic_from_profile(name):
+    """Measured HBM bytes per launch from a committed counter summary, if it was
+    taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", name)
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_decode_leg(args):
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+
+    w = configs.SERVING
+    dev = "cuda"
+    n0 = w.context
+    total = n0 + args.warmup + args.steps
+    log(f"[bench] decode workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} n={n0}")
+    k, v = gen.kv_tensors(w, 0, total, dev)
+    t16, tinvt = gen.key_transforms(w, 0)
+    t16, tinvt = t16.to(dev), tinvt.to(dev)
+    spec = W.CacheSpec(batch=w.batch, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=total,
+                       sink=w.sink, recent=w.recent, chunk=w.chunk, bits_k=w.bits_k, bits_v=w.bits_v,
+                       quant_k=W.Q_AFFINE, quant_v=W.Q_AFFINE, pct_lo=w.pct_lo, pct_hi=w.pct_hi)
+    cache = W.KVCache(spec, dev)
+    W.append_flush(cache, k[:, :, :n0].contiguous(), v[:, :, :n0].contiguous(), t16)
+    steps_k = [k[:, :, n0 + i:n0 + i + 1].contiguous() for i in range(args.warmup + args.steps)]
+    steps_v = [v[:, :, n0 + i:n0 + i + 1].contiguous() for i in range(args.warmup + args.steps)]
+    qs = [gen.queries(w, 0, i, dev) for i in range(args.warmup + args.steps)]
+    qt = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    out = torch.empty_like(qt)
+    P = W.decode_num_splits(cache, total, w.num_q_heads, 0)
+    ws = W.decode_workspace(cache, total, w.num_q_heads, P)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill done; splits={P}")
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        W.append_flush(cache, steps_k[i], steps_v[i], t16)
+        if ev is not None:
+            ev[1].record()
+        W.query_transform(tinvt, qs[i], w.num_kv_heads, out=qt)
+        if ev is not None:
+            ev[2].record()
+        W.decode_attention(cache, qs[i], qt, num_splits=P, workspace=ws, out=out)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    n_start = cache.n
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    app = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    qtm = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    dec = [e[2].elapsed_time(e[3]) for e in evs]
+    dec_ms = sum(dec) / len(dec)
+    ms_step = wall * 1e3 / args.steps
+    nbytes = sum(decode_bytes(w, n_start + j + 1) for j in range(args.steps)) / args.steps
+    log(f"[bench] step {ms_step:.4f} ms (append {app:.4f}, qtransform {qtm:.4f}, decode {dec_ms:.4f} ms); "
+        f"decode bytes {nbytes / 1e6:.1f} MB")
+    return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, app_ms=app, qt_ms=qtm, bytes=nbytes, splits=P,
+                n=n_start, cache=cache)
+
+
+def run_flush_leg(args):
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+
+    w = configs.BULK_FLUSH
+    dev = "cuda"
+    n = w.context
+    layers = w.layers
+    log(f"[bench] bulk flush workload {w.name}: {layers} layers x Hkv={w.num_kv_heads} x {n} tokens")
+    kv = [gen.kv_tensors(w, l, n, dev) for l in range(layers)]
+    tks = [gen.key_transforms(w, l)[0].to(dev) for l in range(layers)]
+    res = {}
+    for bits in w.flush_bits:
+        spec = W.CacheSpec(batch=1, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=n,
+                           sink=w.sink, recent=w.recent, chunk=w.chunk, bits_k=bits, bits_v=bits,
+                           quant_k=W.Q_QUEST, quant_v=W.Q_QUEST)
+        caches = [W.KVCache(spec, dev) for _ in range(layers)]
+        for rep in range(2):  # first pass warms up
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(layers):
+                W.append_flush(caches[l], kv[l][0], kv[l][1], tks[l], n_before=0)
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        nbytes = layers * flush_bytes(w, bits, n)
+        res[bits] = dict(ms=ms, tokens_per_s=n / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
+                         bytes=nbytes)
+        log(f"[bench] flush {bits}-bit: {ms:.3f} ms for {layers} layers -> {n / (ms * 1e-3):.3e} tokens/s, "
+            f"{nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+        del caches
+    del kv
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_cpu_leg(dl, sample_heads=16):
+    """The oracle, as it stands, on a bounded sample of the decode step: the G query
+    heads of `sample_heads` (batch row, KV head) pairs, at the same context."""
+    import numpy as np
+
+    from oracle import wushkv_ref as R
+    from synth import gen
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    w = dl["workload"]
+    n = dl["n"]
+    t16, _ = gen.key_transforms(w, 0)
+    cache_pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)][:: (w.batch * w.num_kv_heads) // sample_heads][:sample_heads]
+    q = gen.queries(w, 0, 0, "cpu").float().numpy().astype(np.float64)
+    heads = []
+    for b, g in cache_pairs:
+        kb, vb = gen.kv_block(w, 0, b, g, n, "cuda")
+        kb, vb = kb.float().cpu().numpy().astype(np.float64), vb.float().cpu().numpy().astype(np.float64)
+        heads.append((b, g, R.build_head_cache(kb, vb, t16[g].numpy(), n, sink=w.sink, recent=w.recent,
+                                               chunk=w.chunk, quant_k=w.quant_k, quant_v=w.quant_v,
+                                               bits_k=w.bits_k, bits_v=w.bits_v, pct_lo=w.pct_lo,
+                                               pct_hi=w.pct_hi)))
+    if threadpool_limits:
+        threadpool_limits(limits=cores)
+    used = cores
+    if threadpool_info:
+        infos = threadpool_info()
+        if infos:
+            used = max(i.get("num_threads", 1) for i in infos)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for b, g, c in heads:
+            for h in range(g * w.group, (g + 1) * w.group):
+                qt = R.query_transform(t16[g].numpy(), q[b, h])
+                R.decode_head(c, q[b, h], qt)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0:
+            break
+    el = (time.perf_counter() - t0) / reps
+    frac = len(heads) / (w.batch * w.num_kv_heads)
+    sample_bytes = dl["bytes"] * frac
+    return dict(value=sample_bytes / el / 1e9, unit="GB/s", cores=used, kind="oracle",
+                sample=f"{len(heads)} of {w.batch * w.num_kv_heads} (batch row, KV head) pairs x {w.group} query heads, "
+                       f"n={n}, query transform + decode, {reps} reps in {el * reps:.1f} s; "
+                       f"step time scaled to the full batch = {el / frac * 1e3:.0f} ms")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every workload runs on a single MI355X); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    dl = run_decode_leg(args)
+    w = dl["workload"]
+    fl = {} if args.no_flush else run_flush_leg(args)
+    achieved = dl["bytes"] / (dl["dec_ms"] * 1e-3) / 1e9
+    traffic = traffic_from_profile("decode_c2_counters.json")
+    value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
+    line = {
+        "metric": "2-bit GQA decode-attention HBM GB/s (% of peak); flush tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dl["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Student-t K/V under per-head covariance, random per-head T_K)",
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": dl["n"],
+                   "quant": "percentile-clipped affine 2-bit K and V", "sink": w.sink, "recent": w.recent,
+                   "chunk": w.chunk, "splits": dl["splits"], "parallelism": "single GPU"},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_breakdown_ms": {"append_flush": round(dl["app_ms"], 5), "query_transform": round(dl["qt_ms"], 5),
+                              "decode_attention": round(dl["dec_ms"], 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode attention (partials + merge, one launch)",
+                     "bytes_per_launch": int(dl["bytes"])},
+    }
+    if fl:
+        line["flush"] = {f"{b}bit": {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_36_layers": round(r["ms"], 3),
+                                     "GB_per_s": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / HBM_PEAK_GBS, 4)}
+                         for b, r in fl.items()}
+    if not args.no_cpu:
+        line["cpu_baseline"] = run_cpu_leg(dl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

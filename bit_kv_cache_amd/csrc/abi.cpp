@@ -1,6 +1,7 @@
 // Host side of libwushkv: argument validation, plane geometry and dispatch of the
 // gfx950 kernels.  Every check runs before anything is enqueued.
 #include <math.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "wushkv_internal.h"
@@ -263,6 +264,9 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void 
   size_t cnt_off = (rows * g.d * 4 + rows * 2 * 4 + 255) / 256 * 256;
   a.counters = (unsigned *)((char *)workspace + cnt_off);
   a.out = out;
+  // WUSHKV_DECODE_KERNEL=generic routes every decode to the generic kernel (cross-checks)
+  const char *kern = getenv("WUSHKV_DECODE_KERNEL");
+  a.force_generic = kern && strcmp(kern, "generic") == 0;
   hipGetLastError();
   if (launch_decode(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
   return hip_status();

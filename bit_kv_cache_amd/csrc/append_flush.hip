@@ -315,7 +315,8 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a) {
     }
   }
 
-  // 5c. V set words: lane = 16c + m, word t; field f = 4a + e <-> token 16a + 4c + e
+  // 5c. V set words: lane = 16c + m, word t; field f = 4a + e <-> token 16a + 4c + e,
+  //     2-bit field at bit 2(f>>1) + 16(f&1), 1-bit field at bit (f>>1) + 8(f&1)
   {
     constexpr int NT = D / 16;
     uint8_t *vb = a.codes_v + bg * a.vcode_bytes + (size_t)set * a.vset_bytes;
@@ -332,9 +333,10 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a) {
         const int r = 16 * (f / 4) + 4 * c + (f % 4);
         if (r < r0 || r >= r1) continue;
         const unsigned code = sm.cv[r][j];
-        w0 = (w0 & ~(3u << (2 * f))) | ((code & 3u) << (2 * f));
-        if (a.bits_v == 3) w1 = (w1 & ~(1u << f)) | (((code >> 2) & 1u) << f);
-        if (a.bits_v == 4) w1 = (w1 & ~(3u << (2 * f))) | (((code >> 2) & 3u) << (2 * f));
+        const int b2 = 2 * (f >> 1) + 16 * (f & 1), b1 = (f >> 1) + 8 * (f & 1);
+        w0 = (w0 & ~(3u << b2)) | ((code & 3u) << b2);
+        if (a.bits_v == 3) w1 = (w1 & ~(1u << b1)) | (((code >> 2) & 1u) << b1);
+        if (a.bits_v == 4) w1 = (w1 & ~(3u << b2)) | (((code >> 2) & 3u) << b2);
       }
       ((unsigned *)vb)[idx] = w0;
       if (a.bits_v == 4) ((unsigned *)(vb + 64 * NT * 4))[idx] = w1;

@@ -1,0 +1,608 @@
+// GQA decode attention over the 2-bit key cache on MFMA (gfx950), head_dim 128,
+// G = 4 or 8 query heads per KV head, 2- or 3-bit values.
+//
+// What it computes is the plain softmax attention of the pages' method: scores
+// (q . k)/sqrt(d) on the FP16 sink and recent tokens and (q~ . x^)/sqrt(d) on the
+// quantized body, q~ = T^{-T} q (WUSH-KV digest, "method key points"); every KV
+// head's codes are read once for its G query heads (review blog, Key Terms: GQA).
+//
+// Per body token the key reconstruction is x^ = s*c + z (affine) or (c - (L-1)/2)*s
+// (QuEST), so q~ . x^ = s*(q~ . c) + z*sum(q~): the per-token parameters come out of
+// the dot product and q~ . c is an integer-code contraction.
+//
+// Grid (ceil(P/4) + 1, B * Hkv), 256 threads.  Each wave of a body workgroup streams
+// the 64-token sets of one KV partition:
+//   QK: v_mfma_i32_16x16x64_i8.  A = one 16-token tile of 2-bit codes spread to
+//       bytes, B = q~ split into three signed 8-bit digits (q~ ~ alpha*(65536 d0 +
+//       256 d1 + d2)), one digit per group of G columns, so the integer dot products
+//       are exact and q~ keeps ~23 bits.  The digit columns are recombined in fp32
+//       with DPP row shifts and the tiles are packed into full 64-lane registers
+//       (lane column = G * tile + head) with bank-masked DPP moves.
+//   softmax: online, base 2, per head; W = p * s_V as an fp16 hi + lo pair.
+//   PV: v_mfma_f32_16x16x32_f16.  A = W (row = tile * G + head, zero outside the
+//       row's own tile), B = value codes read straight from the set layout: a
+//       field pair is one and/or with an fp16 exponent pattern, giving BASE + c;
+//       BASE * sum(W) is removed through the per-head zero term.  W enters as two
+//       MFMAs (hi and lo fp16 parts), so its rounding does not show in the output.
+// The window workgroup takes the FP16 sink + recent tokens on plain fp32 VALU.
+// Each workgroup merges its 4 waves in LDS and writes one partial (m, l, o); the
+// last workgroup of a (b, g) to arrive merges the partials in fixed order.
+#include "wushkv_internal.h"
+
+namespace wushkv {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// DPP encodings (gfx9): row_shl:n = 0x100+n (lane i reads i+n), row_shr:n = 0x110+n
+// (lane i reads i-n), row_ror:n = 0x120+n; bank b = lanes 4b..4b+3 of each row.
+template <int CTRL, int BANK = 0xF>
+__device__ __forceinline__ float dpp(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
+}
+
+struct __align__(16) FastSmem {
+  union {
+    struct {
+      float qt[16][kD];
+      float q[16][kD];
+      float wp[kWaves][16][64];   // window waves: probabilities [head][token]
+    } pre;
+    float o[kWaves][16][kD];      // per wave: rows (tile-phase, head), columns channels
+  } u;
+  float alpha[16], sq[16];
+  float m[kWaves][16], l[kWaves][16], z[kWaves][16];
+  int last;
+};
+
+__device__ __forceinline__ int digit_of(float qt, float inv_alpha, int dg) {
+  int Q = (int)rintf(qt * inv_alpha);
+  int d2 = ((Q + 128) & 255) - 128;
+  int Q1 = (Q - d2) >> 8;
+  int d1 = ((Q1 + 128) & 255) - 128;
+  int d0 = (Q1 - d1) >> 8;
+  return dg == 0 ? d0 : (dg == 1 ? d1 : d2);
+}
+
+__device__ __forceinline__ unsigned pack_h2(float x, float y) {
+  f16x2 v = {(_Float16)x, (_Float16)y};
+  return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ float h_lo(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float h_hi(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+
+template <int K>
+__device__ __forceinline__ unsigned shift_to4(unsigned w) {
+  if constexpr (K == 4) return w;
+  else if constexpr (K < 4) return w << (2 * (4 - K));
+  else return w >> (2 * (K - 4));
+}
+
+template <int K>
+__device__ __forceinline__ unsigned shift_to3(unsigned w) {
+  if constexpr (K == 3) return w;
+  else if constexpr (K < 3) return w << (2 * (3 - K));
+  else return w >> (2 * (K - 3));
+}
+
+// fp16 pair (BASE + c) for the field pair at bits (2k, 2k+16) of a value word.
+// 2-bit: c at mantissa bits 8..9 with exponent 2^2 -> 4 + c.
+// 3-bit: low 2 bits at mantissa 6..7, the third bit at mantissa 8, exponent 2^4 -> 16 + c.
+template <int BV, int K>
+__device__ __forceinline__ unsigned v_pair(unsigned w, unsigned hi) {
+  if constexpr (BV == 2) {
+    return (shift_to4<K>(w) & 0x03000300u) | 0x44004400u;
+  } else {
+    unsigned lo = shift_to3<K>(w) & 0x00C000C0u;
+    unsigned hb = (hi >> K) & 0x01000100u;
+    return lo | hb | 0x4C004C00u;
+  }
+}
+
+template <int BV>
+__device__ __forceinline__ f16x8 v_operand(unsigned w, unsigned hi, int iota) {
+  unsigned r0, r1, r2, r3;
+  if (iota == 0) {
+    r0 = v_pair<BV, 0>(w, hi); r1 = v_pair<BV, 1>(w, hi); r2 = v_pair<BV, 2>(w, hi); r3 = v_pair<BV, 3>(w, hi);
+  } else {
+    r0 = v_pair<BV, 4>(w, hi); r1 = v_pair<BV, 5>(w, hi); r2 = v_pair<BV, 6>(w, hi); r3 = v_pair<BV, 7>(w, hi);
+  }
+  u32x4 r = {r0, r1, r2, r3};
+  return __builtin_bit_cast(f16x8, r);
+}
+
+__device__ __forceinline__ i32x4 k_operand(unsigned w) {
+  i32x4 r;
+  r[0] = (int)(w & 0x03030303u);
+  r[1] = (int)((w >> 2) & 0x03030303u);
+  r[2] = (int)((w >> 4) & 0x03030303u);
+  r[3] = (int)((w >> 6) & 0x03030303u);
+  return r;
+}
+
+template <int G>
+__device__ __forceinline__ float head_max(float x) {
+  if constexpr (G == 4) {
+    x = fmaxf(x, dpp<0x124>(x, x));
+    x = fmaxf(x, dpp<0x128>(x, x));
+  } else {
+    x = fmaxf(x, dpp<0x128>(x, x));
+  }
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+template <int G>
+__device__ __forceinline__ float head_sum(float x) {
+  if constexpr (G == 4) {
+    x += dpp<0x124>(x, x);
+    x += dpp<0x128>(x, x);
+  } else {
+    x += dpp<0x128>(x, x);
+  }
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// One body wave: the sets [s0, s1) of one (b, g).
+template <int G, int BV>
+__device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0, int64_t s1,
+                          f32x4 (&O)[8], float &m_out, float &l_out, float &z_out) {
+  constexpr int TPG = 16 / G;          // tiles per packed register group
+  constexpr int NGRP = 4 / TPG;        // groups per 64-token set
+  constexpr int NMF = (3 * G + 15) / 16;  // QK MFMAs per (tile, k-step)
+  const int lane = threadIdx.x & 63;
+  const int q4 = lane >> 4, col = lane & 15;
+  const int hc = col % G;              // head of this lane's packed column
+  const int tcol = col / G;            // tile within a packed group
+  const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
+  const int Lk = 4, Lv = 1 << BV;
+  constexpr float kBase = BV == 2 ? 4.0f : 16.0f;
+
+  // q~ digits as B operands: column c of MFMA mf holds digit dg of head h
+  i32x4 bq[NMF][2];
+#pragma unroll
+  for (int mf = 0; mf < NMF; ++mf) {
+    int dg, h;
+    bool live;
+    if constexpr (G == 4) { dg = col >> 2; h = col & 3; live = col < 12; }
+    else { dg = mf == 0 ? (col >> 3) : 2; h = col & 7; live = mf == 0 || col < 8; }
+    const float inv_alpha = live ? 1.0f / sm.alpha[h] : 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        unsigned word = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int ch = 16 * (2 * q4 + s) + 4 * bb + k;
+          const int dig = live ? digit_of(sm.u.pre.qt[h][ch], inv_alpha, dg) : 0;
+          word |= ((unsigned)dig & 0xFFu) << (8 * bb);
+        }
+        bq[mf][s][k] = (int)word;
+      }
+    }
+  }
+  const float a_sc = sm.alpha[hc] * 65536.0f * qk_scale;
+  const float b_sc = sm.sq[hc] * qk_scale;
+
+  float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
+  const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
+  const _Float16 *kpar = (const _Float16 *)((const char *)a.par_k + (size_t)bg * a.kpar_bytes);
+  const _Float16 *vpar = (const _Float16 *)((const char *)a.par_v + (size_t)bg * a.vpar_bytes);
+  const bool kq = a.quant_k == WUSHKV_Q_QUEST, vq = a.quant_v == WUSHKV_Q_QUEST;
+
+  for (int64_t set = s0; set < s1; ++set) {
+    const int64_t base = set * kSet;
+    // ---- loads
+    u32x2 kw[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+      kw[T] = __builtin_nontemporal_load((const u32x2 *)(kplane + (size_t)(base + 16 * T + col) * 32 + 8 * q4));
+    const uint8_t *vset = vplane + (size_t)set * a.vset_bytes;
+    u32x4 vw0 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32));
+    u32x4 vw1 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32 + 16));
+    u32x4 vh = {0u, 0u, 0u, 0u};
+    if constexpr (BV == 3) vh = __builtin_nontemporal_load((const u32x4 *)(vset + 64 * 32 + lane * 16));
+    u32x4 kp[NGRP], vp[NGRP];
+#pragma unroll
+    for (int gr = 0; gr < NGRP; ++gr) {
+      const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
+      if (kq) { u32x2 x = *(const u32x2 *)(kpar + t0); kp[gr] = (u32x4){x[0], x[1], 0u, 0u}; }
+      else kp[gr] = *(const u32x4 *)(kpar + 2 * t0);
+      if (vq) { u32x2 x = *(const u32x2 *)(vpar + t0); vp[gr] = (u32x4){x[0], x[1], 0u, 0u}; }
+      else vp[gr] = *(const u32x4 *)(vpar + 2 * t0);
+    }
+
+    // ---- QK on the int8 MFMA, digit recombination, packing
+    float C[NGRP][4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const i32x4 a0 = k_operand(kw[T][0]), a1 = k_operand(kw[T][1]);
+      float r[4];
+      if constexpr (G == 4) {
+        i32x4 d = {0, 0, 0, 0};
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq[0][0], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[0][1], d, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f = (float)d[i];
+          r[i] = fmaf(dpp<0x108>(f, f), 1.0f / 65536.0f, fmaf(dpp<0x104>(f, f), 1.0f / 256.0f, f));
+        }
+      } else {
+        i32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
+        d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq[0][0], d0, 0, 0, 0);
+        d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[0][1], d0, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq[1][0], d1, 0, 0, 0);
+        d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[1][1], d1, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float f = (float)d0[i];
+          r[i] = fmaf((float)d1[i], 1.0f / 65536.0f, fmaf(dpp<0x108>(f, f), 1.0f / 256.0f, f));
+        }
+      }
+      const int gr = T / TPG, tp = T % TPG;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (G == 4) {
+          if (tp == 0) C[gr][i] = r[i];
+          else if (tp == 1) C[gr][i] = dpp<0x114, 0x2>(C[gr][i], r[i]);
+          else if (tp == 2) C[gr][i] = dpp<0x118, 0x4>(C[gr][i], r[i]);
+          else C[gr][i] = dpp<0x11C, 0x8>(C[gr][i], r[i]);
+        } else {
+          if (tp == 0) C[gr][i] = r[i];
+          else C[gr][i] = dpp<0x118, 0xC>(C[gr][i], r[i]);
+        }
+      }
+    }
+
+    // ---- scores and online softmax (base 2)
+    float sc[NGRP][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int gr = 0; gr < NGRP; ++gr) {
+      const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float s_t, z_t;
+        if (kq) {
+          const unsigned pw = kp[gr][i >> 1];
+          s_t = (i & 1) ? h_hi(pw) : h_lo(pw);
+          z_t = -0.5f * (Lk - 1) * s_t;
+        } else {
+          s_t = h_lo(kp[gr][i]);
+          z_t = h_hi(kp[gr][i]);
+        }
+        const bool valid = t0 + i < a.nq;
+        sc[gr][i] = valid ? fmaf(s_t, C[gr][i] * a_sc, z_t * b_sc) : -INFINITY;
+        mx = fmaxf(mx, sc[gr][i]);
+      }
+    }
+    mx = head_max<G>(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__any(alpha != 1.0f)) {
+      l_lane *= alpha;
+      zacc *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int src = (4 * q4 + i) % G;  // packed column of head (4*q4+i) % G, row 0
+        const float f = __shfl(alpha, src);
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) O[ct][i] *= f;
+      }
+    }
+    m_run = m_new;
+
+    unsigned wp[NGRP][2], wl[NGRP][2];
+#pragma unroll
+    for (int gr = 0; gr < NGRP; ++gr) {
+      const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
+      float W[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[gr][i] - m_run);
+        float s_t, z_t;
+        if (vq) {
+          const unsigned pw = vp[gr][i >> 1];
+          s_t = (i & 1) ? h_hi(pw) : h_lo(pw);
+          z_t = -0.5f * (Lv - 1) * s_t;
+        } else {
+          s_t = h_lo(vp[gr][i]);
+          z_t = h_hi(vp[gr][i]);
+        }
+        const bool valid = t0 + i < a.nq;
+        l_lane += p;
+        W[i] = valid ? p * s_t : 0.f;
+        zacc += valid ? p * fmaf(-kBase, s_t, z_t) : 0.f;
+      }
+      // W = hi + lo, both fp16: ~22 bits of weight, so neither the fp16 rounding nor
+      // the BASE offset of the value operand shows in the output
+      wp[gr][0] = pack_h2(W[0], W[1]);
+      wp[gr][1] = pack_h2(W[2], W[3]);
+      wl[gr][0] = pack_h2(W[0] - h_lo(wp[gr][0]), W[1] - h_hi(wp[gr][0]));
+      wl[gr][1] = pack_h2(W[2] - h_lo(wp[gr][1]), W[3] - h_hi(wp[gr][1]));
+    }
+
+    // ---- PV on the f16 MFMA: instruction iota covers tiles 2*iota, 2*iota+1
+    const unsigned vws[8] = {vw0[0], vw0[1], vw0[2], vw0[3], vw1[0], vw1[1], vw1[2], vw1[3]};
+    unsigned hws[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      if constexpr (BV == 3) {
+        const unsigned h16 = (vh[ct >> 1] >> (16 * (ct & 1))) & 0xFFFFu;
+        hws[ct] = ((h16 & 0xFFu) << 8) | ((h16 & 0xFF00u) << 16);
+      } else {
+        hws[ct] = 0u;
+      }
+    }
+#pragma unroll
+    for (int iota = 0; iota < 2; ++iota) {
+      const int T = TPG * ((G == 4) ? 0 : iota) + tcol;  // lane's tile for this instruction's group
+      const int gr = (G == 4) ? 0 : iota;
+      const bool mine = (T >> 1) == iota;
+      const int vp2 = 2 * (T & 1);
+      u32x4 av, al;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        av[v] = (mine && v == vp2) ? wp[gr][0] : ((mine && v == vp2 + 1) ? wp[gr][1] : 0u);
+        al[v] = (mine && v == vp2) ? wl[gr][0] : ((mine && v == vp2 + 1) ? wl[gr][1] : 0u);
+      }
+      const f16x8 Ah = __builtin_bit_cast(f16x8, av);
+      const f16x8 Al = __builtin_bit_cast(f16x8, al);
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const f16x8 Bv = v_operand<BV>(vws[ct], hws[ct], iota);
+        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv, O[ct], 0, 0, 0);
+        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv, O[ct], 0, 0, 0);
+      }
+    }
+  }
+
+  // per-head totals; every lane of a head holds them
+  m_out = m_run;
+  l_out = head_sum<G>(l_lane);
+  z_out = head_sum<G>(zacc);
+}
+
+// One window wave: window-list tokens [t0, t1) (sink tokens first, then recent).
+template <int G>
+__device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t t0, int64_t t1, int w,
+                            float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]) {
+  const int lane = threadIdx.x & 63;
+  const float qk_scale = kLog2e * 0.08838834764831845f;
+  const int64_t ns = a.n < a.S ? a.n : a.S;
+  const _Float16 *sink_k = (const _Float16 *)((const char *)a.sink_k + (size_t)bg * a.sink_bytes);
+  const _Float16 *sink_v = (const _Float16 *)((const char *)a.sink_v + (size_t)bg * a.sink_bytes);
+  const _Float16 *ring_k = (const _Float16 *)((const char *)a.ring_k + (size_t)bg * a.ring_bytes);
+  const _Float16 *ring_v = (const _Float16 *)((const char *)a.ring_v + (size_t)bg * a.ring_bytes);
+  for (int64_t p0 = t0; p0 < t1; p0 += 64) {
+    const int64_t t = p0 + lane;
+    const bool valid = t < t1;
+    const int64_t pos = t < ns ? t : a.S + a.nq + (t - ns);
+    const _Float16 *krow = pos < a.S ? sink_k + pos * kD : ring_k + ((pos - a.S) % (a.R + a.C)) * kD;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+    if (valid) {
+      for (int j = 0; j < kD; j += 8) {
+        const f16x8 kv = *(const f16x8 *)(krow + j);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kf = (float)kv[e];
+#pragma unroll
+          for (int h = 0; h < G; ++h) s[h] = fmaf(sm.u.pre.q[h][j + e], kf, s[h]);
+        }
+      }
+    }
+    const int cnt = (int)((t1 - p0) < 64 ? (t1 - p0) : 64);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sc = valid ? s[h] * qk_scale : -INFINITY;
+      const float mx = wave_max(sc);
+      const float mn = fmaxf(mrun[h], mx);
+      const float al = __builtin_amdgcn_exp2f(mrun[h] - mn);
+      const float p = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
+      lrun[h] = lrun[h] * al + wave_sum(p);
+      mrun[h] = mn;
+      acc[h][0] *= al;
+      acc[h][1] *= al;
+      sm.u.pre.wp[w][h][lane] = p;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int tt = 0; tt < cnt; ++tt) {
+      const int64_t tk = p0 + tt;
+      const int64_t ps = tk < ns ? tk : a.S + a.nq + (tk - ns);
+      const _Float16 *vrow = ps < a.S ? sink_v + ps * kD : ring_v + ((ps - a.S) % (a.R + a.C)) * kD;
+      const f16x2 v2 = *(const f16x2 *)(vrow + 2 * lane);
+      const float v0 = (float)v2[0], v1 = (float)v2[1];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = sm.u.pre.wp[w][h][tt];
+        acc[h][0] = fmaf(p, v0, acc[h][0]);
+        acc[h][1] = fmaf(p, v1, acc[h][1]);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int G, int BV>
+__global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int nwg_body) {
+  __shared__ FastSmem sm;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63;
+  const int bg = blockIdx.y;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int h0 = g * G;
+  const bool window = (int)blockIdx.x == nwg_body;
+
+  for (int i = tid; i < G * kD; i += kThreads) {
+    const int hh = i / kD, j = i % kD;
+    const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
+    sm.u.pre.qt[hh][j] = a.qt[off];
+    sm.u.pre.q[hh][j] = load_in(a.q, a.q_dtype, off);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mxa = 0.f, s = 0.f;
+    for (int j = 0; j < kD; ++j) {
+      const float v = sm.u.pre.qt[tid][j];
+      mxa = fmaxf(mxa, fabsf(v));
+      s += v;
+    }
+    // q~ ~ alpha * Q with |Q| <= 127 * 65536, split into three signed 8-bit digits
+    sm.alpha[tid] = mxa > 0.f ? mxa / (127.0f * 65536.0f) : 1.0f;
+    sm.sq[tid] = s;
+  }
+  __syncthreads();
+
+  float wacc[G][2], wm[G], wl[G];
+  f32x4 O[8];
+  float bm = -INFINITY, bl = 0.f, bz = 0.f;
+  const int part = (int)blockIdx.x * kWaves + w;
+  if (!window) {
+    const int64_t nsets = (a.nq + kSet - 1) / kSet;
+    if (part < a.P) {
+      const int64_t s0 = nsets * part / a.P, s1 = nsets * (part + 1) / a.P;
+      body_wave<G, BV>(a, sm, bg, s0, s1, O, bm, bl, bz);
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) { wacc[h][0] = wacc[h][1] = 0.f; wm[h] = -INFINITY; wl[h] = 0.f; }
+    const int64_t ns = a.n < a.S ? a.n : a.S;
+    const int64_t nw = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+    window_wave<G>(a, sm, bg, nw * w / kWaves, nw * (w + 1) / kWaves, w, wacc, wm, wl);
+  }
+  __syncthreads();  // everyone is done with the q / q~ / probability buffers aliased by u.o
+  if (window) {
+    if (lane < G) { sm.m[w][lane] = wm[lane]; sm.l[w][lane] = wl[lane]; sm.z[w][lane] = 0.f; }
+    for (int r = 0; r < 16; ++r) {
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (r == h) { v0 = wacc[h][0]; v1 = wacc[h][1]; }
+      sm.u.o[w][r][2 * lane] = v0;
+      sm.u.o[w][r][2 * lane + 1] = v1;
+    }
+  } else if (part < a.P) {
+    if (lane < G) { sm.m[w][lane] = bm; sm.l[w][lane] = bl; sm.z[w][lane] = bz; }
+    const int q4 = lane >> 4, col = lane & 15;
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.u.o[w][4 * q4 + i][16 * ct + col] = O[ct][i];
+  } else {
+    if (lane < G) { sm.m[w][lane] = -INFINITY; sm.l[w][lane] = 0.f; sm.z[w][lane] = 0.f; }
+    for (int r = 0; r < 16; ++r) {
+      sm.u.o[w][r][2 * lane] = 0.f;
+      sm.u.o[w][r][2 * lane + 1] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves into this workgroup's partial
+  const int P1 = a.P + 1;
+  for (int i = tid; i < G * kD; i += kThreads) {
+    const int hh = i / kD, j = i % kD;
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww)
+      if (sm.l[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.m[ww][hh]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      if (!(sm.l[ww][hh] > 0.f)) continue;
+      const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
+      float o = sm.z[ww][hh];
+#pragma unroll
+      for (int tp = 0; tp < 16 / G; ++tp) o += sm.u.o[ww][G * tp + hh][j];
+      num = fmaf(f, o, num);
+      den = fmaf(f, sm.l[ww][hh], den);
+    }
+    const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1 + blockIdx.x;
+    a.part_o[row * kD + j] = num;
+    if (j == 0) {
+      a.part_ml[row * 2] = mstar;
+      a.part_ml[row * 2 + 1] = den;
+    }
+  }
+
+  // ---- publish; the last workgroup of this (b, g) merges all partials
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned prev = __hip_atomic_fetch_add(&a.counters[bg], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sm.last = prev == (unsigned)nwg_body;
+  }
+  __syncthreads();
+  if (!sm.last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int nparts = nwg_body + 1;
+  for (int i = tid; i < G * kD; i += kThreads) {
+    const int hh = i / kD, j = i % kD;
+    const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1;
+    float mstar = -INFINITY;
+    for (int p = 0; p < nparts; ++p) {
+      const float *ml = a.part_ml + (row + p) * 2;
+      if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
+    }
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+      const float *ml = a.part_ml + (row + p) * 2;
+      if (!(ml[1] > 0.f)) continue;
+      const float f = __builtin_amdgcn_exp2f(ml[0] - mstar);
+      num = fmaf(f, a.part_o[(row + p) * kD + j], num);
+      den = fmaf(f, ml[1], den);
+    }
+    a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / den;
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+bool decode_fast_supported(const DecodeArgs &a) {
+  return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8);
+}
+
+hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
+  const int nwg = (a.P + kWaves - 1) / kWaves;
+  dim3 grid(nwg + 1, a.B * a.Hkv);
+  if (a.G == 4 && a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2>), grid, dim3(kThreads), 0, s, a, nwg);
+  else if (a.G == 4) hipLaunchKernelGGL((decode_fast_kernel<4, 3>), grid, dim3(kThreads), 0, s, a, nwg);
+  else if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<8, 2>), grid, dim3(kThreads), 0, s, a, nwg);
+  else hipLaunchKernelGGL((decode_fast_kernel<8, 3>), grid, dim3(kThreads), 0, s, a, nwg);
+  return hipGetLastError();
+}
+
+}  // namespace wushkv

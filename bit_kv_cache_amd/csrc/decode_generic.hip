@@ -41,10 +41,11 @@ __device__ __forceinline__ int v_code(const uint8_t *set, int d, int bits, int u
   const int a = u / 16, c = (u / 4) % 4, e = u % 4;
   const int lane = 16 * c + (j % 16), t = j / 16;
   const int f = 4 * a + e;
+  const int b2 = 2 * (f >> 1) + 16 * (f & 1), b1 = (f >> 1) + 8 * (f & 1);
   const int idx = lane * (d / 16) + t;
-  int code = (((const unsigned *)set)[idx] >> (2 * f)) & 3;
-  if (bits == 3) code |= ((((const unsigned short *)(set + 64 * (d / 16) * 4))[idx] >> f) & 1) << 2;
-  if (bits == 4) code |= ((((const unsigned *)(set + 64 * (d / 16) * 4))[idx] >> (2 * f)) & 3) << 2;
+  int code = (((const unsigned *)set)[idx] >> b2) & 3;
+  if (bits == 3) code |= ((((const unsigned short *)(set + 64 * (d / 16) * 4))[idx] >> b1) & 1) << 2;
+  if (bits == 4) code |= ((((const unsigned *)(set + 64 * (d / 16) * 4))[idx] >> b2) & 3) << 2;
   return code;
 }
 
@@ -239,6 +240,7 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+  if (decode_fast_supported(a) && !a.force_generic) return launch_decode_fast(a, s);
   return launch_decode_generic(a, s);
 }
 

@@ -84,12 +84,16 @@ struct DecodeArgs {
   float *part_o, *part_ml;        // workspace: [B][Hq][P+1][d], [B][Hq][P+1][2]
   unsigned *counters;             // [B][Hkv]
   float *out;                     // [B][Hq][d]
+  int force_generic;              // route to the generic kernel (testing hook)
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_flush(const FlushArgs &a, hipStream_t s);
 hipError_t launch_qtransform(const QtArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s);
+bool decode_fast_supported(const DecodeArgs &a);
 
 // Device helpers ------------------------------------------------------------
 

@@ -91,9 +91,10 @@ enum {
  *           plane 1 (bits 3) = d/32 u32, word w bit f = bit 2 of channel 32w+f;
  *           plane 1 (bits 4) = d/16 u32, word w bits 2f..2f+1 = bits 2..3 of channel 16w+f.
  *   V set:  token u = 64*sigma + 16*a + 4*c + e, channel j = 16*t + m go to lane 16*c+m,
- *           field f = 4*a + e.  plane 0 = u32 word [lane*(d/16) + t], bits 2f..2f+1 = low
- *           2 bits; plane 1 (bits 3) = u16 [lane*(d/16) + t] after plane 0, bit f = bit 2;
- *           plane 1 (bits 4) = u32 [lane*(d/16) + t] after plane 0, bits 2f..2f+1 = bits 2..3.
+ *           field f = 4*a + e.  plane 0 = u32 word [lane*(d/16) + t], low 2 bits of the
+ *           code at bit 2*(f>>1) + 16*(f&1); plane 1 (bits 3) = u16 [lane*(d/16) + t] after
+ *           plane 0, bit 2 of the code at bit (f>>1) + 8*(f&1); plane 1 (bits 4) = u32
+ *           [lane*(d/16) + t] after plane 0, bits 2..3 at bit 2*(f>>1) + 16*(f&1).
  * Token p of an n-token cache is a sink token if p < S, a body token if
  * S <= p < S + Q(n) with Q(n) = C * floor(max(0, n - S - R) / C), and a recent
  * token otherwise: the ring holds up to R + C tokens and flushes its oldest C

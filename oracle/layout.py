@@ -15,13 +15,14 @@ K code plane -- token-major rows of d*b/8 bytes (body index u = p - sink):
 
 V code plane -- sets of 64 body tokens, 8*d*b bytes per set.  Token
 u = 64*sigma + 16*a + 4*c + e (a, c, e in 0..3) and channel j = 16*t + m
-(t in 0..d/16-1, m in 0..15) are stored at lane = 16*c + m, field f = 4*a + e:
-  plane 0: u32 words indexed lane*(d/16) + t; bits 2f..2f+1 hold the low two
-           bits of the code.
+(t in 0..d/16-1, m in 0..15) are stored at lane = 16*c + m, field f = 4*a + e.
+Even fields fill the low half of a word and odd fields the high half:
+  plane 0: u32 words indexed lane*(d/16) + t; the low two bits of the code sit
+           at bit 2*(f >> 1) + 16*(f & 1).
   plane 1: b = 3: u16 halfwords indexed lane*(d/16) + t, after plane 0;
-           bit f holds bit 2 of the code.
-           b = 4: u32 words indexed as plane 0, after plane 0; bits 2f..2f+1
-           hold bits 2..3 of the code.
+           bit 2 of the code sits at bit (f >> 1) + 8*(f & 1).
+           b = 4: u32 words indexed as plane 0, after plane 0; bits 2..3 of
+           the code sit at bit 2*(f >> 1) + 16*(f & 1).
 A set that is only partly filled holds zero codes in its unused fields.
 """
 import numpy as np
@@ -88,14 +89,19 @@ def unpack_k(raw, bits, d, T):
 
 
 def _v_index(d):
-    """For each (token-in-set, channel): (lane, t, field)."""
+    """For each (token-in-set, channel): (lane, t, bit of a 2-bit field in a u32,
+    bit of a 1-bit field in a u16)."""
     u = np.arange(SET)[:, None]
     j = np.arange(d)[None, :]
     a, c, e = u // 16, (u // 4) % 4, u % 4
     t, m = j // 16, j % 16
     lane = 16 * c + m
     f = 4 * a + e
-    return np.broadcast_to(lane, (SET, d)), np.broadcast_to(t, (SET, d)), np.broadcast_to(f, (SET, d))
+    b2 = 2 * (f >> 1) + 16 * (f & 1)
+    b1 = (f >> 1) + 8 * (f & 1)
+    shp = (SET, d)
+    return (np.broadcast_to(lane, shp), np.broadcast_to(t, shp), np.broadcast_to(b2, shp),
+            np.broadcast_to(b1, shp))
 
 
 def pack_v(codes, bits):
@@ -105,21 +111,21 @@ def pack_v(codes, bits):
     nset = -(-T // SET)
     full = np.zeros((nset * SET, d), dtype=np.int64)
     full[:T] = codes
-    lane, t, f = _v_index(d)
+    lane, t, b2, b1 = _v_index(d)
     nt = d // 16
     out = []
     for s in range(nset):
         blk = full[s * SET:(s + 1) * SET]
         w0 = np.zeros(64 * nt, dtype=np.uint64)
-        np.bitwise_or.at(w0, (lane * nt + t).ravel(), ((blk & 3).astype(np.uint64) << (2 * f).astype(np.uint64)).ravel())
+        np.bitwise_or.at(w0, (lane * nt + t).ravel(), ((blk & 3).astype(np.uint64) << b2.astype(np.uint64)).ravel())
         parts = [w0.astype("<u4").view(np.uint8)]
         if bits == 3:
             w1 = np.zeros(64 * nt, dtype=np.uint64)
-            np.bitwise_or.at(w1, (lane * nt + t).ravel(), (((blk >> 2) & 1).astype(np.uint64) << f.astype(np.uint64)).ravel())
+            np.bitwise_or.at(w1, (lane * nt + t).ravel(), (((blk >> 2) & 1).astype(np.uint64) << b1.astype(np.uint64)).ravel())
             parts.append(w1.astype("<u2").view(np.uint8))
         elif bits == 4:
             w1 = np.zeros(64 * nt, dtype=np.uint64)
-            np.bitwise_or.at(w1, (lane * nt + t).ravel(), (((blk >> 2) & 3).astype(np.uint64) << (2 * f).astype(np.uint64)).ravel())
+            np.bitwise_or.at(w1, (lane * nt + t).ravel(), (((blk >> 2) & 3).astype(np.uint64) << b2.astype(np.uint64)).ravel())
             parts.append(w1.astype("<u4").view(np.uint8))
         out.append(np.concatenate(parts))
     if not out:
@@ -134,18 +140,18 @@ def unpack_v(raw, bits, d, T):
     nset = -(-T // SET)
     sb = v_set_bytes(d, bits)
     raw = np.ascontiguousarray(np.asarray(raw, dtype=np.uint8).reshape(-1)[: nset * sb]).reshape(nset, sb)
-    lane, t, f = _v_index(d)
+    lane, t, b2, b1 = _v_index(d)
     nt = d // 16
     idx = lane * nt + t
     codes = np.zeros((nset * SET, d), dtype=np.int64)
     for s in range(nset):
         w0 = _words(raw[s, :64 * nt * 4]).astype(np.int64)
-        c = (w0[idx] >> (2 * f)) & 3
+        c = (w0[idx] >> b2) & 3
         if bits == 3:
             w1 = np.frombuffer(raw[s, 64 * nt * 4:].tobytes(), dtype="<u2").astype(np.int64)
-            c |= ((w1[idx] >> f) & 1) << 2
+            c |= ((w1[idx] >> b1) & 1) << 2
         elif bits == 4:
             w1 = _words(raw[s, 64 * nt * 4:]).astype(np.int64)
-            c |= ((w1[idx] >> (2 * f)) & 3) << 2
+            c |= ((w1[idx] >> b2) & 3) << 2
         codes[s * SET:(s + 1) * SET] = c
     return codes[:T]

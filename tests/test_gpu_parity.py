@@ -154,3 +154,22 @@ def test_snapshot_restore_continues_bitwise():
     for s in range(20):
         r.append(1)
         assert torch.equal(r.decode(s)[2], outs[s]), s
+
+
+@pytest.mark.parametrize("wl,P", [("serving", 0), ("serving", 13), ("long", 128), ("layer", 0)])
+def test_fast_decode_matches_generic_kernel(wl, P, monkeypatch):
+    """The MFMA decode and the generic decode agree on the same cache."""
+    w = {"serving": configs.SERVING.scaled(batch=3, context=5000, seed=21),
+         "long": configs.LONG_CONTEXT.scaled(batch=2, context=9000, seed=22),
+         "layer": configs.LAYER_8B.scaled(context=3000, seed=23)}[wl]
+    r = Run(w)
+    r.append(w.context)
+    r.append(1)
+    q, qt, fast = r.decode(0, num_splits=P)
+    monkeypatch.setenv("WUSHKV_DECODE_KERNEL", "generic")
+    _, _, gen_out = r.decode(0, num_splits=P)
+    monkeypatch.delenv("WUSHKV_DECODE_KERNEL")
+    rel = float((fast - gen_out).norm() / gen_out.norm())
+    say(f"[fast vs generic] {wl} P={P} rel-L2 {rel:.3e}")
+    assert rel < 1e-4
+    r.check_decode(q, qt, fast)
