@@ -162,8 +162,6 @@ size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, in
   if (P <= 0 || make_geom(c, &g) != WUSHKV_OK) return 0;
   size_t rows = (size_t)g.B * num_q_heads * (P + 1);
   size_t bytes = rows * g.d * 4 + rows * 2 * 4;
-  bytes = (bytes + 255) / 256 * 256;
-  bytes += (size_t)g.B * g.Hkv * 4;
   return (bytes + 255) / 256 * 256;
 }
 
@@ -261,8 +259,6 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void 
   size_t rows = (size_t)g.B * num_q_heads * (P + 1);
   a.part_o = (float *)workspace;
   a.part_ml = a.part_o + rows * g.d;
-  size_t cnt_off = (rows * g.d * 4 + rows * 2 * 4 + 255) / 256 * 256;
-  a.counters = (unsigned *)((char *)workspace + cnt_off);
   a.out = out;
   // WUSHKV_DECODE_KERNEL=generic routes every decode to the generic kernel (cross-checks)
   const char *kern = getenv("WUSHKV_DECODE_KERNEL");

@@ -21,12 +21,13 @@
 //   softmax: online, base 2, per head; W = p * s_V as an fp16 hi + lo pair.
 //   PV: v_mfma_f32_16x16x32_f16.  A = W (row = tile * G + head, zero outside the
 //       row's own tile), B = value codes read straight from the set layout: a
-//       field pair is one and/or with an fp16 exponent pattern, giving BASE + c;
-//       BASE * sum(W) is removed through the per-head zero term.  W enters as two
-//       MFMAs (hi and lo fp16 parts), so its rounding does not show in the output.
+//       field pair is one and/or with an fp16 exponent pattern, giving BASE + c
+//       (BASE = 4, 16 or 64 by the pair's position); BASE * W is removed exactly
+//       through the per-head zero term.  W enters as two MFMAs (hi and lo fp16
+//       parts), so its rounding does not show in the output.
 // The window workgroup takes the FP16 sink + recent tokens on plain fp32 VALU.
 // Each workgroup merges its 4 waves in LDS and writes one partial (m, l, o); the
-// last workgroup of a (b, g) to arrive merges the partials in fixed order.
+// merge kernel that follows on the stream combines the partials.
 #include "wushkv_internal.h"
 
 namespace wushkv {
@@ -46,6 +47,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // DPP encodings (gfx9): row_shl:n = 0x100+n (lane i reads i+n), row_shr:n = 0x110+n
 // (lane i reads i-n), row_ror:n = 0x120+n; bank b = lanes 4b..4b+3 of each row.
+// acc += src[lane + 4 or 8 in the row] * k as one v_fmac_f32_dpp; a lane whose source
+// lies outside its row keeps acc.  The s_nop 1 gives the two wait states a DPP read
+// needs after a VALU write of its source (the compiler does not see into asm).
+__device__ __forceinline__ void fmac_shl4(float &acc, float src, float k) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_shl:4 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(src), "v"(k));
+}
+__device__ __forceinline__ void fmac_shl8(float &acc, float src, float k) {
+  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_shl:8 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(src), "v"(k));
+}
+
 template <int CTRL, int BANK = 0xF>
 __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
@@ -57,12 +68,12 @@ struct __align__(16) FastSmem {
       float qt[16][kD];
       float q[16][kD];
       float wp[kWaves][16][64];   // window waves: probabilities [head][token]
+      int rows[kWaves][64];       // window waves: row of each token (sign bit: ring)
     } pre;
     float o[kWaves][16][kD];      // per wave: rows (tile-phase, head), columns channels
   } u;
   float alpha[16], sq[16];
   float m[kWaves][16], l[kWaves][16], z[kWaves][16];
-  int last;
 };
 
 __device__ __forceinline__ int digit_of(float qt, float inv_alpha, int dg) {
@@ -82,11 +93,38 @@ __device__ __forceinline__ unsigned pack_h2(float x, float y) {
 __device__ __forceinline__ float h_lo(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
 __device__ __forceinline__ float h_hi(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 
-template <int K>
-__device__ __forceinline__ unsigned shift_to4(unsigned w) {
-  if constexpr (K == 4) return w;
-  else if constexpr (K < 4) return w << (2 * (4 - K));
-  else return w >> (2 * (K - 4));
+// A 32-bit constant held in a VGPR the compiler cannot fold, so masks and exponent
+// patterns feed three-operand VALU forms (gfx9 VOP3 has no literal operand).
+__device__ __forceinline__ unsigned vconst(unsigned c) {
+  unsigned r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+  return r;
+}
+
+// Value-code pair k of a word sits at bits (2k, 2k+16).  With the code at mantissa
+// bits 4-5, 6-7 or 8-9 of an fp16 whose exponent makes that field's unit 1, the
+// fp16 is exactly BASE + c with BASE = 64, 16 or 4.  Pairs 2, 3, 4 are read in place,
+// pairs 5, 6, 7 from w >> 6 and pairs 0, 1 from w << 4, so a word costs two shifts
+// and one and/or per pair.
+struct VConst {
+  unsigned m2, m3, m4, e2, e3, e4;  // masks and exponent patterns of positions 2, 3, 4
+  unsigned m3b, mhi, e3b;           // 3-bit codes: low bits at 6-7, third bit at 8, base 16
+};
+
+__device__ __forceinline__ VConst make_vconst() {
+  VConst c;
+  c.m2 = vconst(0x00300030u); c.e2 = vconst(0x54005400u);
+  c.m3 = vconst(0x00C000C0u); c.e3 = vconst(0x4C004C00u);
+  c.m4 = vconst(0x03000300u); c.e4 = vconst(0x44004400u);
+  c.m3b = c.m3; c.mhi = vconst(0x01000100u); c.e3b = c.e3;
+  return c;
+}
+
+__device__ __forceinline__ unsigned and_or(unsigned x, unsigned m, unsigned o) { return (x & m) | o; }
+
+// BASE of value pair k for 2-bit codes (see above): k = 0,2,5 -> 64; 1,3,6 -> 16; 4,7 -> 4.
+__device__ __forceinline__ float vbase2(int k) {
+  return (k == 4 || k == 7) ? 4.0f : ((k == 1 || k == 3 || k == 6) ? 16.0f : 64.0f);
 }
 
 template <int K>
@@ -96,29 +134,37 @@ __device__ __forceinline__ unsigned shift_to3(unsigned w) {
   else return w >> (2 * (K - 3));
 }
 
-// fp16 pair (BASE + c) for the field pair at bits (2k, 2k+16) of a value word.
-// 2-bit: c at mantissa bits 8..9 with exponent 2^2 -> 4 + c.
 // 3-bit: low 2 bits at mantissa 6..7, the third bit at mantissa 8, exponent 2^4 -> 16 + c.
-template <int BV, int K>
-__device__ __forceinline__ unsigned v_pair(unsigned w, unsigned hi) {
-  if constexpr (BV == 2) {
-    return (shift_to4<K>(w) & 0x03000300u) | 0x44004400u;
-  } else {
-    unsigned lo = shift_to3<K>(w) & 0x00C000C0u;
-    unsigned hb = (hi >> K) & 0x01000100u;
-    return lo | hb | 0x4C004C00u;
-  }
+template <int K>
+__device__ __forceinline__ unsigned v_pair3(unsigned w, unsigned hi, const VConst &c) {
+  return (shift_to3<K>(w) & c.m3b) | ((hi >> K) & c.mhi) | c.e3b;
 }
 
+// B operand of PV instruction iota (pairs 4*iota .. 4*iota+3) from one value word.
 template <int BV>
-__device__ __forceinline__ f16x8 v_operand(unsigned w, unsigned hi, int iota) {
-  unsigned r0, r1, r2, r3;
-  if (iota == 0) {
-    r0 = v_pair<BV, 0>(w, hi); r1 = v_pair<BV, 1>(w, hi); r2 = v_pair<BV, 2>(w, hi); r3 = v_pair<BV, 3>(w, hi);
+__device__ __forceinline__ f16x8 v_operand(unsigned w, unsigned hi, int iota, const VConst &c) {
+  u32x4 r;
+  if constexpr (BV == 2) {
+    if (iota == 0) {
+      const unsigned w4 = w << 4;
+      r[0] = and_or(w4, c.m2, c.e2);   // pair 0
+      r[1] = and_or(w4, c.m3, c.e3);   // pair 1
+      r[2] = and_or(w, c.m2, c.e2);    // pair 2
+      r[3] = and_or(w, c.m3, c.e3);    // pair 3
+    } else {
+      const unsigned w6 = w >> 6;
+      r[0] = and_or(w, c.m4, c.e4);    // pair 4
+      r[1] = and_or(w6, c.m2, c.e2);   // pair 5
+      r[2] = and_or(w6, c.m3, c.e3);   // pair 6
+      r[3] = and_or(w6, c.m4, c.e4);   // pair 7
+    }
   } else {
-    r0 = v_pair<BV, 4>(w, hi); r1 = v_pair<BV, 5>(w, hi); r2 = v_pair<BV, 6>(w, hi); r3 = v_pair<BV, 7>(w, hi);
+    if (iota == 0) {
+      r[0] = v_pair3<0>(w, hi, c); r[1] = v_pair3<1>(w, hi, c); r[2] = v_pair3<2>(w, hi, c); r[3] = v_pair3<3>(w, hi, c);
+    } else {
+      r[0] = v_pair3<4>(w, hi, c); r[1] = v_pair3<5>(w, hi, c); r[2] = v_pair3<6>(w, hi, c); r[3] = v_pair3<7>(w, hi, c);
+    }
   }
-  u32x4 r = {r0, r1, r2, r3};
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -167,6 +213,48 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+template <int NGRP>
+struct SetData {
+  u32x2 kw[4];          // key codes: words 2*q4, 2*q4+1 of rows 16T + col
+  u32x4 vw0, vw1, vh;   // value words of this lane (8 column tiles), 3rd-bit plane
+  u32x4 kp[NGRP], vp[NGRP];  // per-token parameters of this lane's 4 packed tokens
+};
+
+template <int NGRP, int TPG, int BV>
+__device__ __forceinline__ void load_set(const DecodeArgs &a, const uint8_t *kplane, const uint8_t *vplane,
+                                         const _Float16 *kpar, const _Float16 *vpar, int64_t set,
+                                         SetData<NGRP> &d) {
+  const int lane = threadIdx.x & 63;
+  const int q4 = lane >> 4, col = lane & 15;
+  const int G = 16 / TPG;
+  const int tcol = col / G;
+  const int64_t base = set * kSet;
+#pragma unroll
+  for (int T = 0; T < 4; ++T)
+    d.kw[T] = __builtin_nontemporal_load((const u32x2 *)(kplane + (size_t)(base + 16 * T + col) * 32 + 8 * q4));
+  const uint8_t *vset = vplane + (size_t)set * a.vset_bytes;
+  d.vw0 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32));
+  d.vw1 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32 + 16));
+  if constexpr (BV == 3) d.vh = __builtin_nontemporal_load((const u32x4 *)(vset + 64 * 32 + lane * 16));
+  else d.vh = (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int gr = 0; gr < NGRP; ++gr) {
+    const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
+    if (a.quant_k == WUSHKV_Q_QUEST) {
+      const u32x2 x = __builtin_nontemporal_load((const u32x2 *)(kpar + t0));
+      d.kp[gr] = (u32x4){x[0], x[1], 0u, 0u};
+    } else {
+      d.kp[gr] = __builtin_nontemporal_load((const u32x4 *)(kpar + 2 * t0));
+    }
+    if (a.quant_v == WUSHKV_Q_QUEST) {
+      const u32x2 x = __builtin_nontemporal_load((const u32x2 *)(vpar + t0));
+      d.vp[gr] = (u32x4){x[0], x[1], 0u, 0u};
+    } else {
+      d.vp[gr] = __builtin_nontemporal_load((const u32x4 *)(vpar + 2 * t0));
+    }
+  }
+}
+
 // One body wave: the sets [s0, s1) of one (b, g).
 template <int G, int BV>
 __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0, int64_t s1,
@@ -180,7 +268,6 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
   const int tcol = col / G;            // tile within a packed group
   const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int Lk = 4, Lv = 1 << BV;
-  constexpr float kBase = BV == 2 ? 4.0f : 16.0f;
 
   // q~ digits as B operands: column c of MFMA mf holds digit dg of head h
   i32x4 bq[NMF][2];
@@ -208,6 +295,19 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
   }
   const float a_sc = sm.alpha[hc] * 65536.0f * qk_scale;
   const float b_sc = sm.sq[hc] * qk_scale;
+  const VConst vc = make_vconst();
+  // digit weights as VGPR values so the DPP reads fuse into v_fmac_f32_dpp
+  const float inv256 = __uint_as_float(vconst(0x3B800000u));    // 2^-8
+  const float inv65536 = __uint_as_float(vconst(0x37800000u));  // 2^-16
+  // BASE of the value operand that multiplies this lane's weights W[i] of packed
+  // group gr: the lane's tile T sits in PV instruction T/2 at pair 2T + i/2
+  float vbase[NGRP][2];
+#pragma unroll
+  for (int gr = 0; gr < NGRP; ++gr) {
+    const int T = TPG * gr + tcol;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) vbase[gr][hf] = BV == 2 ? vbase2(2 * T + hf) : 16.0f;
+  }
 
   float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
 #pragma unroll
@@ -219,27 +319,15 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
   const _Float16 *vpar = (const _Float16 *)((const char *)a.par_v + (size_t)bg * a.vpar_bytes);
   const bool kq = a.quant_k == WUSHKV_Q_QUEST, vq = a.quant_v == WUSHKV_Q_QUEST;
 
+  SetData<NGRP> cur, nxt;
+  if (s0 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, s0, cur);
   for (int64_t set = s0; set < s1; ++set) {
     const int64_t base = set * kSet;
-    // ---- loads
-    u32x2 kw[4];
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-      kw[T] = __builtin_nontemporal_load((const u32x2 *)(kplane + (size_t)(base + 16 * T + col) * 32 + 8 * q4));
-    const uint8_t *vset = vplane + (size_t)set * a.vset_bytes;
-    u32x4 vw0 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32));
-    u32x4 vw1 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32 + 16));
-    u32x4 vh = {0u, 0u, 0u, 0u};
-    if constexpr (BV == 3) vh = __builtin_nontemporal_load((const u32x4 *)(vset + 64 * 32 + lane * 16));
-    u32x4 kp[NGRP], vp[NGRP];
-#pragma unroll
-    for (int gr = 0; gr < NGRP; ++gr) {
-      const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
-      if (kq) { u32x2 x = *(const u32x2 *)(kpar + t0); kp[gr] = (u32x4){x[0], x[1], 0u, 0u}; }
-      else kp[gr] = *(const u32x4 *)(kpar + 2 * t0);
-      if (vq) { u32x2 x = *(const u32x2 *)(vpar + t0); vp[gr] = (u32x4){x[0], x[1], 0u, 0u}; }
-      else vp[gr] = *(const u32x4 *)(vpar + 2 * t0);
-    }
+    // the next set's codes and parameters are in flight while this one computes
+    if (set + 1 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, set + 1, nxt);
+    const u32x2 *kw = cur.kw;
+    const u32x4 vw0 = cur.vw0, vw1 = cur.vw1, vh = cur.vh;
+    const u32x4 *kp = cur.kp, *vp = cur.vp;
 
     // ---- QK on the int8 MFMA, digit recombination, packing
     float C[NGRP][4];
@@ -253,8 +341,12 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
         d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[0][1], d, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float f = (float)d[i];
-          r[i] = fmaf(dpp<0x108>(f, f), 1.0f / 65536.0f, fmaf(dpp<0x104>(f, f), 1.0f / 256.0f, f));
+          // digit columns h, h+4, h+8 -> lane h; columns 12..15 hold zeros, so the first
+          // step leaves lanes 8..11 (read by the second) unchanged
+          float f = (float)d[i];
+          fmac_shl4(f, f, inv256);
+          fmac_shl8(f, f, inv65536);
+          r[i] = f;
         }
       } else {
         i32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
@@ -264,8 +356,9 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
         d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[1][1], d1, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float f = (float)d0[i];
-          r[i] = fmaf((float)d1[i], 1.0f / 65536.0f, fmaf(dpp<0x108>(f, f), 1.0f / 256.0f, f));
+          float f = (float)d0[i];
+          fmac_shl8(f, f, inv256);
+          r[i] = fmaf((float)d1[i], inv65536, f);
         }
       }
       const int gr = T / TPG, tp = T % TPG;
@@ -341,14 +434,17 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
         const bool valid = t0 + i < a.nq;
         l_lane += p;
         W[i] = valid ? p * s_t : 0.f;
-        zacc += valid ? p * fmaf(-kBase, s_t, z_t) : 0.f;
+        zacc += valid ? p * z_t : 0.f;
       }
-      // W = hi + lo, both fp16: ~22 bits of weight, so neither the fp16 rounding nor
-      // the BASE offset of the value operand shows in the output
+      // W = hi + lo, both fp16 (~22 bits).  The MFMA forms sum (hi + lo) * (BASE + c);
+      // hi + lo is exact in fp32, so BASE * (hi + lo) is taken out exactly.
       wp[gr][0] = pack_h2(W[0], W[1]);
       wp[gr][1] = pack_h2(W[2], W[3]);
       wl[gr][0] = pack_h2(W[0] - h_lo(wp[gr][0]), W[1] - h_hi(wp[gr][0]));
       wl[gr][1] = pack_h2(W[2] - h_lo(wp[gr][1]), W[3] - h_hi(wp[gr][1]));
+      const float s01 = (h_lo(wp[gr][0]) + h_lo(wl[gr][0])) + (h_hi(wp[gr][0]) + h_hi(wl[gr][0]));
+      const float s23 = (h_lo(wp[gr][1]) + h_lo(wl[gr][1])) + (h_hi(wp[gr][1]) + h_hi(wl[gr][1]));
+      zacc = fmaf(-vbase[gr][0], s01, fmaf(-vbase[gr][1], s23, zacc));
     }
 
     // ---- PV on the f16 MFMA: instruction iota covers tiles 2*iota, 2*iota+1
@@ -379,11 +475,12 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
       const f16x8 Al = __builtin_bit_cast(f16x8, al);
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct) {
-        const f16x8 Bv = v_operand<BV>(vws[ct], hws[ct], iota);
+        const f16x8 Bv = v_operand<BV>(vws[ct], hws[ct], iota, vc);
         O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv, O[ct], 0, 0, 0);
         O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv, O[ct], 0, 0, 0);
       }
     }
+    cur = nxt;
   }
 
   // per-head totals; every lane of a head holds them
@@ -392,64 +489,85 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
   z_out = head_sum<G>(zacc);
 }
 
-// One window wave: window-list tokens [t0, t1) (sink tokens first, then recent).
+// One window wave: window-list tokens [t0, t1) (sink tokens first, then recent),
+// plain fp32 VALU.  Scores: lane = token; values: lane = two channels.
 template <int G>
-__device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t t0, int64_t t1, int w,
+__device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, int t1, int w,
                             float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]) {
   const int lane = threadIdx.x & 63;
   const float qk_scale = kLog2e * 0.08838834764831845f;
-  const int64_t ns = a.n < a.S ? a.n : a.S;
+  const int ns = (int)(a.n < a.S ? a.n : a.S);
+  const unsigned ring = (unsigned)(a.R + a.C);
+  const unsigned first_slot = (unsigned)(a.nq % ring);  // slot of the oldest recent token
   const _Float16 *sink_k = (const _Float16 *)((const char *)a.sink_k + (size_t)bg * a.sink_bytes);
   const _Float16 *sink_v = (const _Float16 *)((const char *)a.sink_v + (size_t)bg * a.sink_bytes);
   const _Float16 *ring_k = (const _Float16 *)((const char *)a.ring_k + (size_t)bg * a.ring_bytes);
   const _Float16 *ring_v = (const _Float16 *)((const char *)a.ring_v + (size_t)bg * a.ring_bytes);
-  for (int64_t p0 = t0; p0 < t1; p0 += 64) {
-    const int64_t t = p0 + lane;
+  for (int p0 = t0; p0 < t1; p0 += 64) {
+    const int t = p0 + lane;
     const bool valid = t < t1;
-    const int64_t pos = t < ns ? t : a.S + a.nq + (t - ns);
-    const _Float16 *krow = pos < a.S ? sink_k + pos * kD : ring_k + ((pos - a.S) % (a.R + a.C)) * kD;
+    // row of token t: sink row t, or ring slot (first_slot + t - ns) mod (R + C)
+    const bool is_sink = t < ns;
+    const unsigned row = is_sink ? (unsigned)t : (first_slot + (unsigned)(t - ns)) % ring;
+    sm.u.pre.rows[w][lane] = (int)(is_sink ? row : row | 0x80000000u);
     float s[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) s[h] = 0.f;
     if (valid) {
-      for (int j = 0; j < kD; j += 8) {
-        const f16x8 kv = *(const f16x8 *)(krow + j);
+      const _Float16 *krow = (is_sink ? sink_k : ring_k) + (size_t)row * kD;
+      f16x8 kv[16];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float kf = (float)kv[e];
+      for (int c = 0; c < 16; ++c) kv[c] = *(const f16x8 *)(krow + 8 * c);
 #pragma unroll
-          for (int h = 0; h < G; ++h) s[h] = fmaf(sm.u.pre.q[h][j + e], kf, s[h]);
+      for (int c = 0; c < 16; ++c) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const f32x4 q0 = *(const f32x4 *)&sm.u.pre.q[h][8 * c];
+          const f32x4 q1 = *(const f32x4 *)&sm.u.pre.q[h][8 * c + 4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[h] = fmaf(q0[e], (float)kv[c][e], s[h]);
+            s[h] = fmaf(q1[e], (float)kv[c][4 + e], s[h]);
+          }
         }
       }
     }
-    const int cnt = (int)((t1 - p0) < 64 ? (t1 - p0) : 64);
+    const int cnt = (t1 - p0) < 64 ? (t1 - p0) : 64;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float sc = valid ? s[h] * qk_scale : -INFINITY;
       const float mx = wave_max(sc);
       const float mn = fmaxf(mrun[h], mx);
       const float al = __builtin_amdgcn_exp2f(mrun[h] - mn);
-      const float p = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-      lrun[h] = lrun[h] * al + wave_sum(p);
+      const float pr = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
+      lrun[h] = lrun[h] * al + wave_sum(pr);
       mrun[h] = mn;
       acc[h][0] *= al;
       acc[h][1] *= al;
-      sm.u.pre.wp[w][h][lane] = p;
+      sm.u.pre.wp[w][h][lane] = pr;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int tt = 0; tt < cnt; ++tt) {
-      const int64_t tk = p0 + tt;
-      const int64_t ps = tk < ns ? tk : a.S + a.nq + (tk - ns);
-      const _Float16 *vrow = ps < a.S ? sink_v + ps * kD : ring_v + ((ps - a.S) % (a.R + a.C)) * kD;
-      const f16x2 v2 = *(const f16x2 *)(vrow + 2 * lane);
-      const float v0 = (float)v2[0], v1 = (float)v2[1];
+    for (int tt0 = 0; tt0 < cnt; tt0 += 8) {
+      f16x2 v2[8];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float p = sm.u.pre.wp[w][h][tt];
-        acc[h][0] = fmaf(p, v0, acc[h][0]);
-        acc[h][1] = fmaf(p, v1, acc[h][1]);
+      for (int u = 0; u < 8; ++u) {
+        const int tt = tt0 + u < cnt ? tt0 + u : cnt - 1;
+        const int rr = sm.u.pre.rows[w][tt];
+        const _Float16 *vrow = rr >= 0 ? sink_v + (size_t)rr * kD : ring_v + (size_t)(rr & 0x7FFFFFFF) * kD;
+        v2[u] = *(const f16x2 *)(vrow + 2 * lane);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (tt0 + u >= cnt) break;
+        const float v0 = (float)v2[u][0], v1 = (float)v2[u][1];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float pr = sm.u.pre.wp[w][h][tt0 + u];
+          acc[h][0] = fmaf(pr, v0, acc[h][0]);
+          acc[h][1] = fmaf(pr, v1, acc[h][1]);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -501,7 +619,7 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     for (int h = 0; h < G; ++h) { wacc[h][0] = wacc[h][1] = 0.f; wm[h] = -INFINITY; wl[h] = 0.f; }
     const int64_t ns = a.n < a.S ? a.n : a.S;
     const int64_t nw = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
-    window_wave<G>(a, sm, bg, nw * w / kWaves, nw * (w + 1) / kWaves, w, wacc, wm, wl);
+    window_wave<G>(a, sm, bg, (int)(nw * w / kWaves), (int)(nw * (w + 1) / kWaves), w, wacc, wm, wl);
   }
   __syncthreads();  // everyone is done with the q / q~ / probability buffers aliased by u.o
   if (window) {
@@ -557,36 +675,6 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     }
   }
 
-  // ---- publish; the last workgroup of this (b, g) merges all partials
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev = __hip_atomic_fetch_add(&a.counters[bg], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sm.last = prev == (unsigned)nwg_body;
-  }
-  __syncthreads();
-  if (!sm.last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  const int nparts = nwg_body + 1;
-  for (int i = tid; i < G * kD; i += kThreads) {
-    const int hh = i / kD, j = i % kD;
-    const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1;
-    float mstar = -INFINITY;
-    for (int p = 0; p < nparts; ++p) {
-      const float *ml = a.part_ml + (row + p) * 2;
-      if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
-    }
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-      const float *ml = a.part_ml + (row + p) * 2;
-      if (!(ml[1] > 0.f)) continue;
-      const float f = __builtin_amdgcn_exp2f(ml[0] - mstar);
-      num = fmaf(f, a.part_o[(row + p) * kD + j], num);
-      den = fmaf(f, ml[1], den);
-    }
-    a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / den;
-  }
-  if (tid == 0) __hip_atomic_store(&a.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -594,6 +682,8 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
 bool decode_fast_supported(const DecodeArgs &a) {
   return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8);
 }
+
+int decode_fast_partials(const DecodeArgs &a) { return (a.P + kWaves - 1) / kWaves + 1; }
 
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
   const int nwg = (a.P + kWaves - 1) / kWaves;

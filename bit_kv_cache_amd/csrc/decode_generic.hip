@@ -7,9 +7,8 @@
 // scores for the G query heads of its KV head (raw q on FP16 keys, q~ = T^{-T} q on
 // transformed body keys; WUSH-KV digest, "method key points"), an online softmax
 // in the exp2 domain, and the weighted value sum, and writes a partial
-// (m, l, o).  The last workgroup of each (b, g) to finish -- found with an
-// agent-scope acquire/release counter -- merges the P + 1 partials in fixed order
-// and resets the counter.
+// (m, l, o); merge_kernel, launched next on the same stream, combines the P + 1
+// partials of each (batch row, query head) in fixed order.
 #include "wushkv_internal.h"
 
 namespace wushkv {
@@ -26,7 +25,6 @@ struct GenSmem {
   float s[kMaxG][kSet];        // scores, then probabilities
   float m[kMaxG], l[kMaxG], alpha[kMaxG];
   float pv[kSet][2];           // value parameters of the tile's tokens
-  int is_body;
 };
 
 __device__ __forceinline__ int k_code(const uint8_t *row, int d, int bits, int j) {
@@ -50,7 +48,7 @@ __device__ __forceinline__ int v_code(const uint8_t *set, int d, int bits, int u
 }
 
 __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) {
-  __shared__ GenSmem sm;
+  __shared__ GenSmem sm;  // one partial per workgroup; merge_kernel combines them
   const int tid = threadIdx.x;
   const int part = blockIdx.x;
   const int bg = blockIdx.y;
@@ -200,35 +198,31 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
     ml[0] = sm.m[tid];
     ml[1] = sm.l[tid];
   }
-  // publish, count arrivals; the last workgroup of this (b, g) merges
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) {
-    unsigned prev = __hip_atomic_fetch_add(&a.counters[bg], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    sm.is_body = (prev == (unsigned)a.P);
+}
+
+// Online-softmax merge of the partials of one (batch row, query head), thread =
+// channel: m* = max m_p, out = sum 2^{m_p - m*} o_p / sum 2^{m_p - m*} l_p over the
+// partials with l_p > 0, in fixed partition order.
+__global__ void __launch_bounds__(128) merge_kernel(DecodeArgs a, int nparts) {
+  const int bh = blockIdx.x;
+  const int j = threadIdx.x;
+  if (j >= a.d) return;
+  const int P1 = a.P + 1;
+  const size_t row = (size_t)bh * P1;
+  float mstar = -INFINITY;
+  for (int p = 0; p < nparts; ++p) {
+    const float *ml = a.part_ml + (row + p) * 2;
+    if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
   }
-  __syncthreads();
-  if (!sm.is_body) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int o = tid; o < G * d; o += kThreads) {
-    const int hh = o / d, j = o % d;
-    const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1;
-    float mstar = -INFINITY;
-    for (int p = 0; p < P1; ++p) {
-      const float *ml = a.part_ml + (row + p) * 2;
-      if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
-    }
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < P1; ++p) {
-      const float *ml = a.part_ml + (row + p) * 2;
-      if (!(ml[1] > 0.f)) continue;
-      const float w = __builtin_amdgcn_exp2f(ml[0] - mstar);
-      num = fmaf(w, a.part_o[(row + p) * d + j], num);
-      den = fmaf(w, ml[1], den);
-    }
-    a.out[((size_t)b * a.Hq + h0 + hh) * d + j] = num / den;
+  float num = 0.f, den = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float *ml = a.part_ml + (row + p) * 2;
+    if (!(ml[1] > 0.f)) continue;
+    const float f = __builtin_amdgcn_exp2f(ml[0] - mstar);
+    num = fmaf(f, a.part_o[(row + p) * a.d + j], num);
+    den = fmaf(f, ml[1], den);
   }
-  if (tid == 0) __hip_atomic_store(&a.counters[bg], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a.out[(size_t)bh * a.d + j] = num / den;
 }
 
 }  // namespace
@@ -240,8 +234,18 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
-  if (decode_fast_supported(a) && !a.force_generic) return launch_decode_fast(a, s);
-  return launch_decode_generic(a, s);
+  hipError_t e;
+  int nparts;
+  if (decode_fast_supported(a) && !a.force_generic) {
+    e = launch_decode_fast(a, s);
+    nparts = decode_fast_partials(a);
+  } else {
+    e = launch_decode_generic(a, s);
+    nparts = a.P + 1;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a, nparts);
+  return hipGetLastError();
 }
 
 }  // namespace wushkv

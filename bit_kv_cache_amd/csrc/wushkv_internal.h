@@ -82,7 +82,6 @@ struct DecodeArgs {
   size_t sink_bytes, ring_bytes, kcode_row, kcode_bytes, vset_bytes, vcode_bytes, kpar_bytes, vpar_bytes;
   int bits_k, bits_v, quant_k, quant_v, kpar_n, vpar_n;
   float *part_o, *part_ml;        // workspace: [B][Hq][P+1][d], [B][Hq][P+1][2]
-  unsigned *counters;             // [B][Hkv]
   float *out;                     // [B][Hq][d]
   int force_generic;              // route to the generic kernel (testing hook)
 };
@@ -94,6 +93,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s);
 bool decode_fast_supported(const DecodeArgs &a);
+int decode_fast_partials(const DecodeArgs &a);
 
 // Device helpers ------------------------------------------------------------
 

@@ -135,10 +135,9 @@ int32_t wushkv_decode_num_splits(const wushkv_cache *c, int64_t n_tokens, int32_
                                  int32_t num_splits);
 
 /* Bytes of decode workspace needed for these arguments (0 when invalid).  The
- * workspace holds split-K partials and per-(b, g) arrival counters; its counter
- * region must be zero before its first use (allocate it zero-filled) and every
- * completed call leaves it zero again.  Calls that overlap in time must not share
- * a workspace. */
+ * workspace holds the split-K partials (fp32 [batch][num_q_heads][splits + 1][d]
+ * plus [..][2] maxima and sums); no initialisation is needed.  Calls that overlap
+ * in time must not share a workspace. */
 size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads,
                                      int32_t num_splits);
 
@@ -185,7 +184,7 @@ int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtyp
  *   fp16 value or the dequantized value.  Each KV head's data is read once for all
  *   G query heads of its group.  The body is split into num_splits KV partitions
  *   (0 = library's choice) whose partial (max, sum, weighted values) are merged with
- *   the online-softmax rule inside the same launch.
+ *   the online-softmax rule by a second kernel launched on the same stream.
  *   q      [batch][num_q_heads][d] in q_dtype;  q_t  fp32 [batch][num_q_heads][d]
  *   out    fp32 [batch][num_q_heads][d]
  *   workspace  device buffer of at least wushkv_decode_workspace_bytes() bytes.
