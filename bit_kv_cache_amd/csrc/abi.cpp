@@ -94,18 +94,23 @@ int hip_status() {
   return e == hipSuccess ? WUSHKV_OK : WUSHKV_ERR_HIP;
 }
 
-// Body partitions for a decode: the caller's count, or enough waves to fill the
-// chip (about 2048 resident waves) with at least one 64-token set each.
-int32_t choose_splits(const Geom &g, int64_t nq, int32_t requested) {
-  int64_t nsets = (nq + kSet - 1) / kSet;
-  if (requested > 0) {
-    return requested;
+// KV partitions of a decode: the caller's count, or (library's choice) as many
+// partitions as the GPU holds resident decode waves, rounded up to whole 4-wave
+// workgroups, but never more than there are 64-token body sets.
+int32_t choose_splits(const Geom &g, int64_t nq, int32_t requested, int G) {
+  if (requested > 0) return requested;
+  const int64_t nsets = (nq + kSet - 1) / kSet;
+  int64_t waves = 2048;
+  if (g.d == 128 && g.bits_k == 2 && (g.bits_v == 2 || g.bits_v == 3) && (G == 4 || G == 8)) {
+    const int r = decode_fast_resident_waves(G, g.bits_v);
+    if (r > 0) waves = r;
   }
-  int64_t heads = (int64_t)g.B * g.Hkv;
-  int64_t want = (2048 + heads - 1) / heads;
+  const int64_t heads = (int64_t)g.B * g.Hkv;
+  int64_t want = (waves + heads - 1) / heads;
+  want = (want + 3) / 4 * 4;
+  if (want > nsets) want = nsets;
   if (want < 1) want = 1;
-  if (want > nsets) want = nsets > 0 ? nsets : 1;
-  if (want > 1024) want = 1024;
+  if (want > 4096) want = 4096;
   return (int32_t)want;
 }
 
@@ -153,7 +158,7 @@ int32_t wushkv_decode_num_splits(const wushkv_cache *c, int64_t n_tokens, int32_
   Geom g;
   if (make_geom(c, &g) != WUSHKV_OK) return 0;
   if (n_tokens < 1 || n_tokens > g.cap || num_q_heads < 1 || num_q_heads % g.Hkv || num_splits < 0) return 0;
-  return choose_splits(g, n_quantized(n_tokens, g.S, g.R, g.C), num_splits);
+  return choose_splits(g, n_quantized(n_tokens, g.S, g.R, g.C), num_splits, num_q_heads / g.Hkv);
 }
 
 size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads, int32_t num_splits) {

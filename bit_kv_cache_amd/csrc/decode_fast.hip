@@ -10,8 +10,8 @@
 // (QuEST), so q~ . x^ = s*(q~ . c) + z*sum(q~): the per-token parameters come out of
 // the dot product and q~ . c is an integer-code contraction.
 //
-// Grid (ceil(P/4) + 1, B * Hkv), 256 threads.  Each wave of a body workgroup streams
-// the 64-token sets of one KV partition:
+// Grid (ceil(P/4), B * Hkv), 256 threads.  Each wave streams the 64-token sets of one
+// KV partition:
 //   QK: v_mfma_i32_16x16x64_i8.  A = one 16-token tile of 2-bit codes spread to
 //       bytes, B = q~ split into three signed 8-bit digits (q~ ~ alpha*(65536 d0 +
 //       256 d1 + d2)), one digit per group of G columns, so the integer dot products
@@ -25,7 +25,8 @@
 //       (BASE = 4, 16 or 64 by the pair's position); BASE * W is removed exactly
 //       through the per-head zero term.  W enters as two MFMAs (hi and lo fp16
 //       parts), so its rounding does not show in the output.
-// The window workgroup takes the FP16 sink + recent tokens on plain fp32 VALU.
+// Each partition wave first takes its share of the FP16 sink + recent tokens on
+// plain fp32 VALU, which seeds its softmax state, then streams its body sets.
 // Each workgroup merges its 4 waves in LDS and writes one partial (m, l, o); the
 // merge kernel that follows on the stream combines the partials.
 #include "wushkv_internal.h"
@@ -68,7 +69,6 @@ struct __align__(16) FastSmem {
       float qt[16][kD];
       float q[16][kD];
       float wp[kWaves][16][64];   // window waves: probabilities [head][token]
-      int rows[kWaves][64];       // window waves: row of each token (sign bit: ring)
     } pre;
     float o[kWaves][16][kD];      // per wave: rows (tile-phase, head), columns channels
   } u;
@@ -256,8 +256,14 @@ __device__ __forceinline__ void load_set(const DecodeArgs &a, const uint8_t *kpl
 }
 
 // One body wave: the sets [s0, s1) of one (b, g).
+template <int G>
+__device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, int t1, int w,
+                            float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]);
+
+// One wave of a KV partition: first its share [w0, w1) of the FP16 window tokens on
+// VALU, whose result seeds the online-softmax state, then the body sets [s0, s1).
 template <int G, int BV>
-__device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0, int64_t s1,
+__device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0, int64_t s1, int w0, int w1,
                           f32x4 (&O)[8], float &m_out, float &l_out, float &z_out) {
   constexpr int TPG = 16 / G;          // tiles per packed register group
   constexpr int NGRP = 4 / TPG;        // groups per 64-token set
@@ -309,56 +315,92 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
     for (int hf = 0; hf < 2; ++hf) vbase[gr][hf] = BV == 2 ? vbase2(2 * T + hf) : 16.0f;
   }
 
-  float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
-#pragma unroll
-  for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
   const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
   const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
   const _Float16 *kpar = (const _Float16 *)((const char *)a.par_k + (size_t)bg * a.kpar_bytes);
   const _Float16 *vpar = (const _Float16 *)((const char *)a.par_v + (size_t)bg * a.vpar_bytes);
+  SetData<NGRP> cur, nxt;
+
+  float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (w0 < w1) {
+    const int w = threadIdx.x >> 6;
+    float wacc[G][2], wm[G], wl[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) { wacc[h][0] = wacc[h][1] = 0.f; wm[h] = -INFINITY; wl[h] = 0.f; }
+    window_wave<G>(a, sm, bg, w0, w1, w, wacc, wm, wl);
+    // packed lane layout: head hc's max in every lane of hc, its sum counted once
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      if (hc == h) {
+        m_run = wm[h];
+        l_lane = (q4 == 0 && tcol == 0) ? wl[h] : 0.f;
+      }
+    }
+    // window values -> rows (tile 0, head h) of the PV accumulators, through this
+    // wave's probability buffer (free again after the window pass)
+    float *buf = &sm.u.pre.wp[w][0][0];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      buf[h * kD + 2 * lane] = wacc[h][0];
+      buf[h * kD + 2 * lane + 1] = wacc[h][1];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * q4 + i;
+        O[ct][i] = m < G ? buf[m * kD + 16 * ct + col] : 0.f;
+      }
+    __builtin_amdgcn_wave_barrier();
+  }
+
   const bool kq = a.quant_k == WUSHKV_Q_QUEST, vq = a.quant_v == WUSHKV_Q_QUEST;
 
-  SetData<NGRP> cur, nxt;
-  if (s0 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, s0, cur);
-  for (int64_t set = s0; set < s1; ++set) {
+  // one 64-token set: QK, softmax update, PV
+  auto compute = [&](int64_t set, const SetData<NGRP> &cur) {
     const int64_t base = set * kSet;
-    // the next set's codes and parameters are in flight while this one computes
-    if (set + 1 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, set + 1, nxt);
     const u32x2 *kw = cur.kw;
     const u32x4 vw0 = cur.vw0, vw1 = cur.vw1, vh = cur.vh;
     const u32x4 *kp = cur.kp, *vp = cur.vp;
 
-    // ---- QK on the int8 MFMA, digit recombination, packing
+    // ---- QK on the int8 MFMA (all tiles' first k-step before any second one, so no
+    // MFMA waits on the one just issued), digit recombination, packing
     float C[NGRP][4];
+    i32x4 dq[4][NMF];
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int mf = 0; mf < NMF; ++mf)
+        dq[T][mf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k_operand(kw[T][0]), bq[mf][0], (i32x4){0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int mf = 0; mf < NMF; ++mf)
+        dq[T][mf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k_operand(kw[T][1]), bq[mf][1], dq[T][mf], 0, 0, 0);
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const i32x4 a0 = k_operand(kw[T][0]), a1 = k_operand(kw[T][1]);
       float r[4];
       if constexpr (G == 4) {
-        i32x4 d = {0, 0, 0, 0};
-        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq[0][0], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[0][1], d, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // digit columns h, h+4, h+8 -> lane h; columns 12..15 hold zeros, so the first
           // step leaves lanes 8..11 (read by the second) unchanged
-          float f = (float)d[i];
+          float f = (float)dq[T][0][i];
           fmac_shl4(f, f, inv256);
           fmac_shl8(f, f, inv65536);
           r[i] = f;
         }
       } else {
-        i32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
-        d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq[0][0], d0, 0, 0, 0);
-        d0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[0][1], d0, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, bq[1][0], d1, 0, 0, 0);
-        d1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, bq[1][1], d1, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float f = (float)d0[i];
+          float f = (float)dq[T][0][i];
           fmac_shl8(f, f, inv256);
-          r[i] = fmaf((float)d1[i], inv65536, f);
+          r[i] = fmaf((float)dq[T][1][i], inv65536, f);
         }
       }
       const int gr = T / TPG, tp = T % TPG;
@@ -473,13 +515,27 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
       }
       const f16x8 Ah = __builtin_bit_cast(f16x8, av);
       const f16x8 Al = __builtin_bit_cast(f16x8, al);
+      // four column tiles at a time, hi parts before lo parts: each accumulator's
+      // second MFMA is issued three independent MFMAs after its first
 #pragma unroll
-      for (int ct = 0; ct < 8; ++ct) {
-        const f16x8 Bv = v_operand<BV>(vws[ct], hws[ct], iota, vc);
-        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv, O[ct], 0, 0, 0);
-        O[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv, O[ct], 0, 0, 0);
+      for (int ct0 = 0; ct0 < 8; ct0 += 4) {
+        f16x8 Bv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) Bv[c] = v_operand<BV>(vws[ct0 + c], hws[ct0 + c], iota, vc);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv[c], O[ct0 + c], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv[c], O[ct0 + c], 0, 0, 0);
       }
     }
+  };
+
+  // the next set's codes and parameters are in flight while the current one computes
+  // (one copy of the set body: fewer live registers than an unrolled rotation)
+  if (s0 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, s0, cur);
+  for (int64_t set = s0; set < s1; ++set) {
+    if (set + 1 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, set + 1, nxt);
+    compute(set, cur);
     cur = nxt;
   }
 
@@ -489,50 +545,63 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
   z_out = head_sum<G>(zacc);
 }
 
-// One window wave: window-list tokens [t0, t1) (sink tokens first, then recent),
-// plain fp32 VALU.  Scores: lane = token; values: lane = two channels.
+// Row of window-list token t: sink row t, or the ring slot of the t-th token after the
+// sink (first_slot = slot of the oldest recent token); the sign bit marks the ring.
+__device__ __forceinline__ int window_row(int t, int ns, unsigned first_slot, unsigned ring) {
+  return t < ns ? t : (int)(((first_slot + (unsigned)(t - ns)) % ring) | 0x80000000u);
+}
+
+// One window wave: window-list tokens [t0, t1) (sink tokens first, then recent), on
+// plain fp32 VALU in passes of 16 tokens.  Scores: four lanes per token, 32 channels
+// each, summed over the quad; values: lane = two channels.  A pass issues all of its
+// key and value loads before using any of them.
 template <int G>
 __device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, int t1, int w,
                             float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]) {
   const int lane = threadIdx.x & 63;
+  const int ti = lane >> 2, qq = lane & 3;   // token of the pass, quarter of the channels
   const float qk_scale = kLog2e * 0.08838834764831845f;
   const int ns = (int)(a.n < a.S ? a.n : a.S);
   const unsigned ring = (unsigned)(a.R + a.C);
-  const unsigned first_slot = (unsigned)(a.nq % ring);  // slot of the oldest recent token
+  const unsigned first_slot = (unsigned)(a.nq % ring);
   const _Float16 *sink_k = (const _Float16 *)((const char *)a.sink_k + (size_t)bg * a.sink_bytes);
   const _Float16 *sink_v = (const _Float16 *)((const char *)a.sink_v + (size_t)bg * a.sink_bytes);
   const _Float16 *ring_k = (const _Float16 *)((const char *)a.ring_k + (size_t)bg * a.ring_bytes);
   const _Float16 *ring_v = (const _Float16 *)((const char *)a.ring_v + (size_t)bg * a.ring_bytes);
-  for (int p0 = t0; p0 < t1; p0 += 64) {
-    const int t = p0 + lane;
-    const bool valid = t < t1;
-    // row of token t: sink row t, or ring slot (first_slot + t - ns) mod (R + C)
-    const bool is_sink = t < ns;
-    const unsigned row = is_sink ? (unsigned)t : (first_slot + (unsigned)(t - ns)) % ring;
-    sm.u.pre.rows[w][lane] = (int)(is_sink ? row : row | 0x80000000u);
+  constexpr int kPass = 16;
+  for (int p0 = t0; p0 < t1; p0 += kPass) {
+    const int cnt = (t1 - p0) < kPass ? (t1 - p0) : kPass;
+    const bool valid = ti < cnt;
+    const int rr = window_row(p0 + (valid ? ti : 0), ns, first_slot, ring);
+    const _Float16 *krow = (rr >= 0 ? sink_k + (size_t)rr * kD : ring_k + (size_t)(rr & 0x7FFFFFFF) * kD) + 32 * qq;
+    f16x8 kv[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kv[c] = valid ? *(const f16x8 *)(krow + 8 * c) : (f16x8){};
+    f16x2 vv[kPass];
+#pragma unroll
+    for (int u = 0; u < kPass; ++u) {
+      const int ru = window_row(p0 + (u < cnt ? u : 0), ns, first_slot, ring);
+      const _Float16 *vrow = ru >= 0 ? sink_v + (size_t)ru * kD : ring_v + (size_t)(ru & 0x7FFFFFFF) * kD;
+      vv[u] = u < cnt ? *(const f16x2 *)(vrow + 2 * lane) : (f16x2){};
+    }
     float s[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) s[h] = 0.f;
-    if (valid) {
-      const _Float16 *krow = (is_sink ? sink_k : ring_k) + (size_t)row * kD;
-      f16x8 kv[16];
+    for (int h = 0; h < G; ++h) {
+      float x = 0.f;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) kv[c] = *(const f16x8 *)(krow + 8 * c);
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 q0 = *(const f32x4 *)&sm.u.pre.q[h][32 * qq + 8 * c];
+        const f32x4 q1 = *(const f32x4 *)&sm.u.pre.q[h][32 * qq + 8 * c + 4];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const f32x4 q0 = *(const f32x4 *)&sm.u.pre.q[h][8 * c];
-          const f32x4 q1 = *(const f32x4 *)&sm.u.pre.q[h][8 * c + 4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            s[h] = fmaf(q0[e], (float)kv[c][e], s[h]);
-            s[h] = fmaf(q1[e], (float)kv[c][4 + e], s[h]);
-          }
+        for (int e = 0; e < 4; ++e) {
+          x = fmaf(q0[e], (float)kv[c][e], x);
+          x = fmaf(q1[e], (float)kv[c][4 + e], x);
         }
       }
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      s[h] = x;
     }
-    const int cnt = (t1 - p0) < 64 ? (t1 - p0) : 64;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float sc = valid ? s[h] * qk_scale : -INFINITY;
@@ -540,34 +609,24 @@ __device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, i
       const float mn = fmaxf(mrun[h], mx);
       const float al = __builtin_amdgcn_exp2f(mrun[h] - mn);
       const float pr = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-      lrun[h] = lrun[h] * al + wave_sum(pr);
+      lrun[h] = lrun[h] * al + wave_sum(qq == 0 ? pr : 0.f);
       mrun[h] = mn;
       acc[h][0] *= al;
       acc[h][1] *= al;
-      sm.u.pre.wp[w][h][lane] = pr;
+      if (qq == 0) sm.u.pre.wp[w][h][ti] = pr;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    for (int tt0 = 0; tt0 < cnt; tt0 += 8) {
-      f16x2 v2[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int tt = tt0 + u < cnt ? tt0 + u : cnt - 1;
-        const int rr = sm.u.pre.rows[w][tt];
-        const _Float16 *vrow = rr >= 0 ? sink_v + (size_t)rr * kD : ring_v + (size_t)(rr & 0x7FFFFFFF) * kD;
-        v2[u] = *(const f16x2 *)(vrow + 2 * lane);
-      }
+    for (int u = 0; u < kPass; ++u) {
+      if (u >= cnt) break;
+      const float v0 = (float)vv[u][0], v1 = (float)vv[u][1];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (tt0 + u >= cnt) break;
-        const float v0 = (float)v2[u][0], v1 = (float)v2[u][1];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float pr = sm.u.pre.wp[w][h][tt0 + u];
-          acc[h][0] = fmaf(pr, v0, acc[h][0]);
-          acc[h][1] = fmaf(pr, v1, acc[h][1]);
-        }
+      for (int h = 0; h < G; ++h) {
+        const float pr = sm.u.pre.wp[w][h][u];
+        acc[h][0] = fmaf(pr, v0, acc[h][0]);
+        acc[h][1] = fmaf(pr, v1, acc[h][1]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -582,7 +641,6 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int h0 = g * G;
-  const bool window = (int)blockIdx.x == nwg_body;
 
   for (int i = tid; i < G * kD; i += kThreads) {
     const int hh = i / kD, j = i % kD;
@@ -604,35 +662,19 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
   }
   __syncthreads();
 
-  float wacc[G][2], wm[G], wl[G];
   f32x4 O[8];
   float bm = -INFINITY, bl = 0.f, bz = 0.f;
   const int part = (int)blockIdx.x * kWaves + w;
-  if (!window) {
+  if (part < a.P) {
     const int64_t nsets = (a.nq + kSet - 1) / kSet;
-    if (part < a.P) {
-      const int64_t s0 = nsets * part / a.P, s1 = nsets * (part + 1) / a.P;
-      body_wave<G, BV>(a, sm, bg, s0, s1, O, bm, bl, bz);
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < G; ++h) { wacc[h][0] = wacc[h][1] = 0.f; wm[h] = -INFINITY; wl[h] = 0.f; }
+    const int64_t s0 = nsets * part / a.P, s1 = nsets * (part + 1) / a.P;
     const int64_t ns = a.n < a.S ? a.n : a.S;
     const int64_t nw = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
-    window_wave<G>(a, sm, bg, (int)(nw * w / kWaves), (int)(nw * (w + 1) / kWaves), w, wacc, wm, wl);
+    const int w0 = (int)(nw * part / a.P), w1 = (int)(nw * (part + 1) / a.P);
+    body_wave<G, BV>(a, sm, bg, s0, s1, w0, w1, O, bm, bl, bz);
   }
   __syncthreads();  // everyone is done with the q / q~ / probability buffers aliased by u.o
-  if (window) {
-    if (lane < G) { sm.m[w][lane] = wm[lane]; sm.l[w][lane] = wl[lane]; sm.z[w][lane] = 0.f; }
-    for (int r = 0; r < 16; ++r) {
-      float v0 = 0.f, v1 = 0.f;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (r == h) { v0 = wacc[h][0]; v1 = wacc[h][1]; }
-      sm.u.o[w][r][2 * lane] = v0;
-      sm.u.o[w][r][2 * lane + 1] = v1;
-    }
-  } else if (part < a.P) {
+  if (part < a.P) {
     if (lane < G) { sm.m[w][lane] = bm; sm.l[w][lane] = bl; sm.z[w][lane] = bz; }
     const int q4 = lane >> 4, col = lane & 15;
 #pragma unroll
@@ -683,11 +725,29 @@ bool decode_fast_supported(const DecodeArgs &a) {
   return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8);
 }
 
-int decode_fast_partials(const DecodeArgs &a) { return (a.P + kWaves - 1) / kWaves + 1; }
+int decode_fast_partials(const DecodeArgs &a) { return (a.P + kWaves - 1) / kWaves; }
+
+// Waves of the MFMA decode the GPU holds at once for (G, bits_v); 0 if unknown.
+int decode_fast_resident_waves(int G, int bits_v) {
+  static int cache[2][2] = {{-1, -1}, {-1, -1}};
+  int &c = cache[G == 8][bits_v == 3];
+  if (c >= 0) return c;
+  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2> : (const void *)decode_fast_kernel<4, 3>)
+                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2> : (const void *)decode_fast_kernel<8, 3>);
+  int dev = 0, blocks = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess) {
+    hipGetLastError();
+    return 0;
+  }
+  c = blocks * kWaves * prop.multiProcessorCount;
+  return c;
+}
 
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
   const int nwg = (a.P + kWaves - 1) / kWaves;
-  dim3 grid(nwg + 1, a.B * a.Hkv);
+  dim3 grid(nwg, a.B * a.Hkv);
   if (a.G == 4 && a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2>), grid, dim3(kThreads), 0, s, a, nwg);
   else if (a.G == 4) hipLaunchKernelGGL((decode_fast_kernel<4, 3>), grid, dim3(kThreads), 0, s, a, nwg);
   else if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<8, 2>), grid, dim3(kThreads), 0, s, a, nwg);
