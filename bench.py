@@ -29,12 +29,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
+DECODE_SOURCES = ("decode_fast.hip", "decode_generic.hip", "wushkv_internal.h")
+
+
+def kernel_source_hash(files=DECODE_SOURCES):
+    """Hash of the sources of the decode kernels, to tell whether a committed counter
+    summary was taken on the kernels as they are now."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_kv_cache_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in files:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -237,6 +241,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
+                    help="first copy a MIB-sized device buffer three times: a plain copy of known size, whose "
+                         "FETCH_SIZE / WRITE_SIZE counters calibrate the decode kernel's traffic figures")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -244,6 +251,15 @@ def main():
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_check > 0:
+        n = args.copy_check << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy check: 3 copies of {n} bytes")
+        del src, dst
 
     dl = run_decode_leg(args)
     w = dl["workload"]
