@@ -5,21 +5,16 @@
 // "takeaways" / "method key points": FP16 sink and recent windows, chunked flush;
 // the key transform after RoPE, one d x d product per token).
 //
-// Flush, per workgroup: one (batch row, KV head, 64-token V set).
-//   1. stage the rows' fp16 K and V in LDS (from the ring or the new input);
-//   2. x = T_K k16 on MFMA (v_mfma_f32_16x16x32_f16: fp16 x fp16 products are exact,
-//      accumulation fp32 in four 32-term steps);
-//   3. per-token parameters from LDS: sum of squares (QuEST) or the few smallest /
-//      largest values (percentile-clipped affine), reduced across 4 lanes per row;
-//   4. codes into LDS, then packed: K rows token-major, V words in the set layout
-//      (read-modify-write when the flush covers only part of a set).
+// Flush: per token, x = T_K k16 (keys) on MFMA, the token's quantizer parameters
+// (RMS step or percentile-clipped scale / zero), codes, then K rows and V set words
+// packed and stored.  The kernel's own layout of work is described at flush_kernel.
 #include "wushkv_internal.h"
 
 namespace wushkv {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 
@@ -58,290 +53,607 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
 }
 
 // ------------------------------------------------------------------ flush
+//
+// Workgroup of 4 waves; it stages T_K of its KV head in LDS once and then walks
+// steps of 128 body tokens (two 64-token V sets).  In a step, wave w holds 32
+// tokens as two 16-token tiles.  Lane (q, tok) = (lane / 16, lane % 16) owns
+// channels [CPL*q, CPL*q + CPL) of token tok of each tile, CPL = D / 4, so a
+// token's row sits in the 4 lanes tok, tok+16, tok+32, tok+48 and every per-token
+// reduction is two cross-row exchanges.
+//   keys:   x = T_K k16 on v_mfma_f32_16x16x32_f16 with A = T_K rows (LDS) and
+//           B = the lane's own fp16 channels, so the result D[out channel][token]
+//           lands with lane (q, tok) holding out channels 16*ct + 4*q + i of tok;
+//   values: used as loaded (their fp16 value).
+// Codes go to LDS (keys token-major, values channel-major), then the whole
+// workgroup packs K rows and V set words and writes them with 16-byte stores.
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kStepTok = 128;      // body tokens per workgroup step (two V sets)
+// An element whose scaled value lies within these distances (in bins) of a
+// decision boundary is decided again from its exact value in fp64.  Keys carry
+// the fp32 accumulation error of the MFMA contraction; values only the rounding
+// of the scale's reciprocal and of one product.
+constexpr float kEdgeK = 2e-4f;
+constexpr float kEdgeV = 1e-5f;
 
 template <int D>
 struct FlushSmem {
-  static constexpr int KP = D + 8;         // fp16 row pitch (16 B pad)
-  static constexpr int XP = D + 4;         // fp32 row pitch
-  _Float16 k16[kSet][KP];
-  _Float16 v16[kSet][KP];
-  float x[kSet][XP];                       // transformed keys
-  uint8_t ck[kSet][D];                     // K codes
-  uint8_t cv[kSet][D];                     // V codes
-  float stat[kSet][4][2 * kMaxOrderStats]; // per row, per quarter: smallest / largest
-  float par[2][kSet][2];                   // [K|V][row][scale, zero]
+  static constexpr int TP = D + 8;      // T_K row pitch (halves)
+  static constexpr int KP = D + 16;     // key-code row pitch (bytes; rows stay 16-byte aligned)
+  static constexpr int VP = kSet + 4;   // value-code row pitch (bytes), one row per channel
+  _Float16 t[D][TP];
+  uint8_t kc[kStepTok][KP];
+  uint8_t vc[2][D][VP];
 };
 
-__device__ __forceinline__ void insert_lo(float *lo, int n, float v) {
-  // keep lo[0..n) ascending: the n smallest values seen
-  if (v >= lo[n - 1]) return;
-  int i = n - 1;
-  while (i > 0 && lo[i - 1] > v) { lo[i] = lo[i - 1]; --i; }
-  lo[i] = v;
+// Raw bytes of one lane's CPL channels of one token row, in the input's element size.
+template <int ES, int CPL>
+struct RawSeg {
+  u32x4 r[CPL * ES / 16];
+};
+
+template <int ES, int CPL>
+__device__ __forceinline__ unsigned raw_word(const RawSeg<ES, CPL> &s, int i) {
+  return s.r[i >> 2][i & 3];
 }
 
-__device__ __forceinline__ void insert_hi(float *hi, int n, float v) {
-  // keep hi[0..n) descending: the n largest values seen
-  if (v <= hi[n - 1]) return;
-  int i = n - 1;
-  while (i > 0 && hi[i - 1] < v) { hi[i] = hi[i - 1]; --i; }
-  hi[i] = v;
-}
-
-// Per-row quantizer parameters from the row's values in LDS (4 threads per row).
-// Returns (scale, zero) in fp32 holding fp16-rounded values; QuEST puts the step
-// in scale and leaves zero unused.
-template <int D, bool KEYS>
-__device__ __forceinline__ float row_val(const FlushSmem<D> &sm, int r, int j) {
-  if constexpr (KEYS) return sm.x[r][j];
-  else return (float)sm.v16[r][j];
-}
-
-template <int D, bool KEYS>
-__device__ void row_params(const FlushArgs &a, FlushSmem<D> &sm, int row, int part, int quant, int bits) {
-  const int which = KEYS ? 0 : 1;
-  constexpr int Q = D / 4;
-  const int j0 = part * Q;
-  const int L = 1 << bits;
-  if (quant == WUSHKV_Q_QUEST) {
-    // pairwise: 4 partial sums of Q/4 terms per thread, then across the 4 threads
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+// Load the segment of body token u (valid) from the ring if it was appended by an
+// earlier call, else from the new input.  Returns true for a ring (fp16) row.
+template <int D, int ES>
+__device__ __forceinline__ bool load_seg(const FlushArgs &a, const _Float16 *ring, const void *inp, int bg,
+                                         int b, int g, int64_t u, bool valid, int q, RawSeg<ES, D / 4> &s) {
+  constexpr int CPL = D / 4;
 #pragma unroll
-    for (int j = 0; j < Q; ++j) {
-      float v = row_val<D, KEYS>(sm, row, j0 + j);
-      s[j & 3] = fmaf(v, v, s[j & 3]);
-    }
-    float ss = (s[0] + s[1]) + (s[2] + s[3]);
-    ss += __shfl_xor(ss, 1);
-    ss += __shfl_xor(ss, 2);
-    if (part == 0) {
-      float r = sqrtf(ss / (float)D);
-      float step = (float)(_Float16)(2.0f * a.clip * r / (float)L);
-      sm.par[which][row][0] = step;
-      sm.par[which][row][1] = 0.f;
-    }
-  } else {
-    float lo[kMaxOrderStats], hi[kMaxOrderStats];
+  for (int i = 0; i < CPL * ES / 16; ++i) s.r[i] = (u32x4){0u, 0u, 0u, 0u};
+  if (!valid) return true;   // zeros read as fp16
+  const int64_t p = a.S + u;
+  if (p < a.n_before) {
+    const int64_t slot = (p - a.S) % (a.R + a.C);
+    const u32x4 *src = (const u32x4 *)((const char *)ring + (size_t)bg * a.ring_bytes + ((size_t)slot * D + CPL * q) * 2);
 #pragma unroll
-    for (int i = 0; i < kMaxOrderStats; ++i) { lo[i] = INFINITY; hi[i] = -INFINITY; }
-    const int nl = a.need_lo, nh = a.need_hi;
-    for (int j = 0; j < Q; ++j) {
-      float v = row_val<D, KEYS>(sm, row, j0 + j);
-      insert_lo(lo, nl, v);
-      insert_hi(hi, nh, v);
-    }
-    for (int i = 0; i < nl; ++i) sm.stat[row][part][i] = lo[i];
-    for (int i = 0; i < nh; ++i) sm.stat[row][part][kMaxOrderStats + i] = hi[i];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (part == 0) {
-      for (int p = 1; p < 4; ++p) {
-        for (int i = 0; i < nl; ++i) insert_lo(lo, nl, sm.stat[row][p][i]);
-        for (int i = 0; i < nh; ++i) insert_hi(hi, nh, sm.stat[row][p][kMaxOrderStats + i]);
-      }
-      // sorted ascending xs: xs[k] = lo[k] for small k, xs[D-1-k] = hi[k]
-      float x0 = lo[a.lo_i], x1 = (a.lo_i + 1 < D) ? lo[a.lo_i + 1] : x0;
-      float vlo = (a.lo_i + 1 < D) ? x0 + a.lo_t * (x1 - x0) : x0;
-      int hk = D - 1 - a.hi_i;  // index of xs[hi_i] in hi[]
-      float y0 = hi[hk], y1 = (hk >= 1) ? hi[hk - 1] : y0;
-      float vhi = (a.hi_i + 1 < D) ? y0 + a.hi_t * (y1 - y0) : y0;
-      float scale = (float)(_Float16)((vhi - vlo) / (float)(L - 1));
-      float zero = (float)(_Float16)vlo;
-      sm.par[which][row][0] = scale;
-      sm.par[which][row][1] = zero;
-    }
+    for (int i = 0; i < CPL * 2 / 16; ++i) s.r[i] = src[i];
+    return true;
   }
+  const size_t e0 = (((size_t)b * a.Hkv + g) * a.n_new + (size_t)(p - a.n_before)) * D + CPL * q;
+  const u32x4 *src = (const u32x4 *)((const char *)inp + e0 * ES);
+#pragma unroll
+  for (int i = 0; i < CPL * ES / 16; ++i) s.r[i] = __builtin_nontemporal_load(src + i);
+  return false;
 }
 
-// The exact quantizer input: the transformed key sum_m T[j][m] k16[m] in fp64
-// (fp16 x fp16 products are exact in fp64), or the value's fp16 itself.
-template <int D, bool KEYS>
-__device__ __noinline__ double exact_val(const FlushArgs &a, const FlushSmem<D> &sm, int g, int row, int j) {
-  if constexpr (KEYS) {
-    const _Float16 *T = a.tk + ((size_t)g * D + j) * D;
-    double s = 0.0;
-    for (int m = 0; m < D; ++m) s = fma((double)T[m], (double)sm.k16[row][m], s);
-    return s;
-  } else {
-    return (double)sm.v16[row][j];
-  }
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float f16_lo(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16_hi(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+__device__ __forceinline__ float f16_round(float x) { return (float)(_Float16)x; }
+__device__ __forceinline__ unsigned pack_f16(float x, float y) {
+  f16x2 v = {(_Float16)x, (_Float16)y};
+  return __builtin_bit_cast(unsigned, v);
 }
 
-// Codes from the fp32 value; an element whose scaled value lies within kEdge bins
-// of a decision boundary is decided again from the exact input in fp64, so the
-// code is that of the exact transformed key whatever the fp32 rounding did.
-constexpr float kEdge = 2e-4f;
-
-template <int D, bool KEYS>
-__device__ void quantize_row_part(const FlushArgs &a, FlushSmem<D> &sm, int g, int row, int part, int quant, int bits) {
-  const int which = KEYS ? 0 : 1;
-  uint8_t (*codes)[D] = KEYS ? sm.ck : sm.cv;
-  constexpr int Q = D / 4;
-  const int L = 1 << bits;
-  const float sc = sm.par[which][row][0], z = sm.par[which][row][1];
-  if (quant == WUSHKV_Q_QUEST) {
-    if (sc == 0.f) {
-      for (int j = 0; j < Q; ++j) codes[row][part * Q + j] = (uint8_t)(L / 2);
-      return;
-    }
-    const float inv = 1.0f / sc;
-    for (int j = 0; j < Q; ++j) {
-      float v = row_val<D, KEYS>(sm, row, part * Q + j);
-      float t = fmaf(v, inv, (float)(L / 2));
-      float c = floorf(t);
-      if (t - c < kEdge || c + 1.0f - t < kEdge) {
-        double td = exact_val<D, KEYS>(a, sm, g, row, part * Q + j) / (double)sc + (double)(L / 2);
-        c = (float)floor(td);
-      }
-      c = fminf(fmaxf(c, 0.f), (float)(L - 1));
-      codes[row][part * Q + j] = (uint8_t)c;
+// The segment as fp16 pairs (the key's fp16 value, round-to-nearest-even).
+template <int ES, int CPL>
+__device__ __forceinline__ void seg_half2(const RawSeg<ES, CPL> &s, bool ring, int dt, unsigned (&h)[CPL / 2]) {
+  if (ring || (ES == 2 && dt == WUSHKV_DT_F16)) {
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) h[i] = raw_word(s, i);
+  } else if (ES == 2) {
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) {
+      const unsigned w = raw_word(s, i);
+      h[i] = pack_f16(bf16_lo(w), bf16_hi(w));
     }
   } else {
-    if (sc == 0.f) {
-      for (int j = 0; j < Q; ++j) codes[row][part * Q + j] = 0;
-      return;
-    }
-    const float inv = 1.0f / sc;
-    for (int j = 0; j < Q; ++j) {
-      float v = row_val<D, KEYS>(sm, row, part * Q + j);
-      float t = (v - z) * inv;
-      float c = rintf(t);
-      if (fabsf(t - floorf(t) - 0.5f) < kEdge) {
-        double td = (exact_val<D, KEYS>(a, sm, g, row, part * Q + j) - (double)z) / (double)sc;
-        c = (float)rint(td);
-      }
-      c = fminf(fmaxf(c, 0.f), (float)(L - 1));
-      codes[row][part * Q + j] = (uint8_t)c;
-    }
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i)
+      h[i] = pack_f16(__uint_as_float(raw_word(s, 2 * i)), __uint_as_float(raw_word(s, 2 * i + 1)));
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a) {
+// The segment as floats holding the fp16 values.
+template <int ES, int CPL>
+__device__ __forceinline__ void seg_float(const RawSeg<ES, CPL> &s, bool ring, int dt, float (&x)[CPL]) {
+  if (ring || (ES == 2 && dt == WUSHKV_DT_F16)) {
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) {
+      const unsigned w = raw_word(s, i);
+      x[2 * i] = f16_lo(w);
+      x[2 * i + 1] = f16_hi(w);
+    }
+  } else if (ES == 2) {
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) {
+      const unsigned w = raw_word(s, i);
+      x[2 * i] = f16_round(bf16_lo(w));
+      x[2 * i + 1] = f16_round(bf16_hi(w));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) x[i] = f16_round(__uint_as_float(raw_word(s, i)));
+  }
+}
+
+// ---- per-token parameters; the 4 lanes of a token exchange through lanes ^16, ^32
+
+template <int NL>
+struct OrderStats {
+  float lo[NL > 0 ? NL : 1], hi[NL > 0 ? NL : 1];  // lo ascending, hi descending
+};
+
+template <int NL>
+__device__ __forceinline__ void os_init(OrderStats<NL> &o) {
+#pragma unroll
+  for (int k = 0; k < NL; ++k) { o.lo[k] = INFINITY; o.hi[k] = -INFINITY; }
+}
+
+template <int NL>
+__device__ __forceinline__ void os_insert(OrderStats<NL> &o, float v) {
+#pragma unroll
+  for (int k = NL - 1; k > 0; --k) o.lo[k] = __builtin_amdgcn_fmed3f(o.lo[k - 1], o.lo[k], v);
+  o.lo[0] = fminf(o.lo[0], v);
+#pragma unroll
+  for (int k = NL - 1; k > 0; --k) o.hi[k] = __builtin_amdgcn_fmed3f(o.hi[k - 1], o.hi[k], v);
+  o.hi[0] = fmaxf(o.hi[0], v);
+}
+
+// Keep the NL smallest / largest of this lane's lists and those of lane ^ mask:
+// pairing a[k] with b[NL-1-k] leaves a bitonic sequence of the NL extremes, which
+// a bitonic merge sorts.
+template <int NL>
+__device__ __forceinline__ void os_merge(OrderStats<NL> &o, int mask) {
+  float bl[NL], bh[NL];
+#pragma unroll
+  for (int k = 0; k < NL; ++k) { bl[k] = __shfl_xor(o.lo[k], mask); bh[k] = __shfl_xor(o.hi[k], mask); }
+#pragma unroll
+  for (int k = 0; k < NL; ++k) { o.lo[k] = fminf(o.lo[k], bl[NL - 1 - k]); o.hi[k] = fmaxf(o.hi[k], bh[NL - 1 - k]); }
+  constexpr int LOG = NL >= 8 ? 3 : (NL >= 4 ? 2 : (NL >= 2 ? 1 : 0));
+#pragma unroll
+  for (int ls = LOG - 1; ls >= 0; --ls)
+#pragma unroll
+    for (int k = 0; k < NL; ++k)
+      if ((k & (1 << ls)) == 0) {
+        const int st = 1 << ls;
+        const float x = o.lo[k], y = o.lo[k + st];
+        o.lo[k] = fminf(x, y); o.lo[k + st] = fmaxf(x, y);
+        const float u = o.hi[k], v = o.hi[k + st];
+        o.hi[k] = fmaxf(u, v); o.hi[k + st] = fminf(u, v);
+      }
+}
+
+template <int NL>
+__device__ __forceinline__ float pick(const float (&x)[NL > 0 ? NL : 1], int i) {
+  // a select chain kept in registers (the empty asm stops it being turned into an
+  // indexed scratch load)
+  float r = x[0];
+#pragma unroll
+  for (int k = 1; k < NL; ++k) {
+    float c = x[k];
+    asm("" : "+v"(c));
+    r = (i == k) ? c : r;
+  }
+  return r;
+}
+
+// (scale, zero) of a row from its merged order statistics: linear interpolation at
+// virtual index (D-1)*pct/100 between sorted values, both rounded to fp16.
+template <int D, int NL>
+__device__ __forceinline__ void affine_from_stats(const FlushArgs &a, const OrderStats<NL> &o, int L, float &sc, float &zp) {
+  const float x0 = pick<NL>(o.lo, a.lo_i);
+  const float x1 = (a.lo_i + 1 < D) ? pick<NL>(o.lo, a.lo_i + 1) : x0;
+  const float vlo = (a.lo_i + 1 < D) ? x0 + a.lo_t * (x1 - x0) : x0;
+  const int hk = D - 1 - a.hi_i;
+  const float y0 = pick<NL>(o.hi, hk);
+  const float y1 = (hk >= 1) ? pick<NL>(o.hi, hk - 1) : y0;
+  const float vhi = (a.hi_i + 1 < D) ? y0 + a.hi_t * (y1 - y0) : y0;
+  sc = f16_round((vhi - vlo) / (float)(L - 1));
+  zp = f16_round(vlo);
+}
+
+__device__ __forceinline__ float quest_step(float ss, float clip, int L, int D) {
+  return f16_round(2.0f * clip * sqrtf(ss / (float)D) / (float)L);
+}
+
+// Exact code of a value known in fp64.
+__device__ __forceinline__ int exact_code(double x, float sc, float zp, int quant, int L) {
+  double t;
+  if (quant == WUSHKV_Q_QUEST) t = floor(x / (double)sc + (double)(L / 2));
+  else t = rint((x - (double)zp) / (double)sc);
+  return (int)fmin(fmax(t, 0.0), (double)(L - 1));
+}
+
+// Code of x as a float and the distance terms of the boundary test.
+struct Quant {
+  float inv, add, top;
+  bool quest;
+};
+
+__device__ __forceinline__ Quant make_quant(float sc, float zp, int quant, int L) {
+  Quant q;
+  q.quest = quant == WUSHKV_Q_QUEST;
+  q.top = (float)(L - 1);
+  if (q.quest) {
+    q.inv = sc != 0.f ? 1.0f / sc : 0.f;
+    q.add = (float)(L / 2);
+  } else {
+    q.inv = sc != 0.f ? 1.0f / sc : 0.f;
+    q.add = zp;
+  }
+  return q;
+}
+
+// QuEST: t = x/step + L/2, code floor(t); affine: t = (x - z)/s, code rint(t).
+// `edge` accumulates the largest |fraction - 1/2| (QuEST) or |t - rint(t)| (affine).
+__device__ __forceinline__ float code_of(const Quant &q, float x, float &edge) {
+  float c;
+  if (q.quest) {
+    const float t = fmaf(x, q.inv, q.add);
+    c = floorf(t);
+    edge = fmaxf(edge, fabsf(t - c - 0.5f));
+  } else {
+    const float t = (x - q.add) * q.inv;
+    c = rintf(t);
+    edge = fmaxf(edge, fabsf(t - c));
+  }
+  return __builtin_amdgcn_fmed3f(c, 0.f, q.top);
+}
+
+__device__ __forceinline__ bool near_edge(const Quant &q, float edge, float tol) {
+  if (q.inv == 0.f) return false;
+  return edge > 0.5f - tol;
+}
+
+// DPP quad permutations (gfx9 quad_perm): lane i of a quad reads lane i^2 / i^1.
+__device__ __forceinline__ unsigned quad_xor2(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ unsigned quad_xor1(unsigned x) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+}
+
+// 4 x 4 byte transpose across a quad: lane e holds bytes [x_e0..x_e3] in, lane r
+// holds [x_0r..x_3r] out (two exchanges: 16-bit halves with lane ^2, bytes with ^1).
+__device__ __forceinline__ unsigned quad_transpose(unsigned x, unsigned selA, unsigned selB) {
+  x = __builtin_amdgcn_perm(quad_xor2(x), x, selA);
+  return __builtin_amdgcn_perm(quad_xor1(x), x, selB);
+}
+
+// V set word fields from a dword of 4 tokens' codes (bytes e = 0..3 of one channel):
+// low 2 bits of e at bit 4*(e>>1)... i.e. e0 -> 0, e2 -> 2, e1 -> 16, e3 -> 18.
+__device__ __forceinline__ unsigned vfield2(unsigned x) {
+  const unsigned m = x & 0x03030303u;
+  const unsigned p = __builtin_amdgcn_perm(m, m, 0x03010200u);  // bytes [e0, e2, e1, e3]
+  return (p | (p >> 6)) & 0x000F000Fu;
+}
+// Third bit (bit 2 of the code) of e at e0 -> 0, e2 -> 1, e1 -> 8, e3 -> 9.
+__device__ __forceinline__ unsigned vfield1(unsigned x) {
+  const unsigned n = (x >> 2) & 0x01010101u;
+  const unsigned p = __builtin_amdgcn_perm(n, n, 0x03010200u);
+  const unsigned y = (p | (p >> 7)) & 0x00030003u;
+  return (y | (y >> 8)) & 0x0303u;
+}
+// K row packing: 4 consecutive channels' codes (bytes) -> 8 bits (2 bits each).
+__device__ __forceinline__ unsigned kpack2(unsigned x) {
+  const unsigned m = x & 0x03030303u;
+  const unsigned y = (m | (m >> 6)) & 0x000F000Fu;
+  return (y | (y >> 12)) & 0xFFu;
+}
+// ... bit 2 of each of 4 codes -> 4 bits.
+__device__ __forceinline__ unsigned kpack1(unsigned x) {
+  const unsigned n = (x >> 2) & 0x01010101u;
+  const unsigned y = (n | (n >> 7)) & 0x00030003u;
+  return (y | (y >> 14)) & 0xFu;
+}
+
+template <int D, int ES, int NL>
+__global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_per_wg) {
+  constexpr int CPL = D / 4, KS = D / 32, NCT = D / 16;
   __shared__ FlushSmem<D> sm;
-  const int tid = threadIdx.x;
-  const int bg = blockIdx.y;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
-  const int64_t set = a.u0 / kSet + blockIdx.x;
-  const int64_t base = set * kSet;                  // body index of row 0
-  const int64_t r0 = a.u0 > base ? a.u0 - base : 0; // rows [r0, r1) of this set are flushed
-  const int64_t r1 = (a.u1 < base + kSet) ? a.u1 - base : kSet;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = lane >> 4, tok = lane & 15;
+  const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
+  const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
+  const int64_t s_first = a.u0 / kSet, s_end = (a.u1 + kSet - 1) / kSet;
 
-  // 1. stage fp16 K and V rows
-  for (int idx = tid; idx < kSet * D; idx += kThreads) {
-    const int r = idx / D, j = idx % D;
-    _Float16 hk = (_Float16)0.f, hv = (_Float16)0.f;
-    if (r >= r0 && r < r1) {
-      const int64_t p = a.S + base + r;
-      if (p < a.n_before) {
-        const int64_t slot = (p - a.S) % (a.R + a.C);
-        hk = ((const _Float16 *)((const char *)a.ring_k + bg * a.ring_bytes))[slot * D + j];
-        hv = ((const _Float16 *)((const char *)a.ring_v + bg * a.ring_bytes))[slot * D + j];
-      } else {
-        const size_t src = (((size_t)b * a.Hkv + g) * a.n_new + (p - a.n_before)) * D + j;
-        hk = (_Float16)load_in(a.k_new, a.in_dtype, src);
-        hv = (_Float16)load_in(a.v_new, a.in_dtype, src);
-      }
-    }
-    sm.k16[r][j] = hk;
-    sm.v16[r][j] = hv;
-  }
-  __syncthreads();
-
-  // 2. x = k16 T^T on MFMA: tiles of 16 rows x 16 output channels, K = D
   {
-    const int wave = tid / 64, lane = tid % 64;
-    const int lq = lane / 16, lr = lane % 16;
     const _Float16 *T = a.tk + (size_t)g * D * D;
-    constexpr int CT = D / 16;
-    for (int tile = wave; tile < 4 * CT; tile += 4) {
-      const int rt = tile / CT, ct = tile % CT;
-      float4v acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        half8 av = *(const half8 *)&sm.k16[rt * 16 + lr][32 * s + 8 * lq];
-        half8 bv = *(const half8 *)&T[(size_t)(ct * 16 + lr) * D + 32 * s + 8 * lq];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sm.x[rt * 16 + 4 * lq + i][ct * 16 + lr] = acc[i];
+    for (int i = tid; i < D * D / 8; i += kThreads) {
+      const int r = i / (D / 8), c8 = i % (D / 8);
+      *(u32x4 *)&sm.t[r][8 * c8] = *(const u32x4 *)(T + (size_t)r * D + 8 * c8);
     }
   }
+  // quad-transpose selectors of this lane (position e = tok & 3 in its quad)
+  const unsigned selA = (tok & 2) ? 0x03020706u : 0x05040100u;
+  const unsigned selB = (tok & 1) ? 0x03070105u : 0x06020400u;
   __syncthreads();
 
-  // 3. parameters: 4 threads per row (adjacent lanes)
-  const int row = tid / 4, part = tid % 4;
-  row_params<D, true>(a, sm, row, part, a.quant_k, a.bits_k);
-  row_params<D, false>(a, sm, row, part, a.quant_v, a.bits_v);
-  __syncthreads();
+  for (int64_t st = (int64_t)blockIdx.x * steps_per_wg; st < (int64_t)(blockIdx.x + 1) * steps_per_wg; ++st) {
+    const int64_t set0 = s_first + 2 * st;
+    if (set0 >= s_end) break;
+    const int64_t ubase = set0 * kSet + 32 * wave;   // this wave's first token
 
-  // 4. codes
-  quantize_row_part<D, true>(a, sm, g, row, part, a.quant_k, a.bits_k);
-  quantize_row_part<D, false>(a, sm, g, row, part, a.quant_v, a.bits_v);
-  __syncthreads();
+    // ---- loads: keys and values of both tiles
+    RawSeg<ES, CPL> rk[2], rv[2];
+    bool kring[2], vring[2], valid[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t u = ubase + 16 * tt + tok;
+      valid[tt] = u >= a.u0 && u < a.u1;
+      kring[tt] = load_seg<D, ES>(a, a.ring_k, a.k_new, bg, b, g, u, valid[tt], q, rk[tt]);
+      vring[tt] = load_seg<D, ES>(a, a.ring_v, a.v_new, bg, b, g, u, valid[tt], q, rv[tt]);
+    }
 
-  // 5a. parameters out
-  if (tid < kSet && tid >= r0 && tid < r1) {
-    const int64_t u = base + tid;
-    _Float16 *pk = (_Float16 *)((char *)a.par_k + bg * a.kpar_bytes) + u * a.kpar_n;
-    _Float16 *pv = (_Float16 *)((char *)a.par_v + bg * a.vpar_bytes) + u * a.vpar_n;
-    pk[0] = (_Float16)sm.par[0][tid][0];
-    if (a.kpar_n == 2) pk[1] = (_Float16)sm.par[0][tid][1];
-    pv[0] = (_Float16)sm.par[1][tid][0];
-    if (a.vpar_n == 2) pv[1] = (_Float16)sm.par[1][tid][1];
-  }
-
-  // 5b. K rows: plane 0 words (16 channels), then plane 1
-  {
-    constexpr int W0 = D / 16;
-    const int w1n = a.bits_k == 3 ? D / 32 : (a.bits_k == 4 ? D / 16 : 0);
-    const int wrow = W0 + w1n;
-    uint8_t *kb = a.codes_k + bg * a.kcode_bytes;
-    for (int idx = tid; idx < kSet * wrow; idx += kThreads) {
-      const int r = idx / wrow, w = idx % wrow;
-      if (r < r0 || r >= r1) continue;
-      unsigned word = 0;
-      if (w < W0) {
-        for (int f = 0; f < 16; ++f) word |= (unsigned)(sm.ck[r][16 * w + f] & 3) << (2 * f);
-      } else if (a.bits_k == 3) {
-        const int ww = w - W0;
-        for (int f = 0; f < 32; ++f) word |= (unsigned)((sm.ck[r][32 * ww + f] >> 2) & 1) << f;
+    // ---- keys, one tile at a time: x = T_K k16 on MFMA, parameters, codes
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      unsigned kh[CPL / 2];
+      seg_half2<ES, CPL>(rk[tt], kring[tt], a.in_dtype, kh);
+      f32x4 acc[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const half8 A = *(const half8 *)&sm.t[16 * ct + tok][CPL * q + 8 * s];
+          const u32x4 bw = {kh[4 * s], kh[4 * s + 1], kh[4 * s + 2], kh[4 * s + 3]};
+          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8, bw), acc[ct], 0, 0, 0);
+        }
+      }
+      const int row = 32 * wave + 16 * tt + tok;
+      const int64_t u = ubase + 16 * tt + tok;
+      // parameters
+      float sc, zp = 0.f;
+      if (a.quant_k == WUSHKV_Q_QUEST) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s4[i] = fmaf(acc[ct][i], acc[ct][i], s4[i]);
+        float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        sc = quest_step(ss, a.clip, Lk, D);
       } else {
-        const int ww = w - W0;
-        for (int f = 0; f < 16; ++f) word |= (unsigned)((sm.ck[r][16 * ww + f] >> 2) & 3) << (2 * f);
+        if constexpr (NL > 0) {
+          OrderStats<NL> o;
+          os_init(o);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) os_insert(o, acc[ct][i]);
+          os_merge(o, 16);
+          os_merge(o, 32);
+          affine_from_stats<D, NL>(a, o, Lk, sc, zp);
+        } else {
+          sc = 0.f;
+        }
       }
-      *(unsigned *)(kb + (size_t)(base + r) * a.kcode_row + 4 * w) = word;
+      if (q == 0 && valid[tt]) {
+        _Float16 *pk = (_Float16 *)((char *)a.par_k + (size_t)bg * a.kpar_bytes) + u * a.kpar_n;
+        if (a.kpar_n == 2) *(unsigned *)pk = pack_f16(sc, zp);
+        else pk[0] = (_Float16)sc;
+      }
+      // codes
+      const Quant qk = make_quant(sc, zp, a.quant_k, Lk);
+      float edge = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        unsigned w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_cvt_pk_u8_f32(code_of(qk, acc[ct][i], edge), i, w);
+        *(unsigned *)&sm.kc[row][16 * ct + 4 * q] = w;
+      }
+      // elements near a boundary: the 4 lanes of a token take one candidate at a
+      // time, each summing its CPL channels' exact products in fp64
+      const bool kn = valid[tt] && near_edge(qk, edge, kEdgeK);
+      if (__any(kn)) {
+        unsigned m = 0;
+        if (kn) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float e1 = 0.f;
+              code_of(qk, acc[ct][i], e1);
+              if (e1 > 0.5f - kEdgeK) m |= 1u << (4 * ct + i);
+            }
+        }
+        while (__any(m != 0)) {
+          const unsigned m0 = __shfl(m, tok), m1 = __shfl(m, 16 + tok), m2 = __shfl(m, 32 + tok), m3 = __shfl(m, 48 + tok);
+          const int qs = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : (m3 ? 3 : -1)));
+          const unsigned mm = qs == 0 ? m0 : (qs == 1 ? m1 : (qs == 2 ? m2 : m3));
+          const int bit = qs >= 0 ? __builtin_ctz(mm) : 0;
+          const int j = 16 * (bit >> 2) + 4 * (qs >= 0 ? qs : 0) + (bit & 3);
+          double part = 0.0;
+#pragma unroll
+          for (int s = 0; s < CPL / 8; ++s) {
+            const half8 tv = *(const half8 *)&sm.t[j][CPL * q + 8 * s];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const unsigned w = kh[4 * s + e / 2];
+              const float kv = (e & 1) ? f16_hi(w) : f16_lo(w);
+              part += (double)((float)tv[e] * kv);   // fp16 x fp16 is exact in fp32
+            }
+          }
+          part += __shfl_xor(part, 16);
+          part += __shfl_xor(part, 32);
+          if (qs == q) {
+            sm.kc[row][j] = (uint8_t)exact_code(part, sc, zp, a.quant_k, Lk);
+            m &= ~(1u << bit);
+          }
+        }
+      }
     }
-  }
 
-  // 5c. V set words: lane = 16c + m, word t; field f = 4a + e <-> token 16a + 4c + e,
-  //     2-bit field at bit 2(f>>1) + 16(f&1), 1-bit field at bit (f>>1) + 8(f&1)
-  {
-    constexpr int NT = D / 16;
-    uint8_t *vb = a.codes_v + bg * a.vcode_bytes + (size_t)set * a.vset_bytes;
-    const bool full = (r0 == 0 && r1 == kSet);
-    for (int idx = tid; idx < 64 * NT; idx += kThreads) {
-      const int lanei = idx / NT, t = idx % NT;
-      const int c = lanei / 16, m = lanei % 16;
-      const int j = 16 * t + m;
-      unsigned w0 = full ? 0u : ((unsigned *)vb)[idx];
-      unsigned w1 = 0;
-      if (a.bits_v == 4) w1 = full ? 0u : ((unsigned *)(vb + 64 * NT * 4))[idx];
-      if (a.bits_v == 3) w1 = full ? 0u : ((unsigned short *)(vb + 64 * NT * 4))[idx];
-      for (int f = 0; f < 16; ++f) {
-        const int r = 16 * (f / 4) + 4 * c + (f % 4);
-        if (r < r0 || r >= r1) continue;
-        const unsigned code = sm.cv[r][j];
-        const int b2 = 2 * (f >> 1) + 16 * (f & 1), b1 = (f >> 1) + 8 * (f & 1);
-        w0 = (w0 & ~(3u << b2)) | ((code & 3u) << b2);
-        if (a.bits_v == 3) w1 = (w1 & ~(1u << b1)) | (((code >> 2) & 1u) << b1);
-        if (a.bits_v == 4) w1 = (w1 & ~(3u << b2)) | (((code >> 2) & 3u) << b2);
+    // ---- values
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float xv[CPL];
+      seg_float<ES, CPL>(rv[tt], vring[tt], a.in_dtype, xv);
+      const int64_t u = ubase + 16 * tt + tok;
+      float sc, zp = 0.f;
+      if (a.quant_v == WUSHKV_Q_QUEST) {
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) s4[k & 3] = fmaf(xv[k], xv[k], s4[k & 3]);
+        float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        sc = quest_step(ss, a.clip, Lv, D);
+      } else {
+        if constexpr (NL > 0) {
+          OrderStats<NL> o;
+          os_init(o);
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) os_insert(o, xv[k]);
+          os_merge(o, 16);
+          os_merge(o, 32);
+          affine_from_stats<D, NL>(a, o, Lv, sc, zp);
+        } else {
+          sc = 0.f;
+        }
       }
-      ((unsigned *)vb)[idx] = w0;
-      if (a.bits_v == 4) ((unsigned *)(vb + 64 * NT * 4))[idx] = w1;
-      if (a.bits_v == 3) ((unsigned short *)(vb + 64 * NT * 4))[idx] = (unsigned short)w1;
+      if (q == 0 && valid[tt]) {
+        _Float16 *pv = (_Float16 *)((char *)a.par_v + (size_t)bg * a.vpar_bytes) + u * a.vpar_n;
+        if (a.vpar_n == 2) *(unsigned *)pv = pack_f16(sc, zp);
+        else pv[0] = (_Float16)sc;
+      }
+      const Quant qv = make_quant(sc, zp, a.quant_v, Lv);
+      float edge = 0.f;
+      const int s2 = wave >> 1;                       // set of this wave within the step
+      const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
+#pragma unroll
+      for (int g4 = 0; g4 < CPL / 4; ++g4) {
+        unsigned w = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) w = __builtin_amdgcn_cvt_pk_u8_f32(code_of(qv, xv[4 * g4 + r], edge), r, w);
+        // lane tok = 4c + e now gets channel 4*g4 + e of tokens 4c .. 4c+3
+        w = quad_transpose(w, selA, selB);
+        *(unsigned *)&sm.vc[s2][CPL * q + 4 * g4 + (tok & 3)][col + 4 * (tok >> 2)] = w;
+      }
+      const bool vn = valid[tt] && near_edge(qv, edge, kEdgeV);
+      if (__any(vn)) {
+        if (vn) {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) {
+            float e1 = 0.f;
+            code_of(qv, xv[k], e1);
+            if (e1 > 0.5f - kEdgeV) sm.vc[s2][CPL * q + k][col + tok] = (uint8_t)exact_code((double)xv[k], sc, zp, a.quant_v, Lv);
+          }
+        }
+      }
     }
+    __syncthreads();
+
+    // ---- K rows: two threads per token, D/2 channels each
+    {
+      const int r = tid >> 1, h = tid & 1;
+      const int64_t u = set0 * kSet + r;
+      if (u >= a.u0 && u < a.u1) {
+        constexpr int HC = D / 2;
+        uint8_t *rowp = a.codes_k + (size_t)bg * a.kcode_bytes + (size_t)u * a.kcode_row;
+        u32x4 cw[HC / 16];
+#pragma unroll
+        for (int i = 0; i < HC / 16; ++i) cw[i] = *(const u32x4 *)&sm.kc[r][HC * h + 16 * i];
+        unsigned p0[HC / 16];
+#pragma unroll
+        for (int k = 0; k < HC / 16; ++k)
+          p0[k] = kpack2(cw[k][0]) | (kpack2(cw[k][1]) << 8) | (kpack2(cw[k][2]) << 16) | (kpack2(cw[k][3]) << 24);
+        if constexpr (HC / 16 == 4) *(u32x4 *)(rowp + 16 * h) = (u32x4){p0[0], p0[1], p0[2], p0[3]};
+        else *(u32x2 *)(rowp + 8 * h) = (u32x2){p0[0], p0[1]};
+        if (a.bits_k == 3) {
+          unsigned p1[HC / 32];
+#pragma unroll
+          for (int k = 0; k < HC / 32; ++k) {
+            unsigned w = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w |= kpack1(cw[2 * k + e / 4][e % 4]) << (4 * e);
+            p1[k] = w;
+          }
+          if constexpr (HC / 32 == 2) *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p1[0], p1[1]};
+          else *(unsigned *)(rowp + D / 4 + 4 * h) = p1[0];
+        } else if (a.bits_k == 4) {
+#pragma unroll
+          for (int k = 0; k < HC / 16; ++k)
+            p0[k] = kpack2(cw[k][0] >> 2) | (kpack2(cw[k][1] >> 2) << 8) | (kpack2(cw[k][2] >> 2) << 16) |
+                    (kpack2(cw[k][3] >> 2) << 24);
+          if constexpr (HC / 16 == 4) *(u32x4 *)(rowp + D / 4 + 16 * h) = (u32x4){p0[0], p0[1], p0[2], p0[3]};
+          else *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p0[0], p0[1]};
+        }
+      }
+    }
+
+    // ---- V set words: 128 threads per set, 4 consecutive words each
+    {
+      constexpr int NT = D / 16, NW = 64 * NT;
+      const int s2 = tid >> 7, t128 = tid & 127;
+      const int64_t sidx = set0 + s2;
+      const int64_t base = sidx * kSet;
+      const int64_t lo = a.u0 > base ? a.u0 : base;
+      const int64_t hi = a.u1 < base + kSet ? a.u1 : base + kSet;
+      if (lo < hi && 4 * t128 < NW) {
+        const int r0 = (int)(lo - base), r1 = (int)(hi - base);
+        const bool full = r0 == 0 && r1 == kSet;
+        uint8_t *vb = a.codes_v + (size_t)bg * a.vcode_bytes + (size_t)sidx * a.vset_bytes;
+        unsigned w0[4], w1[4], k0[4], k1[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int wi = 4 * t128 + jj;
+          const int ln = wi / NT, t = wi % NT;
+          const int c = ln >> 4, j = 16 * t + (ln & 15);
+          w0[jj] = w1[jj] = k0[jj] = k1[jj] = 0u;
+#pragma unroll
+          for (int aa = 0; aa < 4; ++aa) {
+            const unsigned x = *(const unsigned *)&sm.vc[s2][j][16 * aa + 4 * c];
+            w0[jj] |= vfield2(x) << (4 * aa);
+            if (a.bits_v == 3) w1[jj] |= vfield1(x) << (2 * aa);
+            if (a.bits_v == 4) w1[jj] |= vfield2(x >> 2) << (4 * aa);
+            if (!full) {
+              unsigned vm = 0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int r = 16 * aa + 4 * c + e;
+                if (r >= r0 && r < r1) vm |= 0x0Fu << (8 * e);
+              }
+              k0[jj] |= vfield2(vm) << (4 * aa);
+              if (a.bits_v == 3) k1[jj] |= vfield1(vm) << (2 * aa);
+              if (a.bits_v == 4) k1[jj] |= vfield2(vm >> 2) << (4 * aa);
+            }
+          }
+        }
+        u32x4 *p0 = (u32x4 *)(vb + 16 * t128);
+        if (full) {
+          *p0 = (u32x4){w0[0], w0[1], w0[2], w0[3]};
+        } else {
+          u32x4 old = *p0;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) old[jj] = (old[jj] & ~k0[jj]) | (w0[jj] & k0[jj]);
+          *p0 = old;
+        }
+        if (a.bits_v == 3) {
+          u32x2 *p1 = (u32x2 *)(vb + 4 * NW + 8 * t128);
+          u32x2 nw = {w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16)};
+          if (!full) {
+            const u32x2 mk = {k1[0] | (k1[1] << 16), k1[2] | (k1[3] << 16)};
+            const u32x2 old = *p1;
+            nw = (old & ~mk) | (nw & mk);
+          }
+          *p1 = nw;
+        } else if (a.bits_v == 4) {
+          u32x4 *p1 = (u32x4 *)(vb + 4 * NW + 16 * t128);
+          u32x4 nw = {w1[0], w1[1], w1[2], w1[3]};
+          if (!full) {
+            const u32x4 old = *p1;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) nw[jj] = (old[jj] & ~k1[jj]) | (nw[jj] & k1[jj]);
+          }
+          *p1 = nw;
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -356,11 +668,34 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   const int64_t s0 = a.u0 / kSet, s1 = (a.u1 + kSet - 1) / kSet;
-  dim3 grid((unsigned)(s1 - s0), a.B * a.Hkv);
-  if (a.d == 128)
-    hipLaunchKernelGGL(flush_kernel<128>, grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(flush_kernel<64>, grid, dim3(kThreads), 0, s, a);
+  const int64_t steps = (s1 - s0 + 1) / 2;
+  const int64_t heads = (int64_t)a.B * a.Hkv;
+  // about 2048 workgroups (four rounds of the two that fit per CU); each walks a
+  // contiguous run of steps of one KV head, so T_K is staged once per run
+  int64_t spw = steps * heads / 2048;
+  if (spw < 1) spw = 1;
+  dim3 grid((unsigned)((steps + spw - 1) / spw), (unsigned)heads);
+  int need = 0;
+  if (a.quant_k == WUSHKV_Q_AFFINE_PCT || a.quant_v == WUSHKV_Q_AFFINE_PCT)
+    need = a.need_lo > a.need_hi ? a.need_lo : a.need_hi;
+  const int nl = need == 0 ? 0 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
+  const bool f32 = a.in_dtype == WUSHKV_DT_F32;
+  const int sp = (int)spw;
+#define WUSHKV_FLUSH(D, ES, NL) hipLaunchKernelGGL((flush_kernel<D, ES, NL>), grid, dim3(kThreads), 0, s, a, sp)
+#define WUSHKV_FLUSH_NL(D, ES)            \
+  switch (nl) {                            \
+    case 0: WUSHKV_FLUSH(D, ES, 0); break; \
+    case 2: WUSHKV_FLUSH(D, ES, 2); break; \
+    case 4: WUSHKV_FLUSH(D, ES, 4); break; \
+    default: WUSHKV_FLUSH(D, ES, 8); break; \
+  }
+  if (a.d == 128) {
+    if (f32) { WUSHKV_FLUSH_NL(128, 4) } else { WUSHKV_FLUSH_NL(128, 2) }
+  } else {
+    if (f32) { WUSHKV_FLUSH_NL(64, 4) } else { WUSHKV_FLUSH_NL(64, 2) }
+  }
+#undef WUSHKV_FLUSH_NL
+#undef WUSHKV_FLUSH
   return hipGetLastError();
 }
 
