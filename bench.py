@@ -158,7 +158,8 @@ def run_flush_leg(args):
     kv = [gen.kv_tensors(w, l, n, dev) for l in range(layers)]
     tks = [gen.key_transforms(w, l)[0].to(dev) for l in range(layers)]
     res = {}
-    for bits in w.flush_bits:
+    bits_list = [int(b) for b in args.flush_bits.split(",")] if args.flush_bits else list(w.flush_bits)
+    for bits in bits_list:
         spec = W.CacheSpec(batch=1, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=n,
                            sink=w.sink, recent=w.recent, chunk=w.chunk, bits_k=bits, bits_v=bits,
                            quant_k=W.Q_QUEST, quant_v=W.Q_QUEST)
@@ -241,6 +242,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (profiling the flush alone)")
+    ap.add_argument("--flush-bits", type=str, default="", help="comma-separated bit widths of the flush leg")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-sized device buffer three times: a plain copy of known size, whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the decode kernel's traffic figures")
@@ -261,6 +264,10 @@ def main():
         log(f"[bench] copy check: 3 copies of {n} bytes")
         del src, dst
 
+    if args.no_decode:
+        fl = run_flush_leg(args)
+        print(json.dumps({"flush": {f"{b}bit": r for b, r in fl.items()}}), flush=True)
+        return
     dl = run_decode_leg(args)
     w = dl["workload"]
     fl = {} if args.no_flush else run_flush_leg(args)

@@ -8,6 +8,8 @@
 // Flush: per token, x = T_K k16 (keys) on MFMA, the token's quantizer parameters
 // (RMS step or percentile-clipped scale / zero), codes, then K rows and V set words
 // packed and stored.  The kernel's own layout of work is described at flush_kernel.
+#include <type_traits>
+
 #include "wushkv_internal.h"
 
 namespace wushkv {
@@ -74,9 +76,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kStepTok = 128;      // body tokens per workgroup step (two V sets)
 // An element whose scaled value lies within these distances (in bins) of a
 // decision boundary is decided again from its exact value in fp64.  Keys carry
-// the fp32 accumulation error of the MFMA contraction; values only the rounding
-// of the scale's reciprocal and of one product.
-constexpr float kEdgeK = 2e-4f;
+// the fp32 accumulation error of the MFMA contraction (at most 6.2e-6 bins at 4
+// bits, 1.5e-6 at 2 bits, over 1.3e8 transformed keys of the bulk-flush
+// workload); values only the rounding of the scale's reciprocal and of one product.
+constexpr float kEdgeK = 5e-5f;
 constexpr float kEdgeV = 1e-5f;
 
 template <int D>
@@ -264,45 +267,72 @@ __device__ __forceinline__ int exact_code(double x, float sc, float zp, int quan
   return (int)fmin(fmax(t, 0.0), (double)(L - 1));
 }
 
-// Code of x as a float and the distance terms of the boundary test.
+// Quantizer of one row.  QuEST: t = x/step + L/2, code floor(t).  Affine: t = (x - z)/s,
+// code rint(t) (half to even).  Codes are clamped to [0, L-1].  The boundary test
+// tracks, over the row, the smallest and largest fraction t - floor(t) (QuEST) or
+// the largest |t - rint(t)| (affine); a zero step / scale gives the degenerate code
+// (L/2, resp. 0) and no boundary.
+template <bool QU>
 struct Quant {
   float inv, add, top;
-  bool quest;
 };
 
-__device__ __forceinline__ Quant make_quant(float sc, float zp, int quant, int L) {
-  Quant q;
-  q.quest = quant == WUSHKV_Q_QUEST;
+template <bool QU>
+__device__ __forceinline__ Quant<QU> make_quant(float sc, float zp, int L) {
+  Quant<QU> q;
+  q.inv = sc != 0.f ? 1.0f / sc : 0.f;
+  q.add = QU ? (float)(L / 2) : zp;
   q.top = (float)(L - 1);
-  if (q.quest) {
-    q.inv = sc != 0.f ? 1.0f / sc : 0.f;
-    q.add = (float)(L / 2);
-  } else {
-    q.inv = sc != 0.f ? 1.0f / sc : 0.f;
-    q.add = zp;
-  }
   return q;
 }
 
-// QuEST: t = x/step + L/2, code floor(t); affine: t = (x - z)/s, code rint(t).
-// `edge` accumulates the largest |fraction - 1/2| (QuEST) or |t - rint(t)| (affine).
-__device__ __forceinline__ float code_of(const Quant &q, float x, float &edge) {
-  float c;
-  if (q.quest) {
-    const float t = fmaf(x, q.inv, q.add);
-    c = floorf(t);
-    edge = fmaxf(edge, fabsf(t - c - 0.5f));
-  } else {
-    const float t = (x - q.add) * q.inv;
-    c = rintf(t);
-    edge = fmaxf(edge, fabsf(t - c));
-  }
-  return __builtin_amdgcn_fmed3f(c, 0.f, q.top);
+struct Edge {
+  float lo, hi;
+};
+
+__device__ __forceinline__ Edge edge_init() { return Edge{1.0f, 0.0f}; }
+
+template <bool QU>
+__device__ __forceinline__ float scaled(const Quant<QU> &q, float x) {
+  return QU ? fmaf(x, q.inv, q.add) : (x - q.add) * q.inv;
 }
 
-__device__ __forceinline__ bool near_edge(const Quant &q, float edge, float tol) {
+// Codes of two values; the fraction extrema of both enter the edge in one
+// three-operand min / max.
+template <bool QU>
+__device__ __forceinline__ void code2(const Quant<QU> &q, float x0, float x1, Edge &e, float &c0, float &c1) {
+  const float t0 = scaled(q, x0), t1 = scaled(q, x1);
+  if constexpr (QU) {
+    const float f0 = floorf(t0), f1 = floorf(t1);
+    const float r0 = t0 - f0, r1 = t1 - f1;
+    e.lo = fminf(e.lo, fminf(r0, r1));
+    e.hi = fmaxf(e.hi, fmaxf(r0, r1));
+    c0 = f0; c1 = f1;
+  } else {
+    const float f0 = rintf(t0), f1 = rintf(t1);
+    e.hi = fmaxf(e.hi, fmaxf(fabsf(t0 - f0), fabsf(t1 - f1)));
+    c0 = f0; c1 = f1;
+  }
+  c0 = __builtin_amdgcn_fmed3f(c0, 0.f, q.top);
+  c1 = __builtin_amdgcn_fmed3f(c1, 0.f, q.top);
+}
+
+template <bool QU>
+__device__ __forceinline__ bool edge_near(const Quant<QU> &q, const Edge &e, float tol) {
   if (q.inv == 0.f) return false;
-  return edge > 0.5f - tol;
+  return QU ? (e.lo < tol || e.hi > 1.0f - tol) : (e.hi > 0.5f - tol);
+}
+
+// The same test for one value.
+template <bool QU>
+__device__ __forceinline__ bool value_near(const Quant<QU> &q, float x, float tol) {
+  const float t = scaled(q, x);
+  if constexpr (QU) {
+    const float r = t - floorf(t);
+    return r < tol || r > 1.0f - tol;
+  } else {
+    return fabsf(t - rintf(t)) > 0.5f - tol;
+  }
 }
 
 // DPP quad permutations (gfx9 quad_perm): lane i of a quad reads lane i^2 / i^1.
@@ -348,15 +378,33 @@ __device__ __forceinline__ unsigned kpack1(unsigned x) {
 }
 
 template <int D, int ES, int NL>
-__global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_per_wg) {
+__global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int steps_per_wg) {
   constexpr int CPL = D / 4, KS = D / 32, NCT = D / 16;
+  using QuestTag = std::integral_constant<bool, true>;
+  using AffineTag = std::integral_constant<bool, false>;
   __shared__ FlushSmem<D> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, tok = lane & 15;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
   const int64_t s_first = a.u0 / kSet, s_end = (a.u1 + kSet - 1) / kSet;
+  const int64_t nsteps = (s_end - s_first + 1) / 2;
+  const int64_t st0 = (int64_t)blockIdx.x * steps_per_wg;
+  const int64_t st1 = st0 + steps_per_wg < nsteps ? st0 + steps_per_wg : nsteps;
 
+  RawSeg<ES, CPL> rk[2], rv[2];
+  bool kring[2], vring[2], valid[2];
+  auto issue_loads = [&](int64_t st) {
+    const int64_t ub = (s_first + 2 * st) * kSet + 32 * wave;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int64_t u = ub + 16 * tt + tok;
+      valid[tt] = u >= a.u0 && u < a.u1;
+      kring[tt] = load_seg<D, ES>(a, a.ring_k, a.k_new, bg, b, g, u, valid[tt], q, rk[tt]);
+      vring[tt] = load_seg<D, ES>(a, a.ring_v, a.v_new, bg, b, g, u, valid[tt], q, rv[tt]);
+    }
+  };
+  if (st0 < st1) issue_loads(st0);   // in flight while T_K is staged
   {
     const _Float16 *T = a.tk + (size_t)g * D * D;
     for (int i = tid; i < D * D / 8; i += kThreads) {
@@ -369,21 +417,9 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_
   const unsigned selB = (tok & 1) ? 0x03070105u : 0x06020400u;
   __syncthreads();
 
-  for (int64_t st = (int64_t)blockIdx.x * steps_per_wg; st < (int64_t)(blockIdx.x + 1) * steps_per_wg; ++st) {
+  for (int64_t st = st0; st < st1; ++st) {
     const int64_t set0 = s_first + 2 * st;
-    if (set0 >= s_end) break;
     const int64_t ubase = set0 * kSet + 32 * wave;   // this wave's first token
-
-    // ---- loads: keys and values of both tiles
-    RawSeg<ES, CPL> rk[2], rv[2];
-    bool kring[2], vring[2], valid[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int64_t u = ubase + 16 * tt + tok;
-      valid[tt] = u >= a.u0 && u < a.u1;
-      kring[tt] = load_seg<D, ES>(a, a.ring_k, a.k_new, bg, b, g, u, valid[tt], q, rk[tt]);
-      vring[tt] = load_seg<D, ES>(a, a.ring_v, a.v_new, bg, b, g, u, valid[tt], q, rv[tt]);
-    }
 
     // ---- keys, one tile at a time: x = T_K k16 on MFMA, parameters, codes
 #pragma unroll
@@ -403,20 +439,20 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_
       }
       const int row = 32 * wave + 16 * tt + tok;
       const int64_t u = ubase + 16 * tt + tok;
-      // parameters
-      float sc, zp = 0.f;
-      if (a.quant_k == WUSHKV_Q_QUEST) {
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      auto key_tile = [&](auto tag) {
+        constexpr bool QU = decltype(tag)::value;
+        float sc, zp = 0.f;
+        if constexpr (QU) {
+          float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+          for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s4[i] = fmaf(acc[ct][i], acc[ct][i], s4[i]);
-        float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        sc = quest_step(ss, a.clip, Lk, D);
-      } else {
-        if constexpr (NL > 0) {
+            for (int i = 0; i < 4; ++i) s4[i] = fmaf(acc[ct][i], acc[ct][i], s4[i]);
+          float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          sc = quest_step(ss, a.clip, Lk, D);
+        } else if constexpr (NL > 0) {
           OrderStats<NL> o;
           os_init(o);
 #pragma unroll
@@ -429,62 +465,64 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_
         } else {
           sc = 0.f;
         }
-      }
-      if (q == 0 && valid[tt]) {
-        _Float16 *pk = (_Float16 *)((char *)a.par_k + (size_t)bg * a.kpar_bytes) + u * a.kpar_n;
-        if (a.kpar_n == 2) *(unsigned *)pk = pack_f16(sc, zp);
-        else pk[0] = (_Float16)sc;
-      }
-      // codes
-      const Quant qk = make_quant(sc, zp, a.quant_k, Lk);
-      float edge = 0.f;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        unsigned w = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_cvt_pk_u8_f32(code_of(qk, acc[ct][i], edge), i, w);
-        *(unsigned *)&sm.kc[row][16 * ct + 4 * q] = w;
-      }
-      // elements near a boundary: the 4 lanes of a token take one candidate at a
-      // time, each summing its CPL channels' exact products in fp64
-      const bool kn = valid[tt] && near_edge(qk, edge, kEdgeK);
-      if (__any(kn)) {
-        unsigned m = 0;
-        if (kn) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float e1 = 0.f;
-              code_of(qk, acc[ct][i], e1);
-              if (e1 > 0.5f - kEdgeK) m |= 1u << (4 * ct + i);
-            }
+        if (q == 0 && valid[tt]) {
+          _Float16 *pk = (_Float16 *)((char *)a.par_k + (size_t)bg * a.kpar_bytes) + u * a.kpar_n;
+          if constexpr (QU) pk[0] = (_Float16)sc;
+          else *(unsigned *)pk = pack_f16(sc, zp);
         }
-        while (__any(m != 0)) {
-          const unsigned m0 = __shfl(m, tok), m1 = __shfl(m, 16 + tok), m2 = __shfl(m, 32 + tok), m3 = __shfl(m, 48 + tok);
-          const int qs = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : (m3 ? 3 : -1)));
-          const unsigned mm = qs == 0 ? m0 : (qs == 1 ? m1 : (qs == 2 ? m2 : m3));
-          const int bit = qs >= 0 ? __builtin_ctz(mm) : 0;
-          const int j = 16 * (bit >> 2) + 4 * (qs >= 0 ? qs : 0) + (bit & 3);
-          double part = 0.0;
+        const Quant<QU> qk = make_quant<QU>(sc, zp, Lk);
+        Edge e = edge_init();
 #pragma unroll
-          for (int s = 0; s < CPL / 8; ++s) {
-            const half8 tv = *(const half8 *)&sm.t[j][CPL * q + 8 * s];
+        for (int ct = 0; ct < NCT; ++ct) {
+          float c0, c1, c2, c3;
+          code2(qk, acc[ct][0], acc[ct][1], e, c0, c1);
+          code2(qk, acc[ct][2], acc[ct][3], e, c2, c3);
+          unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(c0, 0, 0u);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(c1, 1, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(c2, 2, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(c3, 3, w);
+          *(unsigned *)&sm.kc[row][16 * ct + 4 * q] = w;
+        }
+        // elements near a boundary: the 4 lanes of a token take one candidate at a
+        // time, each summing its CPL channels' exact products in fp64
+        const bool kn = valid[tt] && edge_near(qk, e, kEdgeK);
+        if (__any(kn)) {
+          unsigned m = 0;
+          if (kn) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const unsigned w = kh[4 * s + e / 2];
-              const float kv = (e & 1) ? f16_hi(w) : f16_lo(w);
-              part += (double)((float)tv[e] * kv);   // fp16 x fp16 is exact in fp32
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                if (value_near(qk, acc[ct][i], kEdgeK)) m |= 1u << (4 * ct + i);
+          }
+          while (__any(m != 0)) {
+            const unsigned m0 = __shfl(m, tok), m1 = __shfl(m, 16 + tok), m2 = __shfl(m, 32 + tok), m3 = __shfl(m, 48 + tok);
+            const int qs = m0 ? 0 : (m1 ? 1 : (m2 ? 2 : (m3 ? 3 : -1)));
+            const unsigned mm = qs == 0 ? m0 : (qs == 1 ? m1 : (qs == 2 ? m2 : m3));
+            const int bit = qs >= 0 ? __builtin_ctz(mm) : 0;
+            const int j = 16 * (bit >> 2) + 4 * (qs >= 0 ? qs : 0) + (bit & 3);
+            double part = 0.0;
+#pragma unroll
+            for (int s = 0; s < CPL / 8; ++s) {
+              const half8 tv = *(const half8 *)&sm.t[j][CPL * q + 8 * s];
+#pragma unroll
+              for (int e8 = 0; e8 < 8; ++e8) {
+                const unsigned w = kh[4 * s + e8 / 2];
+                const float kv = (e8 & 1) ? f16_hi(w) : f16_lo(w);
+                part += (double)((float)tv[e8] * kv);   // fp16 x fp16 is exact in fp32
+              }
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (qs == q) {
+              sm.kc[row][j] = (uint8_t)exact_code(part, sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lk);
+              m &= ~(1u << bit);
             }
           }
-          part += __shfl_xor(part, 16);
-          part += __shfl_xor(part, 32);
-          if (qs == q) {
-            sm.kc[row][j] = (uint8_t)exact_code(part, sc, zp, a.quant_k, Lk);
-            m &= ~(1u << bit);
-          }
         }
-      }
+      };
+      if (a.quant_k == WUSHKV_Q_QUEST) key_tile(QuestTag{});
+      else key_tile(AffineTag{});
     }
 
     // ---- values
@@ -493,17 +531,20 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_
       float xv[CPL];
       seg_float<ES, CPL>(rv[tt], vring[tt], a.in_dtype, xv);
       const int64_t u = ubase + 16 * tt + tok;
-      float sc, zp = 0.f;
-      if (a.quant_v == WUSHKV_Q_QUEST) {
-        float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      const int s2 = wave >> 1;                       // set of this wave within the step
+      const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
+      auto value_tile = [&](auto tag) {
+        constexpr bool QU = decltype(tag)::value;
+        float sc, zp = 0.f;
+        if constexpr (QU) {
+          float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) s4[k & 3] = fmaf(xv[k], xv[k], s4[k & 3]);
-        float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        sc = quest_step(ss, a.clip, Lv, D);
-      } else {
-        if constexpr (NL > 0) {
+          for (int k = 0; k < CPL; ++k) s4[k & 3] = fmaf(xv[k], xv[k], s4[k & 3]);
+          float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          sc = quest_step(ss, a.clip, Lv, D);
+        } else if constexpr (NL > 0) {
           OrderStats<NL> o;
           os_init(o);
 #pragma unroll
@@ -514,39 +555,43 @@ __global__ void __launch_bounds__(kThreads) flush_kernel(FlushArgs a, int steps_
         } else {
           sc = 0.f;
         }
-      }
-      if (q == 0 && valid[tt]) {
-        _Float16 *pv = (_Float16 *)((char *)a.par_v + (size_t)bg * a.vpar_bytes) + u * a.vpar_n;
-        if (a.vpar_n == 2) *(unsigned *)pv = pack_f16(sc, zp);
-        else pv[0] = (_Float16)sc;
-      }
-      const Quant qv = make_quant(sc, zp, a.quant_v, Lv);
-      float edge = 0.f;
-      const int s2 = wave >> 1;                       // set of this wave within the step
-      const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
+        if (q == 0 && valid[tt]) {
+          _Float16 *pv = (_Float16 *)((char *)a.par_v + (size_t)bg * a.vpar_bytes) + u * a.vpar_n;
+          if constexpr (QU) pv[0] = (_Float16)sc;
+          else *(unsigned *)pv = pack_f16(sc, zp);
+        }
+        const Quant<QU> qv = make_quant<QU>(sc, zp, Lv);
+        Edge e = edge_init();
 #pragma unroll
-      for (int g4 = 0; g4 < CPL / 4; ++g4) {
-        unsigned w = 0;
+        for (int g4 = 0; g4 < CPL / 4; ++g4) {
+          float c0, c1, c2, c3;
+          code2(qv, xv[4 * g4], xv[4 * g4 + 1], e, c0, c1);
+          code2(qv, xv[4 * g4 + 2], xv[4 * g4 + 3], e, c2, c3);
+          unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(c0, 0, 0u);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(c1, 1, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(c2, 2, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(c3, 3, w);
+          // lane tok = 4c + e now gets channel 4*g4 + e of tokens 4c .. 4c+3
+          w = quad_transpose(w, selA, selB);
+          *(unsigned *)&sm.vc[s2][CPL * q + 4 * g4 + (tok & 3)][col + 4 * (tok >> 2)] = w;
+        }
+        const bool vn = valid[tt] && edge_near(qv, e, kEdgeV);
+        if (__any(vn)) {
+          if (vn) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w = __builtin_amdgcn_cvt_pk_u8_f32(code_of(qv, xv[4 * g4 + r], edge), r, w);
-        // lane tok = 4c + e now gets channel 4*g4 + e of tokens 4c .. 4c+3
-        w = quad_transpose(w, selA, selB);
-        *(unsigned *)&sm.vc[s2][CPL * q + 4 * g4 + (tok & 3)][col + 4 * (tok >> 2)] = w;
-      }
-      const bool vn = valid[tt] && near_edge(qv, edge, kEdgeV);
-      if (__any(vn)) {
-        if (vn) {
-#pragma unroll
-          for (int k = 0; k < CPL; ++k) {
-            float e1 = 0.f;
-            code_of(qv, xv[k], e1);
-            if (e1 > 0.5f - kEdgeV) sm.vc[s2][CPL * q + k][col + tok] = (uint8_t)exact_code((double)xv[k], sc, zp, a.quant_v, Lv);
+            for (int k = 0; k < CPL; ++k)
+              if (value_near(qv, xv[k], kEdgeV))
+                sm.vc[s2][CPL * q + k][col + tok] =
+                    (uint8_t)exact_code((double)xv[k], sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lv);
           }
         }
-      }
+      };
+      if (a.quant_v == WUSHKV_Q_QUEST) value_tile(QuestTag{});
+      else value_tile(AffineTag{});
     }
     __syncthreads();
-
+    // the next step's rows load while this step's codes are packed and stored
+    if (st + 1 < st1) issue_loads(st + 1);
     // ---- K rows: two threads per token, D/2 channels each
     {
       const int r = tid >> 1, h = tid & 1;
@@ -670,10 +715,11 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   const int64_t s0 = a.u0 / kSet, s1 = (a.u1 + kSet - 1) / kSet;
   const int64_t steps = (s1 - s0 + 1) / 2;
   const int64_t heads = (int64_t)a.B * a.Hkv;
-  // about 2048 workgroups (four rounds of the two that fit per CU); each walks a
-  // contiguous run of steps of one KV head, so T_K is staged once per run
-  int64_t spw = steps * heads / 2048;
-  if (spw < 1) spw = 1;
+  // about 1024 workgroups (two rounds of the two that fit per CU); each walks a
+  // contiguous run of at least two steps of one KV head, so T_K is staged once per
+  // run and a step's loads overlap the previous step's stores
+  int64_t spw = (steps * heads + 1023) / 1024;
+  if (spw < 2) spw = 2;
   dim3 grid((unsigned)((steps + spw - 1) / spw), (unsigned)heads);
   int need = 0;
   if (a.quant_k == WUSHKV_Q_AFFINE_PCT || a.quant_v == WUSHKV_Q_AFFINE_PCT)
