@@ -29,6 +29,8 @@
 // plain fp32 VALU, which seeds its softmax state, then streams its body sets.
 // Each workgroup merges its 4 waves in LDS and writes one partial (m, l, o); the
 // merge kernel that follows on the stream combines the partials.
+#include <type_traits>
+
 #include "wushkv_internal.h"
 
 namespace wushkv {
@@ -63,13 +65,26 @@ __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
 }
 
+// Byte layout of one staged 64-token set: key codes (2 KB, verbatim), value codes
+// (2 KB; lane l's 32 bytes split into its first and second 16 bytes at 16 l and
+// 1024 + 16 l), the 3-bit plane (1 KB, verbatim), then key and value parameters
+// (up to 256 B each, verbatim).
+template <int BV>
+struct Stage {
+  static constexpr int K = 0, V = 2048, VH = 4096;
+  static constexpr int KP = BV == 3 ? 5120 : 4096, VP = KP + 256, SIZE = VP + 256;
+  static constexpr int DMAS = BV == 3 ? 7 : 6;   // load-to-LDS instructions per set
+};
+
+constexpr int kStages = 2;   // body sets staged per wave: the one computed and the next
+
+template <int G, int BV>
 struct __align__(16) FastSmem {
+  float qt[G][kD];
+  float q[G][kD];
+  float wp[kWaves][G][kD];        // window waves: probabilities [head][token], then values
   union {
-    struct {
-      float qt[16][kD];
-      float q[16][kD];
-      float wp[kWaves][16][64];   // window waves: probabilities [head][token]
-    } pre;
+    uint8_t ring[kWaves][kStages][Stage<BV>::SIZE];
     float o[kWaves][16][kD];      // per wave: rows (tile-phase, head), columns channels
   } u;
   float alpha[16], sq[16];
@@ -220,50 +235,79 @@ struct SetData {
   u32x4 kp[NGRP], vp[NGRP];  // per-token parameters of this lane's 4 packed tokens
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Queue the loads of body set `set` into the wave's ring slot `st` (load-to-LDS:
+// lane i's bytes land at the slot offset + i * size).  Stage<BV>::DMAS instructions.
+template <int BV>
+__device__ __forceinline__ void stage_set(const DecodeArgs &a, const uint8_t *kplane, const uint8_t *vplane,
+                                          const uint8_t *kpar, const uint8_t *vpar, int64_t set, uint8_t *st) {
+  using S = Stage<BV>;
+  const int lane = threadIdx.x & 63;
+  constexpr int aux = 2;   // nontemporal: streamed once
+  const uint8_t *kg = kplane + (size_t)set * 2048;
+  __builtin_amdgcn_global_load_lds(kg + 16 * lane, (lds_void *)(st + S::K), 16, 0, aux);
+  __builtin_amdgcn_global_load_lds(kg + 1024 + 16 * lane, (lds_void *)(st + S::K + 1024), 16, 0, aux);
+  const uint8_t *vg = vplane + (size_t)set * a.vset_bytes;
+  __builtin_amdgcn_global_load_lds(vg + 32 * lane, (lds_void *)(st + S::V), 16, 0, aux);
+  __builtin_amdgcn_global_load_lds(vg + 32 * lane + 16, (lds_void *)(st + S::V + 1024), 16, 0, aux);
+  if constexpr (BV == 3) __builtin_amdgcn_global_load_lds(vg + 2048 + 16 * lane, (lds_void *)(st + S::VH), 16, 0, aux);
+  // parameters: 64 tokens x (2 or 4) bytes
+  const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
+  if (lane < 16 * kb)
+    __builtin_amdgcn_global_load_lds(kpar + (size_t)set * 64 * kb + 4 * lane, (lds_void *)(st + S::KP), 4, 0, aux);
+  if (lane < 16 * vbn)
+    __builtin_amdgcn_global_load_lds(vpar + (size_t)set * 64 * vbn + 4 * lane, (lds_void *)(st + S::VP), 4, 0, aux);
+}
+
+// Wait until at most `pending` staged sets' loads are still in flight.
+template <int BV>
+__device__ __forceinline__ void wait_staged(int pending) {
+  constexpr int D = Stage<BV>::DMAS;
+  if (pending <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+}
+
+// This lane's operands of a staged set.
 template <int NGRP, int TPG, int BV>
-__device__ __forceinline__ void load_set(const DecodeArgs &a, const uint8_t *kplane, const uint8_t *vplane,
-                                         const _Float16 *kpar, const _Float16 *vpar, int64_t set,
-                                         SetData<NGRP> &d) {
+__device__ __forceinline__ void read_set(const DecodeArgs &a, const uint8_t *st, SetData<NGRP> &d) {
+  using S = Stage<BV>;
   const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4, col = lane & 15;
-  const int G = 16 / TPG;
-  const int tcol = col / G;
-  const int64_t base = set * kSet;
+  const int tcol = col / (16 / TPG);
 #pragma unroll
-  for (int T = 0; T < 4; ++T)
-    d.kw[T] = __builtin_nontemporal_load((const u32x2 *)(kplane + (size_t)(base + 16 * T + col) * 32 + 8 * q4));
-  const uint8_t *vset = vplane + (size_t)set * a.vset_bytes;
-  d.vw0 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32));
-  d.vw1 = __builtin_nontemporal_load((const u32x4 *)(vset + lane * 32 + 16));
-  if constexpr (BV == 3) d.vh = __builtin_nontemporal_load((const u32x4 *)(vset + 64 * 32 + lane * 16));
+  for (int T = 0; T < 4; ++T) d.kw[T] = *(const u32x2 *)(st + S::K + (16 * T + col) * 32 + 8 * q4);
+  d.vw0 = *(const u32x4 *)(st + S::V + 16 * lane);
+  d.vw1 = *(const u32x4 *)(st + S::V + 1024 + 16 * lane);
+  if constexpr (BV == 3) d.vh = *(const u32x4 *)(st + S::VH + 16 * lane);
   else d.vh = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
   for (int gr = 0; gr < NGRP; ++gr) {
-    const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
+    const int t0 = 16 * (TPG * gr + tcol) + 4 * q4;
     if (a.quant_k == WUSHKV_Q_QUEST) {
-      const u32x2 x = __builtin_nontemporal_load((const u32x2 *)(kpar + t0));
+      const u32x2 x = *(const u32x2 *)(st + S::KP + 2 * t0);
       d.kp[gr] = (u32x4){x[0], x[1], 0u, 0u};
     } else {
-      d.kp[gr] = __builtin_nontemporal_load((const u32x4 *)(kpar + 2 * t0));
+      d.kp[gr] = *(const u32x4 *)(st + S::KP + 4 * t0);
     }
     if (a.quant_v == WUSHKV_Q_QUEST) {
-      const u32x2 x = __builtin_nontemporal_load((const u32x2 *)(vpar + t0));
+      const u32x2 x = *(const u32x2 *)(st + S::VP + 2 * t0);
       d.vp[gr] = (u32x4){x[0], x[1], 0u, 0u};
     } else {
-      d.vp[gr] = __builtin_nontemporal_load((const u32x4 *)(vpar + 2 * t0));
+      d.vp[gr] = *(const u32x4 *)(st + S::VP + 4 * t0);
     }
   }
 }
 
 // One body wave: the sets [s0, s1) of one (b, g).
-template <int G>
-__device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, int t1, int w,
+template <int G, int BV>
+__device__ void window_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int t0, int t1, int w,
                             float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]);
 
 // One wave of a KV partition: first its share [w0, w1) of the FP16 window tokens on
 // VALU, whose result seeds the online-softmax state, then the body sets [s0, s1).
 template <int G, int BV>
-__device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0, int64_t s1, int w0, int w1,
+__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int64_t s0, int64_t s1, int w0, int w1,
                           f32x4 (&O)[8], float &m_out, float &l_out, float &z_out) {
   constexpr int TPG = 16 / G;          // tiles per packed register group
   constexpr int NGRP = 4 / TPG;        // groups per 64-token set
@@ -292,7 +336,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
           const int ch = 16 * (2 * q4 + s) + 4 * bb + k;
-          const int dig = live ? digit_of(sm.u.pre.qt[h][ch], inv_alpha, dg) : 0;
+          const int dig = live ? digit_of(sm.qt[h][ch], inv_alpha, dg) : 0;
           word |= ((unsigned)dig & 0xFFu) << (8 * bb);
         }
         bq[mf][s][k] = (int)word;
@@ -317,9 +361,12 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
 
   const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
   const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
-  const _Float16 *kpar = (const _Float16 *)((const char *)a.par_k + (size_t)bg * a.kpar_bytes);
-  const _Float16 *vpar = (const _Float16 *)((const char *)a.par_v + (size_t)bg * a.vpar_bytes);
-  SetData<NGRP> cur, nxt;
+  const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
+  const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
+  uint8_t *ring = &sm.u.ring[threadIdx.x >> 6][0][0];
+  constexpr int SB = Stage<BV>::SIZE;
+  // the first body set is in flight during the window pass
+  if (s0 < s1) stage_set<BV>(a, kplane, vplane, kpar, vpar, s0, ring);
 
   float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
 #pragma unroll
@@ -329,7 +376,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
     float wacc[G][2], wm[G], wl[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) { wacc[h][0] = wacc[h][1] = 0.f; wm[h] = -INFINITY; wl[h] = 0.f; }
-    window_wave<G>(a, sm, bg, w0, w1, w, wacc, wm, wl);
+    window_wave<G, BV>(a, sm, bg, w0, w1, w, wacc, wm, wl);
     // packed lane layout: head hc's max in every lane of hc, its sum counted once
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -340,7 +387,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
     }
     // window values -> rows (tile 0, head h) of the PV accumulators, through this
     // wave's probability buffer (free again after the window pass)
-    float *buf = &sm.u.pre.wp[w][0][0];
+    float *buf = &sm.wp[w][0][0];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       buf[h * kD + 2 * lane] = wacc[h][0];
@@ -361,8 +408,10 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
 
   const bool kq = a.quant_k == WUSHKV_Q_QUEST, vq = a.quant_v == WUSHKV_Q_QUEST;
 
-  // one 64-token set: QK, softmax update, PV
-  auto compute = [&](int64_t set, const SetData<NGRP> &cur) {
+  // one 64-token set: QK, softmax update, PV.  FULL: every token of the set is in
+  // the body (no validity selects).
+  auto compute = [&](auto full_tag, int64_t set, const SetData<NGRP> &cur) {
+    constexpr bool FULL = decltype(full_tag)::value;
     const int64_t base = set * kSet;
     const u32x2 *kw = cur.kw;
     const u32x4 vw0 = cur.vw0, vw1 = cur.vw1, vh = cur.vh;
@@ -435,7 +484,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
           s_t = h_lo(kp[gr][i]);
           z_t = h_hi(kp[gr][i]);
         }
-        const bool valid = t0 + i < a.nq;
+        const bool valid = FULL || t0 + i < a.nq;
         sc[gr][i] = valid ? fmaf(s_t, C[gr][i] * a_sc, z_t * b_sc) : -INFINITY;
         mx = fmaxf(mx, sc[gr][i]);
       }
@@ -473,20 +522,19 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
           s_t = h_lo(vp[gr][i]);
           z_t = h_hi(vp[gr][i]);
         }
-        const bool valid = t0 + i < a.nq;
+        // W = p s enters the MFMA as fp16 hi + lo (~22 bits) against BASE + c; the
+        // zero term takes p z - BASE W, with W in place of hi + lo (they differ by
+        // ~2^-22 W, i.e. ~1.5e-5 W at BASE = 64)
+        const bool valid = FULL || t0 + i < a.nq;
         l_lane += p;
         W[i] = valid ? p * s_t : 0.f;
-        zacc += valid ? p * z_t : 0.f;
+        const float zb = fmaf(-vbase[gr][i >> 1], s_t, z_t);
+        zacc = valid ? fmaf(p, zb, zacc) : zacc;
       }
-      // W = hi + lo, both fp16 (~22 bits).  The MFMA forms sum (hi + lo) * (BASE + c);
-      // hi + lo is exact in fp32, so BASE * (hi + lo) is taken out exactly.
       wp[gr][0] = pack_h2(W[0], W[1]);
       wp[gr][1] = pack_h2(W[2], W[3]);
       wl[gr][0] = pack_h2(W[0] - h_lo(wp[gr][0]), W[1] - h_hi(wp[gr][0]));
       wl[gr][1] = pack_h2(W[2] - h_lo(wp[gr][1]), W[3] - h_hi(wp[gr][1]));
-      const float s01 = (h_lo(wp[gr][0]) + h_lo(wl[gr][0])) + (h_hi(wp[gr][0]) + h_hi(wl[gr][0]));
-      const float s23 = (h_lo(wp[gr][1]) + h_lo(wl[gr][1])) + (h_hi(wp[gr][1]) + h_hi(wl[gr][1]));
-      zacc = fmaf(-vbase[gr][0], s01, fmaf(-vbase[gr][1], s23, zacc));
     }
 
     // ---- PV on the f16 MFMA: instruction iota covers tiles 2*iota, 2*iota+1
@@ -530,13 +578,20 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem &sm, int bg, int64_t s0,
     }
   };
 
-  // the next set's codes and parameters are in flight while the current one computes
-  // (one copy of the set body: fewer live registers than an unrolled rotation)
-  if (s0 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, s0, cur);
+  // body sets: set k + 1 is staged while set k computes
+  using FullTag = std::integral_constant<bool, true>;
+  using TailTag = std::integral_constant<bool, false>;
+  int slot = 0;
   for (int64_t set = s0; set < s1; ++set) {
-    if (set + 1 < s1) load_set<NGRP, TPG, BV>(a, kplane, vplane, kpar, vpar, set + 1, nxt);
-    compute(set, cur);
-    cur = nxt;
+    const int nslot = slot + 1 == kStages ? 0 : slot + 1;
+    const bool more = set + 1 < s1;
+    if (more) stage_set<BV>(a, kplane, vplane, kpar, vpar, set + 1, ring + nslot * SB);
+    wait_staged<BV>(more ? 1 : 0);
+    SetData<NGRP> cur;
+    read_set<NGRP, TPG, BV>(a, ring + slot * SB, cur);
+    if ((set + 1) * kSet <= a.nq) compute(FullTag{}, set, cur);
+    else compute(TailTag{}, set, cur);
+    slot = nslot;
   }
 
   // per-head totals; every lane of a head holds them
@@ -555,8 +610,8 @@ __device__ __forceinline__ int window_row(int t, int ns, unsigned first_slot, un
 // plain fp32 VALU in passes of 16 tokens.  Scores: four lanes per token, 32 channels
 // each, summed over the quad; values: lane = two channels.  A pass issues all of its
 // key and value loads before using any of them.
-template <int G>
-__device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, int t1, int w,
+template <int G, int BV>
+__device__ void window_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int t0, int t1, int w,
                             float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]) {
   const int lane = threadIdx.x & 63;
   const int ti = lane >> 2, qq = lane & 3;   // token of the pass, quarter of the channels
@@ -590,8 +645,8 @@ __device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, i
       float x = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const f32x4 q0 = *(const f32x4 *)&sm.u.pre.q[h][32 * qq + 8 * c];
-        const f32x4 q1 = *(const f32x4 *)&sm.u.pre.q[h][32 * qq + 8 * c + 4];
+        const f32x4 q0 = *(const f32x4 *)&sm.q[h][32 * qq + 8 * c];
+        const f32x4 q1 = *(const f32x4 *)&sm.q[h][32 * qq + 8 * c + 4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           x = fmaf(q0[e], (float)kv[c][e], x);
@@ -613,7 +668,7 @@ __device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, i
       mrun[h] = mn;
       acc[h][0] *= al;
       acc[h][1] *= al;
-      if (qq == 0) sm.u.pre.wp[w][h][ti] = pr;
+      if (qq == 0) sm.wp[w][h][ti] = pr;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -624,7 +679,7 @@ __device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, i
       const float v0 = (float)vv[u][0], v1 = (float)vv[u][1];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float pr = sm.u.pre.wp[w][h][u];
+        const float pr = sm.wp[w][h][u];
         acc[h][0] = fmaf(pr, v0, acc[h][0]);
         acc[h][1] = fmaf(pr, v1, acc[h][1]);
       }
@@ -635,7 +690,7 @@ __device__ void window_wave(const DecodeArgs &a, FastSmem &sm, int bg, int t0, i
 
 template <int G, int BV>
 __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int nwg_body) {
-  __shared__ FastSmem sm;
+  __shared__ FastSmem<G, BV> sm;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int bg = blockIdx.y;
@@ -645,14 +700,14 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
   for (int i = tid; i < G * kD; i += kThreads) {
     const int hh = i / kD, j = i % kD;
     const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
-    sm.u.pre.qt[hh][j] = a.qt[off];
-    sm.u.pre.q[hh][j] = load_in(a.q, a.q_dtype, off);
+    sm.qt[hh][j] = a.qt[off];
+    sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
   }
   __syncthreads();
   if (tid < G) {
     float mxa = 0.f, s = 0.f;
     for (int j = 0; j < kD; ++j) {
-      const float v = sm.u.pre.qt[tid][j];
+      const float v = sm.qt[tid][j];
       mxa = fmaxf(mxa, fabsf(v));
       s += v;
     }
