@@ -65,15 +65,17 @@ __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
 }
 
-// Byte layout of one staged 64-token set: key codes (2 KB, verbatim), value codes
-// (2 KB; lane l's 32 bytes split into its first and second 16 bytes at 16 l and
-// 1024 + 16 l), the 3-bit plane (1 KB, verbatim), then key and value parameters
-// (up to 256 B each, verbatim).
+// Byte layout of one ring slot.  A body set: key codes (2 KB), value codes (2 KB),
+// the 3-bit plane (1 KB), key then value parameters (up to 256 B each), all copied
+// verbatim.  A window stage: 8 FP16 key rows (2 KB) then 8 FP16 value rows (2 KB).
+// Both kinds are filled by exactly DMAS load-to-LDS instructions, so one vmcnt per
+// pending slot covers either.
 template <int BV>
 struct Stage {
   static constexpr int K = 0, V = 2048, VH = 4096;
   static constexpr int KP = BV == 3 ? 5120 : 4096, VP = KP + 256, SIZE = VP + 256;
-  static constexpr int DMAS = BV == 3 ? 7 : 6;   // load-to-LDS instructions per set
+  static constexpr int WK = 0, WV = 2048;
+  static constexpr int DMAS = BV == 3 ? 6 : 5;
 };
 
 constexpr int kStages = 2;   // body sets staged per wave: the one computed and the next
@@ -82,10 +84,14 @@ template <int G, int BV>
 struct __align__(16) FastSmem {
   float qt[G][kD];
   float q[G][kD];
-  float wp[kWaves][G][kD];        // window waves: probabilities [head][token], then values
+  float wp[kWaves][G][8];         // window stage: probabilities [head][token]
+  float wmx[kWaves][16], wls[kWaves][16];  // window partial: max and sum per head
   union {
     uint8_t ring[kWaves][kStages][Stage<BV>::SIZE];
-    float o[kWaves][16][kD];      // per wave: rows (tile-phase, head), columns channels
+    struct {
+      float o[kWaves][16][kD];    // per wave: rows (tile-phase, head), columns channels
+      float wo[kWaves][G][kD];    // window partial: weighted FP16 values [head][channel]
+    };
   } u;
   float alpha[16], sq[16];
   float m[kWaves][16], l[kWaves][16], z[kWaves][16];
@@ -249,15 +255,47 @@ __device__ __forceinline__ void stage_set(const DecodeArgs &a, const uint8_t *kp
   __builtin_amdgcn_global_load_lds(kg + 16 * lane, (lds_void *)(st + S::K), 16, 0, aux);
   __builtin_amdgcn_global_load_lds(kg + 1024 + 16 * lane, (lds_void *)(st + S::K + 1024), 16, 0, aux);
   const uint8_t *vg = vplane + (size_t)set * a.vset_bytes;
-  __builtin_amdgcn_global_load_lds(vg + 32 * lane, (lds_void *)(st + S::V), 16, 0, aux);
-  __builtin_amdgcn_global_load_lds(vg + 32 * lane + 16, (lds_void *)(st + S::V + 1024), 16, 0, aux);
+  __builtin_amdgcn_global_load_lds(vg + 16 * lane, (lds_void *)(st + S::V), 16, 0, aux);
+  __builtin_amdgcn_global_load_lds(vg + 1024 + 16 * lane, (lds_void *)(st + S::V + 1024), 16, 0, aux);
   if constexpr (BV == 3) __builtin_amdgcn_global_load_lds(vg + 2048 + 16 * lane, (lds_void *)(st + S::VH), 16, 0, aux);
-  // parameters: 64 tokens x (2 or 4) bytes
+  // parameters, one instruction: lanes 0-15 the keys', 16-31 the values' (64 tokens x
+  // 2 or 4 bytes each; lane 0 is always active, so the instruction always issues)
   const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
-  if (lane < 16 * kb)
-    __builtin_amdgcn_global_load_lds(kpar + (size_t)set * 64 * kb + 4 * lane, (lds_void *)(st + S::KP), 4, 0, aux);
-  if (lane < 16 * vbn)
-    __builtin_amdgcn_global_load_lds(vpar + (size_t)set * 64 * vbn + 4 * lane, (lds_void *)(st + S::VP), 4, 0, aux);
+  const bool pk = lane < 4 * kb, pv = lane >= 16 && lane - 16 < 4 * vbn;
+  if (pk || pv) {
+    const uint8_t *src = pk ? kpar + (size_t)set * 64 * kb + 16 * lane : vpar + (size_t)set * 64 * vbn + 16 * (lane - 16);
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + S::KP), 16, 0, aux);
+  }
+}
+
+// Row of window-list token t: sink row t, or the ring slot of the t-th token after the
+// sink (first_slot = slot of the oldest recent token); the sign bit marks the ring.
+__device__ __forceinline__ int window_row(int t, int ns, unsigned first_slot, unsigned ring) {
+  return t < ns ? t : (int)(((first_slot + (unsigned)(t - ns)) % ring) | 0x80000000u);
+}
+
+// Queue window-list tokens [t0, t0 + cnt), cnt <= 8, into a ring slot: 8 key rows and
+// 8 value rows of 256 bytes (lanes past cnt re-read token t0, so every instruction
+// issues with all lanes), plus DMAS - 4 single-lane filler loads into the slot's
+// unused parameter area so a window slot counts like a body slot.
+template <int BV>
+__device__ __forceinline__ void stage_window(const uint8_t *sinkk, const uint8_t *sinkv, const uint8_t *ringk,
+                                             const uint8_t *ringv, int t0, int cnt, int ns, unsigned first_slot,
+                                             unsigned rsz, const void *filler, uint8_t *st) {
+  using S = Stage<BV>;
+  const int lane = threadIdx.x & 63;
+  constexpr int aux = 2;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = 4 * i + (lane >> 4);
+    const int r = window_row(t0 + (j < cnt ? j : 0), ns, first_slot, rsz);
+    const size_t off = (size_t)(r & 0x7FFFFFFF) * 256 + 16 * (lane & 15);
+    __builtin_amdgcn_global_load_lds((r >= 0 ? sinkk : ringk) + off, (lds_void *)(st + S::WK + 1024 * i), 16, 0, aux);
+    __builtin_amdgcn_global_load_lds((r >= 0 ? sinkv : ringv) + off, (lds_void *)(st + S::WV + 1024 * i), 16, 0, aux);
+  }
+#pragma unroll
+  for (int i = 0; i < S::DMAS - 4; ++i)
+    if (lane == 0) __builtin_amdgcn_global_load_lds(filler, (lds_void *)(st + S::KP + 64 * i), 16, 0, aux);
 }
 
 // Wait until at most `pending` staged sets' loads are still in flight.
@@ -277,8 +315,8 @@ __device__ __forceinline__ void read_set(const DecodeArgs &a, const uint8_t *st,
   const int tcol = col / (16 / TPG);
 #pragma unroll
   for (int T = 0; T < 4; ++T) d.kw[T] = *(const u32x2 *)(st + S::K + (16 * T + col) * 32 + 8 * q4);
-  d.vw0 = *(const u32x4 *)(st + S::V + 16 * lane);
-  d.vw1 = *(const u32x4 *)(st + S::V + 1024 + 16 * lane);
+  d.vw0 = *(const u32x4 *)(st + S::V + 32 * lane);
+  d.vw1 = *(const u32x4 *)(st + S::V + 32 * lane + 16);
   if constexpr (BV == 3) d.vh = *(const u32x4 *)(st + S::VH + 16 * lane);
   else d.vh = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
@@ -299,16 +337,16 @@ __device__ __forceinline__ void read_set(const DecodeArgs &a, const uint8_t *st,
   }
 }
 
-// One body wave: the sets [s0, s1) of one (b, g).
 template <int G, int BV>
-__device__ void window_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int t0, int t1, int w,
-                            float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]);
+__device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
+                             float (&wl)[G], float (&wacc)[G][2]);
 
-// One wave of a KV partition: first its share [w0, w1) of the FP16 window tokens on
-// VALU, whose result seeds the online-softmax state, then the body sets [s0, s1).
+// One wave of a KV partition: its body sets [s0, s1), then its 8-token stages
+// [ws0, ws1) of the FP16 window list, all streamed through the wave's LDS ring.
 template <int G, int BV>
-__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int64_t s0, int64_t s1, int w0, int w1,
-                          f32x4 (&O)[8], float &m_out, float &l_out, float &z_out) {
+__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
+                          f32x4 (&O)[8], float &m_out, float &l_out, float &z_out, float (&wm_out)[G],
+                          float (&wl_out)[G], float (&wacc_out)[G][2]) {
   constexpr int TPG = 16 / G;          // tiles per packed register group
   constexpr int NGRP = 4 / TPG;        // groups per 64-token set
   constexpr int NMF = (3 * G + 15) / 16;  // QK MFMAs per (tile, k-step)
@@ -363,48 +401,32 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
   const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
   const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
-  uint8_t *ring = &sm.u.ring[threadIdx.x >> 6][0][0];
+  const int w = threadIdx.x >> 6;
+  uint8_t *ring = &sm.u.ring[w][0][0];
   constexpr int SB = Stage<BV>::SIZE;
-  // the first body set is in flight during the window pass
-  if (s0 < s1) stage_set<BV>(a, kplane, vplane, kpar, vpar, s0, ring);
+  // items of this wave: body sets s0 .. s1-1, then 8-token window stages ws0 .. ws1-1
+  const int nb = (int)(s1 - s0), nitems = nb + (ws1 - ws0);
+  const int ns = (int)(a.n < a.S ? a.n : a.S);
+  const int nw = ns + (int)(a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+  const unsigned rsz = (unsigned)(a.R + a.C);
+  const unsigned first_slot = (unsigned)(a.nq % rsz);
+  const uint8_t *sinkk = (const uint8_t *)a.sink_k + (size_t)bg * a.sink_bytes;
+  const uint8_t *sinkv = (const uint8_t *)a.sink_v + (size_t)bg * a.sink_bytes;
+  const uint8_t *ringk = (const uint8_t *)a.ring_k + (size_t)bg * a.ring_bytes;
+  const uint8_t *ringv = (const uint8_t *)a.ring_v + (size_t)bg * a.ring_bytes;
+  auto issue = [&](int item, uint8_t *dst) {
+    if (item < nb) {
+      stage_set<BV>(a, kplane, vplane, kpar, vpar, s0 + item, dst);
+    } else {
+      const int t0 = 8 * (ws0 + item - nb);
+      stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
+    }
+  };
+  if (nitems > 0) issue(0, ring);
 
   float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  if (w0 < w1) {
-    const int w = threadIdx.x >> 6;
-    float wacc[G][2], wm[G], wl[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) { wacc[h][0] = wacc[h][1] = 0.f; wm[h] = -INFINITY; wl[h] = 0.f; }
-    window_wave<G, BV>(a, sm, bg, w0, w1, w, wacc, wm, wl);
-    // packed lane layout: head hc's max in every lane of hc, its sum counted once
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (hc == h) {
-        m_run = wm[h];
-        l_lane = (q4 == 0 && tcol == 0) ? wl[h] : 0.f;
-      }
-    }
-    // window values -> rows (tile 0, head h) of the PV accumulators, through this
-    // wave's probability buffer (free again after the window pass)
-    float *buf = &sm.wp[w][0][0];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      buf[h * kD + 2 * lane] = wacc[h][0];
-      buf[h * kD + 2 * lane + 1] = wacc[h][1];
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * q4 + i;
-        O[ct][i] = m < G ? buf[m * kD + 16 * ct + col] : 0.f;
-      }
-    __builtin_amdgcn_wave_barrier();
-  }
 
   const bool kq = a.quant_k == WUSHKV_Q_QUEST, vq = a.quant_v == WUSHKV_Q_QUEST;
 
@@ -578,20 +600,36 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     }
   };
 
-  // body sets: set k + 1 is staged while set k computes
+  // items: item k + 1 is staged while item k computes
   using FullTag = std::integral_constant<bool, true>;
   using TailTag = std::integral_constant<bool, false>;
-  int slot = 0;
-  for (int64_t set = s0; set < s1; ++set) {
-    const int nslot = slot + 1 == kStages ? 0 : slot + 1;
-    const bool more = set + 1 < s1;
-    if (more) stage_set<BV>(a, kplane, vplane, kpar, vpar, set + 1, ring + nslot * SB);
+  int it = 0;
+  for (; it < nb; ++it) {
+    const bool more = it + 1 < nitems;
+    if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
     wait_staged<BV>(more ? 1 : 0);
     SetData<NGRP> cur;
-    read_set<NGRP, TPG, BV>(a, ring + slot * SB, cur);
+    read_set<NGRP, TPG, BV>(a, ring + (it & 1) * SB, cur);
+    const int64_t set = s0 + it;
     if ((set + 1) * kSet <= a.nq) compute(FullTag{}, set, cur);
     else compute(TailTag{}, set, cur);
-    slot = nslot;
+  }
+  float wm[G], wl[G], wacc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
+  for (; it < nitems; ++it) {
+    const bool more = it + 1 < nitems;
+    if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
+    wait_staged<BV>(more ? 1 : 0);
+    const int t0 = 8 * (ws0 + it - nb);
+    window_stage<G, BV>(sm, ring + (it & 1) * SB, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    wm_out[h] = wm[h];
+    wl_out[h] = wl[h];
+    wacc_out[h][0] = wacc[h][0];
+    wacc_out[h][1] = wacc[h][1];
   }
 
   // per-head totals; every lane of a head holds them
@@ -600,92 +638,63 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   z_out = head_sum<G>(zacc);
 }
 
-// Row of window-list token t: sink row t, or the ring slot of the t-th token after the
-// sink (first_slot = slot of the oldest recent token); the sign bit marks the ring.
-__device__ __forceinline__ int window_row(int t, int ns, unsigned first_slot, unsigned ring) {
-  return t < ns ? t : (int)(((first_slot + (unsigned)(t - ns)) % ring) | 0x80000000u);
-}
-
-// One window wave: window-list tokens [t0, t1) (sink tokens first, then recent), on
-// plain fp32 VALU in passes of 16 tokens.  Scores: four lanes per token, 32 channels
-// each, summed over the quad; values: lane = two channels.  A pass issues all of its
-// key and value loads before using any of them.
+// One window stage: cnt <= 8 FP16 window tokens in a ring slot, on fp32 VALU.  Scores:
+// 8 lanes per token, 16 channels each, summed over the 8; values: lane = two
+// channels.  The stage folds into this wave's window partial: per head the running
+// max and sum (the same in every lane) and this lane's two weighted value channels.
 template <int G, int BV>
-__device__ void window_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int t0, int t1, int w,
-                            float (&acc)[G][2], float (&mrun)[G], float (&lrun)[G]) {
+__device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
+                             float (&wl)[G], float (&wacc)[G][2]) {
+  using S = Stage<BV>;
   const int lane = threadIdx.x & 63;
-  const int ti = lane >> 2, qq = lane & 3;   // token of the pass, quarter of the channels
+  const int j = lane >> 3, cc = lane & 7;   // token of the stage, 16-channel chunk
   const float qk_scale = kLog2e * 0.08838834764831845f;
-  const int ns = (int)(a.n < a.S ? a.n : a.S);
-  const unsigned ring = (unsigned)(a.R + a.C);
-  const unsigned first_slot = (unsigned)(a.nq % ring);
-  const _Float16 *sink_k = (const _Float16 *)((const char *)a.sink_k + (size_t)bg * a.sink_bytes);
-  const _Float16 *sink_v = (const _Float16 *)((const char *)a.sink_v + (size_t)bg * a.sink_bytes);
-  const _Float16 *ring_k = (const _Float16 *)((const char *)a.ring_k + (size_t)bg * a.ring_bytes);
-  const _Float16 *ring_v = (const _Float16 *)((const char *)a.ring_v + (size_t)bg * a.ring_bytes);
-  constexpr int kPass = 16;
-  for (int p0 = t0; p0 < t1; p0 += kPass) {
-    const int cnt = (t1 - p0) < kPass ? (t1 - p0) : kPass;
-    const bool valid = ti < cnt;
-    const int rr = window_row(p0 + (valid ? ti : 0), ns, first_slot, ring);
-    const _Float16 *krow = (rr >= 0 ? sink_k + (size_t)rr * kD : ring_k + (size_t)(rr & 0x7FFFFFFF) * kD) + 32 * qq;
-    f16x8 kv[4];
+  const bool valid = j < cnt;
+  const f16x8 k0 = *(const f16x8 *)(st + S::WK + 256 * j + 32 * cc);
+  const f16x8 k1 = *(const f16x8 *)(st + S::WK + 256 * j + 32 * cc + 16);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kv[c] = valid ? *(const f16x8 *)(krow + 8 * c) : (f16x8){};
-    f16x2 vv[kPass];
+  for (int h = 0; h < G; ++h) {
+    float x = 0.f;
 #pragma unroll
-    for (int u = 0; u < kPass; ++u) {
-      const int ru = window_row(p0 + (u < cnt ? u : 0), ns, first_slot, ring);
-      const _Float16 *vrow = ru >= 0 ? sink_v + (size_t)ru * kD : ring_v + (size_t)(ru & 0x7FFFFFFF) * kD;
-      vv[u] = u < cnt ? *(const f16x2 *)(vrow + 2 * lane) : (f16x2){};
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 qv = *(const f32x4 *)&sm.q[h][16 * cc + 4 * c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x = fmaf(qv[e], (float)(c < 2 ? k0[4 * c + e] : k1[4 * (c - 2) + e]), x);
     }
-    float s[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float x = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x4 q0 = *(const f32x4 *)&sm.q[h][32 * qq + 8 * c];
-        const f32x4 q1 = *(const f32x4 *)&sm.q[h][32 * qq + 8 * c + 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x = fmaf(q0[e], (float)kv[c][e], x);
-          x = fmaf(q1[e], (float)kv[c][4 + e], x);
-        }
-      }
-      x += __shfl_xor(x, 1);
-      x += __shfl_xor(x, 2);
-      s[h] = x;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float sc = valid ? s[h] * qk_scale : -INFINITY;
-      const float mx = wave_max(sc);
-      const float mn = fmaxf(mrun[h], mx);
-      const float al = __builtin_amdgcn_exp2f(mrun[h] - mn);
-      const float pr = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-      lrun[h] = lrun[h] * al + wave_sum(qq == 0 ? pr : 0.f);
-      mrun[h] = mn;
-      acc[h][0] *= al;
-      acc[h][1] *= al;
-      if (qq == 0) sm.wp[w][h][ti] = pr;
-    }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int u = 0; u < kPass; ++u) {
-      if (u >= cnt) break;
-      const float v0 = (float)vv[u][0], v1 = (float)vv[u][1];
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float pr = sm.wp[w][h][u];
-        acc[h][0] = fmaf(pr, v0, acc[h][0]);
-        acc[h][1] = fmaf(pr, v1, acc[h][1]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+    x += __shfl_xor(x, 1);
+    x += __shfl_xor(x, 2);
+    x += __shfl_xor(x, 4);
+    // every lane of token j holds its score; max and sum run over the 8 tokens
+    const float sc = valid ? x * qk_scale : -INFINITY;
+    float mx = fmaxf(sc, __shfl_xor(sc, 8));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(wm[h], mx);
+    const float al = __builtin_amdgcn_exp2f(wm[h] - mn);
+    const float pr = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
+    float ps = pr + __shfl_xor(pr, 8);
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    if (cc == 0) sm.wp[w][h][j] = pr;
+    wl[h] = wl[h] * al + ps;
+    wm[h] = mn;
+    wacc[h][0] *= al;
+    wacc[h][1] *= al;
   }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int u = 0; u < cnt; ++u) {
+    const f16x2 vv = *(const f16x2 *)(st + S::WV + 256 * u + 4 * lane);
+    const float v0 = (float)vv[0], v1 = (float)vv[1];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float pr = sm.wp[w][h][u];
+      wacc[h][0] = fmaf(pr, v0, wacc[h][0]);
+      wacc[h][1] = fmaf(pr, v1, wacc[h][1]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
 }
 
 template <int G, int BV>
@@ -719,16 +728,26 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
 
   f32x4 O[8];
   float bm = -INFINITY, bl = 0.f, bz = 0.f;
+  float wm[G], wl[G], wacc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
   const int part = (int)blockIdx.x * kWaves + w;
   if (part < a.P) {
     const int64_t nsets = (a.nq + kSet - 1) / kSet;
     const int64_t s0 = nsets * part / a.P, s1 = nsets * (part + 1) / a.P;
     const int64_t ns = a.n < a.S ? a.n : a.S;
     const int64_t nw = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
-    const int w0 = (int)(nw * part / a.P), w1 = (int)(nw * (part + 1) / a.P);
-    body_wave<G, BV>(a, sm, bg, s0, s1, w0, w1, O, bm, bl, bz);
+    const int64_t nws = (nw + 7) / 8;
+    const int ws0 = (int)(nws * part / a.P), ws1 = (int)(nws * (part + 1) / a.P);
+    body_wave<G, BV>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
   }
-  __syncthreads();  // everyone is done with the q / q~ / probability buffers aliased by u.o
+  __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    sm.u.wo[w][h][2 * lane] = wacc[h][0];
+    sm.u.wo[w][h][2 * lane + 1] = wacc[h][1];
+    if (lane == 0) { sm.wmx[w][h] = wm[h]; sm.wls[w][h] = wl[h]; }
+  }
   if (part < a.P) {
     if (lane < G) { sm.m[w][lane] = bm; sm.l[w][lane] = bl; sm.z[w][lane] = bz; }
     const int q4 = lane >> 4, col = lane & 15;
@@ -751,18 +770,26 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     const int hh = i / kD, j = i % kD;
     float mstar = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww)
+    for (int ww = 0; ww < kWaves; ++ww) {
       if (sm.l[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.m[ww][hh]);
+      if (sm.wls[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.wmx[ww][hh]);
+    }
     float num = 0.f, den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      if (!(sm.l[ww][hh] > 0.f)) continue;
-      const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
-      float o = sm.z[ww][hh];
+      if (sm.l[ww][hh] > 0.f) {
+        const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
+        float o = sm.z[ww][hh];
 #pragma unroll
-      for (int tp = 0; tp < 16 / G; ++tp) o += sm.u.o[ww][G * tp + hh][j];
-      num = fmaf(f, o, num);
-      den = fmaf(f, sm.l[ww][hh], den);
+        for (int tp = 0; tp < 16 / G; ++tp) o += sm.u.o[ww][G * tp + hh][j];
+        num = fmaf(f, o, num);
+        den = fmaf(f, sm.l[ww][hh], den);
+      }
+      if (sm.wls[ww][hh] > 0.f) {
+        const float f = __builtin_amdgcn_exp2f(sm.wmx[ww][hh] - mstar);
+        num = fmaf(f, sm.u.wo[ww][hh][j], num);
+        den = fmaf(f, sm.wls[ww][hh], den);
+      }
     }
     const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1 + blockIdx.x;
     a.part_o[row * kD + j] = num;
