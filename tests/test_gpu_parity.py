@@ -173,3 +173,60 @@ def test_fast_decode_matches_generic_kernel(wl, P, monkeypatch):
     say(f"[fast vs generic] {wl} P={P} rel-L2 {rel:.3e}")
     assert rel < 1e-4
     r.check_decode(q, qt, fast)
+
+
+# ---- full-size workloads, in the launch configuration the benchmark times, checked on
+# sampled (batch row, KV head) pairs (the oracle builds each sampled head's whole cache)
+
+def test_c2_serving_full_size_sampled():
+    w = configs.SERVING                       # B=32, n=32768, affine 2/2-bit, chunk 16
+    r = Run(w)
+    r.append(w.context)
+    heads = [(0, 0), (13, 5), (31, 7)]
+    _, stats = r.check_cache(heads)
+    say(f"[c2 full] cache {stats}")
+    r.append(1)
+    q, qt, out = r.decode(0, num_splits=0)    # the library's split choice, as timed
+    r.check_decode(q, qt, out, heads=heads)
+
+
+def test_c4_long_context_full_size_sampled():
+    w = configs.LONG_CONTEXT                  # B=8, n=131072, G=8, affine K 2-bit / V 3-bit
+    r = Run(w)
+    r.append(w.context)
+    heads = [(0, 0), (7, 6)]
+    _, stats = r.check_cache(heads)
+    say(f"[c4 full] cache {stats}")
+    r.append(1)
+    q, qt, out = r.decode(0, num_splits=w.num_splits)
+    r.check_decode(q, qt, out, heads=heads)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_c3_bulk_flush_full_size_sampled(bits):
+    # one of the 36 layer calls: 8 KV heads x 65536 tokens, the timed launch
+    w = configs.BULK_FLUSH.scaled(bits_k=bits, bits_v=bits)
+    r = Run(w, layer=5, n_total=w.context)
+    r.append(w.context)
+    _, stats = r.check_cache([(0, 1), (0, 6)])
+    say(f"[c3 full bits={bits}] {stats}")
+
+
+def test_degenerate_rows():
+    """All-zero rows (QuEST step 0 -> code L/2; affine scale 0 -> code 0) and
+    constant rows (affine hi == lo) in both K and V, flushed and decoded."""
+    for quant in ("quest", "affine"):
+        w = configs.SERVING.scaled(name=f"degen_{quant}", seed=31, batch=1, num_kv_heads=2, num_q_heads=8,
+                                   context=700, decode_steps=1, quant_k=quant, quant_v=quant, chunk=8)
+        r = Run(w)
+        k, v = r.k, r.v
+        k[:, :, 100:140] = 0
+        v[:, :, 120:160] = 0
+        k[:, 1, 300:340] = 1.5
+        v[:, 0, 310:350] = -0.75
+        r.append(w.context)
+        _, stats = r.check_cache()
+        say(f"[degenerate {quant}] {stats}")
+        r.append(1)
+        q, qt, out = r.decode(0)
+        r.check_decode(q, qt, out)
