@@ -1,36 +1,64 @@
 // Query transform q~ = T^{-T} q per query head (WUSH-KV digest, "method key points":
 // the query side of the key transform is one d x d product per query, which keeps
-// q~ . (T k) = q . k).  One workgroup per (batch row, query head); thread i forms
-// output channel i from the row i of T^{-T} with four interleaved fp32 partial sums.
+// q~ . (T k) = q . k).
+//
+// One workgroup per (batch row, KV head): the head's T^{-T} is staged in LDS once
+// (coalesced 16-byte loads) and serves all of its query heads.  Thread t forms output
+// channel t % d of query head t / d (and the heads 256 / d further on), reading its row
+// of T^{-T} from LDS with four interleaved fp32 partial sums.
 #include "wushkv_internal.h"
 
 namespace wushkv {
 namespace {
 
-__global__ void __launch_bounds__(128) qtransform_kernel(QtArgs a) {
-  __shared__ float qs[128];
-  const int bh = blockIdx.x;
-  const int h = bh % a.Hq;
-  const int g = h / (a.Hq / a.Hkv);
-  const int i = threadIdx.x;
-  if (i < a.d) qs[i] = load_in(a.q, a.q_dtype, (size_t)bh * a.d + i);
-  __syncthreads();
-  if (i >= a.d) return;
-  const float *row = a.tinvt + ((size_t)g * a.d + i) * a.d;
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-  for (int j = 0; j < a.d; j += 4) {
-    s0 = fmaf(row[j], qs[j], s0);
-    s1 = fmaf(row[j + 1], qs[j + 1], s1);
-    s2 = fmaf(row[j + 2], qs[j + 2], s2);
-    s3 = fmaf(row[j + 3], qs[j + 3], s3);
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+constexpr int kHeadChunk = 16;   // query heads staged at a time
+
+template <int D>
+__global__ void __launch_bounds__(kThreads) qtransform_kernel(QtArgs a) {
+  __shared__ float T[D][D + 4];            // +4: rows start in different banks
+  __shared__ float qs[kHeadChunk][D];
+  const int tid = threadIdx.x;
+  const int bg = blockIdx.x;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const float *src = a.tinvt + (size_t)g * D * D;
+  for (int i = tid; i < D * D / 4; i += kThreads) {
+    const int r = i / (D / 4), c4 = i % (D / 4);
+    *(f32x4 *)&T[r][4 * c4] = *(const f32x4 *)(src + (size_t)r * D + 4 * c4);
   }
-  a.qt[(size_t)bh * a.d + i] = (s0 + s1) + (s2 + s3);
+  for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
+    const int nh = G - h0 < kHeadChunk ? G - h0 : kHeadChunk;
+    const size_t qbase = ((size_t)b * a.Hq + (size_t)g * G + h0) * D;
+    __syncthreads();   // T staged; the previous chunk's qs reads are done
+    for (int i = tid; i < nh * D; i += kThreads) qs[i / D][i % D] = load_in(a.q, a.q_dtype, qbase + i);
+    __syncthreads();
+    for (int o = tid; o < nh * D; o += kThreads) {
+      const int h = o / D, i = o % D;
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int j = 0; j < D; j += 4) {
+        const f32x4 t = *(const f32x4 *)&T[i][j];
+        const f32x4 x = *(const f32x4 *)&qs[h][j];
+        s[0] = fmaf(t[0], x[0], s[0]);
+        s[1] = fmaf(t[1], x[1], s[1]);
+        s[2] = fmaf(t[2], x[2], s[2]);
+        s[3] = fmaf(t[3], x[3], s[3]);
+      }
+      a.qt[qbase + o] = (s[0] + s[1]) + (s[2] + s[3]);
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_qtransform(const QtArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(qtransform_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a);
+  if (a.d == 128)
+    hipLaunchKernelGGL(qtransform_kernel<128>, dim3(a.B * a.Hkv), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(qtransform_kernel<64>, dim3(a.B * a.Hkv), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
