@@ -11,24 +11,24 @@
 // the dot product and q~ . c is an integer-code contraction.
 //
 // Grid (ceil(P/4), B * Hkv), 256 threads.  Each wave streams the 64-token sets of one
-// KV partition:
-//   QK: v_mfma_i32_16x16x64_i8.  A = one 16-token tile of 2-bit codes spread to
-//       bytes, B = q~ split into three signed 8-bit digits (q~ ~ alpha*(65536 d0 +
-//       256 d1 + d2)), one digit per group of G columns, so the integer dot products
-//       are exact and q~ keeps ~23 bits.  The digit columns are recombined in fp32
-//       with DPP row shifts and the tiles are packed into full 64-lane registers
-//       (lane column = G * tile + head) with bank-masked DPP moves.
-//   softmax: online, base 2, per head; W = p * s_V as an fp16 hi + lo pair.
-//   PV: v_mfma_f32_16x16x32_f16.  A = W (row = tile * G + head, zero outside the
-//       row's own tile), B = value codes read straight from the set layout: a
-//       field pair is one and/or with an fp16 exponent pattern, giving BASE + c
-//       (BASE = 4, 16 or 64 by the pair's position); BASE * W is removed exactly
-//       through the per-head zero term.  W enters as two MFMAs (hi and lo fp16
-//       parts), so its rounding does not show in the output.
-// Each partition wave first takes its share of the FP16 sink + recent tokens on
-// plain fp32 VALU, which seeds its softmax state, then streams its body sets.
-// Each workgroup merges its 4 waves in LDS and writes one partial (m, l, o); the
-// merge kernel that follows on the stream combines the partials.
+// KV partition through a two-slot LDS ring filled by load-to-LDS DMA (the next set is
+// in flight while the current one is computed):
+//   QK: v_mfma_scale_f32_16x16x128_f8f6f4, A = q~ as six balanced base-16 digits
+//       (integers in [-8, 7], exact in e4m3) on one fixed-point grid per head, B = the
+//       key codes as fp4 (a code c in a nibble's low bits is exactly c / 2), so each
+//       dot product is exact and q~ keeps ~23 bits.  Rows of the result are (head,
+//       digit), columns tokens; the digits are summed per lane, smallest first.
+//   softmax: online, base 2, per head (DPP reductions over the 16 token columns);
+//       W = p * s_V as an fp16 hi + lo pair, passed through LDS as the PV A operand.
+//   PV: v_mfma_f32_16x16x32_f16.  A = W rows (head) over the set's tokens, B = value
+//       codes read straight from the set layout: a field pair is one and/or with an
+//       fp16 exponent pattern, giving BASE + c (BASE = 4, 16 or 64 by the pair's
+//       position); BASE * W is removed exactly through the per-head zero term.  W
+//       enters as two MFMAs (hi and lo fp16 parts), so its rounding does not show.
+// The FP16 sink + recent tokens follow the body sets through the same ring, 8 rows per
+// stage, on fp32 VALU in a softmax partial of their own.  Each workgroup merges its 4
+// waves in LDS and writes one partial (m, l, o); the merge kernel that follows on the
+// stream combines the partials.
 #include <type_traits>
 
 #include "wushkv_internal.h"
@@ -36,7 +36,7 @@
 namespace wushkv {
 namespace {
 
-typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -48,18 +48,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// DPP encodings (gfx9): row_shl:n = 0x100+n (lane i reads i+n), row_shr:n = 0x110+n
-// (lane i reads i-n), row_ror:n = 0x120+n; bank b = lanes 4b..4b+3 of each row.
-// acc += src[lane + 4 or 8 in the row] * k as one v_fmac_f32_dpp; a lane whose source
-// lies outside its row keeps acc.  The s_nop 1 gives the two wait states a DPP read
-// needs after a VALU write of its source (the compiler does not see into asm).
-__device__ __forceinline__ void fmac_shl4(float &acc, float src, float k) {
-  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_shl:4 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(src), "v"(k));
-}
-__device__ __forceinline__ void fmac_shl8(float &acc, float src, float k) {
-  asm("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_shl:8 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(src), "v"(k));
-}
-
+// DPP encodings (gfx9): row_ror:n = 0x120 + n rotates within a row of 16 lanes,
+// quad_perm [2,3,0,1] = 0x4E and [1,0,3,2] = 0xB1 swap within groups of four lanes.
 template <int CTRL, int BANK = 0xF>
 __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
@@ -82,8 +72,11 @@ constexpr int kStages = 2;   // body sets staged per wave: the one computed and 
 
 template <int G, int BV>
 struct __align__(16) FastSmem {
-  float qt[G][kD];
+  unsigned qi[G][kD];             // q~ in fixed point, offset to unsigned (balanced digits)
   float q[G][kD];
+  unsigned wb[kWaves][G][kSet];   // body set: W as fp16 (hi | lo << 16) [head][token]
+  unsigned wzero[kSet];           // zeros: the PV A rows past G read these
+  int qe[16];                     // per head: q~ = (qi - kDigitBias) 2^(e - 21)
   float wp[kWaves][G][8];         // window stage: probabilities [head][token]
   float wmx[kWaves][16], wls[kWaves][16];  // window partial: max and sum per head
   union {
@@ -93,26 +86,9 @@ struct __align__(16) FastSmem {
       float wo[kWaves][G][kD];    // window partial: weighted FP16 values [head][channel]
     };
   } u;
-  float alpha[16], sq[16];
+  float sq[16];                   // per head: sum of q~ (the zero-point term)
   float m[kWaves][16], l[kWaves][16], z[kWaves][16];
 };
-
-__device__ __forceinline__ int digit_of(float qt, float inv_alpha, int dg) {
-  int Q = (int)rintf(qt * inv_alpha);
-  int d2 = ((Q + 128) & 255) - 128;
-  int Q1 = (Q - d2) >> 8;
-  int d1 = ((Q1 + 128) & 255) - 128;
-  int d0 = (Q1 - d1) >> 8;
-  return dg == 0 ? d0 : (dg == 1 ? d1 : d2);
-}
-
-__device__ __forceinline__ unsigned pack_h2(float x, float y) {
-  f16x2 v = {(_Float16)x, (_Float16)y};
-  return __builtin_bit_cast(unsigned, v);
-}
-
-__device__ __forceinline__ float h_lo(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
-__device__ __forceinline__ float h_hi(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 
 // A 32-bit constant held in a VGPR the compiler cannot fold, so masks and exponent
 // patterns feed three-operand VALU forms (gfx9 VOP3 has no literal operand).
@@ -189,57 +165,65 @@ __device__ __forceinline__ f16x8 v_operand(unsigned w, unsigned hi, int iota, co
   return __builtin_bit_cast(f16x8, r);
 }
 
-__device__ __forceinline__ i32x4 k_operand(unsigned w) {
-  i32x4 r;
-  r[0] = (int)(w & 0x03030303u);
-  r[1] = (int)((w >> 2) & 0x03030303u);
-  r[2] = (int)((w >> 4) & 0x03030303u);
-  r[3] = (int)((w >> 6) & 0x03030303u);
-  return r;
+// QK on v_mfma_scale_f32_16x16x128_f8f6f4 with A = q~ digits (fp8 e4m3) and B = key
+// codes (fp4 e2m1: a 2-bit code c in the low bits of a nibble is exactly c / 2).
+// Operand maps of that instruction (16 x 16 x 128): fp4 B lane l holds column l % 16,
+// K-slots 32 (l / 16) + nibble (low nibble first); fp8 A lane l holds row l % 16, bytes
+// 0..15 at K 16 (l / 16) + byte and bytes 16..31 at K 64 + 16 (l / 16) + byte - 16; the
+// E8M0 scale byte of lane l scales its row (A) / column (B) over K-block l / 16.
+// A key word (16 codes, code f at bits 2f) gives two B dwords with one mask each:
+// (w & 0x33333333) holds the even codes, ((w >> 2) & 0x33333333) the odd ones, so
+// K-slot 32 g + 8 d + i of lane group g reads channel 32 g + 16 (d >> 1) + 2 i + (d & 1).
+__device__ __forceinline__ int kslot_channel(int k) {
+  const int g = k >> 5, n = k & 31, d = n >> 3, i = n & 7;
+  return 32 * g + 16 * (d >> 1) + 2 * i + (d & 1);
 }
 
+__device__ __forceinline__ int a_kslot(int g, int jb) { return jb < 16 ? 16 * g + jb : 64 + 16 * g + (jb - 16); }
+
+// Offset that makes six balanced base-16 digits (each in [-8, 7]) unsigned nibbles:
+// u = Q + 0x888888 for integers |Q| <= 0x777777.
+constexpr unsigned kDigitBias = 0x888888u;
+
+// Head and digit of row r of q~ operand m: G = 4: operand 0 digits 0-3 (row 4 h + j),
+// operand 1 digits 4-5 (rows 4 h + j - 4, rows with j >= 6 unused).  G = 8: operands 0 and
+// 1 digits 0-3 of heads 0-3 and 4-7, operand 2 digits 4-5 of heads g and g + 4 in rows
+// 4 g + i (i = 0, 1: head g; 2, 3: head g + 4).
 template <int G>
-__device__ __forceinline__ float head_max(float x) {
-  if constexpr (G == 4) {
-    x = fmaxf(x, dpp<0x124>(x, x));
-    x = fmaxf(x, dpp<0x128>(x, x));
+__device__ __forceinline__ void digit_row(int m, int r, int &h, int &j) {
+  if (G == 4) {
+    h = r >> 2;
+    j = 4 * m + (r & 3);
+  } else if (m < 2) {
+    h = 4 * m + (r >> 2);
+    j = r & 3;
   } else {
-    x = fmaxf(x, dpp<0x128>(x, x));
+    h = (r >> 2) + 4 * ((r & 3) >> 1);
+    j = 4 + (r & 1);
   }
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+}
+
+__device__ __forceinline__ i32x8 key_fp4(u32x2 w) {
+  const unsigned M = 0x33333333u;
+  return (i32x8){(int)(w[0] & M), (int)((w[0] >> 2) & M), (int)(w[1] & M), (int)((w[1] >> 2) & M), 0, 0, 0, 0};
+}
+
+// Max / sum over the 16 lanes of a row (DPP rotations within the row, then quad swaps).
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp<0x128>(x, x));
+  x = fmaxf(x, dpp<0x124>(x, x));
+  x = fmaxf(x, dpp<0x4E>(x, x));
+  x = fmaxf(x, dpp<0xB1>(x, x));
   return x;
 }
 
-template <int G>
-__device__ __forceinline__ float head_sum(float x) {
-  if constexpr (G == 4) {
-    x += dpp<0x124>(x, x);
-    x += dpp<0x128>(x, x);
-  } else {
-    x += dpp<0x128>(x, x);
-  }
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<0x128>(x, x);
+  x += dpp<0x124>(x, x);
+  x += dpp<0x4E>(x, x);
+  x += dpp<0xB1>(x, x);
   return x;
 }
-
-__device__ __forceinline__ float wave_max(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-template <int NGRP>
-struct SetData {
-  u32x2 kw[4];          // key codes: words 2*q4, 2*q4+1 of rows 16T + col
-  u32x4 vw0, vw1, vh;   // value words of this lane (8 column tiles), 3rd-bit plane
-  u32x4 kp[NGRP], vp[NGRP];  // per-token parameters of this lane's 4 packed tokens
-};
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -306,102 +290,74 @@ __device__ __forceinline__ void wait_staged(int pending) {
   else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
 }
 
-// This lane's operands of a staged set.
-template <int NGRP, int TPG, int BV>
-__device__ __forceinline__ void read_set(const DecodeArgs &a, const uint8_t *st, SetData<NGRP> &d) {
-  using S = Stage<BV>;
-  const int lane = threadIdx.x & 63;
-  const int q4 = lane >> 4, col = lane & 15;
-  const int tcol = col / (16 / TPG);
-#pragma unroll
-  for (int T = 0; T < 4; ++T) d.kw[T] = *(const u32x2 *)(st + S::K + (16 * T + col) * 32 + 8 * q4);
-  d.vw0 = *(const u32x4 *)(st + S::V + 32 * lane);
-  d.vw1 = *(const u32x4 *)(st + S::V + 32 * lane + 16);
-  if constexpr (BV == 3) d.vh = *(const u32x4 *)(st + S::VH + 16 * lane);
-  else d.vh = (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int gr = 0; gr < NGRP; ++gr) {
-    const int t0 = 16 * (TPG * gr + tcol) + 4 * q4;
-    if (a.quant_k == WUSHKV_Q_QUEST) {
-      const u32x2 x = *(const u32x2 *)(st + S::KP + 2 * t0);
-      d.kp[gr] = (u32x4){x[0], x[1], 0u, 0u};
-    } else {
-      d.kp[gr] = *(const u32x4 *)(st + S::KP + 4 * t0);
-    }
-    if (a.quant_v == WUSHKV_Q_QUEST) {
-      const u32x2 x = *(const u32x2 *)(st + S::VP + 2 * t0);
-      d.vp[gr] = (u32x4){x[0], x[1], 0u, 0u};
-    } else {
-      d.vp[gr] = *(const u32x4 *)(st + S::VP + 4 * t0);
-    }
-  }
-}
-
 template <int G, int BV>
 __device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
                              float (&wl)[G], float (&wacc)[G][2]);
 
 // One wave of a KV partition: its body sets [s0, s1), then its 8-token stages
 // [ws0, ws1) of the FP16 window list, all streamed through the wave's LDS ring.
+// Lane (h, t) = (lane / 16, lane % 16) scores token 16 T + t of each set (T = 0..3) for
+// heads h + 4 qd (qd < G / 4).  PV output rows are heads: O lane l holds heads
+// 4 (l / 16) + i, channels 16 ct + l % 16.
 template <int G, int BV>
 __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
-                          f32x4 (&O)[8], float &m_out, float &l_out, float &z_out, float (&wm_out)[G],
-                          float (&wl_out)[G], float (&wacc_out)[G][2]) {
-  constexpr int TPG = 16 / G;          // tiles per packed register group
-  constexpr int NGRP = 4 / TPG;        // groups per 64-token set
-  constexpr int NMF = (3 * G + 15) / 16;  // QK MFMAs per (tile, k-step)
+                          f32x4 (&O)[8], float (&m_out)[G / 4], float (&l_out)[G / 4], float (&z_out)[G / 4],
+                          float (&wm_out)[G], float (&wl_out)[G], float (&wacc_out)[G][2]) {
+  constexpr int NQ = G / 4;            // head quads: QK MFMAs per tile
   const int lane = threadIdx.x & 63;
-  const int q4 = lane >> 4, col = lane & 15;
-  const int hc = col % G;              // head of this lane's packed column
-  const int tcol = col / G;            // tile within a packed group
+  const int g4 = lane >> 4, t16 = lane & 15;
+  const int w = threadIdx.x >> 6;
   const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
-  const int Lk = 4, Lv = 1 << BV;
+  const int Lv = 1 << BV;
 
-  // q~ digits as B operands: column c of MFMA mf holds digit dg of head h
-  i32x4 bq[NMF][2];
+  // q~ as six balanced base-16 digits (integers in [-8, 7], exact in e4m3) on one fixed
+  // point grid per head, in the rows of NM A operands: row r of operand m holds digit j
+  // of head h (digit_row), weighted 2^(e - 1 - 4 j) through the row's E8M0 scale.  On a
+  // common grid every product of a digit MFMA is a multiple of 1/2 below 13, which the
+  // matrix core sums exactly (it does not for operands of mixed exponents).  Lane
+  // (g4, t16)'s result rows 4 g4 + i are digits of its heads.
+  constexpr int NM = G == 4 ? 2 : 3;
+  i32x8 aq[NM];
+  int sa[NM];
 #pragma unroll
-  for (int mf = 0; mf < NMF; ++mf) {
-    int dg, h;
-    bool live;
-    if constexpr (G == 4) { dg = col >> 2; h = col & 3; live = col < 12; }
-    else { dg = mf == 0 ? (col >> 3) : 2; h = col & 7; live = mf == 0 || col < 8; }
-    const float inv_alpha = live ? 1.0f / sm.alpha[h] : 0.f;
+  for (int m = 0; m < NM; ++m) {
+    const int r = lane & 15;
+    int h, j;
+    digit_row<G>(m, r, h, j);
+    const int sft = 20 - 4 * j;
+    unsigned wd[8];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int d = 0; d < 8; ++d) {
+      unsigned word = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        unsigned word = 0;
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-          const int ch = 16 * (2 * q4 + s) + 4 * bb + k;
-          const int dig = live ? digit_of(sm.qt[h][ch], inv_alpha, dg) : 0;
-          word |= ((unsigned)dig & 0xFFu) << (8 * bb);
-        }
-        bq[mf][s][k] = (int)word;
+      for (int bb = 0; bb < 4; ++bb) {
+        const int ch = kslot_channel(a_kslot(g4, 4 * d + bb));
+        const int dig = (int)((sm.qi[h][ch] >> (sft & 31)) & 15u) - 8;
+        word |= (j < 6 ? (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32((float)dig, 0.f, 0, false) & 0xFFu : 0u)
+                << (8 * bb);
       }
+      wd[d] = word;
     }
+    aq[m] = (i32x8){(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3], (int)wd[4], (int)wd[5], (int)wd[6], (int)wd[7]};
+    sa[m] = j < 6 ? 126 + sm.qe[h] - 4 * j : 127;
   }
-  const float a_sc = sm.alpha[hc] * 65536.0f * qk_scale;
-  const float b_sc = sm.sq[hc] * qk_scale;
+  // scores: s (q~ . c) + z sum(q~); the MFMA sums q~ . (c / 2)
+  float a_sc = 2.0f * qk_scale, b_sc[NQ];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) b_sc[qd] = sm.sq[4 * qd + g4] * qk_scale;
   const VConst vc = make_vconst();
-  // digit weights as VGPR values so the DPP reads fuse into v_fmac_f32_dpp
-  const float inv256 = __uint_as_float(vconst(0x3B800000u));    // 2^-8
-  const float inv65536 = __uint_as_float(vconst(0x37800000u));  // 2^-16
-  // BASE of the value operand that multiplies this lane's weights W[i] of packed
-  // group gr: the lane's tile T sits in PV instruction T/2 at pair 2T + i/2
-  float vbase[NGRP][2];
+  // BASE of the value operand for token 16 T + t16: pair 2 T + (t16 & 3) / 2 of its word
+  float vbase[4];
 #pragma unroll
-  for (int gr = 0; gr < NGRP; ++gr) {
-    const int T = TPG * gr + tcol;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) vbase[gr][hf] = BV == 2 ? vbase2(2 * T + hf) : 16.0f;
-  }
+  for (int T = 0; T < 4; ++T) vbase[T] = BV == 2 ? vbase2(2 * T + ((t16 & 3) >> 1)) : 16.0f;
+  // PV A rows: head r of this wave's W buffer, or zeros past G
+  const int ar = lane & 15;
+  const unsigned *arow = ar < G ? &sm.wb[w][ar][0] : &sm.wzero[0];
 
   const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
   const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
   const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
   const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
-  const int w = threadIdx.x >> 6;
   uint8_t *ring = &sm.u.ring[w][0][0];
   constexpr int SB = Stage<BV>::SIZE;
   // items of this wave: body sets s0 .. s1-1, then 8-token window stages ws0 .. ws1-1
@@ -424,7 +380,9 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   };
   if (nitems > 0) issue(0, ring);
 
-  float m_run = -INFINITY, l_lane = 0.f, zacc = 0.f;
+  float m_run[NQ], l_lane[NQ], zacc[NQ];
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) { m_run[qd] = -INFINITY; l_lane[qd] = 0.f; zacc[qd] = 0.f; }
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -432,134 +390,123 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 
   // one 64-token set: QK, softmax update, PV.  FULL: every token of the set is in
   // the body (no validity selects).
-  auto compute = [&](auto full_tag, int64_t set, const SetData<NGRP> &cur) {
+  auto compute = [&](auto full_tag, int64_t set, const uint8_t *st) {
     constexpr bool FULL = decltype(full_tag)::value;
+    using S = Stage<BV>;
     const int64_t base = set * kSet;
-    const u32x2 *kw = cur.kw;
-    const u32x4 vw0 = cur.vw0, vw1 = cur.vw1, vh = cur.vh;
-    const u32x4 *kp = cur.kp, *vp = cur.vp;
 
-    // ---- QK on the int8 MFMA (all tiles' first k-step before any second one, so no
-    // MFMA waits on the one just issued), digit recombination, packing
-    float C[NGRP][4];
-    i32x4 dq[4][NMF];
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int mf = 0; mf < NMF; ++mf)
-        dq[T][mf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k_operand(kw[T][0]), bq[mf][0], (i32x4){0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-    for (int T = 0; T < 4; ++T)
-#pragma unroll
-      for (int mf = 0; mf < NMF; ++mf)
-        dq[T][mf] = __builtin_amdgcn_mfma_i32_16x16x64_i8(k_operand(kw[T][1]), bq[mf][1], dq[T][mf], 0, 0, 0);
+    // ---- QK: one scaled MFMA per (tile, head quad); the lane's 4 result rows are the
+    // digits of its head, already weighted
+    float sc[NQ][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      float r[4];
+      const i32x8 bk = key_fp4(*(const u32x2 *)(st + S::K + (16 * T + t16) * 32 + 8 * g4));
+      f32x4 d[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        d[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[m], bk, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
+                                                                sa[m], 0, 127);
+      // small digits first
       if constexpr (G == 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // digit columns h, h+4, h+8 -> lane h; columns 12..15 hold zeros, so the first
-          // step leaves lanes 8..11 (read by the second) unchanged
-          float f = (float)dq[T][0][i];
-          fmac_shl4(f, f, inv256);
-          fmac_shl8(f, f, inv65536);
-          r[i] = f;
-        }
+        sc[0][T] = ((d[1][0] + d[1][1]) + (d[0][3] + d[0][2])) + (d[0][1] + d[0][0]);
       } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float f = (float)dq[T][0][i];
-          fmac_shl8(f, f, inv256);
-          r[i] = fmaf((float)dq[T][1][i], inv65536, f);
-        }
-      }
-      const int gr = T / TPG, tp = T % TPG;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (G == 4) {
-          if (tp == 0) C[gr][i] = r[i];
-          else if (tp == 1) C[gr][i] = dpp<0x114, 0x2>(C[gr][i], r[i]);
-          else if (tp == 2) C[gr][i] = dpp<0x118, 0x4>(C[gr][i], r[i]);
-          else C[gr][i] = dpp<0x11C, 0x8>(C[gr][i], r[i]);
-        } else {
-          if (tp == 0) C[gr][i] = r[i];
-          else C[gr][i] = dpp<0x118, 0xC>(C[gr][i], r[i]);
-        }
+        sc[0][T] = ((d[2][0] + d[2][1]) + (d[0][3] + d[0][2])) + (d[0][1] + d[0][0]);
+        sc[1][T] = ((d[2][2] + d[2][3]) + (d[1][3] + d[1][2])) + (d[1][1] + d[1][0]);
       }
     }
-
     // ---- scores and online softmax (base 2)
-    float sc[NGRP][4];
-    float mx = -INFINITY;
+    float mx[NQ];
 #pragma unroll
-    for (int gr = 0; gr < NGRP; ++gr) {
-      const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
+    for (int qd = 0; qd < NQ; ++qd) mx[qd] = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 4; ++T) {
+      const int u = 16 * T + t16;
+      float s_t, z_t;
+      if (kq) {
+        s_t = (float)*(const _Float16 *)(st + S::KP + 2 * u);
+        z_t = -1.5f * s_t;
+      } else {
+        const f16x2 pz = *(const f16x2 *)(st + S::KP + 4 * u);
+        s_t = (float)pz[0];
+        z_t = (float)pz[1];
+      }
+      const bool valid = FULL || base + u < a.nq;
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        sc[qd][T] = valid ? fmaf(s_t, sc[qd][T] * a_sc, z_t * b_sc[qd]) : -INFINITY;
+        mx[qd] = fmaxf(mx[qd], sc[qd][T]);
+      }
+    }
+    float alpha[NQ];
+    bool rescale = false;
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const float m_new = fmaxf(m_run[qd], row_max(mx[qd]));
+      alpha[qd] = __builtin_amdgcn_exp2f(m_run[qd] - m_new);
+      m_run[qd] = m_new;
+      rescale |= alpha[qd] != 1.0f;
+    }
+    if (__any(rescale)) {
+      // O row 4 (l / 16) + i is head 4 (l / 16) + i: its factor sits in lane group
+      // (row % 4), head quad row / 4
+      float f[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s_t, z_t;
-        if (kq) {
-          const unsigned pw = kp[gr][i >> 1];
-          s_t = (i & 1) ? h_hi(pw) : h_lo(pw);
-          z_t = -0.5f * (Lk - 1) * s_t;
-        } else {
-          s_t = h_lo(kp[gr][i]);
-          z_t = h_hi(kp[gr][i]);
+        f[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * i));
+        if constexpr (NQ == 2) {
+          const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[1]), 16 * i));
+          f[i] = g4 == 1 ? f1 : f[i];
         }
-        const bool valid = FULL || t0 + i < a.nq;
-        sc[gr][i] = valid ? fmaf(s_t, C[gr][i] * a_sc, z_t * b_sc) : -INFINITY;
-        mx = fmaxf(mx, sc[gr][i]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) O[ct][i] *= f[i];
+#pragma unroll
+      for (int qd = 0; qd < NQ; ++qd) {
+        l_lane[qd] *= alpha[qd];
+        zacc[qd] *= alpha[qd];
       }
     }
-    mx = head_max<G>(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    if (__any(alpha != 1.0f)) {
-      l_lane *= alpha;
-      zacc *= alpha;
+    // ---- p, W = p s_V as fp16 hi + lo into the wave's W buffer, zero term
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int src = (4 * q4 + i) % G;  // packed column of head (4*q4+i) % G, row 0
-        const float f = __shfl(alpha, src);
+    for (int T = 0; T < 4; ++T) {
+      const int u = 16 * T + t16;
+      float s_t, z_t;
+      if (vq) {
+        s_t = (float)*(const _Float16 *)(st + S::VP + 2 * u);
+        z_t = -0.5f * (Lv - 1) * s_t;
+      } else {
+        const f16x2 pz = *(const f16x2 *)(st + S::VP + 4 * u);
+        s_t = (float)pz[0];
+        z_t = (float)pz[1];
+      }
+      const bool valid = FULL || base + u < a.nq;
+      // the MFMA forms sum (hi + lo) (BASE + c); the zero term takes p z - BASE W with
+      // W in place of hi + lo (they differ by ~2^-22 W)
+      const float zb = fmaf(-vbase[T], s_t, z_t);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) O[ct][i] *= f;
+      for (int qd = 0; qd < NQ; ++qd) {
+        const float p = __builtin_amdgcn_exp2f(sc[qd][T] - m_run[qd]);
+        l_lane[qd] += p;
+        const float W = valid ? p * s_t : 0.f;
+        zacc[qd] = valid ? fmaf(p, zb, zacc[qd]) : zacc[qd];
+        const _Float16 hi = (_Float16)W;
+        const _Float16 lo = (_Float16)(W - (float)hi);
+        sm.wb[w][4 * qd + g4][u] = (unsigned)__builtin_bit_cast(unsigned short, hi) |
+                                   ((unsigned)__builtin_bit_cast(unsigned short, lo) << 16);
       }
     }
-    m_run = m_new;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    unsigned wp[NGRP][2], wl[NGRP][2];
-#pragma unroll
-    for (int gr = 0; gr < NGRP; ++gr) {
-      const int64_t t0 = base + 16 * (TPG * gr + tcol) + 4 * q4;
-      float W[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[gr][i] - m_run);
-        float s_t, z_t;
-        if (vq) {
-          const unsigned pw = vp[gr][i >> 1];
-          s_t = (i & 1) ? h_hi(pw) : h_lo(pw);
-          z_t = -0.5f * (Lv - 1) * s_t;
-        } else {
-          s_t = h_lo(vp[gr][i]);
-          z_t = h_hi(vp[gr][i]);
-        }
-        // W = p s enters the MFMA as fp16 hi + lo (~22 bits) against BASE + c; the
-        // zero term takes p z - BASE W, with W in place of hi + lo (they differ by
-        // ~2^-22 W, i.e. ~1.5e-5 W at BASE = 64)
-        const bool valid = FULL || t0 + i < a.nq;
-        l_lane += p;
-        W[i] = valid ? p * s_t : 0.f;
-        const float zb = fmaf(-vbase[gr][i >> 1], s_t, z_t);
-        zacc = valid ? fmaf(p, zb, zacc) : zacc;
-      }
-      wp[gr][0] = pack_h2(W[0], W[1]);
-      wp[gr][1] = pack_h2(W[2], W[3]);
-      wl[gr][0] = pack_h2(W[0] - h_lo(wp[gr][0]), W[1] - h_hi(wp[gr][0]));
-      wl[gr][1] = pack_h2(W[2] - h_lo(wp[gr][1]), W[3] - h_hi(wp[gr][1]));
-    }
-
-    // ---- PV on the f16 MFMA: instruction iota covers tiles 2*iota, 2*iota+1
+    // ---- PV on the f16 MFMA: instruction iota covers tiles 2 iota, 2 iota + 1; A row
+    // r = head, K-slots 8 c .. 8 c + 7 = tokens 16 a + 4 c + e of those tiles
+    const u32x4 vw0 = *(const u32x4 *)(st + S::V + 32 * lane);
+    const u32x4 vw1 = *(const u32x4 *)(st + S::V + 32 * lane + 16);
+    u32x4 vh = (u32x4){0u, 0u, 0u, 0u};
+    if constexpr (BV == 3) vh = *(const u32x4 *)(st + S::VH + 16 * lane);
     const unsigned vws[8] = {vw0[0], vw0[1], vw0[2], vw0[3], vw1[0], vw1[1], vw1[2], vw1[3]};
     unsigned hws[8];
 #pragma unroll
@@ -573,20 +520,14 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     }
 #pragma unroll
     for (int iota = 0; iota < 2; ++iota) {
-      const int T = TPG * ((G == 4) ? 0 : iota) + tcol;  // lane's tile for this instruction's group
-      const int gr = (G == 4) ? 0 : iota;
-      const bool mine = (T >> 1) == iota;
-      const int vp2 = 2 * (T & 1);
-      u32x4 av, al;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        av[v] = (mine && v == vp2) ? wp[gr][0] : ((mine && v == vp2 + 1) ? wp[gr][1] : 0u);
-        al[v] = (mine && v == vp2) ? wl[gr][0] : ((mine && v == vp2 + 1) ? wl[gr][1] : 0u);
-      }
-      const f16x8 Ah = __builtin_bit_cast(f16x8, av);
+      const u32x4 x0 = *(const u32x4 *)(arow + 16 * (2 * iota) + 4 * g4);
+      const u32x4 x1 = *(const u32x4 *)(arow + 16 * (2 * iota + 1) + 4 * g4);
+      const u32x4 ah = {__builtin_amdgcn_perm(x0[1], x0[0], 0x05040100u), __builtin_amdgcn_perm(x0[3], x0[2], 0x05040100u),
+                        __builtin_amdgcn_perm(x1[1], x1[0], 0x05040100u), __builtin_amdgcn_perm(x1[3], x1[2], 0x05040100u)};
+      const u32x4 al = {__builtin_amdgcn_perm(x0[1], x0[0], 0x07060302u), __builtin_amdgcn_perm(x0[3], x0[2], 0x07060302u),
+                        __builtin_amdgcn_perm(x1[1], x1[0], 0x07060302u), __builtin_amdgcn_perm(x1[3], x1[2], 0x07060302u)};
+      const f16x8 Ah = __builtin_bit_cast(f16x8, ah);
       const f16x8 Al = __builtin_bit_cast(f16x8, al);
-      // four column tiles at a time, hi parts before lo parts: each accumulator's
-      // second MFMA is issued three independent MFMAs after its first
 #pragma unroll
       for (int ct0 = 0; ct0 < 8; ct0 += 4) {
         f16x8 Bv[4];
@@ -598,6 +539,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
         for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv[c], O[ct0 + c], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_wave_barrier();
   };
 
   // items: item k + 1 is staged while item k computes
@@ -608,11 +550,9 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     const bool more = it + 1 < nitems;
     if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
     wait_staged<BV>(more ? 1 : 0);
-    SetData<NGRP> cur;
-    read_set<NGRP, TPG, BV>(a, ring + (it & 1) * SB, cur);
     const int64_t set = s0 + it;
-    if ((set + 1) * kSet <= a.nq) compute(FullTag{}, set, cur);
-    else compute(TailTag{}, set, cur);
+    if ((set + 1) * kSet <= a.nq) compute(FullTag{}, set, ring + (it & 1) * SB);
+    else compute(TailTag{}, set, ring + (it & 1) * SB);
   }
   float wm[G], wl[G], wacc[G][2];
 #pragma unroll
@@ -632,10 +572,13 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     wacc_out[h][1] = wacc[h][1];
   }
 
-  // per-head totals; every lane of a head holds them
-  m_out = m_run;
-  l_out = head_sum<G>(l_lane);
-  z_out = head_sum<G>(zacc);
+  // per-head totals; every lane of head 4 qd + lane / 16 holds them
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    m_out[qd] = m_run[qd];
+    l_out[qd] = row_sum(l_lane[qd]);
+    z_out[qd] = row_sum(zacc[qd]);
+  }
 }
 
 // One window stage: cnt <= 8 FP16 window tokens in a ring slot, on fp32 VALU.  Scores:
@@ -709,25 +652,36 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
   for (int i = tid; i < G * kD; i += kThreads) {
     const int hh = i / kD, j = i % kD;
     const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
-    sm.qt[hh][j] = a.qt[off];
+    sm.qi[hh][j] = __float_as_uint(a.qt[off]);
     sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
   }
   __syncthreads();
   if (tid < G) {
     float mxa = 0.f, s = 0.f;
     for (int j = 0; j < kD; ++j) {
-      const float v = sm.qt[tid][j];
+      const float v = __uint_as_float(sm.qi[tid][j]);
       mxa = fmaxf(mxa, fabsf(v));
       s += v;
     }
-    // q~ ~ alpha * Q with |Q| <= 127 * 65536, split into three signed 8-bit digits
-    sm.alpha[tid] = mxa > 0.f ? mxa / (127.0f * 65536.0f) : 1.0f;
+    // |q~| < 2^(e + 1); heads below 2^-100 count as zero (their digits are all zero)
+    sm.qe[tid] = mxa >= 0x1p-100f ? ilogbf(mxa) : -100;
     sm.sq[tid] = s;
+  }
+  if (tid < kSet) sm.wzero[tid] = 0u;
+  __syncthreads();
+  // fixed point: Q = rint(q~ 2^(21 - e)), |Q| <= 2^22, stored as Q + kDigitBias
+  for (int i = tid; i < G * kD; i += kThreads) {
+    const int hh = i / kD, j = i % kD;
+    const float v = __uint_as_float(sm.qi[hh][j]);
+    const int Q = (int)rintf(ldexpf(v, 21 - sm.qe[hh]));
+    sm.qi[hh][j] = (unsigned)(Q + (int)kDigitBias);
   }
   __syncthreads();
 
   f32x4 O[8];
-  float bm = -INFINITY, bl = 0.f, bz = 0.f;
+  float bm[G / 4], bl[G / 4], bz[G / 4];
+#pragma unroll
+  for (int qd = 0; qd < G / 4; ++qd) { bm[qd] = -INFINITY; bl[qd] = 0.f; bz[qd] = 0.f; }
   float wm[G], wl[G], wacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
@@ -740,6 +694,9 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     const int64_t nws = (nw + 7) / 8;
     const int ws0 = (int)(nws * part / a.P), ws1 = (int)(nws * (part + 1) / a.P);
     body_wave<G, BV>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
 #pragma unroll
@@ -748,18 +705,22 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     sm.u.wo[w][h][2 * lane + 1] = wacc[h][1];
     if (lane == 0) { sm.wmx[w][h] = wm[h]; sm.wls[w][h] = wl[h]; }
   }
-  if (part < a.P) {
-    if (lane < G) { sm.m[w][lane] = bm; sm.l[w][lane] = bl; sm.z[w][lane] = bz; }
+  {
+    // rows of O are heads; lane 16 hh + t of head quad qd carries head 4 qd + hh's totals
     const int q4 = lane >> 4, col = lane & 15;
+    if (col == 0) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+      for (int qd = 0; qd < G / 4; ++qd) {
+        sm.m[w][4 * qd + q4] = bm[qd];
+        sm.l[w][4 * qd + q4] = bl[qd];
+        sm.z[w][4 * qd + q4] = bz[qd];
+      }
+    }
+    if (4 * q4 < G) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sm.u.o[w][4 * q4 + i][16 * ct + col] = O[ct][i];
-  } else {
-    if (lane < G) { sm.m[w][lane] = -INFINITY; sm.l[w][lane] = 0.f; sm.z[w][lane] = 0.f; }
-    for (int r = 0; r < 16; ++r) {
-      sm.u.o[w][r][2 * lane] = 0.f;
-      sm.u.o[w][r][2 * lane + 1] = 0.f;
+      for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.u.o[w][4 * q4 + i][16 * ct + col] = O[ct][i];
     }
   }
   __syncthreads();
@@ -779,9 +740,7 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     for (int ww = 0; ww < kWaves; ++ww) {
       if (sm.l[ww][hh] > 0.f) {
         const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
-        float o = sm.z[ww][hh];
-#pragma unroll
-        for (int tp = 0; tp < 16 / G; ++tp) o += sm.u.o[ww][G * tp + hh][j];
+        const float o = sm.z[ww][hh] + sm.u.o[ww][hh][j];
         num = fmaf(f, o, num);
         den = fmaf(f, sm.l[ww][hh], den);
       }
