@@ -13,10 +13,10 @@
 // Grid (ceil(P/4), B * Hkv), 256 threads.  Each wave streams the 64-token sets of one
 // KV partition through a two-slot LDS ring filled by load-to-LDS DMA (the next set is
 // in flight while the current one is computed):
-//   QK: v_mfma_scale_f32_16x16x128_f8f6f4, A = q~ as six balanced base-16 digits
-//       (integers in [-8, 7], exact in e4m3) on one fixed-point grid per head, B = the
-//       key codes as fp4 (a code c in a nibble's low bits is exactly c / 2), so each
-//       dot product is exact and q~ keeps ~23 bits.  Rows of the result are (head,
+//   QK: v_mfma_scale_f32_16x16x128_f8f6f4 on fp4 x fp4, A = q~ as eight balanced
+//       base-8 digits (integers in [-4, 3], exact in e2m1) on one fixed-point grid per
+//       head, B = the key codes (a code c in a nibble's low bits is exactly c / 2), so
+//       each dot product is exact and q~ keeps ~23 bits.  Rows of the result are (head,
 //       digit), columns tokens; the digits are summed per lane, smallest first.
 //   softmax: online, base 2, per head (DPP reductions over the 16 token columns);
 //       W = p * s_V as an fp16 hi + lo pair, passed through LDS as the PV A operand.
@@ -165,12 +165,11 @@ __device__ __forceinline__ f16x8 v_operand(unsigned w, unsigned hi, int iota, co
   return __builtin_bit_cast(f16x8, r);
 }
 
-// QK on v_mfma_scale_f32_16x16x128_f8f6f4 with A = q~ digits (fp8 e4m3) and B = key
-// codes (fp4 e2m1: a 2-bit code c in the low bits of a nibble is exactly c / 2).
-// Operand maps of that instruction (16 x 16 x 128): fp4 B lane l holds column l % 16,
-// K-slots 32 (l / 16) + nibble (low nibble first); fp8 A lane l holds row l % 16, bytes
-// 0..15 at K 16 (l / 16) + byte and bytes 16..31 at K 64 + 16 (l / 16) + byte - 16; the
-// E8M0 scale byte of lane l scales its row (A) / column (B) over K-block l / 16.
+// QK on v_mfma_scale_f32_16x16x128_f8f6f4 with A = q~ digits and B = key codes, both
+// fp4 e2m1 (a 2-bit code c in the low bits of a nibble is exactly c / 2).  Operand map
+// of that instruction (16 x 16 x 128) for fp4: lane l holds row (A) / column (B) l % 16,
+// K-slots 32 (l / 16) + nibble (low nibble first); the E8M0 scale byte of lane l scales
+// its row (A) / column (B) over K-block l / 16.
 // A key word (16 codes, code f at bits 2f) gives two B dwords with one mask each:
 // (w & 0x33333333) holds the even codes, ((w >> 2) & 0x33333333) the odd ones, so
 // K-slot 32 g + 8 d + i of lane group g reads channel 32 g + 16 (d >> 1) + 2 i + (d & 1).
@@ -179,28 +178,19 @@ __device__ __forceinline__ int kslot_channel(int k) {
   return 32 * g + 16 * (d >> 1) + 2 * i + (d & 1);
 }
 
-__device__ __forceinline__ int a_kslot(int g, int jb) { return jb < 16 ? 16 * g + jb : 64 + 16 * g + (jb - 16); }
 
-// Offset that makes six balanced base-16 digits (each in [-8, 7]) unsigned nibbles:
-// u = Q + 0x888888 for integers |Q| <= 0x777777.
-constexpr unsigned kDigitBias = 0x888888u;
+// q~ enters the QK MFMA as eight balanced base-8 digits, integers in [-4, 3], which
+// e2m1 holds exactly: u = Q + kDigitBias (|Q| <= 2^22) makes them the unsigned 3-bit
+// fields of u, digit j = field 7 - j minus 4.
+constexpr unsigned kDigitBias = 0x924924u;
+// e2m1 nibble of the digit with field value f (digit f - 4), nibble f of this word.
+constexpr unsigned kDigitE2M1 = 0x5420ACDEu;
 
-// Head and digit of row r of q~ operand m: G = 4: operand 0 digits 0-3 (row 4 h + j),
-// operand 1 digits 4-5 (rows 4 h + j - 4, rows with j >= 6 unused).  G = 8: operands 0 and
-// 1 digits 0-3 of heads 0-3 and 4-7, operand 2 digits 4-5 of heads g and g + 4 in rows
-// 4 g + i (i = 0, 1: head g; 2, 3: head g + 4).
-template <int G>
+// Head and digit of row r of q~ operand m: head quad m / 2, rows 4 h + i hold digit
+// 4 (m % 2) + i of head 4 (m / 2) + h, so a lane's four result rows are one head's digits.
 __device__ __forceinline__ void digit_row(int m, int r, int &h, int &j) {
-  if (G == 4) {
-    h = r >> 2;
-    j = 4 * m + (r & 3);
-  } else if (m < 2) {
-    h = 4 * m + (r >> 2);
-    j = r & 3;
-  } else {
-    h = (r >> 2) + 4 * ((r & 3) >> 1);
-    j = 4 + (r & 1);
-  }
+  h = 4 * (m >> 1) + (r >> 2);
+  j = 4 * (m & 1) + (r & 3);
 }
 
 __device__ __forceinline__ i32x8 key_fp4(u32x2 w) {
@@ -209,11 +199,14 @@ __device__ __forceinline__ i32x8 key_fp4(u32x2 w) {
 }
 
 // Max / sum over the 16 lanes of a row (DPP rotations within the row, then quad swaps).
+// The max is one v_max_f32 with a DPP source per step (its inputs are never NaN); each
+// s_nop 1 gives the two wait states a DPP read needs after a VALU write of its source.
 __device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, dpp<0x128>(x, x));
-  x = fmaxf(x, dpp<0x124>(x, x));
-  x = fmaxf(x, dpp<0x4E>(x, x));
-  x = fmaxf(x, dpp<0xB1>(x, x));
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\tv_max_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "+v"(x));
   return x;
 }
 
@@ -227,29 +220,39 @@ __device__ __forceinline__ float row_sum(float x) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Word 3 of a raw buffer resource on gfx9 (32-bit dword data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
+// Where a wave's body sets come from: buffer resources over its KV head's key and
+// value code planes (a set's offset goes in an SGPR, so the lanes do no address
+// arithmetic) and the lane's base in the parameter planes.
+struct SetSource {
+  __amdgpu_buffer_rsrc_t k, v;
+  const uint8_t *par;   // keys' parameters (lanes < 16) or values' (lanes 16-31)
+  int pstride;          // the lane's parameter bytes per set
+  int vset;             // value-set bytes
+  bool pact;            // the lane carries parameter bytes
+};
+
 // Queue the loads of body set `set` into the wave's ring slot `st` (load-to-LDS:
 // lane i's bytes land at the slot offset + i * size).  Stage<BV>::DMAS instructions.
 template <int BV>
-__device__ __forceinline__ void stage_set(const DecodeArgs &a, const uint8_t *kplane, const uint8_t *vplane,
-                                          const uint8_t *kpar, const uint8_t *vpar, int64_t set, uint8_t *st) {
+__device__ __forceinline__ void stage_set(const SetSource &src, int set, uint8_t *st) {
   using S = Stage<BV>;
   const int lane = threadIdx.x & 63;
   constexpr int aux = 2;   // nontemporal: streamed once
-  const uint8_t *kg = kplane + (size_t)set * 2048;
-  __builtin_amdgcn_global_load_lds(kg + 16 * lane, (lds_void *)(st + S::K), 16, 0, aux);
-  __builtin_amdgcn_global_load_lds(kg + 1024 + 16 * lane, (lds_void *)(st + S::K + 1024), 16, 0, aux);
-  const uint8_t *vg = vplane + (size_t)set * a.vset_bytes;
-  __builtin_amdgcn_global_load_lds(vg + 16 * lane, (lds_void *)(st + S::V), 16, 0, aux);
-  __builtin_amdgcn_global_load_lds(vg + 1024 + 16 * lane, (lds_void *)(st + S::V + 1024), 16, 0, aux);
-  if constexpr (BV == 3) __builtin_amdgcn_global_load_lds(vg + 2048 + 16 * lane, (lds_void *)(st + S::VH), 16, 0, aux);
+  const unsigned vo = 16u * (unsigned)lane;
+  const int ko = set * 2048, vso = set * src.vset;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K), 16, vo, ko, 0, aux);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K + 1024), 16, vo, ko + 1024, 0, aux);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V), 16, vo, vso, 0, aux);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V + 1024), 16, vo, vso + 1024, 0, aux);
+  if constexpr (BV == 3)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::VH), 16, vo, vso + 2048, 0, aux);
   // parameters, one instruction: lanes 0-15 the keys', 16-31 the values' (64 tokens x
   // 2 or 4 bytes each; lane 0 is always active, so the instruction always issues)
-  const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
-  const bool pk = lane < 4 * kb, pv = lane >= 16 && lane - 16 < 4 * vbn;
-  if (pk || pv) {
-    const uint8_t *src = pk ? kpar + (size_t)set * 64 * kb + 16 * lane : vpar + (size_t)set * 64 * vbn + 16 * (lane - 16);
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(st + S::KP), 16, 0, aux);
-  }
+  if (src.pact)
+    __builtin_amdgcn_global_load_lds(src.par + (size_t)set * src.pstride, (lds_void *)(st + S::KP), 16, 0, aux);
 }
 
 // Row of window-list token t: sink row t, or the ring slot of the t-th token after the
@@ -297,8 +300,9 @@ __device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, in
 // One wave of a KV partition: its body sets [s0, s1), then its 8-token stages
 // [ws0, ws1) of the FP16 window list, all streamed through the wave's LDS ring.
 // Lane (h, t) = (lane / 16, lane % 16) scores token 16 T + t of each set (T = 0..3) for
-// heads h + 4 qd (qd < G / 4).  PV output rows are heads: O lane l holds heads
-// 4 (l / 16) + i, channels 16 ct + l % 16.
+// heads h + 4 qd (qd < G / 4).  PV output row r (O lane l holds rows 4 (l / 16) + i,
+// channels 16 ct + l % 16) is head r's hi part for r < G and head r - G's lo part for
+// G <= r < 2 G; the two are summed in the workgroup merge.
 template <int G, int BV>
 __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
                           f32x4 (&O)[8], float (&m_out)[G / 4], float (&l_out)[G / 4], float (&z_out)[G / 4],
@@ -306,58 +310,71 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   constexpr int NQ = G / 4;            // head quads: QK MFMAs per tile
   const int lane = threadIdx.x & 63;
   const int g4 = lane >> 4, t16 = lane & 15;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int Lv = 1 << BV;
 
-  // q~ as six balanced base-16 digits (integers in [-8, 7], exact in e4m3) on one fixed
-  // point grid per head, in the rows of NM A operands: row r of operand m holds digit j
-  // of head h (digit_row), weighted 2^(e - 1 - 4 j) through the row's E8M0 scale.  On a
-  // common grid every product of a digit MFMA is a multiple of 1/2 below 13, which the
-  // matrix core sums exactly (it does not for operands of mixed exponents).  Lane
-  // (g4, t16)'s result rows 4 g4 + i are digits of its heads.
-  constexpr int NM = G == 4 ? 2 : 3;
+  // q~ as eight balanced base-8 digits (integers in [-4, 3], exact in e2m1) on one fixed
+  // point grid per head, in the rows of NM fp4 A operands: row r of operand m holds
+  // digit j of head h (digit_row), weighted 2^(e - 3 j) through the row's E8M0 scale.
+  // On a common grid every product of a digit MFMA is a multiple of 1/2 of magnitude
+  // at most 6, which the matrix core sums exactly (it does not for operands of mixed
+  // exponents).  Lane (g4, t16)'s result rows 4 g4 + i are digits of one head.
+  constexpr int NM = G / 2;
   i32x8 aq[NM];
   int sa[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    const int r = lane & 15;
     int h, j;
-    digit_row<G>(m, r, h, j);
-    const int sft = 20 - 4 * j;
-    unsigned wd[8];
+    digit_row(m, lane & 15, h, j);
+    const int sft = 21 - 3 * j;
+    unsigned wd[4];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
+    for (int d = 0; d < 4; ++d) {
       unsigned word = 0;
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int ch = kslot_channel(a_kslot(g4, 4 * d + bb));
-        const int dig = (int)((sm.qi[h][ch] >> (sft & 31)) & 15u) - 8;
-        word |= (j < 6 ? (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32((float)dig, 0.f, 0, false) & 0xFFu : 0u)
-                << (8 * bb);
+      for (int i = 0; i < 8; ++i) {
+        const int ch = kslot_channel(32 * g4 + 8 * d + i);
+        const unsigned f = (sm.qi[h][ch] >> sft) & 7u;
+        word |= ((kDigitE2M1 >> (4 * f)) & 15u) << (4 * i);
       }
       wd[d] = word;
     }
-    aq[m] = (i32x8){(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3], (int)wd[4], (int)wd[5], (int)wd[6], (int)wd[7]};
-    sa[m] = j < 6 ? 126 + sm.qe[h] - 4 * j : 127;
+    aq[m] = (i32x8){(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3], 0, 0, 0, 0};
+    sa[m] = 127 + sm.qe[h] - 3 * j;
   }
-  // scores: s (q~ . c) + z sum(q~); the MFMA sums q~ . (c / 2)
-  float a_sc = 2.0f * qk_scale, b_sc[NQ];
+  // scores in units of 1 / a_sc: s (q~ . c / 2) + z sum(q~) / 2 (the MFMA sums
+  // q~ . (c / 2)); a_sc = 2 log2(e) / sqrt(d) turns them into base-2 logits
+  const float a_sc = 2.0f * qk_scale;
+  float b_sc[NQ];
 #pragma unroll
-  for (int qd = 0; qd < NQ; ++qd) b_sc[qd] = sm.sq[4 * qd + g4] * qk_scale;
+  for (int qd = 0; qd < NQ; ++qd) b_sc[qd] = 0.5f * sm.sq[4 * qd + g4];
   const VConst vc = make_vconst();
   // BASE of the value operand for token 16 T + t16: pair 2 T + (t16 & 3) / 2 of its word
   float vbase[4];
 #pragma unroll
   for (int T = 0; T < 4; ++T) vbase[T] = BV == 2 ? vbase2(2 * T + ((t16 & 3) >> 1)) : 16.0f;
-  // PV A rows: head r of this wave's W buffer, or zeros past G
+  // PV A rows: row r < G is head r's W hi part, G <= r < 2 G head r - G's lo part (the
+  // two halves of one word of the W buffer), zeros past 2 G
   const int ar = lane & 15;
-  const unsigned *arow = ar < G ? &sm.wb[w][ar][0] : &sm.wzero[0];
+  const unsigned *arow = ar < 2 * G ? &sm.wb[w][ar < G ? ar : ar - G][0] : &sm.wzero[0];
+  const unsigned asel = ar < G ? 0x05040100u : 0x07060302u;
 
-  const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
-  const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
-  const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
-  const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
+  SetSource src;
+  {
+    const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
+    const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
+    const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
+    const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
+    src.k = __builtin_amdgcn_make_buffer_rsrc((void *)kplane, 0, (int)a.kcode_bytes, kRsrcWord3);
+    src.v = __builtin_amdgcn_make_buffer_rsrc((void *)vplane, 0, (int)a.vcode_bytes, kRsrcWord3);
+    const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
+    const bool pk = lane < 4 * kb;
+    src.pact = pk || (lane >= 16 && lane - 16 < 4 * vbn);
+    src.par = pk ? kpar + 16 * lane : vpar + 16 * (lane - 16);
+    src.pstride = 64 * (pk ? kb : vbn);
+    src.vset = (int)a.vset_bytes;
+  }
   uint8_t *ring = &sm.u.ring[w][0][0];
   constexpr int SB = Stage<BV>::SIZE;
   // items of this wave: body sets s0 .. s1-1, then 8-token window stages ws0 .. ws1-1
@@ -372,7 +389,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   const uint8_t *ringv = (const uint8_t *)a.ring_v + (size_t)bg * a.ring_bytes;
   auto issue = [&](int item, uint8_t *dst) {
     if (item < nb) {
-      stage_set<BV>(a, kplane, vplane, kpar, vpar, s0 + item, dst);
+      stage_set<BV>(src, (int)s0 + item, dst);
     } else {
       const int t0 = 8 * (ws0 + item - nb);
       stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
@@ -386,12 +403,12 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const bool kq = a.quant_k == WUSHKV_Q_QUEST, vq = a.quant_v == WUSHKV_Q_QUEST;
-
   // one 64-token set: QK, softmax update, PV.  FULL: every token of the set is in
-  // the body (no validity selects).
-  auto compute = [&](auto full_tag, int64_t set, const uint8_t *st) {
+  // the body (no validity selects); KQ / VQ: QuEST (one scale per token) rather than
+  // affine (scale, zero) parameters for the keys / values.
+  auto compute = [&](auto full_tag, auto kq_tag, auto vq_tag, int64_t set, const uint8_t *st) {
     constexpr bool FULL = decltype(full_tag)::value;
+    constexpr bool KQ = decltype(kq_tag)::value, VQ = decltype(vq_tag)::value;
     using S = Stage<BV>;
     const int64_t base = set * kSet;
 
@@ -401,17 +418,14 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const i32x8 bk = key_fp4(*(const u32x2 *)(st + S::K + (16 * T + t16) * 32 + 8 * g4));
-      f32x4 d[NM];
+      // per head quad: digits 4-7 accumulate onto the rows of digits 0-3
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
-        d[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[m], bk, (f32x4){0.f, 0.f, 0.f, 0.f}, 0, 4, 0,
-                                                                sa[m], 0, 127);
-      // small digits first
-      if constexpr (G == 4) {
-        sc[0][T] = ((d[1][0] + d[1][1]) + (d[0][3] + d[0][2])) + (d[0][1] + d[0][0]);
-      } else {
-        sc[0][T] = ((d[2][0] + d[2][1]) + (d[0][3] + d[0][2])) + (d[0][1] + d[0][0]);
-        sc[1][T] = ((d[2][2] + d[2][3]) + (d[1][3] + d[1][2])) + (d[1][1] + d[1][0]);
+      for (int qd = 0; qd < NQ; ++qd) {
+        const f32x4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bk, (f32x4){0.f, 0.f, 0.f, 0.f},
+                                                                          4, 4, 0, sa[2 * qd], 0, 127);
+        const f32x4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bk, d0, 4, 4, 0,
+                                                                          sa[2 * qd + 1], 0, 127);
+        sc[qd][T] = (d1[3] + d1[2]) + (d1[1] + d1[0]);
       }
     }
     // ---- scores and online softmax (base 2)
@@ -422,7 +436,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     for (int T = 0; T < 4; ++T) {
       const int u = 16 * T + t16;
       float s_t, z_t;
-      if (kq) {
+      if constexpr (KQ) {
         s_t = (float)*(const _Float16 *)(st + S::KP + 2 * u);
         z_t = -1.5f * s_t;
       } else {
@@ -433,7 +447,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
       const bool valid = FULL || base + u < a.nq;
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        sc[qd][T] = valid ? fmaf(s_t, sc[qd][T] * a_sc, z_t * b_sc[qd]) : -INFINITY;
+        sc[qd][T] = valid ? fmaf(s_t, sc[qd][T], z_t * b_sc[qd]) : -INFINITY;
         mx[qd] = fmaxf(mx[qd], sc[qd][T]);
       }
     }
@@ -442,20 +456,20 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
       const float m_new = fmaxf(m_run[qd], row_max(mx[qd]));
-      alpha[qd] = __builtin_amdgcn_exp2f(m_run[qd] - m_new);
+      alpha[qd] = __builtin_amdgcn_exp2f((m_run[qd] - m_new) * a_sc);
       m_run[qd] = m_new;
       rescale |= alpha[qd] != 1.0f;
     }
     if (__any(rescale)) {
-      // O row 4 (l / 16) + i is head 4 (l / 16) + i: its factor sits in lane group
-      // (row % 4), head quad row / 4
+      // O row r = 4 (l / 16) + i holds head r % G (hi part for r < G, lo part after):
+      // its factor sits in lane group i, head quad (r % G) / 4
       float f[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         f[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * i));
         if constexpr (NQ == 2) {
           const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[1]), 16 * i));
-          f[i] = g4 == 1 ? f1 : f[i];
+          f[i] = (g4 & 1) ? f1 : f[i];
         }
       }
 #pragma unroll
@@ -469,11 +483,14 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
       }
     }
     // ---- p, W = p s_V as fp16 hi + lo into the wave's W buffer, zero term
+    float m_sc[NQ];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) m_sc[qd] = m_run[qd] * a_sc;
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const int u = 16 * T + t16;
       float s_t, z_t;
-      if (vq) {
+      if constexpr (VQ) {
         s_t = (float)*(const _Float16 *)(st + S::VP + 2 * u);
         z_t = -0.5f * (Lv - 1) * s_t;
       } else {
@@ -487,7 +504,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
       const float zb = fmaf(-vbase[T], s_t, z_t);
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        const float p = __builtin_amdgcn_exp2f(sc[qd][T] - m_run[qd]);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[qd][T], a_sc, -m_sc[qd]));
         l_lane[qd] += p;
         const float W = valid ? p * s_t : 0.f;
         zacc[qd] = valid ? fmaf(p, zb, zacc[qd]) : zacc[qd];
@@ -522,21 +539,16 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     for (int iota = 0; iota < 2; ++iota) {
       const u32x4 x0 = *(const u32x4 *)(arow + 16 * (2 * iota) + 4 * g4);
       const u32x4 x1 = *(const u32x4 *)(arow + 16 * (2 * iota + 1) + 4 * g4);
-      const u32x4 ah = {__builtin_amdgcn_perm(x0[1], x0[0], 0x05040100u), __builtin_amdgcn_perm(x0[3], x0[2], 0x05040100u),
-                        __builtin_amdgcn_perm(x1[1], x1[0], 0x05040100u), __builtin_amdgcn_perm(x1[3], x1[2], 0x05040100u)};
-      const u32x4 al = {__builtin_amdgcn_perm(x0[1], x0[0], 0x07060302u), __builtin_amdgcn_perm(x0[3], x0[2], 0x07060302u),
-                        __builtin_amdgcn_perm(x1[1], x1[0], 0x07060302u), __builtin_amdgcn_perm(x1[3], x1[2], 0x07060302u)};
-      const f16x8 Ah = __builtin_bit_cast(f16x8, ah);
-      const f16x8 Al = __builtin_bit_cast(f16x8, al);
+      const u32x4 av = {__builtin_amdgcn_perm(x0[1], x0[0], asel), __builtin_amdgcn_perm(x0[3], x0[2], asel),
+                        __builtin_amdgcn_perm(x1[1], x1[0], asel), __builtin_amdgcn_perm(x1[3], x1[2], asel)};
+      const f16x8 Aw = __builtin_bit_cast(f16x8, av);
 #pragma unroll
       for (int ct0 = 0; ct0 < 8; ct0 += 4) {
         f16x8 Bv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) Bv[c] = v_operand<BV>(vws[ct0 + c], hws[ct0 + c], iota, vc);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, Bv[c], O[ct0 + c], 0, 0, 0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, Bv[c], O[ct0 + c], 0, 0, 0);
+        for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aw, Bv[c], O[ct0 + c], 0, 0, 0);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -545,15 +557,26 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   // items: item k + 1 is staged while item k computes
   using FullTag = std::integral_constant<bool, true>;
   using TailTag = std::integral_constant<bool, false>;
-  int it = 0;
-  for (; it < nb; ++it) {
-    const bool more = it + 1 < nitems;
-    if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
-    wait_staged<BV>(more ? 1 : 0);
-    const int64_t set = s0 + it;
-    if ((set + 1) * kSet <= a.nq) compute(FullTag{}, set, ring + (it & 1) * SB);
-    else compute(TailTag{}, set, ring + (it & 1) * SB);
+  auto body_sets = [&](auto kq_tag, auto vq_tag) {
+    for (int it = 0; it < nb; ++it) {
+      const bool more = it + 1 < nitems;
+      if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
+      wait_staged<BV>(more ? 1 : 0);
+      const int64_t set = s0 + it;
+      if ((set + 1) * kSet <= a.nq) compute(FullTag{}, kq_tag, vq_tag, set, ring + (it & 1) * SB);
+      else compute(TailTag{}, kq_tag, vq_tag, set, ring + (it & 1) * SB);
+    }
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  if (a.quant_k == WUSHKV_Q_QUEST) {
+    if (a.quant_v == WUSHKV_Q_QUEST) body_sets(Yes{}, Yes{});
+    else body_sets(Yes{}, No{});
+  } else {
+    if (a.quant_v == WUSHKV_Q_QUEST) body_sets(No{}, Yes{});
+    else body_sets(No{}, No{});
   }
+  int it = nb;
   float wm[G], wl[G], wacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
@@ -575,7 +598,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   // per-head totals; every lane of head 4 qd + lane / 16 holds them
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) {
-    m_out[qd] = m_run[qd];
+    m_out[qd] = m_run[qd] * a_sc;
     l_out[qd] = row_sum(l_lane[qd]);
     z_out[qd] = row_sum(zacc[qd]);
   }
@@ -644,7 +667,7 @@ template <int G, int BV>
 __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int nwg_body) {
   __shared__ FastSmem<G, BV> sm;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int h0 = g * G;
@@ -716,7 +739,7 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
         sm.z[w][4 * qd + q4] = bz[qd];
       }
     }
-    if (4 * q4 < G) {
+    if (4 * q4 < 2 * G) {
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -740,7 +763,7 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
     for (int ww = 0; ww < kWaves; ++ww) {
       if (sm.l[ww][hh] > 0.f) {
         const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
-        const float o = sm.z[ww][hh] + sm.u.o[ww][hh][j];
+        const float o = sm.z[ww][hh] + (sm.u.o[ww][hh][j] + sm.u.o[ww][G + hh][j]);
         num = fmaf(f, o, num);
         den = fmaf(f, sm.l[ww][hh], den);
       }
@@ -763,7 +786,10 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
 }  // namespace
 
 bool decode_fast_supported(const DecodeArgs &a) {
-  return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8);
+  // buffer resources address each KV head's code planes with 31-bit offsets
+  return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8) &&
+         a.kcode_bytes < (1u << 31) && a.vcode_bytes < (1u << 31) && a.kpar_bytes < (1u << 31) &&
+         a.vpar_bytes < (1u << 31);
 }
 
 int decode_fast_partials(const DecodeArgs &a) { return (a.P + kWaves - 1) / kWaves; }
