@@ -88,7 +88,8 @@ def run_decode_leg(args):
     w = configs.SERVING
     dev = "cuda"
     n0 = w.context
-    total = n0 + args.warmup + args.steps
+    n_breakdown = 20
+    total = n0 + args.warmup + args.steps + n_breakdown
     log(f"[bench] decode workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} n={n0}")
     k, v = gen.kv_tensors(w, 0, total, dev)
     t16, tinvt = gen.key_transforms(w, 0)
@@ -98,9 +99,11 @@ def run_decode_leg(args):
                        quant_k=W.Q_AFFINE, quant_v=W.Q_AFFINE, pct_lo=w.pct_lo, pct_hi=w.pct_hi)
     cache = W.KVCache(spec, dev)
     W.append_flush(cache, k[:, :, :n0].contiguous(), v[:, :, :n0].contiguous(), t16)
-    steps_k = [k[:, :, n0 + i:n0 + i + 1].contiguous() for i in range(args.warmup + args.steps)]
-    steps_v = [v[:, :, n0 + i:n0 + i + 1].contiguous() for i in range(args.warmup + args.steps)]
-    qs = [gen.queries(w, 0, i, dev) for i in range(args.warmup + args.steps)]
+    nsteps = args.warmup + args.steps + n_breakdown
+    steps_k = [k[:, :, n0 + i:n0 + i + 1].contiguous() for i in range(nsteps)]
+    steps_v = [v[:, :, n0 + i:n0 + i + 1].contiguous() for i in range(nsteps)]
+    del k, v
+    qs = [gen.queries(w, 0, i, dev) for i in range(nsteps)]
     qt = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     out = torch.empty_like(qt)
     P = W.decode_num_splits(cache, total, w.num_q_heads, 0)
@@ -124,24 +127,47 @@ def run_decode_leg(args):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: K whole steps, wall clock between two synchronizations (no events
+    # inside: each event record costs the GPU a few microseconds)
     n_start = cache.n
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
-        step(args.warmup + j, evs[j])
+        step(args.warmup + j)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    app = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    qtm = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    dec = [e[2].elapsed_time(e[3]) for e in evs]
-    dec_ms = sum(dec) / len(dec)
     ms_step = wall * 1e3 / args.steps
     nbytes = sum(decode_bytes(w, n_start + j + 1) for j in range(args.steps)) / args.steps
-    log(f"[bench] step {ms_step:.4f} ms (append {app:.4f}, qtransform {qtm:.4f}, decode {dec_ms:.4f} ms); "
-        f"decode bytes {nbytes / 1e6:.1f} MB")
+    # breakdown of a step, from further (untimed) steps with events between the calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_breakdown)]
+    for j in range(n_breakdown):
+        step(args.warmup + args.steps + j, evs[j])
+    torch.cuda.synchronize()
+    app = sum(e[0].elapsed_time(e[1]) for e in evs) / n_breakdown
+    qtm = sum(e[1].elapsed_time(e[2]) for e in evs) / n_breakdown
+    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / n_breakdown
+    log(f"[bench] step {ms_step:.4f} ms; breakdown (event intervals): append {app:.4f}, qtransform {qtm:.4f}, "
+        f"decode {dec_ms:.4f} ms; decode bytes {nbytes / 1e6:.1f} MB")
+
+    # The decode kernel's own average launch duration, for the roofline figure: the
+    # same decode launched back to back on the stream, the host ahead of the GPU, so
+    # no launch gap of the step loop is counted.
+    q_last = qs[-1]
+    reps = 30
+    for _ in range(3):
+        W.decode_attention(cache, q_last, qt, num_splits=P, workspace=ws, out=out)
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(reps):
+        W.decode_attention(cache, q_last, qt, num_splits=P, workspace=ws, out=out)
+    k1.record()
+    torch.cuda.synchronize()
+    kern_ms = k0.elapsed_time(k1) / reps
+    kern_bytes = decode_bytes(w, cache.n)
+    log(f"[bench] decode kernel back to back: {kern_ms * 1e3:.1f} us per launch at n={cache.n} "
+        f"({kern_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s)")
     return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, app_ms=app, qt_ms=qtm, bytes=nbytes, splits=P,
-                n=n_start, cache=cache)
+                n=n_start, cache=cache, kern_ms=kern_ms, kern_bytes=kern_bytes)
 
 
 def run_flush_leg(args):
@@ -239,7 +265,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (profiling the flush alone)")
@@ -271,7 +297,7 @@ def main():
     dl = run_decode_leg(args)
     w = dl["workload"]
     fl = {} if args.no_flush else run_flush_leg(args)
-    achieved = dl["bytes"] / (dl["dec_ms"] * 1e-3) / 1e9
+    achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile("decode_c2_counters.json")
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
     line = {
@@ -293,12 +319,13 @@ def main():
                    "chunk": w.chunk, "splits": dl["splits"], "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_breakdown_ms": {"append_flush": round(dl["app_ms"], 5), "query_transform": round(dl["qt_ms"], 5),
-                              "decode_attention": round(dl["dec_ms"], 5)},
+                              "decode_attention": round(dl["dec_ms"], 5),
+                              "note": "event intervals of untimed steps after the timed region"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode attention (partials + merge, one launch)",
-                     "bytes_per_launch": int(dl["bytes"])},
+                     "kernel": "decode attention: decode_fast_kernel<4,2> (split-K GQA decode) + merge_kernel",
+                     "bytes_per_launch": int(dl["kern_bytes"]), "us_per_launch": round(dl["kern_ms"] * 1e3, 2)},
     }
     if fl:
         line["flush"] = {f"{b}bit": {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_36_layers": round(r["ms"], 3),

@@ -79,22 +79,30 @@ def _check(status, what):
         raise WushKVError(status, what)
 
 
+_DTYPES = None
+
+
 def _dtype_code(t):
-    import torch
-    return {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}[t.dtype]
+    global _DTYPES
+    if _DTYPES is None:
+        import torch
+        _DTYPES = {torch.float32: DT_F32, torch.bfloat16: DT_BF16, torch.float16: DT_F16}
+    return _DTYPES[t.dtype]
 
 
-def _stream(stream):
+def _stream(stream, device):
+    """Raw HIP stream handle: the given torch stream, else torch's current stream on device."""
+    if stream is not None:
+        return stream.cuda_stream
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(stream.cuda_stream)
+    index = device.index if device.index is not None else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(index)
 
 
 def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors passed to libwushkv must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 @dataclass
@@ -165,7 +173,8 @@ def append_flush(cache: KVCache, k_new, v_new, t_k16, n_before=None, stream=None
     if k_new.dtype != v_new.dtype or t_k16.dtype != torch.float16:
         raise ValueError("k_new/v_new must share a dtype and t_k16 must be float16")
     _check(lib().wushkv_append_flush(ctypes.byref(cache.desc), n_before, n_new, _ptr(k_new), _ptr(v_new),
-                                     _dtype_code(k_new), _ptr(t_k16), _stream(stream)), "append_flush")
+                                     _dtype_code(k_new), _ptr(t_k16), _stream(stream, k_new.device)),
+           "append_flush")
     cache.n = n_before + n_new
 
 
@@ -176,7 +185,7 @@ def query_transform(t_inv_t, q, num_kv_heads, out=None, stream=None):
     if out is None:
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     _check(lib().wushkv_query_transform(_ptr(t_inv_t), _ptr(q), _dtype_code(q), B, Hq, num_kv_heads, d,
-                                        _ptr(out), _stream(stream)), "query_transform")
+                                        _ptr(out), _stream(stream, q.device)), "query_transform")
     return out
 
 
@@ -204,5 +213,5 @@ def decode_attention(cache: KVCache, q, q_t, n_tokens=None, num_splits=0, worksp
         out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
     _check(lib().wushkv_decode_attention(ctypes.byref(cache.desc), n_tokens, _ptr(q), _dtype_code(q), _ptr(q_t),
                                          Hq, num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
-                                         _stream(stream)), "decode_attention")
+                                         _stream(stream, q.device)), "decode_attention")
     return out

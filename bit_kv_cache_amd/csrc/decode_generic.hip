@@ -200,29 +200,9 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   }
 }
 
-// Online-softmax merge of the partials of one (batch row, query head), thread =
-// channel: m* = max m_p, out = sum 2^{m_p - m*} o_p / sum 2^{m_p - m*} l_p over the
-// partials with l_p > 0, in fixed partition order.
+// The merge of one (batch row, query head) per workgroup, thread = channel.
 __global__ void __launch_bounds__(128) merge_kernel(DecodeArgs a, int nparts) {
-  const int bh = blockIdx.x;
-  const int j = threadIdx.x;
-  if (j >= a.d) return;
-  const int P1 = a.P + 1;
-  const size_t row = (size_t)bh * P1;
-  float mstar = -INFINITY;
-  for (int p = 0; p < nparts; ++p) {
-    const float *ml = a.part_ml + (row + p) * 2;
-    if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
-  }
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float *ml = a.part_ml + (row + p) * 2;
-    if (!(ml[1] > 0.f)) continue;
-    const float f = __builtin_amdgcn_exp2f(ml[0] - mstar);
-    num = fmaf(f, a.part_o[(row + p) * a.d + j], num);
-    den = fmaf(f, ml[1], den);
-  }
-  a.out[(size_t)bh * a.d + j] = num / den;
+  if ((int)threadIdx.x < a.d) merge_row(a, blockIdx.x, nparts, threadIdx.x);
 }
 
 }  // namespace

@@ -141,6 +141,36 @@ def test_decode_deterministic_and_split_invariant():
         assert rel < 1e-5, (P, rel)
 
 
+def test_decode_workspace_reuse():
+    """One workspace serves decodes of different split counts: each call matches a
+    call on a fresh workspace bit for bit."""
+    w = configs.SERVING.scaled(name="wsreuse", seed=12, batch=3, context=4000)
+    r = Run(w)
+    r.append(w.context)
+    r.append(1)
+    q = r.decode(0)[0]
+    qt = W.query_transform(r.tinvt, q, w.num_kv_heads)
+    ws = W.decode_workspace(r.cache, r.cache.n, w.num_q_heads, 64)
+    for P in (5, 1, 17, 64, 5, 0, 3):
+        fresh = W.decode_attention(r.cache, q, qt, num_splits=P)
+        reused = W.decode_attention(r.cache, q, qt, num_splits=P, workspace=ws)
+        torch.cuda.synchronize()
+        say(f"[workspace reuse] P={P}")
+        assert torch.equal(fresh, reused), P
+    r.check_decode(q, qt, reused)
+
+
+def test_decode_large_batch_short_context():
+    """A batch of 520 sequences at a short context: 4160 (batch row, KV head) grid rows,
+    few body sets each."""
+    w = configs.SERVING.scaled(name="manyheads", seed=13, batch=520, context=700)
+    r = Run(w)
+    r.append(w.context)
+    r.append(1)
+    q, qt, out = r.decode(0)
+    r.check_decode(q, qt, out, heads=[(0, 0), (263, 4), (519, 7)])
+
+
 def test_snapshot_restore_continues_bitwise():
     w = configs.LAYER_8B.scaled(name="snap", context=1000, decode_steps=20)
     r = Run(w)
