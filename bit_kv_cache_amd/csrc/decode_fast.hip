@@ -68,7 +68,7 @@ struct Stage {
   static constexpr int DMAS = BV == 3 ? 6 : 5;
 };
 
-constexpr int kStages = 2;   // body sets staged per wave: the one computed and the next
+constexpr int kStages = 2;   // ring slots per wave: the item computed and kStages - 1 ahead
 
 template <int G, int BV>
 struct __align__(16) FastSmem {
@@ -285,12 +285,15 @@ __device__ __forceinline__ void stage_window(const uint8_t *sinkk, const uint8_t
     if (lane == 0) __builtin_amdgcn_global_load_lds(filler, (lds_void *)(st + S::KP + 64 * i), 16, 0, aux);
 }
 
-// Wait until at most `pending` staged sets' loads are still in flight.
+// Wait until at most `pending` (< kStages) staged items' loads are still in flight.
 template <int BV>
 __device__ __forceinline__ void wait_staged(int pending) {
   constexpr int D = Stage<BV>::DMAS;
+  static_assert(kStages >= 2 && kStages <= 4, "ring depth");
   if (pending <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+  else if (kStages == 2 || pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
+  else if (kStages == 3 || pending == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * D) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
 }
 
 template <int G, int BV>
@@ -395,7 +398,16 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
       stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
     }
   };
-  if (nitems > 0) issue(0, ring);
+  // prologue: the first kStages - 1 items; item k lives in slot k % kStages
+  for (int k = 0; k < kStages - 1 && k < nitems; ++k) issue(k, ring + k * SB);
+  // before item it computes: queue item it + kStages - 1, wait until item it landed
+  auto advance = [&](int it) {
+    const int ahead = it + kStages - 1;
+    if (ahead < nitems) issue(ahead, ring + (ahead % kStages) * SB);
+    const int pending = nitems - 1 - it < kStages - 1 ? nitems - 1 - it : kStages - 1;
+    wait_staged<BV>(pending);
+    return ring + (it % kStages) * SB;
+  };
 
   float m_run[NQ], l_lane[NQ], zacc[NQ];
 #pragma unroll
@@ -403,18 +415,20 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // one 64-token set: QK, softmax update, PV.  FULL: every token of the set is in
-  // the body (no validity selects); KQ / VQ: QuEST (one scale per token) rather than
-  // affine (scale, zero) parameters for the keys / values.
-  auto compute = [&](auto full_tag, auto kq_tag, auto vq_tag, int64_t set, const uint8_t *st) {
+  // A 64-token set in two phases.  FULL: every token of the set is in the body (no
+  // validity selects); KQ / VQ: QuEST (one scale per token) rather than affine (scale,
+  // zero) parameters for the keys / values.
+  // Phase 1: QK and scores; mxr = each head's max over the set.  Returns whether any
+  // head's running max rises (the same in every lane).
+  auto phase1 = [&](auto full_tag, auto kq_tag, int64_t set, const uint8_t *st, float (&sc)[NQ][4],
+                    float (&mxr)[NQ]) {
     constexpr bool FULL = decltype(full_tag)::value;
-    constexpr bool KQ = decltype(kq_tag)::value, VQ = decltype(vq_tag)::value;
+    constexpr bool KQ = decltype(kq_tag)::value;
     using S = Stage<BV>;
     const int64_t base = set * kSet;
 
     // ---- QK: one scaled MFMA per (tile, head quad); the lane's 4 result rows are the
     // digits of its head, already weighted
-    float sc[NQ][4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
       const i32x8 bk = key_fp4(*(const u32x2 *)(st + S::K + (16 * T + t16) * 32 + 8 * g4));
@@ -451,37 +465,51 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
         mx[qd] = fmaxf(mx[qd], sc[qd][T]);
       }
     }
-    float alpha[NQ];
-    bool rescale = false;
+    bool up = false;
 #pragma unroll
     for (int qd = 0; qd < NQ; ++qd) {
-      const float m_new = fmaxf(m_run[qd], row_max(mx[qd]));
+      mxr[qd] = row_max(mx[qd]);
+      up |= mxr[qd] > m_run[qd];
+    }
+    return __any(up);
+  };
+  // A set raised a running max: rescale O, l and z to it (rare once a partition is
+  // under way; kept out of the common path so the accumulators stay in place).
+  auto rescale = [&](const float (&mxr)[NQ]) {
+    float alpha[NQ];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      const float m_new = fmaxf(m_run[qd], mxr[qd]);
       alpha[qd] = __builtin_amdgcn_exp2f((m_run[qd] - m_new) * a_sc);
       m_run[qd] = m_new;
-      rescale |= alpha[qd] != 1.0f;
     }
-    if (__any(rescale)) {
-      // O row r = 4 (l / 16) + i holds head r % G (hi part for r < G, lo part after):
-      // its factor sits in lane group i, head quad (r % G) / 4
-      float f[4];
+    // O row r = 4 (l / 16) + i holds head r % G (hi part for r < G, lo part after):
+    // its factor sits in lane group i, head quad (r % G) / 4
+    float f[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * i));
-        if constexpr (NQ == 2) {
-          const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[1]), 16 * i));
-          f[i] = (g4 & 1) ? f1 : f[i];
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) O[ct][i] *= f[i];
-#pragma unroll
-      for (int qd = 0; qd < NQ; ++qd) {
-        l_lane[qd] *= alpha[qd];
-        zacc[qd] *= alpha[qd];
+    for (int i = 0; i < 4; ++i) {
+      f[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[0]), 16 * i));
+      if constexpr (NQ == 2) {
+        const float f1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[1]), 16 * i));
+        f[i] = (g4 & 1) ? f1 : f[i];
       }
     }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) O[ct][i] *= f[i];
+#pragma unroll
+    for (int qd = 0; qd < NQ; ++qd) {
+      l_lane[qd] *= alpha[qd];
+      zacc[qd] *= alpha[qd];
+    }
+  };
+  // Phase 2: p and W = p s_V against the running max, then PV.
+  auto phase2 = [&](auto full_tag, auto vq_tag, int64_t set, const uint8_t *st, const float (&sc)[NQ][4]) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr bool VQ = decltype(vq_tag)::value;
+    using S = Stage<BV>;
+    const int64_t base = set * kSet;
     // ---- p, W = p s_V as fp16 hi + lo into the wave's W buffer, zero term
     float m_sc[NQ];
 #pragma unroll
@@ -554,17 +582,34 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     __builtin_amdgcn_wave_barrier();
   };
 
-  // items: item k + 1 is staged while item k computes
+  // items: items it + 1 .. it + kStages - 1 are staged while item it computes.  The
+  // inner loop takes full sets that raise no running max; a set that does leaves it
+  // for the rescale and finishes there; the ragged last set, if any, comes after.
   using FullTag = std::integral_constant<bool, true>;
   using TailTag = std::integral_constant<bool, false>;
   auto body_sets = [&](auto kq_tag, auto vq_tag) {
-    for (int it = 0; it < nb; ++it) {
-      const bool more = it + 1 < nitems;
-      if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
-      wait_staged<BV>(more ? 1 : 0);
-      const int64_t set = s0 + it;
-      if ((set + 1) * kSet <= a.nq) compute(FullTag{}, kq_tag, vq_tag, set, ring + (it & 1) * SB);
-      else compute(TailTag{}, kq_tag, vq_tag, set, ring + (it & 1) * SB);
+    const int64_t full_end = a.nq / kSet;   // sets below this index are full
+    const int nfull = full_end <= s0 ? 0 : (int)(full_end - s0 < nb ? full_end - s0 : nb);
+    float sc[NQ][4], mxr[NQ];
+    int it = 0;
+    while (it < nfull) {
+      const uint8_t *st = nullptr;
+      bool up = false;
+      for (; it < nfull; ++it) {
+        st = advance(it);
+        up = phase1(FullTag{}, kq_tag, s0 + it, st, sc, mxr);
+        if (up) break;
+        phase2(FullTag{}, vq_tag, s0 + it, st, sc);
+      }
+      if (!up) break;
+      rescale(mxr);
+      phase2(FullTag{}, vq_tag, s0 + it, st, sc);
+      ++it;
+    }
+    for (; it < nb; ++it) {
+      const uint8_t *st = advance(it);
+      if (phase1(TailTag{}, kq_tag, s0 + it, st, sc, mxr)) rescale(mxr);
+      phase2(TailTag{}, vq_tag, s0 + it, st, sc);
     }
   };
   using Yes = std::true_type;
@@ -581,11 +626,9 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 #pragma unroll
   for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
   for (; it < nitems; ++it) {
-    const bool more = it + 1 < nitems;
-    if (more) issue(it + 1, ring + ((it + 1) & 1) * SB);
-    wait_staged<BV>(more ? 1 : 0);
+    const uint8_t *st = advance(it);
     const int t0 = 8 * (ws0 + it - nb);
-    window_stage<G, BV>(sm, ring + (it & 1) * SB, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
+    window_stage<G, BV>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
