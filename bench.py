@@ -76,7 +76,8 @@ def traffic_from_profile(name):
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    # the decode call: partials kernel + merge kernel
+    return rec.get("bytes_per_launch", 0) + rec.get("merge_bytes_per_launch", 0)
 
 
 def run_decode_leg(args):
@@ -298,7 +299,7 @@ def main():
     w = dl["workload"]
     fl = {} if args.no_flush else run_flush_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
-    traffic = traffic_from_profile("decode_c2_counters.json")
+    traffic = traffic_from_profile("decode_batched_serving_counters.json")
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": "2-bit GQA decode-attention HBM GB/s (% of peak); flush tokens/s",
