@@ -25,8 +25,8 @@
 //       fp16 exponent pattern, giving BASE + c (BASE = 4, 16 or 64 by the pair's
 //       position); BASE * W is removed exactly through the per-head zero term.  W
 //       enters as two MFMAs (hi and lo fp16 parts), so its rounding does not show.
-// The FP16 sink + recent tokens follow the body sets through the same ring, 8 rows per
-// stage, on fp32 VALU in a softmax partial of their own.  Each workgroup merges its 4
+// The FP16 sink + recent tokens go through the same ring first, 8 rows per stage, on
+// fp32 VALU in a softmax partial of their own.  Each workgroup merges its 4
 // waves in LDS and writes one partial (m, l, o); the merge kernel that follows on the
 // stream combines the partials.
 #include <type_traits>
@@ -55,9 +55,10 @@ __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
 }
 
-// Byte layout of one ring slot.  A body set: key codes (2 KB), value codes (2 KB),
-// the 3-bit plane (1 KB), key then value parameters (up to 256 B each), all copied
-// verbatim.  A window stage: 8 FP16 key rows (2 KB) then 8 FP16 value rows (2 KB).
+// Byte layout of one ring slot.  A body set: key codes (2 KB, verbatim), value codes
+// (2 KB: the first 16 bytes of each lane's 32, then the last 16), the 3-bit plane
+// (1 KB, verbatim), key then value parameters (up to 256 B each).  A window stage:
+// 8 FP16 key rows (2 KB) then 8 FP16 value rows (2 KB).
 // Both kinds are filled by exactly DMAS load-to-LDS instructions, so one vmcnt per
 // pending slot covers either.
 template <int BV>
@@ -68,13 +69,18 @@ struct Stage {
   static constexpr int DMAS = BV == 3 ? 6 : 5;
 };
 
+// Row pitch (dwords) of the W buffer: rows 16 banks apart, so the 64 lanes' W stores
+// (4 heads x 16 tokens) hit each bank twice and the PV operand reads (16 rows x 4
+// column quads) spread over all eight 4-bank groups.
+constexpr int kWbPitch = 80;
+
 constexpr int kStages = 2;   // ring slots per wave: the item computed and kStages - 1 ahead
 
 template <int G, int BV>
 struct __align__(16) FastSmem {
   unsigned qi[G][kD];             // q~ in fixed point, offset to unsigned (balanced digits)
   float q[G][kD];
-  unsigned wb[kWaves][G][kSet];   // body set: W as fp16 (hi | lo << 16) [head][token]
+  unsigned wb[kWaves][G][kWbPitch];  // body set: W as fp16 (hi | lo << 16) [head][token]
   unsigned wzero[kSet];           // zeros: the PV A rows past G read these
   int qe[16];                     // per head: q~ = (qi - kDigitBias) 2^(e - 21)
   float wp[kWaves][G][8];         // window stage: probabilities [head][token]
@@ -245,8 +251,10 @@ __device__ __forceinline__ void stage_set(const SetSource &src, int set, uint8_t
   const int ko = set * 2048, vso = set * src.vset;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K), 16, vo, ko, 0, aux);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K + 1024), 16, vo, ko + 1024, 0, aux);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V), 16, vo, vso, 0, aux);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V + 1024), 16, vo, vso + 1024, 0, aux);
+  // value words: lane l's 32 bytes split into its first 16 (slot bytes 16 l) and last
+  // 16 (1024 + 16 l), so each of the lane's two 16-byte reads is contiguous across lanes
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V), 16, 2 * vo, vso, 0, aux);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V + 1024), 16, 2 * vo, vso + 16, 0, aux);
   if constexpr (BV == 3)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::VH), 16, vo, vso + 2048, 0, aux);
   // parameters, one instruction: lanes 0-15 the keys', 16-31 the values' (64 tokens x
@@ -300,8 +308,8 @@ template <int G, int BV>
 __device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
                              float (&wl)[G], float (&wacc)[G][2]);
 
-// One wave of a KV partition: its body sets [s0, s1), then its 8-token stages
-// [ws0, ws1) of the FP16 window list, all streamed through the wave's LDS ring.
+// One wave of a KV partition: its 8-token stages [ws0, ws1) of the FP16 window list,
+// then its body sets [s0, s1), all streamed through the wave's LDS ring.
 // Lane (h, t) = (lane / 16, lane % 16) scores token 16 T + t of each set (T = 0..3) for
 // heads h + 4 qd (qd < G / 4).  PV output row r (O lane l holds rows 4 (l / 16) + i,
 // channels 16 ct + l % 16) is head r's hi part for r < G and head r - G's lo part for
@@ -380,7 +388,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   }
   uint8_t *ring = &sm.u.ring[w][0][0];
   constexpr int SB = Stage<BV>::SIZE;
-  // items of this wave: body sets s0 .. s1-1, then 8-token window stages ws0 .. ws1-1
+  // items of this wave: 8-token window stages ws0 .. ws1-1, then body sets s0 .. s1-1
   const int nb = (int)(s1 - s0), nitems = nb + (ws1 - ws0);
   const int ns = (int)(a.n < a.S ? a.n : a.S);
   const int nw = ns + (int)(a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
@@ -390,11 +398,14 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   const uint8_t *sinkv = (const uint8_t *)a.sink_v + (size_t)bg * a.sink_bytes;
   const uint8_t *ringk = (const uint8_t *)a.ring_k + (size_t)bg * a.ring_bytes;
   const uint8_t *ringv = (const uint8_t *)a.ring_v + (size_t)bg * a.ring_bytes;
+  // items 0 .. nwin-1 are the window stages (first, so their VALU work overlaps the other
+  // waves' streaming rather than forming every wave's tail), then the body sets
+  const int nwin = ws1 - ws0;
   auto issue = [&](int item, uint8_t *dst) {
-    if (item < nb) {
-      stage_set<BV>(src, (int)s0 + item, dst);
+    if (item >= nwin) {
+      stage_set<BV>(src, (int)s0 + item - nwin, dst);
     } else {
-      const int t0 = 8 * (ws0 + item - nb);
+      const int t0 = 8 * (ws0 + item);
       stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
     }
   };
@@ -548,8 +559,8 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 
     // ---- PV on the f16 MFMA: instruction iota covers tiles 2 iota, 2 iota + 1; A row
     // r = head, K-slots 8 c .. 8 c + 7 = tokens 16 a + 4 c + e of those tiles
-    const u32x4 vw0 = *(const u32x4 *)(st + S::V + 32 * lane);
-    const u32x4 vw1 = *(const u32x4 *)(st + S::V + 32 * lane + 16);
+    const u32x4 vw0 = *(const u32x4 *)(st + S::V + 16 * lane);
+    const u32x4 vw1 = *(const u32x4 *)(st + S::V + 1024 + 16 * lane);
     u32x4 vh = (u32x4){0u, 0u, 0u, 0u};
     if constexpr (BV == 3) vh = *(const u32x4 *)(st + S::VH + 16 * lane);
     const unsigned vws[8] = {vw0[0], vw0[1], vw0[2], vw0[3], vw1[0], vw1[1], vw1[2], vw1[3]};
@@ -583,8 +594,9 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   };
 
   // items: items it + 1 .. it + kStages - 1 are staged while item it computes.  The
-  // inner loop takes full sets that raise no running max; a set that does leaves it
-  // for the rescale and finishes there; the ragged last set, if any, comes after.
+  // loop takes the full sets; the rescale is marked unlikely, which keeps it out of line
+  // and the PV accumulators in place from set to set (with it inline the compiler
+  // copies them around every set).  The ragged last set, if any, comes after.
   using FullTag = std::integral_constant<bool, true>;
   using TailTag = std::integral_constant<bool, false>;
   auto body_sets = [&](auto kq_tag, auto vq_tag) {
@@ -592,26 +604,25 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
     const int nfull = full_end <= s0 ? 0 : (int)(full_end - s0 < nb ? full_end - s0 : nb);
     float sc[NQ][4], mxr[NQ];
     int it = 0;
-    while (it < nfull) {
-      const uint8_t *st = nullptr;
-      bool up = false;
-      for (; it < nfull; ++it) {
-        st = advance(it);
-        up = phase1(FullTag{}, kq_tag, s0 + it, st, sc, mxr);
-        if (up) break;
-        phase2(FullTag{}, vq_tag, s0 + it, st, sc);
-      }
-      if (!up) break;
-      rescale(mxr);
+    for (; it < nfull; ++it) {
+      const uint8_t *st = advance(nwin + it);
+      if (__builtin_expect(phase1(FullTag{}, kq_tag, s0 + it, st, sc, mxr), 0)) rescale(mxr);
       phase2(FullTag{}, vq_tag, s0 + it, st, sc);
-      ++it;
     }
     for (; it < nb; ++it) {
-      const uint8_t *st = advance(it);
+      const uint8_t *st = advance(nwin + it);
       if (phase1(TailTag{}, kq_tag, s0 + it, st, sc, mxr)) rescale(mxr);
       phase2(TailTag{}, vq_tag, s0 + it, st, sc);
     }
   };
+  float wm[G], wl[G], wacc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
+  for (int it = 0; it < nwin; ++it) {
+    const uint8_t *st = advance(it);
+    const int t0 = 8 * (ws0 + it);
+    window_stage<G, BV>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
+  }
   using Yes = std::true_type;
   using No = std::false_type;
   if (a.quant_k == WUSHKV_Q_QUEST) {
@@ -620,15 +631,6 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   } else {
     if (a.quant_v == WUSHKV_Q_QUEST) body_sets(No{}, Yes{});
     else body_sets(No{}, No{});
-  }
-  int it = nb;
-  float wm[G], wl[G], wacc[G][2];
-#pragma unroll
-  for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
-  for (; it < nitems; ++it) {
-    const uint8_t *st = advance(it);
-    const int t0 = 8 * (ws0 + it - nb);
-    window_stage<G, BV>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
