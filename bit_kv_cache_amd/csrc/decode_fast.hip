@@ -44,8 +44,11 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: kSplitWaves when a KV head's partitions span several workgroups
+// (their partials merged by merge_kernel), kWholeWaves when one workgroup holds all of a
+// KV head's partitions and writes its output directly.
+constexpr int kSplitWaves = 4;
+constexpr int kWholeWaves = 12;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // DPP encodings (gfx9): row_ror:n = 0x120 + n rotates within a row of 16 lanes,
@@ -76,24 +79,24 @@ constexpr int kWbPitch = 80;
 
 constexpr int kStages = 2;   // ring slots per wave: the item computed and kStages - 1 ahead
 
-template <int G, int BV>
+template <int G, int BV, int NW>
 struct __align__(16) FastSmem {
   unsigned qi[G][kD];             // q~ in fixed point, offset to unsigned (balanced digits)
   float q[G][kD];
-  unsigned wb[kWaves][G][kWbPitch];  // body set: W as fp16 (hi | lo << 16) [head][token]
-  unsigned wzero[kSet];           // zeros: the PV A rows past G read these
+  unsigned wb[NW][G][kWbPitch];   // body set: W as fp16 (hi | lo << 16) [head][token]
+  unsigned wzero[kSet];           // zeros: the PV A rows past 2 G read these
   int qe[16];                     // per head: q~ = (qi - kDigitBias) 2^(e - 21)
-  float wp[kWaves][G][8];         // window stage: probabilities [head][token]
-  float wmx[kWaves][16], wls[kWaves][16];  // window partial: max and sum per head
+  float wp[NW][G][8];             // window stage: probabilities [head][token]
+  float wmx[NW][16], wls[NW][16]; // window partial: max and sum per head
   union {
-    uint8_t ring[kWaves][kStages][Stage<BV>::SIZE];
+    uint8_t ring[NW][kStages][Stage<BV>::SIZE];
     struct {
-      float o[kWaves][16][kD];    // per wave: rows (tile-phase, head), columns channels
-      float wo[kWaves][G][kD];    // window partial: weighted FP16 values [head][channel]
+      float o[NW][2 * G][kD];     // per wave: PV rows (hi parts, then lo parts), channels
+      float wo[NW][G][kD];        // window partial: weighted FP16 values [head][channel]
     };
   } u;
   float sq[16];                   // per head: sum of q~ (the zero-point term)
-  float m[kWaves][16], l[kWaves][16], z[kWaves][16];
+  float m[NW][16], l[NW][16], z[NW][16];
 };
 
 // A 32-bit constant held in a VGPR the compiler cannot fold, so masks and exponent
@@ -304,9 +307,45 @@ __device__ __forceinline__ void wait_staged(int pending) {
   else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
 }
 
-template <int G, int BV>
-__device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
+template <int G, int BV, int NW>
+__device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
                              float (&wl)[G], float (&wacc)[G][2]);
+
+// The workgroup's query setup: q and q~ of its G heads into LDS, per head the exponent
+// e of max |q~| and sum(q~), then q~ on its fixed-point grid.  Every wave calls it.
+template <int G, int BV, int NW>
+__device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int b, int h0) {
+  constexpr int NT = 64 * NW;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < G * kD; i += NT) {
+    const int hh = i / kD, j = i % kD;
+    const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
+    sm.qi[hh][j] = __float_as_uint(a.qt[off]);
+    sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
+  }
+  __syncthreads();
+  if (tid < G) {
+    float mxa = 0.f, s = 0.f;
+    for (int j = 0; j < kD; ++j) {
+      const float v = __uint_as_float(sm.qi[tid][j]);
+      mxa = fmaxf(mxa, fabsf(v));
+      s += v;
+    }
+    // |q~| < 2^(e + 1); heads below 2^-100 count as zero (their digits are all zero)
+    sm.qe[tid] = mxa >= 0x1p-100f ? ilogbf(mxa) : -100;
+    sm.sq[tid] = s;
+  }
+  if (tid < kSet) sm.wzero[tid] = 0u;
+  __syncthreads();
+  // fixed point: Q = rint(q~ 2^(21 - e)), |Q| <= 2^22, stored as Q + kDigitBias
+  for (int i = tid; i < G * kD; i += NT) {
+    const int hh = i / kD, j = i % kD;
+    const float v = __uint_as_float(sm.qi[hh][j]);
+    const int Q = (int)rintf(ldexpf(v, 21 - sm.qe[hh]));
+    sm.qi[hh][j] = (unsigned)(Q + (int)kDigitBias);
+  }
+  __syncthreads();
+}
 
 // One wave of a KV partition: its 8-token stages [ws0, ws1) of the FP16 window list,
 // then its body sets [s0, s1), all streamed through the wave's LDS ring.
@@ -314,8 +353,8 @@ __device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, in
 // heads h + 4 qd (qd < G / 4).  PV output row r (O lane l holds rows 4 (l / 16) + i,
 // channels 16 ct + l % 16) is head r's hi part for r < G and head r - G's lo part for
 // G <= r < 2 G; the two are summed in the workgroup merge.
-template <int G, int BV>
-__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
+template <int G, int BV, int NW>
+__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
                           f32x4 (&O)[8], float (&m_out)[G / 4], float (&l_out)[G / 4], float (&z_out)[G / 4],
                           float (&wm_out)[G], float (&wl_out)[G], float (&wacc_out)[G][2]) {
   constexpr int NQ = G / 4;            // head quads: QK MFMAs per tile
@@ -324,6 +363,49 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int Lv = 1 << BV;
+
+  SetSource src;
+  {
+    const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
+    const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
+    const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
+    const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
+    src.k = __builtin_amdgcn_make_buffer_rsrc((void *)kplane, 0, (int)a.kcode_bytes, kRsrcWord3);
+    src.v = __builtin_amdgcn_make_buffer_rsrc((void *)vplane, 0, (int)a.vcode_bytes, kRsrcWord3);
+    const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
+    const bool pk = lane < 4 * kb;
+    src.pact = pk || (lane >= 16 && lane - 16 < 4 * vbn);
+    src.par = pk ? kpar + 16 * lane : vpar + 16 * (lane - 16);
+    src.pstride = 64 * (pk ? kb : vbn);
+    src.vset = (int)a.vset_bytes;
+  }
+  uint8_t *ring = &sm.u.ring[w][0][0];
+  constexpr int SB = Stage<BV>::SIZE;
+  // items of this wave: 8-token window stages ws0 .. ws1-1, then body sets s0 .. s1-1
+  const int nb = (int)(s1 - s0), nitems = nb + (ws1 - ws0);
+  const int ns = (int)(a.n < a.S ? a.n : a.S);
+  const int nw = ns + (int)(a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+  const unsigned rsz = (unsigned)(a.R + a.C);
+  const unsigned first_slot = (unsigned)(a.nq % rsz);
+  const uint8_t *sinkk = (const uint8_t *)a.sink_k + (size_t)bg * a.sink_bytes;
+  const uint8_t *sinkv = (const uint8_t *)a.sink_v + (size_t)bg * a.sink_bytes;
+  const uint8_t *ringk = (const uint8_t *)a.ring_k + (size_t)bg * a.ring_bytes;
+  const uint8_t *ringv = (const uint8_t *)a.ring_v + (size_t)bg * a.ring_bytes;
+  // items 0 .. nwin-1 are the window stages (first, so their VALU work overlaps the other
+  // waves' streaming rather than forming every wave's tail), then the body sets
+  const int nwin = ws1 - ws0;
+  auto issue = [&](int item, uint8_t *dst) {
+    if (item >= nwin) {
+      stage_set<BV>(src, (int)s0 + item - nwin, dst);
+    } else {
+      const int t0 = 8 * (ws0 + item);
+      stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
+    }
+  };
+  // prologue: the first kStages - 1 items (item k lives in slot k % kStages), queued
+  // before the query setup so that the setup overlaps their loads
+  for (int k = 0; k < kStages - 1 && k < nitems; ++k) issue(k, ring + k * SB);
+  setup_queries(a, sm, bg / a.Hkv, (bg % a.Hkv) * G);
 
   // q~ as eight balanced base-8 digits (integers in [-4, 3], exact in e2m1) on one fixed
   // point grid per head, in the rows of NM fp4 A operands: row r of operand m holds
@@ -371,46 +453,6 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   const unsigned *arow = ar < 2 * G ? &sm.wb[w][ar < G ? ar : ar - G][0] : &sm.wzero[0];
   const unsigned asel = ar < G ? 0x05040100u : 0x07060302u;
 
-  SetSource src;
-  {
-    const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
-    const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
-    const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
-    const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
-    src.k = __builtin_amdgcn_make_buffer_rsrc((void *)kplane, 0, (int)a.kcode_bytes, kRsrcWord3);
-    src.v = __builtin_amdgcn_make_buffer_rsrc((void *)vplane, 0, (int)a.vcode_bytes, kRsrcWord3);
-    const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
-    const bool pk = lane < 4 * kb;
-    src.pact = pk || (lane >= 16 && lane - 16 < 4 * vbn);
-    src.par = pk ? kpar + 16 * lane : vpar + 16 * (lane - 16);
-    src.pstride = 64 * (pk ? kb : vbn);
-    src.vset = (int)a.vset_bytes;
-  }
-  uint8_t *ring = &sm.u.ring[w][0][0];
-  constexpr int SB = Stage<BV>::SIZE;
-  // items of this wave: 8-token window stages ws0 .. ws1-1, then body sets s0 .. s1-1
-  const int nb = (int)(s1 - s0), nitems = nb + (ws1 - ws0);
-  const int ns = (int)(a.n < a.S ? a.n : a.S);
-  const int nw = ns + (int)(a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
-  const unsigned rsz = (unsigned)(a.R + a.C);
-  const unsigned first_slot = (unsigned)(a.nq % rsz);
-  const uint8_t *sinkk = (const uint8_t *)a.sink_k + (size_t)bg * a.sink_bytes;
-  const uint8_t *sinkv = (const uint8_t *)a.sink_v + (size_t)bg * a.sink_bytes;
-  const uint8_t *ringk = (const uint8_t *)a.ring_k + (size_t)bg * a.ring_bytes;
-  const uint8_t *ringv = (const uint8_t *)a.ring_v + (size_t)bg * a.ring_bytes;
-  // items 0 .. nwin-1 are the window stages (first, so their VALU work overlaps the other
-  // waves' streaming rather than forming every wave's tail), then the body sets
-  const int nwin = ws1 - ws0;
-  auto issue = [&](int item, uint8_t *dst) {
-    if (item >= nwin) {
-      stage_set<BV>(src, (int)s0 + item - nwin, dst);
-    } else {
-      const int t0 = 8 * (ws0 + item);
-      stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
-    }
-  };
-  // prologue: the first kStages - 1 items; item k lives in slot k % kStages
-  for (int k = 0; k < kStages - 1 && k < nitems; ++k) issue(k, ring + k * SB);
   // before item it computes: queue item it + kStages - 1, wait until item it landed
   auto advance = [&](int it) {
     const int ahead = it + kStages - 1;
@@ -621,7 +663,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
   for (int it = 0; it < nwin; ++it) {
     const uint8_t *st = advance(it);
     const int t0 = 8 * (ws0 + it);
-    window_stage<G, BV>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
+    window_stage<G, BV, NW>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
   }
   using Yes = std::true_type;
   using No = std::false_type;
@@ -653,8 +695,8 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV> &sm, int bg, int6
 // 8 lanes per token, 16 channels each, summed over the 8; values: lane = two
 // channels.  The stage folds into this wave's window partial: per head the running
 // max and sum (the same in every lane) and this lane's two weighted value channels.
-template <int G, int BV>
-__device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
+template <int G, int BV, int NW>
+__device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
                              float (&wl)[G], float (&wacc)[G][2]) {
   using S = Stage<BV>;
   const int lane = threadIdx.x & 63;
@@ -708,43 +750,16 @@ __device__ void window_stage(FastSmem<G, BV> &sm, const uint8_t *st, int cnt, in
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int G, int BV>
-__global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int nwg_body) {
-  __shared__ FastSmem<G, BV> sm;
+// nwg_body workgroups per KV head; with one, the workgroup's merge is the output.
+template <int G, int BV, int NW>
+__global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int nwg_body) {
+  constexpr int NT = 64 * NW;
+  __shared__ FastSmem<G, BV, NW> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int h0 = g * G;
-
-  for (int i = tid; i < G * kD; i += kThreads) {
-    const int hh = i / kD, j = i % kD;
-    const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
-    sm.qi[hh][j] = __float_as_uint(a.qt[off]);
-    sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
-  }
-  __syncthreads();
-  if (tid < G) {
-    float mxa = 0.f, s = 0.f;
-    for (int j = 0; j < kD; ++j) {
-      const float v = __uint_as_float(sm.qi[tid][j]);
-      mxa = fmaxf(mxa, fabsf(v));
-      s += v;
-    }
-    // |q~| < 2^(e + 1); heads below 2^-100 count as zero (their digits are all zero)
-    sm.qe[tid] = mxa >= 0x1p-100f ? ilogbf(mxa) : -100;
-    sm.sq[tid] = s;
-  }
-  if (tid < kSet) sm.wzero[tid] = 0u;
-  __syncthreads();
-  // fixed point: Q = rint(q~ 2^(21 - e)), |Q| <= 2^22, stored as Q + kDigitBias
-  for (int i = tid; i < G * kD; i += kThreads) {
-    const int hh = i / kD, j = i % kD;
-    const float v = __uint_as_float(sm.qi[hh][j]);
-    const int Q = (int)rintf(ldexpf(v, 21 - sm.qe[hh]));
-    sm.qi[hh][j] = (unsigned)(Q + (int)kDigitBias);
-  }
-  __syncthreads();
 
   f32x4 O[8];
   float bm[G / 4], bl[G / 4], bz[G / 4];
@@ -753,19 +768,22 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
   float wm[G], wl[G], wacc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) { wm[h] = -INFINITY; wl[h] = 0.f; wacc[h][0] = wacc[h][1] = 0.f; }
-  const int part = (int)blockIdx.x * kWaves + w;
+  // every wave runs body_wave (its query setup is workgroup-wide); waves past the last
+  // partition get empty ranges
+  const int part = (int)blockIdx.x * NW + w;
+  int64_t s0 = 0, s1 = 0;
+  int ws0 = 0, ws1 = 0;
   if (part < a.P) {
     const int64_t nsets = (a.nq + kSet - 1) / kSet;
-    const int64_t s0 = nsets * part / a.P, s1 = nsets * (part + 1) / a.P;
+    s0 = nsets * part / a.P;
+    s1 = nsets * (part + 1) / a.P;
     const int64_t ns = a.n < a.S ? a.n : a.S;
     const int64_t nw = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
     const int64_t nws = (nw + 7) / 8;
-    const int ws0 = (int)(nws * part / a.P), ws1 = (int)(nws * (part + 1) / a.P);
-    body_wave<G, BV>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
-  } else {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) O[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    ws0 = (int)(nws * part / a.P);
+    ws1 = (int)(nws * (part + 1) / a.P);
   }
+  body_wave<G, BV, NW>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
   __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -793,19 +811,21 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
   }
   __syncthreads();
 
-  // ---- merge the 4 waves into this workgroup's partial
+  // ---- merge the workgroup's waves: its partial, or the output when it is the only
+  // workgroup of its KV head
   const int P1 = a.P + 1;
-  for (int i = tid; i < G * kD; i += kThreads) {
+  const bool direct = nwg_body == 1;
+  for (int i = tid; i < G * kD; i += NT) {
     const int hh = i / kD, j = i % kD;
     float mstar = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       if (sm.l[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.m[ww][hh]);
       if (sm.wls[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.wmx[ww][hh]);
     }
     float num = 0.f, den = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       if (sm.l[ww][hh] > 0.f) {
         const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
         const float o = sm.z[ww][hh] + (sm.u.o[ww][hh][j] + sm.u.o[ww][G + hh][j]);
@@ -818,11 +838,15 @@ __global__ void __launch_bounds__(kThreads) decode_fast_kernel(DecodeArgs a, int
         den = fmaf(f, sm.wls[ww][hh], den);
       }
     }
-    const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1 + blockIdx.x;
-    a.part_o[row * kD + j] = num;
-    if (j == 0) {
-      a.part_ml[row * 2] = mstar;
-      a.part_ml[row * 2 + 1] = den;
+    if (direct) {
+      a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / den;
+    } else {
+      const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1 + blockIdx.x;
+      a.part_o[row * kD + j] = num;
+      if (j == 0) {
+        a.part_ml[row * 2] = mstar;
+        a.part_ml[row * 2 + 1] = den;
+      }
     }
   }
 
@@ -837,33 +861,66 @@ bool decode_fast_supported(const DecodeArgs &a) {
          a.vpar_bytes < (1u << 31);
 }
 
-int decode_fast_partials(const DecodeArgs &a) { return (a.P + kWaves - 1) / kWaves; }
+// Launch shape: one kWholeWaves-wave workgroup per KV head when the split count equals
+// it and there are at least as many KV heads as compute units (G = 4, whose LDS fits),
+// else ceil(P / kSplitWaves) workgroups of kSplitWaves waves per KV head.
+static int cu_count() {
+  static int c = -1;
+  if (c < 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      hipGetLastError();
+      return 1 << 30;
+    }
+    c = prop.multiProcessorCount;
+  }
+  return c;
+}
 
-// Waves of the MFMA decode the GPU holds at once for (G, bits_v); 0 if unknown.
+static bool whole_layout(const DecodeArgs &a) {
+  return a.G == 4 && a.P == kWholeWaves && a.B * a.Hkv >= cu_count();
+}
+
+int decode_fast_partials(const DecodeArgs &a) {
+  return whole_layout(a) ? 1 : (a.P + kSplitWaves - 1) / kSplitWaves;
+}
+
+bool decode_fast_direct(const DecodeArgs &a) { return decode_fast_partials(a) == 1; }
+
+// Waves of the MFMA decode the GPU holds at once for (G, bits_v) in the split layout;
+// 0 if unknown.
 int decode_fast_resident_waves(int G, int bits_v) {
   static int cache[2][2] = {{-1, -1}, {-1, -1}};
   int &c = cache[G == 8][bits_v == 3];
   if (c >= 0) return c;
-  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2> : (const void *)decode_fast_kernel<4, 3>)
-                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2> : (const void *)decode_fast_kernel<8, 3>);
-  int dev = 0, blocks = 0;
-  hipDeviceProp_t prop;
-  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, kThreads, 0) != hipSuccess) {
+  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2, kSplitWaves>
+                                           : (const void *)decode_fast_kernel<4, 3, kSplitWaves>)
+                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2, kSplitWaves>
+                                           : (const void *)decode_fast_kernel<8, 3, kSplitWaves>);
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * kSplitWaves, 0) != hipSuccess) {
     hipGetLastError();
     return 0;
   }
-  c = blocks * kWaves * prop.multiProcessorCount;
+  c = blocks * kSplitWaves * cu_count();
   return c;
 }
 
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
-  const int nwg = (a.P + kWaves - 1) / kWaves;
+  const int nwg = decode_fast_partials(a);
   dim3 grid(nwg, a.B * a.Hkv);
-  if (a.G == 4 && a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2>), grid, dim3(kThreads), 0, s, a, nwg);
-  else if (a.G == 4) hipLaunchKernelGGL((decode_fast_kernel<4, 3>), grid, dim3(kThreads), 0, s, a, nwg);
-  else if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<8, 2>), grid, dim3(kThreads), 0, s, a, nwg);
-  else hipLaunchKernelGGL((decode_fast_kernel<8, 3>), grid, dim3(kThreads), 0, s, a, nwg);
+  if (whole_layout(a)) {
+    constexpr int NT = 64 * kWholeWaves;
+    if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2, kWholeWaves>), grid, dim3(NT), 0, s, a, nwg);
+    else hipLaunchKernelGGL((decode_fast_kernel<4, 3, kWholeWaves>), grid, dim3(NT), 0, s, a, nwg);
+    return hipGetLastError();
+  }
+  constexpr int NT = 64 * kSplitWaves;
+  if (a.G == 4 && a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
+  else if (a.G == 4) hipLaunchKernelGGL((decode_fast_kernel<4, 3, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
+  else if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<8, 2, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
+  else hipLaunchKernelGGL((decode_fast_kernel<8, 3, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
   return hipGetLastError();
 }
 

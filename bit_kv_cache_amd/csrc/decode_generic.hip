@@ -218,6 +218,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
   int nparts;
   if (decode_fast_supported(a) && !a.force_generic) {
     e = launch_decode_fast(a, s);
+    if (e != hipSuccess || decode_fast_direct(a)) return e;
     nparts = decode_fast_partials(a);
   } else {
     e = launch_decode_generic(a, s);

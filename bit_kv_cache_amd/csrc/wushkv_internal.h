@@ -94,6 +94,7 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s);
 bool decode_fast_supported(const DecodeArgs &a);
 int decode_fast_partials(const DecodeArgs &a);
+bool decode_fast_direct(const DecodeArgs &a);   // the fast kernel writes out itself
 int decode_fast_resident_waves(int G, int bits_v);
 
 // Device helpers ------------------------------------------------------------

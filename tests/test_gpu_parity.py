@@ -205,6 +205,27 @@ def test_fast_decode_matches_generic_kernel(wl, P, monkeypatch):
     r.check_decode(q, qt, fast)
 
 
+@pytest.mark.parametrize("bits_v", [2, 3])
+def test_whole_workgroup_layout_matches_generic(bits_v, monkeypatch):
+    """At the serving batch (256 (batch row, KV head) pairs) with 12 splits (the
+    library's choice for 2-bit values) each KV head's partitions share one workgroup,
+    which writes the output itself."""
+    w = configs.SERVING.scaled(name=f"whole{bits_v}", seed=24 + bits_v, context=2000, bits_v=bits_v)
+    r = Run(w)
+    r.append(w.context)
+    r.append(1)
+    if bits_v == 2:
+        assert W.decode_num_splits(r.cache, r.cache.n, w.num_q_heads, 0) == 12
+    q, qt, fast = r.decode(0, num_splits=12)
+    monkeypatch.setenv("WUSHKV_DECODE_KERNEL", "generic")
+    _, _, gen_out = r.decode(0, num_splits=12)
+    monkeypatch.delenv("WUSHKV_DECODE_KERNEL")
+    rel = float((fast - gen_out).norm() / gen_out.norm())
+    say(f"[whole vs generic] bits_v={bits_v} rel-L2 {rel:.3e}")
+    assert rel < 1e-4
+    r.check_decode(q, qt, fast, heads=[(0, 0), (17, 3), (31, 7)])
+
+
 # ---- full-size workloads, in the launch configuration the benchmark times, checked on
 # sampled (batch row, KV head) pairs (the oracle builds each sampled head's whole cache)
 
