@@ -97,6 +97,8 @@ struct __align__(16) FastSmem {
   } u;
   float sq[16];                   // per head: sum of q~ (the zero-point term)
   float m[NW][16], l[NW][16], z[NW][16];
+  unsigned aqw[G / 2][4][64];     // q~ digit operands [operand][register][lane], shared by the waves
+  float mst[16], den[16];         // merge: per head the workgroup's max and denominator
 };
 
 // A 32-bit constant held in a VGPR the compiler cannot fold, so masks and exponent
@@ -345,6 +347,22 @@ __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int 
     sm.qi[hh][j] = (unsigned)(Q + (int)kDigitBias);
   }
   __syncthreads();
+  // the fp4 A operands of the QK MFMA, the same for every wave: register d of operand m
+  // for lane l holds nibbles i = 0..7 at K-slot 32 (l / 16) + 8 d + i of row l % 16
+  for (int e = tid; e < (G / 2) * 4 * 64; e += NT) {
+    const int m = e >> 8, d = (e >> 6) & 3, l = e & 63;
+    int h, j;
+    digit_row(m, l & 15, h, j);
+    const int sft = 21 - 3 * j;
+    unsigned word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned f = (sm.qi[h][kslot_channel(32 * (l >> 4) + 8 * d + i)] >> sft) & 7u;
+      word |= ((kDigitE2M1 >> (4 * f)) & 15u) << (4 * i);
+    }
+    sm.aqw[m][d][l] = word;
+  }
+  __syncthreads();
 }
 
 // One wave of a KV partition: its 8-token stages [ws0, ws1) of the FP16 window list,
@@ -420,20 +438,8 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   for (int m = 0; m < NM; ++m) {
     int h, j;
     digit_row(m, lane & 15, h, j);
-    const int sft = 21 - 3 * j;
-    unsigned wd[4];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      unsigned word = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int ch = kslot_channel(32 * g4 + 8 * d + i);
-        const unsigned f = (sm.qi[h][ch] >> sft) & 7u;
-        word |= ((kDigitE2M1 >> (4 * f)) & 15u) << (4 * i);
-      }
-      wd[d] = word;
-    }
-    aq[m] = (i32x8){(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3], 0, 0, 0, 0};
+    aq[m] = (i32x8){(int)sm.aqw[m][0][lane], (int)sm.aqw[m][1][lane], (int)sm.aqw[m][2][lane],
+                    (int)sm.aqw[m][3][lane], 0, 0, 0, 0};
     sa[m] = 127 + sm.qe[h] - 3 * j;
   }
   // scores in units of 1 / a_sc: s (q~ . c / 2) + z sum(q~) / 2 (the MFMA sums
@@ -812,44 +818,53 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
   __syncthreads();
 
   // ---- merge the workgroup's waves: its partial, or the output when it is the only
-  // workgroup of its KV head
+  // workgroup of its KV head.  Per head first: the max over the waves' non-empty body
+  // and window partials, each partial's factor 2^(m - max) (0 when empty) in place of
+  // its max, and the denominator.
   const int P1 = a.P + 1;
   const bool direct = nwg_body == 1;
-  for (int i = tid; i < G * kD; i += NT) {
-    const int hh = i / kD, j = i % kD;
+  if (tid < G) {
+    const int hh = tid;
     float mstar = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       if (sm.l[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.m[ww][hh]);
       if (sm.wls[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.wmx[ww][hh]);
     }
-    float num = 0.f, den = 0.f;
+    float den = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      if (sm.l[ww][hh] > 0.f) {
-        const float f = __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar);
-        const float o = sm.z[ww][hh] + (sm.u.o[ww][hh][j] + sm.u.o[ww][G + hh][j]);
-        num = fmaf(f, o, num);
-        den = fmaf(f, sm.l[ww][hh], den);
-      }
-      if (sm.wls[ww][hh] > 0.f) {
-        const float f = __builtin_amdgcn_exp2f(sm.wmx[ww][hh] - mstar);
-        num = fmaf(f, sm.u.wo[ww][hh][j], num);
-        den = fmaf(f, sm.wls[ww][hh], den);
-      }
+      const float fb = sm.l[ww][hh] > 0.f ? __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar) : 0.f;
+      const float fw = sm.wls[ww][hh] > 0.f ? __builtin_amdgcn_exp2f(sm.wmx[ww][hh] - mstar) : 0.f;
+      den = fmaf(fb, sm.l[ww][hh], den);
+      den = fmaf(fw, sm.wls[ww][hh], den);
+      sm.m[ww][hh] = fb;
+      sm.wmx[ww][hh] = fw;
+    }
+    sm.mst[hh] = mstar;
+    sm.den[hh] = den;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * kD; i += NT) {
+    const int hh = i / kD, j = i % kD;
+    float num = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      // an empty partial has factor 0 and finite (zero) sums
+      num = fmaf(sm.m[ww][hh], sm.z[ww][hh] + (sm.u.o[ww][hh][j] + sm.u.o[ww][G + hh][j]), num);
+      num = fmaf(sm.wmx[ww][hh], sm.u.wo[ww][hh][j], num);
     }
     if (direct) {
-      a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / den;
+      a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / sm.den[hh];
     } else {
       const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1 + blockIdx.x;
       a.part_o[row * kD + j] = num;
       if (j == 0) {
-        a.part_ml[row * 2] = mstar;
-        a.part_ml[row * 2 + 1] = den;
+        a.part_ml[row * 2] = sm.mst[hh];
+        a.part_ml[row * 2 + 1] = sm.den[hh];
       }
     }
   }
-
 }
 
 }  // namespace
