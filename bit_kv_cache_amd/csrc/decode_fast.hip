@@ -698,7 +698,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
 }
 
 // One window stage: cnt <= 8 FP16 window tokens in a ring slot, on fp32 VALU.  Scores:
-// 8 lanes per token, 16 channels each, summed over the 8; values: lane = two
+// 8 lanes per token, 16 channels each, summed over the 8 with DPP; values: lane = two
 // channels.  The stage folds into this wave's window partial: per head the running
 // max and sum (the same in every lane) and this lane's two weighted value channels.
 template <int G, int BV, int NW>
@@ -711,6 +711,12 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
   const bool valid = j < cnt;
   const f16x8 k0 = *(const f16x8 *)(st + S::WK + 256 * j + 32 * cc);
   const f16x8 k1 = *(const f16x8 *)(st + S::WK + 256 * j + 32 * cc + 16);
+  float kf[16];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kf[e] = (float)k0[e];
+    kf[8 + e] = (float)k1[e];
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float x = 0.f;
@@ -718,22 +724,31 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
     for (int c = 0; c < 4; ++c) {
       const f32x4 qv = *(const f32x4 *)&sm.q[h][16 * cc + 4 * c];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x = fmaf(qv[e], (float)(c < 2 ? k0[4 * c + e] : k1[4 * (c - 2) + e]), x);
+      for (int e = 0; e < 4; ++e) x = fmaf(qv[e], kf[4 * c + e], x);
     }
-    x += __shfl_xor(x, 1);
-    x += __shfl_xor(x, 2);
-    x += __shfl_xor(x, 4);
-    // every lane of token j holds its score; max and sum run over the 8 tokens
+    // sum over the token's 8 lanes (quad swaps, then the half-row mirror pairs the quads)
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_half_mirror row_mask:0xf bank_mask:0xf"
+        : "+v"(x));
+    // every lane of token j holds its score; a row holds tokens 2r and 2r + 1, so the
+    // max and sum over the 8 tokens are a row_ror:8 step and the four rows' lane 0
     const float sc = valid ? x * qk_scale : -INFINITY;
-    float mx = fmaxf(sc, __shfl_xor(sc, 8));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mr = sc;
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf" : "+v"(mr));
+    const float mx = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 0)),
+                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 16))),
+                           fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 32)),
+                                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mr), 48))));
     const float mn = fmaxf(wm[h], mx);
     const float al = __builtin_amdgcn_exp2f(wm[h] - mn);
     const float pr = valid ? __builtin_amdgcn_exp2f(sc - mn) : 0.f;
-    float ps = pr + __shfl_xor(pr, 8);
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    float pp = pr;
+    asm("s_nop 1\n\tv_add_f32_dpp %0, %0, %0 row_ror:8 row_mask:0xf bank_mask:0xf" : "+v"(pp));
+    const float ps = (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 0)) +
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 16))) +
+                     (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 32)) +
+                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pp), 48)));
     if (cc == 0) sm.wp[w][h][j] = pr;
     wl[h] = wl[h] * al + ps;
     wm[h] = mn;
@@ -743,12 +758,21 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  for (int u = 0; u < cnt; ++u) {
+  // values: lane = two channels; rows past cnt hold a copy of the first token and have
+  // probability 0
+  f32x4 pw[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    pw[h][0] = *(const f32x4 *)&sm.wp[w][h][0];
+    pw[h][1] = *(const f32x4 *)&sm.wp[w][h][4];
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
     const f16x2 vv = *(const f16x2 *)(st + S::WV + 256 * u + 4 * lane);
     const float v0 = (float)vv[0], v1 = (float)vv[1];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float pr = sm.wp[w][h][u];
+      const float pr = pw[h][u >> 2][u & 3];
       wacc[h][0] = fmaf(pr, v0, wacc[h][0]);
       wacc[h][1] = fmaf(pr, v1, wacc[h][1]);
     }
