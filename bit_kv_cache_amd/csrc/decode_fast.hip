@@ -420,9 +420,9 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
       stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
     }
   };
-  // prologue: the first kStages - 1 items (item k lives in slot k % kStages), queued
-  // before the query setup so that the setup overlaps their loads
-  for (int k = 0; k < kStages - 1 && k < nitems; ++k) issue(k, ring + k * SB);
+  // prologue: the first kStages items fill the ring (item k lives in slot k % kStages),
+  // queued before the query setup so that the setup overlaps their loads
+  for (int k = 0; k < kStages && k < nitems; ++k) issue(k, ring + k * SB);
   setup_queries(a, sm, bg / a.Hkv, (bg % a.Hkv) * G);
 
   // q~ as eight balanced base-8 digits (integers in [-4, 3], exact in e2m1) on one fixed
@@ -459,10 +459,11 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   const unsigned *arow = ar < 2 * G ? &sm.wb[w][ar < G ? ar : ar - G][0] : &sm.wzero[0];
   const unsigned asel = ar < G ? 0x05040100u : 0x07060302u;
 
-  // before item it computes: queue item it + kStages - 1, wait until item it landed
+  // before item it computes: queue item it + kStages - 1 (the prologue queued it for
+  // it == 0), wait until item it landed
   auto advance = [&](int it) {
-    const int ahead = it + kStages - 1;
-    if (ahead < nitems) issue(ahead, ring + (ahead % kStages) * SB);
+    const int ahead = it + kStages - 1;   // queued by the prologue when it == 0
+    if (it > 0 && ahead < nitems) issue(ahead, ring + (ahead % kStages) * SB);
     const int pending = nitems - 1 - it < kStages - 1 ? nitems - 1 - it : kStages - 1;
     wait_staged<BV>(pending);
     return ring + (it % kStages) * SB;
