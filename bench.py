@@ -3,8 +3,8 @@
 A step is one decode step of the batched-serving workload (32 sequences of
 32768 tokens, 32 query / 8 KV heads, head_dim 128, 2-bit percentile-clipped
 affine K and V, sink 64 / recent 256 / chunk 16): append one token to every
-sequence (flushing 16 tokens every 16th step), transform the queries, and run
-GQA decode attention over the whole cache.  The headline value is decode
+sequence (flushing 16 tokens every 16th step), then GQA decode attention over the
+whole cache with the query transform folded into its prologue.  The headline value is decode
 attention GB/s: algorithmic bytes the decode must move (codes, parameters, FP16
 windows, q, q~, out) per step over the step time.  A second leg times the bulk
 prefill flush (36 layers x 8 KV heads x 65536 tokens) at 2, 3 and 4 bits, and a
@@ -118,12 +118,9 @@ def run_decode_leg(args):
         W.append_flush(cache, steps_k[i], steps_v[i], t16)
         if ev is not None:
             ev[1].record()
-        W.query_transform(tinvt, qs[i], w.num_kv_heads, out=qt)
+        W.decode_attention_fused(cache, qs[i], tinvt, num_splits=P, workspace=ws, out=out, q_t=qt)
         if ev is not None:
             ev[2].record()
-        W.decode_attention(cache, qs[i], qt, num_splits=P, workspace=ws, out=out)
-        if ev is not None:
-            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
@@ -139,35 +136,36 @@ def run_decode_leg(args):
     ms_step = wall * 1e3 / args.steps
     nbytes = sum(decode_bytes(w, n_start + j + 1) for j in range(args.steps)) / args.steps
     # breakdown of a step, from further (untimed) steps with events between the calls
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_breakdown)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_breakdown)]
     for j in range(n_breakdown):
         step(args.warmup + args.steps + j, evs[j])
     torch.cuda.synchronize()
     app = sum(e[0].elapsed_time(e[1]) for e in evs) / n_breakdown
-    qtm = sum(e[1].elapsed_time(e[2]) for e in evs) / n_breakdown
-    dec_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / n_breakdown
-    log(f"[bench] step {ms_step:.4f} ms; breakdown (event intervals): append {app:.4f}, qtransform {qtm:.4f}, "
-        f"decode {dec_ms:.4f} ms; decode bytes {nbytes / 1e6:.1f} MB")
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n_breakdown
+    log(f"[bench] step {ms_step:.4f} ms; breakdown (event intervals): append {app:.4f}, "
+        f"decode with query transform {dec_ms:.4f} ms; decode bytes {nbytes / 1e6:.1f} MB")
 
     # The decode kernel's own average launch duration, for the roofline figure: the
     # same decode launched back to back on the stream, the host ahead of the GPU, so
     # no launch gap of the step loop is counted.
     q_last = qs[-1]
     reps = 30
+    def dec():
+        W.decode_attention_fused(cache, q_last, tinvt, num_splits=P, workspace=ws, out=out, q_t=qt)
     for _ in range(3):
-        W.decode_attention(cache, q_last, qt, num_splits=P, workspace=ws, out=out)
+        dec()
     torch.cuda.synchronize()
     k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     k0.record()
     for _ in range(reps):
-        W.decode_attention(cache, q_last, qt, num_splits=P, workspace=ws, out=out)
+        dec()
     k1.record()
     torch.cuda.synchronize()
     kern_ms = k0.elapsed_time(k1) / reps
     kern_bytes = decode_bytes(w, cache.n)
     log(f"[bench] decode kernel back to back: {kern_ms * 1e3:.1f} us per launch at n={cache.n} "
         f"({kern_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s)")
-    return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, app_ms=app, qt_ms=qtm, bytes=nbytes, splits=P,
+    return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, app_ms=app, bytes=nbytes, splits=P,
                 n=n_start, cache=cache, kern_ms=kern_ms, kern_bytes=kern_bytes)
 
 
@@ -319,13 +317,14 @@ def main():
                    "quant": "percentile-clipped affine 2-bit K and V", "sink": w.sink, "recent": w.recent,
                    "chunk": w.chunk, "splits": dl["splits"], "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "step_breakdown_ms": {"append_flush": round(dl["app_ms"], 5), "query_transform": round(dl["qt_ms"], 5),
-                              "decode_attention": round(dl["dec_ms"], 5),
+        "step_breakdown_ms": {"append_flush": round(dl["app_ms"], 5),
+                              "decode_attention_fused": round(dl["dec_ms"], 5),
                               "note": "event intervals of untimed steps after the timed region"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode attention: decode_fast_kernel<4,2> (split-K GQA decode) + merge_kernel",
+                     "kernel": "decode_fast_kernel<4,2,12>: GQA decode with the query transform in its "
+                               "prologue, one 12-wave workgroup per KV head (12 splits, merged in LDS)",
                      "bytes_per_launch": int(dl["kern_bytes"]), "us_per_launch": round(dl["kern_ms"] * 1e3, 2)},
     }
     if fl:

@@ -19,7 +19,7 @@ Q_QUEST, Q_AFFINE = 0, 1
 PLANES = ("sink_k", "sink_v", "ring_k", "ring_v", "codes_k", "codes_v", "par_k", "par_v")
 EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "wushkv_plane_bytes",
            "wushkv_decode_num_splits", "wushkv_decode_workspace_bytes", "wushkv_append_flush",
-           "wushkv_query_transform", "wushkv_decode_attention")
+           "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused")
 
 
 class WushKVError(RuntimeError):
@@ -62,10 +62,12 @@ def lib():
             "wushkv_append_flush": (ctypes.c_int, [P, i64, i32, vp, vp, i32, vp, vp]),
             "wushkv_query_transform": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, vp]),
             "wushkv_decode_attention": (ctypes.c_int, [P, i64, vp, i32, vp, i32, i32, vp, sz, vp, vp]),
+            "wushkv_decode_attention_fused": (ctypes.c_int, [P, i64, vp, i32, vp, vp, i32, i32, vp, sz, vp, vp]),
         }
         for name, (res, args) in sig.items():
-            fn = getattr(L, name)
-            fn.restype, fn.argtypes = res, args
+            fn = getattr(L, name, None)   # an older build may lack later entry points
+            if fn is not None:
+                fn.restype, fn.argtypes = res, args
         _lib = L
     return _lib
 
@@ -215,3 +217,23 @@ def decode_attention(cache: KVCache, q, q_t, n_tokens=None, num_splits=0, worksp
                                          Hq, num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
                                          _stream(stream, q.device)), "decode_attention")
     return out
+
+
+def decode_attention_fused(cache: KVCache, q, t_inv_t, n_tokens=None, num_splits=0, workspace=None, out=None,
+                           q_t=None, stream=None):
+    """decode_attention with the query transform folded in: forms q~ = T^{-T} q itself
+    (written to q_t, fp32 [B, Hq, d]) -> (out, q_t)."""
+    import torch
+    n_tokens = cache.n if n_tokens is None else n_tokens
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(cache, n_tokens, Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if q_t is None:
+        q_t = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention_fused(ctypes.byref(cache.desc), n_tokens, _ptr(q), _dtype_code(q),
+                                               _ptr(t_inv_t), _ptr(q_t), Hq, num_splits, _ptr(workspace),
+                                               workspace.numel(), _ptr(out), _stream(stream, q.device)),
+           "decode_attention_fused")
+    return out, q_t

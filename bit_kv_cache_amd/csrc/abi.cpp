@@ -229,9 +229,14 @@ int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtyp
   return hip_status();
 }
 
-int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
-                            const float *q_t, int32_t num_q_heads, int32_t num_splits, void *workspace,
-                            size_t workspace_bytes, float *out, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Decode with q~ given (tinvt == nullptr) or formed from q and T^{-T} into q_t.
+int decode_impl(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype, float *q_t,
+                const float *tinvt, int32_t num_q_heads, int32_t num_splits, void *workspace,
+                size_t workspace_bytes, float *out, void *stream) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -242,7 +247,7 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void 
   if (n_tokens > g.cap) return WUSHKV_ERR_CAPACITY;
   if ((st = check_planes(c)) != WUSHKV_OK) return st;
   if (!q || !q_t || !out) return WUSHKV_ERR_NULL;
-  if (misaligned(q) || misaligned(q_t) || misaligned(out)) return WUSHKV_ERR_ALIGN;
+  if (misaligned(q) || misaligned(q_t) || misaligned(out) || misaligned(tinvt)) return WUSHKV_ERR_ALIGN;
   size_t need = wushkv_decode_workspace_bytes(c, n_tokens, num_q_heads, num_splits);
   if (!workspace || need == 0 || workspace_bytes < need) return WUSHKV_ERR_WORKSPACE;
   if (misaligned(workspace)) return WUSHKV_ERR_ALIGN;
@@ -253,6 +258,7 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void 
   a.B = g.B; a.Hkv = g.Hkv; a.Hq = num_q_heads; a.G = G; a.d = g.d; a.S = g.S; a.R = g.R; a.C = g.C;
   a.n = n_tokens; a.nq = n_quantized(n_tokens, g.S, g.R, g.C); a.P = P;
   a.q = q; a.q_dtype = q_dtype; a.qt = q_t;
+  a.tinvt = tinvt; a.qt_out = tinvt ? q_t : nullptr;
   a.sink_k = (const _Float16 *)c->sink_k; a.sink_v = (const _Float16 *)c->sink_v;
   a.ring_k = (const _Float16 *)c->ring_k; a.ring_v = (const _Float16 *)c->ring_v;
   a.codes_k = (const uint8_t *)c->codes_k; a.codes_v = (const uint8_t *)c->codes_v;
@@ -271,6 +277,25 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void 
   hipGetLastError();
   if (launch_decode(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
   return hip_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
+                            const float *q_t, int32_t num_q_heads, int32_t num_splits, void *workspace,
+                            size_t workspace_bytes, float *out, void *stream) {
+  return decode_impl(c, n_tokens, q, q_dtype, const_cast<float *>(q_t), nullptr, num_q_heads, num_splits,
+                     workspace, workspace_bytes, out, stream);
+}
+
+int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
+                                  const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
+                                  void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  if (!t_k_inv_t) return WUSHKV_ERR_NULL;
+  return decode_impl(c, n_tokens, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+                     workspace_bytes, out, stream);
 }
 
 }  // extern "C"

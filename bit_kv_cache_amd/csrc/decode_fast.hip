@@ -315,17 +315,49 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
 
 // The workgroup's query setup: q and q~ of its G heads into LDS, per head the exponent
 // e of max |q~| and sum(q~), then q~ on its fixed-point grid.  Every wave calls it.
+// With a.tinvt the workgroup forms q~ = T^{-T} q itself (WUSH-KV digest, "method key
+// points": one d x d product per query), in the query transform kernel's arithmetic:
+// row i of T^{-T} per thread, four interleaved fp32 partial sums, so q~ is bit-identical
+// to that kernel's; the partition-0 workgroup writes it to a.qt_out.
 template <int G, int BV, int NW>
 __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int b, int h0) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
+  const bool fused = a.tinvt != nullptr;
   for (int i = tid; i < G * kD; i += NT) {
     const int hh = i / kD, j = i % kD;
     const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
-    sm.qi[hh][j] = __float_as_uint(a.qt[off]);
+    if (!fused) sm.qi[hh][j] = __float_as_uint(a.qt[off]);
     sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
   }
   __syncthreads();
+  if (fused) {
+    const float *M = a.tinvt + (size_t)(h0 / G) * kD * kD;
+    for (int i = tid; i < kD; i += NT) {
+      f32x4 s[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) s[hh] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int j = 0; j < kD; j += 4) {
+        const f32x4 t = *(const f32x4 *)(M + (size_t)i * kD + j);
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const f32x4 x = *(const f32x4 *)&sm.q[hh][j];
+          s[hh][0] = fmaf(t[0], x[0], s[hh][0]);
+          s[hh][1] = fmaf(t[1], x[1], s[hh][1]);
+          s[hh][2] = fmaf(t[2], x[2], s[hh][2]);
+          s[hh][3] = fmaf(t[3], x[3], s[hh][3]);
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float v = (s[hh][0] + s[hh][1]) + (s[hh][2] + s[hh][3]);
+        sm.qi[hh][i] = __float_as_uint(v);
+        if (blockIdx.x == 0) a.qt_out[((size_t)b * a.Hq + h0 + hh) * kD + i] = v;
+      }
+    }
+    __syncthreads();
+  }
   if (tid < G) {
     float mxa = 0.f, s = 0.f;
     for (int j = 0; j < kD; ++j) {

@@ -213,9 +213,17 @@ hipError_t launch_decode_generic(const DecodeArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_decode(const DecodeArgs &a0, hipStream_t s) {
   hipError_t e;
   int nparts;
+  DecodeArgs a = a0;
+  if (a.tinvt && (!decode_fast_supported(a) || a.force_generic)) {
+    // the fused query transform only lives in the MFMA kernel: form q~ first here
+    QtArgs qa{a.tinvt, a.q, a.qt_out, a.q_dtype, a.B, a.Hq, a.Hkv, a.d};
+    if ((e = launch_qtransform(qa, s)) != hipSuccess) return e;
+    a.qt = a.qt_out;
+    a.tinvt = nullptr;
+  }
   if (decode_fast_supported(a) && !a.force_generic) {
     e = launch_decode_fast(a, s);
     if (e != hipSuccess || decode_fast_direct(a)) return e;

@@ -76,6 +76,8 @@ struct DecodeArgs {
   const void *q;
   int q_dtype;
   const float *qt;
+  const float *tinvt;             // non-null: the decode forms q~ = T^{-T} q itself and
+  float *qt_out;                  // writes it here (else q~ is read from qt)
   const _Float16 *sink_k, *sink_v, *ring_k, *ring_v;
   const uint8_t *codes_k, *codes_v;
   const _Float16 *par_k, *par_v;

@@ -197,6 +197,23 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens,
                             void *workspace, size_t workspace_bytes,
                             float *out, void *stream);
 
+/*
+ * wushkv_decode_attention with the query transform folded in (WUSH-KV digest,
+ * "method key points": the query side of the key transform is one d x d product per
+ * query): the decode forms q~ = T^{-T} q itself and also writes it to q_t.
+ *   t_k_inv_t  fp32 [num_kv_heads][d][d], as for wushkv_query_transform.
+ *   q_t        fp32 [batch][num_q_heads][d], output: exactly what
+ *              wushkv_query_transform writes for the same q and t_k_inv_t.
+ * out equals that of wushkv_query_transform followed by wushkv_decode_attention bit
+ * for bit; one launch fewer (shapes the MFMA decode does not serve launch both).
+ * Arguments, workspace and errors as wushkv_decode_attention; t_k_inv_t NULL -> ERR_NULL.
+ */
+int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens,
+                                  const void *q, int32_t q_dtype, const float *t_k_inv_t,
+                                  float *q_t, int32_t num_q_heads, int32_t num_splits,
+                                  void *workspace, size_t workspace_bytes,
+                                  float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

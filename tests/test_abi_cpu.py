@@ -136,6 +136,22 @@ def test_decode_validation_and_workspace(lib):
     assert lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 0, 32, 0) == 0
 
 
+def test_fused_decode_validation(lib):
+    """The fused entry checks its arguments like the plain decode (nothing launches)."""
+    d = _spec().desc()
+    _fake_planes(d)
+    f = lib.wushkv_decode_attention_fused
+    p = ctypes.c_void_p(0x900000)
+    ws_need = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, None, p, 32, 0, p, ws_need, p, None) == W.ERR_NULL
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, ctypes.c_void_p(0x900004), p, 32, 0, p, ws_need, p,
+             None) == W.ERR_ALIGN
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, None, 32, 0, p, ws_need, p, None) == W.ERR_NULL
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, p, 32, 0, p, ws_need - 1, p, None) == W.ERR_WORKSPACE
+    assert f(ctypes.byref(d), 9000, p, W.DT_BF16, p, p, 32, 0, p, ws_need, p, None) == W.ERR_CAPACITY
+    assert f(ctypes.byref(d), 8000, p, W.DT_BF16, p, p, 30, 0, p, ws_need, p, None) == W.ERR_SHAPE
+
+
 def test_product_package_does_not_use_the_oracle():
     pkg = os.path.join(ROOT, "bit_kv_cache_amd")
     for dirpath, _, files in os.walk(pkg):

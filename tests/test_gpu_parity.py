@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import bit_kv_cache_amd as W
-from synth import configs
+from synth import configs, gen
 from tests.parity_util import Run, say
 
 pytestmark = pytest.mark.gpu
@@ -169,6 +169,30 @@ def test_decode_large_batch_short_context():
     r.append(1)
     q, qt, out = r.decode(0)
     r.check_decode(q, qt, out, heads=[(0, 0), (263, 4), (519, 7)])
+
+
+@pytest.mark.parametrize("wl", ["whole", "split", "generic", "forced"])
+def test_fused_query_transform_is_bitwise(wl, monkeypatch):
+    """The decode that forms q~ itself returns the same q~ and output, bit for bit, as
+    the query transform followed by the plain decode: the 12-wave layout, the split
+    layout, a shape only the generic kernel serves, and the generic kernel forced."""
+    w = {"whole": configs.SERVING.scaled(name="fw", seed=31, context=1500),
+         "split": configs.LAYER_8B.scaled(name="fs", seed=32, context=3000),
+         "generic": configs.TINY.scaled(name="fg", seed=33),
+         "forced": configs.LAYER_8B.scaled(name="ff", seed=34, context=2000)}[wl]
+    if wl == "forced":
+        monkeypatch.setenv("WUSHKV_DECODE_KERNEL", "generic")
+    r = Run(w, n_total=w.context + 1)
+    r.append(w.context)
+    r.append(1)
+    q = gen.queries(w, 0, 0, "cuda")
+    qt = W.query_transform(r.tinvt, q, w.num_kv_heads)
+    ref = W.decode_attention(r.cache, q, qt)
+    out, qt2 = W.decode_attention_fused(r.cache, q, r.tinvt)
+    torch.cuda.synchronize()
+    say(f"[fused] {wl}: q~ equal {torch.equal(qt, qt2)}, out equal {torch.equal(ref, out)}")
+    assert torch.equal(qt, qt2)
+    assert torch.equal(ref, out)
 
 
 def test_snapshot_restore_continues_bitwise():
