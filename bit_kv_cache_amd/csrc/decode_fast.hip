@@ -114,9 +114,14 @@ __device__ __forceinline__ unsigned vconst(unsigned c) {
 // fp16 is exactly BASE + c with BASE = 64, 16 or 4.  Pairs 2, 3, 4 are read in place,
 // pairs 5, 6, 7 from w >> 6 and pairs 0, 1 from w << 4, so a word costs two shifts
 // and one and/or per pair.
+// A 3-bit code c = c2 + 4 h enters as two operands on the same A: the 2-bit part c2
+// as above, and h alone at mantissa bit p = 6 + (k & 3) of an fp16 whose unit there
+// is 4, i.e. HBASE + 4 h with HBASE = 64 >> (k & 3).  The sixteen third bits of a word
+// come as a halfword of the high-bit plane; a byte permute puts pair k's two bits at
+// (k, 16 + k), and shifts by 6 (pairs 0-3) and 2 (pairs 4-7) carry them to p.
 struct VConst {
   unsigned m2, m3, m4, e2, e3, e4;  // masks and exponent patterns of positions 2, 3, 4
-  unsigned m3b, mhi, e3b;           // 3-bit codes: low bits at 6-7, third bit at 8, base 16
+  unsigned mh[4], eh[4];            // third bit at mantissa 6 + i, unit 4
 };
 
 __device__ __forceinline__ VConst make_vconst() {
@@ -124,7 +129,10 @@ __device__ __forceinline__ VConst make_vconst() {
   c.m2 = vconst(0x00300030u); c.e2 = vconst(0x54005400u);
   c.m3 = vconst(0x00C000C0u); c.e3 = vconst(0x4C004C00u);
   c.m4 = vconst(0x03000300u); c.e4 = vconst(0x44004400u);
-  c.m3b = c.m3; c.mhi = vconst(0x01000100u); c.e3b = c.e3;
+  c.mh[0] = vconst(0x00400040u); c.eh[0] = c.e2;                  // 2^6 (1 + m / 1024)
+  c.mh[1] = vconst(0x00800080u); c.eh[1] = vconst(0x50005000u);   // 2^5
+  c.mh[2] = vconst(0x01000100u); c.eh[2] = c.e3;                  // 2^4
+  c.mh[3] = vconst(0x02000200u); c.eh[3] = vconst(0x48004800u);   // 2^3
   return c;
 }
 
@@ -135,44 +143,32 @@ __device__ __forceinline__ float vbase2(int k) {
   return (k == 4 || k == 7) ? 4.0f : ((k == 1 || k == 3 || k == 6) ? 16.0f : 64.0f);
 }
 
-template <int K>
-__device__ __forceinline__ unsigned shift_to3(unsigned w) {
-  if constexpr (K == 3) return w;
-  else if constexpr (K < 3) return w << (2 * (3 - K));
-  else return w >> (2 * (K - 3));
-}
-
-// 3-bit: low 2 bits at mantissa 6..7, the third bit at mantissa 8, exponent 2^4 -> 16 + c.
-template <int K>
-__device__ __forceinline__ unsigned v_pair3(unsigned w, unsigned hi, const VConst &c) {
-  return (shift_to3<K>(w) & c.m3b) | ((hi >> K) & c.mhi) | c.e3b;
-}
-
-// B operand of PV instruction iota (pairs 4*iota .. 4*iota+3) from one value word.
-template <int BV>
-__device__ __forceinline__ f16x8 v_operand(unsigned w, unsigned hi, int iota, const VConst &c) {
+// B operand of PV instruction iota (pairs 4*iota .. 4*iota+3) from one value word,
+// the 2-bit codes (or the low two bits of 3-bit codes).
+__device__ __forceinline__ f16x8 v_operand2(unsigned w, int iota, const VConst &c) {
   u32x4 r;
-  if constexpr (BV == 2) {
-    if (iota == 0) {
-      const unsigned w4 = w << 4;
-      r[0] = and_or(w4, c.m2, c.e2);   // pair 0
-      r[1] = and_or(w4, c.m3, c.e3);   // pair 1
-      r[2] = and_or(w, c.m2, c.e2);    // pair 2
-      r[3] = and_or(w, c.m3, c.e3);    // pair 3
-    } else {
-      const unsigned w6 = w >> 6;
-      r[0] = and_or(w, c.m4, c.e4);    // pair 4
-      r[1] = and_or(w6, c.m2, c.e2);   // pair 5
-      r[2] = and_or(w6, c.m3, c.e3);   // pair 6
-      r[3] = and_or(w6, c.m4, c.e4);   // pair 7
-    }
+  if (iota == 0) {
+    const unsigned w4 = w << 4;
+    r[0] = and_or(w4, c.m2, c.e2);   // pair 0
+    r[1] = and_or(w4, c.m3, c.e3);   // pair 1
+    r[2] = and_or(w, c.m2, c.e2);    // pair 2
+    r[3] = and_or(w, c.m3, c.e3);    // pair 3
   } else {
-    if (iota == 0) {
-      r[0] = v_pair3<0>(w, hi, c); r[1] = v_pair3<1>(w, hi, c); r[2] = v_pair3<2>(w, hi, c); r[3] = v_pair3<3>(w, hi, c);
-    } else {
-      r[0] = v_pair3<4>(w, hi, c); r[1] = v_pair3<5>(w, hi, c); r[2] = v_pair3<6>(w, hi, c); r[3] = v_pair3<7>(w, hi, c);
-    }
+    const unsigned w6 = w >> 6;
+    r[0] = and_or(w, c.m4, c.e4);    // pair 4
+    r[1] = and_or(w6, c.m2, c.e2);   // pair 5
+    r[2] = and_or(w6, c.m3, c.e3);   // pair 6
+    r[3] = and_or(w6, c.m4, c.e4);   // pair 7
   }
+  return __builtin_bit_cast(f16x8, r);
+}
+
+// The same for the third bits, x = the word's sixteen third bits with pair k at (k, 16 + k).
+__device__ __forceinline__ f16x8 v_operand_hi(unsigned x, int iota, const VConst &c) {
+  const unsigned xs = iota == 0 ? x << 6 : x << 2;
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = and_or(xs, c.mh[i], c.eh[i]);
   return __builtin_bit_cast(f16x8, r);
 }
 
@@ -484,7 +480,10 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   // BASE of the value operand for token 16 T + t16: pair 2 T + (t16 & 3) / 2 of its word
   float vbase[4];
 #pragma unroll
-  for (int T = 0; T < 4; ++T) vbase[T] = BV == 2 ? vbase2(2 * T + ((t16 & 3) >> 1)) : 16.0f;
+  for (int T = 0; T < 4; ++T) {
+    const int k = 2 * T + ((t16 & 3) >> 1);
+    vbase[T] = vbase2(k) + (BV == 3 ? (float)(64 >> (k & 3)) : 0.0f);
+  }
   // PV A rows: row r < G is head r's W hi part, G <= r < 2 G head r - G's lo part (the
   // two halves of one word of the W buffer), zeros past 2 G
   const int ar = lane & 15;
@@ -642,18 +641,13 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
     // r = head, K-slots 8 c .. 8 c + 7 = tokens 16 a + 4 c + e of those tiles
     const u32x4 vw0 = *(const u32x4 *)(st + S::V + 16 * lane);
     const u32x4 vw1 = *(const u32x4 *)(st + S::V + 1024 + 16 * lane);
-    u32x4 vh = (u32x4){0u, 0u, 0u, 0u};
-    if constexpr (BV == 3) vh = *(const u32x4 *)(st + S::VH + 16 * lane);
     const unsigned vws[8] = {vw0[0], vw0[1], vw0[2], vw0[3], vw1[0], vw1[1], vw1[2], vw1[3]};
-    unsigned hws[8];
+    unsigned hx[8];
+    if constexpr (BV == 3) {
+      const u32x4 vh = *(const u32x4 *)(st + S::VH + 16 * lane);
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      if constexpr (BV == 3) {
-        const unsigned h16 = (vh[ct >> 1] >> (16 * (ct & 1))) & 0xFFFFu;
-        hws[ct] = ((h16 & 0xFFu) << 8) | ((h16 & 0xFF00u) << 16);
-      } else {
-        hws[ct] = 0u;
-      }
+      for (int ct = 0; ct < 8; ++ct)
+        hx[ct] = __builtin_amdgcn_perm(0u, vh[ct >> 1], (ct & 1) ? 0x0C030C02u : 0x0C010C00u);
     }
 #pragma unroll
     for (int iota = 0; iota < 2; ++iota) {
@@ -666,9 +660,16 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
       for (int ct0 = 0; ct0 < 8; ct0 += 4) {
         f16x8 Bv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) Bv[c] = v_operand<BV>(vws[ct0 + c], hws[ct0 + c], iota, vc);
+        for (int c = 0; c < 4; ++c) Bv[c] = v_operand2(vws[ct0 + c], iota, vc);
 #pragma unroll
         for (int c = 0; c < 4; ++c) O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aw, Bv[c], O[ct0 + c], 0, 0, 0);
+        if constexpr (BV == 3) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) Bv[c] = v_operand_hi(hx[ct0 + c], iota, vc);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aw, Bv[c], O[ct0 + c], 0, 0, 0);
+        }
       }
     }
     __builtin_amdgcn_wave_barrier();
