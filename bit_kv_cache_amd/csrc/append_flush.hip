@@ -59,9 +59,9 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
 // Workgroup of 4 waves; it stages T_K of its KV head in LDS once and then walks
 // steps of 128 body tokens (two 64-token V sets).  In a step, wave w holds 32
 // tokens as two 16-token tiles.  Lane (q, tok) = (lane / 16, lane % 16) owns
-// channels [CPL*q, CPL*q + CPL) of token tok of each tile, CPL = D / 4, so a
-// token's row sits in the 4 lanes tok, tok+16, tok+32, tok+48 and every per-token
-// reduction is two cross-row exchanges.
+// CPL = D / 4 channels of token tok of each tile (eight-channel chunks q, q + 4, ...
+// of the row), so a token's row sits in the 4 lanes tok, tok+16, tok+32, tok+48 and
+// every per-token reduction is two cross-row exchanges.
 //   keys:   x = T_K k16 on v_mfma_f32_16x16x32_f16 with A = T_K rows (LDS) and
 //           B = the lane's own fp16 channels, so the result D[out channel][token]
 //           lands with lane (q, tok) holding out channels 16*ct + 4*q + i of tok;
@@ -93,6 +93,9 @@ struct FlushSmem {
 };
 
 // Raw bytes of one lane's CPL channels of one token row, in the input's element size.
+// Channel of position k of lane group q's list.
+__device__ __forceinline__ int seg_chan(int q, int k) { return 32 * (k >> 3) + 8 * q + (k & 7); }
+
 template <int ES, int CPL>
 struct RawSeg {
   u32x4 r[CPL * ES / 16];
@@ -104,27 +107,29 @@ __device__ __forceinline__ unsigned raw_word(const RawSeg<ES, CPL> &s, int i) {
 }
 
 // Load the segment of body token u (valid) from the ring if it was appended by an
-// earlier call, else from the new input.  Returns true for a ring (fp16) row.
+// earlier call (an fp16 row), else from the new input; an invalid token reads zeros.
+// Lane group q holds channels 32 i + 8 q .. 32 i + 8 q + 7 (i = 0 .. D/32 - 1), at
+// position 8 i + e of its list: one load instruction then covers 32 contiguous
+// channels of each of its 16 rows.
 template <int D, int ES>
-__device__ __forceinline__ bool load_seg(const FlushArgs &a, const _Float16 *ring, const void *inp, int bg,
-                                         int b, int g, int64_t u, bool valid, int q, RawSeg<ES, D / 4> &s) {
+__device__ __forceinline__ void load_seg(const FlushArgs &a, const char *ring_h, const char *in_h, int64_t u, bool valid,
+                                         int q, RawSeg<ES, D / 4> &s) {
   constexpr int CPL = D / 4;
 #pragma unroll
   for (int i = 0; i < CPL * ES / 16; ++i) s.r[i] = (u32x4){0u, 0u, 0u, 0u};
-  if (!valid) return true;   // zeros read as fp16
-  const int64_t p = a.S + u;
-  if (p < a.n_before) {
-    const int64_t slot = (p - a.S) % (a.R + a.C);
-    const u32x4 *src = (const u32x4 *)((const char *)ring + (size_t)bg * a.ring_bytes + ((size_t)slot * D + CPL * q) * 2);
+  if (!valid) return;
+  if (a.S + u < a.n_before) {
+    const unsigned slot = (unsigned)u % (unsigned)(a.R + a.C);
+    const u32x4 *src = (const u32x4 *)(ring_h + (size_t)slot * (D * 2)) + q;
 #pragma unroll
-    for (int i = 0; i < CPL * 2 / 16; ++i) s.r[i] = src[i];
-    return true;
+    for (int i = 0; i < CPL / 8; ++i) s.r[i] = src[4 * i];
+    return;
   }
-  const size_t e0 = (((size_t)b * a.Hkv + g) * a.n_new + (size_t)(p - a.n_before)) * D + CPL * q;
-  const u32x4 *src = (const u32x4 *)((const char *)inp + e0 * ES);
+  const u32x4 *src = (const u32x4 *)(in_h + (size_t)(a.S + u - a.n_before) * (D * ES)) + (ES / 2) * q;
 #pragma unroll
-  for (int i = 0; i < CPL * ES / 16; ++i) s.r[i] = __builtin_nontemporal_load(src + i);
-  return false;
+  for (int i = 0; i < CPL / 8; ++i)
+#pragma unroll
+    for (int h = 0; h < ES / 2; ++h) s.r[(ES / 2) * i + h] = __builtin_nontemporal_load(src + 2 * ES * i + h);
 }
 
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
@@ -267,80 +272,62 @@ __device__ __forceinline__ int exact_code(double x, float sc, float zp, int quan
   return (int)fmin(fmax(t, 0.0), (double)(L - 1));
 }
 
-// Quantizer of one row.  QuEST: t = x/step + L/2, code floor(t).  Affine: t = (x - z)/s,
-// code rint(t) (half to even).  Codes are clamped to [0, L-1].  The boundary test
-// tracks, over the row, the smallest and largest fraction t - floor(t) (QuEST) or
-// the largest |t - rint(t)| (affine); a zero step / scale gives the degenerate code
-// (L/2, resp. 0) and no boundary.
+// Quantizer of one row.  QuEST: code floor(x/step + L/2).  Affine: code
+// rint((x - z)/s), half to even.  Codes are clamped to [0, L-1].  Both are taken as
+// floor(v) of v = x/step + L/2 + tol, resp. (x - z)/s + 1/2 + tol: that equals the
+// code unless the unshifted value lies within tol (bins) of a decision boundary,
+// which is exactly when frac(v) < 2 tol.  The row keeps the smallest frac(v); rows
+// that reach the band are decided again in fp64.  A zero step / scale gives the
+// degenerate code (L/2, resp. 0) and no boundary.
 template <bool QU>
 struct Quant {
-  float inv, add, top;
+  float inv, add, z, top, band;
 };
 
 template <bool QU>
-__device__ __forceinline__ Quant<QU> make_quant(float sc, float zp, int L) {
+__device__ __forceinline__ Quant<QU> make_quant(float sc, float zp, int L, float tol) {
   Quant<QU> q;
   q.inv = sc != 0.f ? 1.0f / sc : 0.f;
-  q.add = QU ? (float)(L / 2) : zp;
+  q.add = (QU ? (float)(L / 2) : 0.5f) + tol;
+  q.z = zp;
   q.top = (float)(L - 1);
+  q.band = 2.0f * tol;
   return q;
 }
 
-struct Edge {
-  float lo, hi;
-};
-
-__device__ __forceinline__ Edge edge_init() { return Edge{1.0f, 0.0f}; }
-
 template <bool QU>
 __device__ __forceinline__ float scaled(const Quant<QU> &q, float x) {
-  return QU ? fmaf(x, q.inv, q.add) : (x - q.add) * q.inv;
+  return QU ? fmaf(x, q.inv, q.add) : fmaf(x - q.z, q.inv, q.add);
 }
 
-// Codes of two values; the fraction extrema of both enter the edge in one
-// three-operand min / max.
+// Codes of two values; their fractions enter the row's minimum in one min3.
 template <bool QU>
-__device__ __forceinline__ void code2(const Quant<QU> &q, float x0, float x1, Edge &e, float &c0, float &c1) {
-  const float t0 = scaled(q, x0), t1 = scaled(q, x1);
-  if constexpr (QU) {
-    const float f0 = floorf(t0), f1 = floorf(t1);
-    const float r0 = t0 - f0, r1 = t1 - f1;
-    e.lo = fminf(e.lo, fminf(r0, r1));
-    e.hi = fmaxf(e.hi, fmaxf(r0, r1));
-    c0 = f0; c1 = f1;
-  } else {
-    const float f0 = rintf(t0), f1 = rintf(t1);
-    e.hi = fmaxf(e.hi, fmaxf(fabsf(t0 - f0), fabsf(t1 - f1)));
-    c0 = f0; c1 = f1;
-  }
-  c0 = __builtin_amdgcn_fmed3f(c0, 0.f, q.top);
-  c1 = __builtin_amdgcn_fmed3f(c1, 0.f, q.top);
+__device__ __forceinline__ void code2(const Quant<QU> &q, float x0, float x1, float &e, float &c0, float &c1) {
+  const float v0 = scaled(q, x0), v1 = scaled(q, x1);
+  const float f0 = floorf(v0), f1 = floorf(v1);
+  e = fminf(fminf(e, v0 - f0), v1 - f1);
+  c0 = __builtin_amdgcn_fmed3f(f0, 0.f, q.top);
+  c1 = __builtin_amdgcn_fmed3f(f1, 0.f, q.top);
 }
 
 template <bool QU>
-__device__ __forceinline__ bool edge_near(const Quant<QU> &q, const Edge &e, float tol) {
-  if (q.inv == 0.f) return false;
-  return QU ? (e.lo < tol || e.hi > 1.0f - tol) : (e.hi > 0.5f - tol);
+__device__ __forceinline__ bool edge_near(const Quant<QU> &q, float e) {
+  return q.inv != 0.f && e < q.band;
 }
 
 // The same test for one value.
 template <bool QU>
-__device__ __forceinline__ bool value_near(const Quant<QU> &q, float x, float tol) {
-  const float t = scaled(q, x);
-  if constexpr (QU) {
-    const float r = t - floorf(t);
-    return r < tol || r > 1.0f - tol;
-  } else {
-    return fabsf(t - rintf(t)) > 0.5f - tol;
-  }
+__device__ __forceinline__ bool value_near(const Quant<QU> &q, float x) {
+  const float v = scaled(q, x);
+  return v - floorf(v) < q.band;
 }
 
 // DPP quad permutations (gfx9 quad_perm): lane i of a quad reads lane i^2 / i^1.
 __device__ __forceinline__ unsigned quad_xor2(unsigned x) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
 }
 __device__ __forceinline__ unsigned quad_xor1(unsigned x) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true);
 }
 
 // 4 x 4 byte transpose across a quad: lane e holds bytes [x_e0..x_e3] in, lane r
@@ -392,19 +379,31 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const int64_t st0 = (int64_t)blockIdx.x * steps_per_wg;
   const int64_t st1 = st0 + steps_per_wg < nsteps ? st0 + steps_per_wg : nsteps;
 
+  // Each tile's raw rows are refilled with the next step's as soon as they have been
+  // converted, so every load has about a step of work to hide behind.
   RawSeg<ES, CPL> rk[2], rv[2];
-  bool kring[2], vring[2], valid[2];
-  auto issue_loads = [&](int64_t st) {
-    const int64_t ub = (s_first + 2 * st) * kSet + 32 * wave;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int64_t u = ub + 16 * tt + tok;
-      valid[tt] = u >= a.u0 && u < a.u1;
-      kring[tt] = load_seg<D, ES>(a, a.ring_k, a.k_new, bg, b, g, u, valid[tt], q, rk[tt]);
-      vring[tt] = load_seg<D, ES>(a, a.ring_v, a.v_new, bg, b, g, u, valid[tt], q, rv[tt]);
-    }
+  auto tok_of = [&](int64_t st, int tt) { return (s_first + 2 * st) * kSet + 32 * wave + 16 * tt + tok; };
+  auto tok_valid = [&](int64_t u) { return u >= a.u0 && u < a.u1; };
+  // rows of earlier calls come from the ring (fp16); invalid rows read as fp16 zeros
+  auto tok_ring = [&](int64_t u) { return !tok_valid(u) || a.S + u < a.n_before; };
+  // this KV head's ring and input rows
+  const char *ring_kh = (const char *)a.ring_k + (size_t)bg * a.ring_bytes;
+  const char *ring_vh = (const char *)a.ring_v + (size_t)bg * a.ring_bytes;
+  const size_t in_off = (size_t)bg * (size_t)a.n_new * (D * ES);
+  const char *in_kh = (const char *)a.k_new + in_off;
+  const char *in_vh = (const char *)a.v_new + in_off;
+  auto load_k = [&](int64_t st, int tt) {
+    const int64_t u = tok_of(st, tt);
+    load_seg<D, ES>(a, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
   };
-  if (st0 < st1) issue_loads(st0);   // in flight while T_K is staged
+  auto load_v = [&](int64_t st, int tt) {
+    const int64_t u = tok_of(st, tt);
+    load_seg<D, ES>(a, ring_vh, in_vh, u, tok_valid(u), q, rv[tt]);
+  };
+  if (st0 < st1) {   // in flight while T_K is staged
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) { load_k(st0, tt); load_v(st0, tt); }
+  }
   {
     const _Float16 *T = a.tk + (size_t)g * D * D;
     for (int i = tid; i < D * D / 8; i += kThreads) {
@@ -424,21 +423,25 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     // ---- keys, one tile at a time: x = T_K k16 on MFMA, parameters, codes
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
+      const int64_t u = ubase + 16 * tt + tok;
+      const bool vt = tok_valid(u);
       unsigned kh[CPL / 2];
-      seg_half2<ES, CPL>(rk[tt], kring[tt], a.in_dtype, kh);
+      seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
+      if (st + 1 < st1) load_k(st + 1, tt);
+      // K-steps outer, tiles inner: NCT independent accumulation chains
       f32x4 acc[NCT];
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int ct = 0; ct < NCT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const half8 A = *(const half8 *)&sm.t[16 * ct + tok][CPL * q + 8 * s];
-          const u32x4 bw = {kh[4 * s], kh[4 * s + 1], kh[4 * s + 2], kh[4 * s + 3]};
+      for (int s = 0; s < KS; ++s) {
+        const u32x4 bw = {kh[4 * s], kh[4 * s + 1], kh[4 * s + 2], kh[4 * s + 3]};
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const half8 A = *(const half8 *)&sm.t[16 * ct + tok][32 * s + 8 * q];
           acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8, bw), acc[ct], 0, 0, 0);
         }
       }
       const int row = 32 * wave + 16 * tt + tok;
-      const int64_t u = ubase + 16 * tt + tok;
       auto key_tile = [&](auto tag) {
         constexpr bool QU = decltype(tag)::value;
         float sc, zp = 0.f;
@@ -465,13 +468,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         } else {
           sc = 0.f;
         }
-        if (q == 0 && valid[tt]) {
+        if (q == 0 && vt) {
           _Float16 *pk = (_Float16 *)((char *)a.par_k + (size_t)bg * a.kpar_bytes) + u * a.kpar_n;
           if constexpr (QU) pk[0] = (_Float16)sc;
           else *(unsigned *)pk = pack_f16(sc, zp);
         }
-        const Quant<QU> qk = make_quant<QU>(sc, zp, Lk);
-        Edge e = edge_init();
+        const Quant<QU> qk = make_quant<QU>(sc, zp, Lk, kEdgeK);
+        float e = 1.0f;
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           float c0, c1, c2, c3;
@@ -485,7 +488,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         }
         // elements near a boundary: the 4 lanes of a token take one candidate at a
         // time, each summing its CPL channels' exact products in fp64
-        const bool kn = valid[tt] && edge_near(qk, e, kEdgeK);
+        const bool kn = vt && edge_near(qk, e);
         if (__any(kn)) {
           unsigned m = 0;
           if (kn) {
@@ -493,7 +496,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
               for (int i = 0; i < 4; ++i)
-                if (value_near(qk, acc[ct][i], kEdgeK)) m |= 1u << (4 * ct + i);
+                if (value_near(qk, acc[ct][i])) m |= 1u << (4 * ct + i);
           }
           while (__any(m != 0)) {
             const unsigned m0 = __shfl(m, tok), m1 = __shfl(m, 16 + tok), m2 = __shfl(m, 32 + tok), m3 = __shfl(m, 48 + tok);
@@ -504,7 +507,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             double part = 0.0;
 #pragma unroll
             for (int s = 0; s < CPL / 8; ++s) {
-              const half8 tv = *(const half8 *)&sm.t[j][CPL * q + 8 * s];
+              const half8 tv = *(const half8 *)&sm.t[j][32 * s + 8 * q];
 #pragma unroll
               for (int e8 = 0; e8 < 8; ++e8) {
                 const unsigned w = kh[4 * s + e8 / 2];
@@ -528,9 +531,11 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     // ---- values
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      float xv[CPL];
-      seg_float<ES, CPL>(rv[tt], vring[tt], a.in_dtype, xv);
       const int64_t u = ubase + 16 * tt + tok;
+      const bool vt = tok_valid(u);
+      float xv[CPL];
+      seg_float<ES, CPL>(rv[tt], tok_ring(u), a.in_dtype, xv);
+      if (st + 1 < st1) load_v(st + 1, tt);
       const int s2 = wave >> 1;                       // set of this wave within the step
       const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
       auto value_tile = [&](auto tag) {
@@ -555,13 +560,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         } else {
           sc = 0.f;
         }
-        if (q == 0 && valid[tt]) {
+        if (q == 0 && vt) {
           _Float16 *pv = (_Float16 *)((char *)a.par_v + (size_t)bg * a.vpar_bytes) + u * a.vpar_n;
           if constexpr (QU) pv[0] = (_Float16)sc;
           else *(unsigned *)pv = pack_f16(sc, zp);
         }
-        const Quant<QU> qv = make_quant<QU>(sc, zp, Lv);
-        Edge e = edge_init();
+        const Quant<QU> qv = make_quant<QU>(sc, zp, Lv, kEdgeV);
+        float e = 1.0f;
 #pragma unroll
         for (int g4 = 0; g4 < CPL / 4; ++g4) {
           float c0, c1, c2, c3;
@@ -573,15 +578,15 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           w = __builtin_amdgcn_cvt_pk_u8_f32(c3, 3, w);
           // lane tok = 4c + e now gets channel 4*g4 + e of tokens 4c .. 4c+3
           w = quad_transpose(w, selA, selB);
-          *(unsigned *)&sm.vc[s2][CPL * q + 4 * g4 + (tok & 3)][col + 4 * (tok >> 2)] = w;
+          *(unsigned *)&sm.vc[s2][seg_chan(q, 4 * g4 + (tok & 3))][col + 4 * (tok >> 2)] = w;
         }
-        const bool vn = valid[tt] && edge_near(qv, e, kEdgeV);
+        const bool vn = vt && edge_near(qv, e);
         if (__any(vn)) {
           if (vn) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
-              if (value_near(qv, xv[k], kEdgeV))
-                sm.vc[s2][CPL * q + k][col + tok] =
+              if (value_near(qv, xv[k]))
+                sm.vc[s2][seg_chan(q, k)][col + tok] =
                     (uint8_t)exact_code((double)xv[k], sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lv);
           }
         }
@@ -590,112 +595,130 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       else value_tile(AffineTag{});
     }
     __syncthreads();
-    // the next step's rows load while this step's codes are packed and stored
-    if (st + 1 < st1) issue_loads(st + 1);
-    // ---- K rows: two threads per token, D/2 channels each
-    {
+    // ---- K rows: two threads per token, D/2 channels each (the bit width is a
+    // template argument so only its own packing is issued)
+    auto pack_k_rows = [&](auto bits_tag) {
+      constexpr int BK = decltype(bits_tag)::value;
       const int r = tid >> 1, h = tid & 1;
       const int64_t u = set0 * kSet + r;
-      if (u >= a.u0 && u < a.u1) {
-        constexpr int HC = D / 2;
-        uint8_t *rowp = a.codes_k + (size_t)bg * a.kcode_bytes + (size_t)u * a.kcode_row;
-        u32x4 cw[HC / 16];
+      if (u < a.u0 || u >= a.u1) return;
+      constexpr int HC = D / 2;
+      uint8_t *rowp = a.codes_k + (size_t)bg * a.kcode_bytes + (size_t)u * a.kcode_row;
+      u32x4 cw[HC / 16];
 #pragma unroll
-        for (int i = 0; i < HC / 16; ++i) cw[i] = *(const u32x4 *)&sm.kc[r][HC * h + 16 * i];
-        unsigned p0[HC / 16];
+      for (int i = 0; i < HC / 16; ++i) cw[i] = *(const u32x4 *)&sm.kc[r][HC * h + 16 * i];
+      unsigned p0[HC / 16];
+#pragma unroll
+      for (int k = 0; k < HC / 16; ++k)
+        p0[k] = kpack2(cw[k][0]) | (kpack2(cw[k][1]) << 8) | (kpack2(cw[k][2]) << 16) | (kpack2(cw[k][3]) << 24);
+      if constexpr (HC / 16 == 4) *(u32x4 *)(rowp + 16 * h) = (u32x4){p0[0], p0[1], p0[2], p0[3]};
+      else *(u32x2 *)(rowp + 8 * h) = (u32x2){p0[0], p0[1]};
+      if constexpr (BK == 3) {
+        unsigned p1[HC / 32];
+#pragma unroll
+        for (int k = 0; k < HC / 32; ++k) {
+          unsigned w = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w |= kpack1(cw[2 * k + e / 4][e % 4]) << (4 * e);
+          p1[k] = w;
+        }
+        if constexpr (HC / 32 == 2) *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p1[0], p1[1]};
+        else *(unsigned *)(rowp + D / 4 + 4 * h) = p1[0];
+      } else if constexpr (BK == 4) {
 #pragma unroll
         for (int k = 0; k < HC / 16; ++k)
-          p0[k] = kpack2(cw[k][0]) | (kpack2(cw[k][1]) << 8) | (kpack2(cw[k][2]) << 16) | (kpack2(cw[k][3]) << 24);
-        if constexpr (HC / 16 == 4) *(u32x4 *)(rowp + 16 * h) = (u32x4){p0[0], p0[1], p0[2], p0[3]};
-        else *(u32x2 *)(rowp + 8 * h) = (u32x2){p0[0], p0[1]};
-        if (a.bits_k == 3) {
-          unsigned p1[HC / 32];
+          p0[k] = kpack2(cw[k][0] >> 2) | (kpack2(cw[k][1] >> 2) << 8) | (kpack2(cw[k][2] >> 2) << 16) |
+                  (kpack2(cw[k][3] >> 2) << 24);
+        if constexpr (HC / 16 == 4) *(u32x4 *)(rowp + D / 4 + 16 * h) = (u32x4){p0[0], p0[1], p0[2], p0[3]};
+        else *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p0[0], p0[1]};
+      }
+    };
+    using B2 = std::integral_constant<int, 2>;
+    using B3 = std::integral_constant<int, 3>;
+    using B4 = std::integral_constant<int, 4>;
+    if (a.bits_k == 2) pack_k_rows(B2{});
+    else if (a.bits_k == 3) pack_k_rows(B3{});
+    else pack_k_rows(B4{});
+
+    // ---- V set words: 128 threads per set, 4 consecutive words each.  A set only
+    // partly covered by this call keeps its other tokens' fields.
+    constexpr int NT = D / 16, NW = 64 * NT;
+    const int s2 = tid >> 7, t128 = tid & 127;
+    const int64_t sidx = set0 + s2;
+    const int64_t vbase = sidx * kSet;
+    const int64_t vlo = a.u0 > vbase ? a.u0 : vbase;
+    const int64_t vhi = a.u1 < vbase + kSet ? a.u1 : vbase + kSet;
+    auto pack_v_words = [&](auto bits_tag, auto full_tag) {
+      constexpr int BVV = decltype(bits_tag)::value;
+      constexpr bool FULL = decltype(full_tag)::value;
+      const int r0 = (int)(vlo - vbase), r1 = (int)(vhi - vbase);
+      uint8_t *vb = a.codes_v + (size_t)bg * a.vcode_bytes + (size_t)sidx * a.vset_bytes;
+      unsigned w0[4], w1[4], k0[4], k1[4];
 #pragma unroll
-          for (int k = 0; k < HC / 32; ++k) {
-            unsigned w = 0;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int wi = 4 * t128 + jj;
+        const int ln = wi / NT, t = wi % NT;
+        const int c = ln >> 4, j = 16 * t + (ln & 15);
+        w0[jj] = w1[jj] = k0[jj] = k1[jj] = 0u;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) w |= kpack1(cw[2 * k + e / 4][e % 4]) << (4 * e);
-            p1[k] = w;
+        for (int aa = 0; aa < 4; ++aa) {
+          const unsigned x = *(const unsigned *)&sm.vc[s2][j][16 * aa + 4 * c];
+          w0[jj] |= vfield2(x) << (4 * aa);
+          if constexpr (BVV == 3) w1[jj] |= vfield1(x) << (2 * aa);
+          if constexpr (BVV == 4) w1[jj] |= vfield2(x >> 2) << (4 * aa);
+          if constexpr (!FULL) {
+            unsigned vm = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int rr = 16 * aa + 4 * c + e;
+              if (rr >= r0 && rr < r1) vm |= 0x0Fu << (8 * e);
+            }
+            k0[jj] |= vfield2(vm) << (4 * aa);
+            if constexpr (BVV == 3) k1[jj] |= vfield1(vm) << (2 * aa);
+            if constexpr (BVV == 4) k1[jj] |= vfield2(vm >> 2) << (4 * aa);
           }
-          if constexpr (HC / 32 == 2) *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p1[0], p1[1]};
-          else *(unsigned *)(rowp + D / 4 + 4 * h) = p1[0];
-        } else if (a.bits_k == 4) {
-#pragma unroll
-          for (int k = 0; k < HC / 16; ++k)
-            p0[k] = kpack2(cw[k][0] >> 2) | (kpack2(cw[k][1] >> 2) << 8) | (kpack2(cw[k][2] >> 2) << 16) |
-                    (kpack2(cw[k][3] >> 2) << 24);
-          if constexpr (HC / 16 == 4) *(u32x4 *)(rowp + D / 4 + 16 * h) = (u32x4){p0[0], p0[1], p0[2], p0[3]};
-          else *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p0[0], p0[1]};
         }
       }
-    }
-
-    // ---- V set words: 128 threads per set, 4 consecutive words each
-    {
-      constexpr int NT = D / 16, NW = 64 * NT;
-      const int s2 = tid >> 7, t128 = tid & 127;
-      const int64_t sidx = set0 + s2;
-      const int64_t base = sidx * kSet;
-      const int64_t lo = a.u0 > base ? a.u0 : base;
-      const int64_t hi = a.u1 < base + kSet ? a.u1 : base + kSet;
-      if (lo < hi && 4 * t128 < NW) {
-        const int r0 = (int)(lo - base), r1 = (int)(hi - base);
-        const bool full = r0 == 0 && r1 == kSet;
-        uint8_t *vb = a.codes_v + (size_t)bg * a.vcode_bytes + (size_t)sidx * a.vset_bytes;
-        unsigned w0[4], w1[4], k0[4], k1[4];
+      u32x4 *p0 = (u32x4 *)(vb + 16 * t128);
+      if constexpr (FULL) {
+        *p0 = (u32x4){w0[0], w0[1], w0[2], w0[3]};
+      } else {
+        u32x4 old = *p0;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int wi = 4 * t128 + jj;
-          const int ln = wi / NT, t = wi % NT;
-          const int c = ln >> 4, j = 16 * t + (ln & 15);
-          w0[jj] = w1[jj] = k0[jj] = k1[jj] = 0u;
-#pragma unroll
-          for (int aa = 0; aa < 4; ++aa) {
-            const unsigned x = *(const unsigned *)&sm.vc[s2][j][16 * aa + 4 * c];
-            w0[jj] |= vfield2(x) << (4 * aa);
-            if (a.bits_v == 3) w1[jj] |= vfield1(x) << (2 * aa);
-            if (a.bits_v == 4) w1[jj] |= vfield2(x >> 2) << (4 * aa);
-            if (!full) {
-              unsigned vm = 0;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int r = 16 * aa + 4 * c + e;
-                if (r >= r0 && r < r1) vm |= 0x0Fu << (8 * e);
-              }
-              k0[jj] |= vfield2(vm) << (4 * aa);
-              if (a.bits_v == 3) k1[jj] |= vfield1(vm) << (2 * aa);
-              if (a.bits_v == 4) k1[jj] |= vfield2(vm >> 2) << (4 * aa);
-            }
-          }
+        for (int jj = 0; jj < 4; ++jj) old[jj] = (old[jj] & ~k0[jj]) | (w0[jj] & k0[jj]);
+        *p0 = old;
+      }
+      if constexpr (BVV == 3) {
+        u32x2 *p1 = (u32x2 *)(vb + 4 * NW + 8 * t128);
+        u32x2 nw = {w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16)};
+        if constexpr (!FULL) {
+          const u32x2 mk = {k1[0] | (k1[1] << 16), k1[2] | (k1[3] << 16)};
+          const u32x2 old = *p1;
+          nw = (old & ~mk) | (nw & mk);
         }
-        u32x4 *p0 = (u32x4 *)(vb + 16 * t128);
-        if (full) {
-          *p0 = (u32x4){w0[0], w0[1], w0[2], w0[3]};
-        } else {
-          u32x4 old = *p0;
+        *p1 = nw;
+      } else if constexpr (BVV == 4) {
+        u32x4 *p1 = (u32x4 *)(vb + 4 * NW + 16 * t128);
+        u32x4 nw = {w1[0], w1[1], w1[2], w1[3]};
+        if constexpr (!FULL) {
+          const u32x4 old = *p1;
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) old[jj] = (old[jj] & ~k0[jj]) | (w0[jj] & k0[jj]);
-          *p0 = old;
+          for (int jj = 0; jj < 4; ++jj) nw[jj] = (old[jj] & ~k1[jj]) | (nw[jj] & k1[jj]);
         }
-        if (a.bits_v == 3) {
-          u32x2 *p1 = (u32x2 *)(vb + 4 * NW + 8 * t128);
-          u32x2 nw = {w1[0] | (w1[1] << 16), w1[2] | (w1[3] << 16)};
-          if (!full) {
-            const u32x2 mk = {k1[0] | (k1[1] << 16), k1[2] | (k1[3] << 16)};
-            const u32x2 old = *p1;
-            nw = (old & ~mk) | (nw & mk);
-          }
-          *p1 = nw;
-        } else if (a.bits_v == 4) {
-          u32x4 *p1 = (u32x4 *)(vb + 4 * NW + 16 * t128);
-          u32x4 nw = {w1[0], w1[1], w1[2], w1[3]};
-          if (!full) {
-            const u32x4 old = *p1;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) nw[jj] = (old[jj] & ~k1[jj]) | (nw[jj] & k1[jj]);
-          }
-          *p1 = nw;
-        }
+        *p1 = nw;
+      }
+    };
+    if (vlo < vhi && 4 * t128 < NW) {
+      using Full = std::integral_constant<bool, true>;
+      using Part = std::integral_constant<bool, false>;
+      if (vlo == vbase && vhi == vbase + kSet) {
+        if (a.bits_v == 2) pack_v_words(B2{}, Full{});
+        else if (a.bits_v == 3) pack_v_words(B3{}, Full{});
+        else pack_v_words(B4{}, Full{});
+      } else {
+        if (a.bits_v == 2) pack_v_words(B2{}, Part{});
+        else if (a.bits_v == 3) pack_v_words(B3{}, Part{});
+        else pack_v_words(B4{}, Part{});
       }
     }
     __syncthreads();
