@@ -6,9 +6,12 @@ affine K and V, sink 64 / recent 256 / chunk 16): append one token to every
 sequence (flushing 16 tokens every 16th step), then GQA decode attention over the
 whole cache with the query transform folded into its prologue.  The headline value is decode
 attention GB/s: algorithmic bytes the decode must move (codes, parameters, FP16
-windows, q, q~, out) per step over the step time.  A second leg times the bulk
-prefill flush (36 layers x 8 KV heads x 65536 tokens) at 2, 3 and 4 bits, and a
-third times the CPU oracle on a bounded sample of the decode step.
+windows, q, q~, out) per step over the step time.  Before the warm-up steps the
+decode is launched untimed for a fraction of a second so that the timed steps run at
+the chip's steady clocks.  Further legs time the bulk prefill flush (36 layers x 8 KV
+heads x 65536 tokens) at 2, 3 and 4 bits, the long-context decode (8 sequences of
+131072 tokens, 64 query / 8 KV heads, 2-bit K / 3-bit V), and the CPU oracle on a
+bounded sample of the decode step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-flush] [--no-cpu]
 """
@@ -66,9 +69,9 @@ def flush_bytes(w, bits, n):
     return heads * (read + write) + w.num_kv_heads * d * d * 2
 
 
-def traffic_from_profile(name):
-    """Measured HBM bytes per launch from a committed counter summary, if it was
-    taken on the current kernel sources."""
+def traffic_from_profile(name, kernels):
+    """Measured HBM bytes per launch of `kernels` (summed) from a committed counter
+    summary, if it was taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", name)
     try:
         rec = json.load(open(p))
@@ -76,8 +79,10 @@ def traffic_from_profile(name):
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    # the decode call: partials kernel + merge kernel
-    return rec.get("bytes_per_launch", 0) + rec.get("merge_bytes_per_launch", 0)
+    try:
+        return sum(rec["kernels"][k]["bytes_per_dispatch"] for k in kernels)
+    except KeyError:
+        return None
 
 
 def run_decode_leg(args):
@@ -89,7 +94,7 @@ def run_decode_leg(args):
     w = configs.SERVING
     dev = "cuda"
     n0 = w.context
-    n_breakdown = 20
+    n_breakdown = args.steps
     total = n0 + args.warmup + args.steps + n_breakdown
     log(f"[bench] decode workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} n={n0}")
     k, v = gen.kv_tensors(w, 0, total, dev)
@@ -122,6 +127,18 @@ def run_decode_leg(args):
         if ev is not None:
             ev[2].record()
 
+    # Settle: after idle the chip runs the first few dozen decodes fast, then slower for
+    # ~150 launches while its power management adjusts, then steadily.  Decode-only
+    # launches (the cache does not grow) for at least settle_s seconds before the
+    # warm-up steps put the timed region in the steady state.
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while n_settle < 300 or time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(50):
+            W.decode_attention_fused(cache, qs[n_settle % nsteps], tinvt, num_splits=P, workspace=ws, out=out, q_t=qt)
+        n_settle += 50
+        torch.cuda.synchronize()
+    log(f"[bench] settle: {n_settle} decode launches in {time.perf_counter() - t_settle:.2f} s")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -135,38 +152,22 @@ def run_decode_leg(args):
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     nbytes = sum(decode_bytes(w, n_start + j + 1) for j in range(args.steps)) / args.steps
-    # breakdown of a step, from further (untimed) steps with events between the calls
+    # The same K steps once more with HIP events (on the library's stream, torch's
+    # current one) around each call: the decode kernel's average launch duration for
+    # the roofline figure, and the step's breakdown.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_breakdown)]
+    n_ev = cache.n
     for j in range(n_breakdown):
         step(args.warmup + args.steps + j, evs[j])
     torch.cuda.synchronize()
     app = sum(e[0].elapsed_time(e[1]) for e in evs) / n_breakdown
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n_breakdown
-    log(f"[bench] step {ms_step:.4f} ms; breakdown (event intervals): append {app:.4f}, "
-        f"decode with query transform {dec_ms:.4f} ms; decode bytes {nbytes / 1e6:.1f} MB")
-
-    # The decode kernel's own average launch duration, for the roofline figure: the
-    # same decode launched back to back on the stream, the host ahead of the GPU, so
-    # no launch gap of the step loop is counted.
-    q_last = qs[-1]
-    reps = 30
-    def dec():
-        W.decode_attention_fused(cache, q_last, tinvt, num_splits=P, workspace=ws, out=out, q_t=qt)
-    for _ in range(3):
-        dec()
-    torch.cuda.synchronize()
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for _ in range(reps):
-        dec()
-    k1.record()
-    torch.cuda.synchronize()
-    kern_ms = k0.elapsed_time(k1) / reps
-    kern_bytes = decode_bytes(w, cache.n)
-    log(f"[bench] decode kernel back to back: {kern_ms * 1e3:.1f} us per launch at n={cache.n} "
-        f"({kern_bytes / (kern_ms * 1e-3) / 1e9:.0f} GB/s)")
+    kern_bytes = sum(decode_bytes(w, n_ev + j + 1) for j in range(n_breakdown)) / n_breakdown
+    log(f"[bench] step {ms_step:.4f} ms; with events around each call: append {app:.4f}, "
+        f"decode with query transform {dec_ms:.4f} ms ({kern_bytes / (dec_ms * 1e-3) / 1e9:.0f} GB/s); "
+        f"decode bytes {nbytes / 1e6:.1f} MB")
     return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, app_ms=app, bytes=nbytes, splits=P,
-                n=n_start, cache=cache, kern_ms=kern_ms, kern_bytes=kern_bytes)
+                n=n_start, cache=cache, kern_ms=dec_ms, kern_bytes=kern_bytes)
 
 
 def run_flush_leg(args):
@@ -207,6 +208,103 @@ def run_flush_leg(args):
     del kv
     torch.cuda.empty_cache()
     return res
+
+
+def configs_name(attr):
+    from synth import configs
+    return getattr(configs, attr).name
+
+
+def run_long_leg(args):
+    """Decode calls on the long-context workload (8 sequences of 131072 tokens, 64 query /
+    8 KV heads, affine 2-bit K / 3-bit V), launched back to back: at 128 splits, the
+    configuration's own count, and at the count the library picks."""
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+
+    w = configs.LONG_CONTEXT
+    dev = "cuda"
+    n = w.context + 1
+    log(f"[bench] long-context workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} n={n}")
+    k, v = gen.kv_tensors(w, 0, n, dev)
+    t16, tinvt = gen.key_transforms(w, 0)
+    t16, tinvt = t16.to(dev), tinvt.to(dev)
+    spec = W.CacheSpec(batch=w.batch, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=n,
+                       sink=w.sink, recent=w.recent, chunk=w.chunk, bits_k=w.bits_k, bits_v=w.bits_v,
+                       quant_k=W.Q_AFFINE, quant_v=W.Q_AFFINE, pct_lo=w.pct_lo, pct_hi=w.pct_hi)
+    cache = W.KVCache(spec, dev)
+    W.append_flush(cache, k[:, :, :n - 1].contiguous(), v[:, :, :n - 1].contiguous(), t16)
+    W.append_flush(cache, k[:, :, n - 1:].contiguous(), v[:, :, n - 1:].contiguous(), t16)
+    del k, v
+    q = gen.queries(w, 0, 0, dev)
+    nbytes = decode_bytes(w, cache.n)
+    out = {}
+    for label, P in (("splits_128", 128), ("library_splits", 0)):
+        splits = W.decode_num_splits(cache, cache.n, w.num_q_heads, P)
+        ws = W.decode_workspace(cache, cache.n, w.num_q_heads, P)
+        o = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+        qt = torch.empty_like(o)
+        f = lambda: W.decode_attention_fused(cache, q, tinvt, num_splits=P, workspace=ws, out=o, q_t=qt)
+        t0 = time.perf_counter()   # settle, as in the decode leg
+        while time.perf_counter() - t0 < args.settle_s:
+            for _ in range(20):
+                f()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 50
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[label] = {"splits": splits, "us_per_call": round(us, 2), "GB_per_s": round(gbs, 1),
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"[bench] long-context decode, {splits} splits: {us:.1f} us per call ({gbs:.0f} GB/s)")
+    out["bytes_per_call"] = int(nbytes)
+    del cache
+    torch.cuda.empty_cache()
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv, copy_mib):
+    """Per-dispatch HBM bytes of the library's kernels from two rocprofv3 --pmc runs
+    (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
+    reads for the plain copy of --copy-check (its bytes are known)."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        copy = []
+        copy_items = (copy_mib << 20) // 4
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            if "wushkv" in name:
+                acc[name.replace("void ", "").replace("wushkv::(anonymous namespace)::", "").split("(")[0]].append(val)
+            elif "elementwise" in name and int(r["Grid_Size"]) >= copy_items // 4:
+                copy.append(val)
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}, copy
+
+    fetch, nf, cf = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, nw, cw = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib << 20
+    ff = copy_bytes / (sum(cf) / len(cf) * 1024)
+    wf = copy_bytes / (sum(cw) / len(cw) * 1024)
+    kernels = {}
+    for k in sorted(fetch):
+        kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write.get(k, 0.0), 1),
+                      "dispatches": nf[k],
+                      "bytes_per_dispatch": int(fetch[k] * 1024 * ff + write.get(k, 0.0) * 1024 * wf)}
+    return {"calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": round(sum(cf) / len(cf), 1),
+                            "copy_write_kib": round(sum(cw) / len(cw), 1), "fetch_factor": round(ff, 5),
+                            "write_factor": round(wf, 5), "copy_dispatches": len(cf)},
+            "kernels": kernels}
 
 
 def run_cpu_leg(dl, sample_heads=16):
@@ -269,10 +367,21 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (profiling the flush alone)")
     ap.add_argument("--flush-bits", type=str, default="", help="comma-separated bit widths of the flush leg")
+    ap.add_argument("--no-long", action="store_true", help="skip the long-context decode leg")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed decode-only launches before the warm-up steps")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
                     help="first copy a MIB-sized device buffer three times: a plain copy of known size, whose "
                          "FETCH_SIZE / WRITE_SIZE counters calibrate the decode kernel's traffic figures")
+    ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU work: summarize two rocprofv3 counter_collection.csv files (runs made with "
+                         "--copy-check MIB) as JSON on stdout")
     args = ap.parse_args()
+    if args.counters_summary:
+        rec = summarize_counters(*args.counters_summary, args.copy_check or 1024)
+        rec["source_hash"] = kernel_source_hash()
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every workload runs on a single MI355X); run with --gpus 1.", file=sys.stderr)
@@ -296,8 +405,9 @@ def main():
     dl = run_decode_leg(args)
     w = dl["workload"]
     fl = {} if args.no_flush else run_flush_leg(args)
+    lc = {} if args.no_long else run_long_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
-    traffic = traffic_from_profile("decode_batched_serving_counters.json")
+    traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": "2-bit GQA decode-attention HBM GB/s (% of peak); flush tokens/s",
@@ -319,7 +429,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "step_breakdown_ms": {"append_flush": round(dl["app_ms"], 5),
                               "decode_attention_fused": round(dl["dec_ms"], 5),
-                              "note": "event intervals of untimed steps after the timed region"},
+                              "note": "HIP-event intervals around each call over K further steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
@@ -331,6 +441,9 @@ def main():
         line["flush"] = {f"{b}bit": {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_36_layers": round(r["ms"], 3),
                                      "GB_per_s": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / HBM_PEAK_GBS, 4)}
                          for b, r in fl.items()}
+    if lc:
+        line["long_context"] = dict(lc, workload=configs_name("LONG_CONTEXT"),
+                                    quant="percentile-clipped affine 2-bit K / 3-bit V")
     if not args.no_cpu:
         line["cpu_baseline"] = run_cpu_leg(dl)
     print(json.dumps(line), flush=True)
