@@ -273,35 +273,37 @@ def run_long_leg(args):
 def summarize_counters(fetch_csv, write_csv, copy_mib):
     """Per-dispatch HBM bytes of the library's kernels from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
-    reads for the plain copy of --copy-check (its bytes are known)."""
+    reads for the fp32 -> fp64 copy of --copy-check (its bytes are known)."""
     import csv
     import collections
 
     def per_kernel(path, counter):
         acc = collections.defaultdict(list)
         copy = []
-        copy_items = (copy_mib << 20) // 4
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
                 continue
             name, val = r["Kernel_Name"], float(r["Counter_Value"])
             if "wushkv" in name:
                 acc[name.replace("void ", "").replace("wushkv::(anonymous namespace)::", "").split("(")[0]].append(val)
-            elif "elementwise" in name and int(r["Grid_Size"]) >= copy_items // 4:
+            elif "copy" in name and "double" in name:
                 copy.append(val)
         return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}, copy
 
     fetch, nf, cf = per_kernel(fetch_csv, "FETCH_SIZE")
     write, nw, cw = per_kernel(write_csv, "WRITE_SIZE")
-    copy_bytes = copy_mib << 20
+    copy_bytes = copy_mib << 20          # read by the fp32 -> fp64 copy; it writes twice that
+    if not cf or not cw:
+        raise SystemExit("no fp32 -> fp64 copy-check dispatches in the counter files (run with --copy-check)")
     ff = copy_bytes / (sum(cf) / len(cf) * 1024)
-    wf = copy_bytes / (sum(cw) / len(cw) * 1024)
+    wf = 2 * copy_bytes / (sum(cw) / len(cw) * 1024)
     kernels = {}
     for k in sorted(fetch):
         kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write.get(k, 0.0), 1),
                       "dispatches": nf[k],
                       "bytes_per_dispatch": int(fetch[k] * 1024 * ff + write.get(k, 0.0) * 1024 * wf)}
-    return {"calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": round(sum(cf) / len(cf), 1),
+    return {"calibration": {"copy_read_bytes": copy_bytes, "copy_write_bytes": 2 * copy_bytes,
+                            "copy_fetch_kib": round(sum(cf) / len(cf), 1),
                             "copy_write_kib": round(sum(cw) / len(cw), 1), "fetch_factor": round(ff, 5),
                             "write_factor": round(wf, 5), "copy_dispatches": len(cf)},
             "kernels": kernels}
@@ -389,13 +391,15 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_check > 0:
+        # an fp32 -> fp64 conversion copy: MIB read, 2 MIB written, by a kernel no
+        # workload launches (a same-dtype copy goes through the runtime's blit path)
         n = args.copy_check << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
+        dst = torch.empty(n // 4, dtype=torch.float64, device="cuda")
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        log(f"[bench] copy check: 3 copies of {n} bytes")
+        log(f"[bench] copy check: 3 fp32 -> fp64 copies of {n} bytes")
         del src, dst
 
     if args.no_decode:
