@@ -10,8 +10,9 @@ windows, q, q~, out) per step over the step time.  Before the warm-up steps the
 decode is launched untimed for a fraction of a second so that the timed steps run at
 the chip's steady clocks.  Further legs time the bulk prefill flush (36 layers x 8 KV
 heads x 65536 tokens) at 2, 3 and 4 bits, the long-context decode (8 sequences of
-131072 tokens, 64 query / 8 KV heads, 2-bit K / 3-bit V), and the CPU oracle on a
-bounded sample of the decode step.
+131072 tokens, 64 query / 8 KV heads, 2-bit K / 3-bit V), the calibration sums of one
+layer (128 sequences of 1024 tokens), and the CPU oracle on a bounded sample of the
+decode step.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-flush] [--no-cpu]
 """
@@ -270,6 +271,58 @@ def run_long_leg(args):
     return out
 
 
+def run_calib_leg(args):
+    """Calibration sums of one layer of the calibration workload (128 sequences x 1024
+    tokens, 8 KV / 32 query heads): key Gram, value Gram and the key Hessian (query heads
+    grouped by KV head), each timed over back-to-back calls after a settle."""
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+
+    w = configs.CALIB
+    dev = "cuda"
+    T = w.context
+    log(f"[bench] calibration workload {w.name}: {w.batch} sequences x {T} tokens, Hkv={w.num_kv_heads} Hq={w.num_q_heads}")
+    k, v = gen.kv_tensors(w, 0, T, dev)
+    q = gen.calib_queries(w, 0, T, dev)
+    res = {}
+    total_bytes, total_flop, total_us = 0, 0, 0.0
+    for name, x, group in (("key_gram", k, 1), ("value_gram", v, 1), ("key_hessian", q, w.group)):
+        B, H, _, d = x.shape
+        ws = W.calib_workspace(B, H, T, d, group, dev)
+        out = torch.empty((H // group, d, d), dtype=torch.float32, device=dev)
+        f = lambda: W.calib_stats(x, group, workspace=ws, out=out)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.settle_s:
+            for _ in range(10):
+                f()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 30
+        e0.record()
+        for _ in range(reps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        nbytes = x.numel() * x.element_size() + out.numel() * 4
+        flop = 2 * B * H * T * d * d
+        res[name] = {"us_per_call": round(us, 2), "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "TFLOP_per_s": round(flop / (us * 1e-6) / 1e12, 1), "bytes": int(nbytes), "flop": int(flop)}
+        total_bytes += nbytes
+        total_flop += flop
+        total_us += us
+        log(f"[bench] calib {name}: {us:.1f} us ({nbytes / (us * 1e-6) / 1e9:.0f} GB/s, "
+            f"{flop / (us * 1e-6) / 1e12:.0f} TFLOP/s)")
+    res["layer"] = {"us": round(total_us, 2), "GB_per_s": round(total_bytes / (total_us * 1e-6) / 1e9, 1),
+                    "frac_hbm": round(total_bytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "TFLOP_per_s": round(total_flop / (total_us * 1e-6) / 1e12, 1)}
+    del k, v, q
+    torch.cuda.empty_cache()
+    return res
+
+
 def summarize_counters(fetch_csv, write_csv, copy_mib):
     """Per-dispatch HBM bytes of the library's kernels from two rocprofv3 --pmc runs
     (FETCH_SIZE, WRITE_SIZE, KiB per dispatch), each scaled by what the same counter
@@ -370,6 +423,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (profiling the flush alone)")
     ap.add_argument("--flush-bits", type=str, default="", help="comma-separated bit widths of the flush leg")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode leg")
+    ap.add_argument("--no-calib", action="store_true", help="skip the calibration-statistics leg")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of untimed decode-only launches before the warm-up steps")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
@@ -410,6 +464,7 @@ def main():
     w = dl["workload"]
     fl = {} if args.no_flush else run_flush_leg(args)
     lc = {} if args.no_long else run_long_leg(args)
+    cl = {} if args.no_calib else run_calib_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
@@ -448,6 +503,9 @@ def main():
     if lc:
         line["long_context"] = dict(lc, workload=configs_name("LONG_CONTEXT"),
                                     quant="percentile-clipped affine 2-bit K / 3-bit V")
+    if cl:
+        line["calibration"] = dict(cl, workload=configs_name("CALIB"),
+                                   note="bf16 rows; out[g] = sum of x x^T; flop counted as 2 N d^2 per head")
     if not args.no_cpu:
         line["cpu_baseline"] = run_cpu_leg(dl)
     print(json.dumps(line), flush=True)

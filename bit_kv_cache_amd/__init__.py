@@ -19,7 +19,8 @@ Q_QUEST, Q_AFFINE = 0, 1
 PLANES = ("sink_k", "sink_v", "ring_k", "ring_v", "codes_k", "codes_v", "par_k", "par_v")
 EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "wushkv_plane_bytes",
            "wushkv_decode_num_splits", "wushkv_decode_workspace_bytes", "wushkv_append_flush",
-           "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused")
+           "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused",
+           "wushkv_calib_stats", "wushkv_calib_workspace_bytes")
 
 
 class WushKVError(RuntimeError):
@@ -63,6 +64,8 @@ def lib():
             "wushkv_query_transform": (ctypes.c_int, [vp, vp, i32, i32, i32, i32, i32, vp, vp]),
             "wushkv_decode_attention": (ctypes.c_int, [P, i64, vp, i32, vp, i32, i32, vp, sz, vp, vp]),
             "wushkv_decode_attention_fused": (ctypes.c_int, [P, i64, vp, i32, vp, vp, i32, i32, vp, sz, vp, vp]),
+            "wushkv_calib_stats": (ctypes.c_int, [vp, i32, i32, i32, i64, i32, i32, vp, sz, vp, vp]),
+            "wushkv_calib_workspace_bytes": (sz, [i32, i32, i64, i32, i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name, None)   # an older build may lack later entry points
@@ -237,3 +240,26 @@ def decode_attention_fused(cache: KVCache, q, t_inv_t, n_tokens=None, num_splits
                                                workspace.numel(), _ptr(out), _stream(stream, q.device)),
            "decode_attention_fused")
     return out, q_t
+
+
+def calib_workspace(batch, num_heads, tokens, head_dim=128, group=1, device="cuda"):
+    """A workspace for calib_stats of these sizes."""
+    import torch
+    n = lib().wushkv_calib_workspace_bytes(batch, num_heads, tokens, head_dim, group)
+    if n == 0:
+        raise WushKVError(ERR_SHAPE, "calib_workspace")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def calib_stats(x, group=1, workspace=None, out=None, stream=None):
+    """Second-order calibration sums: x [B, H, T, d] bf16/f16 -> fp32 [H / group, d, d],
+    out[g] = sum of x x^T over the rows of heads g*group .. g*group + group - 1."""
+    import torch
+    B, H, T, d = x.shape
+    if workspace is None:
+        workspace = calib_workspace(B, H, T, d, group, x.device)
+    if out is None:
+        out = torch.empty((H // group, d, d), dtype=torch.float32, device=x.device)
+    _check(lib().wushkv_calib_stats(_ptr(x), _dtype_code(x), B, H, T, d, group, _ptr(workspace), workspace.numel(),
+                                    _ptr(out), _stream(stream, x.device)), "calib_stats")
+    return out

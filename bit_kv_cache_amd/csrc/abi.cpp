@@ -229,6 +229,37 @@ int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtyp
   return hip_status();
 }
 
+size_t wushkv_calib_workspace_bytes(int32_t batch, int32_t num_heads, int64_t tokens, int32_t head_dim,
+                                    int32_t group) {
+  if (batch < 1 || num_heads < 1 || tokens < 1 || head_dim != 128 || group < 1 || num_heads % group) return 0;
+  return calib_partial_floats(batch, num_heads, group) * sizeof(float);
+}
+
+int wushkv_calib_stats(const void *x, int32_t dtype, int32_t batch, int32_t num_heads, int64_t tokens,
+                       int32_t head_dim, int32_t group, void *workspace, size_t workspace_bytes, float *out,
+                       void *stream) {
+  if (batch < 1 || num_heads < 1 || tokens < 1 || group < 1 || num_heads % group) return WUSHKV_ERR_SHAPE;
+  if (!check_dtype(dtype)) return WUSHKV_ERR_SHAPE;
+  if (head_dim != 128 || dtype == WUSHKV_DT_F32) return WUSHKV_ERR_UNSUPPORTED;
+  if (!x || !out) return WUSHKV_ERR_NULL;
+  if (misaligned(x) || misaligned(out) || misaligned(workspace)) return WUSHKV_ERR_ALIGN;
+  const size_t need = wushkv_calib_workspace_bytes(batch, num_heads, tokens, head_dim, group);
+  if (!workspace || workspace_bytes < need) return WUSHKV_ERR_WORKSPACE;
+  CalibArgs a{};
+  a.x = x;
+  a.dtype = dtype;
+  a.B = batch;
+  a.H = num_heads;
+  a.group = group;
+  a.T = tokens;
+  a.bpw = calib_batch_per_wg(batch, num_heads / group);
+  a.partials = (float *)workspace;
+  a.out = out;
+  hipGetLastError();
+  if (launch_calib(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
+  return hip_status();
+}
+
 }  // extern "C"
 
 namespace {

@@ -88,7 +88,21 @@ struct DecodeArgs {
   int force_generic;              // route to the generic kernel (testing hook)
 };
 
+// Calibration sums S_g = sum x x^T over the rows of heads h with h / group == g.
+struct CalibArgs {
+  const void *x;                  // [B][H][T][128] bf16 or f16
+  int dtype, B, H, group;
+  int64_t T;
+  int bpw;                        // batch rows per workgroup
+  int nparts;                     // partials per group (set by launch_calib)
+  float *partials;                // workspace: [H / group][nparts][10 tiles][32][32]
+  float *out;                     // [H / group][128][128]
+};
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_calib(const CalibArgs &a, hipStream_t s);
+int calib_batch_per_wg(int B, int groups);
+size_t calib_partial_floats(int B, int H, int group);
 hipError_t launch_flush(const FlushArgs &a, hipStream_t s);
 hipError_t launch_qtransform(const QtArgs &a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);

@@ -214,6 +214,33 @@ int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens,
                                   void *workspace, size_t workspace_bytes,
                                   float *out, void *stream);
 
+/*
+ * Calibration statistics (WUSH-KV digest, "method key points": per KV head, the key
+ * transform's Hessian is the sum of Q Q^T over the query heads that read the key and
+ * the Gram matrices are the sums over the keys and values themselves; "takeaways": the
+ * transforms come from one calibration pass):
+ *   out[g] = sum over b, t and every head h with h / group == g of x[b][h][t] x[b][h][t]^T
+ *   x      [batch][num_heads][tokens][head_dim] in dtype (BF16 or F16), e.g. post-RoPE
+ *          keys (group 1: per-head Gram), values (group 1), or queries with group =
+ *          num_q_heads / num_kv_heads (the key Hessian of each KV head).
+ *   out    fp32 [num_heads / group][head_dim][head_dim], row-major, symmetric; written
+ *          whole (no accumulation into it).
+ *   workspace  device buffer of at least wushkv_calib_workspace_bytes() bytes (partial
+ *          sums; no initialisation needed).
+ * Products are exact in fp32 and summed in fp32 on the matrix cores; the partial sums of
+ * a group are added in a fixed order, so the result is the same on every call.
+ * Errors: ERR_SHAPE (non-positive sizes, num_heads % group != 0, unknown dtype),
+ * ERR_UNSUPPORTED (head_dim != 128, F32 input), ERR_NULL, ERR_ALIGN (x, out or workspace
+ * not 16-byte aligned), ERR_WORKSPACE.
+ */
+int wushkv_calib_stats(const void *x, int32_t dtype, int32_t batch, int32_t num_heads,
+                       int64_t tokens, int32_t head_dim, int32_t group,
+                       void *workspace, size_t workspace_bytes, float *out, void *stream);
+
+/* Workspace bytes wushkv_calib_stats needs for these sizes; 0 for sizes it rejects. */
+size_t wushkv_calib_workspace_bytes(int32_t batch, int32_t num_heads, int64_t tokens,
+                                    int32_t head_dim, int32_t group);
+
 #ifdef __cplusplus
 }
 #endif

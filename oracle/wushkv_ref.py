@@ -403,3 +403,32 @@ def decode_head_split(c, q, qt, bounds):
     edges = [0] + list(bounds) + [len(s)]
     parts = [partial_attend(s[a:b], v[a:b]) for a, b in zip(edges[:-1], edges[1:])]
     return merge_partials(parts)
+
+
+# ----------------------------------------------------------------------------
+# calibration statistics
+# ----------------------------------------------------------------------------
+
+def calib_stats(x, group=1):
+    """Second-order calibration sums per KV head (digest, method key points: the key
+    transform's Hessian is built from the query heads that consume the key, a sum of
+    Q Q^T, and the Gram matrices from the keys and values themselves).
+
+    x: [B, H, T, d] (any float dtype; taken exactly in float64).  Returns float64
+    [H // group, d, d]: entry g sums x x^T over every row x[b, h, t] with
+    h // group == g, i.e. X_g^T X_g for X_g the stacked rows of the group."""
+    x = np.asarray(x, dtype=np.float64)
+    B, H, T, d = x.shape
+    if H % group:
+        raise ValueError("num_heads must be a multiple of group")
+    out = np.zeros((H // group, d, d))
+    for g in range(H // group):
+        rows = x[:, g * group:(g + 1) * group].reshape(-1, d)
+        out[g] = rows.T @ rows
+    return out
+
+
+def calib_sum_abs(x, group=1):
+    """Entrywise sum |x_i| |x_j| over the same rows: the scale of the rounding error of
+    any fp32 evaluation of calib_stats (error <= n u sum |x_i x_j| for n sequential adds)."""
+    return calib_stats(np.abs(np.asarray(x, dtype=np.float64)), group)

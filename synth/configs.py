@@ -83,4 +83,14 @@ LONG_CONTEXT = Workload(
     bits_k=2, bits_v=3, chunk=8, decode_steps=1, num_splits=128, k_dist="t3", v_dist="t3")
 
 ALL = [TINY, LAYER_8B, SERVING, BULK_FLUSH, LONG_CONTEXT]
+
+# Calibration statistics (outside the decode/flush configurations above): one
+# attention layer of the 8B geometry over 128 calibration sequences of 1024 tokens
+# (digest, key experiments: 128 calibration sequences; the length 1024 stated for the
+# evaluation sequences is taken for them too).  Keys as in the 8B layer workload.
+CALIB = Workload(
+    name="c5_calibration_stats", seed=5, layers=1, batch=128, num_q_heads=32, num_kv_heads=8,
+    head_dim=128, context=1024, in_dtype="bf16", quant_k=QUEST, quant_v=QUEST,
+    bits_k=2, bits_v=2, chunk=8, decode_steps=0, k_dist="gauss", v_dist="gauss_iso",
+    k_outliers=4)
 BY_NAME = {w.name: w for w in ALL}

@@ -17,7 +17,8 @@ Recipe (per layer l and KV head g; "stream" separates independent draws):
 * T_K = Q diag(s), Q Haar-orthogonal, s_i = 2**Uniform(-2, 2) (log-uniform on
   [0.25, 4]), rounded to fp16.  T^{-T} is the float64 inverse-transpose of
   that fp16 matrix, handed over in fp32.
-* Queries q ~ N(0, I).
+* Queries q ~ N(0, I).  Calibration queries (a sequence of rows per query head):
+  q = U_h diag(sqrt(lambda_h)) z under each query head's own U_h and lambda_h.
 * Everything is rounded to bf16 (round-to-nearest-even) unless the workload's
   input dtype is fp32.
 
@@ -35,6 +36,7 @@ from .configs import Workload
 STREAM_K_STATS, STREAM_V_STATS, STREAM_T = 0, 1, 2
 STREAM_K_ROWS, STREAM_V_ROWS = 10, 11
 STREAM_Q = 20
+STREAM_QC_STATS, STREAM_QC_ROWS = 30, 31
 
 
 def _seed(*key) -> int:
@@ -128,3 +130,28 @@ def queries(w: Workload, layer: int, step: int, device="cpu") -> torch.Tensor:
     rng = _rng(w.seed, layer, STREAM_Q, step)
     q = rng.standard_normal((w.batch, w.num_q_heads, w.head_dim)).astype(np.float32)
     return torch.from_numpy(q).to(torch_dtype(w.in_dtype)).to(device)
+
+
+def _calib_query_mix(w: Workload, layer: int, h: int, device) -> torch.Tensor:
+    rng = _rng(w.seed, layer, h, STREAM_QC_STATS)
+    u = haar_orthogonal(rng, w.head_dim)
+    lam = 10.0 ** rng.uniform(-2.0, 2.0, size=w.head_dim)
+    return torch.from_numpy((u * np.sqrt(lam)[None, :]).T.astype(np.float32)).to(device)
+
+
+def calib_query_block(w: Workload, layer: int, b: int, h: int, n: int, device="cpu", mix=None) -> torch.Tensor:
+    """Calibration query rows [n, d] (input dtype) of batch row b, query head h."""
+    mix = _calib_query_mix(w, layer, h, device) if mix is None else mix
+    gen = torch.Generator(device=device).manual_seed(_seed(w.seed, layer, h, b, STREAM_QC_ROWS))
+    return (_rows(n, w.head_dim, "gauss", gen, device) @ mix).to(torch_dtype(w.in_dtype))
+
+
+def calib_queries(w: Workload, layer: int, n: int, device="cpu", heads=None) -> torch.Tensor:
+    """Calibration queries [B, len(heads), n, d] (all query heads by default)."""
+    heads = list(range(w.num_q_heads)) if heads is None else list(heads)
+    q = torch.empty((w.batch, len(heads), n, w.head_dim), dtype=torch_dtype(w.in_dtype), device=device)
+    for i, h in enumerate(heads):
+        mix = _calib_query_mix(w, layer, h, device)
+        for b in range(w.batch):
+            q[b, i] = calib_query_block(w, layer, b, h, n, device, mix)
+    return q

@@ -159,3 +159,27 @@ def test_product_package_does_not_use_the_oracle():
             if fn.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.replace("oracle of", ""), fn
+
+
+def test_calib_validation_and_workspace(lib):
+    """Calibration sums: argument checks on the host (nothing launches) and the
+    workspace size (10 upper-triangle 32 x 32 fp32 tiles per partial)."""
+    f = lib.wushkv_calib_stats
+    wsb = lib.wushkv_calib_workspace_bytes
+    p = ctypes.c_void_p(0x900000)
+    need = wsb(128, 32, 1024, 128, 4)
+    assert need > 0 and need % (10 * 1024 * 4) == 0
+    assert (need // (10 * 1024 * 4)) % 8 == 0          # a whole number of partials per group
+    assert wsb(128, 32, 1024, 64, 4) == 0 and wsb(128, 30, 1024, 128, 4) == 0 and wsb(0, 8, 1, 128, 1) == 0
+    n1 = wsb(2, 8, 64, 128, 1)
+    assert f(p, W.DT_BF16, 2, 8, 64, 128, 3, p, n1, p, None) == W.ERR_SHAPE       # 8 % 3
+    assert f(p, W.DT_BF16, 0, 8, 64, 128, 1, p, n1, p, None) == W.ERR_SHAPE
+    assert f(p, W.DT_BF16, 2, 8, 0, 128, 1, p, n1, p, None) == W.ERR_SHAPE
+    assert f(p, 9, 2, 8, 64, 128, 1, p, n1, p, None) == W.ERR_SHAPE
+    assert f(p, W.DT_F32, 2, 8, 64, 128, 1, p, n1, p, None) == W.ERR_UNSUPPORTED
+    assert f(p, W.DT_BF16, 2, 8, 64, 64, 1, p, n1, p, None) == W.ERR_UNSUPPORTED
+    assert f(None, W.DT_BF16, 2, 8, 64, 128, 1, p, n1, p, None) == W.ERR_NULL
+    assert f(p, W.DT_BF16, 2, 8, 64, 128, 1, p, n1, None, None) == W.ERR_NULL
+    assert f(ctypes.c_void_p(0x900002), W.DT_BF16, 2, 8, 64, 128, 1, p, n1, p, None) == W.ERR_ALIGN
+    assert f(p, W.DT_BF16, 2, 8, 64, 128, 1, p, n1 - 1, p, None) == W.ERR_WORKSPACE
+    assert f(p, W.DT_BF16, 2, 8, 64, 128, 1, None, n1, p, None) == W.ERR_WORKSPACE
