@@ -14,8 +14,8 @@
 // 10 tiles with I <= J of the 4 x 4 tiling at d = 128 are formed, the reduction mirrors them.
 //
 // Work: a workgroup takes one group (its heads) and a block of batch rows, streams their
-// tokens in steps of 64 through LDS, transposed to channel-major on the way in (16-bit
-// stores), and writes its 10 tiles as one partial; a second kernel sums a group's
+// tokens in steps of 64 (loaded two steps ahead into registers) through LDS, transposed to
+// channel-major on the way in (16-bit stores), and writes its 10 tiles as one partial; a second kernel sums a group's
 // partials in a fixed order (the result does not depend on timing) and writes the full
 // matrix.
 #include "wushkv_internal.h"
@@ -40,30 +40,52 @@ __host__ __device__ constexpr int tile_j(int t) {
   return t < 4 ? t : (t < 7 ? t - 3 : (t < 9 ? t - 5 : 3));
 }
 
-// One step of 64 rows: thread i takes row i % 64 and its 16-byte chunks (8 channels
-// each) i / 64, i / 64 + 4, i / 64 + 8, i / 64 + 12; rows past the end read as zeros.
+// LDS holds a step channel-major, lds[channel][token], with the 8-token chunks of a
+// channel row permuted: token t of channel c sits at column
+//   ((t / 8) xor ((c / 16) mod 8)) * 8 + t mod 8.
+// A 16-byte operand read (8 consecutive tokens of one channel) stays contiguous, the 16
+// lanes of a read pass (16 consecutive channels) share the permutation and hit distinct
+// banks through the row pitch, and the 16-bit stores below (16 channel groups x 4
+// tokens per instruction) are spread over all banks by it.
+__device__ __forceinline__ int lds_col(int c, int t) { return (((t >> 3) ^ ((c >> 4) & 7)) << 3) | (t & 7); }
+
+// One step of 64 rows, loaded contiguously: 16-byte chunk i of the step's 16 KB goes to
+// thread i % 256 (row i / 16, channels 8 (i % 16) .. + 7), so one load instruction reads
+// four whole rows.  The loads are unconditional (a row past the end re-reads the last
+// row and is zeroed at the store), so the compiler counts the loads in flight exactly
+// instead of draining them.
 __device__ __forceinline__ void load_step(const uint8_t *rows, int64_t t0, int64_t T, int tid, u32x4 (&r)[4]) {
-  const int64_t t = t0 + (tid & 63);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[i] = (u32x4){0u, 0u, 0u, 0u};
-    if (t < T) r[i] = __builtin_nontemporal_load((const u32x4 *)(rows + (size_t)t * (kCD * 2)) + (tid >> 6) + 4 * i);
+    const int c = tid + kCalibThreads * i;
+    const int64_t t = t0 + c / 16;
+    r[i] = __builtin_nontemporal_load((const u32x4 *)(rows + (size_t)(t < T ? t : T - 1) * (kCD * 2)) + (c % 16));
   }
 }
 
-// ... stored channel-major, lds[channel][row]: each 16-bit store instruction writes one
-// channel of the wave's 64 rows, 128 contiguous bytes (no bank conflicts).
-__device__ __forceinline__ void store_step(uint16_t *lds, int tid, const u32x4 (&r)[4]) {
-  uint16_t *col = lds + (tid & 63);
+// ... stored channel-major (16-bit stores, element by element).
+__device__ __forceinline__ void store_step(uint16_t *lds, int tid, int64_t t0, int64_t T, const u32x4 (&r)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int ch0 = 8 * ((tid >> 6) + 4 * i);
+    const int c = tid + kCalibThreads * i;
+    const int row = c / 16, ch0 = 8 * (c % 16);
+    const bool valid = t0 + row < T;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      col[(ch0 + 2 * k) * kPitch] = (uint16_t)(r[i][k] & 0xFFFFu);
-      col[(ch0 + 2 * k + 1) * kPitch] = (uint16_t)(r[i][k] >> 16);
+      const unsigned w = valid ? r[i][k] : 0u;
+      const int c0 = ch0 + 2 * k, c1 = c0 + 1;
+      lds[c0 * kPitch + lds_col(c0, row)] = (uint16_t)(w & 0xFFFFu);
+      lds[c1 * kPitch + lds_col(c1, row)] = (uint16_t)(w >> 16);
     }
   }
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations complete, then
+// s_barrier.  (__syncthreads also waits for every outstanding global load, which would
+// drain the prefetched rows at each step.)  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 template <bool BF16>
@@ -109,27 +131,35 @@ __global__ void __launch_bounds__(kCalibThreads, 2) calib_partial_kernel(CalibAr
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
 
-  u32x4 r[4];
+  // Rows of step s are loaded into registers during step s - 2 and stored to LDS (stage
+  // s % 2) during step s - 1, so every load has two steps of work to land in.  Two
+  // register sets alternate; the loop body is written for both orders.
+  u32x4 ra[4], rb[4];
+  // step s's token offset, and whether this thread's row of it exists
+  auto t0_of = [&](int64_t s) { return (s % steps_per_row) * kStep; };
+  // a step past the last re-reads the last one (branch-free loads; never stored)
+  auto clamp = [&](int64_t s) { return s < nsteps ? s : nsteps - 1; };
   if (nsteps > 0) {
-    load_step(rows_of(0), 0, a.T, tid, r);
-    store_step(stage[0], tid, r);
+    load_step(rows_of(0), 0, a.T, tid, ra);
+    load_step(rows_of(clamp(1)), t0_of(clamp(1)), a.T, tid, rb);
+    store_step(stage[0], tid, 0, a.T, ra);
   }
-  __syncthreads();
+  lds_barrier();
   // operand of lane l for channel block I and 16-token chunk kc: channel 32 I + l % 32,
   // tokens 16 kc + 8 (l / 32) .. + 7
   const int orow = lane & 31, ocol = 8 * (lane >> 5);
-  for (int64_t s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      const int64_t sn = s + 1;
-      load_step(rows_of(sn), (sn % steps_per_row) * kStep, a.T, tid, r);
-    }
+  auto step = [&](int64_t s, u32x4 (&rload)[4], u32x4 (&rstore)[4]) {
+    const int64_t sl = clamp(s + 2);
+    load_step(rows_of(sl), t0_of(sl), a.T, tid, rload);
     const uint16_t *st = stage[s & 1];
 #pragma unroll
     for (int kc = 0; kc < kStep / 16; ++kc) {
       u32x4 op[4];
 #pragma unroll
-      for (int I = 0; I < 4; ++I) op[I] = *(const u32x4 *)(st + (32 * I + orow) * kPitch + 16 * kc + ocol);
+      for (int I = 0; I < 4; ++I) {
+        const int c = 32 * I + orow;
+        op[I] = *(const u32x4 *)(st + c * kPitch + lds_col(c, 16 * kc + ocol));
+      }
       switch (wave) {   // wave-uniform
         case 0: wave_tiles<BF16, 0>(acc, op); break;
         case 1: wave_tiles<BF16, 1>(acc, op); break;
@@ -137,8 +167,12 @@ __global__ void __launch_bounds__(kCalibThreads, 2) calib_partial_kernel(CalibAr
         default: wave_tiles<BF16, 3>(acc, op); break;
       }
     }
-    if (more) store_step(stage[(s + 1) & 1], tid, r);
-    __syncthreads();
+    if (s + 1 < nsteps) store_step(stage[(s + 1) & 1], tid, t0_of(s + 1), a.T, rstore);
+    lds_barrier();
+  };
+  for (int64_t s = 0; s < nsteps; s += 2) {
+    step(s, ra, rb);                       // loads step s + 2 into ra, stores step s + 1 from rb
+    if (s + 1 < nsteps) step(s + 1, rb, ra);
   }
   // partial (g, bc), tile-major 32 x 32 blocks
   float *part = a.partials + ((size_t)g * a.nparts + bc) * (kTiles * 1024);
