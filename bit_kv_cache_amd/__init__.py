@@ -20,7 +20,8 @@ PLANES = ("sink_k", "sink_v", "ring_k", "ring_v", "codes_k", "codes_v", "par_k",
 EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "wushkv_plane_bytes",
            "wushkv_decode_num_splits", "wushkv_decode_workspace_bytes", "wushkv_append_flush",
            "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused",
-           "wushkv_calib_stats", "wushkv_calib_workspace_bytes")
+           "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
+           "wushkv_decode_attention_ragged")
 
 
 class WushKVError(RuntimeError):
@@ -65,6 +66,9 @@ def lib():
             "wushkv_decode_attention": (ctypes.c_int, [P, i64, vp, i32, vp, i32, i32, vp, sz, vp, vp]),
             "wushkv_decode_attention_fused": (ctypes.c_int, [P, i64, vp, i32, vp, vp, i32, i32, vp, sz, vp, vp]),
             "wushkv_calib_stats": (ctypes.c_int, [vp, i32, i32, i32, i64, i32, i32, vp, sz, vp, vp]),
+            "wushkv_append_flush_ragged": (ctypes.c_int, [P, ctypes.POINTER(i64), i32, vp, vp, i32, vp, vp]),
+            "wushkv_decode_attention_ragged": (ctypes.c_int, [P, ctypes.POINTER(i64), vp, i32, vp, vp, i32, i32, vp, sz,
+                                                              vp, vp]),
             "wushkv_calib_workspace_bytes": (sz, [i32, i32, i64, i32, i32]),
         }
         for name, (res, args) in sig.items():
@@ -154,6 +158,24 @@ class KVCache:
                        for p, n in spec.plane_bytes().items()}
         self.desc = spec.desc(self.planes)
         self.n = 0
+        self.seq_n = None   # per-sequence token counts of a ragged batch
+
+    def sequence(self, b):
+        """Batch row b as a one-sequence cache sharing this cache's memory (planes are
+        [batch][...], so a row's block is contiguous): the uniform entry points then
+        serve one sequence of a ragged batch, e.g. to prefill it."""
+        import copy
+        s = copy.copy(self.spec)
+        s.batch = 1
+        sub = KVCache.__new__(KVCache)
+        sub.spec = s
+        full = self.spec.plane_bytes()
+        sub.planes = {p: self.planes[p][b * (full[p] // self.spec.batch):(b + 1) * (full[p] // self.spec.batch)]
+                      for p in PLANES}
+        sub.desc = s.desc(sub.planes)
+        sub.n = self.seq_n[b] if self.seq_n is not None else self.n
+        sub.seq_n = None
+        return sub
 
     def view(self, plane, dtype=None):
         import torch
@@ -263,3 +285,45 @@ def calib_stats(x, group=1, workspace=None, out=None, stream=None):
     _check(lib().wushkv_calib_stats(_ptr(x), _dtype_code(x), B, H, T, d, group, _ptr(workspace), workspace.numel(),
                                     _ptr(out), _stream(stream, x.device)), "calib_stats")
     return out
+
+
+def _i64_array(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def append_flush_ragged(cache: KVCache, k_new, v_new, t_k16, n_before=None, stream=None):
+    """Append [B, Hkv, n_new, d] keys/values to a ragged batch: sequence b holds
+    n_before[b] tokens (default: cache.seq_n) and receives its n_new tokens."""
+    import torch
+    n_before = list(cache.seq_n if n_before is None else n_before)
+    n_new = k_new.shape[2]
+    if k_new.dtype != v_new.dtype or t_k16.dtype != torch.float16:
+        raise ValueError("k_new/v_new must share a dtype and t_k16 must be float16")
+    _check(lib().wushkv_append_flush_ragged(ctypes.byref(cache.desc), _i64_array(n_before), n_new, _ptr(k_new),
+                                            _ptr(v_new), _dtype_code(k_new), _ptr(t_k16),
+                                            _stream(stream, k_new.device)), "append_flush_ragged")
+    cache.seq_n = [n + n_new for n in n_before]
+
+
+def decode_attention_ragged(cache: KVCache, q, q_t=None, t_inv_t=None, n_tokens=None, num_splits=0, workspace=None,
+                            out=None, stream=None):
+    """GQA decode of a ragged batch: sequence b attends n_tokens[b] tokens (default:
+    cache.seq_n).  With t_inv_t the decode forms q~ itself into q_t (returned);
+    otherwise q_t is the caller's q~.  -> (out, q_t)."""
+    import torch
+    n_tokens = list(cache.seq_n if n_tokens is None else n_tokens)
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(cache, max(n_tokens), Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if q_t is None:
+        if t_inv_t is None:
+            raise ValueError("decode_attention_ragged needs q_t or t_inv_t")
+        q_t = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention_ragged(ctypes.byref(cache.desc), _i64_array(n_tokens), _ptr(q),
+                                                _dtype_code(q), None if t_inv_t is None else _ptr(t_inv_t),
+                                                _ptr(q_t), Hq, num_splits, _ptr(workspace), workspace.numel(),
+                                                _ptr(out), _stream(stream, q.device)), "decode_attention_ragged")
+    return out, q_t

@@ -31,12 +31,14 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   if (idx >= a.n_new * groups) return;
   const int64_t t = idx / groups;
   const int j0 = (int)(idx % groups) * 8;
-  const int64_t p = a.n_before + t;
+  const int64_t n_before = a.ragged ? a.seq_nb[b] : a.n_before;
+  const int64_t q_after = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.q_after;
+  const int64_t p = n_before + t;
   _Float16 *dk, *dv;
   if (p < a.S) {
     dk = (_Float16 *)((char *)a.sink_k + bg * a.sink_bytes) + p * a.d;
     dv = (_Float16 *)((char *)a.sink_v + bg * a.sink_bytes) + p * a.d;
-  } else if (p >= a.S + a.q_after) {
+  } else if (p >= a.S + q_after) {
     const int64_t slot = (p - a.S) % (a.R + a.C);
     dk = (_Float16 *)((char *)a.ring_k + bg * a.ring_bytes) + slot * a.d;
     dv = (_Float16 *)((char *)a.ring_v + bg * a.ring_bytes) + slot * a.d;
@@ -112,20 +114,20 @@ __device__ __forceinline__ unsigned raw_word(const RawSeg<ES, CPL> &s, int i) {
 // position 8 i + e of its list: one load instruction then covers 32 contiguous
 // channels of each of its 16 rows.
 template <int D, int ES>
-__device__ __forceinline__ void load_seg(const FlushArgs &a, const char *ring_h, const char *in_h, int64_t u, bool valid,
-                                         int q, RawSeg<ES, D / 4> &s) {
+__device__ __forceinline__ void load_seg(const FlushArgs &a, int64_t n_before, const char *ring_h, const char *in_h,
+                                         int64_t u, bool valid, int q, RawSeg<ES, D / 4> &s) {
   constexpr int CPL = D / 4;
 #pragma unroll
   for (int i = 0; i < CPL * ES / 16; ++i) s.r[i] = (u32x4){0u, 0u, 0u, 0u};
   if (!valid) return;
-  if (a.S + u < a.n_before) {
+  if (a.S + u < n_before) {
     const unsigned slot = (unsigned)u % (unsigned)(a.R + a.C);
     const u32x4 *src = (const u32x4 *)(ring_h + (size_t)slot * (D * 2)) + q;
 #pragma unroll
     for (int i = 0; i < CPL / 8; ++i) s.r[i] = src[4 * i];
     return;
   }
-  const u32x4 *src = (const u32x4 *)(in_h + (size_t)(a.S + u - a.n_before) * (D * ES)) + (ES / 2) * q;
+  const u32x4 *src = (const u32x4 *)(in_h + (size_t)(a.S + u - n_before) * (D * ES)) + (ES / 2) * q;
 #pragma unroll
   for (int i = 0; i < CPL / 8; ++i)
 #pragma unroll
@@ -374,18 +376,23 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const int q = lane >> 4, tok = lane & 15;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
-  const int64_t s_first = a.u0 / kSet, s_end = (a.u1 + kSet - 1) / kSet;
-  const int64_t nsteps = (s_end - s_first + 1) / 2;
+  // this sequence's rows before the call and its flushed body rows [u0, u1)
+  const int64_t n_before = a.ragged ? a.seq_nb[b] : a.n_before;
+  const int64_t u0 = a.ragged ? n_quantized(n_before, a.S, a.R, a.C) : a.u0;
+  const int64_t u1 = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.u1;
+  const int64_t s_first = u0 / kSet, s_end = (u1 + kSet - 1) / kSet;
+  const int64_t nsteps = u1 > u0 ? (s_end - s_first + 1) / 2 : 0;
   const int64_t st0 = (int64_t)blockIdx.x * steps_per_wg;
   const int64_t st1 = st0 + steps_per_wg < nsteps ? st0 + steps_per_wg : nsteps;
+  if (st0 >= st1) return;   // (ragged batch) this sequence needs fewer steps
 
   // Each tile's raw rows are refilled with the next step's as soon as they have been
   // converted, so every load has about a step of work to hide behind.
   RawSeg<ES, CPL> rk[2], rv[2];
   auto tok_of = [&](int64_t st, int tt) { return (s_first + 2 * st) * kSet + 32 * wave + 16 * tt + tok; };
-  auto tok_valid = [&](int64_t u) { return u >= a.u0 && u < a.u1; };
+  auto tok_valid = [&](int64_t u) { return u >= u0 && u < u1; };
   // rows of earlier calls come from the ring (fp16); invalid rows read as fp16 zeros
-  auto tok_ring = [&](int64_t u) { return !tok_valid(u) || a.S + u < a.n_before; };
+  auto tok_ring = [&](int64_t u) { return !tok_valid(u) || a.S + u < n_before; };
   // this KV head's ring and input rows
   const char *ring_kh = (const char *)a.ring_k + (size_t)bg * a.ring_bytes;
   const char *ring_vh = (const char *)a.ring_v + (size_t)bg * a.ring_bytes;
@@ -394,11 +401,11 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const char *in_vh = (const char *)a.v_new + in_off;
   auto load_k = [&](int64_t st, int tt) {
     const int64_t u = tok_of(st, tt);
-    load_seg<D, ES>(a, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
+    load_seg<D, ES>(a, n_before, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
   };
   auto load_v = [&](int64_t st, int tt) {
     const int64_t u = tok_of(st, tt);
-    load_seg<D, ES>(a, ring_vh, in_vh, u, tok_valid(u), q, rv[tt]);
+    load_seg<D, ES>(a, n_before, ring_vh, in_vh, u, tok_valid(u), q, rv[tt]);
   };
   if (st0 < st1) {   // in flight while T_K is staged
 #pragma unroll
@@ -601,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       constexpr int BK = decltype(bits_tag)::value;
       const int r = tid >> 1, h = tid & 1;
       const int64_t u = set0 * kSet + r;
-      if (u < a.u0 || u >= a.u1) return;
+      if (u < u0 || u >= u1) return;
       constexpr int HC = D / 2;
       uint8_t *rowp = a.codes_k + (size_t)bg * a.kcode_bytes + (size_t)u * a.kcode_row;
       u32x4 cw[HC / 16];
@@ -646,8 +653,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     const int s2 = tid >> 7, t128 = tid & 127;
     const int64_t sidx = set0 + s2;
     const int64_t vbase = sidx * kSet;
-    const int64_t vlo = a.u0 > vbase ? a.u0 : vbase;
-    const int64_t vhi = a.u1 < vbase + kSet ? a.u1 : vbase + kSet;
+    const int64_t vlo = u0 > vbase ? u0 : vbase;
+    const int64_t vhi = u1 < vbase + kSet ? u1 : vbase + kSet;
     auto pack_v_words = [&](auto bits_tag, auto full_tag) {
       constexpr int BVV = decltype(bits_tag)::value;
       constexpr bool FULL = decltype(full_tag)::value;
@@ -734,9 +741,25 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Steps (128 body rows) of a flush of body rows [u0, u1).
+static int64_t flush_steps(int64_t u0, int64_t u1) {
+  if (u1 <= u0) return 0;
+  const int64_t s0 = u0 / kSet, s1 = (u1 + kSet - 1) / kSet;
+  return (s1 - s0 + 1) / 2;
+}
+
 hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
-  const int64_t s0 = a.u0 / kSet, s1 = (a.u1 + kSet - 1) / kSet;
-  const int64_t steps = (s1 - s0 + 1) / 2;
+  int64_t steps = 0;   // the most any sequence needs; workgroups past a sequence's own return
+  if (a.ragged) {
+    for (int b = 0; b < a.B; ++b) {
+      const int64_t nb = a.seq_nb[b];
+      const int64_t st = flush_steps(n_quantized(nb, a.S, a.R, a.C), n_quantized(nb + a.n_new, a.S, a.R, a.C));
+      if (st > steps) steps = st;
+    }
+  } else {
+    steps = flush_steps(a.u0, a.u1);
+  }
+  if (steps == 0) return hipSuccess;
   const int64_t heads = (int64_t)a.B * a.Hkv;
   // about 1024 workgroups (two rounds of the two that fit per CU); each walks a
   // contiguous run of at least two steps of one KV head, so T_K is staged once per

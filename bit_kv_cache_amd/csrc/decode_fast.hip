@@ -409,6 +409,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const float qk_scale = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
   const int Lv = 1 << BV;
+  const SeqLen sl = seq_len(a, bg / a.Hkv);   // this sequence's tokens and body tokens
 
   SetSource src;
   {
@@ -429,10 +430,10 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   constexpr int SB = Stage<BV>::SIZE;
   // items of this wave: 8-token window stages ws0 .. ws1-1, then body sets s0 .. s1-1
   const int nb = (int)(s1 - s0), nitems = nb + (ws1 - ws0);
-  const int ns = (int)(a.n < a.S ? a.n : a.S);
-  const int nw = ns + (int)(a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+  const int ns = (int)(sl.n < a.S ? sl.n : a.S);
+  const int nw = ns + (int)(sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
   const unsigned rsz = (unsigned)(a.R + a.C);
-  const unsigned first_slot = (unsigned)(a.nq % rsz);
+  const unsigned first_slot = (unsigned)(sl.nq % rsz);
   const uint8_t *sinkk = (const uint8_t *)a.sink_k + (size_t)bg * a.sink_bytes;
   const uint8_t *sinkv = (const uint8_t *)a.sink_v + (size_t)bg * a.sink_bytes;
   const uint8_t *ringk = (const uint8_t *)a.ring_k + (size_t)bg * a.ring_bytes;
@@ -549,7 +550,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
         s_t = (float)pz[0];
         z_t = (float)pz[1];
       }
-      const bool valid = FULL || base + u < a.nq;
+      const bool valid = FULL || base + u < sl.nq;
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
         sc[qd][T] = valid ? fmaf(s_t, sc[qd][T], z_t * b_sc[qd]) : -INFINITY;
@@ -617,7 +618,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
         s_t = (float)pz[0];
         z_t = (float)pz[1];
       }
-      const bool valid = FULL || base + u < a.nq;
+      const bool valid = FULL || base + u < sl.nq;
       // the MFMA forms sum (hi + lo) (BASE + c); the zero term takes p z - BASE W with
       // W in place of hi + lo (they differ by ~2^-22 W)
       const float zb = fmaf(-vbase[T], s_t, z_t);
@@ -682,7 +683,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   using FullTag = std::integral_constant<bool, true>;
   using TailTag = std::integral_constant<bool, false>;
   auto body_sets = [&](auto kq_tag, auto vq_tag) {
-    const int64_t full_end = a.nq / kSet;   // sets below this index are full
+    const int64_t full_end = sl.nq / kSet;   // sets below this index are full
     const int nfull = full_end <= s0 ? 0 : (int)(full_end - s0 < nb ? full_end - s0 : nb);
     float sc[NQ][4], mxr[NQ];
     int it = 0;
@@ -838,11 +839,12 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
   int64_t s0 = 0, s1 = 0;
   int ws0 = 0, ws1 = 0;
   if (part < a.P) {
-    const int64_t nsets = (a.nq + kSet - 1) / kSet;
+    const SeqLen sl = seq_len(a, b);
+    const int64_t nsets = (sl.nq + kSet - 1) / kSet;
     s0 = nsets * part / a.P;
     s1 = nsets * (part + 1) / a.P;
-    const int64_t ns = a.n < a.S ? a.n : a.S;
-    const int64_t nw = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+    const int64_t ns = sl.n < a.S ? sl.n : a.S;
+    const int64_t nw = ns + (sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
     const int64_t nws = (nw + 7) / 8;
     ws0 = (int)(nws * part / a.P);
     ws1 = (int)(nws * (part + 1) / a.P);

@@ -56,6 +56,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   const int G = a.G, d = a.d;
   const float qk_scale = kLog2e / sqrtf((float)d);
   const int h0 = g * G;  // first query head of this group
+  const SeqLen sl = seq_len(a, b);   // this sequence's tokens and body tokens
 
   for (int i = tid; i < G * d; i += kThreads) {
     const int hh = i / d, j = i % d;
@@ -72,17 +73,17 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   }
 
   // token range of this workgroup
-  const int64_t nsets = (a.nq + kSet - 1) / kSet;
+  const int64_t nsets = (sl.nq + kSet - 1) / kSet;
   const bool window = (part == a.P);
   int64_t t_begin, t_end;  // body indices, or window list indices
-  const int64_t ns = a.n < a.S ? a.n : a.S;
+  const int64_t ns = sl.n < a.S ? sl.n : a.S;
   if (!window) {
     t_begin = nsets * part / a.P * kSet;
     t_end = nsets * (part + 1) / a.P * kSet;
-    if (t_end > a.nq) t_end = a.nq;
+    if (t_end > sl.nq) t_end = sl.nq;
   } else {
     t_begin = 0;
-    t_end = ns + (a.n - a.S - a.nq > 0 ? a.n - a.S - a.nq : 0);
+    t_end = ns + (sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
   }
   const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
   const uint8_t *kplane = a.codes_k + bg * a.kcode_bytes;
@@ -124,7 +125,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
             sm.pv[tt][1] = a.vpar_n == 2 ? (float)vpar[ti * a.vpar_n + 1] : 0.f;
           }
         } else {
-          const int64_t p = ti < ns ? ti : a.S + a.nq + (ti - ns);
+          const int64_t p = ti < ns ? ti : a.S + sl.nq + (ti - ns);
           const _Float16 *krow = p < a.S ? sink_k + p * d : ring_k + ((p - a.S) % (a.R + a.C)) * d;
           for (int hh = hg; hh < G; hh += kThreads / kSet) {
             float dot = 0.f;
@@ -173,7 +174,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
           else v = fmaf((float)code, sm.pv[t][0], sm.pv[t][1]);
         } else {
           const int64_t ti = t0 + t;
-          const int64_t p = ti < ns ? ti : a.S + a.nq + (ti - ns);
+          const int64_t p = ti < ns ? ti : a.S + sl.nq + (ti - ns);
           const _Float16 *vrow = p < a.S ? sink_v + p * d : ring_v + ((p - a.S) % (a.R + a.C)) * d;
           v = (float)vrow[j];
         }

@@ -30,16 +30,22 @@ struct Geom {
 
 int make_geom(const wushkv_cache *c, Geom *g);
 
-inline int64_t n_quantized(int64_t n, int S, int R, int C) {
+__host__ __device__ inline int64_t n_quantized(int64_t n, int S, int R, int C) {
   int64_t e = n - S - R;
   return e > 0 ? (int64_t)C * (e / C) : 0;
 }
+
+// Ragged batches: per-sequence token counts travel in the argument blocks (by value,
+// so a call allocates and copies nothing), for at most this many sequences.
+constexpr int kMaxRagged = 256;
 
 // Plain-old-data argument blocks handed to kernels by value.
 struct FlushArgs {
   int B, Hkv, d, S, R, C;
   int64_t n_before, n_new;
-  int64_t u0, u1;                 // body rows [u0, u1) flushed by this call
+  int64_t u0, u1;                 // body rows [u0, u1) flushed by this call (uniform batch)
+  int ragged;                     // nonzero: sequence b holds seq_nb[b] tokens before the call
+  int32_t seq_nb[kMaxRagged];
   int in_dtype;
   const void *k_new, *v_new;      // [B][Hkv][n_new][d]
   const _Float16 *tk;             // [Hkv][d][d]
@@ -56,6 +62,8 @@ struct FlushArgs {
 struct AppendArgs {
   int B, Hkv, d, S, R, C;
   int64_t n_before, n_new, q_after;
+  int ragged;                     // nonzero: sequence b holds seq_nb[b] tokens before the call
+  int32_t seq_nb[kMaxRagged];
   int in_dtype;
   const void *k_new, *v_new;
   _Float16 *sink_k, *sink_v, *ring_k, *ring_v;
@@ -71,7 +79,9 @@ struct QtArgs {
 
 struct DecodeArgs {
   int B, Hkv, Hq, G, d, S, R, C;
-  int64_t n, nq;                  // tokens attended, body tokens Q(n)
+  int64_t n, nq;                  // tokens attended, body tokens Q(n) (the largest, if ragged)
+  int ragged;                     // nonzero: sequence b attends seq_n[b] tokens
+  int32_t seq_n[kMaxRagged];
   int P;                          // body partitions
   const void *q;
   int q_dtype;
@@ -114,6 +124,16 @@ bool decode_fast_direct(const DecodeArgs &a);   // the fast kernel writes out it
 int decode_fast_resident_waves(int G, int bits_v);
 
 // Device helpers ------------------------------------------------------------
+
+// Tokens attended by sequence b and its body tokens Q(n).
+struct SeqLen {
+  int64_t n, nq;
+};
+__device__ __forceinline__ SeqLen seq_len(const DecodeArgs &a, int b) {
+  if (!a.ragged) return SeqLen{a.n, a.nq};
+  const int64_t n = a.seq_n[b];
+  return SeqLen{n, n_quantized(n, a.S, a.R, a.C)};
+}
 
 // Online-softmax merge of the partials of one (batch row, query head) row bh, channel
 // j: m* = max m_p, out = sum 2^{m_p - m*} o_p / sum 2^{m_p - m*} l_p over the partials

@@ -215,6 +215,37 @@ int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens,
                                   float *out, void *stream);
 
 /*
+ * Ragged batches (the serving case of the WUSH-KV digest, "takeaways": the cache sits in
+ * a serving stack where the sequences of a batch have different lengths).  Same cache
+ * layout; each sequence keeps its own token count, and the window policy applies to each
+ * sequence separately.  At most 256 sequences per cache (batch > 256 -> ERR_UNSUPPORTED).
+ *
+ * wushkv_append_flush_ragged: as wushkv_append_flush, with sequence b holding
+ * n_before[b] tokens (host array [batch]) before the call; every sequence receives the
+ * n_new tokens of its slice of k_new / v_new.  Errors as wushkv_append_flush
+ * (n_before[b] < 0 -> ERR_SHAPE, n_before[b] + n_new > capacity -> ERR_CAPACITY,
+ * n_before NULL -> ERR_NULL).
+ */
+int wushkv_append_flush_ragged(const wushkv_cache *c, const int64_t *n_before, int32_t n_new,
+                               const void *k_new, const void *v_new, int32_t in_dtype,
+                               const void *t_k_f16, void *stream);
+
+/*
+ * wushkv_decode_attention_ragged: the decode with sequence b attending its n_tokens[b]
+ * tokens (host array [batch], each in [1, capacity]); the workspace is sized by
+ * wushkv_decode_workspace_bytes for the longest sequence, and num_splits = 0 chooses
+ * the split count for it.  t_k_inv_t NULL: q_t is the caller's q~ (as
+ * wushkv_decode_attention); non-NULL: the decode forms q~ and writes it to q_t (as
+ * wushkv_decode_attention_fused).  Errors as wushkv_decode_attention; n_tokens NULL ->
+ * ERR_NULL.
+ */
+int wushkv_decode_attention_ragged(const wushkv_cache *c, const int64_t *n_tokens,
+                                   const void *q, int32_t q_dtype, const float *t_k_inv_t,
+                                   float *q_t, int32_t num_q_heads, int32_t num_splits,
+                                   void *workspace, size_t workspace_bytes,
+                                   float *out, void *stream);
+
+/*
  * Calibration statistics (WUSH-KV digest, "method key points": per KV head, the key
  * transform's Hessian is the sum of Q Q^T over the query heads that read the key and
  * the Gram matrices are the sums over the keys and values themselves; "takeaways": the

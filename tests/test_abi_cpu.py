@@ -183,3 +183,26 @@ def test_calib_validation_and_workspace(lib):
     assert f(ctypes.c_void_p(0x900002), W.DT_BF16, 2, 8, 64, 128, 1, p, n1, p, None) == W.ERR_ALIGN
     assert f(p, W.DT_BF16, 2, 8, 64, 128, 1, p, n1 - 1, p, None) == W.ERR_WORKSPACE
     assert f(p, W.DT_BF16, 2, 8, 64, 128, 1, None, n1, p, None) == W.ERR_WORKSPACE
+
+
+def test_ragged_validation(lib):
+    """Ragged append and decode check every sequence's count on the host."""
+    d = _spec(batch=3).desc()
+    _fake_planes(d)
+    kv = ctypes.c_void_p(0x900000)
+    arr = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    fa = lib.wushkv_append_flush_ragged
+    assert fa(ctypes.byref(d), None, 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    assert fa(ctypes.byref(d), arr(0, -1, 5), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_SHAPE
+    assert fa(ctypes.byref(d), arr(0, 8256, 5), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_CAPACITY
+    assert fa(ctypes.byref(d), arr(0, 3, 5), 0, kv, kv, W.DT_BF16, kv, None) == W.OK   # no-op
+    big = _spec(batch=300).desc()
+    _fake_planes(big)
+    assert fa(ctypes.byref(big), (ctypes.c_int64 * 300)(), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_UNSUPPORTED
+    fd = lib.wushkv_decode_attention_ragged
+    p = ctypes.c_void_p(0x900000)
+    ws = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    assert fd(ctypes.byref(d), None, p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_NULL
+    assert fd(ctypes.byref(d), arr(5, 0, 7), p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_SHAPE
+    assert fd(ctypes.byref(d), arr(5, 9000, 7), p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_CAPACITY
+    assert fd(ctypes.byref(d), arr(5, 8000, 7), p, W.DT_BF16, None, p, 32, 0, p, ws - 1, p, None) == W.ERR_WORKSPACE
