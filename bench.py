@@ -33,15 +33,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-DECODE_SOURCES = ("decode_fast.hip", "decode_generic.hip", "wushkv_internal.h")
 
 
-def kernel_source_hash(files=DECODE_SOURCES):
-    """Hash of the sources of the decode kernels, to tell whether a committed counter
-    summary was taken on the kernels as they are now."""
+# kernel sources each counter summary depends on
+COUNTER_SOURCES = {
+    "decode": ("decode_fast.hip", "decode_generic.hip", "wushkv_internal.h"),
+    "flush": ("append_flush.hip", "wushkv_internal.h"),
+    "calib": ("calib.hip", "wushkv_internal.h"),
+}
+
+
+def kernel_source_hash(files):
+    """Hash of the named kernel sources, to tell whether a committed counter summary
+    was taken on the kernels as they are now."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_kv_cache_amd", "csrc")
     for f in files:
+        h.update(f.encode())
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -78,7 +86,8 @@ def traffic_from_profile(name, kernels):
         rec = json.load(open(p))
     except (OSError, ValueError):
         return None
-    if rec.get("source_hash") != kernel_source_hash():
+    files = rec.get("source_files")
+    if not files or rec.get("source_hash") != kernel_source_hash(files):
         return None
     try:
         return sum(rec["kernels"][k]["bytes_per_dispatch"] for k in kernels)
@@ -288,7 +297,10 @@ def run_calib_leg(args):
     q = gen.calib_queries(w, 0, T, dev)
     res = {}
     total_bytes, total_flop, total_us = 0, 0, 0.0
-    for name, x, group in (("key_gram", k, 1), ("value_gram", v, 1), ("key_hessian", q, w.group)):
+    legs = [(name, x, group) for name, x, group in (("key_gram", k, 1), ("value_gram", v, 1),
+                                                     ("key_hessian", q, w.group))
+            if name in args.calib_legs.split(",")]
+    for name, x, group in legs:
         B, H, _, d = x.shape
         ws = W.calib_workspace(B, H, T, d, group, dev)
         out = torch.empty((H // group, d, d), dtype=torch.float32, device=dev)
@@ -318,6 +330,15 @@ def run_calib_leg(args):
     res["layer"] = {"us": round(total_us, 2), "GB_per_s": round(total_bytes / (total_us * 1e-6) / 1e9, 1),
                     "frac_hbm": round(total_bytes / (total_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                     "TFLOP_per_s": round(total_flop / (total_us * 1e-6) / 1e12, 1)}
+    kg = res.get("key_gram")
+    if kg is not None:
+        achieved = kg["bytes"] / (kg["us_per_call"] * 1e-6) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": traffic_from_profile("calib_key_gram_counters.json",
+                                                           ["calib_partial_kernel<true>", "calib_reduce_kernel"]),
+                           "kernel": "calib_partial_kernel<true> + calib_reduce_kernel on the key Gram (bf16 "
+                                     "keys, group 1): bytes = keys read + fp32 output written, per call"}
     del k, v, q
     torch.cuda.empty_cache()
     return res
@@ -424,6 +445,8 @@ def main():
     ap.add_argument("--flush-bits", type=str, default="", help="comma-separated bit widths of the flush leg")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode leg")
     ap.add_argument("--no-calib", action="store_true", help="skip the calibration-statistics leg")
+    ap.add_argument("--calib-legs", type=str, default="key_gram,value_gram,key_hessian",
+                    help="comma-separated sums the calibration leg times")
     ap.add_argument("--settle-s", type=float, default=0.3,
                     help="seconds of untimed decode-only launches before the warm-up steps")
     ap.add_argument("--copy-check", type=int, default=0, metavar="MIB",
@@ -432,10 +455,13 @@ def main():
     ap.add_argument("--counters-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU work: summarize two rocprofv3 counter_collection.csv files (runs made with "
                          "--copy-check MIB) as JSON on stdout")
+    ap.add_argument("--counters-kernels", choices=sorted(COUNTER_SOURCES), default="decode",
+                    help="which kernels' sources the counter summary is tied to")
     args = ap.parse_args()
     if args.counters_summary:
         rec = summarize_counters(*args.counters_summary, args.copy_check or 1024)
-        rec["source_hash"] = kernel_source_hash()
+        rec["source_files"] = list(COUNTER_SOURCES[args.counters_kernels])
+        rec["source_hash"] = kernel_source_hash(rec["source_files"])
         print(json.dumps(rec, indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -457,8 +483,12 @@ def main():
         del src, dst
 
     if args.no_decode:
-        fl = run_flush_leg(args)
-        print(json.dumps({"flush": {f"{b}bit": r for b, r in fl.items()}}), flush=True)
+        rec = {}
+        if not args.no_flush:
+            rec["flush"] = {f"{b}bit": r for b, r in run_flush_leg(args).items()}
+        if not args.no_calib:
+            rec["calibration"] = run_calib_leg(args)
+        print(json.dumps(rec), flush=True)
         return
     dl = run_decode_leg(args)
     w = dl["workload"]
