@@ -13,9 +13,11 @@
 // one block read serves as A of tile (I, .) and B of tile (., I).  S is symmetric: the
 // 10 tiles with I <= J of the 4 x 4 tiling at d = 128 are formed, the reduction mirrors them.
 //
-// Work: a workgroup takes one group (its heads) and a block of batch rows, streams their
-// tokens in steps of 64 (loaded two steps ahead into registers) through LDS, transposed to
-// channel-major on the way in (16-bit stores), and writes its 10 tiles as one partial; a second kernel sums a group's
+// Work: a workgroup takes one group (its heads) and a block of batch rows (about one
+// resident round of workgroups in all), streams their tokens in steps of 64 (loaded two
+// steps ahead into registers) through LDS, transposed to channel-major on the way in
+// (16-bit stores); each of its four waves forms all 10 tiles over its own 16 tokens of a
+// step, and the waves' sums are added into one partial.  A second kernel sums a group's
 // partials in a fixed order (the result does not depend on timing) and writes the full
 // matrix.
 #include "wushkv_internal.h"
@@ -52,14 +54,14 @@ __device__ __forceinline__ int lds_col(int c, int t) { return (((t >> 3) ^ ((c >
 // One step of 64 rows, loaded contiguously: 16-byte chunk i of the step's 16 KB goes to
 // thread i % 256 (row i / 16, channels 8 (i % 16) .. + 7), so one load instruction reads
 // four whole rows.  The loads are unconditional (a row past the end re-reads the last
-// row and is zeroed at the store), so the compiler counts the loads in flight exactly
-// instead of draining them.
+// row, which the cache still holds, and is zeroed at the store), so the compiler counts
+// the loads in flight exactly instead of draining them.
 __device__ __forceinline__ void load_step(const uint8_t *rows, int64_t t0, int64_t T, int tid, u32x4 (&r)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = tid + kCalibThreads * i;
     const int64_t t = t0 + c / 16;
-    r[i] = __builtin_nontemporal_load((const u32x4 *)(rows + (size_t)(t < T ? t : T - 1) * (kCD * 2)) + (c % 16));
+    r[i] = *((const u32x4 *)(rows + (size_t)(t < T ? t : T - 1) * (kCD * 2)) + (c % 16));
   }
 }
 
@@ -96,18 +98,10 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4 &a, const u32x4 &b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// The MFMAs of wave WV on one 16-token chunk: tiles WV, WV + 4, WV + 8 (those below 10),
-// with compile-time operand indices (the operands stay in registers).
-template <bool BF16, int WV>
-__device__ __forceinline__ void wave_tiles(f32x16 (&acc)[3], const u32x4 (&op)[4]) {
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    if (WV + 4 * k < kTiles) acc[k] = mfma32<BF16>(op[tile_i(WV + 4 * k)], op[tile_j(WV + 4 * k)], acc[k]);
-  }
-}
-
 // Grid (batch blocks, groups): the workgroup sums the rows of its group's heads over its
-// batch rows.  Wave w owns tiles w, w + 4, w + 8 (those below 10).
+// batch rows.  Wave w takes tokens 16 w .. 16 w + 15 of every step for all 10 tiles, so
+// each staged element is read from LDS once; the four waves' sums are added in wave
+// order at the end.
 template <bool BF16>
 __global__ void __launch_bounds__(kCalibThreads, 2) calib_partial_kernel(CalibArgs a) {
   __shared__ __align__(16) uint16_t stage[2][kCD * kPitch];
@@ -124,10 +118,9 @@ __global__ void __launch_bounds__(kCalibThreads, 2) calib_partial_kernel(CalibAr
     const int b = b0 + (int)(hb / a.group), h = g * a.group + (int)(hb % a.group);
     return (const uint8_t *)a.x + ((size_t)b * a.H + h) * (size_t)a.T * (kCD * 2);
   };
-  constexpr int NT = 3;
-  f32x16 acc[NT];
+  f32x16 acc[kTiles];
 #pragma unroll
-  for (int k = 0; k < NT; ++k)
+  for (int k = 0; k < kTiles; ++k)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[k][v] = 0.f;
 
@@ -145,28 +138,21 @@ __global__ void __launch_bounds__(kCalibThreads, 2) calib_partial_kernel(CalibAr
     store_step(stage[0], tid, 0, a.T, ra);
   }
   lds_barrier();
-  // operand of lane l for channel block I and 16-token chunk kc: channel 32 I + l % 32,
-  // tokens 16 kc + 8 (l / 32) .. + 7
-  const int orow = lane & 31, ocol = 8 * (lane >> 5);
+  // operand of lane l for channel block I: channel 32 I + l % 32, tokens
+  // 16 wave + 8 (l / 32) .. + 7 of the step
+  const int orow = lane & 31, ocol = 16 * wave + 8 * (lane >> 5);
   auto step = [&](int64_t s, u32x4 (&rload)[4], u32x4 (&rstore)[4]) {
     const int64_t sl = clamp(s + 2);
     load_step(rows_of(sl), t0_of(sl), a.T, tid, rload);
     const uint16_t *st = stage[s & 1];
+    u32x4 op[4];
 #pragma unroll
-    for (int kc = 0; kc < kStep / 16; ++kc) {
-      u32x4 op[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        const int c = 32 * I + orow;
-        op[I] = *(const u32x4 *)(st + c * kPitch + lds_col(c, 16 * kc + ocol));
-      }
-      switch (wave) {   // wave-uniform
-        case 0: wave_tiles<BF16, 0>(acc, op); break;
-        case 1: wave_tiles<BF16, 1>(acc, op); break;
-        case 2: wave_tiles<BF16, 2>(acc, op); break;
-        default: wave_tiles<BF16, 3>(acc, op); break;
-      }
+    for (int I = 0; I < 4; ++I) {
+      const int c = 32 * I + orow;
+      op[I] = *(const u32x4 *)(st + c * kPitch + lds_col(c, ocol));
     }
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) acc[t] = mfma32<BF16>(op[tile_i(t)], op[tile_j(t)], acc[t]);
     if (s + 1 < nsteps) store_step(stage[(s + 1) & 1], tid, t0_of(s + 1), a.T, rstore);
     lds_barrier();
   };
@@ -174,43 +160,71 @@ __global__ void __launch_bounds__(kCalibThreads, 2) calib_partial_kernel(CalibAr
     step(s, ra, rb);                       // loads step s + 2 into ra, stores step s + 1 from rb
     if (s + 1 < nsteps) step(s + 1, rb, ra);
   }
-  // partial (g, bc), tile-major 32 x 32 blocks
+  // partial (g, bc): the 10 tiles, each 1024 floats in the MFMA's D order (item v of
+  // lane l at v * 64 + l).  The waves' sums are added in wave order through LDS, two
+  // tiles at a time (the last step's barrier has retired every operand read).
+  float *red = reinterpret_cast<float *>(&stage[0][0]);   // [2 tiles][4 waves][1024]
   float *part = a.partials + ((size_t)g * a.nparts + bc) * (kTiles * 1024);
 #pragma unroll
-  for (int k = 0; k < NT; ++k) {
-    const int t = wave + 4 * k;
-    if (t >= kTiles) continue;
-    // D layout of the 32 x 32 MFMA: item v of lane l is row 8 (v / 4) + 4 (l / 32) + v % 4,
-    // column l % 32
+  for (int t0 = 0; t0 < kTiles; t0 += 2) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int i = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3), j = lane & 31;
-      part[t * 1024 + i * 32 + j] = acc[k][v];
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((tt * 4 + wave) * 16 + v) * 64 + lane] = acc[t0 + tt][v];
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int e = 4 * tid + 1024 * k;                   // 4 consecutive elements of tile t0 + k
+      const float4 *r = reinterpret_cast<const float4 *>(red + k * 4096 + (e & 1023));
+      const float4 sum = ((r[0] + r[256]) + r[512]) + r[768];
+      *reinterpret_cast<float4 *>(part + (t0 + k) * 1024 + (e & 1023)) = sum;
     }
+    lds_barrier();
   }
 }
 
-// Grid (groups, tiles, 4): one thread per element of a tile; the group's partials are
-// summed in index order and the sum written to the full symmetric matrix (tile (I, J)
-// and its mirror).
+// Grid (groups, tiles, 4): a workgroup sums 256 elements of one tile over the group's
+// partials.  Wave q takes 4 consecutive elements per lane over the q-th quarter of the
+// partials, in index order; the quarters are then added in order q = 0, 1, 2, 3 (the
+// result does not depend on timing) and written to the full symmetric matrix (tile
+// (I, J) and its mirror).
 __global__ void __launch_bounds__(kCalibThreads) calib_reduce_kernel(CalibArgs a) {
-  const int g = blockIdx.x, t = blockIdx.y, e = blockIdx.z * kCalibThreads + threadIdx.x;
+  __shared__ float4 quarter[3][64];
+  const int g = blockIdx.x, t = blockIdx.y, lane = threadIdx.x & 63;
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e4 = blockIdx.z * 64 + lane;            // float4 index within the tile
+  const int per = (a.nparts + 3) / 4;
+  const int p0 = q * per, p1 = p0 + per < a.nparts ? p0 + per : a.nparts;
+  const float4 *part = (const float4 *)(a.partials + (size_t)g * a.nparts * (kTiles * 1024) + t * 1024) + e4;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int p = p0; p < p1; ++p) sum += part[(size_t)p * (kTiles * 256)];
+  if (q > 0) quarter[q - 1][lane] = sum;
+  __syncthreads();
+  if (q != 0) return;
+  sum = ((sum + quarter[0][lane]) + quarter[1][lane]) + quarter[2][lane];
+  // element 4 e4 of the tile in D order: item v = e / 64 of lane l = e % 64 is row
+  // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32 (the four elements are columns j .. j + 3)
   const int I = tile_i(t), J = tile_j(t);
-  const float *part = a.partials + (size_t)g * a.nparts * (kTiles * 1024) + t * 1024 + e;
-  float sum = 0.f;
-#pragma unroll 8
-  for (int p = 0; p < a.nparts; ++p) sum += part[(size_t)p * (kTiles * 1024)];
   float *out = a.out + (size_t)g * kCD * kCD;
-  const int i = 32 * I + e / 32, j = 32 * J + e % 32;
-  out[i * kCD + j] = sum;
-  if (I != J) out[j * kCD + i] = sum;
+  const int v = (4 * e4) >> 6, l = (4 * e4) & 63;
+  const int i = 32 * I + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3), j = 32 * J + (l & 31);
+  *(float4 *)(out + i * kCD + j) = sum;
+  if (I != J) {
+    out[(j + 0) * kCD + i] = sum.x;
+    out[(j + 1) * kCD + i] = sum.y;
+    out[(j + 2) * kCD + i] = sum.z;
+    out[(j + 3) * kCD + i] = sum.w;
+  }
 }
 
 }  // namespace
 
-// Batch rows per workgroup: enough workgroups for about two rounds of two per CU.
+// Batch rows per workgroup: about one round of two workgroups per CU (256 CUs), so
+// that each workgroup streams many steps and the group has few partials to sum.
+constexpr int kCalibTargetBlocks = 512;
 int calib_batch_per_wg(int B, int groups) {
-  const int want_blocks = (1024 + groups - 1) / groups;
+  const int want_blocks = (kCalibTargetBlocks + groups - 1) / groups;
   const int blocks = want_blocks < B ? want_blocks : B;
   return (B + blocks - 1) / blocks;
 }
