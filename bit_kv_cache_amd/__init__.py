@@ -21,7 +21,7 @@ EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "
            "wushkv_decode_num_splits", "wushkv_decode_workspace_bytes", "wushkv_append_flush",
            "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused",
            "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
-           "wushkv_decode_attention_ragged")
+           "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device")
 
 
 class WushKVError(RuntimeError):
@@ -70,6 +70,9 @@ def lib():
             "wushkv_decode_attention_ragged": (ctypes.c_int, [P, ctypes.POINTER(i64), vp, i32, vp, vp, i32, i32, vp, sz,
                                                               vp, vp]),
             "wushkv_calib_workspace_bytes": (sz, [i32, i32, i64, i32, i32]),
+            "wushkv_append_flush_device": (ctypes.c_int, [P, vp, i32, vp, vp, i32, vp, vp]),
+            "wushkv_decode_attention_device": (ctypes.c_int, [P, vp, i64, vp, i32, vp, vp, i32, i32, vp, sz, vp,
+                                                              vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name, None)   # an older build may lack later entry points
@@ -326,4 +329,49 @@ def decode_attention_ragged(cache: KVCache, q, q_t=None, t_inv_t=None, n_tokens=
                                                 _dtype_code(q), None if t_inv_t is None else _ptr(t_inv_t),
                                                 _ptr(q_t), Hq, num_splits, _ptr(workspace), workspace.numel(),
                                                 _ptr(out), _stream(stream, q.device)), "decode_attention_ragged")
+    return out, q_t
+
+
+def _device_counts(seq_n, batch, device):
+    import torch
+    if seq_n.dtype != torch.int32 or seq_n.shape != (batch,) or seq_n.device != device:
+        raise ValueError("seq_n must be an int32 tensor [batch] on the cache's device")
+    return _ptr(seq_n)
+
+
+def append_flush_device(cache: KVCache, seq_n, k_new, v_new, t_k16, stream=None):
+    """Append [B, Hkv, n_new, d] keys/values with the token counts in device memory:
+    sequence b holds seq_n[b] tokens (int32 tensor [B] on the GPU), and the call adds
+    n_new to each count on the stream.  Nothing here reads the counts on the host, so
+    the call can be recorded into a CUDA/HIP graph and replayed as later steps.
+    cache.seq_n (the host-side view) is not updated."""
+    import torch
+    if k_new.dtype != v_new.dtype or t_k16.dtype != torch.float16:
+        raise ValueError("k_new/v_new must share a dtype and t_k16 must be float16")
+    _check(lib().wushkv_append_flush_device(ctypes.byref(cache.desc), _device_counts(seq_n, cache.spec.batch,
+                                                                                     k_new.device),
+                                            k_new.shape[2], _ptr(k_new), _ptr(v_new), _dtype_code(k_new),
+                                            _ptr(t_k16), _stream(stream, k_new.device)), "append_flush_device")
+
+
+def decode_attention_device(cache: KVCache, seq_n, max_tokens, q, t_inv_t=None, q_t=None, num_splits=0,
+                            workspace=None, out=None, stream=None):
+    """GQA decode with sequence b attending seq_n[b] tokens, read on the device
+    (int32 tensor [B]); max_tokens bounds the counts and sizes the split count and
+    workspace.  With t_inv_t the decode forms q~ itself into q_t.  -> (out, q_t)."""
+    import torch
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(cache, max_tokens, Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if q_t is None:
+        if t_inv_t is None:
+            raise ValueError("decode_attention_device needs q_t or t_inv_t")
+        q_t = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention_device(ctypes.byref(cache.desc), _device_counts(seq_n, B, q.device),
+                                                int(max_tokens), _ptr(q), _dtype_code(q),
+                                                None if t_inv_t is None else _ptr(t_inv_t), _ptr(q_t), Hq,
+                                                num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
+                                                _stream(stream, q.device)), "decode_attention_device")
     return out, q_t

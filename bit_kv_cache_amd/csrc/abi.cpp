@@ -174,14 +174,19 @@ size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, in
 
 namespace {
 
-// Append + flush for a uniform batch (seq_nb == nullptr: every sequence holds
-// n_before tokens) or a ragged one (sequence b holds seq_nb[b]).
-int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *seq_nb, int32_t n_new,
-                      const void *k_new, const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
+// Append + flush for a uniform batch (seq_nb == dev_n == nullptr: every sequence holds
+// n_before tokens), a ragged one (sequence b holds seq_nb[b]) or one whose counts live
+// in device memory (dev_n[b]; the call then advances them by n_new).
+int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *seq_nb, int32_t *dev_n,
+                      int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype, const void *t_k_f16,
+                      void *stream) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
-  if (seq_nb) {
+  if (dev_n) {
+    if (((uintptr_t)dev_n & 3u) != 0) return WUSHKV_ERR_ALIGN;
+    n_before = 0;   // the counts are checked by the kernels
+  } else if (seq_nb) {
     if (g.B > kMaxRagged) return WUSHKV_ERR_UNSUPPORTED;
     n_before = 0;
     for (int b = 0; b < g.B; ++b) {
@@ -199,7 +204,9 @@ int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *se
   int64_t n_after = n_before + n_new;
   int64_t qb = n_quantized(n_before, g.S, g.R, g.C), qa = n_quantized(n_after, g.S, g.R, g.C);
   bool flush = qa > qb;
-  if (seq_nb) {
+  if (dev_n) {
+    flush = true;   // whether one is due is decided per sequence on the device
+  } else if (seq_nb) {
     flush = false;
     for (int b = 0; b < g.B; ++b)
       flush |= n_quantized(seq_nb[b] + n_new, g.S, g.R, g.C) > n_quantized(seq_nb[b], g.S, g.R, g.C);
@@ -221,8 +228,12 @@ int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *se
     f.bits_k = g.bits_k; f.bits_v = g.bits_v; f.quant_k = g.quant_k; f.quant_v = g.quant_v;
     f.kpar_n = g.kpar_n; f.vpar_n = g.vpar_n; f.clip = g.clip;
     f.lo_i = g.lo_i; f.hi_i = g.hi_i; f.lo_t = g.lo_t; f.hi_t = g.hi_t; f.need_lo = g.need_lo; f.need_hi = g.need_hi;
-    if (seq_nb) {
-      f.ragged = 1;
+    f.cap = g.cap;
+    if (dev_n) {
+      f.ragged = kRaggedDevice;
+      f.dev_n = dev_n;
+    } else if (seq_nb) {
+      f.ragged = kRaggedHost;
       for (int b = 0; b < g.B; ++b) f.seq_nb[b] = (int32_t)seq_nb[b];
     }
     if (launch_flush(f, s) != hipSuccess) return WUSHKV_ERR_HIP;
@@ -235,11 +246,16 @@ int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *se
   a.sink_k = (_Float16 *)c->sink_k; a.sink_v = (_Float16 *)c->sink_v;
   a.ring_k = (_Float16 *)c->ring_k; a.ring_v = (_Float16 *)c->ring_v;
   a.sink_bytes = g.sink_bytes; a.ring_bytes = g.ring_bytes;
-  if (seq_nb) {
-    a.ragged = 1;
+  a.cap = g.cap;
+  if (dev_n) {
+    a.ragged = kRaggedDevice;
+    a.dev_n = dev_n;
+  } else if (seq_nb) {
+    a.ragged = kRaggedHost;
     for (int b = 0; b < g.B; ++b) a.seq_nb[b] = (int32_t)seq_nb[b];
   }
   if (launch_append(a, s) != hipSuccess) return WUSHKV_ERR_HIP;
+  if (dev_n && launch_advance(dev_n, g.B, n_new, g.cap, s) != hipSuccess) return WUSHKV_ERR_HIP;
   return hip_status();
 }
 
@@ -249,13 +265,19 @@ extern "C" {
 
 int wushkv_append_flush(const wushkv_cache *c, int64_t n_before, int32_t n_new, const void *k_new,
                         const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
-  return append_flush_impl(c, n_before, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+  return append_flush_impl(c, n_before, nullptr, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
 }
 
 int wushkv_append_flush_ragged(const wushkv_cache *c, const int64_t *n_before, int32_t n_new, const void *k_new,
                                const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
   if (!n_before) return WUSHKV_ERR_NULL;
-  return append_flush_impl(c, 0, n_before, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+  return append_flush_impl(c, 0, n_before, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+}
+
+int wushkv_append_flush_device(const wushkv_cache *c, int32_t *seq_n, int32_t n_new, const void *k_new,
+                               const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
+  if (!seq_n) return WUSHKV_ERR_NULL;
+  return append_flush_impl(c, 0, nullptr, seq_n, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
 }
 
 int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtype, int32_t batch,
@@ -308,13 +330,16 @@ int wushkv_calib_stats(const void *x, int32_t dtype, int32_t batch, int32_t num_
 namespace {
 
 // Decode with q~ given (tinvt == nullptr) or formed from q and T^{-T} into q_t.
-int decode_impl(const wushkv_cache *c, int64_t n_tokens, const int64_t *seq_n, const void *q, int32_t q_dtype,
-                float *q_t, const float *tinvt, int32_t num_q_heads, int32_t num_splits, void *workspace,
-                size_t workspace_bytes, float *out, void *stream) {
+// With dev_n, the counts are read on the device and n_tokens bounds them.
+int decode_impl(const wushkv_cache *c, int64_t n_tokens, const int64_t *seq_n, const int32_t *dev_n,
+                const void *q, int32_t q_dtype, float *q_t, const float *tinvt, int32_t num_q_heads,
+                int32_t num_splits, void *workspace, size_t workspace_bytes, float *out, void *stream) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
-  if (seq_n) {   // ragged: the checks, split count and workspace follow the longest sequence
+  if (dev_n) {
+    if (((uintptr_t)dev_n & 3u) != 0) return WUSHKV_ERR_ALIGN;
+  } else if (seq_n) {   // ragged: the checks, split count and workspace follow the longest sequence
     if (g.B > kMaxRagged) return WUSHKV_ERR_UNSUPPORTED;
     n_tokens = 0;
     for (int b = 0; b < g.B; ++b) {
@@ -340,8 +365,12 @@ int decode_impl(const wushkv_cache *c, int64_t n_tokens, const int64_t *seq_n, c
   memset(&a, 0, sizeof a);
   a.B = g.B; a.Hkv = g.Hkv; a.Hq = num_q_heads; a.G = G; a.d = g.d; a.S = g.S; a.R = g.R; a.C = g.C;
   a.n = n_tokens; a.nq = n_quantized(n_tokens, g.S, g.R, g.C); a.P = P;
-  if (seq_n) {
-    a.ragged = 1;
+  if (dev_n) {
+    a.ragged = kRaggedDevice;
+    a.dev_n = dev_n;
+    a.max_n = n_tokens;
+  } else if (seq_n) {
+    a.ragged = kRaggedHost;
     for (int b = 0; b < g.B; ++b) a.seq_n[b] = (int32_t)seq_n[b];
   }
   a.q = q; a.q_dtype = q_dtype; a.qt = q_t;
@@ -373,15 +402,15 @@ extern "C" {
 int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
                             const float *q_t, int32_t num_q_heads, int32_t num_splits, void *workspace,
                             size_t workspace_bytes, float *out, void *stream) {
-  return decode_impl(c, n_tokens, nullptr, q, q_dtype, const_cast<float *>(q_t), nullptr, num_q_heads, num_splits,
-                     workspace, workspace_bytes, out, stream);
+  return decode_impl(c, n_tokens, nullptr, nullptr, q, q_dtype, const_cast<float *>(q_t), nullptr, num_q_heads,
+                     num_splits, workspace, workspace_bytes, out, stream);
 }
 
 int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
                                   const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
                                   void *workspace, size_t workspace_bytes, float *out, void *stream) {
   if (!t_k_inv_t) return WUSHKV_ERR_NULL;
-  return decode_impl(c, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+  return decode_impl(c, n_tokens, nullptr, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
 }
 
@@ -389,7 +418,16 @@ int wushkv_decode_attention_ragged(const wushkv_cache *c, const int64_t *n_token
                                    const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
                                    void *workspace, size_t workspace_bytes, float *out, void *stream) {
   if (!n_tokens) return WUSHKV_ERR_NULL;
-  return decode_impl(c, 0, n_tokens, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+  return decode_impl(c, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+                     workspace_bytes, out, stream);
+}
+
+int wushkv_decode_attention_device(const wushkv_cache *c, const int32_t *seq_n, int64_t max_tokens, const void *q,
+                                   int32_t q_dtype, const float *t_k_inv_t, float *q_t, int32_t num_q_heads,
+                                   int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                                   void *stream) {
+  if (!seq_n) return WUSHKV_ERR_NULL;
+  return decode_impl(c, max_tokens, nullptr, seq_n, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
 }
 

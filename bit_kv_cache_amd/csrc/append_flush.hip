@@ -31,7 +31,8 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   if (idx >= a.n_new * groups) return;
   const int64_t t = idx / groups;
   const int j0 = (int)(idx % groups) * 8;
-  const int64_t n_before = a.ragged ? a.seq_nb[b] : a.n_before;
+  const int64_t n_before = seq_before(a, b);
+  if (n_before < 0) return;
   const int64_t q_after = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.q_after;
   const int64_t p = n_before + t;
   _Float16 *dk, *dv;
@@ -377,14 +378,15 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
   // this sequence's rows before the call and its flushed body rows [u0, u1)
-  const int64_t n_before = a.ragged ? a.seq_nb[b] : a.n_before;
+  const int64_t n_before = seq_before(a, b);
+  if (n_before < 0) return;   // (device counts) out of range: the sequence is left alone
   const int64_t u0 = a.ragged ? n_quantized(n_before, a.S, a.R, a.C) : a.u0;
   const int64_t u1 = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.u1;
   const int64_t s_first = u0 / kSet, s_end = (u1 + kSet - 1) / kSet;
   const int64_t nsteps = u1 > u0 ? (s_end - s_first + 1) / 2 : 0;
   const int64_t st0 = (int64_t)blockIdx.x * steps_per_wg;
   const int64_t st1 = st0 + steps_per_wg < nsteps ? st0 + steps_per_wg : nsteps;
-  if (st0 >= st1) return;   // (ragged batch) this sequence needs fewer steps
+  if (st0 >= st1) return;   // (ragged batch) this sequence needs fewer steps, or none
 
   // Each tile's raw rows are refilled with the next step's as soon as they have been
   // converted, so every load has about a step of work to hide behind.
@@ -741,6 +743,20 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Device token counts: after a call's flush and append, each in-range count grows by
+// n_new (the same range test as seq_before, so a skipped sequence keeps its count).
+__global__ void advance_kernel(int32_t *dev_n, int B, int n_new, int64_t cap) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int64_t n = dev_n[b];
+  if (n >= 0 && n + n_new <= cap) dev_n[b] = (int32_t)(n + n_new);
+}
+
+hipError_t launch_advance(int32_t *dev_n, int B, int n_new, int64_t cap, hipStream_t s) {
+  hipLaunchKernelGGL(advance_kernel, dim3((B + kThreads - 1) / kThreads), dim3(kThreads), 0, s, dev_n, B, n_new, cap);
+  return hipGetLastError();
+}
+
 // Steps (128 body rows) of a flush of body rows [u0, u1).
 static int64_t flush_steps(int64_t u0, int64_t u1) {
   if (u1 <= u0) return 0;
@@ -750,7 +766,12 @@ static int64_t flush_steps(int64_t u0, int64_t u1) {
 
 hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   int64_t steps = 0;   // the most any sequence needs; workgroups past a sequence's own return
-  if (a.ragged) {
+  if (a.ragged == kRaggedDevice) {
+    // counts unknown here: the most n_new tokens can make due, n_new + C - 1 body rows
+    // starting anywhere in a 64-row set
+    const int64_t sets = (a.n_new + a.C - 1 + kSet - 1) / kSet + 1;
+    steps = (sets + 1) / 2;
+  } else if (a.ragged) {
     for (int b = 0; b < a.B; ++b) {
       const int64_t nb = a.seq_nb[b];
       const int64_t st = flush_steps(n_quantized(nb, a.S, a.R, a.C), n_quantized(nb + a.n_new, a.S, a.R, a.C));

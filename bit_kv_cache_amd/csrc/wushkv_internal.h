@@ -36,16 +36,21 @@ __host__ __device__ inline int64_t n_quantized(int64_t n, int S, int R, int C) {
 }
 
 // Ragged batches: per-sequence token counts travel in the argument blocks (by value,
-// so a call allocates and copies nothing), for at most this many sequences.
+// so a call allocates and copies nothing), for at most this many sequences.  Or they
+// live in device memory (int32 per sequence), read by the kernels themselves, so that
+// a captured call sequence does not bake them in.
 constexpr int kMaxRagged = 256;
+enum { kUniform = 0, kRaggedHost = 1, kRaggedDevice = 2 };
 
 // Plain-old-data argument blocks handed to kernels by value.
 struct FlushArgs {
   int B, Hkv, d, S, R, C;
   int64_t n_before, n_new;
   int64_t u0, u1;                 // body rows [u0, u1) flushed by this call (uniform batch)
-  int ragged;                     // nonzero: sequence b holds seq_nb[b] tokens before the call
-  int32_t seq_nb[kMaxRagged];
+  int ragged;                     // kRaggedHost: sequence b holds seq_nb[b] tokens before the
+  int32_t seq_nb[kMaxRagged];     // call; kRaggedDevice: dev_n[b] (device memory)
+  const int32_t *dev_n;
+  int64_t cap;                    // capacity (device counts are checked against it)
   int in_dtype;
   const void *k_new, *v_new;      // [B][Hkv][n_new][d]
   const _Float16 *tk;             // [Hkv][d][d]
@@ -62,8 +67,10 @@ struct FlushArgs {
 struct AppendArgs {
   int B, Hkv, d, S, R, C;
   int64_t n_before, n_new, q_after;
-  int ragged;                     // nonzero: sequence b holds seq_nb[b] tokens before the call
+  int ragged;                     // as FlushArgs
   int32_t seq_nb[kMaxRagged];
+  const int32_t *dev_n;
+  int64_t cap;
   int in_dtype;
   const void *k_new, *v_new;
   _Float16 *sink_k, *sink_v, *ring_k, *ring_v;
@@ -80,8 +87,10 @@ struct QtArgs {
 struct DecodeArgs {
   int B, Hkv, Hq, G, d, S, R, C;
   int64_t n, nq;                  // tokens attended, body tokens Q(n) (the largest, if ragged)
-  int ragged;                     // nonzero: sequence b attends seq_n[b] tokens
-  int32_t seq_n[kMaxRagged];
+  int ragged;                     // kRaggedHost: sequence b attends seq_n[b] tokens;
+  int32_t seq_n[kMaxRagged];      // kRaggedDevice: dev_n[b] (device memory), at most max_n
+  const int32_t *dev_n;
+  int64_t max_n;
   int P;                          // body partitions
   const void *q;
   int q_dtype;
@@ -110,6 +119,7 @@ struct CalibArgs {
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_advance(int32_t *dev_n, int B, int n_new, int64_t cap, hipStream_t s);
 hipError_t launch_calib(const CalibArgs &a, hipStream_t s);
 int calib_batch_per_wg(int B, int groups);
 size_t calib_partial_floats(int B, int H, int group);
@@ -129,10 +139,29 @@ int decode_fast_resident_waves(int G, int bits_v);
 struct SeqLen {
   int64_t n, nq;
 };
+// A device count outside [1, max_n] attends nothing, which makes the sequence's output
+// rows NaN (an empty softmax) without touching its cache.
 __device__ __forceinline__ SeqLen seq_len(const DecodeArgs &a, int b) {
-  if (!a.ragged) return SeqLen{a.n, a.nq};
-  const int64_t n = a.seq_n[b];
+  if (a.ragged == kUniform) return SeqLen{a.n, a.nq};
+  int64_t n;
+  if (a.ragged == kRaggedDevice) {
+    n = a.dev_n[b];
+    if (n < 1 || n > a.max_n) n = 0;
+  } else {
+    n = a.seq_n[b];
+  }
   return SeqLen{n, n_quantized(n, a.S, a.R, a.C)};
+}
+
+// Tokens sequence b holds before an append / flush call; -1 for a device count outside
+// [0, capacity - n_new] (the call then leaves that sequence alone).
+template <class Args>
+__device__ __forceinline__ int64_t seq_before(const Args &a, int b) {
+  if (a.ragged == kRaggedDevice) {
+    const int64_t n = a.dev_n[b];
+    return n >= 0 && n + a.n_new <= a.cap ? n : -1;
+  }
+  return a.ragged == kRaggedHost ? a.seq_nb[b] : a.n_before;
 }
 
 // Online-softmax merge of the partials of one (batch row, query head) row bh, channel

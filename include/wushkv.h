@@ -246,6 +246,37 @@ int wushkv_decode_attention_ragged(const wushkv_cache *c, const int64_t *n_token
                                    float *out, void *stream);
 
 /*
+ * Device-resident token counts, for serving loops captured as a HIP graph (the same
+ * serving case; a captured launch keeps the arguments it was recorded with, so counts
+ * that change every step must come from memory).  seq_n is caller-owned device memory,
+ * int32 [batch], 4-byte aligned; the kernels read it, and nothing else in the call
+ * depends on its values, so one recorded append + decode replays as the next step.
+ *
+ * wushkv_append_flush_device: as wushkv_append_flush_ragged with n_before[b] = seq_n[b];
+ * after its kernels (same stream) the call adds n_new to every seq_n[b].  The flush
+ * kernel is always launched, sized for the most that n_new tokens can make due, and
+ * sequences with nothing due return at once.  A count outside [0, capacity - n_new]
+ * leaves that sequence, and its count, unchanged.  Errors: as wushkv_append_flush for
+ * the host-side checks (n_new > capacity -> ERR_CAPACITY), seq_n NULL -> ERR_NULL,
+ * seq_n not 4-byte aligned -> ERR_ALIGN.
+ */
+int wushkv_append_flush_device(const wushkv_cache *c, int32_t *seq_n, int32_t n_new, const void *k_new,
+                               const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream);
+
+/*
+ * wushkv_decode_attention_device: the decode with sequence b attending seq_n[b] tokens,
+ * read on the device.  max_tokens (host, in [1, capacity]) bounds every count: the split
+ * count (num_splits = 0) and the workspace size are those of a batch of max_tokens-token
+ * sequences.  A count outside [1, max_tokens] makes that sequence's output rows NaN.
+ * t_k_inv_t as in wushkv_decode_attention_ragged.  Errors as wushkv_decode_attention,
+ * seq_n NULL -> ERR_NULL, seq_n not 4-byte aligned -> ERR_ALIGN.
+ */
+int wushkv_decode_attention_device(const wushkv_cache *c, const int32_t *seq_n, int64_t max_tokens,
+                                   const void *q, int32_t q_dtype, const float *t_k_inv_t, float *q_t,
+                                   int32_t num_q_heads, int32_t num_splits, void *workspace,
+                                   size_t workspace_bytes, float *out, void *stream);
+
+/*
  * Calibration statistics (WUSH-KV digest, "method key points": per KV head, the key
  * transform's Hessian is the sum of Q Q^T over the query heads that read the key and
  * the Gram matrices are the sums over the keys and values themselves; "takeaways": the

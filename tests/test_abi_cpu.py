@@ -206,3 +206,30 @@ def test_ragged_validation(lib):
     assert fd(ctypes.byref(d), arr(5, 0, 7), p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_SHAPE
     assert fd(ctypes.byref(d), arr(5, 9000, 7), p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_CAPACITY
     assert fd(ctypes.byref(d), arr(5, 8000, 7), p, W.DT_BF16, None, p, 32, 0, p, ws - 1, p, None) == W.ERR_WORKSPACE
+
+
+def test_device_count_validation(lib):
+    """Device-count append and decode: host-side checks only (the counts themselves
+    are read, and range-checked, by the kernels)."""
+    d = _spec(batch=3).desc()
+    _fake_planes(d)
+    kv = ctypes.c_void_p(0x900000)
+    fa = lib.wushkv_append_flush_device
+    assert fa(ctypes.byref(d), None, 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    assert fa(ctypes.byref(d), ctypes.c_void_p(0x900002), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_ALIGN
+    assert fa(ctypes.byref(d), kv, -1, kv, kv, W.DT_BF16, kv, None) == W.ERR_SHAPE
+    assert fa(ctypes.byref(d), kv, 8257, kv, kv, W.DT_BF16, kv, None) == W.ERR_CAPACITY
+    assert fa(ctypes.byref(d), kv, 0, kv, kv, W.DT_BF16, kv, None) == W.OK        # no-op: counts unchanged
+    assert fa(ctypes.byref(d), kv, 1, None, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    fd = lib.wushkv_decode_attention_device
+    p = ctypes.c_void_p(0x900000)
+    ws = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    assert fd(ctypes.byref(d), None, 8000, p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_NULL
+    assert fd(ctypes.byref(d), ctypes.c_void_p(0x900001), 8000, p, W.DT_BF16, None, p, 32, 0, p, ws, p,
+              None) == W.ERR_ALIGN
+    assert fd(ctypes.byref(d), p, 0, p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_SHAPE
+    assert fd(ctypes.byref(d), p, 9000, p, W.DT_BF16, None, p, 32, 0, p, ws, p, None) == W.ERR_CAPACITY
+    assert fd(ctypes.byref(d), p, 8000, p, W.DT_BF16, None, p, 32, 0, p, ws - 1, p, None) == W.ERR_WORKSPACE
+    big = _spec(batch=300).desc()      # no per-sequence array in the launch: any batch size
+    _fake_planes(big)
+    assert fa(ctypes.byref(big), kv, 0, kv, kv, W.DT_BF16, kv, None) == W.OK
