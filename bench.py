@@ -280,6 +280,78 @@ def run_long_leg(args):
     return out
 
 
+def run_graph_leg(args):
+    """The launch-bound decode step of one sequence of an 8B-class layer (32 query / 8 KV
+    heads, 8192 cached tokens, QuEST 2-bit K and V, chunk 8): append + flush + decode with
+    the query transform, per step, launched eagerly with host-side counts, eagerly with
+    device-resident counts, and as one recorded graph replayed once per step."""
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+
+    w = configs.LAYER_8B
+    dev = "cuda"
+    n0, warm, steps = w.context, 16, 256
+    cap = n0 + 3 * (warm + steps) + 1
+    k, v = gen.kv_tensors(w, 0, n0 + 1, dev)
+    t16, tinvt = gen.key_transforms(w, 0)
+    t16, tinvt = t16.to(dev), tinvt.to(dev)
+    spec = W.CacheSpec(batch=1, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=cap, sink=w.sink,
+                       recent=w.recent, chunk=w.chunk, bits_k=w.bits_k, bits_v=w.bits_v, quant_k=W.Q_QUEST,
+                       quant_v=W.Q_QUEST, clip_mult=w.clip_mult)
+    cache = W.KVCache(spec, dev)
+    W.append_flush(cache, k[:, :, :n0].contiguous(), v[:, :, :n0].contiguous(), t16)
+    ks, vs = k[:, :, n0:n0 + 1].contiguous(), v[:, :, n0:n0 + 1].contiguous()
+    q = gen.queries(w, 0, 0, dev)
+    Hq = w.num_q_heads
+    P = W.decode_num_splits(cache, cap, Hq, 0)
+    ws = W.decode_workspace(cache, cap, Hq, P)
+    o = torch.empty(1, Hq, w.head_dim, dtype=torch.float32, device=dev)
+    qt = torch.empty_like(o)
+    counts = torch.tensor([n0], dtype=torch.int32, device=dev)
+
+    def host_step():
+        W.append_flush(cache, ks, vs, t16)
+        W.decode_attention_fused(cache, q, tinvt, num_splits=P, workspace=ws, out=o, q_t=qt)
+
+    def device_step():
+        W.append_flush_device(cache, counts, ks, vs, t16)
+        W.decode_attention_device(cache, counts, cap, q, t_inv_t=tinvt, q_t=qt, num_splits=P, workspace=ws, out=o)
+
+    def timed(f):
+        for _ in range(warm):
+            f()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    host_us = timed(host_step)
+    counts.fill_(cache.n)
+    dev_us = timed(device_step)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        device_step()
+    graph_us = timed(g.replay)
+    n_end = int(counts.item())
+    log(f"[bench] 8B-layer decode step ({w.name}, n {n0} -> {n_end}): eager {host_us:.1f} us, eager with device "
+        f"counts {dev_us:.1f} us, graph replay {graph_us:.1f} us")
+    out = {"workload": w.name, "context_start": n0, "steps_timed": steps, "splits": P,
+           "eager_host_counts_us": round(host_us, 2), "eager_device_counts_us": round(dev_us, 2),
+           "graph_replay_us": round(graph_us, 2),
+           "bytes_per_decode": int(decode_bytes(w, n0)),
+           "note": "append + flush (when due) + decode with the query transform, per step; 3 x (16 + 256) "
+                   "steps past the prefill"}
+    del cache
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_calib_leg(args):
     """Calibration sums of one layer of the calibration workload (128 sequences x 1024
     tokens, 8 KV / 32 query heads): key Gram, value Gram and the key Hessian (query heads
@@ -445,6 +517,7 @@ def main():
     ap.add_argument("--flush-bits", type=str, default="", help="comma-separated bit widths of the flush leg")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode leg")
     ap.add_argument("--no-calib", action="store_true", help="skip the calibration-statistics leg")
+    ap.add_argument("--no-graph", action="store_true", help="skip the launch-bound decode-step leg")
     ap.add_argument("--calib-legs", type=str, default="key_gram,value_gram,key_hessian",
                     help="comma-separated sums the calibration leg times")
     ap.add_argument("--settle-s", type=float, default=0.3,
@@ -495,6 +568,7 @@ def main():
     fl = {} if args.no_flush else run_flush_leg(args)
     lc = {} if args.no_long else run_long_leg(args)
     cl = {} if args.no_calib else run_calib_leg(args)
+    gl = {} if args.no_graph else run_graph_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
@@ -533,6 +607,8 @@ def main():
     if lc:
         line["long_context"] = dict(lc, workload=configs_name("LONG_CONTEXT"),
                                     quant="percentile-clipped affine 2-bit K / 3-bit V")
+    if gl:
+        line["decode_step_graph"] = gl
     if cl:
         line["calibration"] = dict(cl, workload=configs_name("CALIB"),
                                    note="bf16 rows; out[g] = sum of x x^T; flop counted as 2 N d^2 per head")

@@ -201,9 +201,67 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   }
 }
 
-// The merge of one (batch row, query head) per workgroup, thread = channel.
-__global__ void __launch_bounds__(128) merge_kernel(DecodeArgs a, int nparts) {
-  if ((int)threadIdx.x < a.d) merge_row(a, blockIdx.x, nparts, threadIdx.x);
+// Online-softmax merge of the nparts partials (m_p, l_p, o_p) of one (batch row, query
+// head) row per workgroup: m* = max m_p, out = sum 2^{m_p - m*} o_p / sum 2^{m_p - m*} l_p
+// over the partials with l_p > 0.  Thread (k, c) of the workgroup takes channels
+// 4 c .. 4 c + 3 of the k-th of kMergeRanges contiguous ranges of partials, loading them
+// all before it sums them in partition order; the ranges' sums are then added in range
+// order, so the result does not depend on timing.  Every load is in bounds and
+// unconditional (an empty partial's o_p is read but masked), so a range costs about one
+// memory latency instead of one per partial.
+constexpr int kMergeThreads = 256;
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(DecodeArgs a, int nparts) {
+  __shared__ float red[kMergeThreads];
+  __shared__ float4 rnum[kMergeThreads];
+  __shared__ float rden[kMergeThreads];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  const int cpg = a.d / 4, ranges = kMergeThreads / cpg;    // channel quads, partial ranges
+  const size_t row = (size_t)bh * (a.P + 1);
+  const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml) + row;
+  // m*: the largest m_p of a non-empty partial (a max: the order does not matter)
+  float mx = -INFINITY;
+  for (int p = tid; p < nparts; p += kMergeThreads) {
+    const float2 v = ml[p];
+    if (v.y > 0.f) mx = fmaxf(mx, v.x);
+  }
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float mstar = red[0];
+  const int k = tid / cpg, c = tid % cpg;
+  const int p0 = (int)((int64_t)nparts * k / ranges), p1 = (int)((int64_t)nparts * (k + 1) / ranges);
+  const float4 *o = reinterpret_cast<const float4 *>(a.part_o + row * a.d) + c;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  {
+#pragma unroll 16
+    for (int p = p0; p < p1; ++p) {
+      const float2 v = ml[p];
+      const float4 op = o[(size_t)p * cpg];
+      const bool live = v.y > 0.f;
+      const float f = live ? __builtin_amdgcn_exp2f(v.x - mstar) : 0.f;
+      num.x = fmaf(f, live ? op.x : 0.f, num.x);
+      num.y = fmaf(f, live ? op.y : 0.f, num.y);
+      num.z = fmaf(f, live ? op.z : 0.f, num.z);
+      num.w = fmaf(f, live ? op.w : 0.f, num.w);
+      den = fmaf(f, live ? v.y : 0.f, den);
+    }
+  }
+  rnum[tid] = num;
+  rden[tid] = den;
+  __syncthreads();
+  if (tid >= cpg) return;
+  float4 n = rnum[tid];
+  float dd = rden[tid];
+  for (int r = 1; r < ranges; ++r) {
+    const float4 x = rnum[r * cpg + tid];
+    n.x += x.x; n.y += x.y; n.z += x.z; n.w += x.w;
+    dd += rden[r * cpg + tid];
+  }
+  reinterpret_cast<float4 *>(a.out + (size_t)bh * a.d)[tid] = make_float4(n.x / dd, n.y / dd, n.z / dd, n.w / dd);
 }
 
 }  // namespace
@@ -234,7 +292,7 @@ hipError_t launch_decode(const DecodeArgs &a0, hipStream_t s) {
     nparts = a.P + 1;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, s, a, nparts);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(kMergeThreads), 0, s, a, nparts);
   return hipGetLastError();
 }
 

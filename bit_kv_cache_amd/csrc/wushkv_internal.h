@@ -164,27 +164,6 @@ __device__ __forceinline__ int64_t seq_before(const Args &a, int b) {
   return a.ragged == kRaggedHost ? a.seq_nb[b] : a.n_before;
 }
 
-// Online-softmax merge of the partials of one (batch row, query head) row bh, channel
-// j: m* = max m_p, out = sum 2^{m_p - m*} o_p / sum 2^{m_p - m*} l_p over the partials
-// with l_p > 0, in fixed partition order.
-__device__ __forceinline__ void merge_row(const DecodeArgs &a, int bh, int nparts, int j) {
-  const size_t row = (size_t)bh * (a.P + 1);
-  float mstar = -INFINITY;
-  for (int p = 0; p < nparts; ++p) {
-    const float *ml = a.part_ml + (row + p) * 2;
-    if (ml[1] > 0.f) mstar = fmaxf(mstar, ml[0]);
-  }
-  float num = 0.f, den = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float *ml = a.part_ml + (row + p) * 2;
-    if (!(ml[1] > 0.f)) continue;
-    const float f = __builtin_amdgcn_exp2f(ml[0] - mstar);
-    num = fmaf(f, a.part_o[(row + p) * a.d + j], num);
-    den = fmaf(f, ml[1], den);
-  }
-  a.out[(size_t)bh * a.d + j] = num / den;
-}
-
 __device__ __forceinline__ float load_in(const void *p, int dtype, size_t i) {
   if (dtype == WUSHKV_DT_F32) return ((const float *)p)[i];
   if (dtype == WUSHKV_DT_BF16) {
