@@ -352,6 +352,72 @@ def run_graph_leg(args):
     return out
 
 
+def run_transform_leg(args):
+    """Module-output error of the path under different key transforms, on synthetic
+    attention modules: 8 modules (layers) of 4 sequences x 1024 tokens, 32 query / 8 KV
+    heads, d = 128, bf16 keys with outlier channels under per-head covariance.  Each
+    module is prefilled through the library with T_K = identity, the orthonormal
+    Hadamard matrix, the workloads' random dense transform, or Gram whitening (from the
+    library's calibration sums over held-out keys of the same heads), then decoded for 16
+    queries per sequence.  The error is the relative Frobenius error of the attention
+    outputs against full-precision attention over the unquantized keys and values (fp32
+    on the GPU), summarized over the modules by a geometric mean.  Synthetic data: the
+    figures show the transforms' effect on such data, not on a trained model."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+    from synth import transforms as TR
+
+    base = configs.SERVING.scaled(batch=4, context=1024)
+    n, nq, modules = 1024, 16, 8
+    d, H, G = base.head_dim, base.num_kv_heads, base.group
+    settings = [("affine", 2), ("quest", 2), ("quest", 3), ("quest", 4)]
+    kinds = ["identity", "hadamard", "dense", "whitening"]
+    errs = {(k, s): [] for k in kinds for s in settings}
+    t0 = time.perf_counter()
+    for layer in range(modules):
+        k, v = gen.kv_tensors(base, layer, n, "cuda")
+        qs = torch.stack([gen.queries(base, layer, s, "cuda") for s in range(nq)])       # [nq, B, Hq, d]
+        # full-precision reference: per KV head its G query heads over all n tokens
+        qg = qs.float().reshape(nq, base.batch, H, G, d).permute(1, 2, 0, 3, 4).reshape(base.batch, H, nq * G, d)
+        kf, vf = k.float(), v.float()
+        sc = torch.matmul(qg, kf.transpose(-1, -2).contiguous()) / np.sqrt(d)
+        ref = torch.matmul(torch.softmax(sc, dim=-1), vf)                                  # [B, H, nq*G, d]
+        ref = ref.reshape(base.batch, H, nq, G, d).permute(2, 0, 1, 3, 4).reshape(nq, base.batch, H * G, d)
+        held = torch.stack([torch.stack([gen.kv_block(base, layer, base.batch + b, g, n, "cuda")[0]
+                                         for g in range(H)]) for b in range(base.batch)]).contiguous()
+        gram = W.calib_stats(held, 1).double().cpu().numpy()
+        trans = {"identity": TR.as_inputs(TR.per_head(np.eye(d), H)),
+                 "hadamard": TR.as_inputs(TR.per_head(TR.hadamard(d), H)),
+                 "dense": gen.key_transforms(base, layer),
+                 "whitening": TR.as_inputs(np.stack([TR.whitening(gram[g], base.batch * n) for g in range(H)]))}
+        for kind in kinds:
+            t16, tinvt = trans[kind][0].cuda(), trans[kind][1].cuda()
+            for quant, bits in settings:
+                qc = W.Q_AFFINE if quant == "affine" else W.Q_QUEST
+                spec = W.CacheSpec(batch=base.batch, num_kv_heads=H, head_dim=d, capacity=n, sink=base.sink,
+                                   recent=base.recent, chunk=base.chunk, bits_k=bits, bits_v=bits, quant_k=qc,
+                                   quant_v=qc, clip_mult=base.clip_mult, pct_lo=base.pct_lo, pct_hi=base.pct_hi)
+                cache = W.KVCache(spec, "cuda")
+                W.append_flush(cache, k, v, t16)
+                out = torch.stack([W.decode_attention_fused(cache, qs[s], tinvt)[0] for s in range(nq)])
+                e = float(torch.linalg.vector_norm((out - ref).double()) / torch.linalg.vector_norm(ref.double()))
+                errs[(kind, (quant, bits))].append(e)
+    res = {}
+    for (kind, (quant, bits)), e in errs.items():
+        res.setdefault(f"{quant}_{bits}bit", {})[kind] = round(float(np.exp(np.mean(np.log(e)))), 4)
+    log(f"[bench] module-output error (geometric mean over {modules} synthetic modules, "
+        f"{time.perf_counter() - t0:.1f} s): " + "; ".join(f"{s}: " + ", ".join(f"{k} {v:.3f}" for k, v in r.items())
+                                                      for s, r in res.items()))
+    res["note"] = ("synthetic modules: 4 sequences x 1024 tokens, 8 KV heads, 16 decode queries each; relative "
+                   "Frobenius error of the attention outputs vs full precision, geometric mean over 8 modules; "
+                   "whitening = (key second moment)^(-1/2) from held-out keys, Frobenius-normalized (not the "
+                   "pages' WUSH construction)")
+    return res
+
+
 def run_calib_leg(args):
     """Calibration sums of one layer of the calibration workload (128 sequences x 1024
     tokens, 8 KV / 32 query heads): key Gram, value Gram and the key Hessian (query heads
@@ -518,6 +584,7 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode leg")
     ap.add_argument("--no-calib", action="store_true", help="skip the calibration-statistics leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the launch-bound decode-step leg")
+    ap.add_argument("--no-transforms", action="store_true", help="skip the key-transform module-error leg")
     ap.add_argument("--calib-legs", type=str, default="key_gram,value_gram,key_hessian",
                     help="comma-separated sums the calibration leg times")
     ap.add_argument("--settle-s", type=float, default=0.3,
@@ -569,6 +636,7 @@ def main():
     lc = {} if args.no_long else run_long_leg(args)
     cl = {} if args.no_calib else run_calib_leg(args)
     gl = {} if args.no_graph else run_graph_leg(args)
+    tl = {} if args.no_transforms else run_transform_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
@@ -609,6 +677,8 @@ def main():
                                     quant="percentile-clipped affine 2-bit K / 3-bit V")
     if gl:
         line["decode_step_graph"] = gl
+    if tl:
+        line["transform_module_error"] = tl
     if cl:
         line["calibration"] = dict(cl, workload=configs_name("CALIB"),
                                    note="bf16 rows; out[g] = sum of x x^T; flop counted as 2 N d^2 per head")

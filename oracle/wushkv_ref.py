@@ -432,3 +432,35 @@ def calib_sum_abs(x, group=1):
     """Entrywise sum |x_i| |x_j| over the same rows: the scale of the rounding error of
     any fp32 evaluation of calib_stats (error <= n u sum |x_i x_j| for n sequential adds)."""
     return calib_stats(np.abs(np.asarray(x, dtype=np.float64)), group)
+
+
+# ----------------------------------------------------------------------------
+# module-output error (WUSH-KV digest, "key experiments": per attention module the
+# error of the module's output with the quantized cache, summarized over modules by a
+# geometric mean; the pages give the numbers but not the formula, so the plain reading
+# is taken: relative Frobenius error of the attention output against full precision)
+
+def attention_fp(q, k, v):
+    """Full-precision softmax attention of query rows q [m, d] over keys k [n, d] and
+    values v [n, d], scale 1/sqrt(d): the output [m, d] the quantized cache is judged
+    against."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    s = q @ k.T / math.sqrt(q.shape[-1])
+    s = s - s.max(axis=-1, keepdims=True)
+    w = np.exp(s)
+    return (w @ v) / w.sum(axis=-1, keepdims=True)
+
+
+def module_output_error(out, ref):
+    """||out - ref||_F / ||ref||_F over all of one module's outputs."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(out - ref) / np.linalg.norm(ref))
+
+
+def geometric_mean(errors):
+    """exp(mean(log e)) over the modules' errors."""
+    e = np.asarray(errors, np.float64)
+    return float(np.exp(np.mean(np.log(e))))
