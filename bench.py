@@ -521,6 +521,29 @@ def summarize_counters(fetch_csv, write_csv, copy_mib):
             "kernels": kernels}
 
 
+def summarize_trace(trace_csv):
+    """Library kernels of a rocprofv3 kernel-trace CSV grouped by (kernel, grid, workgroup
+    size): the legs of this bench launch distinct grids.  Durations in microseconds."""
+    import csv
+    import collections
+    import statistics
+
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        name = r["Kernel_Name"]
+        if "wushkv" not in name:
+            continue
+        name = name.replace("void ", "").replace("wushkv::(anonymous namespace)::", "").replace("wushkv::", "")
+        key = (name.split("(")[0], f'{r["Grid_Size_X"]},{r["Grid_Size_Y"]},{r["Grid_Size_Z"]}', r["Workgroup_Size_X"])
+        groups[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = [f"{'kernel':34s} {'grid x,y,z':>22s} {'wg':>5s} {'calls':>6s} {'avg':>9s} {'median':>9s} {'min':>9s}"]
+    for key in sorted(groups, key=lambda k: -sum(groups[k])):
+        v = groups[key]
+        lines.append(f"{key[0]:34s} {key[1]:>22s} {key[2]:>5s} {len(v):6d} {sum(v) / len(v):9.2f} "
+                     f"{statistics.median(v):9.2f} {min(v):9.2f}")
+    return "\n".join(lines)
+
+
 def run_cpu_leg(dl, sample_heads=16):
     """The oracle, as it stands, on a bounded sample of the decode step: the G query
     heads of `sample_heads` (batch row, KV head) pairs, at the same context."""
@@ -597,7 +620,12 @@ def main():
                          "--copy-check MIB) as JSON on stdout")
     ap.add_argument("--counters-kernels", choices=sorted(COUNTER_SOURCES), default="decode",
                     help="which kernels' sources the counter summary is tied to")
+    ap.add_argument("--trace-summary", metavar="TRACE_CSV",
+                    help="no GPU work: group a rocprofv3 kernel_trace.csv by kernel and grid and print it")
     args = ap.parse_args()
+    if args.trace_summary:
+        print(summarize_trace(args.trace_summary))
+        return
     if args.counters_summary:
         rec = summarize_counters(*args.counters_summary, args.copy_check or 1024)
         rec["source_files"] = list(COUNTER_SOURCES[args.counters_kernels])
