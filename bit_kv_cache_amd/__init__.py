@@ -21,7 +21,8 @@ EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "
            "wushkv_decode_num_splits", "wushkv_decode_workspace_bytes", "wushkv_append_flush",
            "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused",
            "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
-           "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device")
+           "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device",
+           "wushkv_pool_bytes", "wushkv_append_flush_paged", "wushkv_decode_attention_paged")
 
 
 class WushKVError(RuntimeError):
@@ -71,6 +72,11 @@ def lib():
                                                               vp, vp]),
             "wushkv_calib_workspace_bytes": (sz, [i32, i32, i64, i32, i32]),
             "wushkv_append_flush_device": (ctypes.c_int, [P, vp, i32, vp, vp, i32, vp, vp]),
+            "wushkv_pool_bytes": (sz, [P, ctypes.POINTER(PagesDesc), ctypes.c_int]),
+            "wushkv_append_flush_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), i32, vp, vp,
+                                                         i32, vp, vp]),
+            "wushkv_decode_attention_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), vp, i32,
+                                                             vp, vp, i32, i32, vp, sz, vp, vp]),
             "wushkv_decode_attention_device": (ctypes.c_int, [P, vp, i64, vp, i32, vp, vp, i32, i32, vp, sz, vp,
                                                               vp]),
         }
@@ -115,6 +121,12 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensors passed to libwushkv must be contiguous")
     return t.data_ptr()
+
+
+class PagesDesc(ctypes.Structure):
+    """wushkv_pages: device page table [batch][max_pages] int32 and the page geometry."""
+    _fields_ = [("table", ctypes.c_void_p), ("page_tokens", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32)]
 
 
 @dataclass
@@ -374,4 +386,84 @@ def decode_attention_device(cache: KVCache, seq_n, max_tokens, q, t_inv_t=None, 
                                                 None if t_inv_t is None else _ptr(t_inv_t), _ptr(q_t), Hq,
                                                 num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
                                                 _stream(stream, q.device)), "decode_attention_device")
+    return out, q_t
+
+
+class PagedKVCache:
+    """A cache whose quantized body lives in page pools: the window planes are
+    [batch][...] as in KVCache, the code and parameter planes are pools of num_pages
+    pages of page_tokens rows per KV head, and table (int32 [batch][max_pages], on the
+    device) maps each sequence's logical body page to a physical page.  The caller
+    fills the table; unused entries may hold anything."""
+
+    def __init__(self, spec: CacheSpec, page_tokens, num_pages, max_pages=None, device="cuda"):
+        import torch
+        self.spec = spec
+        body = max(0, spec.capacity - spec.sink)
+        self.max_pages = max_pages or max(1, -(-body // page_tokens))
+        self.table = torch.zeros((spec.batch, self.max_pages), dtype=torch.int32, device=device)
+        self.pages = PagesDesc(self.table.data_ptr(), page_tokens, self.max_pages, num_pages)
+        d = spec.desc()
+        sizes = {p: int(lib().wushkv_pool_bytes(ctypes.byref(d), ctypes.byref(self.pages), i))
+                 for i, p in enumerate(PLANES)}
+        if any(v == 0 and not p.startswith("sink") for p, v in sizes.items()):
+            raise WushKVError(ERR_SHAPE, "paged cache geometry")
+        self.planes = {p: torch.zeros(max(n, 16), dtype=torch.uint8, device=device) for p, n in sizes.items()}
+        self.desc = spec.desc(self.planes)
+        self.seq_n = [0] * spec.batch
+
+    WINDOWS = ("sink_k", "sink_v", "ring_k", "ring_v")
+
+    def sequence(self, b):
+        """Sequence b as a one-sequence paged cache: its own window rows and table row,
+        the shared pools."""
+        import copy
+        s = copy.copy(self.spec)
+        s.batch = 1
+        sub = PagedKVCache.__new__(PagedKVCache)
+        sub.spec, sub.max_pages = s, self.max_pages
+        sub.table = self.table[b:b + 1]
+        sub.pages = PagesDesc(sub.table.data_ptr(), self.pages.page_tokens, self.max_pages, self.pages.num_pages)
+        sub.planes = dict(self.planes)
+        for p in self.WINDOWS:
+            per = self.planes[p].numel() // self.spec.batch
+            sub.planes[p] = self.planes[p][b * per:(b + 1) * per]
+        sub.desc = s.desc(sub.planes)
+        sub.seq_n = [self.seq_n[b]]
+        return sub
+
+
+def append_flush_paged(cache: PagedKVCache, k_new, v_new, t_k16, n_before=None, stream=None):
+    """append_flush_ragged on a paged cache (sequence b holds n_before[b] tokens,
+    default cache.seq_n)."""
+    import torch
+    n_before = list(cache.seq_n if n_before is None else n_before)
+    n_new = k_new.shape[2]
+    if k_new.dtype != v_new.dtype or t_k16.dtype != torch.float16:
+        raise ValueError("k_new/v_new must share a dtype and t_k16 must be float16")
+    _check(lib().wushkv_append_flush_paged(ctypes.byref(cache.desc), ctypes.byref(cache.pages), _i64_array(n_before),
+                                           n_new, _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(t_k16),
+                                           _stream(stream, k_new.device)), "append_flush_paged")
+    cache.seq_n = [n + n_new for n in n_before]
+
+
+def decode_attention_paged(cache: PagedKVCache, q, q_t=None, t_inv_t=None, n_tokens=None, num_splits=0,
+                           workspace=None, out=None, stream=None):
+    """decode_attention_ragged on a paged cache.  -> (out, q_t)."""
+    import torch
+    n_tokens = list(cache.seq_n if n_tokens is None else n_tokens)
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = decode_workspace(cache, max(n_tokens), Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if q_t is None:
+        if t_inv_t is None:
+            raise ValueError("decode_attention_paged needs q_t or t_inv_t")
+        q_t = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention_paged(ctypes.byref(cache.desc), ctypes.byref(cache.pages),
+                                               _i64_array(n_tokens), _ptr(q), _dtype_code(q),
+                                               None if t_inv_t is None else _ptr(t_inv_t), _ptr(q_t), Hq, num_splits,
+                                               _ptr(workspace), workspace.numel(), _ptr(out),
+                                               _stream(stream, q.device)), "decode_attention_paged")
     return out, q_t

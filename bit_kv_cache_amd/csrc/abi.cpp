@@ -89,6 +89,25 @@ int check_planes(const wushkv_cache *c) {
   return WUSHKV_OK;
 }
 
+// A page table's host-side checks; fills pg (table == nullptr when pages is null).
+int check_pages(const wushkv_pages *pages, const Geom &g, PageTable *pg) {
+  pg->table = nullptr;
+  pg->page_tokens = 0;
+  pg->max_pages = pg->num_pages = 0;
+  if (!pages) return WUSHKV_OK;
+  if (!pages->table) return WUSHKV_ERR_NULL;
+  if (((uintptr_t)pages->table & 3u) != 0) return WUSHKV_ERR_ALIGN;
+  if (pages->page_tokens < kSet || pages->page_tokens % kSet != 0 || pages->max_pages < 1 || pages->num_pages < 1)
+    return WUSHKV_ERR_SHAPE;
+  // every body row a sequence can hold has a logical page
+  if ((int64_t)pages->max_pages * pages->page_tokens < g.body_cap) return WUSHKV_ERR_CAPACITY;
+  pg->table = pages->table;
+  pg->page_tokens = pages->page_tokens;
+  pg->max_pages = pages->max_pages;
+  pg->num_pages = pages->num_pages;
+  return WUSHKV_OK;
+}
+
 int hip_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? WUSHKV_OK : WUSHKV_ERR_HIP;
@@ -154,6 +173,20 @@ size_t wushkv_plane_bytes(const wushkv_cache *c, int plane) {
   }
 }
 
+size_t wushkv_pool_bytes(const wushkv_cache *c, const wushkv_pages *pages, int plane) {
+  Geom g;
+  PageTable pg;
+  if (make_geom(c, &g) != WUSHKV_OK || !pages || check_pages(pages, g, &pg) != WUSHKV_OK) return 0;
+  const size_t rows = (size_t)pg.num_pages * g.Hkv * pg.page_tokens;
+  switch (plane) {
+    case WUSHKV_PLANE_CODES_K: return rows * g.kcode_row;
+    case WUSHKV_PLANE_CODES_V: return rows / kSet * g.vset_bytes;
+    case WUSHKV_PLANE_PAR_K: return rows * 2 * g.kpar_n;
+    case WUSHKV_PLANE_PAR_V: return rows * 2 * g.vpar_n;
+    default: return wushkv_plane_bytes(c, plane);
+  }
+}
+
 int32_t wushkv_decode_num_splits(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads, int32_t num_splits) {
   Geom g;
   if (make_geom(c, &g) != WUSHKV_OK) return 0;
@@ -177,12 +210,14 @@ namespace {
 // Append + flush for a uniform batch (seq_nb == dev_n == nullptr: every sequence holds
 // n_before tokens), a ragged one (sequence b holds seq_nb[b]) or one whose counts live
 // in device memory (dev_n[b]; the call then advances them by n_new).
-int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *seq_nb, int32_t *dev_n,
-                      int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype, const void *t_k_f16,
-                      void *stream) {
+int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_before, const int64_t *seq_nb,
+                      int32_t *dev_n, int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype,
+                      const void *t_k_f16, void *stream) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
+  PageTable pg;
+  if ((st = check_pages(pages, g, &pg)) != WUSHKV_OK) return st;
   if (dev_n) {
     if (((uintptr_t)dev_n & 3u) != 0) return WUSHKV_ERR_ALIGN;
     n_before = 0;   // the counts are checked by the kernels
@@ -229,6 +264,8 @@ int append_flush_impl(const wushkv_cache *c, int64_t n_before, const int64_t *se
     f.kpar_n = g.kpar_n; f.vpar_n = g.vpar_n; f.clip = g.clip;
     f.lo_i = g.lo_i; f.hi_i = g.hi_i; f.lo_t = g.lo_t; f.hi_t = g.hi_t; f.need_lo = g.need_lo; f.need_hi = g.need_hi;
     f.cap = g.cap;
+    f.pg = pg;
+    f.body_cap = g.body_cap;
     if (dev_n) {
       f.ragged = kRaggedDevice;
       f.dev_n = dev_n;
@@ -265,19 +302,26 @@ extern "C" {
 
 int wushkv_append_flush(const wushkv_cache *c, int64_t n_before, int32_t n_new, const void *k_new,
                         const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
-  return append_flush_impl(c, n_before, nullptr, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+  return append_flush_impl(c, nullptr, n_before, nullptr, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
 }
 
 int wushkv_append_flush_ragged(const wushkv_cache *c, const int64_t *n_before, int32_t n_new, const void *k_new,
                                const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
   if (!n_before) return WUSHKV_ERR_NULL;
-  return append_flush_impl(c, 0, n_before, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+  return append_flush_impl(c, nullptr, 0, n_before, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+}
+
+int wushkv_append_flush_paged(const wushkv_cache *c, const wushkv_pages *pages, const int64_t *n_before,
+                              int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype,
+                              const void *t_k_f16, void *stream) {
+  if (!n_before || !pages) return WUSHKV_ERR_NULL;
+  return append_flush_impl(c, pages, 0, n_before, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
 }
 
 int wushkv_append_flush_device(const wushkv_cache *c, int32_t *seq_n, int32_t n_new, const void *k_new,
                                const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
   if (!seq_n) return WUSHKV_ERR_NULL;
-  return append_flush_impl(c, 0, nullptr, seq_n, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+  return append_flush_impl(c, nullptr, 0, nullptr, seq_n, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
 }
 
 int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtype, int32_t batch,
@@ -331,12 +375,15 @@ namespace {
 
 // Decode with q~ given (tinvt == nullptr) or formed from q and T^{-T} into q_t.
 // With dev_n, the counts are read on the device and n_tokens bounds them.
-int decode_impl(const wushkv_cache *c, int64_t n_tokens, const int64_t *seq_n, const int32_t *dev_n,
-                const void *q, int32_t q_dtype, float *q_t, const float *tinvt, int32_t num_q_heads,
-                int32_t num_splits, void *workspace, size_t workspace_bytes, float *out, void *stream) {
+int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_tokens, const int64_t *seq_n,
+                const int32_t *dev_n, const void *q, int32_t q_dtype, float *q_t, const float *tinvt,
+                int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                void *stream) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
+  PageTable pg;
+  if ((st = check_pages(pages, g, &pg)) != WUSHKV_OK) return st;
   if (dev_n) {
     if (((uintptr_t)dev_n & 3u) != 0) return WUSHKV_ERR_ALIGN;
   } else if (seq_n) {   // ragged: the checks, split count and workspace follow the longest sequence
@@ -373,6 +420,8 @@ int decode_impl(const wushkv_cache *c, int64_t n_tokens, const int64_t *seq_n, c
     a.ragged = kRaggedHost;
     for (int b = 0; b < g.B; ++b) a.seq_n[b] = (int32_t)seq_n[b];
   }
+  a.pg = pg;
+  a.body_cap = g.body_cap;
   a.q = q; a.q_dtype = q_dtype; a.qt = q_t;
   a.tinvt = tinvt; a.qt_out = tinvt ? q_t : nullptr;
   a.sink_k = (const _Float16 *)c->sink_k; a.sink_v = (const _Float16 *)c->sink_v;
@@ -402,7 +451,7 @@ extern "C" {
 int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,
                             const float *q_t, int32_t num_q_heads, int32_t num_splits, void *workspace,
                             size_t workspace_bytes, float *out, void *stream) {
-  return decode_impl(c, n_tokens, nullptr, nullptr, q, q_dtype, const_cast<float *>(q_t), nullptr, num_q_heads,
+  return decode_impl(c, nullptr, n_tokens, nullptr, nullptr, q, q_dtype, const_cast<float *>(q_t), nullptr, num_q_heads,
                      num_splits, workspace, workspace_bytes, out, stream);
 }
 
@@ -410,7 +459,7 @@ int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens, const
                                   const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
                                   void *workspace, size_t workspace_bytes, float *out, void *stream) {
   if (!t_k_inv_t) return WUSHKV_ERR_NULL;
-  return decode_impl(c, n_tokens, nullptr, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+  return decode_impl(c, nullptr, n_tokens, nullptr, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
 }
 
@@ -418,7 +467,16 @@ int wushkv_decode_attention_ragged(const wushkv_cache *c, const int64_t *n_token
                                    const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
                                    void *workspace, size_t workspace_bytes, float *out, void *stream) {
   if (!n_tokens) return WUSHKV_ERR_NULL;
-  return decode_impl(c, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+  return decode_impl(c, nullptr, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+                     workspace_bytes, out, stream);
+}
+
+int wushkv_decode_attention_paged(const wushkv_cache *c, const wushkv_pages *pages, const int64_t *n_tokens,
+                                  const void *q, int32_t q_dtype, const float *t_k_inv_t, float *q_t,
+                                  int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                                  float *out, void *stream) {
+  if (!n_tokens || !pages) return WUSHKV_ERR_NULL;
+  return decode_impl(c, pages, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
 }
 
@@ -427,7 +485,7 @@ int wushkv_decode_attention_device(const wushkv_cache *c, const int32_t *seq_n, 
                                    int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
                                    void *stream) {
   if (!seq_n) return WUSHKV_ERR_NULL;
-  return decode_impl(c, max_tokens, nullptr, seq_n, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+  return decode_impl(c, nullptr, max_tokens, nullptr, seq_n, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
 }
 

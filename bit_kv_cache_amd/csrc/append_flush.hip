@@ -367,7 +367,7 @@ __device__ __forceinline__ unsigned kpack1(unsigned x) {
   return (y | (y >> 14)) & 0xFu;
 }
 
-template <int D, int ES, int NL>
+template <int D, int ES, int NL, bool PAGED>
 __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int steps_per_wg) {
   constexpr int CPL = D / 4, KS = D / 32, NCT = D / 16;
   using QuestTag = std::integral_constant<bool, true>;
@@ -478,9 +478,14 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           sc = 0.f;
         }
         if (q == 0 && vt) {
-          _Float16 *pk = (_Float16 *)((char *)a.par_k + (size_t)bg * a.kpar_bytes) + u * a.kpar_n;
-          if constexpr (QU) pk[0] = (_Float16)sc;
-          else *(unsigned *)pk = pack_f16(sc, zp);
+          const int64_t off = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, 2 * a.kpar_n);
+          _Float16 *pk = (_Float16 *)((char *)a.par_k + off);
+          if (PAGED && off < 0) {
+          } else if constexpr (QU) {
+            pk[0] = (_Float16)sc;
+          } else {
+            *(unsigned *)pk = pack_f16(sc, zp);
+          }
         }
         const Quant<QU> qk = make_quant<QU>(sc, zp, Lk, kEdgeK);
         float e = 1.0f;
@@ -570,9 +575,14 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           sc = 0.f;
         }
         if (q == 0 && vt) {
-          _Float16 *pv = (_Float16 *)((char *)a.par_v + (size_t)bg * a.vpar_bytes) + u * a.vpar_n;
-          if constexpr (QU) pv[0] = (_Float16)sc;
-          else *(unsigned *)pv = pack_f16(sc, zp);
+          const int64_t off = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, 2 * a.vpar_n);
+          _Float16 *pv = (_Float16 *)((char *)a.par_v + off);
+          if (PAGED && off < 0) {
+          } else if constexpr (QU) {
+            pv[0] = (_Float16)sc;
+          } else {
+            *(unsigned *)pv = pack_f16(sc, zp);
+          }
         }
         const Quant<QU> qv = make_quant<QU>(sc, zp, Lv, kEdgeV);
         float e = 1.0f;
@@ -612,7 +622,9 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       const int64_t u = set0 * kSet + r;
       if (u < u0 || u >= u1) return;
       constexpr int HC = D / 2;
-      uint8_t *rowp = a.codes_k + (size_t)bg * a.kcode_bytes + (size_t)u * a.kcode_row;
+      const int64_t koff = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, (int64_t)a.kcode_row);
+      if (PAGED && koff < 0) return;   // the row's page is outside the table or the pool
+      uint8_t *rowp = a.codes_k + koff;
       u32x4 cw[HC / 16];
 #pragma unroll
       for (int i = 0; i < HC / 16; ++i) cw[i] = *(const u32x4 *)&sm.kc[r][HC * h + 16 * i];
@@ -661,7 +673,9 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       constexpr int BVV = decltype(bits_tag)::value;
       constexpr bool FULL = decltype(full_tag)::value;
       const int r0 = (int)(vlo - vbase), r1 = (int)(vhi - vbase);
-      uint8_t *vb = a.codes_v + (size_t)bg * a.vcode_bytes + (size_t)sidx * a.vset_bytes;
+      const int64_t voff = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, vbase, (int64_t)(a.vset_bytes / kSet));
+      if (PAGED && voff < 0) return;   // the set's page is outside the table or the pool
+      uint8_t *vb = a.codes_v + voff;
       unsigned w0[4], w1[4], k0[4], k1[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -794,7 +808,9 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   const int nl = need == 0 ? 0 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
   const bool f32 = a.in_dtype == WUSHKV_DT_F32;
   const int sp = (int)spw;
-#define WUSHKV_FLUSH(D, ES, NL) hipLaunchKernelGGL((flush_kernel<D, ES, NL>), grid, dim3(kThreads), 0, s, a, sp)
+#define WUSHKV_FLUSH(D, ES, NL)                                                                          \
+  if (a.pg.table) hipLaunchKernelGGL((flush_kernel<D, ES, NL, true>), grid, dim3(kThreads), 0, s, a, sp); \
+  else hipLaunchKernelGGL((flush_kernel<D, ES, NL, false>), grid, dim3(kThreads), 0, s, a, sp)
 #define WUSHKV_FLUSH_NL(D, ES)            \
   switch (nl) {                            \
     case 0: WUSHKV_FLUSH(D, ES, 0); break; \

@@ -399,7 +399,7 @@ __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int 
 // heads h + 4 qd (qd < G / 4).  PV output row r (O lane l holds rows 4 (l / 16) + i,
 // channels 16 ct + l % 16) is head r's hi part for r < G and head r - G's lo part for
 // G <= r < 2 G; the two are summed in the workgroup merge.
-template <int G, int BV, int NW>
+template <int G, int BV, int NW, bool PAGED>
 __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
                           f32x4 (&O)[8], float (&m_out)[G / 4], float (&l_out)[G / 4], float (&z_out)[G / 4],
                           float (&wm_out)[G], float (&wl_out)[G], float (&wacc_out)[G][2]) {
@@ -411,14 +411,23 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   const int Lv = 1 << BV;
   const SeqLen sl = seq_len(a, bg / a.Hkv);   // this sequence's tokens and body tokens
 
+  // Body sets are addressed by slot: the set index within this KV head's planes, or
+  // with a paged body the set's place in the pools, (page Hkv + g) sets_per_page + the
+  // set's index within its page (the resources then span the pools).
+  constexpr bool paged = PAGED;
+  const int sets_per_page = paged ? (int)(a.pg.page_tokens / kSet) : 1;
   SetSource src;
   {
-    const uint8_t *kplane = a.codes_k + (size_t)bg * a.kcode_bytes;
-    const uint8_t *vplane = a.codes_v + (size_t)bg * a.vcode_bytes;
-    const uint8_t *kpar = (const uint8_t *)a.par_k + (size_t)bg * a.kpar_bytes;
-    const uint8_t *vpar = (const uint8_t *)a.par_v + (size_t)bg * a.vpar_bytes;
-    src.k = __builtin_amdgcn_make_buffer_rsrc((void *)kplane, 0, (int)a.kcode_bytes, kRsrcWord3);
-    src.v = __builtin_amdgcn_make_buffer_rsrc((void *)vplane, 0, (int)a.vcode_bytes, kRsrcWord3);
+    const size_t pool_sets = paged ? (size_t)a.pg.num_pages * a.Hkv * sets_per_page : 0;
+    const size_t hb = paged ? 0 : (size_t)bg;
+    const uint8_t *kplane = a.codes_k + hb * a.kcode_bytes;
+    const uint8_t *vplane = a.codes_v + hb * a.vcode_bytes;
+    const uint8_t *kpar = (const uint8_t *)a.par_k + hb * a.kpar_bytes;
+    const uint8_t *vpar = (const uint8_t *)a.par_v + hb * a.vpar_bytes;
+    const int kbytes = (int)(paged ? pool_sets * kSet * a.kcode_row : a.kcode_bytes);
+    const int vbytes = (int)(paged ? pool_sets * a.vset_bytes : a.vcode_bytes);
+    src.k = __builtin_amdgcn_make_buffer_rsrc((void *)kplane, 0, kbytes, kRsrcWord3);
+    src.v = __builtin_amdgcn_make_buffer_rsrc((void *)vplane, 0, vbytes, kRsrcWord3);
     const int kb = a.kpar_n * 2, vbn = a.vpar_n * 2;
     const bool pk = lane < 4 * kb;
     src.pact = pk || (lane >= 16 && lane - 16 < 4 * vbn);
@@ -441,9 +450,17 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   // items 0 .. nwin-1 are the window stages (first, so their VALU work overlaps the other
   // waves' streaming rather than forming every wave's tail), then the body sets
   const int nwin = ws1 - ws0;
+  const int bq = bg / a.Hkv, gq = bg % a.Hkv;
+  auto slot_of = [&](int set) {
+    if (!paged) return set;
+    const int lp = set / sets_per_page;
+    int page = lp < a.pg.max_pages ? a.pg.table[(int64_t)bq * a.pg.max_pages + lp] : 0;
+    if (page < 0 || page >= a.pg.num_pages) page = 0;   // an invalid entry reads page 0
+    return (page * a.Hkv + gq) * sets_per_page + (set - lp * sets_per_page);
+  };
   auto issue = [&](int item, uint8_t *dst) {
     if (item >= nwin) {
-      stage_set<BV>(src, (int)s0 + item - nwin, dst);
+      stage_set<BV>(src, slot_of((int)s0 + item - nwin), dst);
     } else {
       const int t0 = 8 * (ws0 + item);
       stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
@@ -816,7 +833,7 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
 }
 
 // nwg_body workgroups per KV head; with one, the workgroup's merge is the output.
-template <int G, int BV, int NW>
+template <int G, int BV, int NW, bool PAGED>
 __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int nwg_body) {
   constexpr int NT = 64 * NW;
   __shared__ FastSmem<G, BV, NW> sm;
@@ -849,7 +866,7 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
     ws0 = (int)(nws * part / a.P);
     ws1 = (int)(nws * (part + 1) / a.P);
   }
-  body_wave<G, BV, NW>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
+  body_wave<G, BV, NW, PAGED>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
   __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -930,10 +947,17 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
 }  // namespace
 
 bool decode_fast_supported(const DecodeArgs &a) {
-  // buffer resources address each KV head's code planes with 31-bit offsets
+  // buffer resources address each KV head's code planes (or, paged, the whole pools)
+  // with 31-bit offsets
+  const size_t lim = (size_t)1 << 31;
+  if (a.pg.table) {
+    const size_t rows = (size_t)a.pg.num_pages * a.Hkv * a.pg.page_tokens;
+    if (rows * a.kcode_row >= lim || rows / kSet * a.vset_bytes >= lim || rows * 2 * a.kpar_n >= lim ||
+        rows * 2 * a.vpar_n >= lim)
+      return false;
+  }
   return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8) &&
-         a.kcode_bytes < (1u << 31) && a.vcode_bytes < (1u << 31) && a.kpar_bytes < (1u << 31) &&
-         a.vpar_bytes < (1u << 31);
+         a.kcode_bytes < lim && a.vcode_bytes < lim && a.kpar_bytes < lim && a.vpar_bytes < lim;
 }
 
 // Launch shape: one kWholeWaves-wave workgroup per KV head when the split count equals
@@ -969,10 +993,10 @@ int decode_fast_resident_waves(int G, int bits_v) {
   static int cache[2][2] = {{-1, -1}, {-1, -1}};
   int &c = cache[G == 8][bits_v == 3];
   if (c >= 0) return c;
-  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2, kSplitWaves>
-                                           : (const void *)decode_fast_kernel<4, 3, kSplitWaves>)
-                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2, kSplitWaves>
-                                           : (const void *)decode_fast_kernel<8, 3, kSplitWaves>);
+  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2, kSplitWaves, false>
+                                           : (const void *)decode_fast_kernel<4, 3, kSplitWaves, false>)
+                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2, kSplitWaves, false>
+                                           : (const void *)decode_fast_kernel<8, 3, kSplitWaves, false>);
   int blocks = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * kSplitWaves, 0) != hipSuccess) {
     hipGetLastError();
@@ -985,17 +1009,18 @@ int decode_fast_resident_waves(int G, int bits_v) {
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
   const int nwg = decode_fast_partials(a);
   dim3 grid(nwg, a.B * a.Hkv);
+  const bool pg = a.pg.table != nullptr;
+#define WUSHKV_FAST(G, BV, NW)                                                                            \
+  if (pg) hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, true>), grid, dim3(64 * NW), 0, s, a, nwg); \
+  else hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, false>), grid, dim3(64 * NW), 0, s, a, nwg)
   if (whole_layout(a)) {
-    constexpr int NT = 64 * kWholeWaves;
-    if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2, kWholeWaves>), grid, dim3(NT), 0, s, a, nwg);
-    else hipLaunchKernelGGL((decode_fast_kernel<4, 3, kWholeWaves>), grid, dim3(NT), 0, s, a, nwg);
-    return hipGetLastError();
-  }
-  constexpr int NT = 64 * kSplitWaves;
-  if (a.G == 4 && a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<4, 2, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
-  else if (a.G == 4) hipLaunchKernelGGL((decode_fast_kernel<4, 3, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
-  else if (a.bits_v == 2) hipLaunchKernelGGL((decode_fast_kernel<8, 2, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
-  else hipLaunchKernelGGL((decode_fast_kernel<8, 3, kSplitWaves>), grid, dim3(NT), 0, s, a, nwg);
+    if (a.bits_v == 2) { WUSHKV_FAST(4, 2, kWholeWaves); }
+    else { WUSHKV_FAST(4, 3, kWholeWaves); }
+  } else if (a.G == 4 && a.bits_v == 2) { WUSHKV_FAST(4, 2, kSplitWaves); }
+  else if (a.G == 4) { WUSHKV_FAST(4, 3, kSplitWaves); }
+  else if (a.bits_v == 2) { WUSHKV_FAST(8, 2, kSplitWaves); }
+  else { WUSHKV_FAST(8, 3, kSplitWaves); }
+#undef WUSHKV_FAST
   return hipGetLastError();
 }
 

@@ -86,10 +86,6 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
     t_end = ns + (sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
   }
   const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
-  const uint8_t *kplane = a.codes_k + bg * a.kcode_bytes;
-  const uint8_t *vplane = a.codes_v + bg * a.vcode_bytes;
-  const _Float16 *kpar = (const _Float16 *)((const char *)a.par_k + bg * a.kpar_bytes);
-  const _Float16 *vpar = (const _Float16 *)((const char *)a.par_v + bg * a.vpar_bytes);
   const _Float16 *sink_k = (const _Float16 *)((const char *)a.sink_k + bg * a.sink_bytes);
   const _Float16 *sink_v = (const _Float16 *)((const char *)a.sink_v + bg * a.sink_bytes);
   const _Float16 *ring_k = (const _Float16 *)((const char *)a.ring_k + bg * a.ring_bytes);
@@ -103,15 +99,25 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   __syncthreads();
   for (int64_t t0 = t_begin; t0 < t_end; t0 += kSet) {
     const int cnt = (int)((t_end - t0) < kSet ? (t_end - t0) : kSet);
+    // body: this 64-token set's rows in each plane (t0 is a multiple of 64, and a set
+    // lies within one page)
+    const uint8_t *kset = nullptr, *vset = nullptr;
+    const _Float16 *kpar = nullptr, *vpar = nullptr;
+    if (!window) {
+      kset = a.codes_k + body_read_offset(a.pg, a.Hkv, a.body_cap, b, g, t0, (int64_t)a.kcode_row);
+      vset = a.codes_v + body_read_offset(a.pg, a.Hkv, a.body_cap, b, g, t0, (int64_t)(a.vset_bytes / kSet));
+      kpar = (const _Float16 *)((const char *)a.par_k + body_read_offset(a.pg, a.Hkv, a.body_cap, b, g, t0, 2 * a.kpar_n));
+      vpar = (const _Float16 *)((const char *)a.par_v + body_read_offset(a.pg, a.Hkv, a.body_cap, b, g, t0, 2 * a.vpar_n));
+    }
     // scores: thread (token tt, head group hg)
     {
       const int tt = tid % kSet, hg = tid / kSet;
       if (tt < cnt) {
         const int64_t ti = t0 + tt;
         if (!window) {
-          const uint8_t *row = kplane + ti * a.kcode_row;
-          float kp0 = (float)kpar[ti * a.kpar_n];
-          float kp1 = a.kpar_n == 2 ? (float)kpar[ti * a.kpar_n + 1] : 0.f;
+          const uint8_t *row = kset + tt * a.kcode_row;
+          float kp0 = (float)kpar[tt * a.kpar_n];
+          float kp1 = a.kpar_n == 2 ? (float)kpar[tt * a.kpar_n + 1] : 0.f;
           for (int hh = hg; hh < G; hh += kThreads / kSet) {
             float dot = 0.f;
             for (int j = 0; j < d; ++j) dot = fmaf(sm.qt[hh][j], (float)k_code(row, d, a.bits_k, j), dot);
@@ -121,8 +127,8 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
             sm.s[hh][tt] = sc * qk_scale;
           }
           if (hg == 0) {
-            sm.pv[tt][0] = (float)vpar[ti * a.vpar_n];
-            sm.pv[tt][1] = a.vpar_n == 2 ? (float)vpar[ti * a.vpar_n + 1] : 0.f;
+            sm.pv[tt][0] = (float)vpar[tt * a.vpar_n];
+            sm.pv[tt][1] = a.vpar_n == 2 ? (float)vpar[tt * a.vpar_n + 1] : 0.f;
           }
         } else {
           const int64_t p = ti < ns ? ti : a.S + sl.nq + (ti - ns);
@@ -167,9 +173,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
         const float p = sm.s[hh][t];
         float v;
         if (!window) {
-          const int64_t ti = t0 + t;
-          const int64_t set = ti / kSet;
-          const int code = v_code(vplane + set * a.vset_bytes, d, a.bits_v, (int)(ti % kSet), j);
+          const int code = v_code(vset, d, a.bits_v, t, j);
           if (a.quant_v == WUSHKV_Q_QUEST) v = ((float)code - 0.5f * (Lv - 1)) * sm.pv[t][0];
           else v = fmaf((float)code, sm.pv[t][0], sm.pv[t][1]);
         } else {

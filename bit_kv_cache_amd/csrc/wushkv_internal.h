@@ -42,6 +42,16 @@ __host__ __device__ inline int64_t n_quantized(int64_t n, int S, int R, int C) {
 constexpr int kMaxRagged = 256;
 enum { kUniform = 0, kRaggedHost = 1, kRaggedDevice = 2 };
 
+// Paged body: the code and parameter planes are pools [num_pages][Hkv][page_tokens
+// rows], and table[b][lp] names the physical page of sequence b's logical page lp (body
+// rows lp * page_tokens ..).  page_tokens is a multiple of 64, so a 64-token value set
+// never spans two pages.  table == nullptr: contiguous planes [B][Hkv][body_cap rows].
+struct PageTable {
+  const int32_t *table;
+  int64_t page_tokens;
+  int max_pages, num_pages;
+};
+
 // Plain-old-data argument blocks handed to kernels by value.
 struct FlushArgs {
   int B, Hkv, d, S, R, C;
@@ -62,6 +72,8 @@ struct FlushArgs {
   float clip;
   int lo_i, hi_i, need_lo, need_hi;
   float lo_t, hi_t;
+  PageTable pg;
+  int64_t body_cap;
 };
 
 struct AppendArgs {
@@ -105,6 +117,8 @@ struct DecodeArgs {
   float *part_o, *part_ml;        // workspace: [B][Hq][P+1][d], [B][Hq][P+1][2]
   float *out;                     // [B][Hq][d]
   int force_generic;              // route to the generic kernel (testing hook)
+  PageTable pg;
+  int64_t body_cap;
 };
 
 // Calibration sums S_g = sum x x^T over the rows of heads h with h / group == g.
@@ -134,6 +148,27 @@ bool decode_fast_direct(const DecodeArgs &a);   // the fast kernel writes out it
 int decode_fast_resident_waves(int G, int bits_v);
 
 // Device helpers ------------------------------------------------------------
+
+// Byte offset of body row u of (batch row b, KV head g) in a plane whose rows are `row`
+// bytes (value codes: a set's bytes / 64).  Contiguous planes: ((b Hkv + g) body_cap + u)
+// row.  Paged: ((page Hkv + g) page_tokens + u mod page_tokens) row, or -1 when the
+// logical page is past the table or its entry outside [0, num_pages).
+template <bool PAGED = true>
+__device__ __forceinline__ int64_t body_offset(const PageTable &pg, int Hkv, int64_t body_cap, int b, int g,
+                                               int64_t u, int64_t row) {
+  if (!PAGED || !pg.table) return (((int64_t)b * Hkv + g) * body_cap + u) * row;
+  const int64_t lp = u / pg.page_tokens;
+  const int page = lp < pg.max_pages ? pg.table[(int64_t)b * pg.max_pages + lp] : -1;
+  if (page < 0 || page >= pg.num_pages) return -1;
+  return (((int64_t)page * Hkv + g) * pg.page_tokens + (u - lp * pg.page_tokens)) * row;
+}
+
+// The same for reads: an invalid page reads page 0 (never outside the pool).
+__device__ __forceinline__ int64_t body_read_offset(const PageTable &pg, int Hkv, int64_t body_cap, int b, int g,
+                                                    int64_t u, int64_t row) {
+  const int64_t off = body_offset(pg, Hkv, body_cap, b, g, u, row);
+  return off >= 0 ? off : ((int64_t)g * pg.page_tokens + u % pg.page_tokens) * row;
+}
 
 // Tokens attended by sequence b and its body tokens Q(n).
 struct SeqLen {

@@ -277,6 +277,52 @@ int wushkv_decode_attention_device(const wushkv_cache *c, const int32_t *seq_n, 
                                    size_t workspace_bytes, float *out, void *stream);
 
 /*
+ * Paged body (the serving case of the WUSH-KV digest, "takeaways": the cache sits in a
+ * serving stack's cache manager, which hands out fixed-size blocks).  Only the quantized
+ * body grows with a sequence, so only it is paged; the FP16 windows stay [batch]
+ * [num_kv_heads][...] as in wushkv_cache.  With a page table the cache's code and
+ * parameter planes are pools:
+ *   codes_k  u8  [num_pages][num_kv_heads][page_tokens][d * bits_k / 8]
+ *   codes_v  u8  [num_pages][num_kv_heads][page_tokens / 64][64-token value set]
+ *   par_k/v  f16 [num_pages][num_kv_heads][page_tokens][1 or 2]
+ * and body row u (token sink + u) of sequence b lives on page table[b][u / page_tokens],
+ * row u mod page_tokens.  Each row has the same layout as in the contiguous planes.
+ *   table        device int32 [batch][max_pages], caller-owned, 4-byte aligned; entries
+ *                of pages a sequence does not reach are never read.
+ *   page_tokens  a multiple of 64 (a value set never spans two pages).
+ *   max_pages    logical pages per sequence: max_pages * page_tokens must cover the
+ *                body of a full sequence (else ERR_CAPACITY).
+ *   num_pages    physical pages in each pool.
+ * An entry outside [0, num_pages) is never written through (the flush skips those rows)
+ * and reads as page 0, so no access leaves the pools.  Which physical pages a sequence
+ * uses, and their reuse, is the caller's business.
+ */
+typedef struct {
+  const int32_t *table;
+  int32_t page_tokens, max_pages, num_pages;
+} wushkv_pages;
+
+/* Bytes of plane `plane` of a paged cache: the pool size for code and parameter planes,
+ * wushkv_plane_bytes for the window planes; 0 for invalid arguments. */
+size_t wushkv_pool_bytes(const wushkv_cache *c, const wushkv_pages *pages, int plane);
+
+/* wushkv_append_flush_ragged on a paged cache.  Errors as wushkv_append_flush_ragged,
+ * plus the page-table checks (pages or its table NULL -> ERR_NULL, table misaligned ->
+ * ERR_ALIGN, page_tokens / max_pages / num_pages invalid -> ERR_SHAPE, pages too few
+ * for a full sequence -> ERR_CAPACITY). */
+int wushkv_append_flush_paged(const wushkv_cache *c, const wushkv_pages *pages, const int64_t *n_before,
+                              int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype,
+                              const void *t_k_f16, void *stream);
+
+/* wushkv_decode_attention_ragged on a paged cache; errors as that call plus the
+ * page-table checks.  The workspace is sized by wushkv_decode_workspace_bytes as for the
+ * unpaged cache. */
+int wushkv_decode_attention_paged(const wushkv_cache *c, const wushkv_pages *pages, const int64_t *n_tokens,
+                                  const void *q, int32_t q_dtype, const float *t_k_inv_t, float *q_t,
+                                  int32_t num_q_heads, int32_t num_splits, void *workspace,
+                                  size_t workspace_bytes, float *out, void *stream);
+
+/*
  * Calibration statistics (WUSH-KV digest, "method key points": per KV head, the key
  * transform's Hessian is the sum of Q Q^T over the query heads that read the key and
  * the Gram matrices are the sums over the keys and values themselves; "takeaways": the

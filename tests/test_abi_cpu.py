@@ -233,3 +233,40 @@ def test_device_count_validation(lib):
     big = _spec(batch=300).desc()      # no per-sequence array in the launch: any batch size
     _fake_planes(big)
     assert fa(ctypes.byref(big), kv, 0, kv, kv, W.DT_BF16, kv, None) == W.OK
+
+
+def test_paged_validation_and_pool_bytes(lib):
+    """Page-table checks on the host and pool sizes (no launches)."""
+    s = _spec(batch=3)
+    d = s.desc()
+    _fake_planes(d)
+    kv = ctypes.c_void_p(0x900000)
+    arr = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    body = -(-(8256 - 64) // 64) * 64                       # body rows of a full sequence
+    pages = lambda tab=0x800000, pt=256, mp=-(-body // 256), npg=40: W.PagesDesc(tab, pt, mp, npg)
+    fa, fd = lib.wushkv_append_flush_paged, lib.wushkv_decode_attention_paged
+    ok = pages()
+    assert fa(ctypes.byref(d), None, arr(0, 0, 0), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    assert fa(ctypes.byref(d), ctypes.byref(pages(tab=0)), arr(0, 0, 0), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_NULL
+    assert fa(ctypes.byref(d), ctypes.byref(pages(tab=0x800002)), arr(0, 0, 0), 1, kv, kv, W.DT_BF16, kv,
+              None) == W.ERR_ALIGN
+    assert fa(ctypes.byref(d), ctypes.byref(pages(pt=100)), arr(0, 0, 0), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_SHAPE
+    assert fa(ctypes.byref(d), ctypes.byref(pages(npg=0)), arr(0, 0, 0), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_SHAPE
+    assert fa(ctypes.byref(d), ctypes.byref(pages(mp=2)), arr(0, 0, 0), 1, kv, kv, W.DT_BF16, kv,
+              None) == W.ERR_CAPACITY
+    assert fa(ctypes.byref(d), ctypes.byref(ok), arr(0, 3, 5), 0, kv, kv, W.DT_BF16, kv, None) == W.OK   # no-op
+    assert fa(ctypes.byref(d), ctypes.byref(ok), arr(0, 8256, 5), 1, kv, kv, W.DT_BF16, kv, None) == W.ERR_CAPACITY
+    ws = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    assert fd(ctypes.byref(d), ctypes.byref(pages(pt=64 * 3 + 1)), arr(5, 6, 7), kv, W.DT_BF16, None, kv, 32, 0, kv,
+              ws, kv, None) == W.ERR_SHAPE
+    assert fd(ctypes.byref(d), None, arr(5, 6, 7), kv, W.DT_BF16, None, kv, 32, 0, kv, ws, kv, None) == W.ERR_NULL
+    assert fd(ctypes.byref(d), ctypes.byref(ok), arr(5, 0, 7), kv, W.DT_BF16, None, kv, 32, 0, kv, ws, kv,
+              None) == W.ERR_SHAPE
+    # pools: num_pages x Hkv x page_tokens rows; windows as in the unpaged cache
+    pool = lambda plane: lib.wushkv_pool_bytes(ctypes.byref(d), ctypes.byref(ok), plane)
+    rows = 40 * 8 * 256
+    assert pool(4) == rows * 128 * 2 // 8          # codes_k, 2-bit
+    assert pool(5) == rows // 64 * 64 * 128 * 3 // 8   # codes_v, 3-bit sets
+    assert pool(6) == rows * 4 and pool(7) == rows * 2   # affine (s, z) keys, QuEST values
+    assert pool(0) == lib.wushkv_plane_bytes(ctypes.byref(d), 0)
+    assert lib.wushkv_pool_bytes(ctypes.byref(d), ctypes.byref(pages(pt=100)), 4) == 0
