@@ -352,6 +352,75 @@ def run_graph_leg(args):
     return out
 
 
+def run_paged_leg(args):
+    """The batched-serving decode (32 sequences x 32768 tokens, 32/8 heads, affine 2/2)
+    on a paged body beside the contiguous cache: 256-token pages, each sequence's pages
+    scattered over the pool in a seeded random order.  The two are timed alternately
+    (fused decode with the library's split count), and their outputs must be equal."""
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_amd as W
+    from synth import configs, gen
+
+    w = configs.SERVING
+    n, page = w.context, 256
+    k, v = gen.kv_tensors(w, 0, n, "cuda")
+    t16, tinvt = gen.key_transforms(w, 0)
+    t16, tinvt = t16.cuda(), tinvt.cuda()
+    spec = W.CacheSpec(batch=w.batch, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=n, sink=w.sink,
+                       recent=w.recent, chunk=w.chunk, bits_k=w.bits_k, bits_v=w.bits_v, quant_k=W.Q_AFFINE,
+                       quant_v=W.Q_AFFINE, pct_lo=w.pct_lo, pct_hi=w.pct_hi)
+    ca = W.KVCache(spec, "cuda")
+    W.append_flush(ca, k, v, t16)
+    body = -(-(n - w.sink) // 64) * 64
+    mp = -(-body // page)
+    pc = W.PagedKVCache(spec, page, w.batch * mp, max_pages=mp)
+    perm = np.random.default_rng(7).permutation(w.batch * mp).reshape(w.batch, mp).astype(np.int32)
+    pc.table.copy_(torch.from_numpy(perm))
+    W.append_flush_paged(pc, k, v, t16, n_before=[0] * w.batch)
+    del k, v
+    q = gen.queries(w, 0, 0, "cuda")
+    Hq = w.num_q_heads
+    P = W.decode_num_splits(ca, n, Hq, 0)
+    ws = W.decode_workspace(ca, n, Hq, P)
+    oc = torch.empty(w.batch, Hq, w.head_dim, dtype=torch.float32, device="cuda")
+    op, qc, qp = torch.empty_like(oc), torch.empty_like(oc), torch.empty_like(oc)
+    lens = [n] * w.batch
+    fc = lambda: W.decode_attention_ragged(ca, q, q_t=qc, t_inv_t=tinvt, n_tokens=lens, num_splits=P, workspace=ws,
+                                           out=oc)
+    fp = lambda: W.decode_attention_paged(pc, q, q_t=qp, t_inv_t=tinvt, n_tokens=lens, num_splits=P, workspace=ws,
+                                          out=op)
+    fc()
+    fp()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(oc, op))
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        for _ in range(10):
+            fc()
+            fp()
+        torch.cuda.synchronize()
+    res = {"contiguous": [], "paged": []}
+    for _ in range(6):
+        for name, f in (("contiguous", fc), ("paged", fp)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name].append(e0.elapsed_time(e1) / 20 * 1e3)
+    med = {k2: float(np.median(v2)) for k2, v2 in res.items()}
+    log(f"[bench] paged serving decode ({page}-token pages, {mp} per sequence, scattered): paged "
+        f"{med['paged']:.1f} us, contiguous {med['contiguous']:.1f} us per call (medians), outputs equal: {same}")
+    del ca, pc
+    torch.cuda.empty_cache()
+    return {"page_tokens": page, "pages_per_sequence": mp, "splits": P, "outputs_equal": same,
+            "paged_us_per_call": round(med["paged"], 2), "contiguous_us_per_call": round(med["contiguous"], 2),
+            "note": "ragged-call decode with the query transform fused, alternated 6 x 20 calls, medians"}
+
+
 def run_transform_leg(args):
     """Module-output error of the path under different key transforms, on synthetic
     attention modules: 8 modules (layers) of 4 sequences x 1024 tokens, 32 query / 8 KV
@@ -608,6 +677,7 @@ def main():
     ap.add_argument("--no-calib", action="store_true", help="skip the calibration-statistics leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the launch-bound decode-step leg")
     ap.add_argument("--no-transforms", action="store_true", help="skip the key-transform module-error leg")
+    ap.add_argument("--no-paged", action="store_true", help="skip the paged-body decode leg")
     ap.add_argument("--calib-legs", type=str, default="key_gram,value_gram,key_hessian",
                     help="comma-separated sums the calibration leg times")
     ap.add_argument("--settle-s", type=float, default=0.3,
@@ -665,6 +735,7 @@ def main():
     cl = {} if args.no_calib else run_calib_leg(args)
     gl = {} if args.no_graph else run_graph_leg(args)
     tl = {} if args.no_transforms else run_transform_leg(args)
+    pl = {} if args.no_paged else run_paged_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
     traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
@@ -707,6 +778,8 @@ def main():
         line["decode_step_graph"] = gl
     if tl:
         line["transform_module_error"] = tl
+    if pl:
+        line["paged_decode"] = pl
     if cl:
         line["calibration"] = dict(cl, workload=configs_name("CALIB"),
                                    note="bf16 rows; out[g] = sum of x x^T; flop counted as 2 N d^2 per head")

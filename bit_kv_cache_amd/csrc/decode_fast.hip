@@ -451,11 +451,30 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   // waves' streaming rather than forming every wave's tail), then the body sets
   const int nwin = ws1 - ws0;
   const int bq = bg / a.Hkv, gq = bg % a.Hkv;
+  // paged: the wave's pages are read once, lane i holding the (i + lp0)-th logical
+  // page's physical page, and each set takes its own with a readlane; a range of more
+  // than 64 pages reads the table per set.  An invalid entry reads page 0.
+  int lp0 = 0, wave_pages = 0;
+  bool pages_in_lanes = false;
+  if constexpr (PAGED) {
+    lp0 = (int)(s0 / sets_per_page);
+    const int lp_end = (int)((s1 + sets_per_page - 1) / sets_per_page);
+    pages_in_lanes = lp_end - lp0 <= 64;
+    const int lp = lp0 + lane;
+    int pg = 0;
+    if (pages_in_lanes && lp < lp_end && lp < a.pg.max_pages) pg = a.pg.table[(int64_t)bq * a.pg.max_pages + lp];
+    wave_pages = pg < 0 || pg >= a.pg.num_pages ? 0 : pg;
+  }
   auto slot_of = [&](int set) {
     if (!paged) return set;
     const int lp = set / sets_per_page;
-    int page = lp < a.pg.max_pages ? a.pg.table[(int64_t)bq * a.pg.max_pages + lp] : 0;
-    if (page < 0 || page >= a.pg.num_pages) page = 0;   // an invalid entry reads page 0
+    int page;
+    if (pages_in_lanes) {
+      page = __builtin_amdgcn_readlane(wave_pages, lp - lp0);
+    } else {
+      page = lp < a.pg.max_pages ? a.pg.table[(int64_t)bq * a.pg.max_pages + lp] : 0;
+      if (page < 0 || page >= a.pg.num_pages) page = 0;
+    }
     return (page * a.Hkv + gq) * sets_per_page + (set - lp * sets_per_page);
   };
   auto issue = [&](int item, uint8_t *dst) {
