@@ -127,15 +127,11 @@ def run_decode_leg(args):
     torch.cuda.synchronize()
     log(f"[bench] prefill done; splits={P}")
 
-    def step(i, ev=None):
-        if ev is not None:
-            ev[0].record()
-        W.append_flush(cache, steps_k[i], steps_v[i], t16)
-        if ev is not None:
-            ev[1].record()
-        W.decode_attention_fused(cache, qs[i], tinvt, num_splits=P, workspace=ws, out=out, q_t=qt)
-        if ev is not None:
-            ev[2].record()
+    def step(i):
+        # one decode step in one call: append (fused into the decode kernel), flush when
+        # due, decode with the query transform
+        W.decode_step(cache, steps_k[i], steps_v[i], t16, qs[i], tinvt, q_t=qt, num_splits=P, workspace=ws, out=out)
+
 
     # Settle: after idle the chip runs the first few dozen decodes fast, then slower for
     # ~150 launches while its power management adjusts, then steadily.  Decode-only
@@ -162,22 +158,33 @@ def run_decode_leg(args):
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     nbytes = sum(decode_bytes(w, n_start + j + 1) for j in range(args.steps)) / args.steps
-    # The same K steps once more with HIP events (on the library's stream, torch's
-    # current one) around each call: the decode kernel's average launch duration for
-    # the roofline figure, and the step's breakdown.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_breakdown)]
+    # K further steps with HIP events (on the library's stream, torch's current one)
+    # around each call.  A step with no flush due is one launch, the decode kernel with
+    # the append fused: its average is the kernel's launch duration for the roofline.
+    # Steps with a flush due add the flush kernel.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_breakdown)]
     n_ev = cache.n
     for j in range(n_breakdown):
-        step(args.warmup + args.steps + j, evs[j])
+        evs[j][0].record()
+        step(args.warmup + args.steps + j)
+        evs[j][1].record()
     torch.cuda.synchronize()
-    app = sum(e[0].elapsed_time(e[1]) for e in evs) / n_breakdown
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / n_breakdown
-    kern_bytes = sum(decode_bytes(w, n_ev + j + 1) for j in range(n_breakdown)) / n_breakdown
-    log(f"[bench] step {ms_step:.4f} ms; with events around each call: append {app:.4f}, "
-        f"decode with query transform {dec_ms:.4f} ms ({kern_bytes / (dec_ms * 1e-3) / 1e9:.0f} GB/s); "
-        f"decode bytes {nbytes / 1e6:.1f} MB")
-    return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, app_ms=app, bytes=nbytes, splits=P,
-                n=n_start, cache=cache, kern_ms=dec_ms, kern_bytes=kern_bytes)
+
+    def q_of(nn):
+        return w.chunk * (max(0, nn - w.sink - w.recent) // w.chunk)
+
+    flush_due = [q_of(n_ev + j + 1) > q_of(n_ev + j) for j in range(n_breakdown)]
+    plain = [e[0].elapsed_time(e[1]) for e, f in zip(evs, flush_due) if not f]
+    with_flush = [e[0].elapsed_time(e[1]) for e, f in zip(evs, flush_due) if f]
+    dec_ms = sum(plain) / len(plain)
+    flush_ms = sum(with_flush) / len(with_flush) if with_flush else float("nan")
+    kern_bytes = sum(decode_bytes(w, n_ev + j + 1) for j, f in enumerate(flush_due) if not f) / len(plain)
+    log(f"[bench] step {ms_step:.4f} ms; with events around each call: {dec_ms:.4f} ms with no flush due "
+        f"({len(plain)} steps, {kern_bytes / (dec_ms * 1e-3) / 1e9:.0f} GB/s), {flush_ms:.4f} ms with one "
+        f"({len(with_flush)} steps); decode bytes {nbytes / 1e6:.1f} MB")
+    return dict(workload=w, ms_step=ms_step, dec_ms=dec_ms, flush_step_ms=flush_ms, n_flush=len(with_flush),
+                n_plain=len(plain), bytes=nbytes, splits=P, n=n_start, cache=cache, kern_ms=dec_ms,
+                kern_bytes=kern_bytes)
 
 
 def run_flush_leg(args):
@@ -757,14 +764,17 @@ def main():
                    "quant": "percentile-clipped affine 2-bit K and V", "sink": w.sink, "recent": w.recent,
                    "chunk": w.chunk, "splits": dl["splits"], "parallelism": "single GPU"},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "step_breakdown_ms": {"append_flush": round(dl["app_ms"], 5),
-                              "decode_attention_fused": round(dl["dec_ms"], 5),
-                              "note": "HIP-event intervals around each call over K further steps"},
+        "step_breakdown_ms": {"step_no_flush": round(dl["dec_ms"], 5), "step_with_flush": round(dl["flush_step_ms"], 5),
+                              "steps_no_flush": dl["n_plain"], "steps_with_flush": dl["n_flush"],
+                              "note": "a step is one wushkv_decode_step call: the new token's append fused into "
+                                      "the decode kernel, plus the flush kernel when a chunk is due; HIP-event "
+                                      "intervals around each call over K further steps"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "kernel": "decode_fast_kernel<4,2,12>: GQA decode with the query transform in its "
-                               "prologue, one 12-wave workgroup per KV head (12 splits, merged in LDS)",
+                               "prologue and the new token's append fused, one 12-wave workgroup per KV head "
+                               "(12 splits, merged in LDS); duration from the steps with no flush due",
                      "bytes_per_launch": int(dl["kern_bytes"]), "us_per_launch": round(dl["kern_ms"] * 1e3, 2)},
     }
     if fl:

@@ -210,9 +210,11 @@ namespace {
 // Append + flush for a uniform batch (seq_nb == dev_n == nullptr: every sequence holds
 // n_before tokens), a ragged one (sequence b holds seq_nb[b]) or one whose counts live
 // in device memory (dev_n[b]; the call then advances them by n_new).
+// With `deferred`, the append itself is not launched: its arguments are returned for
+// the caller to launch or to fold into the decode (the flush, when due, is launched).
 int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_before, const int64_t *seq_nb,
                       int32_t *dev_n, int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype,
-                      const void *t_k_f16, void *stream) {
+                      const void *t_k_f16, void *stream, AppendArgs *deferred = nullptr) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -290,6 +292,10 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
   } else if (seq_nb) {
     a.ragged = kRaggedHost;
     for (int b = 0; b < g.B; ++b) a.seq_nb[b] = (int32_t)seq_nb[b];
+  }
+  if (deferred) {
+    *deferred = a;
+    return hip_status();
   }
   if (launch_append(a, s) != hipSuccess) return WUSHKV_ERR_HIP;
   if (dev_n && launch_advance(dev_n, g.B, n_new, g.cap, s) != hipSuccess) return WUSHKV_ERR_HIP;
@@ -375,10 +381,12 @@ namespace {
 
 // Decode with q~ given (tinvt == nullptr) or formed from q and T^{-T} into q_t.
 // With dev_n, the counts are read on the device and n_tokens bounds them.
+// validate_only: the checks alone, nothing launched.  app: the step's one-token append,
+// done by the MFMA decode itself or, on the generic path, launched just before it.
 int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_tokens, const int64_t *seq_n,
                 const int32_t *dev_n, const void *q, int32_t q_dtype, float *q_t, const float *tinvt,
                 int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
-                void *stream) {
+                void *stream, const AppendArgs *app = nullptr, bool validate_only = false) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -439,7 +447,18 @@ int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_toke
   // WUSHKV_DECODE_KERNEL=generic routes every decode to the generic kernel (cross-checks)
   const char *kern = getenv("WUSHKV_DECODE_KERNEL");
   a.force_generic = kern && strcmp(kern, "generic") == 0;
+  if (validate_only) return WUSHKV_OK;
   hipGetLastError();
+  if (app) {
+    if (decode_fast_supported(a) && !a.force_generic) {
+      a.append_new = 1;
+      a.in_dtype = app->in_dtype;
+      a.k_new = app->k_new;
+      a.v_new = app->v_new;
+    } else if (launch_append(*app, (hipStream_t)stream) != hipSuccess) {
+      return WUSHKV_ERR_HIP;
+    }
+  }
   if (launch_decode(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
   return hip_status();
 }
@@ -478,6 +497,23 @@ int wushkv_decode_attention_paged(const wushkv_cache *c, const wushkv_pages *pag
   if (!n_tokens || !pages) return WUSHKV_ERR_NULL;
   return decode_impl(c, pages, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
+}
+
+int wushkv_decode_step(const wushkv_cache *c, int64_t n_before, const void *k_new, const void *v_new, int32_t in_dtype,
+                       const void *t_k_f16, const void *q, int32_t q_dtype, const float *t_k_inv_t, float *q_t,
+                       int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                       void *stream) {
+  if (!t_k_inv_t || !k_new || !v_new || !t_k_f16) return WUSHKV_ERR_NULL;
+  if (n_before < 0) return WUSHKV_ERR_SHAPE;
+  // every check first, so that a failing call enqueues nothing
+  int st = decode_impl(c, nullptr, n_before + 1, nullptr, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads,
+                       num_splits, workspace, workspace_bytes, out, stream, nullptr, true);
+  if (st != WUSHKV_OK) return st;
+  AppendArgs app;
+  st = append_flush_impl(c, nullptr, n_before, nullptr, nullptr, 1, k_new, v_new, in_dtype, t_k_f16, stream, &app);
+  if (st != WUSHKV_OK) return st;
+  return decode_impl(c, nullptr, n_before + 1, nullptr, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits,
+                     workspace, workspace_bytes, out, stream, &app);
 }
 
 int wushkv_decode_attention_device(const wushkv_cache *c, const int32_t *seq_n, int64_t max_tokens, const void *q,

@@ -488,7 +488,34 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   // prologue: the first kStages items fill the ring (item k lives in slot k % kStages),
   // queued before the query setup so that the setup overlaps their loads
   for (int k = 0; k < kStages && k < nitems; ++k) issue(k, ring + k * SB);
+  // Fused append of the step's new token (position n - 1, the last of the window list),
+  // by the wave whose window stages end the list: lanes 0-15 take its key, 16-31 its
+  // value.  The loads are queued with the query setup's and the fp16 row is stored to
+  // its sink row or ring slot after it (a token already quantized was written by the
+  // flush); nothing waits for that store.  This wave's own window stage then reads the
+  // row from registers instead: it is written over the stage's staged copy once that
+  // has landed.
+  const bool appender = a.append_new && nwin > 0 && ws1 == (nw + 7) / 8;
+  const int64_t p_new = sl.n - 1;
+  float raw_new[8];
+  if (appender && lane < 32) {
+    const size_t src = (size_t)bg * kD + 8 * (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) raw_new[e] = load_in(lane >= 16 ? a.v_new : a.k_new, a.in_dtype, src + e);
+  }
   setup_queries(a, sm, bg / a.Hkv, (bg % a.Hkv) * G);
+  f16x8 row_new;
+  if (appender && lane < 32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) row_new[e] = (_Float16)raw_new[e];
+    const bool in_sink = p_new < a.S, in_ring = p_new >= a.S + sl.nq;
+    if (in_sink || in_ring) {
+      const int isv = lane >> 4;
+      const uint8_t *dst = in_sink ? (isv ? sinkv : sinkk) + (size_t)p_new * (kD * 2)
+                                   : (isv ? ringv : ringk) + (size_t)((p_new - a.S) % rsz) * (kD * 2);
+      *(f16x8 *)(const_cast<uint8_t *>(dst) + 16 * (lane & 15)) = row_new;
+    }
+  }
 
   // q~ as eight balanced base-8 digits (integers in [-4, 3], exact in e2m1) on one fixed
   // point grid per head, in the rows of NM fp4 A operands: row r of operand m holds
@@ -740,6 +767,13 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   for (int it = 0; it < nwin; ++it) {
     const uint8_t *st = advance(it);
     const int t0 = 8 * (ws0 + it);
+    if (appender && it == nwin - 1) {
+      // the new token is row nw - 1 - t0 of the last stage (key rows at WK, values at WV)
+      if (lane < 32)
+        *(f16x8 *)(const_cast<uint8_t *>(st) + (lane < 16 ? Stage<BV>::WK : Stage<BV>::WV) +
+                   256 * (nw - 1 - t0) + 16 * (lane & 15)) = row_new;
+      __builtin_amdgcn_wave_barrier();
+    }
     window_stage<G, BV, NW>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
   }
   using Yes = std::true_type;

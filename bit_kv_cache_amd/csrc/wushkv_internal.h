@@ -119,6 +119,10 @@ struct DecodeArgs {
   int force_generic;              // route to the generic kernel (testing hook)
   PageTable pg;
   int64_t body_cap;
+  // One new token per sequence, appended by the decode itself (MFMA path): token n - 1
+  // of each sequence comes from k_new / v_new [B][Hkv][1][d] in in_dtype.
+  int append_new, in_dtype;
+  const void *k_new, *v_new;
 };
 
 // Calibration sums S_g = sum x x^T over the rows of heads h with h / group == g.

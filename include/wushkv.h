@@ -215,6 +215,20 @@ int wushkv_decode_attention_fused(const wushkv_cache *c, int64_t n_tokens,
                                   float *out, void *stream);
 
 /*
+ * One decode step (WUSH-KV digest, "method key points": each generated token is
+ * appended, the windows flush as they fill, and the query attends over the whole
+ * cache): wushkv_append_flush of one token per sequence (k_new / v_new [batch]
+ * [num_kv_heads][1][head_dim]) followed by wushkv_decode_attention_fused over the
+ * n_before + 1 tokens, in one call.  On the MFMA path the decode writes the new token's
+ * window rows itself (no separate append launch); the result is bit-identical to the two
+ * calls.  Every check of both calls runs before anything is enqueued; errors as theirs.
+ */
+int wushkv_decode_step(const wushkv_cache *c, int64_t n_before, const void *k_new, const void *v_new,
+                       int32_t in_dtype, const void *t_k_f16, const void *q, int32_t q_dtype,
+                       const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
+                       void *workspace, size_t workspace_bytes, float *out, void *stream);
+
+/*
  * Ragged batches (the serving case of the WUSH-KV digest, "takeaways": the cache sits in
  * a serving stack where the sequences of a batch have different lengths).  Same cache
  * layout; each sequence keeps its own token count, and the window policy applies to each

@@ -270,3 +270,20 @@ def test_paged_validation_and_pool_bytes(lib):
     assert pool(6) == rows * 4 and pool(7) == rows * 2   # affine (s, z) keys, QuEST values
     assert pool(0) == lib.wushkv_plane_bytes(ctypes.byref(d), 0)
     assert lib.wushkv_pool_bytes(ctypes.byref(d), ctypes.byref(pages(pt=100)), 4) == 0
+
+
+def test_decode_step_validation(lib):
+    """Every check of the fused step runs before anything is enqueued."""
+    d = _spec(batch=2).desc()
+    _fake_planes(d)
+    p = ctypes.c_void_p(0x900000)
+    ws = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    f = lambda nb, kn=p, tinv=p, wsb=ws, q=p: lib.wushkv_decode_step(
+        ctypes.byref(d), nb, kn, p, W.DT_BF16, p, q, W.DT_BF16, tinv, p, 32, 0, p, wsb, p, None)
+    assert f(10, tinv=None) == W.ERR_NULL
+    assert f(10, kn=None) == W.ERR_NULL
+    assert f(-1) == W.ERR_SHAPE
+    assert f(8256) == W.ERR_CAPACITY
+    assert f(7999, wsb=ws - 1) == W.ERR_WORKSPACE
+    assert f(10, kn=ctypes.c_void_p(0x900004)) == W.ERR_ALIGN
+    assert f(10, q=ctypes.c_void_p(0x900008)) == W.ERR_ALIGN
