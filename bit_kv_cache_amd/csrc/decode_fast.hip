@@ -399,7 +399,7 @@ __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int 
 // heads h + 4 qd (qd < G / 4).  PV output row r (O lane l holds rows 4 (l / 16) + i,
 // channels 16 ct + l % 16) is head r's hi part for r < G and head r - G's lo part for
 // G <= r < 2 G; the two are summed in the workgroup merge.
-template <int G, int BV, int NW, bool PAGED>
+template <int G, int BV, int NW, bool PAGED, bool APPEND>
 __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
                           f32x4 (&O)[8], float (&m_out)[G / 4], float (&l_out)[G / 4], float (&z_out)[G / 4],
                           float (&wm_out)[G], float (&wl_out)[G], float (&wacc_out)[G][2]) {
@@ -495,7 +495,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   // flush); nothing waits for that store.  This wave's own window stage then reads the
   // row from registers instead: it is written over the stage's staged copy once that
   // has landed.
-  const bool appender = a.append_new && nwin > 0 && ws1 == (nw + 7) / 8;
+  const bool appender = APPEND && nwin > 0 && ws1 == (nw + 7) / 8;
   const int64_t p_new = sl.n - 1;
   float raw_new[8];
   if (appender && lane < 32) {
@@ -886,7 +886,7 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
 }
 
 // nwg_body workgroups per KV head; with one, the workgroup's merge is the output.
-template <int G, int BV, int NW, bool PAGED>
+template <int G, int BV, int NW, bool PAGED, bool APPEND>
 __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int nwg_body) {
   constexpr int NT = 64 * NW;
   __shared__ FastSmem<G, BV, NW> sm;
@@ -919,7 +919,7 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
     ws0 = (int)(nws * part / a.P);
     ws1 = (int)(nws * (part + 1) / a.P);
   }
-  body_wave<G, BV, NW, PAGED>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
+  body_wave<G, BV, NW, PAGED, APPEND>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
   __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -1046,10 +1046,10 @@ int decode_fast_resident_waves(int G, int bits_v) {
   static int cache[2][2] = {{-1, -1}, {-1, -1}};
   int &c = cache[G == 8][bits_v == 3];
   if (c >= 0) return c;
-  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2, kSplitWaves, false>
-                                           : (const void *)decode_fast_kernel<4, 3, kSplitWaves, false>)
-                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2, kSplitWaves, false>
-                                           : (const void *)decode_fast_kernel<8, 3, kSplitWaves, false>);
+  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2, kSplitWaves, false, false>
+                                           : (const void *)decode_fast_kernel<4, 3, kSplitWaves, false, false>)
+                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2, kSplitWaves, false, false>
+                                           : (const void *)decode_fast_kernel<8, 3, kSplitWaves, false, false>);
   int blocks = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * kSplitWaves, 0) != hipSuccess) {
     hipGetLastError();
@@ -1063,9 +1063,12 @@ hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
   const int nwg = decode_fast_partials(a);
   dim3 grid(nwg, a.B * a.Hkv);
   const bool pg = a.pg.table != nullptr;
-#define WUSHKV_FAST(G, BV, NW)                                                                            \
-  if (pg) hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, true>), grid, dim3(64 * NW), 0, s, a, nwg); \
-  else hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, false>), grid, dim3(64 * NW), 0, s, a, nwg)
+  // (the fused append serves the unpaged one-token step only)
+#define WUSHKV_FAST(G, BV, NW)                                                                                   \
+  if (a.append_new) hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, false, true>), grid, dim3(64 * NW), 0, s, a, \
+                                       nwg);                                                                     \
+  else if (pg) hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, true, false>), grid, dim3(64 * NW), 0, s, a, nwg); \
+  else hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, false, false>), grid, dim3(64 * NW), 0, s, a, nwg)
   if (whole_layout(a)) {
     if (a.bits_v == 2) { WUSHKV_FAST(4, 2, kWholeWaves); }
     else { WUSHKV_FAST(4, 3, kWholeWaves); }
