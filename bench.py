@@ -744,7 +744,7 @@ def main():
     tl = {} if args.no_transforms else run_transform_leg(args)
     pl = {} if args.no_paged else run_paged_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
-    traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12>"])
+    traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12, false, true>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": "2-bit GQA decode-attention HBM GB/s (% of peak); flush tokens/s",
