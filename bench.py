@@ -300,7 +300,7 @@ def run_graph_leg(args):
     w = configs.LAYER_8B
     dev = "cuda"
     n0, warm, steps = w.context, 16, 256
-    cap = n0 + 3 * (warm + steps) + 1
+    cap = n0 + 6 * (warm + steps) + 1
     k, v = gen.kv_tensors(w, 0, n0 + 1, dev)
     t16, tinvt = gen.key_transforms(w, 0)
     t16, tinvt = t16.to(dev), tinvt.to(dev)
@@ -326,6 +326,12 @@ def run_graph_leg(args):
         W.append_flush_device(cache, counts, ks, vs, t16)
         W.decode_attention_device(cache, counts, cap, q, t_inv_t=tinvt, q_t=qt, num_splits=P, workspace=ws, out=o)
 
+    def fused_host_step():
+        W.decode_step(cache, ks, vs, t16, q, tinvt, q_t=qt, num_splits=P, workspace=ws, out=o)
+
+    def fused_device_step():
+        W.decode_step_device(cache, counts, cap, ks, vs, t16, q, tinvt, q_t=qt, num_splits=P, workspace=ws, out=o)
+
     def timed(f):
         for _ in range(warm):
             f()
@@ -339,21 +345,30 @@ def run_graph_leg(args):
         return e0.elapsed_time(e1) / steps * 1e3
 
     host_us = timed(host_step)
+    fused_us = timed(fused_host_step)
     counts.fill_(cache.n)
     dev_us = timed(device_step)
+    fdev_us = timed(fused_device_step)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         device_step()
     graph_us = timed(g.replay)
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        fused_device_step()
+    graph_fused_us = timed(g2.replay)
     n_end = int(counts.item())
-    log(f"[bench] 8B-layer decode step ({w.name}, n {n0} -> {n_end}): eager {host_us:.1f} us, eager with device "
-        f"counts {dev_us:.1f} us, graph replay {graph_us:.1f} us")
+    log(f"[bench] 8B-layer decode step ({w.name}, n {n0} -> {n_end}): eager {host_us:.1f} us (fused step "
+        f"{fused_us:.1f}), eager with device counts {dev_us:.1f} us (fused {fdev_us:.1f}), graph replay "
+        f"{graph_us:.1f} us (fused {graph_fused_us:.1f})")
     out = {"workload": w.name, "context_start": n0, "steps_timed": steps, "splits": P,
-           "eager_host_counts_us": round(host_us, 2), "eager_device_counts_us": round(dev_us, 2),
-           "graph_replay_us": round(graph_us, 2),
+           "eager_host_counts_us": round(host_us, 2), "eager_fused_step_us": round(fused_us, 2),
+           "eager_device_counts_us": round(dev_us, 2), "eager_fused_device_step_us": round(fdev_us, 2),
+           "graph_replay_us": round(graph_us, 2), "graph_replay_fused_us": round(graph_fused_us, 2),
            "bytes_per_decode": int(decode_bytes(w, n0)),
-           "note": "append + flush (when due) + decode with the query transform, per step; 3 x (16 + 256) "
-                   "steps past the prefill"}
+           "note": "append + flush (when due) + decode with the query transform, per step: as separate calls "
+                   "(append_flush then decode) or one fused call (decode_step / decode_step_device); 6 x (16 + "
+                   "256) steps past the prefill"}
     del cache
     torch.cuda.empty_cache()
     return out

@@ -22,7 +22,8 @@ EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "
            "wushkv_query_transform", "wushkv_decode_attention", "wushkv_decode_attention_fused",
            "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
            "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device",
-           "wushkv_pool_bytes", "wushkv_append_flush_paged", "wushkv_decode_attention_paged", "wushkv_decode_step")
+           "wushkv_pool_bytes", "wushkv_append_flush_paged", "wushkv_decode_attention_paged", "wushkv_decode_step",
+           "wushkv_decode_step_device")
 
 
 class WushKVError(RuntimeError):
@@ -74,6 +75,8 @@ def lib():
             "wushkv_append_flush_device": (ctypes.c_int, [P, vp, i32, vp, vp, i32, vp, vp]),
             "wushkv_pool_bytes": (sz, [P, ctypes.POINTER(PagesDesc), ctypes.c_int]),
             "wushkv_decode_step": (ctypes.c_int, [P, i64, vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, vp, sz, vp, vp]),
+            "wushkv_decode_step_device": (ctypes.c_int, [P, vp, i64, vp, vp, i32, vp, vp, i32, vp, vp, i32, i32, vp, sz,
+                                                         vp, vp]),
             "wushkv_append_flush_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), i32, vp, vp,
                                                          i32, vp, vp]),
             "wushkv_decode_attention_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), vp, i32,
@@ -491,4 +494,28 @@ def decode_step(cache: KVCache, k_new, v_new, t_k16, q, t_inv_t, q_t=None, num_s
                                     _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream, q.device)),
            "decode_step")
     cache.n = n_before + 1
+    return out, q_t
+
+
+def decode_step_device(cache: KVCache, seq_n, max_tokens, k_new, v_new, t_k16, q, t_inv_t, q_t=None, num_splits=0,
+                       workspace=None, out=None, stream=None):
+    """decode_step with the counts in device memory (int32 tensor [B]): sequence b
+    holds seq_n[b] tokens, receives one, attends seq_n[b] + 1, and seq_n[b] is advanced
+    on the stream.  Nothing is read on the host, so the call can be recorded into a
+    graph and replayed as each following step.  -> (out, q_t)."""
+    import torch
+    B, Hq, d = q.shape
+    if k_new.dtype != v_new.dtype or t_k16.dtype != torch.float16 or k_new.shape[2] != 1:
+        raise ValueError("one new token per sequence, k_new/v_new of one dtype, t_k16 float16")
+    if workspace is None:
+        workspace = decode_workspace(cache, max_tokens, Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if q_t is None:
+        q_t = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_step_device(ctypes.byref(cache.desc), _device_counts(seq_n, B, q.device),
+                                           int(max_tokens), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(t_k16),
+                                           _ptr(q), _dtype_code(q), _ptr(t_inv_t), _ptr(q_t), Hq, num_splits,
+                                           _ptr(workspace), workspace.numel(), _ptr(out), _stream(stream, q.device)),
+           "decode_step_device")
     return out, q_t

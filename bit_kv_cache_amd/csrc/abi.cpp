@@ -214,7 +214,7 @@ namespace {
 // the caller to launch or to fold into the decode (the flush, when due, is launched).
 int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_before, const int64_t *seq_nb,
                       int32_t *dev_n, int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype,
-                      const void *t_k_f16, void *stream, AppendArgs *deferred = nullptr) {
+                      const void *t_k_f16, void *stream, AppendArgs *deferred = nullptr, int64_t dev_cap = -1) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -265,7 +265,7 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
     f.bits_k = g.bits_k; f.bits_v = g.bits_v; f.quant_k = g.quant_k; f.quant_v = g.quant_v;
     f.kpar_n = g.kpar_n; f.vpar_n = g.vpar_n; f.clip = g.clip;
     f.lo_i = g.lo_i; f.hi_i = g.hi_i; f.lo_t = g.lo_t; f.hi_t = g.hi_t; f.need_lo = g.need_lo; f.need_hi = g.need_hi;
-    f.cap = g.cap;
+    f.cap = dev_cap >= 0 && dev_cap < g.cap ? dev_cap : g.cap;
     f.pg = pg;
     f.body_cap = g.body_cap;
     if (dev_n) {
@@ -285,7 +285,7 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
   a.sink_k = (_Float16 *)c->sink_k; a.sink_v = (_Float16 *)c->sink_v;
   a.ring_k = (_Float16 *)c->ring_k; a.ring_v = (_Float16 *)c->ring_v;
   a.sink_bytes = g.sink_bytes; a.ring_bytes = g.ring_bytes;
-  a.cap = g.cap;
+  a.cap = dev_cap >= 0 && dev_cap < g.cap ? dev_cap : g.cap;
   if (dev_n) {
     a.ragged = kRaggedDevice;
     a.dev_n = dev_n;
@@ -386,7 +386,7 @@ namespace {
 int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_tokens, const int64_t *seq_n,
                 const int32_t *dev_n, const void *q, int32_t q_dtype, float *q_t, const float *tinvt,
                 int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
-                void *stream, const AppendArgs *app = nullptr, bool validate_only = false) {
+                void *stream, const AppendArgs *app = nullptr, bool validate_only = false, int dev_add = 0) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -424,6 +424,7 @@ int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_toke
     a.ragged = kRaggedDevice;
     a.dev_n = dev_n;
     a.max_n = n_tokens;
+    a.dev_add = dev_add;
   } else if (seq_n) {
     a.ragged = kRaggedHost;
     for (int b = 0; b < g.B; ++b) a.seq_n[b] = (int32_t)seq_n[b];
@@ -514,6 +515,28 @@ int wushkv_decode_step(const wushkv_cache *c, int64_t n_before, const void *k_ne
   if (st != WUSHKV_OK) return st;
   return decode_impl(c, nullptr, n_before + 1, nullptr, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits,
                      workspace, workspace_bytes, out, stream, &app);
+}
+
+int wushkv_decode_step_device(const wushkv_cache *c, int32_t *seq_n, int64_t max_tokens, const void *k_new,
+                              const void *v_new, int32_t in_dtype, const void *t_k_f16, const void *q, int32_t q_dtype,
+                              const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
+                              void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  if (!seq_n || !t_k_inv_t || !k_new || !v_new || !t_k_f16) return WUSHKV_ERR_NULL;
+  // every check first, so that a failing call enqueues nothing
+  int st = decode_impl(c, nullptr, max_tokens, nullptr, seq_n, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits,
+                       workspace, workspace_bytes, out, stream, nullptr, true, 1);
+  if (st != WUSHKV_OK) return st;
+  AppendArgs app;
+  // a sequence is stepped only while its next length fits max_tokens (<= capacity): the
+  // flush, the append and the count update all skip it otherwise, and its rows are NaN
+  st = append_flush_impl(c, nullptr, 0, nullptr, seq_n, 1, k_new, v_new, in_dtype, t_k_f16, stream, &app,
+                         max_tokens);
+  if (st != WUSHKV_OK) return st;
+  st = decode_impl(c, nullptr, max_tokens, nullptr, seq_n, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits,
+                   workspace, workspace_bytes, out, stream, &app, false, 1);
+  if (st != WUSHKV_OK) return st;
+  if (launch_advance(seq_n, c->batch, 1, max_tokens, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
+  return hip_status();
 }
 
 int wushkv_decode_attention_device(const wushkv_cache *c, const int32_t *seq_n, int64_t max_tokens, const void *q,

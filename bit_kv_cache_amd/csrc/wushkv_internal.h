@@ -100,9 +100,10 @@ struct DecodeArgs {
   int B, Hkv, Hq, G, d, S, R, C;
   int64_t n, nq;                  // tokens attended, body tokens Q(n) (the largest, if ragged)
   int ragged;                     // kRaggedHost: sequence b attends seq_n[b] tokens;
-  int32_t seq_n[kMaxRagged];      // kRaggedDevice: dev_n[b] (device memory), at most max_n
+  int32_t seq_n[kMaxRagged];      // kRaggedDevice: dev_n[b] + dev_add (device memory), at most max_n
   const int32_t *dev_n;
   int64_t max_n;
+  int dev_add;
   int P;                          // body partitions
   const void *q;
   int q_dtype;
@@ -184,7 +185,7 @@ __device__ __forceinline__ SeqLen seq_len(const DecodeArgs &a, int b) {
   if (a.ragged == kUniform) return SeqLen{a.n, a.nq};
   int64_t n;
   if (a.ragged == kRaggedDevice) {
-    n = a.dev_n[b];
+    n = (int64_t)a.dev_n[b] + a.dev_add;
     if (n < 1 || n > a.max_n) n = 0;
   } else {
     n = a.seq_n[b];

@@ -278,6 +278,22 @@ int wushkv_append_flush_device(const wushkv_cache *c, int32_t *seq_n, int32_t n_
                                const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream);
 
 /*
+ * wushkv_decode_step_device: wushkv_decode_step with device counts, for a serving loop
+ * recorded once into a graph: sequence b holds seq_n[b] tokens before the call, receives
+ * one token, attends the seq_n[b] + 1 tokens, and its count is then advanced by one (three
+ * launches: the flush, sized as in wushkv_append_flush_device; the decode, which appends
+ * the token itself on the MFMA path; the count update).  The same result, bit for bit, as
+ * wushkv_decode_step at the same counts.  max_tokens (host, in [1, capacity]) bounds the
+ * lengths: a sequence is stepped while seq_n[b] is in [0, max_tokens - 1]; any other count
+ * leaves that sequence's cache and count unchanged and makes its output rows NaN.
+ */
+int wushkv_decode_step_device(const wushkv_cache *c, int32_t *seq_n, int64_t max_tokens, const void *k_new,
+                              const void *v_new, int32_t in_dtype, const void *t_k_f16, const void *q,
+                              int32_t q_dtype, const float *t_k_inv_t, float *q_t, int32_t num_q_heads,
+                              int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
+                              void *stream);
+
+/*
  * wushkv_decode_attention_device: the decode with sequence b attending seq_n[b] tokens,
  * read on the device.  max_tokens (host, in [1, capacity]) bounds every count: the split
  * count (num_splits = 0) and the workspace size are those of a batch of max_tokens-token

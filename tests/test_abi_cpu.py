@@ -287,3 +287,18 @@ def test_decode_step_validation(lib):
     assert f(7999, wsb=ws - 1) == W.ERR_WORKSPACE
     assert f(10, kn=ctypes.c_void_p(0x900004)) == W.ERR_ALIGN
     assert f(10, q=ctypes.c_void_p(0x900008)) == W.ERR_ALIGN
+
+
+def test_device_step_validation(lib):
+    d = _spec(batch=3).desc()
+    _fake_planes(d)
+    p = ctypes.c_void_p(0x900000)
+    ws = lib.wushkv_decode_workspace_bytes(ctypes.byref(d), 8000, 32, 0)
+    f = lambda cnt=p, mt=8000, wsb=ws, tinv=p: lib.wushkv_decode_step_device(
+        ctypes.byref(d), cnt, mt, p, p, W.DT_BF16, p, p, W.DT_BF16, tinv, p, 32, 0, p, wsb, p, None)
+    assert f(cnt=None) == W.ERR_NULL
+    assert f(tinv=None) == W.ERR_NULL
+    assert f(cnt=ctypes.c_void_p(0x900002)) == W.ERR_ALIGN
+    assert f(mt=0) == W.ERR_SHAPE
+    assert f(mt=9000) == W.ERR_CAPACITY
+    assert f(wsb=ws - 1) == W.ERR_WORKSPACE

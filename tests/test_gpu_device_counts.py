@@ -164,3 +164,80 @@ def test_device_counts_out_of_range():
     torch.cuda.synchronize()
     assert torch.isnan(od[1]).all() and torch.isnan(od[2]).all()
     assert torch.equal(od[0], oh[0]) and torch.equal(od[3], oh[3])
+
+
+@pytest.mark.parametrize("layout", ["split", "whole"])
+def test_device_step_matches_host_counts(layout):
+    """wushkv_decode_step_device (flush, decode with the append fused, count update)
+    against the host-count ragged calls, bitwise, over steps that cross flushes; the
+    whole layout (one 12-wave workgroup per KV head) needs 32 x 8 KV heads."""
+    if layout == "split":
+        w, lengths = configs.SERVING.scaled(batch=len(LENGTHS)), LENGTHS
+    else:
+        w = configs.SERVING.scaled(batch=32)
+        lengths = [1000 + 7 * b for b in range(32)]
+    (ha, dv), k, v, t16, tinvt, cap = _twin_caches(w, lengths, STEPS)
+    counts = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    P = _splits(ha, cap, w.num_q_heads)
+    for step in range(STEPS):
+        ks, vs = _next_tokens(k, v, ha.seq_n)
+        q = gen.queries(w, 0, step, "cuda")
+        W.append_flush_ragged(ha, ks, vs, t16)
+        oh, qh = W.decode_attention_ragged(ha, q, t_inv_t=tinvt, num_splits=P)
+        od, qd = W.decode_step_device(dv, counts, cap, ks, vs, t16, q, tinvt, num_splits=P)
+        torch.cuda.synchronize()
+        assert counts.tolist() == ha.seq_n, step
+        assert torch.equal(qh, qd), step
+        assert torch.equal(oh, od), (step, float((oh - od).abs().max()))
+    _same_planes(ha, dv)
+    say(f"[device step {layout}] {P} splits, {STEPS} steps: equal to the host-count calls")
+
+
+def test_graph_replays_the_fused_device_step():
+    """One wushkv_decode_step_device call recorded into a graph and replayed STEPS
+    times, as the graph test above, against the host-count calls."""
+    w = configs.SERVING.scaled(batch=len(LENGTHS))
+    (ha, dv), k, v, t16, tinvt, cap = _twin_caches(w, LENGTHS, STEPS + 1)
+    counts = torch.tensor(LENGTHS, dtype=torch.int32, device="cuda")
+    P = _splits(ha, cap, w.num_q_heads)
+    B, Hkv, d, Hq = w.batch, w.num_kv_heads, w.head_dim, w.num_q_heads
+    ks_buf = torch.empty((B, Hkv, 1, d), dtype=k.dtype, device="cuda")
+    vs_buf = torch.empty_like(ks_buf)
+    q_buf = torch.empty((B, Hq, d), dtype=gen.queries(w, 0, 0, "cuda").dtype, device="cuda")
+    qt_buf = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    out_buf = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    ws = W.decode_workspace(dv, cap, Hq, P)
+
+    def fill(step):
+        ks, vs = _next_tokens(k, v, ha.seq_n)
+        ks_buf.copy_(ks)
+        vs_buf.copy_(vs)
+        q_buf.copy_(gen.queries(w, 0, step, "cuda"))
+        return ks, vs
+
+    def device_step():
+        W.decode_step_device(dv, counts, cap, ks_buf, vs_buf, t16, q_buf, tinvt, q_t=qt_buf, num_splits=P,
+                             workspace=ws, out=out_buf)
+
+    def host_step(ks, vs):
+        W.append_flush_ragged(ha, ks, vs, t16)
+        return W.decode_attention_ragged(ha, q_buf, t_inv_t=tinvt, num_splits=P)
+
+    ks, vs = fill(0)
+    device_step()                            # eager first step (primes the library)
+    oh, _ = host_step(ks, vs)
+    torch.cuda.synchronize()
+    assert torch.equal(oh, out_buf)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        device_step()
+    torch.cuda.synchronize()
+    for step in range(1, STEPS + 1):
+        ks, vs = fill(step)
+        g.replay()
+        oh, qh = host_step(ks, vs)
+        torch.cuda.synchronize()
+        assert counts.tolist() == ha.seq_n, step
+        assert torch.equal(qh, qt_buf), step
+        assert torch.equal(oh, out_buf), step
+    _same_planes(ha, dv)
