@@ -14,7 +14,6 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 
 int check_dtype(int dt) { return (dt == WUSHKV_DT_F32 || dt == WUSHKV_DT_BF16 || dt == WUSHKV_DT_F16); }
 
-size_t dtype_size(int dt) { return dt == WUSHKV_DT_F32 ? 4 : 2; }
 
 // Order statistics needed for the linear-interpolation percentile at pct.
 void pct_index(int d, double pct, int *i, float *t) {
@@ -248,7 +247,7 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
     for (int b = 0; b < g.B; ++b)
       flush |= n_quantized(seq_nb[b] + n_new, g.S, g.R, g.C) > n_quantized(seq_nb[b], g.S, g.R, g.C);
   }
-  hipGetLastError();
+  (void)hipGetLastError();   // clear an earlier sticky error before launching
   if (flush) {
     // The flush reads ring rows written by earlier calls, so it runs before this
     // call's ring writes (same stream, in order).
@@ -339,7 +338,7 @@ int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtyp
   if (!t_k_inv_t || !q || !q_t) return WUSHKV_ERR_NULL;
   if (misaligned(t_k_inv_t) || misaligned(q) || misaligned(q_t)) return WUSHKV_ERR_ALIGN;
   QtArgs a{t_k_inv_t, q, q_t, q_dtype, batch, num_q_heads, num_kv_heads, head_dim};
-  hipGetLastError();
+  (void)hipGetLastError();   // clear an earlier sticky error before launching
   if (launch_qtransform(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
   return hip_status();
 }
@@ -370,7 +369,7 @@ int wushkv_calib_stats(const void *x, int32_t dtype, int32_t batch, int32_t num_
   a.bpw = calib_batch_per_wg(batch, num_heads / group);
   a.partials = (float *)workspace;
   a.out = out;
-  hipGetLastError();
+  (void)hipGetLastError();   // clear an earlier sticky error before launching
   if (launch_calib(a, (hipStream_t)stream) != hipSuccess) return WUSHKV_ERR_HIP;
   return hip_status();
 }
@@ -449,7 +448,7 @@ int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_toke
   const char *kern = getenv("WUSHKV_DECODE_KERNEL");
   a.force_generic = kern && strcmp(kern, "generic") == 0;
   if (validate_only) return WUSHKV_OK;
-  hipGetLastError();
+  (void)hipGetLastError();   // clear an earlier sticky error before launching
   if (app) {
     if (decode_fast_supported(a) && !a.force_generic) {
       a.append_new = 1;
