@@ -87,3 +87,47 @@ def test_paged_matches_contiguous(wl):
                 want = cont[b, :, lp * PAGE:lp * PAGE + rows]
                 assert np.array_equal(got, want), (p, b, lp)
     say(f"[paged {w.name}] {STEPS} steps: outputs and every page equal to the contiguous cache")
+
+
+def test_paged_invalid_entries_stay_inside_the_pools():
+    """Table entries outside [0, num_pages) are never written through and read as page
+    0: a sequence whose entries are all invalid leaves every pool page untouched, and
+    the other sequences still equal the contiguous cache bit for bit."""
+    w = configs.SERVING.scaled(batch=3)
+    lengths = [900, 1300, 700]
+    cap = max(lengths) + 4
+    k, v = gen.kv_tensors(w, 0, cap, "cuda")
+    t16, tinvt = gen.key_transforms(w, 0)
+    t16, tinvt = t16.cuda(), tinvt.cuda()
+    spec = spec_of(w, capacity=cap)
+    ca = W.KVCache(spec, "cuda")
+    body = -(-(cap - w.sink) // 64) * 64
+    mp = -(-body // PAGE)
+    npages = 2 * mp + 1                       # page 0 is nobody's; sequences 0 and 2 own the rest
+    pc = W.PagedKVCache(spec, PAGE, npages, max_pages=mp)
+    table = np.zeros((3, mp), dtype=np.int32)
+    table[0] = 1 + np.arange(mp)
+    table[1, ::2], table[1, 1::2] = -1, npages + 5          # all invalid
+    table[2] = 1 + mp + np.arange(mp)
+    pc.table.copy_(torch.from_numpy(table))
+    for b, n in enumerate(lengths):
+        W.append_flush(ca.sequence(b), k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous(), t16,
+                       n_before=0)
+        W.append_flush_paged(pc.sequence(b), k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous(), t16,
+                             n_before=[0])
+    ca.seq_n, pc.seq_n = list(lengths), list(lengths)
+    P = W.decode_num_splits(ca, cap, w.num_q_heads, 0)
+    ks = torch.stack([k[b, :, n:n + 1] for b, n in enumerate(lengths)]).contiguous()
+    vs = torch.stack([v[b, :, n:n + 1] for b, n in enumerate(lengths)]).contiguous()
+    W.append_flush_ragged(ca, ks, vs, t16)
+    W.append_flush_paged(pc, ks, vs, t16)
+    q = gen.queries(w, 0, 0, "cuda")
+    oa, _ = W.decode_attention_ragged(ca, q, t_inv_t=tinvt, num_splits=P)
+    op, _ = W.decode_attention_paged(pc, q, t_inv_t=tinvt, num_splits=P)
+    torch.cuda.synchronize()
+    assert torch.equal(oa[0], op[0]) and torch.equal(oa[2], op[2])
+    assert torch.isfinite(op[1]).all()                      # read from page 0: defined, just not this sequence's
+    H, rb = w.num_kv_heads, _row_bytes(spec)
+    for p, r in rb.items():
+        pool = pc.planes[p].cpu().numpy()[: npages * H * PAGE * r].reshape(npages, H, PAGE, r)
+        assert not pool[0].any(), p                          # nothing was written through an invalid entry
