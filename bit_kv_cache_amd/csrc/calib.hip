@@ -32,6 +32,7 @@ constexpr int kTiles = 10;            // upper-triangle 32 x 32 tiles of a 128 x
 constexpr int kCalibThreads = 256;
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -51,34 +52,37 @@ __host__ __device__ constexpr int tile_j(int t) {
 // tokens per instruction) are spread over all banks by it.
 __device__ __forceinline__ int lds_col(int c, int t) { return (((t >> 3) ^ ((c >> 4) & 7)) << 3) | (t & 7); }
 
-// One step of 64 rows, loaded contiguously: 16-byte chunk i of the step's 16 KB goes to
-// thread i % 256 (row i / 16, channels 8 (i % 16) .. + 7), so one load instruction reads
-// four whole rows.  The loads are unconditional (a row past the end re-reads the last
-// row, which the cache still holds, and is zeroed at the store), so the compiler counts
-// the loads in flight exactly instead of draining them.
+// One step of 64 rows: thread t takes rows 4 (t / 16) .. + 3 and the 16-byte chunk t mod 16
+// of each (channels 8 (t mod 16) .. + 7), so one load instruction reads four whole rows.
+// The loads are unconditional (a row past the end re-reads the last row, which the
+// cache still holds, and is zeroed at the store), so the compiler counts the loads in
+// flight exactly instead of draining them.
 __device__ __forceinline__ void load_step(const uint8_t *rows, int64_t t0, int64_t T, int tid, u32x4 (&r)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + kCalibThreads * i;
-    const int64_t t = t0 + c / 16;
-    r[i] = *((const u32x4 *)(rows + (size_t)(t < T ? t : T - 1) * (kCD * 2)) + (c % 16));
+    const int64_t t = t0 + 4 * (tid >> 4) + i;
+    r[i] = *((const u32x4 *)(rows + (size_t)(t < T ? t : T - 1) * (kCD * 2)) + (tid & 15));
   }
 }
 
-// ... stored channel-major (16-bit stores, element by element).
+// ... stored channel-major: for each of its 8 channels the thread packs its four
+// consecutive tokens into 8 bytes (two byte permutes) and writes them with one 64-bit
+// store, which stays inside one 8-token chunk of the permuted row.
 __device__ __forceinline__ void store_step(uint16_t *lds, int tid, int64_t t0, int64_t T, const u32x4 (&r)[4]) {
+  const int tq = 4 * (tid >> 4), ch0 = 8 * (tid & 15);
+  u32x4 x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int c = tid + kCalibThreads * i;
-    const int row = c / 16, ch0 = 8 * (c % 16);
-    const bool valid = t0 + row < T;
+    const bool valid = t0 + tq + i < T;
+    x[i] = valid ? r[i] : (u32x4){0u, 0u, 0u, 0u};
+  }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const unsigned w = valid ? r[i][k] : 0u;
-      const int c0 = ch0 + 2 * k, c1 = c0 + 1;
-      lds[c0 * kPitch + lds_col(c0, row)] = (uint16_t)(w & 0xFFFFu);
-      lds[c1 * kPitch + lds_col(c1, row)] = (uint16_t)(w >> 16);
-    }
+  for (int m = 0; m < 8; ++m) {
+    const unsigned sel = (m & 1) ? 0x07060302u : 0x05040100u;   // the high or low halves
+    const unsigned lo = __builtin_amdgcn_perm(x[1][m >> 1], x[0][m >> 1], sel);
+    const unsigned hi = __builtin_amdgcn_perm(x[3][m >> 1], x[2][m >> 1], sel);
+    const int c = ch0 + m;
+    *(u32x2 *)(lds + c * kPitch + lds_col(c, tq)) = (u32x2){lo, hi};
   }
 }
 
