@@ -911,13 +911,22 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
   if (part < a.P) {
     const SeqLen sl = seq_len(a, b);
     const int64_t nsets = (sl.nq + kSet - 1) / kSet;
-    s0 = nsets * part / a.P;
-    s1 = nsets * (part + 1) / a.P;
     const int64_t ns = sl.n < a.S ? sl.n : a.S;
     const int64_t nw = ns + (sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
     const int64_t nws = (nw + 7) / 8;
     ws0 = (int)(nws * part / a.P);
     ws1 = (int)(nws * (part + 1) / a.P);
+    if (nsets >= a.P) {
+      // an equal share of all items (window stages and sets) per partition: its window
+      // stages as above, sets for the rest (the two shares rounded apart left the
+      // partitions 45-47 items long on the serving shape, now 46 each)
+      const int64_t items = nsets + nws;
+      s0 = items * part / a.P - ws0;
+      s1 = items * (part + 1) / a.P - ws1;
+    } else {
+      s0 = nsets * part / a.P;
+      s1 = nsets * (part + 1) / a.P;
+    }
   }
   body_wave<G, BV, NW, PAGED, APPEND>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
   __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
