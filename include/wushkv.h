@@ -19,12 +19,14 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are device pointers (hipMalloc / torch CUDA memory)
- *     owned by the caller; the library allocates nothing, keeps no state
- *     between calls and never synchronizes the stream.  It is thread-safe.
+ *     owned by the caller; the library allocates nothing, keeps no data
+ *     between calls (only cached device properties) and never synchronizes the
+ *     stream.  It is thread-safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work of a call is enqueued on that stream, in order.
- *   - Tensors are dense, row-major, in the shapes documented; every pointer
- *     must be 16-byte aligned (WUSHKV_ERR_ALIGN otherwise).
+ *   - Tensors are dense, row-major, in the shapes documented; every tensor
+ *     pointer must be 16-byte aligned (WUSHKV_ERR_ALIGN otherwise), except the
+ *     int32 token-count arrays and page tables, which need 4 bytes.
  *   - Every argument check runs on the host before any launch; a failing call
  *     enqueues nothing.  After launching, hipGetLastError() is checked and
  *     mapped to WUSHKV_ERR_HIP.  Faults inside kernels surface at the
@@ -42,13 +44,15 @@
 extern "C" {
 #endif
 
-#define WUSHKV_ABI_VERSION 1
+/* 1: append/flush, query transform, decode (plain and fused).  2: adds the decode
+ * step, ragged, device-count and paged calls, and the calibration sums. */
+#define WUSHKV_ABI_VERSION 2
 
 typedef enum {
   WUSHKV_OK = 0,
   WUSHKV_ERR_NULL = 1,        /* a required pointer is NULL                       */
   WUSHKV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent           */
-  WUSHKV_ERR_UNSUPPORTED = 3, /* valid request this build does not implement      */
+  WUSHKV_ERR_UNSUPPORTED = 3, /* a valid request the library does not implement   */
   WUSHKV_ERR_CAPACITY = 4,    /* token count beyond the cache capacity            */
   WUSHKV_ERR_WORKSPACE = 5,   /* decode workspace missing or too small            */
   WUSHKV_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned                 */

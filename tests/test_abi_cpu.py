@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     assert W.status_string(0) == "ok"
     assert "capacity" in W.status_string(W.ERR_CAPACITY)
     assert W.status_string(99) == "unknown status"
-    assert lib.wushkv_abi_version() == 1
+    assert lib.wushkv_abi_version() == 2
 
 
 def _spec(**kw):
