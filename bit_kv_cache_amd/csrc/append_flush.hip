@@ -81,7 +81,10 @@ constexpr int kStepTok = 128;      // body tokens per workgroup step (two V sets
 // decision boundary is decided again from its exact value in fp64.  Keys carry
 // the fp32 accumulation error of the MFMA contraction (at most 6.2e-6 bins at 4
 // bits, 1.5e-6 at 2 bits, over 1.3e8 transformed keys of the bulk-flush
-// workload); values only the rounding of the scale's reciprocal and of one product.
+// workload).  In bins that error grows with the number of levels L (a bin is 1/L of
+// the clip range, resp. 1/(L-1) of the percentile range), so the key distance is
+// kEdgeK * L / 16: the same eightfold margin at every width.  Values carry only the
+// rounding of the scale's reciprocal and of one product.
 constexpr float kEdgeK = 5e-5f;
 constexpr float kEdgeV = 1e-5f;
 
@@ -279,8 +282,8 @@ __device__ __forceinline__ int exact_code(double x, float sc, float zp, int quan
 // rint((x - z)/s), half to even.  Codes are clamped to [0, L-1].  Both are taken as
 // floor(v) of v = x/step + L/2 + tol, resp. (x - z)/s + 1/2 + tol: that equals the
 // code unless the unshifted value lies within tol (bins) of a decision boundary,
-// which is exactly when frac(v) < 2 tol.  The row keeps the smallest frac(v); rows
-// that reach the band are decided again in fp64.  A zero step / scale gives the
+// which is exactly when frac(v) < 2 tol.  The smallest frac(v) of each group of four
+// elements is kept; the elements of groups that reach the band are decided again in fp64.  A zero step / scale gives the
 // degenerate code (L/2, resp. 0) and no boundary.
 template <bool QU>
 struct Quant {
@@ -487,13 +490,14 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             *(unsigned *)pk = pack_f16(sc, zp);
           }
         }
-        const Quant<QU> qk = make_quant<QU>(sc, zp, Lk, kEdgeK);
-        float e = 1.0f;
+        const Quant<QU> qk = make_quant<QU>(sc, zp, Lk, kEdgeK * (float)Lk * (1.0f / 16.0f));
+        float e[NCT];   // per group of 4 elements, so a recheck visits only the near groups
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           float c0, c1, c2, c3;
-          code2(qk, acc[ct][0], acc[ct][1], e, c0, c1);
-          code2(qk, acc[ct][2], acc[ct][3], e, c2, c3);
+          e[ct] = 1.0f;
+          code2(qk, acc[ct][0], acc[ct][1], e[ct], c0, c1);
+          code2(qk, acc[ct][2], acc[ct][3], e[ct], c2, c3);
           unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(c0, 0, 0u);
           w = __builtin_amdgcn_cvt_pk_u8_f32(c1, 1, w);
           w = __builtin_amdgcn_cvt_pk_u8_f32(c2, 2, w);
@@ -502,15 +506,20 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         }
         // elements near a boundary: the 4 lanes of a token take one candidate at a
         // time, each summing its CPL channels' exact products in fp64
-        const bool kn = vt && edge_near(qk, e);
+        float emin = e[0];
+#pragma unroll
+        for (int ct = 1; ct < NCT; ++ct) emin = fminf(emin, e[ct]);
+        const bool kn = vt && edge_near(qk, emin);
         if (__any(kn)) {
           unsigned m = 0;
           if (kn) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
+              if (e[ct] < qk.band) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                if (value_near(qk, acc[ct][i])) m |= 1u << (4 * ct + i);
+                for (int i = 0; i < 4; ++i)
+                  if (value_near(qk, acc[ct][i])) m |= 1u << (4 * ct + i);
+              }
           }
           while (__any(m != 0)) {
             const unsigned m0 = __shfl(m, tok), m1 = __shfl(m, 16 + tok), m2 = __shfl(m, 32 + tok), m3 = __shfl(m, 48 + tok);
@@ -585,12 +594,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           }
         }
         const Quant<QU> qv = make_quant<QU>(sc, zp, Lv, kEdgeV);
-        float e = 1.0f;
+        float e[CPL / 4];   // per group of 4 elements, as for the keys
 #pragma unroll
         for (int g4 = 0; g4 < CPL / 4; ++g4) {
           float c0, c1, c2, c3;
-          code2(qv, xv[4 * g4], xv[4 * g4 + 1], e, c0, c1);
-          code2(qv, xv[4 * g4 + 2], xv[4 * g4 + 3], e, c2, c3);
+          e[g4] = 1.0f;
+          code2(qv, xv[4 * g4], xv[4 * g4 + 1], e[g4], c0, c1);
+          code2(qv, xv[4 * g4 + 2], xv[4 * g4 + 3], e[g4], c2, c3);
           unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(c0, 0, 0u);
           w = __builtin_amdgcn_cvt_pk_u8_f32(c1, 1, w);
           w = __builtin_amdgcn_cvt_pk_u8_f32(c2, 2, w);
@@ -599,14 +609,27 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           w = quad_transpose(w, selA, selB);
           *(unsigned *)&sm.vc[s2][seg_chan(q, 4 * g4 + (tok & 3))][col + 4 * (tok >> 2)] = w;
         }
-        const bool vn = vt && edge_near(qv, e);
+        float emin = e[0];
+#pragma unroll
+        for (int g4 = 1; g4 < CPL / 4; ++g4) emin = fminf(emin, e[g4]);
+        const bool vn = vt && edge_near(qv, emin);
         if (__any(vn)) {
+          unsigned m = 0;
           if (vn) {
 #pragma unroll
-            for (int k = 0; k < CPL; ++k)
-              if (value_near(qv, xv[k]))
-                sm.vc[s2][seg_chan(q, k)][col + tok] =
-                    (uint8_t)exact_code((double)xv[k], sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lv);
+            for (int g4 = 0; g4 < CPL / 4; ++g4)
+              if (e[g4] < qv.band) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (value_near(qv, xv[4 * g4 + i])) m |= 1u << (4 * g4 + i);
+              }
+          }
+          // one near element per pass (a rolled loop keeps this rare path small)
+          while (m != 0) {
+            const int k = __builtin_ctz(m);
+            m &= m - 1;
+            sm.vc[s2][seg_chan(q, k)][col + tok] =
+                (uint8_t)exact_code((double)pick<CPL>(xv, k), sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lv);
           }
         }
       };
