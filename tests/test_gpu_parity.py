@@ -305,3 +305,27 @@ def test_degenerate_rows():
         r.append(1)
         q, qt, out = r.decode(0)
         r.check_decode(q, qt, out)
+
+
+def test_value_rows_on_decision_boundaries():
+    """Value rows whose elements sit exactly on the affine decision boundaries: with two
+    channels at 0 and two at 3, the percentile range is [0, 3], so the 2-bit scale is 1
+    and the zero 0, and the other channels take 0.5, 1.5 and 2.5 (exact in bf16).  Every
+    such element is a tie, decided again in fp64 by the flush (round half to even: codes
+    0, 2, 2), up to 124 per row and 32 per lane.  No mismatch is allowed, not even in the
+    band the parity rule admits."""
+    w = configs.SERVING.scaled(name="value_ties", seed=37, batch=1, num_kv_heads=2, num_q_heads=8,
+                               context=700, decode_steps=1, chunk=16)
+    r = Run(w)
+    d = w.head_dim
+    base = torch.tensor([0.0, 0.0, 3.0, 3.0] + [0.5, 1.5, 2.5] * ((d - 4) // 3) + [1.5] * ((d - 4) % 3))
+    rows = torch.stack([torch.roll(base, 7 * i) for i in range(700)]).to(r.v.dtype).to(r.v.device)
+    r.v[0, 0, 64:600] = rows[64:600]
+    r.v[0, 1, 200:400] = rows[200:400]
+    r.append(w.context)
+    _, stats = r.check_cache()
+    say(f"[value ties] {stats}")
+    assert stats["code_mism"] == 0, stats
+    r.append(1)
+    q, qt, out = r.decode(0)
+    r.check_decode(q, qt, out)
