@@ -10,6 +10,7 @@ import torch
 
 import bit_kv_cache_amd as W
 from synth import configs, gen
+from synth import transforms as TR
 from tests.parity_util import Run, say
 
 pytestmark = pytest.mark.gpu
@@ -325,6 +326,30 @@ def test_value_rows_on_decision_boundaries():
     r.append(w.context)
     _, stats = r.check_cache()
     say(f"[value ties] {stats}")
+    assert stats["code_mism"] == 0, stats
+    r.append(1)
+    q, qt, out = r.decode(0)
+    r.check_decode(q, qt, out)
+
+
+def test_key_rows_on_decision_boundaries():
+    """The same ties on the key side.  With T_K the identity the contraction is exact
+    (products k * 1 and k * 0), so key rows built like the value rows above land exactly
+    on the boundaries, and every tie goes through the per-token fp64 dot product, one
+    candidate per pass of the four lanes of a token (up to 124 passes per tile)."""
+    w = configs.SERVING.scaled(name="key_ties", seed=41, batch=1, num_kv_heads=2, num_q_heads=8,
+                               context=700, decode_steps=1, chunk=16)
+    r = Run(w)
+    d, H = w.head_dim, w.num_kv_heads
+    t16, tinvt = TR.as_inputs(TR.per_head(np.eye(d), H))
+    r.t16_cpu, r.t16, r.tinvt = t16, t16.to(r.k.device), tinvt.to(r.k.device)
+    base = torch.tensor([0.0, 0.0, 3.0, 3.0] + [0.5, 1.5, 2.5] * ((d - 4) // 3) + [1.5] * ((d - 4) % 3))
+    rows = torch.stack([torch.roll(base, 5 * i) for i in range(700)]).to(r.k.dtype).to(r.k.device)
+    r.k[0, 0, 64:600] = rows[64:600]
+    r.k[0, 1, 100:300] = rows[100:300]
+    r.append(w.context)
+    _, stats = r.check_cache()
+    say(f"[key ties] {stats}")
     assert stats["code_mism"] == 0, stats
     r.append(1)
     q, qt, out = r.decode(0)
