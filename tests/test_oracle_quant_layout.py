@@ -244,7 +244,8 @@ def _codes_v(d, rule):
     u = np.arange(64)[:, None]
     j = np.arange(d)[None, :]
     f = {"u//16": u // 16 + 0 * j, "u%4": u % 4 + 0 * j, "(u//4)%4": (u // 4) % 4 + 0 * j,
-         "j%4": j % 4 + 0 * u, "4+u%4": 4 + u % 4 + 0 * j}
+         "j%4": j % 4 + 0 * u, "4+u%4": 4 + u % 4 + 0 * j, "4*(u%4)+u//16": 4 * (u % 4) + u // 16 + 0 * j,
+         "4*(j//16)+j%4": 4 * (j // 16) + j % 4 + 0 * u}
     return f[rule]
 
 
@@ -269,6 +270,22 @@ def test_pack_v_worked_words():
     raw = LY.pack_v(_codes_v(int(d), rule), int(bits))[0]
     assert np.frombuffer(raw[:256].tobytes(), "<u4").tolist() == [int(p0.split()[2], 16)] * 64
     assert np.frombuffer(raw[256:].tobytes(), "<u2").tolist() == [int(p1.split()[2], 16)] * 64
+
+
+def test_pack_v_worked_words_4bit():
+    # plane 1 of a 4-bit value set: its offset, shifts and word index, by hand
+    for spec, p0, p1 in _golden("pack_worked.txt")["v4"]:
+        d, bits, rule = spec.split()
+        d = int(d)
+        raw = LY.pack_v(_codes_v(d, rule), int(bits))[0]
+        nw = 64 * d // 16
+        for plane, text in ((0, p0), (1, p1)):
+            name, kind, *vals = text.split()
+            assert name == f"plane{plane}" and kind == "cycle"
+            want = [int(vals[i % len(vals)], 16) for i in range(nw)]
+            got = np.frombuffer(raw[4 * nw * plane:4 * nw * (plane + 1)].tobytes(), "<u4").tolist()
+            assert got == want, (spec, plane)
+        assert np.array_equal(LY.unpack_v(raw, int(bits), d, 64), _codes_v(d, rule))
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
