@@ -23,7 +23,7 @@ EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "
            "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
            "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device",
            "wushkv_pool_bytes", "wushkv_append_flush_paged", "wushkv_decode_attention_paged", "wushkv_decode_step",
-           "wushkv_decode_step_device")
+           "wushkv_decode_step_device", "wushkv_decode_attention_generic")
 
 
 class WushKVError(RuntimeError):
@@ -79,6 +79,8 @@ def lib():
                                                          vp, vp]),
             "wushkv_append_flush_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), i32, vp, vp,
                                                          i32, vp, vp]),
+            "wushkv_decode_attention_generic": (ctypes.c_int, [P, ctypes.POINTER(i64), vp, i32, vp, vp, i32, i32, vp,
+                                                               sz, vp, vp]),
             "wushkv_decode_attention_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), vp, i32,
                                                              vp, vp, i32, i32, vp, sz, vp, vp]),
             "wushkv_decode_attention_device": (ctypes.c_int, [P, vp, i64, vp, i32, vp, vp, i32, i32, vp, sz, vp,
@@ -345,6 +347,31 @@ def decode_attention_ragged(cache: KVCache, q, q_t=None, t_inv_t=None, n_tokens=
                                                 _dtype_code(q), None if t_inv_t is None else _ptr(t_inv_t),
                                                 _ptr(q_t), Hq, num_splits, _ptr(workspace), workspace.numel(),
                                                 _ptr(out), _stream(stream, q.device)), "decode_attention_ragged")
+    return out, q_t
+
+
+def decode_attention_generic(cache: KVCache, q, q_t=None, t_inv_t=None, n_tokens=None, num_splits=0, workspace=None,
+                             out=None, stream=None):
+    """decode_attention_ragged on the library's plain fp32 decode kernel (every shape,
+    no matrix cores): an independent second decode of the same cache for cross-checks.
+    n_tokens defaults to cache.seq_n, else cache.n for every sequence.  -> (out, q_t)."""
+    import torch
+    B, Hq, d = q.shape
+    if n_tokens is None:
+        n_tokens = cache.seq_n if cache.seq_n is not None else [cache.n] * B
+    n_tokens = list(n_tokens)
+    if workspace is None:
+        workspace = decode_workspace(cache, max(n_tokens), Hq, num_splits)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if q_t is None:
+        if t_inv_t is None:
+            raise ValueError("decode_attention_generic needs q_t or t_inv_t")
+        q_t = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention_generic(ctypes.byref(cache.desc), _i64_array(n_tokens), _ptr(q),
+                                                 _dtype_code(q), None if t_inv_t is None else _ptr(t_inv_t),
+                                                 _ptr(q_t), Hq, num_splits, _ptr(workspace), workspace.numel(),
+                                                 _ptr(out), _stream(stream, q.device)), "decode_attention_generic")
     return out, q_t
 
 

@@ -1,7 +1,6 @@
 // Host side of libwushkv: argument validation, plane geometry and dispatch of the
 // gfx950 kernels.  Every check runs before anything is enqueued.
 #include <math.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include "wushkv_internal.h"
@@ -388,7 +387,8 @@ namespace {
 int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_tokens, const int64_t *seq_n,
                 const int32_t *dev_n, const void *q, int32_t q_dtype, float *q_t, const float *tinvt,
                 int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes, float *out,
-                void *stream, const AppendArgs *app = nullptr, bool validate_only = false, int dev_add = 0) {
+                void *stream, const AppendArgs *app = nullptr, bool validate_only = false, int dev_add = 0,
+                bool force_generic = false) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -447,9 +447,7 @@ int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_toke
   a.part_o = (float *)workspace;
   a.part_ml = a.part_o + rows * g.d;
   a.out = out;
-  // WUSHKV_DECODE_KERNEL=generic routes every decode to the generic kernel (cross-checks)
-  const char *kern = getenv("WUSHKV_DECODE_KERNEL");
-  a.force_generic = kern && strcmp(kern, "generic") == 0;
+  a.force_generic = force_generic;   // wushkv_decode_attention_generic
   if (validate_only) return WUSHKV_OK;
   (void)hipGetLastError();   // clear an earlier sticky error before launching
   if (app) {
@@ -491,6 +489,14 @@ int wushkv_decode_attention_ragged(const wushkv_cache *c, const int64_t *n_token
   if (!n_tokens) return WUSHKV_ERR_NULL;
   return decode_impl(c, nullptr, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
                      workspace_bytes, out, stream);
+}
+
+int wushkv_decode_attention_generic(const wushkv_cache *c, const int64_t *n_tokens, const void *q, int32_t q_dtype,
+                                    const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
+                                    void *workspace, size_t workspace_bytes, float *out, void *stream) {
+  if (!n_tokens) return WUSHKV_ERR_NULL;
+  return decode_impl(c, nullptr, 0, n_tokens, nullptr, q, q_dtype, q_t, t_k_inv_t, num_q_heads, num_splits, workspace,
+                     workspace_bytes, out, stream, nullptr, false, 0, true);
 }
 
 int wushkv_decode_attention_paged(const wushkv_cache *c, const wushkv_pages *pages, const int64_t *n_tokens,

@@ -117,7 +117,7 @@ struct DecodeArgs {
   int bits_k, bits_v, quant_k, quant_v, kpar_n, vpar_n;
   float *part_o, *part_ml;        // workspace: [B][Hq][P+1][d], [B][Hq][P+1][2]
   float *out;                     // [B][Hq][d]
-  int force_generic;              // route to the generic kernel (testing hook)
+  int force_generic;              // the generic kernel for every shape (wushkv_decode_attention_generic)
   PageTable pg;
   int64_t body_cap;
   // One new token per sequence, appended by the decode itself (MFMA path): token n - 1

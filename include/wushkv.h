@@ -45,8 +45,9 @@ extern "C" {
 #endif
 
 /* 1: append/flush, query transform, decode (plain and fused).  2: adds the decode
- * step, ragged, device-count and paged calls, and the calibration sums. */
-#define WUSHKV_ABI_VERSION 2
+ * step, ragged, device-count and paged calls, and the calibration sums.  3: adds
+ * wushkv_decode_attention_generic (the per-call choice of the fp32 decode kernel). */
+#define WUSHKV_ABI_VERSION 3
 
 typedef enum {
   WUSHKV_OK = 0,
@@ -138,7 +139,9 @@ size_t wushkv_plane_bytes(const wushkv_cache *c, int plane);
 int32_t wushkv_decode_num_splits(const wushkv_cache *c, int64_t n_tokens, int32_t num_q_heads,
                                  int32_t num_splits);
 
-/* Bytes of decode workspace needed for these arguments (0 when invalid).  The
+/* Bytes of decode workspace needed for these arguments (0 when invalid).  It takes
+ * n_tokens because the split count, and so the partials' size, follow the body length
+ * (num_splits = 0 lets the library pick it from the body's 64-token sets).  The
  * workspace holds the split-K partials (fp32 [batch][num_q_heads][splits + 1][d]
  * plus [..][2] maxima and sums); no initialisation is needed.  Calls that overlap
  * in time must not share a workspace. */
@@ -181,7 +184,11 @@ int wushkv_query_transform(const float *t_k_inv_t, const void *q, int32_t q_dtyp
                            int32_t head_dim, float *q_t, void *stream);
 
 /*
- * GQA decode attention over the first n_tokens tokens of every sequence:
+ * GQA decode attention over the first n_tokens tokens of every sequence (review blog
+ * "[논문리뷰] WUSH-KV", Key Terms & Definitions: grouped-query attention, several query
+ * heads reading one KV head; WUSH-KV digest, "method key points": the query meets the
+ * transformed keys through q~ = T^{-T} q, so q~ . (T k) = q . k, and the FP16 sink /
+ * recent windows are attended unquantized):
  *   out[b][h] = sum_p softmax_p(s_p) v_p,  s_p = (q . k_p) / sqrt(d) on the FP16 sink
  *   and recent tokens (raw q, raw keys) and s_p = (q~ . x^_p) / sqrt(d) on the body
  *   (q~ from wushkv_query_transform, x^ the dequantized transformed key), v_p the
@@ -200,6 +207,19 @@ int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens,
                             int32_t num_q_heads, int32_t num_splits,
                             void *workspace, size_t workspace_bytes,
                             float *out, void *stream);
+
+/*
+ * wushkv_decode_attention_generic: the decode of wushkv_decode_attention_ragged on the
+ * plain fp32 kernel that serves every supported shape (no matrix cores; slower), chosen
+ * per call.  It is a second, independent decode of the same cache, for callers that
+ * cross-check the matrix-core path: the two agree within fp32 rounding (not bit for
+ * bit).  Arguments, workspace and errors as wushkv_decode_attention_ragged.
+ */
+int wushkv_decode_attention_generic(const wushkv_cache *c, const int64_t *n_tokens,
+                                    const void *q, int32_t q_dtype, const float *t_k_inv_t,
+                                    float *q_t, int32_t num_q_heads, int32_t num_splits,
+                                    void *workspace, size_t workspace_bytes,
+                                    float *out, void *stream);
 
 /*
  * wushkv_decode_attention with the query transform folded in (WUSH-KV digest,
