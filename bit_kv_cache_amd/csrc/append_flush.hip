@@ -22,29 +22,42 @@ constexpr int kThreads = 256;
 
 // ------------------------------------------------------------------ append
 
+// The new tokens of a sequence that land in a window: t in [0, ns) go to the sink, t in
+// [tr, n_new) to the ring; the ones between are quantized straight from the input by the
+// flush kernel.  Returns ns + (n_new - tr).
+__host__ __device__ inline int64_t window_tokens(int64_t n_before, int64_t n_new, int64_t q_after, int S,
+                                                 int64_t &ns, int64_t &tr) {
+  ns = S - n_before;
+  ns = ns < 0 ? 0 : (ns > n_new ? n_new : ns);
+  tr = S + q_after - n_before;
+  tr = tr < ns ? ns : (tr > n_new ? n_new : tr);
+  return ns + (n_new - tr);
+}
+
 __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
-  // one thread per (token, 8-channel group); blockIdx.y = b * Hkv + g
+  // one thread per (window token, 8-channel group); blockIdx.y = b * Hkv + g.  The grid
+  // covers the most window tokens any sequence has, not all n_new tokens.
   const int bg = blockIdx.y;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int groups = a.d / 8;
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.n_new * groups) return;
-  const int64_t t = idx / groups;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = idx / groups;
   const int j0 = (int)(idx % groups) * 8;
   const int64_t n_before = seq_before(a, b);
   if (n_before < 0) return;
   const int64_t q_after = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.q_after;
+  int64_t ns, tr;
+  if (i >= window_tokens(n_before, a.n_new, q_after, a.S, ns, tr)) return;
+  const int64_t t = i < ns ? i : tr + (i - ns);
   const int64_t p = n_before + t;
   _Float16 *dk, *dv;
   if (p < a.S) {
     dk = (_Float16 *)((char *)a.sink_k + bg * a.sink_bytes) + p * a.d;
     dv = (_Float16 *)((char *)a.sink_v + bg * a.sink_bytes) + p * a.d;
-  } else if (p >= a.S + q_after) {
+  } else {
     const int64_t slot = (p - a.S) % (a.R + a.C);
     dk = (_Float16 *)((char *)a.ring_k + bg * a.ring_bytes) + slot * a.d;
     dv = (_Float16 *)((char *)a.ring_v + bg * a.ring_bytes) + slot * a.d;
-  } else {
-    return;  // flushed straight from the input by the flush kernel
   }
   const size_t src = (((size_t)b * a.Hkv + g) * a.n_new + t) * a.d + j0;
   half8 hk, hv;
@@ -774,7 +787,23 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
-  const int64_t work = a.n_new * (a.d / 8);
+  // window tokens of the sequence with the most: exact for host counts; device counts
+  // are unknown here, and a sequence never has more than S + R + C - 1 (the sink, and
+  // a ring that holds fewer than R + C after its flush)
+  int64_t most = 0, ns, tr;
+  if (a.ragged == kRaggedDevice) {
+    most = a.n_new < (int64_t)a.S + a.R + a.C ? a.n_new : (int64_t)a.S + a.R + a.C;
+  } else if (a.ragged == kRaggedHost) {
+    for (int b = 0; b < a.B; ++b) {
+      const int64_t nb = a.seq_nb[b];
+      const int64_t w = window_tokens(nb, a.n_new, n_quantized(nb + a.n_new, a.S, a.R, a.C), a.S, ns, tr);
+      most = w > most ? w : most;
+    }
+  } else {
+    most = window_tokens(a.n_before, a.n_new, a.q_after, a.S, ns, tr);
+  }
+  if (most == 0) return hipSuccess;
+  const int64_t work = most * (a.d / 8);
   dim3 grid((unsigned)((work + kThreads - 1) / kThreads), a.B * a.Hkv);
   hipLaunchKernelGGL(append_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
