@@ -141,6 +141,82 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+def max_head_rel(a, b):
+    """The largest relative L2 error of one (batch row, query head) output row."""
+    a = np.asarray(a, np.float64).reshape(-1, np.shape(a)[-1])
+    b = np.asarray(b, np.float64).reshape(-1, np.shape(b)[-1])
+    return float(np.max(np.linalg.norm(a - b, axis=1) / np.maximum(np.linalg.norm(b, axis=1), 1e-300)))
+
+
+def paged_plane_arrays(pc):
+    """plane_arrays of a paged cache, each sequence's body rows gathered from the pools
+    through its page table into the contiguous layout, so that check_head and
+    device_head_cache read the paged cache itself."""
+    s = pc.spec
+    B, H, d = s.batch, s.num_kv_heads, s.head_dim
+    body_cap = -(-(s.capacity - s.sink) // 64) * 64
+    page = pc.pages.page_tokens
+    npages = pc.pages.num_pages
+    table = pc.table.cpu().numpy()
+    rows = {"codes_k": d * s.bits_k // 8, "codes_v": d * s.bits_v // 8,
+            "par_k": 2 * (1 if s.quant_k == W.Q_QUEST else 2), "par_v": 2 * (1 if s.quant_v == W.Q_QUEST else 2)}
+    out = {}
+    for p in ("sink_k", "sink_v", "ring_k", "ring_v"):
+        n = {"sink": s.sink, "ring": s.recent + s.chunk}[p[:4]]
+        out[p] = pc.planes[p].cpu().numpy()[: B * H * n * d * 2].view(np.float16).reshape(B, H, n, d)
+    for p, r in rows.items():
+        pool = pc.planes[p].cpu().numpy()[: npages * H * page * r].reshape(npages, H, page, r)
+        cont = np.zeros((B, H, body_cap, r), dtype=np.uint8)
+        for b in range(B):
+            for lp in range(-(-body_cap // page)):
+                n = min(page, body_cap - lp * page)
+                cont[b, :, lp * page:lp * page + n] = pool[table[b, lp], :, :n]
+        out[p] = cont
+    kp, vp = rows["par_k"] // 2, rows["par_v"] // 2
+    out["par_k"] = out["par_k"].reshape(B, H, -1).view(np.float16).reshape(B, H, body_cap, kp)
+    out["par_v"] = out["par_v"].reshape(B, H, -1).view(np.float16).reshape(B, H, body_cap, vp)
+    out["codes_k"] = out["codes_k"].reshape(B, H, -1)
+    out["codes_v"] = out["codes_v"].reshape(B, H, -1)
+    out["body_cap"] = body_cap
+    return out
+
+
+def check_decode_lengths(pa, spec, w, k, v, t16, lengths, q, qt, out, heads=None, what="decode", tol=2e-3):
+    """The decode of sequences holding lengths[b] tokens against the oracle, on the
+    sampled (batch row, KV head) pairs (default: all): end to end (the oracle's own cache
+    from the inputs k, v [B, Hkv, >=n, d] and its exact q~), and on the device's own cache
+    contents with the device's q~ (the decode kernel alone).  Reports the pooled and the
+    largest per-(batch row, query head) relative L2 errors."""
+    G = w.group
+    heads = heads or [(b, g) for b in range(len(lengths)) for g in range(w.num_kv_heads)]
+    qn = q.float().cpu().numpy().astype(np.float64)
+    qtn = qt.cpu().numpy().astype(np.float64)
+    on = out.cpu().numpy().astype(np.float64)
+    got, ref_e2e, ref_dev = [], [], []
+    for b, g in heads:
+        n = int(lengths[b])
+        kk = k[b, g].float().cpu().numpy().astype(np.float64)
+        vv = v[b, g].float().cpu().numpy().astype(np.float64)
+        t = t16[g].numpy() if hasattr(t16[g], "numpy") else t16[g]
+        c_or = R.build_head_cache(kk, vv, t, n, sink=w.sink, recent=w.recent, chunk=w.chunk, quant_k=w.quant_k,
+                                  quant_v=w.quant_v, bits_k=w.bits_k, bits_v=w.bits_v, clip_mult=w.clip_mult,
+                                  pct_lo=w.pct_lo, pct_hi=w.pct_hi)
+        c_dev = device_head_cache(pa, spec, b, g, n)
+        for h in range(g * G, (g + 1) * G):
+            got.append(on[b, h])
+            ref_e2e.append(R.decode_head(c_or, qn[b, h], R.query_transform(t, qn[b, h])))
+            ref_dev.append(R.decode_head(c_dev, qn[b, h], qtn[b, h]))
+    e2e, dev = rel_l2(got, ref_e2e), rel_l2(got, ref_dev)
+    e2e_max, dev_max = max_head_rel(got, ref_e2e), max_head_rel(got, ref_dev)
+    say(f"[{what} parity] {len(heads)} KV heads: rel-L2 end-to-end {e2e:.3e} (max per head {e2e_max:.3e}); "
+        f"vs device cache {dev:.3e} (max per head {dev_max:.3e})")
+    assert np.all(np.isfinite(on))
+    assert dev <= 1e-4, dev
+    if tol is not None:
+        assert e2e <= tol, e2e
+    return dict(e2e=e2e, e2e_max=e2e_max, dev=dev, dev_max=dev_max)
+
+
 class Run:
     """A workload run on the device: inputs, transforms, cache, decode steps."""
 
@@ -209,7 +285,9 @@ class Run:
                 ref_dev.append(R.decode_head(c_dev, qn[b, h], qtn[b, h]))
                 got.append(on[b, h])
         e2e, dev = rel_l2(got, ref_e2e), rel_l2(got, ref_dev)
-        say(f"[decode parity] rel-L2 end-to-end {e2e:.3e}  vs device cache {dev:.3e}")
+        e2e_max, dev_max = max_head_rel(got, ref_e2e), max_head_rel(got, ref_dev)
+        say(f"[decode parity] rel-L2 end-to-end {e2e:.3e} (max per head {e2e_max:.3e})  "
+            f"vs device cache {dev:.3e} (max per head {dev_max:.3e})")
         assert np.all(np.isfinite(on))
         assert dev <= 1e-4, dev
         assert e2e <= tol, e2e

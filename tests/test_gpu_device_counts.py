@@ -13,7 +13,7 @@ import torch
 
 import bit_kv_cache_amd as W
 from synth import configs, gen
-from tests.parity_util import say, spec_of
+from tests.parity_util import check_decode_lengths, plane_arrays, say, spec_of
 
 pytestmark = pytest.mark.gpu
 
@@ -175,10 +175,14 @@ def test_device_step_matches_host_counts(layout):
         w, lengths = configs.SERVING.scaled(batch=len(LENGTHS)), LENGTHS
     else:
         w = configs.SERVING.scaled(batch=32)
-        lengths = [1000 + 7 * b for b in range(32)]
+        lengths = [1900 + 7 * b for b in range(32)]
     (ha, dv), k, v, t16, tinvt, cap = _twin_caches(w, lengths, STEPS)
     counts = torch.tensor(lengths, dtype=torch.int32, device="cuda")
     P = _splits(ha, cap, w.num_q_heads)
+    if layout == "whole":
+        assert P == 12, P
+    t16_cpu = gen.key_transforms(w, 0)[0]
+    heads = [(0, 0), (len(lengths) // 2, 3), (len(lengths) - 1, 7)]
     for step in range(STEPS):
         ks, vs = _next_tokens(k, v, ha.seq_n)
         q = gen.queries(w, 0, step, "cuda")
@@ -189,6 +193,10 @@ def test_device_step_matches_host_counts(layout):
         assert counts.tolist() == ha.seq_n, step
         assert torch.equal(qh, qd), step
         assert torch.equal(oh, od), (step, float((oh - od).abs().max()))
+        if step in (0, STEPS - 1):
+            # the device-count step against the oracle itself, on its own cache
+            check_decode_lengths(plane_arrays(dv), dv.spec, w, k, v, t16_cpu, counts.tolist(), q, qd, od,
+                                 heads=heads, what=f"device step {layout}, step {step}")
     _same_planes(ha, dv)
     say(f"[device step {layout}] {P} splits, {STEPS} steps: equal to the host-count calls")
 
@@ -240,4 +248,7 @@ def test_graph_replays_the_fused_device_step():
         assert counts.tolist() == ha.seq_n, step
         assert torch.equal(qh, qt_buf), step
         assert torch.equal(oh, out_buf), step
+    # the last replay against the oracle, on the graph-stepped cache itself
+    check_decode_lengths(plane_arrays(dv), dv.spec, w, k, v, gen.key_transforms(w, 0)[0], counts.tolist(), q_buf,
+                         qt_buf, out_buf, what=f"graph-replayed fused step {STEPS}")
     _same_planes(ha, dv)

@@ -1,11 +1,13 @@
 """Paged body (wushkv_append_flush_paged, wushkv_decode_attention_paged) against the
-contiguous ragged cache.
+oracle and against the contiguous ragged cache.
 
 Paging only moves where each body row lives: every row keeps its layout, the kernels'
 arithmetic is unchanged.  So a paged cache whose sequences map their logical pages to
 physical pages in a shuffled order holds, page by page, exactly the rows of the
-contiguous cache (itself held to the oracle in test_gpu_ragged.py), and decodes to the
-same outputs bit for bit.  Covered: the fast decode's split layout (serving shape), its
+contiguous cache, and decodes to the same outputs bit for bit.  The paged cache itself
+is also held to the oracle: its rows gathered through the page table pass the cache
+parity rule for every (sequence, KV head), and its decode is checked end to end and on
+its own contents.  Covered: the fast decode's split layout (serving shape), its
 3-bit-value path (long-context shape) and the generic kernel (d = 64)."""
 import numpy as np
 import pytest
@@ -13,7 +15,7 @@ import torch
 
 import bit_kv_cache_amd as W
 from synth import configs, gen
-from tests.parity_util import say, spec_of
+from tests.parity_util import check_decode_lengths, check_head, paged_plane_arrays, say, spec_of
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +74,19 @@ def test_paged_matches_contiguous(wl):
         torch.cuda.synchronize()
         assert torch.equal(qa, qp), step
         assert torch.equal(oa, op), (step, float((oa - op).abs().max()))
+    # the paged cache itself against the oracle: every (sequence, KV head), then the last
+    # step's decode end to end and on the paged cache's own contents
+    pa = paged_plane_arrays(pc)
+    stats = {}
+    t16_cpu = gen.key_transforms(w, 0)[0]
+    for b, n in enumerate(pc.seq_n):
+        for g in range(w.num_kv_heads):
+            check_head(pa, spec, b, g, k[b, g].float().cpu().numpy().astype(np.float64),
+                       v[b, g].float().cpu().numpy().astype(np.float64), t16_cpu[g].numpy(), n, stats)
+    if stats.get("code_total"):
+        assert stats["code_mism"] <= 1e-5 * stats["code_total"], stats
+    say(f"[paged {w.name}] paged cache vs oracle after {STEPS} steps: {stats}")
+    check_decode_lengths(pa, spec, w, k, v, t16_cpu, pc.seq_n, q, qp, op, what=f"paged {w.name}", tol=None)
     # windows as they are; body rows page by page
     for p in W.PagedKVCache.WINDOWS:
         assert torch.equal(ca.planes[p], pc.planes[p]), p
