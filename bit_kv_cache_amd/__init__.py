@@ -23,7 +23,7 @@ EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "
            "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
            "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device",
            "wushkv_pool_bytes", "wushkv_append_flush_paged", "wushkv_decode_attention_paged", "wushkv_decode_step",
-           "wushkv_decode_step_device", "wushkv_decode_attention_generic")
+           "wushkv_decode_step_device", "wushkv_decode_attention_generic", "wushkv_decode_attention_noalloc")
 
 
 class WushKVError(RuntimeError):
@@ -79,6 +79,7 @@ def lib():
                                                          vp, vp]),
             "wushkv_append_flush_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), i32, vp, vp,
                                                          i32, vp, vp]),
+            "wushkv_decode_attention_noalloc": (ctypes.c_int, [P, i64, vp, i32, vp, i32, i32, vp, vp]),
             "wushkv_decode_attention_generic": (ctypes.c_int, [P, ctypes.POINTER(i64), vp, i32, vp, vp, i32, i32, vp,
                                                                sz, vp, vp]),
             "wushkv_decode_attention_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), vp, i32,
@@ -262,6 +263,23 @@ def decode_attention(cache: KVCache, q, q_t, n_tokens=None, num_splits=0, worksp
     _check(lib().wushkv_decode_attention(ctypes.byref(cache.desc), n_tokens, _ptr(q), _dtype_code(q), _ptr(q_t),
                                          Hq, num_splits, _ptr(workspace), workspace.numel(), _ptr(out),
                                          _stream(stream, q.device)), "decode_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # WUSHKV_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attention_noalloc(cache: KVCache, q, q_t, n_tokens=None, num_splits=0, out=None, stream=None):
+    """decode_attention with the split-K partials in the library's own fixed device array
+    (no workspace; the call allocates nothing).  Calls overlapping on one GPU race."""
+    import torch
+    n_tokens = cache.n if n_tokens is None else n_tokens
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _check(lib().wushkv_decode_attention_noalloc(ctypes.byref(cache.desc), n_tokens, _ptr(q), _dtype_code(q), _ptr(q_t),
+                                                 Hq, num_splits, _ptr(out), _stream(stream, q.device)),
+           "decode_attention_noalloc")
     return out
 
 

@@ -466,6 +466,17 @@ int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_toke
 
 }  // namespace
 
+namespace wushkv {
+
+int decode_attention_checked(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype, const float *q_t,
+                             int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                             float *out, void *stream, bool validate_only) {
+  return decode_impl(c, nullptr, n_tokens, nullptr, nullptr, q, q_dtype, const_cast<float *>(q_t), nullptr, num_q_heads,
+                     num_splits, workspace, workspace_bytes, out, stream, nullptr, validate_only);
+}
+
+}  // namespace wushkv
+
 extern "C" {
 
 int wushkv_decode_attention(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype,

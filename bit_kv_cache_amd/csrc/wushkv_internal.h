@@ -137,6 +137,11 @@ struct CalibArgs {
   float *out;                     // [H / group][128][128]
 };
 
+// wushkv_decode_attention with every check and, unless validate_only, the launch.
+int decode_attention_checked(const wushkv_cache *c, int64_t n_tokens, const void *q, int32_t q_dtype, const float *q_t,
+                             int32_t num_q_heads, int32_t num_splits, void *workspace, size_t workspace_bytes,
+                             float *out, void *stream, bool validate_only);
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_advance(int32_t *dev_n, int B, int n_new, int64_t cap, hipStream_t s);
 hipError_t launch_calib(const CalibArgs &a, hipStream_t s);

@@ -46,8 +46,9 @@ extern "C" {
 
 /* 1: append/flush, query transform, decode (plain and fused).  2: adds the decode
  * step, ragged, device-count and paged calls, and the calibration sums.  3: adds
- * wushkv_decode_attention_generic (the per-call choice of the fp32 decode kernel). */
-#define WUSHKV_ABI_VERSION 3
+ * wushkv_decode_attention_generic (the per-call choice of the fp32 decode kernel).  4: adds
+ * wushkv_decode_attention_noalloc. */
+#define WUSHKV_ABI_VERSION 4
 
 typedef enum {
   WUSHKV_OK = 0,
@@ -251,6 +252,23 @@ int wushkv_decode_step(const wushkv_cache *c, int64_t n_before, const void *k_ne
                        int32_t in_dtype, const void *t_k_f16, const void *q, int32_t q_dtype,
                        const float *t_k_inv_t, float *q_t, int32_t num_q_heads, int32_t num_splits,
                        void *workspace, size_t workspace_bytes, float *out, void *stream);
+
+/*
+ * wushkv_decode_attention for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  The split-K
+ * partials live in a fixed array inside the library (WUSHKV_NOALLOC_SCRATCH_BYTES per
+ * GPU, held until the process ends) instead of a caller workspace; the call itself
+ * allocates nothing.  Arguments, results and errors as wushkv_decode_attention minus
+ * the workspace; a decode whose wushkv_decode_workspace_bytes() exceeds the array is
+ * rejected with WUSHKV_ERR_WORKSPACE before anything is enqueued.  Every call on a GPU
+ * shares that GPU's array (the partials need no clearing): calls that overlap in time
+ * on one GPU, on any streams, race and must not be issued.
+ */
+#define WUSHKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int wushkv_decode_attention_noalloc(const wushkv_cache *c, int64_t n_tokens,
+                                    const void *q, int32_t q_dtype, const float *q_t,
+                                    int32_t num_q_heads, int32_t num_splits,
+                                    float *out, void *stream);
 
 /*
  * Ragged batches (the serving case of the WUSH-KV digest, "takeaways": the cache sits in
