@@ -14,13 +14,15 @@ bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
 int check_dtype(int dt) { return (dt == WUSHKV_DT_F32 || dt == WUSHKV_DT_BF16 || dt == WUSHKV_DT_F16); }
 
 
-// Order statistics needed for the linear-interpolation percentile at pct.
-void pct_index(int d, double pct, int *i, float *t) {
+// Order statistics needed for the linear-interpolation percentile at pct: the lower
+// index i and the weight t of the next one (fp32 and fp64).
+void pct_index(int d, double pct, int *i, float *t, double *t64) {
   double h = (d - 1) * (pct / 100.0);
   int fi = (int)floor(h);
-  if (fi >= d - 1) { *i = d - 1; *t = 0.0f; return; }
+  if (fi >= d - 1) { *i = d - 1; *t = 0.0f; *t64 = 0.0; return; }
   *i = fi;
-  *t = (float)(h - fi);
+  *t64 = h - fi;
+  *t = (float)*t64;
 }
 
 }  // namespace
@@ -53,10 +55,10 @@ int make_geom(const wushkv_cache *c, Geom *g) {
   G.bits_k = c->bits_k; G.bits_v = c->bits_v;
   G.quant_k = c->quant_k; G.quant_v = c->quant_v;
   G.clip = c->clip_mult;
-  G.lo_i = G.hi_i = 0; G.lo_t = G.hi_t = 0.0f; G.need_lo = G.need_hi = 0;
+  G.lo_i = G.hi_i = 0; G.lo_t = G.hi_t = 0.0f; G.lo_t64 = G.hi_t64 = 0.0; G.need_lo = G.need_hi = 0;
   if (any_aff) {
-    pct_index(G.d, c->pct_lo, &G.lo_i, &G.lo_t);
-    pct_index(G.d, c->pct_hi, &G.hi_i, &G.hi_t);
+    pct_index(G.d, c->pct_lo, &G.lo_i, &G.lo_t, &G.lo_t64);
+    pct_index(G.d, c->pct_hi, &G.hi_i, &G.hi_t, &G.hi_t64);
     G.need_lo = (G.lo_i + 2 < G.d) ? G.lo_i + 2 : G.d;
     G.need_hi = G.d - G.hi_i;
     if (G.need_lo > kMaxOrderStats || G.need_hi > kMaxOrderStats) return WUSHKV_ERR_UNSUPPORTED;
@@ -266,6 +268,7 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
     f.bits_k = g.bits_k; f.bits_v = g.bits_v; f.quant_k = g.quant_k; f.quant_v = g.quant_v;
     f.kpar_n = g.kpar_n; f.vpar_n = g.vpar_n; f.clip = g.clip;
     f.lo_i = g.lo_i; f.hi_i = g.hi_i; f.lo_t = g.lo_t; f.hi_t = g.hi_t; f.need_lo = g.need_lo; f.need_hi = g.need_hi;
+    f.lo_t64 = g.lo_t64; f.hi_t64 = g.hi_t64;
     f.cap = dev_cap >= 0 && dev_cap < g.cap ? dev_cap : g.cap;
     f.pg = pg;
     f.body_cap = g.body_cap;

@@ -101,14 +101,51 @@ constexpr int kStepTok = 128;      // body tokens per workgroup step (two V sets
 constexpr float kEdgeK = 5e-5f;
 constexpr float kEdgeV = 1e-5f;
 
+// fp16 parameters are re-decided in fp64 when their fp32 value lies within these
+// relative distances of an fp16 rounding midpoint (measured on gfx950 over 2.6e5 keys of
+// the bulk-flush workload: the contraction's fp32 error moves a key row's sum of squares
+// by at most 1.2e-7 and an extreme element by at most 4.9e-7 of itself; a row's fp32
+// sum of squares, a chain of 12 roundings, by at most 7.2e-7).
+//   kParV:    values (their x is exact): the fp32 arithmetic alone.
+//   kParKA:   QuEST keys, first stage: all of the fp32 error; the step is then taken
+//             from the fp64 sum of squares of the fp32 x.
+//   kParKB:   QuEST keys, second stage: the contraction's error alone (3x); such rows get
+//             the exact sum of squares from fp64 dot products.
+//   kParKAff: affine keys: the extreme elements' error and the fp32 interpolation (3x);
+//             such rows get their order
+//             statistics from exact fp64 dot products.
+constexpr float kParV = 1.2e-6f;
+constexpr float kParKA = 1.5e-6f;
+constexpr float kParKB = 2e-7f;
+constexpr float kParKAff = 2.5e-6f;
+constexpr float kParKAff2 = 1.5e-6f;   // affine keys after the fp64 interpolation: the elements' error (3x)
+constexpr int kDefer = 32;     // key rows per wave and step queued for exact parameters (all of them)
+constexpr int kStaged = 2;     // of those, per wave, the first ones whose fp16 key row is kept in LDS
+constexpr int kMaxCand = 16;   // affine: order-statistic candidates resolved exactly per row
+
+// A queued key row: its row in the step; affine: each of its four lanes' candidate
+// elements (bit 4 ct + i = out channel 16 ct + 4 q + i) with the cuts, and the first
+// stage's parameters.
+struct DeferRow {
+  unsigned cm[4];
+  float clo, chi, mg, sc, zp;
+  int row;
+};
+
 template <int D>
-struct FlushSmem {
+struct __align__(16) FlushSmem {
   static constexpr int TP = D + 8;      // T_K row pitch (halves)
   static constexpr int KP = D + 16;     // key-code row pitch (bytes; rows stay 16-byte aligned)
   static constexpr int VP = kSet + 4;   // value-code row pitch (bytes), one row per channel
   _Float16 t[D][TP];
   uint8_t kc[kStepTok][KP];
   uint8_t vc[2][D][VP];
+  unsigned krow[D / 2];                 // one key row's fp16 pairs (exact re-decisions)
+  double red[4][2 * kMaxOrderStats];    // per wave: partial sums / order statistics of that row
+  double cand[kMaxCand];                // affine: exact values of the row's candidates
+  int dqn[4];                           // per wave: rows queued in this step
+  DeferRow dq[4][kDefer];               // per wave: the step's queued key rows
+  unsigned kq[4][kStaged][D / 2];       // per wave: the first queued rows' fp16 keys (as krow)
 };
 
 // Raw bytes of one lane's CPL channels of one token row, in the input's element size.
@@ -264,27 +301,69 @@ __device__ __forceinline__ float pick(const float (&x)[NL > 0 ? NL : 1], int i) 
   return r;
 }
 
-// (scale, zero) of a row from its merged order statistics: linear interpolation at
-// virtual index (D-1)*pct/100 between sorted values, both rounded to fp16.
+// (scale, zero) of a row before their fp16 rounding, from its merged order statistics:
+// linear interpolation at virtual index (D-1)*pct/100 between sorted values.  Also the
+// order statistics used: x0 <= x1 at the bottom, y0 >= y1 at the top.
+struct AffPre {
+  float vs, vz, x0, x1, y0, y1;
+};
+
 template <int D, int NL>
-__device__ __forceinline__ void affine_from_stats(const FlushArgs &a, const OrderStats<NL> &o, int L, float &sc, float &zp) {
-  const float x0 = pick<NL>(o.lo, a.lo_i);
-  const float x1 = (a.lo_i + 1 < D) ? pick<NL>(o.lo, a.lo_i + 1) : x0;
-  const float vlo = (a.lo_i + 1 < D) ? x0 + a.lo_t * (x1 - x0) : x0;
+__device__ __forceinline__ AffPre affine_pre(const FlushArgs &a, const OrderStats<NL> &o, int L) {
+  AffPre p;
+  p.x0 = pick<NL>(o.lo, a.lo_i);
+  p.x1 = (a.lo_i + 1 < D) ? pick<NL>(o.lo, a.lo_i + 1) : p.x0;
+  const float vlo = (a.lo_i + 1 < D) ? p.x0 + a.lo_t * (p.x1 - p.x0) : p.x0;
   const int hk = D - 1 - a.hi_i;
-  const float y0 = pick<NL>(o.hi, hk);
-  const float y1 = (hk >= 1) ? pick<NL>(o.hi, hk - 1) : y0;
-  const float vhi = (a.hi_i + 1 < D) ? y0 + a.hi_t * (y1 - y0) : y0;
-  sc = f16_round((vhi - vlo) / (float)(L - 1));
-  zp = f16_round(vlo);
+  p.y0 = pick<NL>(o.hi, hk);
+  p.y1 = (hk >= 1) ? pick<NL>(o.hi, hk - 1) : p.y0;
+  const float vhi = (a.hi_i + 1 < D) ? p.y0 + a.hi_t * (p.y1 - p.y0) : p.y0;
+  p.vs = (vhi - vlo) / (float)(L - 1);
+  p.vz = vlo;
+  return p;
 }
 
-__device__ __forceinline__ float quest_step(float ss, float clip, int L, int D) {
-  return f16_round(2.0f * clip * sqrtf(ss / (float)D) / (float)L);
+__device__ __forceinline__ float quest_pre(float ss, float clip, int L, int D) {
+  return 2.0f * clip * sqrtf(ss / (float)D) / (float)L;
 }
 
-// Exact code of a value known in fp64.
+// fp64 -> fp16, correctly rounded (to nearest, ties to even), returned as a float: round
+// to fp32 toward zero and make it odd when inexact, then round to fp16.  fp32 carries 13
+// more significand bits than fp16, so the two roundings give the single one.
+__device__ __forceinline__ float f16_of_f64(double v) {
+  float f = __double2float_rz(v);
+  if ((double)f != v) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return (float)(_Float16)f;
+}
+
+// Whether an fp16 rounding boundary lies within eps (>= 0) of v: then the rounding of
+// the exact value, which lies within eps of v, may differ from v's.
+__device__ __forceinline__ bool near_mid(float v, float eps) {
+  return (float)(_Float16)(v - eps) != (float)(_Float16)(v + eps);
+}
+
+__device__ __forceinline__ double quest_pre64(double ss, float clip, int L, int D) {
+  return 2.0 * (double)clip * sqrt(ss / (double)D) / (double)L;
+}
+
+// The affine interpolation in fp64 from given order statistics (fp64 weights t of the
+// percentiles' virtual indices): exactly the definition's arithmetic; the fp16
+// parameters, and optionally their values before rounding.
+template <int D>
+__device__ __forceinline__ void affine_exact(const FlushArgs &a, double x0, double x1, double y0, double y1, int L,
+                                             float &sc, float &zp, double *s64 = nullptr, double *z64 = nullptr) {
+  const double lo = (a.lo_i + 1 < D) ? x0 + a.lo_t64 * (x1 - x0) : x0;
+  const double hi = (a.hi_i + 1 < D) ? y0 + a.hi_t64 * (y1 - y0) : y0;
+  const double s = (hi - lo) / (double)(L - 1);
+  sc = f16_of_f64(s);
+  zp = f16_of_f64(lo);
+  if (s64) *s64 = s;
+  if (z64) *z64 = lo;
+}
+
+// Exact code of a value known in fp64 (a zero step or scale gives the degenerate code).
 __device__ __forceinline__ int exact_code(double x, float sc, float zp, int quant, int L) {
+  if (sc == 0.f) return quant == WUSHKV_Q_QUEST ? L / 2 : 0;
   double t;
   if (quant == WUSHKV_Q_QUEST) t = floor(x / (double)sc + (double)(L / 2));
   else t = rint((x - (double)zp) / (double)sc);
@@ -339,6 +418,48 @@ template <bool QU>
 __device__ __forceinline__ bool value_near(const Quant<QU> &q, float x) {
   const float v = scaled(q, x);
   return v - floorf(v) < q.band;
+}
+
+// ---- exact key parameters for the rare rows near an fp16 rounding midpoint.  The whole
+// workgroup works on one row at a time, after the step's tiles.
+
+// The LDS copy of one fp16 key row (sm.krow): word q * (D/8) + w holds channels
+// 32 (w / 4) + 8 q + 2 (w % 4) and the next, the order of a row's lanes in the tiles.
+// Exact x_j = sum_i T[j][i] k[i] over 8-channel block blk of that row, in fp64 (fp16 x
+// fp16 products are exact in fp32).
+template <int D>
+__device__ __forceinline__ double block_dot(const FlushSmem<D> &sm, int j, int blk) {
+  const half8 tv = *(const half8 *)&sm.t[j][8 * blk];
+  const u32x4 kw = *(const u32x4 *)&sm.krow[(blk & 3) * (D / 8) + 4 * (blk >> 2)];
+  double x = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const unsigned w = kw[i >> 1];
+    const float kv = (i & 1) ? (float)__builtin_bit_cast(f16x2, w)[1] : (float)__builtin_bit_cast(f16x2, w)[0];
+    x += (double)((float)tv[i] * kv);
+  }
+  return x;
+}
+
+// Keep the NL smallest (ascending) or largest (descending) values seen.
+template <int NL>
+__device__ __forceinline__ void keep_low(double (&l)[NL], double v) {
+#pragma unroll
+  for (int k = NL - 1; k > 0; --k) l[k] = fmax(l[k - 1], fmin(l[k], v));
+  l[0] = fmin(l[0], v);
+}
+template <int NL>
+__device__ __forceinline__ void keep_high(double (&h)[NL], double v) {
+#pragma unroll
+  for (int k = NL - 1; k > 0; --k) h[k] = fmin(h[k - 1], fmax(h[k], v));
+  h[0] = fmax(h[0], v);
+}
+template <int NL>
+__device__ __forceinline__ double pick64(const double (&x)[NL], int i) {
+  double r = x[0];
+#pragma unroll
+  for (int k = 1; k < NL; ++k) r = (i == k) ? x[k] : r;
+  return r;
 }
 
 // DPP quad permutations (gfx9 quad_perm): lane i of a quad reads lane i^2 / i^1.
@@ -444,6 +565,25 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   for (int64_t st = st0; st < st1; ++st) {
     const int64_t set0 = s_first + 2 * st;
     const int64_t ubase = set0 * kSet + 32 * wave;   // this wave's first token
+    // Key rows whose parameters need the exact x go to this wave's queue (want is the
+    // same in a token's four lanes); the workgroup resolves them after the step's tiles.
+    int ndq = 0;
+    auto defer = [&](bool want, int row, const unsigned (&kh)[D / 8], unsigned cmask, float clo, float chi, float mg,
+                     float sca, float zpa) {
+      const unsigned tm = (unsigned)(__ballot(want) & 0xFFFFull);
+      if (tm == 0) return;
+      const int pos = ndq + __builtin_popcount(tm & ((1u << tok) - 1u));
+      if (want) {
+        DeferRow &d = sm.dq[wave][pos];
+        d.cm[q] = cmask;
+        if (q == 0) { d.row = row; d.clo = clo; d.chi = chi; d.mg = mg; d.sc = sca; d.zp = zpa; }
+        if (pos < kStaged) {
+#pragma unroll
+          for (int w = 0; w < D / 8; ++w) sm.kq[wave][pos][q * (D / 8) + w] = kh[w];
+        }
+      }
+      ndq += __builtin_popcount(tm);
+    };
 
     // ---- keys, one tile at a time: x = T_K k16 on MFMA, parameters, codes
 #pragma unroll
@@ -479,7 +619,24 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
           ss += __shfl_xor(ss, 16);
           ss += __shfl_xor(ss, 32);
-          sc = quest_step(ss, a.clip, Lk, D);
+          const float v32 = quest_pre(ss, a.clip, Lk, D);
+          sc = f16_round(v32);
+          // a step near an fp16 rounding midpoint is decided again: from the fp64 sum of
+          // squares of the fp32 x, then, if still near one, from the exact x
+          const bool pn = vt && near_mid(v32, kParKA * v32);
+          if (__builtin_expect(__any(pn), 0)) {
+            double s64 = 0.0;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) s64 = fma((double)acc[ct][i], (double)acc[ct][i], s64);
+            s64 += __shfl_xor(s64, 16);
+            s64 += __shfl_xor(s64, 32);
+            const double d64 = quest_pre64(s64, a.clip, Lk, D);
+            if (pn) sc = f16_of_f64(d64);
+            // still near one: the exact x after the step's tiles
+            defer(pn && near_mid((float)d64, kParKB * (float)d64), row, kh, 0u, 0.f, 0.f, 0.f, sc, 0.f);
+          }
         } else if constexpr (NL > 0) {
           OrderStats<NL> o;
           os_init(o);
@@ -489,7 +646,35 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             for (int i = 0; i < 4; ++i) os_insert(o, acc[ct][i]);
           os_merge(o, 16);
           os_merge(o, 32);
-          affine_from_stats<D, NL>(a, o, Lk, sc, zp);
+          const AffPre ap = affine_pre<D, NL>(a, o, Lk);
+          sc = f16_round(ap.vs);
+          zp = f16_round(ap.vz);
+          // scale or zero near an fp16 rounding midpoint: decided again from the fp64
+          // interpolation of the order statistics, and if still near one, from the exact x
+          // after the step's tiles
+          const float sx = fabsf(ap.x0) + fabsf(ap.x1), sxy = sx + fabsf(ap.y0) + fabsf(ap.y1);
+          const bool pn = vt && (near_mid(ap.vz, kParKAff * sx) || near_mid(ap.vs, kParKAff * sxy / (float)(Lk - 1)));
+          if (__builtin_expect(__any(pn), 0)) {
+            double s64, z64;
+            float sc1, zp1;
+            affine_exact<D>(a, ap.x0, ap.x1, ap.y0, ap.y1, Lk, sc1, zp1, &s64, &z64);
+            if (pn) { sc = sc1; zp = zp1; }
+            const bool pn2 = pn && (near_mid((float)z64, kParKAff2 * sx) ||
+                                    near_mid((float)s64, kParKAff2 * sxy / (float)(Lk - 1)));
+            // candidates for the exact order statistics: this lane's elements within mg of the
+            // cuts (the contraction's error is far below mg)
+            const float cut_lo = fmaxf(ap.x0, ap.x1), cut_hi = fminf(ap.y0, ap.y1);
+            const float mg = 8e-6f * fmaxf(fabsf(cut_lo), fabsf(cut_hi));
+            unsigned cmask = 0;
+            if (pn2) {
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  if (acc[ct][i] <= cut_lo + mg || acc[ct][i] >= cut_hi - mg) cmask |= 1u << (4 * ct + i);
+            }
+            defer(pn2, row, kh, cmask, cut_lo, cut_hi, mg, sc, zp);
+          }
         } else {
           sc = 0.f;
         }
@@ -523,7 +708,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
         for (int ct = 1; ct < NCT; ++ct) emin = fminf(emin, e[ct]);
         const bool kn = vt && edge_near(qk, emin);
-        if (__any(kn)) {
+        if (__builtin_expect(__any(kn), 0)) {
           unsigned m = 0;
           if (kn) {
 #pragma unroll
@@ -584,7 +769,18 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
           ss += __shfl_xor(ss, 16);
           ss += __shfl_xor(ss, 32);
-          sc = quest_step(ss, a.clip, Lv, D);
+          const float v32 = quest_pre(ss, a.clip, Lv, D);
+          sc = f16_round(v32);
+          // near an fp16 rounding midpoint: the step from the exact (fp64) sum of squares
+          const bool pn = vt && near_mid(v32, kParV * v32);
+          if (__builtin_expect(__any(pn), 0)) {
+            double s64 = 0.0;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) s64 = fma((double)xv[k], (double)xv[k], s64);
+            s64 += __shfl_xor(s64, 16);
+            s64 += __shfl_xor(s64, 32);
+            if (pn) sc = f16_of_f64(quest_pre64(s64, a.clip, Lv, D));
+          }
         } else if constexpr (NL > 0) {
           OrderStats<NL> o;
           os_init(o);
@@ -592,7 +788,15 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           for (int k = 0; k < CPL; ++k) os_insert(o, xv[k]);
           os_merge(o, 16);
           os_merge(o, 32);
-          affine_from_stats<D, NL>(a, o, Lv, sc, zp);
+          const AffPre ap = affine_pre<D, NL>(a, o, Lv);
+          sc = f16_round(ap.vs);
+          zp = f16_round(ap.vz);
+          // near an fp16 rounding midpoint: the interpolation in fp64 (the order statistics
+          // of values are exact)
+          const float ez = kParV * (fabsf(ap.x0) + fabsf(ap.x1));
+          const float es = kParV * (fabsf(ap.x0) + fabsf(ap.x1) + fabsf(ap.y0) + fabsf(ap.y1)) / (float)(Lv - 1);
+          if (__builtin_expect(vt && (near_mid(ap.vz, ez) || near_mid(ap.vs, es)), 0))
+            affine_exact<D>(a, ap.x0, ap.x1, ap.y0, ap.y1, Lv, sc, zp);
         } else {
           sc = 0.f;
         }
@@ -626,7 +830,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
         for (int g4 = 1; g4 < CPL / 4; ++g4) emin = fminf(emin, e[g4]);
         const bool vn = vt && edge_near(qv, emin);
-        if (__any(vn)) {
+        if (__builtin_expect(__any(vn), 0)) {
           unsigned m = 0;
           if (vn) {
 #pragma unroll
@@ -649,7 +853,173 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       if (a.quant_v == WUSHKV_Q_QUEST) value_tile(QuestTag{});
       else value_tile(AffineTag{});
     }
+    // ---- the queued key rows, resolved by the whole workgroup after the step's tiles.  A
+    // row's fp16 key is in LDS (staged when it was queued, else read again from the ring or
+    // the input).  Affine rows first get the exact values of their candidate elements (16
+    // lanes per candidate, one pass); a row whose parameters change, and every QuEST row,
+    // gets the exact x of all channels (thread group of channel j: x_j in fp64), its exact
+    // parameters and the codes of its exact x.
+    if (lane == 0) sm.dqn[wave] = ndq;
     __syncthreads();
+    const int nq0 = sm.dqn[0], nq1 = sm.dqn[1], nq2 = sm.dqn[2], nq3 = sm.dqn[3];
+    if (__builtin_expect(nq0 + nq1 + nq2 + nq3 > 0, 0)) {
+      auto key_row8 = [&](int64_t u, int m) -> u32x4 {
+        if (a.S + u < n_before) {
+          const unsigned slot = (unsigned)u % (unsigned)(a.R + a.C);
+          return *(const u32x4 *)(ring_kh + (size_t)slot * (D * 2) + 16 * m);
+        }
+        const char *src = in_kh + (size_t)(a.S + u - n_before) * (D * ES) + (size_t)8 * ES * m;
+        if constexpr (ES == 2) {
+          const u32x4 w = *(const u32x4 *)src;
+          if (a.in_dtype == WUSHKV_DT_F16) return w;
+          return (u32x4){pack_f16(bf16_lo(w[0]), bf16_hi(w[0])), pack_f16(bf16_lo(w[1]), bf16_hi(w[1])),
+                         pack_f16(bf16_lo(w[2]), bf16_hi(w[2])), pack_f16(bf16_lo(w[3]), bf16_hi(w[3]))};
+        } else {
+          const u32x4 w0 = *(const u32x4 *)src, w1 = *(const u32x4 *)(src + 16);
+          return (u32x4){pack_f16(__uint_as_float(w0[0]), __uint_as_float(w0[1])),
+                         pack_f16(__uint_as_float(w0[2]), __uint_as_float(w0[3])),
+                         pack_f16(__uint_as_float(w1[0]), __uint_as_float(w1[1])),
+                         pack_f16(__uint_as_float(w1[2]), __uint_as_float(w1[3]))};
+        }
+      };
+      constexpr int TPC = kThreads / D;         // threads per channel: 2 (D = 128) or 4 (D = 64)
+      constexpr int BPT = D / 8 / TPC;          // 8-channel blocks per thread
+      const int j = tid / TPC, h = tid % TPC;
+#pragma unroll 1
+      for (int wv = 0; wv < 4; ++wv) {
+        const int nqw = wv == 0 ? nq0 : (wv == 1 ? nq1 : (wv == 2 ? nq2 : nq3));
+#pragma unroll 1
+        for (int e = 0; e < nqw; ++e) {
+          const DeferRow &d = sm.dq[wv][e];
+          const int row = d.row;
+          const int64_t u = set0 * kSet + row;
+          if (e < kStaged) {
+            if (tid < D / 2) sm.krow[tid] = sm.kq[wv][e][tid];
+          } else if (tid < D / 8) {
+            *(u32x4 *)&sm.krow[(tid & 3) * (D / 8) + 4 * (tid >> 2)] = key_row8(u, tid);
+          }
+          __syncthreads();
+          float scx = d.sc, zpx = d.zp;
+          bool full = a.quant_k == WUSHKV_Q_QUEST;
+          int total = 0;
+          if constexpr (NL > 0) {
+            if (!full) {
+              const unsigned cm[4] = {d.cm[0], d.cm[1], d.cm[2], d.cm[3]};
+#pragma unroll
+              for (int qq = 0; qq < 4; ++qq) total += __builtin_popcount(cm[qq]);
+              if (total > kMaxCand) {
+                full = true;
+              } else {
+                // candidate c = tid / 16, its 16 lanes one 8-channel block each
+                const int c = tid >> 4, m = tid & 15;
+                int left = c, jc = 0;
+                bool found = false;
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                  const int cnt = __builtin_popcount(cm[qq]);
+                  if (!found && left < cnt) {
+                    unsigned mm = cm[qq];
+                    for (int s2 = 0; s2 < left; ++s2) mm &= mm - 1;
+                    const int bit = __builtin_ctz(mm);
+                    jc = 16 * (bit >> 2) + 4 * qq + (bit & 3);
+                    found = true;
+                  } else if (!found) {
+                    left -= cnt;
+                  }
+                }
+                double part = (found && m < D / 8) ? block_dot<D>(sm, jc, m) : 0.0;
+#pragma unroll
+                for (int sh = 1; sh < 16; sh <<= 1) part += __shfl_xor(part, sh);
+                if (m == 0 && found) sm.cand[c] = part;
+                __syncthreads();
+                double lo_s[NL], hi_s[NL];
+#pragma unroll
+                for (int k = 0; k < NL; ++k) { lo_s[k] = INFINITY; hi_s[k] = -INFINITY; }
+#pragma unroll 1
+                for (int cc = 0; cc < total; ++cc) {
+                  const double v = sm.cand[cc];
+                  if (v <= (double)(d.clo + d.mg)) keep_low<NL>(lo_s, v);
+                  if (v >= (double)(d.chi - d.mg)) keep_high<NL>(hi_s, v);
+                }
+                const double x0 = pick64<NL>(lo_s, a.lo_i);
+                const double x1 = (a.lo_i + 1 < D) ? pick64<NL>(lo_s, a.lo_i + 1) : x0;
+                const int hk = D - 1 - a.hi_i;
+                const double y0 = pick64<NL>(hi_s, hk);
+                const double y1 = (hk >= 1) ? pick64<NL>(hi_s, hk - 1) : y0;
+                affine_exact<D>(a, x0, x1, y0, y1, Lk, scx, zpx);
+                full = scx != d.sc || zpx != d.zp;   // the codes follow the new parameters
+              }
+            }
+          }
+          if (full) {
+            double xa = 0.0, xb = 0.0;   // two independent chains
+#pragma unroll 2
+            for (int k2 = 0; k2 < BPT; k2 += 2) {
+              xa += block_dot<D>(sm, j, h * BPT + k2);
+              xb += block_dot<D>(sm, j, h * BPT + k2 + 1);
+            }
+            double x = xa + xb;
+#pragma unroll
+            for (int sh = 1; sh < TPC; sh <<= 1) x += __shfl_xor(x, sh);   // every thread of channel j: x_j
+            if (a.quant_k == WUSHKV_Q_QUEST) {
+              // sum of squares: each channel counted TPC times (an exact scaling), waves in order
+              double ss = x * x;
+#pragma unroll
+              for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
+              if (lane == 0) sm.red[wave][0] = ss;
+              __syncthreads();
+              ss = ((sm.red[0][0] + sm.red[1][0]) + (sm.red[2][0] + sm.red[3][0])) / (double)TPC;
+              scx = f16_of_f64(quest_pre64(ss, a.clip, Lk, D));
+            } else if constexpr (NL > 0) {
+              if (total > kMaxCand) {
+                // the NL smallest and largest exact values of all channels: per wave (one
+                // thread per channel), then over the four waves' lists
+                double lo_s[NL], hi_s[NL];
+#pragma unroll
+                for (int k = 0; k < NL; ++k) { lo_s[k] = INFINITY; hi_s[k] = -INFINITY; }
+                if (h == 0) { lo_s[0] = x; hi_s[0] = x; }
+#pragma unroll 1
+                for (int m = 1; m < 64; m <<= 1) {
+                  double ol[NL], oh[NL];
+#pragma unroll
+                  for (int k = 0; k < NL; ++k) { ol[k] = __shfl_xor(lo_s[k], m); oh[k] = __shfl_xor(hi_s[k], m); }
+#pragma unroll
+                  for (int k = 0; k < NL; ++k) { keep_low<NL>(lo_s, ol[k]); keep_high<NL>(hi_s, oh[k]); }
+                }
+                if (lane == 0) {
+#pragma unroll
+                  for (int k = 0; k < NL; ++k) { sm.red[wave][k] = lo_s[k]; sm.red[wave][NL + k] = hi_s[k]; }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < NL; ++k) { lo_s[k] = INFINITY; hi_s[k] = -INFINITY; }
+#pragma unroll
+                for (int wv2 = 0; wv2 < 4; ++wv2)
+#pragma unroll
+                  for (int k = 0; k < NL; ++k) {
+                    keep_low<NL>(lo_s, sm.red[wv2][k]);
+                    keep_high<NL>(hi_s, sm.red[wv2][NL + k]);
+                  }
+                const double x0 = pick64<NL>(lo_s, a.lo_i);
+                const double x1 = (a.lo_i + 1 < D) ? pick64<NL>(lo_s, a.lo_i + 1) : x0;
+                const int hk = D - 1 - a.hi_i;
+                const double y0 = pick64<NL>(hi_s, hk);
+                const double y1 = (hk >= 1) ? pick64<NL>(hi_s, hk - 1) : y0;
+                affine_exact<D>(a, x0, x1, y0, y1, Lk, scx, zpx);
+              }
+            }
+            if (h == 0) sm.kc[row][j] = (uint8_t)exact_code(x, scx, zpx, a.quant_k, Lk);
+          }
+          const int64_t off = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, 2 * a.kpar_n);
+          if (tid == 0 && !(PAGED && off < 0)) {
+            _Float16 *pk = (_Float16 *)((char *)a.par_k + off);
+            if (a.quant_k == WUSHKV_Q_QUEST) pk[0] = (_Float16)scx;
+            else *(unsigned *)pk = pack_f16(scx, zpx);
+          }
+          __syncthreads();
+        }
+      }
+    }
     // ---- K rows: two threads per token, D/2 channels each (the bit width is a
     // template argument so only its own packing is issued)
     auto pack_k_rows = [&](auto bits_tag) {

@@ -22,6 +22,7 @@ struct Geom {
   // lo uses (lo_i, lo_t) counted from the bottom, hi uses (hi_i, hi_t) counted from the bottom.
   int lo_i, hi_i;
   float lo_t, hi_t;
+  double lo_t64, hi_t64; // the same weights in fp64 (exact re-decisions)
   int need_lo, need_hi;  // smallest / largest order statistics a row needs
   // per-(b, g) sizes in bytes
   size_t sink_bytes, ring_bytes, kcode_row, kcode_bytes, vset_bytes, vcode_bytes, kpar_bytes, vpar_bytes;
@@ -72,6 +73,7 @@ struct FlushArgs {
   float clip;
   int lo_i, hi_i, need_lo, need_hi;
   float lo_t, hi_t;
+  double lo_t64, hi_t64;
   PageTable pg;
   int64_t body_cap;
 };

@@ -3,8 +3,9 @@ device planes back, and compare them with the CPU oracle element by element.
 
 Parity rule (codes and parameters):
   * FP16 windows: bitwise equal.
-  * Parameters: equal, or 1 fp16 ulp apart where the oracle's pre-rounding value
-    lies within 1e-6 (relative) of an fp16 rounding midpoint.
+  * Parameters: equal.  (The rule admits 1 fp16 ulp where the oracle's pre-rounding
+    value lies within 1e-6 (relative) of an fp16 rounding midpoint; the flush decides
+    such parameters again in fp64, so the tests require them equal.)
   * Codes: unpacked from the device planes and compared with the oracle's codes
     of its exact x under the device's stored parameters; a mismatch is allowed
     only within 1e-6*max(|b|, bin width) of a decision boundary b, and such
@@ -63,16 +64,17 @@ def plane_arrays(cache):
 
 
 def _param_check(gpu, exact, what):
-    """gpu fp16 params vs the oracle's pre-rounding values; returns #ulp-off rows."""
+    """gpu fp16 params vs the oracle's pre-rounding values rounded to fp16: equal.  Also
+    counts the rows whose exact value lies within 1e-6 of an fp16 rounding midpoint (the
+    ones the flush decides again in fp64); returns (mismatches, near-midpoint rows)."""
     g = gpu.astype(np.float64)
     want = R.f16(exact)
-    ok = (g == want)
+    bad = ~((g == want) | (np.isnan(g) & np.isnan(want)))
     near = R.fp16_midpoint_near(exact)
-    one_ulp = np.abs(gpu.astype(np.float16).view(np.int16).astype(np.int64)
-                     - want.astype(np.float16).view(np.int16).astype(np.int64)) == 1
-    bad = ~ok & ~(near & one_ulp)
-    assert not bad.any(), f"{what}: {bad.sum()} parameters differ beyond the rule; first at {np.argwhere(bad)[:3].tolist()} gpu={g[bad][:3]} want={want[bad][:3]}"
-    return int((~ok).sum())
+    assert not bad.any(), (f"{what}: {bad.sum()} parameters differ ({(bad & near).sum()} of them near a rounding "
+                           f"midpoint); first at {np.argwhere(bad)[:3].tolist()} gpu={g[bad][:3]} want={want[bad][:3]} "
+                           f"exact={np.asarray(exact)[bad][:3]}")
+    return int(bad.sum()), int(near.sum())
 
 
 def check_head(pa, spec, b, g, k_in, v_in, t16, n, stats):
@@ -96,7 +98,9 @@ def check_head(pa, spec, b, g, k_in, v_in, t16, n, stats):
     for name, x, quant, bits in (("k", c.body_xk, qk, spec.bits_k), ("v", c.body_xv, qv, spec.bits_v)):
         gp = pa["par_" + name][b, g, :nb].astype(np.float64)
         ex = R.params_exact(x, quant, bits, spec.clip_mult, spec.pct_lo, spec.pct_hi)
-        stats["param_ulp"] = stats.get("param_ulp", 0) + _param_check(gp, ex, "par_" + name)
+        nbad, nnear = _param_check(gp, ex, "par_" + name)
+        stats["param_ulp"] = stats.get("param_ulp", 0) + nbad
+        stats["param_near_mid"] = stats.get("param_near_mid", 0) + nnear
         if name == "k":
             codes = LY.unpack_k(pa["codes_k"][b, g], bits, d, nb)
         else:

@@ -360,3 +360,21 @@ def test_key_rows_on_decision_boundaries():
     r.append(1)
     q, qt, out = r.decode(0)
     r.check_decode(q, qt, out)
+
+
+def test_wide_percentiles_exact_params():
+    """Affine quantization at the 5th / 95th percentiles: eight order statistics from each
+    end (the most the flush keeps), K and V, prefill and steps across flushes; parameters
+    bit-exact, codes within the boundary rule, decode to the oracle."""
+    w = configs.SERVING.scaled(name="pct5", seed=43, batch=2, num_kv_heads=4, num_q_heads=16, context=3000,
+                               decode_steps=20, pct_lo=5.0, pct_hi=95.0, chunk=8)
+    r = Run(w)
+    r.append(w.context)
+    _, stats = r.check_cache()
+    say(f"[percentiles 5/95] prefill {stats}")
+    for s in range(w.decode_steps):
+        r.append(1)
+    q, qt, out = r.decode(0)
+    _, stats = r.check_cache()
+    say(f"[percentiles 5/95] after {w.decode_steps} steps {stats}")
+    r.check_decode(q, qt, out)
