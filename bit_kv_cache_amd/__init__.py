@@ -23,7 +23,8 @@ EXPORTS = ("wushkv_status_string", "wushkv_abi_version", "wushkv_cache_check", "
            "wushkv_calib_stats", "wushkv_calib_workspace_bytes", "wushkv_append_flush_ragged",
            "wushkv_decode_attention_ragged", "wushkv_append_flush_device", "wushkv_decode_attention_device",
            "wushkv_pool_bytes", "wushkv_append_flush_paged", "wushkv_decode_attention_paged", "wushkv_decode_step",
-           "wushkv_decode_step_device", "wushkv_decode_attention_generic", "wushkv_decode_attention_noalloc")
+           "wushkv_decode_step_device", "wushkv_decode_attention_generic", "wushkv_decode_attention_noalloc",
+           "wushkv_append_flush_hadamard")
 
 
 class WushKVError(RuntimeError):
@@ -79,6 +80,7 @@ def lib():
                                                          vp, vp]),
             "wushkv_append_flush_paged": (ctypes.c_int, [P, ctypes.POINTER(PagesDesc), ctypes.POINTER(i64), i32, vp, vp,
                                                          i32, vp, vp]),
+            "wushkv_append_flush_hadamard": (ctypes.c_int, [P, i64, i32, vp, vp, i32, ctypes.c_float, vp]),
             "wushkv_decode_attention_noalloc": (ctypes.c_int, [P, i64, vp, i32, vp, i32, i32, vp, vp]),
             "wushkv_decode_attention_generic": (ctypes.c_int, [P, ctypes.POINTER(i64), vp, i32, vp, vp, i32, i32, vp,
                                                                sz, vp, vp]),
@@ -224,6 +226,24 @@ def append_flush(cache: KVCache, k_new, v_new, t_k16, n_before=None, stream=None
     _check(lib().wushkv_append_flush(ctypes.byref(cache.desc), n_before, n_new, _ptr(k_new), _ptr(v_new),
                                      _dtype_code(k_new), _ptr(t_k16), _stream(stream, k_new.device)),
            "append_flush")
+    cache.n = n_before + n_new
+
+
+def append_flush_hadamard(cache: KVCache, k_new, v_new, scale=None, n_before=None, stream=None):
+    """append_flush with the fixed key transform T_K = scale * H (Sylvester-Hadamard of order
+    head_dim), formed by an in-register fast Walsh-Hadamard transform.  scale defaults to
+    fp16(1/sqrt(head_dim)), the orthonormal transform."""
+    import numpy as np
+    d = k_new.shape[-1]
+    if scale is None:
+        scale = float(np.float16(1.0 / np.sqrt(d)))
+    n_before = cache.n if n_before is None else n_before
+    n_new = k_new.shape[2]
+    if k_new.dtype != v_new.dtype:
+        raise ValueError("k_new/v_new must share a dtype")
+    _check(lib().wushkv_append_flush_hadamard(ctypes.byref(cache.desc), n_before, n_new, _ptr(k_new), _ptr(v_new),
+                                              _dtype_code(k_new), float(scale), _stream(stream, k_new.device)),
+           "append_flush_hadamard")
     cache.n = n_before + n_new
 
 

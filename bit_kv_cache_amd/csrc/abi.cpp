@@ -217,7 +217,8 @@ namespace {
 // the caller to launch or to fold into the decode (the flush, when due, is launched).
 int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_before, const int64_t *seq_nb,
                       int32_t *dev_n, int32_t n_new, const void *k_new, const void *v_new, int32_t in_dtype,
-                      const void *t_k_f16, void *stream, AppendArgs *deferred = nullptr, int64_t dev_cap = -1) {
+                      const void *t_k_f16, void *stream, AppendArgs *deferred = nullptr, int64_t dev_cap = -1,
+                      float had = 0.f) {
   Geom g;
   int st = make_geom(c, &g);
   if (st != WUSHKV_OK) return st;
@@ -238,8 +239,8 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
   if (n_before + n_new > g.cap) return WUSHKV_ERR_CAPACITY;
   if ((st = check_planes(c)) != WUSHKV_OK) return st;
   if (n_new == 0) return WUSHKV_OK;
-  if (!k_new || !v_new || !t_k_f16) return WUSHKV_ERR_NULL;
-  if (misaligned(k_new) || misaligned(v_new) || misaligned(t_k_f16)) return WUSHKV_ERR_ALIGN;
+  if (!k_new || !v_new || (!t_k_f16 && had == 0.f)) return WUSHKV_ERR_NULL;
+  if (misaligned(k_new) || misaligned(v_new) || (had == 0.f && misaligned(t_k_f16))) return WUSHKV_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   int64_t n_after = n_before + n_new;
   int64_t qb = n_quantized(n_before, g.S, g.R, g.C), qa = n_quantized(n_after, g.S, g.R, g.C);
@@ -272,6 +273,7 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
     f.cap = dev_cap >= 0 && dev_cap < g.cap ? dev_cap : g.cap;
     f.pg = pg;
     f.body_cap = g.body_cap;
+    f.had = had;
     if (dev_n) {
       f.ragged = kRaggedDevice;
       f.dev_n = dev_n;
@@ -313,6 +315,14 @@ extern "C" {
 int wushkv_append_flush(const wushkv_cache *c, int64_t n_before, int32_t n_new, const void *k_new,
                         const void *v_new, int32_t in_dtype, const void *t_k_f16, void *stream) {
   return append_flush_impl(c, nullptr, n_before, nullptr, nullptr, n_new, k_new, v_new, in_dtype, t_k_f16, stream);
+}
+
+int wushkv_append_flush_hadamard(const wushkv_cache *c, int64_t n_before, int32_t n_new, const void *k_new,
+                                 const void *v_new, int32_t in_dtype, float scale, void *stream) {
+  // the scale must be a nonzero, finite fp16 value (T_K = scale * H is used as fp16)
+  if (!(scale != 0.0f && isfinite(scale)) || (float)(_Float16)scale != scale) return WUSHKV_ERR_SHAPE;
+  return append_flush_impl(c, nullptr, n_before, nullptr, nullptr, n_new, k_new, v_new, in_dtype, nullptr, stream,
+                           nullptr, -1, scale);
 }
 
 int wushkv_append_flush_ragged(const wushkv_cache *c, const int64_t *n_before, int32_t n_new, const void *k_new,

@@ -188,6 +188,33 @@ __device__ __forceinline__ void load_seg(const FlushArgs &a, int64_t n_before, c
     for (int h = 0; h < ES / 2; ++h) s.r[(ES / 2) * i + h] = __builtin_nontemporal_load(src + 2 * ES * i + h);
 }
 
+// The same row segment with lane group q holding channels 16 ct + 4 q .. 16 ct + 4 q + 3
+// (ct = 0 .. D/16 - 1), at positions 4 ct + i: the channels the key contraction's output
+// puts in a lane, so that the in-register Hadamard transform needs no transpose.
+template <int D, int ES>
+__device__ __forceinline__ void load_seg_ct(const FlushArgs &a, int64_t n_before, const char *ring_h, const char *in_h,
+                                            int64_t u, bool valid, int q, RawSeg<ES, D / 4> &s) {
+  constexpr int NCT = D / 16;
+#pragma unroll
+  for (int i = 0; i < D * ES / 64; ++i) s.r[i] = (u32x4){0u, 0u, 0u, 0u};
+  if (!valid) return;
+  const bool ring = a.S + u < n_before;
+  const char *row = ring ? ring_h + (size_t)((unsigned)u % (unsigned)(a.R + a.C)) * (D * 2)
+                         : in_h + (size_t)(a.S + u - n_before) * (D * ES);
+  if (ring || ES == 2) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const u32x2 w = ring ? *(const u32x2 *)(row + 32 * ct + 8 * q)
+                           : __builtin_nontemporal_load((const u32x2 *)(row + 32 * ct + 8 * q));
+      s.r[ct >> 1][2 * (ct & 1)] = w[0];
+      s.r[ct >> 1][2 * (ct & 1) + 1] = w[1];
+    }
+  } else {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) s.r[ct] = __builtin_nontemporal_load((const u32x4 *)(row + 64 * ct + 16 * q));
+  }
+}
+
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float f16_lo(unsigned w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
@@ -423,14 +450,13 @@ __device__ __forceinline__ bool value_near(const Quant<QU> &q, float x) {
 // ---- exact key parameters for the rare rows near an fp16 rounding midpoint.  The whole
 // workgroup works on one row at a time, after the step's tiles.
 
-// The LDS copy of one fp16 key row (sm.krow): word q * (D/8) + w holds channels
-// 32 (w / 4) + 8 q + 2 (w % 4) and the next, the order of a row's lanes in the tiles.
+// The LDS copy of one fp16 key row (sm.krow, sm.kq): word c / 2 holds channels c and c + 1.
 // Exact x_j = sum_i T[j][i] k[i] over 8-channel block blk of that row, in fp64 (fp16 x
 // fp16 products are exact in fp32).
 template <int D>
 __device__ __forceinline__ double block_dot(const FlushSmem<D> &sm, int j, int blk) {
   const half8 tv = *(const half8 *)&sm.t[j][8 * blk];
-  const u32x4 kw = *(const u32x4 *)&sm.krow[(blk & 3) * (D / 8) + 4 * (blk >> 2)];
+  const u32x4 kw = *(const u32x4 *)&sm.krow[4 * blk];
   double x = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -504,9 +530,18 @@ __device__ __forceinline__ unsigned kpack1(unsigned x) {
   return (y | (y >> 14)) & 0xFu;
 }
 
-template <int D, int ES, int NL, bool PAGED>
+// HAD: the key transform is T_K = a.had * H (Sylvester-Hadamard, H[j][i] = (-1)^popcount(i & j)),
+// formed by butterflies in registers instead of the contraction; T_K itself is generated
+// in LDS for the exact re-decisions.
+template <int D, int ES, int NL, bool PAGED, bool HAD>
 __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int steps_per_wg) {
   constexpr int CPL = D / 4, KS = D / 32, NCT = D / 16;
+  // word of the LDS key row (channel order) holding this lane's key word w
+  auto kh_word = [](int q, int w) { return HAD ? 8 * (w >> 1) + 2 * q + (w & 1) : 16 * (w >> 2) + 4 * q + (w & 3); };
+  // parameter bands of the key rows: the butterflies' seven fp32 roundings per element
+  // get wider bands than the contraction's measured error
+  constexpr float parKA = HAD ? 4e-6f : kParKA, parKB = HAD ? 1.5e-6f : kParKB;
+  constexpr float parKAff = HAD ? 6e-6f : kParKAff, parKAff2 = HAD ? 4e-6f : kParKAff2;
   using QuestTag = std::integral_constant<bool, true>;
   using AffineTag = std::integral_constant<bool, false>;
   __shared__ FlushSmem<D> sm;
@@ -540,7 +575,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const char *in_vh = (const char *)a.v_new + in_off;
   auto load_k = [&](int64_t st, int tt) {
     const int64_t u = tok_of(st, tt);
-    load_seg<D, ES>(a, n_before, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
+    if constexpr (HAD) load_seg_ct<D, ES>(a, n_before, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
+    else load_seg<D, ES>(a, n_before, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
   };
   auto load_v = [&](int64_t st, int tt) {
     const int64_t u = tok_of(st, tt);
@@ -550,7 +586,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) { load_k(st0, tt); load_v(st0, tt); }
   }
-  {
+  if constexpr (HAD) {
+    const _Float16 hp = (_Float16)a.had, hn = (_Float16)(-a.had);
+    for (int i = tid; i < D * D; i += kThreads) {
+      const int r = i / D, c = i % D;
+      sm.t[r][c] = (__builtin_popcount(r & c) & 1) ? hn : hp;
+    }
+  } else {
     const _Float16 *T = a.tk + (size_t)g * D * D;
     for (int i = tid; i < D * D / 8; i += kThreads) {
       const int r = i / (D / 8), c8 = i % (D / 8);
@@ -579,7 +621,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         if (q == 0) { d.row = row; d.clo = clo; d.chi = chi; d.mg = mg; d.sc = sca; d.zp = zpa; }
         if (pos < kStaged) {
 #pragma unroll
-          for (int w = 0; w < D / 8; ++w) sm.kq[wave][pos][q * (D / 8) + w] = kh[w];
+          for (int w = 0; w < D / 8; ++w) sm.kq[wave][pos][kh_word(q, w)] = kh[w];
         }
       }
       ndq += __builtin_popcount(tm);
@@ -593,17 +635,52 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       unsigned kh[CPL / 2];
       seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
       if (st + 1 < st1) load_k(st + 1, tt);
-      // K-steps outer, tiles inner: NCT independent accumulation chains
       f32x4 acc[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const u32x4 bw = {kh[4 * s], kh[4 * s + 1], kh[4 * s + 2], kh[4 * s + 3]};
+      if constexpr (HAD) {
+        // x = a H k16 by butterflies: element (ct, i) of lane (q, tok) is channel 16 ct + 4 q
+        // + i, so channel bits 0-1 pair elements of a chunk, bits 2-3 pair the token's lanes
+        // (lane ^ 16, ^ 32), bits 4 and up pair chunks
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const half8 A = *(const half8 *)&sm.t[16 * ct + tok][32 * s + 8 * q];
-          acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8, bw), acc[ct], 0, 0, 0);
+          const float k0 = f16_lo(kh[2 * ct]), k1 = f16_hi(kh[2 * ct]);
+          const float k2 = f16_lo(kh[2 * ct + 1]), k3 = f16_hi(kh[2 * ct + 1]);
+          const float a0 = k0 + k1, a1 = k0 - k1, a2 = k2 + k3, a3 = k2 - k3;
+          acc[ct] = (f32x4){a0 + a2, a1 + a3, a0 - a2, a1 - a3};
+        }
+#pragma unroll
+        for (int m = 16; m <= 32; m <<= 1) {
+          const bool upper = (lane & m) != 0;
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float o = __shfl_xor(acc[ct][i], m);
+              acc[ct][i] = upper ? o - acc[ct][i] : acc[ct][i] + o;
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < NCT; m <<= 1)
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct)
+            if (!(ct & m)) {
+              const f32x4 x0 = acc[ct], x1 = acc[ct | m];
+              acc[ct] = x0 + x1;
+              acc[ct | m] = x0 - x1;
+            }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] *= a.had;
+      } else {
+        // K-steps outer, tiles inner: NCT independent accumulation chains
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const u32x4 bw = {kh[4 * s], kh[4 * s + 1], kh[4 * s + 2], kh[4 * s + 3]};
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+            const half8 A = *(const half8 *)&sm.t[16 * ct + tok][32 * s + 8 * q];
+            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(half8, bw), acc[ct], 0, 0, 0);
+          }
         }
       }
       const int row = 32 * wave + 16 * tt + tok;
@@ -623,7 +700,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           sc = f16_round(v32);
           // a step near an fp16 rounding midpoint is decided again: from the fp64 sum of
           // squares of the fp32 x, then, if still near one, from the exact x
-          const bool pn = vt && near_mid(v32, kParKA * v32);
+          const bool pn = vt && near_mid(v32, parKA * v32);
           if (__builtin_expect(__any(pn), 0)) {
             double s64 = 0.0;
 #pragma unroll
@@ -635,7 +712,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             const double d64 = quest_pre64(s64, a.clip, Lk, D);
             if (pn) sc = f16_of_f64(d64);
             // still near one: the exact x after the step's tiles
-            defer(pn && near_mid((float)d64, kParKB * (float)d64), row, kh, 0u, 0.f, 0.f, 0.f, sc, 0.f);
+            defer(pn && near_mid((float)d64, parKB * (float)d64), row, kh, 0u, 0.f, 0.f, 0.f, sc, 0.f);
           }
         } else if constexpr (NL > 0) {
           OrderStats<NL> o;
@@ -653,14 +730,14 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           // interpolation of the order statistics, and if still near one, from the exact x
           // after the step's tiles
           const float sx = fabsf(ap.x0) + fabsf(ap.x1), sxy = sx + fabsf(ap.y0) + fabsf(ap.y1);
-          const bool pn = vt && (near_mid(ap.vz, kParKAff * sx) || near_mid(ap.vs, kParKAff * sxy / (float)(Lk - 1)));
+          const bool pn = vt && (near_mid(ap.vz, parKAff * sx) || near_mid(ap.vs, parKAff * sxy / (float)(Lk - 1)));
           if (__builtin_expect(__any(pn), 0)) {
             double s64, z64;
             float sc1, zp1;
             affine_exact<D>(a, ap.x0, ap.x1, ap.y0, ap.y1, Lk, sc1, zp1, &s64, &z64);
             if (pn) { sc = sc1; zp = zp1; }
-            const bool pn2 = pn && (near_mid((float)z64, kParKAff2 * sx) ||
-                                    near_mid((float)s64, kParKAff2 * sxy / (float)(Lk - 1)));
+            const bool pn2 = pn && (near_mid((float)z64, parKAff2 * sx) ||
+                                    near_mid((float)s64, parKAff2 * sxy / (float)(Lk - 1)));
             // candidates for the exact order statistics: this lane's elements within mg of the
             // cuts (the contraction's error is far below mg)
             const float cut_lo = fmaxf(ap.x0, ap.x1), cut_hi = fminf(ap.y0, ap.y1);
@@ -727,14 +804,11 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             const int j = 16 * (bit >> 2) + 4 * (qs >= 0 ? qs : 0) + (bit & 3);
             double part = 0.0;
 #pragma unroll
-            for (int s = 0; s < CPL / 8; ++s) {
-              const half8 tv = *(const half8 *)&sm.t[j][32 * s + 8 * q];
-#pragma unroll
-              for (int e8 = 0; e8 < 8; ++e8) {
-                const unsigned w = kh[4 * s + e8 / 2];
-                const float kv = (e8 & 1) ? f16_hi(w) : f16_lo(w);
-                part += (double)((float)tv[e8] * kv);   // fp16 x fp16 is exact in fp32
-              }
+            for (int w = 0; w < CPL / 2; ++w) {   // the lane's channels, two per key word
+              const int c0 = 2 * kh_word(q, w);
+              const f16x2 tv = *(const f16x2 *)&sm.t[j][c0];
+              part += (double)((float)tv[0] * f16_lo(kh[w]));   // fp16 x fp16 is exact in fp32
+              part += (double)((float)tv[1] * f16_hi(kh[w]));
             }
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
@@ -896,7 +970,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           if (e < kStaged) {
             if (tid < D / 2) sm.krow[tid] = sm.kq[wv][e][tid];
           } else if (tid < D / 8) {
-            *(u32x4 *)&sm.krow[(tid & 3) * (D / 8) + 4 * (tid >> 2)] = key_row8(u, tid);
+            *(u32x4 *)&sm.krow[4 * tid] = key_row8(u, tid);
           }
           __syncthreads();
           float scx = d.sc, zpx = d.zp;
@@ -1231,9 +1305,10 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   const int nl = need == 0 ? 0 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
   const bool f32 = a.in_dtype == WUSHKV_DT_F32;
   const int sp = (int)spw;
-#define WUSHKV_FLUSH(D, ES, NL)                                                                          \
-  if (a.pg.table) hipLaunchKernelGGL((flush_kernel<D, ES, NL, true>), grid, dim3(kThreads), 0, s, a, sp); \
-  else hipLaunchKernelGGL((flush_kernel<D, ES, NL, false>), grid, dim3(kThreads), 0, s, a, sp)
+#define WUSHKV_FLUSH(D, ES, NL)                                                                                 \
+  if (a.had != 0.f) hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, true>), grid, dim3(kThreads), 0, s, a, sp); \
+  else if (a.pg.table) hipLaunchKernelGGL((flush_kernel<D, ES, NL, true, false>), grid, dim3(kThreads), 0, s, a, sp); \
+  else hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, false>), grid, dim3(kThreads), 0, s, a, sp)
 #define WUSHKV_FLUSH_NL(D, ES)            \
   switch (nl) {                            \
     case 0: WUSHKV_FLUSH(D, ES, 0); break; \

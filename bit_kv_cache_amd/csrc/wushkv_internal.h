@@ -76,6 +76,7 @@ struct FlushArgs {
   double lo_t64, hi_t64;
   PageTable pg;
   int64_t body_cap;
+  float had;                      // nonzero: T_K = had * H (Sylvester-Hadamard), tk unused
 };
 
 struct AppendArgs {

@@ -47,8 +47,8 @@ extern "C" {
 /* 1: append/flush, query transform, decode (plain and fused).  2: adds the decode
  * step, ragged, device-count and paged calls, and the calibration sums.  3: adds
  * wushkv_decode_attention_generic (the per-call choice of the fp32 decode kernel).  4: adds
- * wushkv_decode_attention_noalloc. */
-#define WUSHKV_ABI_VERSION 4
+ * wushkv_decode_attention_noalloc.  5: adds wushkv_append_flush_hadamard. */
+#define WUSHKV_ABI_VERSION 5
 
 typedef enum {
   WUSHKV_OK = 0,
@@ -169,6 +169,22 @@ size_t wushkv_decode_workspace_bytes(const wushkv_cache *c, int64_t n_tokens, in
 int wushkv_append_flush(const wushkv_cache *c, int64_t n_before, int32_t n_new,
                         const void *k_new, const void *v_new, int32_t in_dtype,
                         const void *t_k_f16, void *stream);
+
+/*
+ * wushkv_append_flush with the fixed Hadamard key transform T_K = scale * H, H the
+ * Sylvester-Hadamard matrix of order head_dim (H[j][i] = (-1)^popcount(i & j)), formed
+ * by an in-register fast Walsh-Hadamard transform (head_dim log2(head_dim) additions per
+ * key) instead of the d x d product (WUSH-KV digest, "motivation" and "key experiments":
+ * fixed orthogonal transforms such as Hadamard are the baseline the data-adaptive
+ * transform is compared against).  The result is that of wushkv_append_flush with t_k_f16
+ * = scale * H in fp16; scale = fp16(1/sqrt(head_dim)) gives the orthonormal transform.
+ * The decode takes T^{-T} = H / (scale * head_dim) as for any key transform.
+ * Errors as wushkv_append_flush; scale zero, not finite or not exactly an fp16 value ->
+ * ERR_SHAPE.
+ */
+int wushkv_append_flush_hadamard(const wushkv_cache *c, int64_t n_before, int32_t n_new,
+                                 const void *k_new, const void *v_new, int32_t in_dtype,
+                                 float scale, void *stream);
 
 /*
  * Query transform q~[b][h] = T_{h/G}^{-T} q[b][h] (WUSH-KV digest, "method key

@@ -42,7 +42,7 @@ def test_status_strings_and_version(lib):
     assert W.status_string(0) == "ok"
     assert "capacity" in W.status_string(W.ERR_CAPACITY)
     assert W.status_string(99) == "unknown status"
-    assert lib.wushkv_abi_version() == 4
+    assert lib.wushkv_abi_version() == 5
 
 
 def _spec(**kw):
@@ -302,3 +302,22 @@ def test_device_step_validation(lib):
     assert f(mt=0) == W.ERR_SHAPE
     assert f(mt=9000) == W.ERR_CAPACITY
     assert f(wsb=ws - 1) == W.ERR_WORKSPACE
+
+
+def test_hadamard_flush_argument_checks(lib):
+    """wushkv_append_flush_hadamard: the scale must be a nonzero, finite fp16 value; the
+    usual pointer checks; nothing is launched on these failures."""
+    s = _spec(quant_k=W.Q_QUEST)
+    import ctypes as C
+    desc = s.desc()
+    for p in W.PLANES:
+        setattr(desc, p, 256)
+    fake = C.c_void_p(4096)
+    for scale in (0.0, float("nan"), float("inf"), 0.1, 1e-9):
+        assert lib.wushkv_append_flush_hadamard(C.byref(desc), 0, 16, fake, fake, W.DT_BF16, scale, None) == W.ERR_SHAPE
+    ok_scale = 0.08837890625                      # fp16(1/sqrt(128))
+    assert lib.wushkv_append_flush_hadamard(C.byref(desc), 0, 16, None, fake, W.DT_BF16, ok_scale, None) == W.ERR_NULL
+    assert lib.wushkv_append_flush_hadamard(C.byref(desc), 0, 16, C.c_void_p(4100), fake, W.DT_BF16, ok_scale,
+                                            None) == W.ERR_ALIGN
+    assert lib.wushkv_append_flush_hadamard(C.byref(desc), 9000, 16, fake, fake, W.DT_BF16, ok_scale,
+                                            None) == W.ERR_CAPACITY
