@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
 def log(*a):
@@ -202,6 +203,7 @@ def run_flush_leg(args):
     tks = [gen.key_transforms(w, l)[0].to(dev) for l in range(layers)]
     res = {}
     bits_list = [int(b) for b in args.flush_bits.split(",")] if args.flush_bits else list(w.flush_bits)
+    had_res = None
     for bits in bits_list:
         spec = W.CacheSpec(batch=1, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, capacity=n,
                            sink=w.sink, recent=w.recent, chunk=w.chunk, bits_k=bits, bits_v=bits,
@@ -217,13 +219,42 @@ def run_flush_leg(args):
             torch.cuda.synchronize()
         ms = e0.elapsed_time(e1)
         nbytes = layers * flush_bytes(w, bits, n)
+        # the T_K contraction: 2 d^2 flop per flushed key row, on fp16 MFMA (dense peak 2.5 PFLOP/s)
+        rows = layers * w.num_kv_heads * (w.chunk * (max(0, n - w.sink - w.recent) // w.chunk))
+        tflops = 2 * w.head_dim ** 2 * rows / (ms * 1e-3) / 1e12
         res[bits] = dict(ms=ms, tokens_per_s=n / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
-                         bytes=nbytes)
+                         bytes=nbytes, mfma_tflops=tflops)
         log(f"[bench] flush {bits}-bit: {ms:.3f} ms for {layers} layers -> {n / (ms * 1e-3):.3e} tokens/s, "
             f"{nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
+        if bits == 2 and args.hadamard:
+            # the fixed Hadamard key transform: in-register butterflies vs the same matrix,
+            # fp16(H / sqrt(d)), through the dense contraction
+            import numpy as np
+
+            from synth import transforms as TR
+            th = TR.as_inputs(TR.per_head(TR.hadamard(w.head_dim), w.num_kv_heads))[0].to(dev)
+            scale = float(np.float16(1.0 / np.sqrt(w.head_dim)))
+            hms = {}
+            for name, f in (("fwht", lambda c, l: W.append_flush_hadamard(c, kv[l][0], kv[l][1], scale, n_before=0)),
+                            ("dense_hadamard", lambda c, l: W.append_flush(c, kv[l][0], kv[l][1], th, n_before=0))):
+                for rep in range(2):
+                    torch.cuda.synchronize()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for l in range(layers):
+                        f(caches[l], l)
+                    e1.record()
+                    torch.cuda.synchronize()
+                hms[name] = e0.elapsed_time(e1)
+            res["hadamard"] = hms
+            log(f"[bench] flush 2-bit with the Hadamard key transform: in-register FWHT {hms['fwht']:.3f} ms, "
+                f"the same matrix through the contraction {hms['dense_hadamard']:.3f} ms for {layers} layers")
+        had_res = res.pop("hadamard", had_res)
         del caches
     del kv
     torch.cuda.empty_cache()
+    if had_res:
+        res["hadamard"] = had_res
     return res
 
 
@@ -635,55 +666,110 @@ def summarize_trace(trace_csv):
     return "\n".join(lines)
 
 
-def run_cpu_leg(dl, sample_heads=16):
-    """The oracle, as it stands, on a bounded sample of the decode step: the G query
-    heads of `sample_heads` (batch row, KV head) pairs, at the same context."""
+def _cpu_flush_worker_init(barrier):
+    global _CPU_BARRIER
+    _CPU_BARRIER = barrier
+
+
+def _cpu_flush_worker(job):
+    """One (layer, KV head) block of the bulk flush through the oracle, single-threaded:
+    the key transform, quantization and packing of its 65216 body rows (plus its FP16
+    windows).  Inputs are generated first, untimed; all workers start timing together."""
+    layer, head, bits = job
     import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import layout as LY
+    from oracle import wushkv_ref as R
+    from synth import configs, gen
+    w = configs.BULK_FLUSH
+    k, v = gen.kv_block(w, layer, 0, head, w.context, "cpu")
+    k = k.float().numpy().astype(np.float64)
+    v = v.float().numpy().astype(np.float64)
+    t16 = gen.key_transforms(w, layer)[0][head].numpy()
+    with threadpool_limits(limits=1):
+        _CPU_BARRIER.wait()
+        t0 = time.perf_counter()
+        c = R.build_head_cache(k, v, t16, w.context, sink=w.sink, recent=w.recent, chunk=w.chunk, quant_k="quest",
+                               quant_v="quest", bits_k=bits, bits_v=bits, clip_mult=w.clip_mult)
+        LY.pack_k(c.codes_k, bits)
+        LY.pack_v(c.codes_v, bits)
+        t1 = time.perf_counter()
+    return t0, t1
+
+
+def _cpu_decode_worker(job):
+    """The oracle's decode step for the G query heads of one (batch row, KV head) pair of
+    the batched-serving workload, single-threaded: its cache is built first (untimed), then
+    query transform + decode are repeated for `seconds`; returns (reps, seconds)."""
+    b, g, n, seconds = job
+    import numpy as np
+    from threadpoolctl import threadpool_limits
 
     from oracle import wushkv_ref as R
-    from synth import gen
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_info = threadpool_limits = None
-    cores = len(os.sched_getaffinity(0))
-    w = dl["workload"]
-    n = dl["n"]
-    t16, _ = gen.key_transforms(w, 0)
-    cache_pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)][:: (w.batch * w.num_kv_heads) // sample_heads][:sample_heads]
+    from synth import configs, gen
+    w = configs.SERVING
+    t16 = gen.key_transforms(w, 0)[0][g].numpy()
+    kb, vb = gen.kv_block(w, 0, b, g, n, "cpu")
+    kb, vb = kb.float().numpy().astype(np.float64), vb.float().numpy().astype(np.float64)
+    c = R.build_head_cache(kb, vb, t16, n, sink=w.sink, recent=w.recent, chunk=w.chunk, quant_k=w.quant_k,
+                           quant_v=w.quant_v, bits_k=w.bits_k, bits_v=w.bits_v, pct_lo=w.pct_lo, pct_hi=w.pct_hi)
     q = gen.queries(w, 0, 0, "cpu").float().numpy().astype(np.float64)
-    heads = []
-    for b, g in cache_pairs:
-        kb, vb = gen.kv_block(w, 0, b, g, n, "cuda")
-        kb, vb = kb.float().cpu().numpy().astype(np.float64), vb.float().cpu().numpy().astype(np.float64)
-        heads.append((b, g, R.build_head_cache(kb, vb, t16[g].numpy(), n, sink=w.sink, recent=w.recent,
-                                               chunk=w.chunk, quant_k=w.quant_k, quant_v=w.quant_v,
-                                               bits_k=w.bits_k, bits_v=w.bits_v, pct_lo=w.pct_lo,
-                                               pct_hi=w.pct_hi)))
-    if threadpool_limits:
-        threadpool_limits(limits=cores)
-    used = cores
-    if threadpool_info:
-        infos = threadpool_info()
-        if infos:
-            used = max(i.get("num_threads", 1) for i in infos)
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        for b, g, c in heads:
+    with threadpool_limits(limits=1):
+        _CPU_BARRIER.wait()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < seconds:
             for h in range(g * w.group, (g + 1) * w.group):
-                qt = R.query_transform(t16[g].numpy(), q[b, h])
-                R.decode_head(c, q[b, h], qt)
-        reps += 1
-        if time.perf_counter() - t0 > 10.0:
-            break
-    el = (time.perf_counter() - t0) / reps
-    frac = len(heads) / (w.batch * w.num_kv_heads)
-    sample_bytes = dl["bytes"] * frac
-    return dict(value=sample_bytes / el / 1e9, unit="GB/s", cores=used, kind="oracle",
-                sample=f"{len(heads)} of {w.batch * w.num_kv_heads} (batch row, KV head) pairs x {w.group} query heads, "
-                       f"n={n}, query transform + decode, {reps} reps in {el * reps:.1f} s; "
-                       f"step time scaled to the full batch = {el / frac * 1e3:.0f} ms")
+                R.decode_head(c, q[b, h], R.query_transform(t16, q[b, h]))
+            reps += 1
+        return reps, time.perf_counter() - t0
+
+
+def run_cpu_decode_leg(cores, n, seconds=8.0):
+    """The oracle's decode of the batched-serving step on `cores` (batch row, KV head) pairs
+    at once, one single-threaded process per core; the step time of all 256 pairs is the
+    mean time per pair scaled by 256 / cores (the pairs are independent)."""
+    import multiprocessing as mp
+
+    from synth import configs
+    w = configs.SERVING
+    pairs = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    jobs = [(b, g, n, seconds) for b, g in pairs[:: len(pairs) // cores][:cores]]
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(len(jobs))
+    with ctx.Pool(len(jobs), initializer=_cpu_flush_worker_init, initargs=(barrier,)) as pool:
+        res = pool.map(_cpu_decode_worker, jobs)
+    per_pair = sum(el / reps for reps, el in res) / len(res)
+    step_s = per_pair * len(pairs) / len(jobs)
+    return step_s, per_pair, len(jobs), sum(r for r, _ in res)
+
+
+def run_cpu_flush_leg(cores, bits=2):
+    """The oracle's bulk flush on `cores` (layer, KV head) blocks at once, one process per
+    core (spawned, single-threaded), timed from a common start to the last finish; the full
+    pass (36 layers x 8 KV heads) is that wall time scaled by 288 / blocks."""
+    import multiprocessing as mp
+
+    from synth import configs
+    w = configs.BULK_FLUSH
+    nb = cores
+    jobs = [(l % w.layers, (3 * l) % w.num_kv_heads, bits) for l in range(nb)]
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(nb)
+    with ctx.Pool(nb, initializer=_cpu_flush_worker_init, initargs=(barrier,)) as pool:
+        spans = pool.map(_cpu_flush_worker, jobs)
+    wall = max(t1 for _, t1 in spans) - min(t0 for t0, _ in spans)
+    per_block = sum(t1 - t0 for t0, t1 in spans) / nb
+    blocks = w.layers * w.num_kv_heads
+    pass_s = wall * blocks / nb
+    return {"value": round(w.context / pass_s, 1), "unit": "tokens/s", "cores": nb, "kind": "oracle",
+            "sample": f"{nb} of {blocks} (layer, KV head) blocks of the bulk flush at {bits} bits (65536 tokens each: "
+                      f"key transform, QuEST quantization and packing of 65216 body rows), one single-threaded process "
+                      f"per core, {wall:.2f} s wall; the 36-layer pass scaled to {pass_s:.1f} s",
+            "single_core_tokens_per_s": round(w.context / (per_block * blocks), 1),
+            "single_core_note": f"one block per core in {per_block:.2f} s on average; a full pass on one core would "
+                                f"take {per_block * blocks:.0f} s"}
 
 
 def main():
@@ -696,6 +782,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode leg (profiling the flush alone)")
     ap.add_argument("--flush-bits", type=str, default="", help="comma-separated bit widths of the flush leg")
     ap.add_argument("--no-long", action="store_true", help="skip the long-context decode leg")
+    ap.add_argument("--no-hadamard", dest="hadamard", action="store_false",
+                    help="skip the Hadamard key-transform timing of the flush leg")
     ap.add_argument("--no-calib", action="store_true", help="skip the calibration-statistics leg")
     ap.add_argument("--no-graph", action="store_true", help="skip the launch-bound decode-step leg")
     ap.add_argument("--no-transforms", action="store_true", help="skip the key-transform module-error leg")
@@ -728,6 +816,18 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(every workload runs on a single MI355X); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    # the oracle's flush baseline runs first, in worker processes started before this
+    # process touches the GPU (one per core of the job's share, at most 16)
+    cpu_flush = cpu_decode = None
+    if not args.no_cpu and not args.no_decode:
+        from synth import configs as _cfg
+        ncores = min(16, len(os.sched_getaffinity(0)))
+        n_cpu = _cfg.SERVING.context + args.warmup + args.steps + 1   # the decode leg's context at its timed steps
+        cpu_decode = run_cpu_decode_leg(ncores, n_cpu)
+        log(f"[bench] cpu decode baseline: {cpu_decode[0]:.2f} s per step ({cpu_decode[2]} processes)")
+        if not args.no_flush:
+            cpu_flush = run_cpu_flush_leg(ncores)
+            log(f"[bench] cpu flush baseline: {cpu_flush['value']} tokens/s ({cpu_flush['cores']} processes)")
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.copy_check > 0:
@@ -773,6 +873,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "dtype_note": ("scores, softmax and accumulation in fp32; the body's q~ . c runs on fp4 x fp4 matrix cores "
+                       "as exact digit products of q~ on a 22-bit fixed-point grid, and p * s_V enters the fp16 PV "
+                       "product as an fp16 hi + lo pair (~22 bits); cache codes are 2-bit, windows and "
+                       "parameters fp16"),
         "data": "synthetic (seeded Student-t K/V under per-head covariance, random per-head T_K)",
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "context": dl["n"],
@@ -792,10 +896,25 @@ def main():
                                "(12 splits, merged in LDS); duration from the steps with no flush due",
                      "bytes_per_launch": int(dl["kern_bytes"]), "us_per_launch": round(dl["kern_ms"] * 1e3, 2)},
     }
+    had = fl.pop("hadamard", None) if fl else None
+    w_flush_tokens = 65536
     if fl:
         line["flush"] = {f"{b}bit": {"tokens_per_s": round(r["tokens_per_s"], 1), "ms_36_layers": round(r["ms"], 3),
-                                     "GB_per_s": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / HBM_PEAK_GBS, 4)}
+                                     "GB_per_s": round(r["gbs"], 1), "frac_hbm": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                                     "key_transform_TFLOP_per_s": round(r["mfma_tflops"], 1),
+                                     "key_transform_mfma_util": round(r["mfma_tflops"] / MFMA_F16_PEAK_TFLOPS, 4)}
                          for b, r in fl.items()}
+        if had:
+            line["flush"]["hadamard_2bit"] = {
+                "fwht_ms_36_layers": round(had["fwht"], 3), "dense_ms_36_layers": round(had["dense_hadamard"], 3),
+                "fwht_tokens_per_s": round(w_flush_tokens / (had["fwht"] * 1e-3), 1),
+                "note": "T_K = fp16(H/sqrt(d)): in-register fast Walsh-Hadamard transform "
+                        "(wushkv_append_flush_hadamard) vs the same matrix through the dense matrix-core contraction; "
+                        "bit-identical caches"}
+        line["flush"]["note"] = ("36 x append_flush(n_before=0, n_new=65536) of 8 KV heads, QuEST K and V; the key "
+                                 "transform T_K k on v_mfma_f32_16x16x32_f16, 2 d^2 flop per body row, against the "
+                                 "2.5 PFLOP/s dense fp16 peak (the flush is HBM-bound; at its HBM roofline the "
+                                 "matrix cores would be ~18% busy)")
     if lc:
         line["long_context"] = dict(lc, workload=configs_name("LONG_CONTEXT"),
                                     quant="percentile-clipped affine 2-bit K / 3-bit V")
@@ -809,7 +928,18 @@ def main():
         line["calibration"] = dict(cl, workload=configs_name("CALIB"),
                                    note="bf16 rows; out[g] = sum of x x^T; flop counted as 2 N d^2 per head")
     if not args.no_cpu:
-        line["cpu_baseline"] = run_cpu_leg(dl)
+        step_s, per_pair, nproc, reps = cpu_decode
+        cb = {"value": round(dl["bytes"] / step_s / 1e9, 4), "unit": "GB/s", "cores": nproc, "kind": "oracle",
+              "sample": f"{nproc} of {w.batch * w.num_kv_heads} (batch row, KV head) pairs x {w.group} query heads "
+                        f"at the decode leg's context, one single-threaded process per core, query transform + "
+                        f"decode repeated for 8 s each ({reps} pair-steps, {per_pair * 1e3:.1f} ms per pair); the "
+                        f"step over all pairs scaled to {step_s:.3f} s",
+              "single_core": {"value": round(dl["bytes"] / (per_pair * w.batch * w.num_kv_heads) / 1e9, 4),
+                              "unit": "GB/s", "cores": 1,
+                              "note": "the same pairs' mean time per pair, as if one core decoded all 256"}}
+        if cpu_flush:
+            cb["flush"] = cpu_flush
+        line["cpu_baseline"] = cb
     print(json.dumps(line), flush=True)
 
 
