@@ -223,7 +223,7 @@ def run_flush_leg(args):
         rows = layers * w.num_kv_heads * (w.chunk * (max(0, n - w.sink - w.recent) // w.chunk))
         tflops = 2 * w.head_dim ** 2 * rows / (ms * 1e-3) / 1e12
         res[bits] = dict(ms=ms, tokens_per_s=n / (ms * 1e-3), gbs=nbytes / (ms * 1e-3) / 1e9,
-                         bytes=nbytes, mfma_tflops=tflops)
+                         bytes=nbytes, bytes_layer=flush_bytes(w, bits, n), mfma_tflops=tflops)
         log(f"[bench] flush {bits}-bit: {ms:.3f} ms for {layers} layers -> {n / (ms * 1e-3):.3e} tokens/s, "
             f"{nbytes / (ms * 1e-3) / 1e9:.1f} GB/s")
         if bits == 2 and args.hadamard:
@@ -643,6 +643,40 @@ def summarize_counters(fetch_csv, write_csv, copy_mib):
             "kernels": kernels}
 
 
+def summarize_pmc(csv_path):
+    """Every counter of a rocprofv3 --pmc counter_collection.csv, averaged per dispatch of
+    each of the library's kernels (grouped by kernel and grid), as a text table; with the
+    SQ_* counters also the derived per-wave instruction counts and busy fractions."""
+    import csv
+    import collections
+
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        name = r["Kernel_Name"]
+        if "wushkv" not in name:
+            continue
+        name = name.replace("void ", "").replace("wushkv::(anonymous namespace)::", "").split("(")[0]
+        acc[(name, r["Grid_Size"], r["Workgroup_Size"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    lines = []
+    for (name, grid, wg), cs in sorted(acc.items()):
+        mean = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        lines.append(f"{name}  grid {grid}  workgroup {wg}  ({n} dispatches)")
+        for c in sorted(mean):
+            lines.append(f"    {c:28s} {mean[c]:16.1f}")
+        waves = mean.get("SQ_WAVES")
+        if waves:
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+                if c in mean:
+                    lines.append(f"    {c + ' per wave':28s} {mean[c] / waves:16.1f}")
+        if mean.get("SQ_BUSY_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            lines.append(f"    {'MFMA busy / SQ busy':28s} {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / mean['SQ_BUSY_CYCLES']:16.4f}")
+        if mean.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in mean:
+            lines.append(f"    {'LDS conflict cycles / LDS op':28s} "
+                         f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_INSTS_LDS']:16.3f}")
+    return "\n".join(lines)
+
+
 def summarize_trace(trace_csv):
     """Library kernels of a rocprofv3 kernel-trace CSV grouped by (kernel, grid, workgroup
     size): the legs of this bench launch distinct grids.  Durations in microseconds."""
@@ -800,9 +834,15 @@ def main():
                          "--copy-check MIB) as JSON on stdout")
     ap.add_argument("--counters-kernels", choices=sorted(COUNTER_SOURCES), default="decode",
                     help="which kernels' sources the counter summary is tied to")
+    ap.add_argument("--pmc-summary", metavar="COUNTER_CSV",
+                    help="no GPU work: average every counter of a rocprofv3 --pmc counter_collection.csv per "
+                         "dispatch of each library kernel and print it")
     ap.add_argument("--trace-summary", metavar="TRACE_CSV",
                     help="no GPU work: group a rocprofv3 kernel_trace.csv by kernel and grid and print it")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(summarize_pmc(args.pmc_summary))
+        return
     if args.trace_summary:
         print(summarize_trace(args.trace_summary))
         return
@@ -904,6 +944,13 @@ def main():
                                      "key_transform_TFLOP_per_s": round(r["mfma_tflops"], 1),
                                      "key_transform_mfma_util": round(r["mfma_tflops"] / MFMA_F16_PEAK_TFLOPS, 4)}
                          for b, r in fl.items()}
+        if 2 in fl:
+            # HBM bytes per append_flush call (one layer) from the committed counter summary,
+            # beside the call's algorithmic bytes
+            ft = traffic_from_profile("flush_bulk_counters.json", ["flush_kernel<128, 2, 0, false, false>",
+                                                                   "append_kernel"])
+            line["flush"]["2bit"]["algorithmic_bytes_per_layer"] = fl[2]["bytes_layer"]
+            line["flush"]["2bit"]["traffic_bytes_per_layer"] = ft
         if had:
             line["flush"]["hadamard_2bit"] = {
                 "fwht_ms_36_layers": round(had["fwht"], 3), "dense_ms_36_layers": round(had["dense_hadamard"], 3),
