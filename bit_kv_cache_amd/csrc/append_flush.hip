@@ -269,6 +269,17 @@ __device__ __forceinline__ void seg_float(const RawSeg<ES, CPL> &s, bool ring, i
 
 // ---- per-token parameters; the 4 lanes of a token exchange through lanes ^16, ^32
 
+// x + x of lane ^ M (M = 16 or 32) through gfx950's permlane swaps, which give both lanes
+// of the pair (x of the lower lane, x of the upper lane): the same sum, bit for bit, in
+// both, with no LDS round trip
+template <int M>
+__device__ __forceinline__ float pair_sum(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = M == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int NL>
 struct OrderStats {
   float lo[NL > 0 ? NL : 1], hi[NL > 0 ? NL : 1];  // lo ascending, hi descending
@@ -336,7 +347,7 @@ struct AffPre {
 };
 
 template <int D, int NL>
-__device__ __forceinline__ AffPre affine_pre(const FlushArgs &a, const OrderStats<NL> &o, int L) {
+__device__ __forceinline__ AffPre affine_pre(const FlushArgs &a, const OrderStats<NL> &o, float ilm1) {
   AffPre p;
   p.x0 = pick<NL>(o.lo, a.lo_i);
   p.x1 = (a.lo_i + 1 < D) ? pick<NL>(o.lo, a.lo_i + 1) : p.x0;
@@ -345,13 +356,17 @@ __device__ __forceinline__ AffPre affine_pre(const FlushArgs &a, const OrderStat
   p.y0 = pick<NL>(o.hi, hk);
   p.y1 = (hk >= 1) ? pick<NL>(o.hi, hk - 1) : p.y0;
   const float vhi = (a.hi_i + 1 < D) ? p.y0 + a.hi_t * (p.y1 - p.y0) : p.y0;
-  p.vs = (vhi - vlo) / (float)(L - 1);
+  p.vs = (vhi - vlo) * ilm1;   // ilm1 = 1 / (L - 1)
   p.vz = vlo;
   return p;
 }
 
-__device__ __forceinline__ float quest_pre(float ss, float clip, int L, int D) {
-  return 2.0f * clip * sqrtf(ss / (float)D) / (float)L;
+// The RMS step before its fp16 rounding, sqrt(ss) * fac with fac = 2 c / (sqrt(d) L)
+// (rounded once, from fp64).  v_sqrt_f32 (1 ulp) and the product keep it within 3e-7 of
+// the exact step, inside the parameter bands below.
+__device__ __forceinline__ float quest_pre(float ss, float fac) { return __builtin_amdgcn_sqrtf(ss) * fac; }
+__device__ __forceinline__ float quest_fac(float clip, int L, int D) {
+  return (float)(2.0 * (double)clip / (sqrt((double)D) * (double)L));
 }
 
 // fp64 -> fp16, correctly rounded (to nearest, ties to even), returned as a float: round
@@ -412,7 +427,7 @@ struct Quant {
 template <bool QU>
 __device__ __forceinline__ Quant<QU> make_quant(float sc, float zp, int L, float tol) {
   Quant<QU> q;
-  q.inv = sc != 0.f ? 1.0f / sc : 0.f;
+  q.inv = sc != 0.f ? __builtin_amdgcn_rcpf(sc) : 0.f;   // 1 ulp: far inside the edge bands
   q.add = (QU ? (float)(L / 2) : 0.5f) + tol;
   q.z = zp;
   q.top = (float)(L - 1);
@@ -549,6 +564,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const int q = lane >> 4, tok = lane & 15;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
   const int Lk = 1 << a.bits_k, Lv = 1 << a.bits_v;
+  const float qfac_k = quest_fac(a.clip, Lk, D), qfac_v = quest_fac(a.clip, Lv, D);
+  const float ilm1_k = (float)(1.0 / (double)(Lk - 1)), ilm1_v = (float)(1.0 / (double)(Lv - 1));
   // this sequence's rows before the call and its flushed body rows [u0, u1)
   const int64_t n_before = seq_before(a, b);
   if (n_before < 0) return;   // (device counts) out of range: the sequence is left alone
@@ -694,9 +711,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
             for (int i = 0; i < 4; ++i) s4[i] = fmaf(acc[ct][i], acc[ct][i], s4[i]);
           float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-          ss += __shfl_xor(ss, 16);
-          ss += __shfl_xor(ss, 32);
-          const float v32 = quest_pre(ss, a.clip, Lk, D);
+          ss = pair_sum<32>(pair_sum<16>(ss));
+          const float v32 = quest_pre(ss, qfac_k);
           sc = f16_round(v32);
           // a step near an fp16 rounding midpoint is decided again: from the fp64 sum of
           // squares of the fp32 x, then, if still near one, from the exact x
@@ -723,21 +739,21 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             for (int i = 0; i < 4; ++i) os_insert(o, acc[ct][i]);
           os_merge(o, 16);
           os_merge(o, 32);
-          const AffPre ap = affine_pre<D, NL>(a, o, Lk);
+          const AffPre ap = affine_pre<D, NL>(a, o, ilm1_k);
           sc = f16_round(ap.vs);
           zp = f16_round(ap.vz);
           // scale or zero near an fp16 rounding midpoint: decided again from the fp64
           // interpolation of the order statistics, and if still near one, from the exact x
           // after the step's tiles
           const float sx = fabsf(ap.x0) + fabsf(ap.x1), sxy = sx + fabsf(ap.y0) + fabsf(ap.y1);
-          const bool pn = vt && (near_mid(ap.vz, parKAff * sx) || near_mid(ap.vs, parKAff * sxy / (float)(Lk - 1)));
+          const bool pn = vt && (near_mid(ap.vz, parKAff * sx) || near_mid(ap.vs, parKAff * sxy * ilm1_k));
           if (__builtin_expect(__any(pn), 0)) {
             double s64, z64;
             float sc1, zp1;
             affine_exact<D>(a, ap.x0, ap.x1, ap.y0, ap.y1, Lk, sc1, zp1, &s64, &z64);
             if (pn) { sc = sc1; zp = zp1; }
             const bool pn2 = pn && (near_mid((float)z64, parKAff2 * sx) ||
-                                    near_mid((float)s64, parKAff2 * sxy / (float)(Lk - 1)));
+                                    near_mid((float)s64, parKAff2 * sxy * ilm1_k));
             // candidates for the exact order statistics: this lane's elements within mg of the
             // cuts (the contraction's error is far below mg)
             const float cut_lo = fmaxf(ap.x0, ap.x1), cut_hi = fminf(ap.y0, ap.y1);
@@ -841,9 +857,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
           for (int k = 0; k < CPL; ++k) s4[k & 3] = fmaf(xv[k], xv[k], s4[k & 3]);
           float ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-          ss += __shfl_xor(ss, 16);
-          ss += __shfl_xor(ss, 32);
-          const float v32 = quest_pre(ss, a.clip, Lv, D);
+          ss = pair_sum<32>(pair_sum<16>(ss));
+          const float v32 = quest_pre(ss, qfac_v);
           sc = f16_round(v32);
           // near an fp16 rounding midpoint: the step from the exact (fp64) sum of squares
           const bool pn = vt && near_mid(v32, kParV * v32);
@@ -862,13 +877,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           for (int k = 0; k < CPL; ++k) os_insert(o, xv[k]);
           os_merge(o, 16);
           os_merge(o, 32);
-          const AffPre ap = affine_pre<D, NL>(a, o, Lv);
+          const AffPre ap = affine_pre<D, NL>(a, o, ilm1_v);
           sc = f16_round(ap.vs);
           zp = f16_round(ap.vz);
           // near an fp16 rounding midpoint: the interpolation in fp64 (the order statistics
           // of values are exact)
           const float ez = kParV * (fabsf(ap.x0) + fabsf(ap.x1));
-          const float es = kParV * (fabsf(ap.x0) + fabsf(ap.x1) + fabsf(ap.y0) + fabsf(ap.y1)) / (float)(Lv - 1);
+          const float es = kParV * (fabsf(ap.x0) + fabsf(ap.x1) + fabsf(ap.y0) + fabsf(ap.y1)) * ilm1_v;
           if (__builtin_expect(vt && (near_mid(ap.vz, ez) || near_mid(ap.vs, es)), 0))
             affine_exact<D>(a, ap.x0, ap.x1, ap.y0, ap.y1, Lv, sc, zp);
         } else {
