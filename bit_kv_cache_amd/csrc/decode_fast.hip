@@ -217,6 +217,18 @@ __device__ __forceinline__ float row_max(float x) {
   return x;
 }
 
+// W = p s as an fp16 pair, hi = fp16(p s) in the low half and lo = fp16(p s - hi) in the
+// high half (s the fp16 in the low half of s16): one v_fma_mix each, the product exact
+// inside both, so hi + lo is p s to about 2^-22.
+__device__ __forceinline__ unsigned w_hilo(float p, unsigned s16) {
+  unsigned pk;
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %1, %2, -%0 op_sel_hi:[0,1,1]"
+      : "=&v"(pk)
+      : "v"(p), "v"(s16));
+  return pk;
+}
+
 __device__ __forceinline__ float row_sum(float x) {
   x += dpp<0x128>(x, x);
   x += dpp<0x124>(x, x);
@@ -673,11 +685,14 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
     for (int T = 0; T < 4; ++T) {
       const int u = 16 * T + t16;
       float s_t, z_t;
+      unsigned s16;   // the token's value scale, fp16 in the low half
       if constexpr (VQ) {
-        s_t = (float)*(const _Float16 *)(st + S::VP + 2 * u);
+        s16 = *(const unsigned short *)(st + S::VP + 2 * u);
+        s_t = (float)__builtin_bit_cast(_Float16, (unsigned short)s16);
         z_t = -0.5f * (Lv - 1) * s_t;
       } else {
-        const f16x2 pz = *(const f16x2 *)(st + S::VP + 4 * u);
+        s16 = *(const unsigned *)(st + S::VP + 4 * u);
+        const f16x2 pz = __builtin_bit_cast(f16x2, s16);
         s_t = (float)pz[0];
         z_t = (float)pz[1];
       }
@@ -689,12 +704,8 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
       for (int qd = 0; qd < NQ; ++qd) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sc[qd][T], a_sc, -m_sc[qd]));
         l_lane[qd] += p;
-        const float W = valid ? p * s_t : 0.f;
         zacc[qd] = valid ? fmaf(p, zb, zacc[qd]) : zacc[qd];
-        const _Float16 hi = (_Float16)W;
-        const _Float16 lo = (_Float16)(W - (float)hi);
-        sm.wb[w][4 * qd + g4][u] = (unsigned)__builtin_bit_cast(unsigned short, hi) |
-                                   ((unsigned)__builtin_bit_cast(unsigned short, lo) << 16);
+        sm.wb[w][4 * qd + g4][u] = w_hilo(valid ? p : 0.f, s16);
       }
     }
     __builtin_amdgcn_wave_barrier();
