@@ -313,6 +313,9 @@ def run_long_leg(args):
                       "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
         log(f"[bench] long-context decode, {splits} splits: {us:.1f} us per call ({gbs:.0f} GB/s)")
     out["bytes_per_call"] = int(nbytes)
+    out["note"] = ("splits = KV partitions requested; on the MFMA path a request above the resident decode "
+                   "waves per KV head (32 here) has each wave walk consecutive logical partitions' tokens "
+                   "instead of running extra rounds of workgroups (the same attention, coarser partials)")
     del cache
     torch.cuda.empty_cache()
     return out

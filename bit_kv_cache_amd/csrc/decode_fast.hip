@@ -1079,6 +1079,22 @@ int decode_fast_resident_waves(int G, int bits_v) {
   return c;
 }
 
+// KV partitions the split layout runs for a request of a.P: more partitions than the
+// GPU holds resident decode waves per KV head would run as several rounds of
+// workgroups, each round paying the query setup and the ring's fill again and the last
+// its tail (long context, 8 x 8 KV heads: 128 partitions 214 us, 32 partitions 167 us).
+// Then each wave takes ceil(P / P_run) consecutive logical partitions' tokens instead:
+// the same attention, in coarser split-K partials.
+int decode_fast_run_splits(const DecodeArgs &a) {
+  if (whole_layout(a)) return a.P;
+  const int r = decode_fast_resident_waves(a.G, a.bits_v);
+  const int64_t heads = (int64_t)a.B * a.Hkv;
+  if (r <= 0 || heads <= 0) return a.P;
+  int per_head = (int)(r / heads) / kSplitWaves * kSplitWaves;
+  if (per_head < kSplitWaves) per_head = kSplitWaves;
+  return a.P > per_head ? per_head : a.P;
+}
+
 hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
   const int nwg = decode_fast_partials(a);
   dim3 grid(nwg, a.B * a.Hkv);

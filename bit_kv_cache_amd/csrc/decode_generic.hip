@@ -288,6 +288,7 @@ hipError_t launch_decode(const DecodeArgs &a0, hipStream_t s) {
     a.tinvt = nullptr;
   }
   if (decode_fast_supported(a) && !a.force_generic) {
+    a.P = decode_fast_run_splits(a);   // (the workspace holds the requested count's partials)
     e = launch_decode_fast(a, s);
     if (e != hipSuccess || decode_fast_direct(a)) return e;
     nparts = decode_fast_partials(a);

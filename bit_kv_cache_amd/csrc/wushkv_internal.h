@@ -159,6 +159,7 @@ bool decode_fast_supported(const DecodeArgs &a);
 int decode_fast_partials(const DecodeArgs &a);
 bool decode_fast_direct(const DecodeArgs &a);   // the fast kernel writes out itself
 int decode_fast_resident_waves(int G, int bits_v);
+int decode_fast_run_splits(const DecodeArgs &a);   // partitions the MFMA kernel runs for a.P
 
 // Device helpers ------------------------------------------------------------
 

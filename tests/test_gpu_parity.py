@@ -66,6 +66,24 @@ def test_c4_long_context_scaled_empty_partitions():
     r.check_decode(q, qt, out)
 
 
+def test_c4_partitions_beyond_resident_waves():
+    """More KV partitions than the GPU holds resident decode waves per KV head (64 KV
+    heads ask 128): the MFMA kernel has each wave walk consecutive logical partitions'
+    tokens rather than run several rounds of workgroups, so the request equals the
+    library's own count bit for bit, and is held to the oracle on sampled heads."""
+    w = configs.LONG_CONTEXT.scaled(context=12000)
+    r = Run(w)
+    r.append(w.context)
+    r.append(1)
+    p_lib = W.decode_num_splits(r.cache, r.cache.n, w.num_q_heads, 0)
+    q, qt, out128 = r.decode(0, num_splits=128)
+    r.check_decode(q, qt, out128, heads=[(0, 0), (3, 5), (7, 7)])
+    if p_lib < 128:
+        _, _, out_lib = r.decode(0, num_splits=p_lib)
+        torch.cuda.synchronize()
+        assert torch.equal(out128, out_lib), p_lib
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_c3_bulk_flush_scaled(bits):
     w = configs.BULK_FLUSH.scaled(num_kv_heads=2, num_q_heads=8, context=4096 + 37, bits_k=bits, bits_v=bits)
