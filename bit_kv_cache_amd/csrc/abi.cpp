@@ -120,8 +120,8 @@ int32_t choose_splits(const Geom &g, int64_t nq, int32_t requested, int G) {
   if (requested > 0) return requested;
   const int64_t nsets = (nq + kSet - 1) / kSet;
   int64_t waves = 2048;
-  if (g.d == 128 && g.bits_k == 2 && (g.bits_v == 2 || g.bits_v == 3) && (G == 4 || G == 8)) {
-    const int r = decode_fast_resident_waves(G, g.bits_v);
+  if (g.d == 128 && (g.bits_k == 2 || g.bits_k == 4) && g.bits_v >= 2 && g.bits_v <= 4 && (G == 4 || G == 8)) {
+    const int r = decode_fast_resident_waves(G, g.bits_k, g.bits_v);
     if (r > 0) waves = r;
   }
   const int64_t heads = (int64_t)g.B * g.Hkv;
@@ -464,7 +464,7 @@ int decode_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t n_toke
   if (validate_only) return WUSHKV_OK;
   (void)hipGetLastError();   // clear an earlier sticky error before launching
   if (app) {
-    if (decode_fast_supported(a) && !a.force_generic) {
+    if (decode_fast_appends(a) && !a.force_generic) {
       a.append_new = 1;
       a.in_dtype = app->in_dtype;
       a.k_new = app->k_new;

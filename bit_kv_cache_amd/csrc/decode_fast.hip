@@ -1,5 +1,5 @@
-// GQA decode attention over the 2-bit key cache on MFMA (gfx950), head_dim 128,
-// G = 4 or 8 query heads per KV head, 2- or 3-bit values.
+// GQA decode attention over the quantized cache on MFMA (gfx950), head_dim 128,
+// G = 4 or 8 query heads per KV head, 2- or 4-bit keys, 2-, 3- or 4-bit values.
 //
 // What it computes is the plain softmax attention of the pages' method: scores
 // (q . k)/sqrt(d) on the FP16 sink and recent tokens and (q~ . x^)/sqrt(d) on the
@@ -58,18 +58,22 @@ __device__ __forceinline__ float dpp(float old, float src) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), CTRL, 0xF, BANK, false));
 }
 
-// Byte layout of one ring slot.  A body set: key codes (2 KB, verbatim), value codes
-// (2 KB: the first 16 bytes of each lane's 32, then the last 16), the 3-bit plane
-// (1 KB, verbatim), key then value parameters (up to 256 B each).  A window stage:
-// 8 FP16 key rows (2 KB) then 8 FP16 value rows (2 KB).
+// Byte layout of one ring slot.  A body set: key codes (64 rows verbatim: 2 KB at 2
+// bits, 4 KB at 4 bits, each row its low-bit plane then its high-bit plane), value
+// codes (2 KB: the first 16 bytes of each lane's 32, then the last 16), the values'
+// second plane (3 bits: the third-bit plane, 1 KB verbatim; 4 bits: the high two bits,
+// 2 KB laid out as the first), key then value parameters (up to 256 B each).  A window
+// stage: 8 FP16 key rows (2 KB) then 8 FP16 value rows (2 KB).
 // Both kinds are filled by exactly DMAS load-to-LDS instructions, so one vmcnt per
 // pending slot covers either.
-template <int BV>
+template <int BK, int BV>
 struct Stage {
-  static constexpr int K = 0, V = 2048, VH = 4096;
-  static constexpr int KP = BV == 3 ? 5120 : 4096, VP = KP + 256, SIZE = VP + 256;
+  static constexpr int KROW = BK == 4 ? 64 : 32;          // key row bytes
+  static constexpr int K = 0, V = 64 * KROW, VH = V + 2048;
+  static constexpr int VHB = BV == 3 ? 1024 : (BV == 4 ? 2048 : 0);
+  static constexpr int KP = VH + VHB, VP = KP + 256, SIZE = VP + 256;
   static constexpr int WK = 0, WV = 2048;
-  static constexpr int DMAS = BV == 3 ? 6 : 5;
+  static constexpr int DMAS = V / 1024 + 2 + VHB / 1024 + 1;
 };
 
 // Row pitch (dwords) of the W buffer: rows 16 banks apart, so the 64 lanes' W stores
@@ -79,7 +83,7 @@ constexpr int kWbPitch = 80;
 
 constexpr int kStages = 2;   // ring slots per wave: the item computed and kStages - 1 ahead
 
-template <int G, int BV, int NW>
+template <int G, int BK, int BV, int NW>
 struct __align__(16) FastSmem {
   unsigned qi[G][kD];             // q~ in fixed point, offset to unsigned (balanced digits)
   float q[G][kD];
@@ -89,7 +93,7 @@ struct __align__(16) FastSmem {
   float wp[NW][G][8];             // window stage: probabilities [head][token]
   float wmx[NW][16], wls[NW][16]; // window partial: max and sum per head
   union {
-    uint8_t ring[NW][kStages][Stage<BV>::SIZE];
+    uint8_t ring[NW][kStages][Stage<BK, BV>::SIZE];
     struct {
       float o[NW][2 * G][kD];     // per wave: PV rows (hi parts, then lo parts), channels
       float wo[NW][G][kD];        // window partial: weighted FP16 values [head][channel]
@@ -133,6 +137,16 @@ __device__ __forceinline__ VConst make_vconst() {
   c.mh[1] = vconst(0x00800080u); c.eh[1] = vconst(0x50005000u);   // 2^5
   c.mh[2] = vconst(0x01000100u); c.eh[2] = c.e3;                  // 2^4
   c.mh[3] = vconst(0x02000200u); c.eh[3] = vconst(0x48004800u);   // 2^3
+  return c;
+}
+
+// The same masks with every exponent two higher: the fields read as 4 BASE + 4 c, the
+// high two bits of a 4-bit value code at their weight.
+__device__ __forceinline__ VConst make_vconst_x4() {
+  VConst c = make_vconst();
+  c.e2 = vconst(0x5C005C00u);
+  c.e3 = vconst(0x54005400u);
+  c.e4 = vconst(0x4C004C00u);
   return c;
 }
 
@@ -254,22 +268,28 @@ struct SetSource {
 };
 
 // Queue the loads of body set `set` into the wave's ring slot `st` (load-to-LDS:
-// lane i's bytes land at the slot offset + i * size).  Stage<BV>::DMAS instructions.
-template <int BV>
+// lane i's bytes land at the slot offset + i * size).  Stage<BK, BV>::DMAS instructions.
+template <int BK, int BV>
 __device__ __forceinline__ void stage_set(const SetSource &src, int set, uint8_t *st) {
-  using S = Stage<BV>;
+  using S = Stage<BK, BV>;
   const int lane = threadIdx.x & 63;
   constexpr int aux = 2;   // nontemporal: streamed once
   const unsigned vo = 16u * (unsigned)lane;
-  const int ko = set * 2048, vso = set * src.vset;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K), 16, vo, ko, 0, aux);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K + 1024), 16, vo, ko + 1024, 0, aux);
+  const int ko = set * S::V, vso = set * src.vset;
+#pragma unroll
+  for (int i = 0; i < S::V / 1024; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void *)(st + S::K + 1024 * i), 16, vo, ko + 1024 * i, 0, aux);
   // value words: lane l's 32 bytes split into its first 16 (slot bytes 16 l) and last
   // 16 (1024 + 16 l), so each of the lane's two 16-byte reads is contiguous across lanes
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V), 16, 2 * vo, vso, 0, aux);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::V + 1024), 16, 2 * vo, vso + 16, 0, aux);
   if constexpr (BV == 3)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::VH), 16, vo, vso + 2048, 0, aux);
+  if constexpr (BV == 4) {   // the high two bits, laid out as the low ones
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::VH), 16, 2 * vo, vso + 2048, 0, aux);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void *)(st + S::VH + 1024), 16, 2 * vo, vso + 2048 + 16, 0,
+                                             aux);
+  }
   // parameters, one instruction: lanes 0-15 the keys', 16-31 the values' (64 tokens x
   // 2 or 4 bytes each; lane 0 is always active, so the instruction always issues)
   if (src.pact)
@@ -286,11 +306,11 @@ __device__ __forceinline__ int window_row(int t, int ns, unsigned first_slot, un
 // 8 value rows of 256 bytes (lanes past cnt re-read token t0, so every instruction
 // issues with all lanes), plus DMAS - 4 single-lane filler loads into the slot's
 // unused parameter area so a window slot counts like a body slot.
-template <int BV>
+template <int BK, int BV>
 __device__ __forceinline__ void stage_window(const uint8_t *sinkk, const uint8_t *sinkv, const uint8_t *ringk,
                                              const uint8_t *ringv, int t0, int cnt, int ns, unsigned first_slot,
                                              unsigned rsz, const void *filler, uint8_t *st) {
-  using S = Stage<BV>;
+  using S = Stage<BK, BV>;
   const int lane = threadIdx.x & 63;
   constexpr int aux = 2;
 #pragma unroll
@@ -307,9 +327,9 @@ __device__ __forceinline__ void stage_window(const uint8_t *sinkk, const uint8_t
 }
 
 // Wait until at most `pending` (< kStages) staged items' loads are still in flight.
-template <int BV>
+template <int BK, int BV>
 __device__ __forceinline__ void wait_staged(int pending) {
-  constexpr int D = Stage<BV>::DMAS;
+  constexpr int D = Stage<BK, BV>::DMAS;
   static_assert(kStages >= 2 && kStages <= 4, "ring depth");
   if (pending <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   else if (kStages == 2 || pending == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D) : "memory");
@@ -317,8 +337,8 @@ __device__ __forceinline__ void wait_staged(int pending) {
   else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * D) : "memory");
 }
 
-template <int G, int BV, int NW>
-__device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
+template <int G, int BK, int BV, int NW>
+__device__ void window_stage(FastSmem<G, BK, BV, NW> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
                              float (&wl)[G], float (&wacc)[G][2]);
 
 // The workgroup's query setup: q and q~ of its G heads into LDS, per head the exponent
@@ -327,8 +347,8 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
 // points": one d x d product per query), in the query transform kernel's arithmetic:
 // row i of T^{-T} per thread, four interleaved fp32 partial sums, so q~ is bit-identical
 // to that kernel's; the partition-0 workgroup writes it to a.qt_out.
-template <int G, int BV, int NW>
-__device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int b, int h0) {
+template <int G, int BK, int BV, int NW>
+__device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BK, BV, NW> &sm, int b, int h0) {
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x;
   const bool fused = a.tinvt != nullptr;
@@ -411,8 +431,8 @@ __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int 
 // heads h + 4 qd (qd < G / 4).  PV output row r (O lane l holds rows 4 (l / 16) + i,
 // channels 16 ct + l % 16) is head r's hi part for r < G and head r - G's lo part for
 // G <= r < 2 G; the two are summed in the workgroup merge.
-template <int G, int BV, int NW, bool PAGED, bool APPEND>
-__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
+template <int G, int BK, int BV, int NW, bool PAGED, bool APPEND>
+__device__ void body_wave(const DecodeArgs &a, FastSmem<G, BK, BV, NW> &sm, int bg, int64_t s0, int64_t s1, int ws0, int ws1,
                           f32x4 (&O)[8], float (&m_out)[G / 4], float (&l_out)[G / 4], float (&z_out)[G / 4],
                           float (&wm_out)[G], float (&wl_out)[G], float (&wacc_out)[G][2]) {
   constexpr int NQ = G / 4;            // head quads: QK MFMAs per tile
@@ -448,7 +468,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
     src.vset = (int)a.vset_bytes;
   }
   uint8_t *ring = &sm.u.ring[w][0][0];
-  constexpr int SB = Stage<BV>::SIZE;
+  constexpr int SB = Stage<BK, BV>::SIZE;
   // items of this wave: 8-token window stages ws0 .. ws1-1, then body sets s0 .. s1-1
   const int nb = (int)(s1 - s0), nitems = nb + (ws1 - ws0);
   const int ns = (int)(sl.n < a.S ? sl.n : a.S);
@@ -491,10 +511,10 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   };
   auto issue = [&](int item, uint8_t *dst) {
     if (item >= nwin) {
-      stage_set<BV>(src, slot_of((int)s0 + item - nwin), dst);
+      stage_set<BK, BV>(src, slot_of((int)s0 + item - nwin), dst);
     } else {
       const int t0 = 8 * (ws0 + item);
-      stage_window<BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
+      stage_window<BK, BV>(sinkk, sinkv, ringk, ringv, t0, nw - t0 < 8 ? nw - t0 : 8, ns, first_slot, rsz, a.qt, dst);
     }
   };
   // prologue: the first kStages items fill the ring (item k lives in slot k % kStages),
@@ -553,12 +573,14 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
 #pragma unroll
   for (int qd = 0; qd < NQ; ++qd) b_sc[qd] = 0.5f * sm.sq[4 * qd + g4];
   const VConst vc = make_vconst();
+  VConst vc4;
+  if constexpr (BV == 4) vc4 = make_vconst_x4();
   // BASE of the value operand for token 16 T + t16: pair 2 T + (t16 & 3) / 2 of its word
   float vbase[4];
 #pragma unroll
   for (int T = 0; T < 4; ++T) {
     const int k = 2 * T + ((t16 & 3) >> 1);
-    vbase[T] = vbase2(k) + (BV == 3 ? (float)(64 >> (k & 3)) : 0.0f);
+    vbase[T] = BV == 4 ? 5.0f * vbase2(k) : vbase2(k) + (BV == 3 ? (float)(64 >> (k & 3)) : 0.0f);
   }
   // PV A rows: row r < G is head r's W hi part, G <= r < 2 G head r - G's lo part (the
   // two halves of one word of the W buffer), zeros past 2 G
@@ -572,7 +594,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
     const int ahead = it + kStages - 1;   // queued by the prologue when it == 0
     if (it > 0 && ahead < nitems) issue(ahead, ring + (ahead % kStages) * SB);
     const int pending = nitems - 1 - it < kStages - 1 ? nitems - 1 - it : kStages - 1;
-    wait_staged<BV>(pending);
+    wait_staged<BK, BV>(pending);
     return ring + (it % kStages) * SB;
   };
 
@@ -591,22 +613,30 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
                     float (&mxr)[NQ]) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr bool KQ = decltype(kq_tag)::value;
-    using S = Stage<BV>;
+    using S = Stage<BK, BV>;
     const int64_t base = set * kSet;
 
     // ---- QK: one scaled MFMA per (tile, head quad); the lane's 4 result rows are the
     // digits of its head, already weighted
 #pragma unroll
     for (int T = 0; T < 4; ++T) {
-      const i32x8 bk = key_fp4(*(const u32x2 *)(st + S::K + (16 * T + t16) * 32 + 8 * g4));
+      const uint8_t *kr = st + S::K + (16 * T + t16) * S::KROW + 8 * g4;
+      const i32x8 bk = key_fp4(*(const u32x2 *)kr);
+      // 4-bit keys: the row's second plane holds the high two bits, c = lo + 4 hi; its
+      // products enter the same accumulation with B scaled by 4 (E8M0 129)
+      i32x8 bh;
+      if constexpr (BK == 4) bh = key_fp4(*(const u32x2 *)(kr + 32));
       // per head quad: digits 4-7 accumulate onto the rows of digits 0-3
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
-        const f32x4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bk, (f32x4){0.f, 0.f, 0.f, 0.f},
-                                                                          4, 4, 0, sa[2 * qd], 0, 127);
-        const f32x4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bk, d0, 4, 4, 0,
-                                                                          sa[2 * qd + 1], 0, 127);
-        sc[qd][T] = (d1[3] + d1[2]) + (d1[1] + d1[0]);
+        f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bk, (f32x4){0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                                   0, sa[2 * qd], 0, 127);
+        d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bk, d, 4, 4, 0, sa[2 * qd + 1], 0, 127);
+        if constexpr (BK == 4) {
+          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bh, d, 4, 4, 0, sa[2 * qd], 0, 129);
+          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bh, d, 4, 4, 0, sa[2 * qd + 1], 0, 129);
+        }
+        sc[qd][T] = (d[3] + d[2]) + (d[1] + d[0]);
       }
     }
     // ---- scores and online softmax (base 2)
@@ -619,7 +649,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
       float s_t, z_t;
       if constexpr (KQ) {
         s_t = (float)*(const _Float16 *)(st + S::KP + 2 * u);
-        z_t = -1.5f * s_t;
+        z_t = -0.5f * (float)((1 << BK) - 1) * s_t;
       } else {
         const f16x2 pz = *(const f16x2 *)(st + S::KP + 4 * u);
         s_t = (float)pz[0];
@@ -675,7 +705,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
   auto phase2 = [&](auto full_tag, auto vq_tag, int64_t set, const uint8_t *st, const float (&sc)[NQ][4]) {
     constexpr bool FULL = decltype(full_tag)::value;
     constexpr bool VQ = decltype(vq_tag)::value;
-    using S = Stage<BV>;
+    using S = Stage<BK, BV>;
     const int64_t base = set * kSet;
     // ---- p, W = p s_V as fp16 hi + lo into the wave's W buffer, zero term
     float m_sc[NQ];
@@ -724,6 +754,12 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
       for (int ct = 0; ct < 8; ++ct)
         hx[ct] = __builtin_amdgcn_perm(0u, vh[ct >> 1], (ct & 1) ? 0x0C030C02u : 0x0C010C00u);
     }
+    if constexpr (BV == 4) {   // the high two bits' words, laid out as the low ones'
+      const u32x4 h0 = *(const u32x4 *)(st + S::VH + 16 * lane);
+      const u32x4 h1 = *(const u32x4 *)(st + S::VH + 1024 + 16 * lane);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) { hx[c] = h0[c]; hx[4 + c] = h1[c]; }
+    }
 #pragma unroll
     for (int iota = 0; iota < 2; ++iota) {
       const u32x4 x0 = *(const u32x4 *)(arow + 16 * (2 * iota) + 4 * g4);
@@ -741,6 +777,13 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
         if constexpr (BV == 3) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) Bv[c] = v_operand_hi(hx[ct0 + c], iota, vc);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aw, Bv[c], O[ct0 + c], 0, 0, 0);
+        }
+        if constexpr (BV == 4) {   // 4 BASE + 4 h on the same A
+#pragma unroll
+          for (int c = 0; c < 4; ++c) Bv[c] = v_operand2(hx[ct0 + c], iota, vc4);
 #pragma unroll
           for (int c = 0; c < 4; ++c)
             O[ct0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Aw, Bv[c], O[ct0 + c], 0, 0, 0);
@@ -781,11 +824,11 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
     if (appender && it == nwin - 1) {
       // the new token is row nw - 1 - t0 of the last stage (key rows at WK, values at WV)
       if (lane < 32)
-        *(f16x8 *)(const_cast<uint8_t *>(st) + (lane < 16 ? Stage<BV>::WK : Stage<BV>::WV) +
+        *(f16x8 *)(const_cast<uint8_t *>(st) + (lane < 16 ? Stage<BK, BV>::WK : Stage<BK, BV>::WV) +
                    256 * (nw - 1 - t0) + 16 * (lane & 15)) = row_new;
       __builtin_amdgcn_wave_barrier();
     }
-    window_stage<G, BV, NW>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
+    window_stage<G, BK, BV, NW>(sm, st, nw - t0 < 8 ? nw - t0 : 8, w, wm, wl, wacc);
   }
   using Yes = std::true_type;
   using No = std::false_type;
@@ -817,10 +860,10 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BV, NW> &sm, int bg, 
 // 8 lanes per token, 16 channels each, summed over the 8 with DPP; values: lane = two
 // channels.  The stage folds into this wave's window partial: per head the running
 // max and sum (the same in every lane) and this lane's two weighted value channels.
-template <int G, int BV, int NW>
-__device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
+template <int G, int BK, int BV, int NW>
+__device__ void window_stage(FastSmem<G, BK, BV, NW> &sm, const uint8_t *st, int cnt, int w, float (&wm)[G],
                              float (&wl)[G], float (&wacc)[G][2]) {
-  using S = Stage<BV>;
+  using S = Stage<BK, BV>;
   const int lane = threadIdx.x & 63;
   const int j = lane >> 3, cc = lane & 7;   // token of the stage, 16-channel chunk
   const float qk_scale = kLog2e * 0.08838834764831845f;
@@ -897,10 +940,10 @@ __device__ void window_stage(FastSmem<G, BV, NW> &sm, const uint8_t *st, int cnt
 }
 
 // nwg_body workgroups per KV head; with one, the workgroup's merge is the output.
-template <int G, int BV, int NW, bool PAGED, bool APPEND>
+template <int G, int BK, int BV, int NW, bool PAGED, bool APPEND>
 __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int nwg_body) {
   constexpr int NT = 64 * NW;
-  __shared__ FastSmem<G, BV, NW> sm;
+  __shared__ FastSmem<G, BK, BV, NW> sm;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int bg = blockIdx.y;
@@ -939,7 +982,7 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
       s1 = nsets * (part + 1) / a.P;
     }
   }
-  body_wave<G, BV, NW, PAGED, APPEND>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
+  body_wave<G, BK, BV, NW, PAGED, APPEND>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
   __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -1029,13 +1072,20 @@ bool decode_fast_supported(const DecodeArgs &a) {
         rows * 2 * a.vpar_n >= lim)
       return false;
   }
-  return a.d == 128 && a.bits_k == 2 && (a.bits_v == 2 || a.bits_v == 3) && (a.G == 4 || a.G == 8) &&
+  return a.d == 128 && (a.bits_k == 2 || a.bits_k == 4) && a.bits_v >= 2 && a.bits_v <= 4 && (a.G == 4 || a.G == 8) &&
          a.kcode_bytes < lim && a.vcode_bytes < lim && a.kpar_bytes < lim && a.vpar_bytes < lim;
 }
 
+// The decode-step form (the new token's append fused into the decode) exists for 2-bit
+// keys and 2- or 3-bit values; the wider codes' decode runs after a separate append.
+bool decode_fast_appends(const DecodeArgs &a) {
+  return decode_fast_supported(a) && a.bits_k == 2 && a.bits_v <= 3 && !a.pg.table;
+}
+
 // Launch shape: one kWholeWaves-wave workgroup per KV head when the split count equals
-// it and there are at least as many KV heads as compute units (G = 4, whose LDS fits),
-// else ceil(P / kSplitWaves) workgroups of kSplitWaves waves per KV head.
+// it and there are at least as many KV heads as compute units (G = 4 with 2-bit keys and
+// 2- or 3-bit values, whose LDS fits), else ceil(P / kSplitWaves) workgroups of
+// kSplitWaves waves per KV head.
 static int cu_count() {
   static int c = -1;
   if (c < 0) {
@@ -1051,7 +1101,7 @@ static int cu_count() {
 }
 
 static bool whole_layout(const DecodeArgs &a) {
-  return a.G == 4 && a.P == kWholeWaves && a.B * a.Hkv >= cu_count();
+  return a.G == 4 && a.bits_k == 2 && a.bits_v <= 3 && a.P == kWholeWaves && a.B * a.Hkv >= cu_count();
 }
 
 int decode_fast_partials(const DecodeArgs &a) {
@@ -1060,18 +1110,27 @@ int decode_fast_partials(const DecodeArgs &a) {
 
 bool decode_fast_direct(const DecodeArgs &a) { return decode_fast_partials(a) == 1; }
 
-// Waves of the MFMA decode the GPU holds at once for (G, bits_v) in the split layout;
-// 0 if unknown.
-int decode_fast_resident_waves(int G, int bits_v) {
-  static int cache[2][2] = {{-1, -1}, {-1, -1}};
-  int &c = cache[G == 8][bits_v == 3];
+// The split layout's plain kernel of (G, bits_k, bits_v).
+static const void *split_kernel(int G, int bits_k, int bits_v) {
+#define WUSHKV_K(G_, BK_, BV_) (const void *)decode_fast_kernel<G_, BK_, BV_, kSplitWaves, false, false>
+  if (G == 4) {
+    if (bits_k == 2) return bits_v == 2 ? WUSHKV_K(4, 2, 2) : bits_v == 3 ? WUSHKV_K(4, 2, 3) : WUSHKV_K(4, 2, 4);
+    return bits_v == 2 ? WUSHKV_K(4, 4, 2) : bits_v == 3 ? WUSHKV_K(4, 4, 3) : WUSHKV_K(4, 4, 4);
+  }
+  if (bits_k == 2) return bits_v == 2 ? WUSHKV_K(8, 2, 2) : bits_v == 3 ? WUSHKV_K(8, 2, 3) : WUSHKV_K(8, 2, 4);
+  return bits_v == 2 ? WUSHKV_K(8, 4, 2) : bits_v == 3 ? WUSHKV_K(8, 4, 3) : WUSHKV_K(8, 4, 4);
+#undef WUSHKV_K
+}
+
+// Waves of the MFMA decode the GPU holds at once for (G, bits_k, bits_v) in the split
+// layout; 0 if unknown.
+int decode_fast_resident_waves(int G, int bits_k, int bits_v) {
+  static int cache[2][2][3] = {{{-1, -1, -1}, {-1, -1, -1}}, {{-1, -1, -1}, {-1, -1, -1}}};
+  int &c = cache[G == 8][bits_k == 4][bits_v - 2];
   if (c >= 0) return c;
-  const void *fn = (G == 4) ? (bits_v == 2 ? (const void *)decode_fast_kernel<4, 2, kSplitWaves, false, false>
-                                           : (const void *)decode_fast_kernel<4, 3, kSplitWaves, false, false>)
-                            : (bits_v == 2 ? (const void *)decode_fast_kernel<8, 2, kSplitWaves, false, false>
-                                           : (const void *)decode_fast_kernel<8, 3, kSplitWaves, false, false>);
   int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64 * kSplitWaves, 0) != hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, split_kernel(G, bits_k, bits_v), 64 * kSplitWaves, 0) !=
+      hipSuccess) {
     hipGetLastError();
     return 0;
   }
@@ -1087,7 +1146,7 @@ int decode_fast_resident_waves(int G, int bits_v) {
 // the same attention, in coarser split-K partials.
 int decode_fast_run_splits(const DecodeArgs &a) {
   if (whole_layout(a)) return a.P;
-  const int r = decode_fast_resident_waves(a.G, a.bits_v);
+  const int r = decode_fast_resident_waves(a.G, a.bits_k, a.bits_v);
   const int64_t heads = (int64_t)a.B * a.Hkv;
   if (r <= 0 || heads <= 0) return a.P;
   int per_head = (int)(r / heads) / kSplitWaves * kSplitWaves;
@@ -1099,19 +1158,39 @@ hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
   const int nwg = decode_fast_partials(a);
   dim3 grid(nwg, a.B * a.Hkv);
   const bool pg = a.pg.table != nullptr;
-  // (the fused append serves the unpaged one-token step only)
-#define WUSHKV_FAST(G, BV, NW)                                                                                   \
-  if (a.append_new) hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, false, true>), grid, dim3(64 * NW), 0, s, a, \
-                                       nwg);                                                                     \
-  else if (pg) hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, true, false>), grid, dim3(64 * NW), 0, s, a, nwg); \
-  else hipLaunchKernelGGL((decode_fast_kernel<G, BV, NW, false, false>), grid, dim3(64 * NW), 0, s, a, nwg)
+  // (the fused append serves the unpaged one-token step of 2-bit keys and 2- or 3-bit
+  // values only: decode_fast_appends)
+#define WUSHKV_FAST(G, BK, BV, NW)                                                                                     \
+  if (a.append_new) hipLaunchKernelGGL((decode_fast_kernel<G, BK, BV, NW, false, true>), grid, dim3(64 * NW), 0, s, a, \
+                                       nwg);                                                                           \
+  else if (pg) hipLaunchKernelGGL((decode_fast_kernel<G, BK, BV, NW, true, false>), grid, dim3(64 * NW), 0, s, a, nwg); \
+  else hipLaunchKernelGGL((decode_fast_kernel<G, BK, BV, NW, false, false>), grid, dim3(64 * NW), 0, s, a, nwg)
+#define WUSHKV_FAST_NA(G, BK, BV)                                                                                      \
+  if (pg) hipLaunchKernelGGL((decode_fast_kernel<G, BK, BV, kSplitWaves, true, false>), grid, dim3(64 * kSplitWaves), 0, \
+                             s, a, nwg);                                                                              \
+  else hipLaunchKernelGGL((decode_fast_kernel<G, BK, BV, kSplitWaves, false, false>), grid, dim3(64 * kSplitWaves), 0, s, \
+                          a, nwg)
+  if (a.append_new && !decode_fast_appends(a)) return hipErrorInvalidValue;
   if (whole_layout(a)) {
-    if (a.bits_v == 2) { WUSHKV_FAST(4, 2, kWholeWaves); }
-    else { WUSHKV_FAST(4, 3, kWholeWaves); }
-  } else if (a.G == 4 && a.bits_v == 2) { WUSHKV_FAST(4, 2, kSplitWaves); }
-  else if (a.G == 4) { WUSHKV_FAST(4, 3, kSplitWaves); }
-  else if (a.bits_v == 2) { WUSHKV_FAST(8, 2, kSplitWaves); }
-  else { WUSHKV_FAST(8, 3, kSplitWaves); }
+    if (a.bits_v == 2) { WUSHKV_FAST(4, 2, 2, kWholeWaves); }
+    else { WUSHKV_FAST(4, 2, 3, kWholeWaves); }
+  } else if (a.bits_k == 2 && a.bits_v <= 3) {
+    if (a.G == 4 && a.bits_v == 2) { WUSHKV_FAST(4, 2, 2, kSplitWaves); }
+    else if (a.G == 4) { WUSHKV_FAST(4, 2, 3, kSplitWaves); }
+    else if (a.bits_v == 2) { WUSHKV_FAST(8, 2, 2, kSplitWaves); }
+    else { WUSHKV_FAST(8, 2, 3, kSplitWaves); }
+  } else if (a.G == 4) {
+    if (a.bits_k == 2) { WUSHKV_FAST_NA(4, 2, 4); }
+    else if (a.bits_v == 2) { WUSHKV_FAST_NA(4, 4, 2); }
+    else if (a.bits_v == 3) { WUSHKV_FAST_NA(4, 4, 3); }
+    else { WUSHKV_FAST_NA(4, 4, 4); }
+  } else {
+    if (a.bits_k == 2) { WUSHKV_FAST_NA(8, 2, 4); }
+    else if (a.bits_v == 2) { WUSHKV_FAST_NA(8, 4, 2); }
+    else if (a.bits_v == 3) { WUSHKV_FAST_NA(8, 4, 3); }
+    else { WUSHKV_FAST_NA(8, 4, 4); }
+  }
+#undef WUSHKV_FAST_NA
 #undef WUSHKV_FAST
   return hipGetLastError();
 }

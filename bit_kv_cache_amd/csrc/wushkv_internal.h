@@ -158,7 +158,8 @@ hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s);
 bool decode_fast_supported(const DecodeArgs &a);
 int decode_fast_partials(const DecodeArgs &a);
 bool decode_fast_direct(const DecodeArgs &a);   // the fast kernel writes out itself
-int decode_fast_resident_waves(int G, int bits_v);
+int decode_fast_resident_waves(int G, int bits_k, int bits_v);
+bool decode_fast_appends(const DecodeArgs &a);   // the decode-step form with the append fused
 int decode_fast_run_splits(const DecodeArgs &a);   // partitions the MFMA kernel runs for a.P
 
 // Device helpers ------------------------------------------------------------

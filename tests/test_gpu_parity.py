@@ -255,6 +255,42 @@ def test_fast_decode_matches_generic_kernel(wl, P):
     r.check_decode(q, qt, fast)
 
 
+WIDE = [
+    # bits_k, bits_v, quant_k, quant_v, G
+    (4, 2, "quest", "quest", 4),
+    (2, 4, "affine", "affine", 4),
+    (4, 4, "quest", "quest", 4),
+    (4, 3, "affine", "affine", 8),
+    (4, 4, "affine", "quest", 8),
+    (2, 4, "quest", "affine", 8),
+]
+
+
+@pytest.mark.parametrize("bits_k,bits_v,quant_k,quant_v,G", WIDE)
+def test_wide_codes_mfma_decode(bits_k, bits_v, quant_k, quant_v, G):
+    """4-bit keys (two 2-bit planes on the same q~ digits, the high plane's products
+    scaled by 4) and 4-bit values (a second B operand on the same W at four times the
+    weight) on the MFMA decode: held to the oracle, and to the generic kernel on the same
+    cache, with a ragged last set and several splits."""
+    qk = configs.QUEST if quant_k == "quest" else configs.AFFINE
+    qv = configs.QUEST if quant_v == "quest" else configs.AFFINE
+    w = configs.SERVING.scaled(name=f"wide{bits_k}{bits_v}{G}", seed=40 + bits_k + 3 * bits_v + G, batch=3,
+                               context=3000 + 37, num_q_heads=8 * G, num_kv_heads=8, bits_k=bits_k, bits_v=bits_v,
+                               quant_k=qk, quant_v=qv)
+    r = Run(w)
+    r.append(w.context)
+    r.check_cache(heads=[(0, 0), (2, 7)])
+    r.append(1)
+    for P in (0, 8):
+        q, qt, fast = r.decode(0, num_splits=P)
+        gen_out, _ = W.decode_attention_generic(r.cache, q, q_t=qt, num_splits=P if P else 8)
+        torch.cuda.synchronize()
+        rel = float((fast - gen_out).norm() / gen_out.norm())
+        say(f"[wide {bits_k}/{bits_v} {quant_k}/{quant_v} G={G} P={P}] fast vs generic rel-L2 {rel:.3e}")
+        assert rel < 1e-4
+        r.check_decode(q, qt, fast, heads=[(0, 0), (1, 3), (2, 7)])
+
+
 @pytest.mark.parametrize("bits_v", [2, 3])
 def test_whole_workgroup_layout_matches_generic(bits_v):
     """At the serving batch (256 (batch row, KV head) pairs) with 12 splits (the
