@@ -902,7 +902,7 @@ def main():
     tl = {} if args.no_transforms else run_transform_leg(args)
     pl = {} if args.no_paged else run_paged_leg(args)
     achieved = dl["kern_bytes"] / (dl["kern_ms"] * 1e-3) / 1e9
-    traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 12, false, true>"])
+    traffic = traffic_from_profile("decode_batched_serving_counters.json", ["decode_fast_kernel<4, 2, 2, 12, false, true>"])
     value = dl["bytes"] / (dl["ms_step"] * 1e-3) / 1e9
     line = {
         "metric": "2-bit GQA decode-attention HBM GB/s (% of peak); flush tokens/s",
@@ -934,7 +934,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_fast_kernel<4,2,12>: GQA decode with the query transform in its "
+                     "kernel": "decode_fast_kernel<4,2,2,12>: GQA decode with the query transform in its "
                                "prologue and the new token's append fused, one 12-wave workgroup per KV head "
                                "(12 splits, merged in LDS); duration from the steps with no flush due",
                      "bytes_per_launch": int(dl["kern_bytes"]), "us_per_launch": round(dl["kern_ms"] * 1e3, 2)},
