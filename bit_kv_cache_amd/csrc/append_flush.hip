@@ -138,8 +138,16 @@ struct __align__(16) FlushSmem {
   static constexpr int KP = D + 16;     // key-code row pitch (bytes; rows stay 16-byte aligned)
   static constexpr int VP = kSet + 4;   // value-code row pitch (bytes), one row per channel
   _Float16 t[D][TP];
-  uint8_t kc[kStepTok][KP];
-  uint8_t vc[2][D][VP];
+  union {
+    struct {   // codes as bytes (3- and 4-bit widths)
+      uint8_t kc[kStepTok][KP];
+      uint8_t vc[2][D][VP];
+    };
+    struct {   // 2-bit K and V: packed key rows and, per set and 16-token quarter, set words
+      unsigned kp[kStepTok][D / 16];
+      unsigned vw[2][4][4 * D];
+    };
+  };
   unsigned krow[D / 2];                 // one key row's fp16 pairs (exact re-decisions)
   double red[4][2 * kMaxOrderStats];    // per wave: partial sums / order statistics of that row
   double cand[kMaxCand];                // affine: exact values of the row's candidates
@@ -254,16 +262,16 @@ __device__ __forceinline__ void seg_float(const RawSeg<ES, CPL> &s, bool ring, i
       x[2 * i] = f16_lo(w);
       x[2 * i + 1] = f16_hi(w);
     }
-  } else if (ES == 2) {
+  } else {
+    // one round-to-nearest-even conversion per pair, then the fp16 values as floats
 #pragma unroll
     for (int i = 0; i < CPL / 2; ++i) {
-      const unsigned w = raw_word(s, i);
-      x[2 * i] = f16_round(bf16_lo(w));
-      x[2 * i + 1] = f16_round(bf16_hi(w));
+      unsigned h = ES == 2 ? pack_f16(bf16_lo(raw_word(s, i)), bf16_hi(raw_word(s, i)))
+                           : pack_f16(__uint_as_float(raw_word(s, 2 * i)), __uint_as_float(raw_word(s, 2 * i + 1)));
+      asm("" : "+v"(h));   // keep the paired conversion (not one per element)
+      x[2 * i] = f16_lo(h);
+      x[2 * i + 1] = f16_hi(h);
     }
-  } else {
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) x[i] = f16_round(__uint_as_float(raw_word(s, i)));
   }
 }
 
@@ -518,6 +526,27 @@ __device__ __forceinline__ unsigned quad_transpose(unsigned x, unsigned selA, un
   return __builtin_amdgcn_perm(quad_xor1(x), x, selB);
 }
 
+// 4 x 4 byte transpose across the lane groups q = lane / 16 of a token: lane q holds
+// byte q of each of four dwords X_0..X_3 (its bytes 0..3 from X_0..X_3 of its own row
+// position) in, and X_q's byte q' from lane q' out.  Two exchanges through gfx950's
+// permlane swaps (16-bit halves with lane ^32, bytes with lane ^16), each of which hands
+// a lane both values of its pair: (lower lane's x, upper lane's x).
+__device__ __forceinline__ unsigned qgroup_transpose(unsigned x, int q) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const unsigned z = __builtin_amdgcn_perm(r[1], r[0], q < 2 ? 0x05040100u : 0x07060302u);
+  const auto t = __builtin_amdgcn_permlane16_swap(z, z, false, false);
+  return __builtin_amdgcn_perm(t[1], t[0], (q & 1) ? 0x07030501u : 0x06020400u);
+}
+
+// A 2-bit V set word's fields from one 16-token quarter, unshifted: a dword of 4 tokens'
+// codes (bytes e = 0..3 of one channel, each 0..3) -> e0 at bits 0-1, e2 at 2-3, e1 at
+// 16-17, e3 at 18-19 (the quarter's place in the word is a shift by 4 per quarter).
+__device__ __forceinline__ unsigned vquarter2(unsigned x) {
+  const unsigned hi = __builtin_amdgcn_perm(x, x, 0x0C030C02u);   // [e2, 0, e3, 0]
+  const unsigned lo = __builtin_amdgcn_perm(x, x, 0x0C010C00u);   // [e0, 0, e1, 0]
+  return (hi << 2) + lo;
+}
+
 // V set word fields from a dword of 4 tokens' codes (bytes e = 0..3 of one channel):
 // low 2 bits of e at bit 4*(e>>1)... i.e. e0 -> 0, e2 -> 2, e1 -> 16, e3 -> 18.
 __device__ __forceinline__ unsigned vfield2(unsigned x) {
@@ -548,7 +577,11 @@ __device__ __forceinline__ unsigned kpack1(unsigned x) {
 // HAD: the key transform is T_K = a.had * H (Sylvester-Hadamard, H[j][i] = (-1)^popcount(i & j)),
 // formed by butterflies in registers instead of the contraction; T_K itself is generated
 // in LDS for the exact re-decisions.
-template <int D, int ES, int NL, bool PAGED, bool HAD>
+// B2: 2-bit keys and values.  A lane packs its key codes in registers (four to a byte)
+// and the token's four lanes exchange bytes into row order; value codes go to LDS as
+// set-word fields of their 16-token quarter.  Otherwise codes go to LDS as bytes and
+// the step's packing reads them back.
+template <int D, int ES, int NL, bool PAGED, bool HAD, bool B2>
 __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int steps_per_wg) {
   constexpr int CPL = D / 4, KS = D / 32, NCT = D / 16;
   // word of the LDS key row (channel order) holding this lane's key word w
@@ -650,7 +683,9 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       const int64_t u = ubase + 16 * tt + tok;
       const bool vt = tok_valid(u);
       unsigned kh[CPL / 2];
-      seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
+      // rows of earlier calls (fp16, from the ring) in the tile: rare outside decode steps
+      if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
+      else seg_half2<ES, CPL>(rk[tt], false, a.in_dtype, kh);   // (invalid rows are zeros either way)
       if (st + 1 < st1) load_k(st + 1, tt);
       f32x4 acc[NCT];
       if constexpr (HAD) {
@@ -783,17 +818,25 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         }
         const Quant<QU> qk = make_quant<QU>(sc, zp, Lk, kEdgeK * (float)Lk * (1.0f / 16.0f));
         float e[NCT];   // per group of 4 elements, so a recheck visits only the near groups
+        // B2: byte ct % 4 of word ct / 4 packs out channels 16 ct + 4 q .. 16 ct + 4 q + 3
+        unsigned kpk[B2 ? NCT / 4 : 1];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           float c0, c1, c2, c3;
           e[ct] = 1.0f;
           code2(qk, acc[ct][0], acc[ct][1], e[ct], c0, c1);
           code2(qk, acc[ct][2], acc[ct][3], e[ct], c2, c3);
-          unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(c0, 0, 0u);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(c1, 1, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(c2, 2, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(c3, 3, w);
-          *(unsigned *)&sm.kc[row][16 * ct + 4 * q] = w;
+          if constexpr (B2) {
+            // four 2-bit codes as one byte, exact in fp32
+            const float byte = fmaf(fmaf(fmaf(c3, 4.f, c2), 4.f, c1), 4.f, c0);
+            kpk[ct >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(byte, ct & 3, (ct & 3) ? kpk[ct >> 2] : 0u);
+          } else {
+            unsigned w = __builtin_amdgcn_cvt_pk_u8_f32(c0, 0, 0u);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(c1, 1, w);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(c2, 2, w);
+            w = __builtin_amdgcn_cvt_pk_u8_f32(c3, 3, w);
+            *(unsigned *)&sm.kc[row][16 * ct + 4 * q] = w;
+          }
         }
         // elements near a boundary: the 4 lanes of a token take one candidate at a
         // time, each summing its CPL channels' exact products in fp64
@@ -829,10 +872,23 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
             if (qs == q) {
-              sm.kc[row][j] = (uint8_t)exact_code(part, sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lk);
+              const int code = exact_code(part, sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lk);
+              if constexpr (B2) {
+                const int sh = 8 * ((bit >> 2) & 3) + 2 * (bit & 3);
+#pragma unroll
+                for (int kk = 0; kk < NCT / 4; ++kk)
+                  if (kk == bit >> 4) kpk[kk] = (kpk[kk] & ~(3u << sh)) | ((unsigned)code << sh);
+              } else {
+                sm.kc[row][j] = (uint8_t)code;
+              }
               m &= ~(1u << bit);
             }
           }
+        }
+        if constexpr (B2) {
+          // lane q now writes words q, q + 4, ... of the token's packed row
+#pragma unroll
+          for (int kk = 0; kk < NCT / 4; ++kk) sm.kp[row][4 * kk + q] = qgroup_transpose(kpk[kk], q);
         }
       };
       if (a.quant_k == WUSHKV_Q_QUEST) key_tile(QuestTag{});
@@ -845,7 +901,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       const int64_t u = ubase + 16 * tt + tok;
       const bool vt = tok_valid(u);
       float xv[CPL];
-      seg_float<ES, CPL>(rv[tt], tok_ring(u), a.in_dtype, xv);
+      if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_float<ES, CPL>(rv[tt], tok_ring(u), a.in_dtype, xv);
+      else seg_float<ES, CPL>(rv[tt], false, a.in_dtype, xv);
       if (st + 1 < st1) load_v(st + 1, tt);
       const int s2 = wave >> 1;                       // set of this wave within the step
       const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
@@ -913,7 +970,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           w = __builtin_amdgcn_cvt_pk_u8_f32(c3, 3, w);
           // lane tok = 4c + e now gets channel 4*g4 + e of tokens 4c .. 4c+3
           w = quad_transpose(w, selA, selB);
-          *(unsigned *)&sm.vc[s2][seg_chan(q, 4 * g4 + (tok & 3))][col + 4 * (tok >> 2)] = w;
+          if constexpr (B2) {
+            // the fields of set word (16 c + j % 16, j / 16) from this quarter
+            const int j = seg_chan(q, 4 * g4 + (tok & 3));
+            sm.vw[s2][col >> 4][(16 * (tok >> 2) + (j & 15)) * (D / 16) + (j >> 4)] = vquarter2(w);
+          } else {
+            *(unsigned *)&sm.vc[s2][seg_chan(q, 4 * g4 + (tok & 3))][col + 4 * (tok >> 2)] = w;
+          }
         }
         float emin = e[0];
 #pragma unroll
@@ -934,8 +997,18 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           while (m != 0) {
             const int k = __builtin_ctz(m);
             m &= m - 1;
-            sm.vc[s2][seg_chan(q, k)][col + tok] =
-                (uint8_t)exact_code((double)pick<CPL>(xv, k), sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lv);
+            const int code =
+                exact_code((double)pick<CPL>(xv, k), sc, zp, QU ? WUSHKV_Q_QUEST : WUSHKV_Q_AFFINE_PCT, Lv);
+            if constexpr (B2) {
+              // this token's field of its set word (other lanes may patch the same word)
+              const int j = seg_chan(q, k);
+              const int sh = ((tok & 1) ? 16 : 0) + ((tok & 2) ? 2 : 0);
+              unsigned *wp = &sm.vw[s2][col >> 4][(16 * (tok >> 2) + (j & 15)) * (D / 16) + (j >> 4)];
+              atomicAnd(wp, ~(3u << sh));
+              atomicOr(wp, (unsigned)code << sh);
+            } else {
+              sm.vc[s2][seg_chan(q, k)][col + tok] = (uint8_t)code;
+            }
           }
         }
       };
@@ -1097,7 +1170,16 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
                 affine_exact<D>(a, x0, x1, y0, y1, Lk, scx, zpx);
               }
             }
-            if (h == 0) sm.kc[row][j] = (uint8_t)exact_code(x, scx, zpx, a.quant_k, Lk);
+            if (h == 0) {
+              const int code = exact_code(x, scx, zpx, a.quant_k, Lk);
+              if constexpr (B2) {
+                const int sh = 2 * (j & 15);
+                atomicAnd(&sm.kp[row][j >> 4], ~(3u << sh));
+                atomicOr(&sm.kp[row][j >> 4], (unsigned)code << sh);
+              } else {
+                sm.kc[row][j] = (uint8_t)code;
+              }
+            }
           }
           const int64_t off = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, 2 * a.kpar_n);
           if (tid == 0 && !(PAGED && off < 0)) {
@@ -1149,12 +1231,25 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         else *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p0[0], p0[1]};
       }
     };
-    using B2 = std::integral_constant<int, 2>;
-    using B3 = std::integral_constant<int, 3>;
-    using B4 = std::integral_constant<int, 4>;
-    if (a.bits_k == 2) pack_k_rows(B2{});
-    else if (a.bits_k == 3) pack_k_rows(B3{});
-    else pack_k_rows(B4{});
+    using Bits2 = std::integral_constant<int, 2>;
+    using Bits3 = std::integral_constant<int, 3>;
+    using Bits4 = std::integral_constant<int, 4>;
+    if constexpr (B2) {
+      // packed rows: a copy, two threads per row
+      const int r = tid >> 1, h = tid & 1;
+      const int64_t u = set0 * kSet + r;
+      const int64_t koff = (u >= u0 && u < u1) ? body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, (int64_t)a.kcode_row)
+                                               : -1;
+      if (koff >= 0) {
+        uint8_t *rowp = a.codes_k + koff;
+        if constexpr (D == 128) *(u32x4 *)(rowp + 16 * h) = *(const u32x4 *)&sm.kp[r][4 * h];
+        else *(u32x2 *)(rowp + 8 * h) = *(const u32x2 *)&sm.kp[r][2 * h];
+      }
+    } else {
+      if (a.bits_k == 2) pack_k_rows(Bits2{});
+      else if (a.bits_k == 3) pack_k_rows(Bits3{});
+      else pack_k_rows(Bits4{});
+    }
 
     // ---- V set words: 128 threads per set, 4 consecutive words each.  A set only
     // partly covered by this call keeps its other tokens' fields.
@@ -1178,12 +1273,16 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         const int ln = wi / NT, t = wi % NT;
         const int c = ln >> 4, j = 16 * t + (ln & 15);
         w0[jj] = w1[jj] = k0[jj] = k1[jj] = 0u;
+        if constexpr (B2)   // the four quarters' fields, each shifted to its place
+          w0[jj] = sm.vw[s2][0][wi] | (sm.vw[s2][1][wi] << 4) | (sm.vw[s2][2][wi] << 8) | (sm.vw[s2][3][wi] << 12);
 #pragma unroll
         for (int aa = 0; aa < 4; ++aa) {
-          const unsigned x = *(const unsigned *)&sm.vc[s2][j][16 * aa + 4 * c];
-          w0[jj] |= vfield2(x) << (4 * aa);
-          if constexpr (BVV == 3) w1[jj] |= vfield1(x) << (2 * aa);
-          if constexpr (BVV == 4) w1[jj] |= vfield2(x >> 2) << (4 * aa);
+          if constexpr (!B2) {
+            const unsigned x = *(const unsigned *)&sm.vc[s2][j][16 * aa + 4 * c];
+            w0[jj] |= vfield2(x) << (4 * aa);
+            if constexpr (BVV == 3) w1[jj] |= vfield1(x) << (2 * aa);
+            if constexpr (BVV == 4) w1[jj] |= vfield2(x >> 2) << (4 * aa);
+          }
           if constexpr (!FULL) {
             unsigned vm = 0;
 #pragma unroll
@@ -1229,14 +1328,18 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     if (vlo < vhi && 4 * t128 < NW) {
       using Full = std::integral_constant<bool, true>;
       using Part = std::integral_constant<bool, false>;
-      if (vlo == vbase && vhi == vbase + kSet) {
-        if (a.bits_v == 2) pack_v_words(B2{}, Full{});
-        else if (a.bits_v == 3) pack_v_words(B3{}, Full{});
-        else pack_v_words(B4{}, Full{});
+      const bool full = vlo == vbase && vhi == vbase + kSet;
+      if constexpr (B2) {
+        if (full) pack_v_words(Bits2{}, Full{});
+        else pack_v_words(Bits2{}, Part{});
+      } else if (full) {
+        if (a.bits_v == 2) pack_v_words(Bits2{}, Full{});
+        else if (a.bits_v == 3) pack_v_words(Bits3{}, Full{});
+        else pack_v_words(Bits4{}, Full{});
       } else {
-        if (a.bits_v == 2) pack_v_words(B2{}, Part{});
-        else if (a.bits_v == 3) pack_v_words(B3{}, Part{});
-        else pack_v_words(B4{}, Part{});
+        if (a.bits_v == 2) pack_v_words(Bits2{}, Part{});
+        else if (a.bits_v == 3) pack_v_words(Bits3{}, Part{});
+        else pack_v_words(Bits4{}, Part{});
       }
     }
     __syncthreads();
@@ -1283,6 +1386,25 @@ hipError_t launch_advance(int32_t *dev_n, int B, int n_new, int64_t cap, hipStre
 }
 
 // Steps (128 body rows) of a flush of body rows [u0, u1).
+// The flush instance for (d, input element size, order statistics): Hadamard butterflies,
+// the 2-bit packing (d = 128 only), or the byte-code path; paged or contiguous body.
+template <int D, int ES, int NL>
+static void launch_flush_inst(const FlushArgs &a, bool b2, dim3 grid, hipStream_t s, int sp) {
+  if (a.had != 0.f) {
+    hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, true, false>), grid, dim3(kThreads), 0, s, a, sp);
+    return;
+  }
+  if constexpr (D == 128) {
+    if (b2) {
+      if (a.pg.table) hipLaunchKernelGGL((flush_kernel<D, ES, NL, true, false, true>), grid, dim3(kThreads), 0, s, a, sp);
+      else hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, false, true>), grid, dim3(kThreads), 0, s, a, sp);
+      return;
+    }
+  }
+  if (a.pg.table) hipLaunchKernelGGL((flush_kernel<D, ES, NL, true, false, false>), grid, dim3(kThreads), 0, s, a, sp);
+  else hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, false, false>), grid, dim3(kThreads), 0, s, a, sp);
+}
+
 static int64_t flush_steps(int64_t u0, int64_t u1) {
   if (u1 <= u0) return 0;
   const int64_t s0 = u0 / kSet, s1 = (u1 + kSet - 1) / kSet;
@@ -1320,16 +1442,13 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   const int nl = need == 0 ? 0 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
   const bool f32 = a.in_dtype == WUSHKV_DT_F32;
   const int sp = (int)spw;
-#define WUSHKV_FLUSH(D, ES, NL)                                                                                 \
-  if (a.had != 0.f) hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, true>), grid, dim3(kThreads), 0, s, a, sp); \
-  else if (a.pg.table) hipLaunchKernelGGL((flush_kernel<D, ES, NL, true, false>), grid, dim3(kThreads), 0, s, a, sp); \
-  else hipLaunchKernelGGL((flush_kernel<D, ES, NL, false, false>), grid, dim3(kThreads), 0, s, a, sp)
-#define WUSHKV_FLUSH_NL(D, ES)            \
-  switch (nl) {                            \
-    case 0: WUSHKV_FLUSH(D, ES, 0); break; \
-    case 2: WUSHKV_FLUSH(D, ES, 2); break; \
-    case 4: WUSHKV_FLUSH(D, ES, 4); break; \
-    default: WUSHKV_FLUSH(D, ES, 8); break; \
+  const bool b2 = a.d == 128 && a.bits_k == 2 && a.bits_v == 2 && a.had == 0.f;
+#define WUSHKV_FLUSH_NL(D, ES)                                 \
+  switch (nl) {                                                 \
+    case 0: launch_flush_inst<D, ES, 0>(a, b2, grid, s, sp); break; \
+    case 2: launch_flush_inst<D, ES, 2>(a, b2, grid, s, sp); break; \
+    case 4: launch_flush_inst<D, ES, 4>(a, b2, grid, s, sp); break; \
+    default: launch_flush_inst<D, ES, 8>(a, b2, grid, s, sp); break; \
   }
   if (a.d == 128) {
     if (f32) { WUSHKV_FLUSH_NL(128, 4) } else { WUSHKV_FLUSH_NL(128, 2) }
@@ -1337,7 +1456,6 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
     if (f32) { WUSHKV_FLUSH_NL(64, 4) } else { WUSHKV_FLUSH_NL(64, 2) }
   }
 #undef WUSHKV_FLUSH_NL
-#undef WUSHKV_FLUSH
   return hipGetLastError();
 }
 
