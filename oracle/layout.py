@@ -9,7 +9,9 @@ Terms: per-token QuEST), and the layout below is this implementation's choice.
 K code plane -- token-major rows of d*b/8 bytes (body index u = p - sink):
   plane 0: d/16 little-endian u32 words; word w, bits 2f..2f+1 hold the low
            two bits of channel 16w + f.
-  plane 1: b = 3: d/32 u32 words; word w, bit f holds bit 2 of channel 32w + f.
+  plane 1: b = 3: d/32 u32 words; word w, bit 4*((f >> 1) & 7) + (f & 1) + 2*(f >> 4)
+           holds bit 2 of channel 32w + f (f in 0..31): nibble k of the word holds
+           channels 2k, 2k+1, 16+2k, 17+2k at its bits 0..3.
            b = 4: d/16 u32 words; word w, bits 2f..2f+1 hold bits 2..3 of
            channel 16w + f.
 
@@ -42,6 +44,11 @@ def _words(b):
     return np.frombuffer(np.ascontiguousarray(b, dtype=np.uint8).tobytes(), dtype="<u4")
 
 
+def _k3_bit(f):
+    """Bit of a 3-bit key row's plane-1 word holding channel f (0..31) of its 32."""
+    return 4 * ((f >> 1) & 7) + (f & 1) + 2 * (f >> 4)
+
+
 def pack_k(codes, bits):
     """codes [T, d] ints in [0, 2**bits) -> uint8 [T, d*bits/8]."""
     codes = np.asarray(codes, dtype=np.int64)
@@ -55,7 +62,7 @@ def pack_k(codes, bits):
         hi = (codes >> 2) & 1
         w1 = np.zeros((T, d // 32), dtype=np.uint64)
         for f in range(32):
-            w1 |= (hi[:, f::32].astype(np.uint64) << np.uint64(f))
+            w1 |= (hi[:, f::32].astype(np.uint64) << np.uint64(_k3_bit(f)))
         parts.append(w1)
     elif bits == 4:
         hi = (codes >> 2) & 3
@@ -80,7 +87,7 @@ def unpack_k(raw, bits, d, T):
     if bits == 3:
         w1 = words[:, nw0:nw0 + d // 32]
         for f in range(32):
-            codes[:, f::32] |= ((w1 >> f) & 1) << 2
+            codes[:, f::32] |= ((w1 >> _k3_bit(f)) & 1) << 2
     elif bits == 4:
         w1 = words[:, nw0:2 * nw0]
         for f in range(16):

@@ -228,7 +228,7 @@ def test_transform_invariance_and_inverse():
 
 def _codes_k(d, rule):
     j = np.arange(d)
-    return {"j%4": j % 4, "j%8": j % 8, "j": j}[rule][None, :]
+    return {"j%4": j % 4, "j%8": j % 8, "j": j, "4*(j//16)": 4 * (j // 16), "4*(j%2)": 4 * (j % 2)}[rule][None, :]
 
 
 def test_pack_k_worked_words():
