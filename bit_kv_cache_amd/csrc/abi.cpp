@@ -120,7 +120,7 @@ int32_t choose_splits(const Geom &g, int64_t nq, int32_t requested, int G) {
   if (requested > 0) return requested;
   const int64_t nsets = (nq + kSet - 1) / kSet;
   int64_t waves = 2048;
-  if (g.d == 128 && (g.bits_k == 2 || g.bits_k == 4) && g.bits_v >= 2 && g.bits_v <= 4 && (G == 4 || G == 8)) {
+  if (g.d == 128 && g.bits_k >= 2 && g.bits_k <= 4 && g.bits_v >= 2 && g.bits_v <= 4 && (G == 4 || G == 8)) {
     const int r = decode_fast_resident_waves(G, g.bits_k, g.bits_v);
     if (r > 0) waves = r;
   }

@@ -567,11 +567,13 @@ __device__ __forceinline__ unsigned kpack2(unsigned x) {
   const unsigned y = (m | (m >> 6)) & 0x000F000Fu;
   return (y | (y >> 12)) & 0xFFu;
 }
-// ... bit 2 of each of 4 codes -> 4 bits.
+// ... bit 2 of each of 4 codes (channels 4e .. 4e + 3 of a 32-channel group) -> bits
+// 0, 1, 4, 5: a 3-bit row's third-bit word holds channel f of its 32 at bit
+// 4 ((f >> 1) & 7) + (f & 1) + 2 (f >> 4), so these land at 8 (e & 3) + 2 (e >> 2)
 __device__ __forceinline__ unsigned kpack1(unsigned x) {
   const unsigned n = (x >> 2) & 0x01010101u;
   const unsigned y = (n | (n >> 7)) & 0x00030003u;
-  return (y | (y >> 14)) & 0xFu;
+  return (y | (y >> 12)) & 0x33u;
 }
 
 // HAD: the key transform is T_K = a.had * H (Sylvester-Hadamard, H[j][i] = (-1)^popcount(i & j)),
@@ -1217,7 +1219,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         for (int k = 0; k < HC / 32; ++k) {
           unsigned w = 0;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) w |= kpack1(cw[2 * k + e / 4][e % 4]) << (4 * e);
+          for (int e = 0; e < 8; ++e) w |= kpack1(cw[2 * k + e / 4][e % 4]) << (8 * (e & 3) + 2 * (e >> 2));
           p1[k] = w;
         }
         if constexpr (HC / 32 == 2) *(u32x2 *)(rowp + D / 4 + 8 * h) = (u32x2){p1[0], p1[1]};

@@ -1,5 +1,5 @@
 // GQA decode attention over the quantized cache on MFMA (gfx950), head_dim 128,
-// G = 4 or 8 query heads per KV head, 2- or 4-bit keys, 2-, 3- or 4-bit values.
+// G = 4 or 8 query heads per KV head, 2-, 3- or 4-bit keys and values.
 //
 // What it computes is the plain softmax attention of the pages' method: scores
 // (q . k)/sqrt(d) on the FP16 sink and recent tokens and (q~ . x^)/sqrt(d) on the
@@ -68,7 +68,7 @@ __device__ __forceinline__ float dpp(float old, float src) {
 // pending slot covers either.
 template <int BK, int BV>
 struct Stage {
-  static constexpr int KROW = BK == 4 ? 64 : 32;          // key row bytes
+  static constexpr int KROW = 16 * BK;                     // key row bytes (d = 128)
   static constexpr int K = 0, V = 64 * KROW, VH = V + 2048;
   static constexpr int VHB = BV == 3 ? 1024 : (BV == 4 ? 2048 : 0);
   static constexpr int KP = VH + VHB, VP = KP + 256, SIZE = VP + 256;
@@ -217,6 +217,14 @@ __device__ __forceinline__ void digit_row(int m, int r, int &h, int &j) {
 __device__ __forceinline__ i32x8 key_fp4(u32x2 w) {
   const unsigned M = 0x33333333u;
   return (i32x8){(int)(w[0] & M), (int)((w[0] >> 2) & M), (int)(w[1] & M), (int)((w[1] >> 2) & M), 0, 0, 0, 0};
+}
+
+// A 3-bit key row's third bits for the lane's 32 channels (one plane-1 word: channel f
+// at bit 4 ((f >> 1) & 7) + (f & 1) + 2 (f >> 4)) as fp4 operand words in key_fp4's
+// channel order: each set bit becomes bit 2 of its nibble, the e2m1 value 2.
+__device__ __forceinline__ i32x8 key_bits_fp4(unsigned p) {
+  const unsigned M = 0x44444444u;
+  return (i32x8){(int)((p << 2) & M), (int)((p << 1) & M), (int)(p & M), (int)((p >> 1) & M), 0, 0, 0, 0};
 }
 
 // Max / sum over the 16 lanes of a row (DPP rotations within the row, then quad swaps).
@@ -626,15 +634,19 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BK, BV, NW> &sm, int 
       // products enter the same accumulation with B scaled by 4 (E8M0 129)
       i32x8 bh;
       if constexpr (BK == 4) bh = key_fp4(*(const u32x2 *)(kr + 32));
+      // 3-bit keys: the row's second plane holds the third bits, c = lo + 4 h; a set bit
+      // enters as the e2m1 value 2 (= 4 h / 2, on the low plane's scale)
+      if constexpr (BK == 3) bh = key_bits_fp4(*(const unsigned *)(kr + 32 - 4 * g4));
       // per head quad: digits 4-7 accumulate onto the rows of digits 0-3
 #pragma unroll
       for (int qd = 0; qd < NQ; ++qd) {
         f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bk, (f32x4){0.f, 0.f, 0.f, 0.f}, 4, 4,
                                                                    0, sa[2 * qd], 0, 127);
         d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bk, d, 4, 4, 0, sa[2 * qd + 1], 0, 127);
-        if constexpr (BK == 4) {
-          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bh, d, 4, 4, 0, sa[2 * qd], 0, 129);
-          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bh, d, 4, 4, 0, sa[2 * qd + 1], 0, 129);
+        if constexpr (BK >= 3) {
+          constexpr int SB = BK == 4 ? 129 : 127;
+          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd], bh, d, 4, 4, 0, sa[2 * qd], 0, SB);
+          d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aq[2 * qd + 1], bh, d, 4, 4, 0, sa[2 * qd + 1], 0, SB);
         }
         sc[qd][T] = (d[3] + d[2]) + (d[1] + d[0]);
       }
@@ -1072,7 +1084,7 @@ bool decode_fast_supported(const DecodeArgs &a) {
         rows * 2 * a.vpar_n >= lim)
       return false;
   }
-  return a.d == 128 && (a.bits_k == 2 || a.bits_k == 4) && a.bits_v >= 2 && a.bits_v <= 4 && (a.G == 4 || a.G == 8) &&
+  return a.d == 128 && a.bits_k >= 2 && a.bits_k <= 4 && a.bits_v >= 2 && a.bits_v <= 4 && (a.G == 4 || a.G == 8) &&
          a.kcode_bytes < lim && a.vcode_bytes < lim && a.kpar_bytes < lim && a.vpar_bytes < lim;
 }
 
@@ -1113,20 +1125,18 @@ bool decode_fast_direct(const DecodeArgs &a) { return decode_fast_partials(a) ==
 // The split layout's plain kernel of (G, bits_k, bits_v).
 static const void *split_kernel(int G, int bits_k, int bits_v) {
 #define WUSHKV_K(G_, BK_, BV_) (const void *)decode_fast_kernel<G_, BK_, BV_, kSplitWaves, false, false>
-  if (G == 4) {
-    if (bits_k == 2) return bits_v == 2 ? WUSHKV_K(4, 2, 2) : bits_v == 3 ? WUSHKV_K(4, 2, 3) : WUSHKV_K(4, 2, 4);
-    return bits_v == 2 ? WUSHKV_K(4, 4, 2) : bits_v == 3 ? WUSHKV_K(4, 4, 3) : WUSHKV_K(4, 4, 4);
-  }
-  if (bits_k == 2) return bits_v == 2 ? WUSHKV_K(8, 2, 2) : bits_v == 3 ? WUSHKV_K(8, 2, 3) : WUSHKV_K(8, 2, 4);
-  return bits_v == 2 ? WUSHKV_K(8, 4, 2) : bits_v == 3 ? WUSHKV_K(8, 4, 3) : WUSHKV_K(8, 4, 4);
+#define WUSHKV_KV(G_, BK_) (bits_v == 2 ? WUSHKV_K(G_, BK_, 2) : bits_v == 3 ? WUSHKV_K(G_, BK_, 3) : WUSHKV_K(G_, BK_, 4))
+  if (G == 4) return bits_k == 2 ? WUSHKV_KV(4, 2) : bits_k == 3 ? WUSHKV_KV(4, 3) : WUSHKV_KV(4, 4);
+  return bits_k == 2 ? WUSHKV_KV(8, 2) : bits_k == 3 ? WUSHKV_KV(8, 3) : WUSHKV_KV(8, 4);
+#undef WUSHKV_KV
 #undef WUSHKV_K
 }
 
 // Waves of the MFMA decode the GPU holds at once for (G, bits_k, bits_v) in the split
 // layout; 0 if unknown.
 int decode_fast_resident_waves(int G, int bits_k, int bits_v) {
-  static int cache[2][2][3] = {{{-1, -1, -1}, {-1, -1, -1}}, {{-1, -1, -1}, {-1, -1, -1}}};
-  int &c = cache[G == 8][bits_k == 4][bits_v - 2];
+  static int cache[2][3][3] = {{{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}}, {{-1, -1, -1}, {-1, -1, -1}, {-1, -1, -1}}};
+  int &c = cache[G == 8][bits_k - 2][bits_v - 2];
   if (c >= 0) return c;
   int blocks = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, split_kernel(G, bits_k, bits_v), 64 * kSplitWaves, 0) !=
@@ -1179,16 +1189,21 @@ hipError_t launch_decode_fast(const DecodeArgs &a, hipStream_t s) {
     else if (a.G == 4) { WUSHKV_FAST(4, 2, 3, kSplitWaves); }
     else if (a.bits_v == 2) { WUSHKV_FAST(8, 2, 2, kSplitWaves); }
     else { WUSHKV_FAST(8, 2, 3, kSplitWaves); }
-  } else if (a.G == 4) {
-    if (a.bits_k == 2) { WUSHKV_FAST_NA(4, 2, 4); }
-    else if (a.bits_v == 2) { WUSHKV_FAST_NA(4, 4, 2); }
-    else if (a.bits_v == 3) { WUSHKV_FAST_NA(4, 4, 3); }
-    else { WUSHKV_FAST_NA(4, 4, 4); }
   } else {
-    if (a.bits_k == 2) { WUSHKV_FAST_NA(8, 2, 4); }
-    else if (a.bits_v == 2) { WUSHKV_FAST_NA(8, 4, 2); }
-    else if (a.bits_v == 3) { WUSHKV_FAST_NA(8, 4, 3); }
-    else { WUSHKV_FAST_NA(8, 4, 4); }
+#define WUSHKV_FAST_BV(G, BK)                    \
+  if (a.bits_v == 2) { WUSHKV_FAST_NA(G, BK, 2); } \
+  else if (a.bits_v == 3) { WUSHKV_FAST_NA(G, BK, 3); } \
+  else { WUSHKV_FAST_NA(G, BK, 4); }
+    if (a.G == 4) {
+      if (a.bits_k == 2) { WUSHKV_FAST_NA(4, 2, 4); }
+      else if (a.bits_k == 3) { WUSHKV_FAST_BV(4, 3) }
+      else { WUSHKV_FAST_BV(4, 4) }
+    } else {
+      if (a.bits_k == 2) { WUSHKV_FAST_NA(8, 2, 4); }
+      else if (a.bits_k == 3) { WUSHKV_FAST_BV(8, 3) }
+      else { WUSHKV_FAST_BV(8, 4) }
+    }
+#undef WUSHKV_FAST_BV
   }
 #undef WUSHKV_FAST_NA
 #undef WUSHKV_FAST

@@ -30,7 +30,10 @@ struct GenSmem {
 __device__ __forceinline__ int k_code(const uint8_t *row, int d, int bits, int j) {
   const unsigned *w = (const unsigned *)row;
   int c = (w[j / 16] >> (2 * (j % 16))) & 3;
-  if (bits == 3) c |= ((w[d / 16 + j / 32] >> (j % 32)) & 1) << 2;
+  if (bits == 3) {   // third bits: channel f of each 32 at bit 4 ((f >> 1) & 7) + (f & 1) + 2 (f >> 4)
+    const int f = j % 32;
+    c |= ((w[d / 16 + j / 32] >> (4 * ((f >> 1) & 7) + (f & 1) + 2 * (f >> 4))) & 1) << 2;
+  }
   if (bits == 4) c |= ((w[d / 16 + j / 16] >> (2 * (j % 16))) & 3) << 2;
   return c;
 }

@@ -263,13 +263,18 @@ WIDE = [
     (4, 3, "affine", "affine", 8),
     (4, 4, "affine", "quest", 8),
     (2, 4, "quest", "affine", 8),
+    (3, 2, "quest", "quest", 4),
+    (3, 3, "affine", "affine", 4),
+    (3, 4, "quest", "affine", 8),
+    (3, 3, "quest", "quest", 8),
 ]
 
 
 @pytest.mark.parametrize("bits_k,bits_v,quant_k,quant_v,G", WIDE)
 def test_wide_codes_mfma_decode(bits_k, bits_v, quant_k, quant_v, G):
     """4-bit keys (two 2-bit planes on the same q~ digits, the high plane's products
-    scaled by 4) and 4-bit values (a second B operand on the same W at four times the
+    scaled by 4), 3-bit keys (the third-bit plane as a second fp4 operand of e2m1 value
+    2 per set bit) and 4-bit values (a second B operand on the same W at four times the
     weight) on the MFMA decode: held to the oracle, and to the generic kernel on the same
     cache, with a ragged last set and several splits."""
     qk = configs.QUEST if quant_k == "quest" else configs.AFFINE
