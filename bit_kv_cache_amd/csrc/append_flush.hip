@@ -179,6 +179,22 @@ template <int D, int ES>
 __device__ __forceinline__ void load_seg(const FlushArgs &a, int64_t n_before, const char *ring_h, const char *in_h,
                                          int64_t u, bool valid, int q, RawSeg<ES, D / 4> &s) {
   constexpr int CPL = D / 4;
+  if constexpr (ES == 2) {
+    // 2-byte input rows have the ring's layout: every lane issues the same loads from a
+    // selected row (an invalid token reads the head's first input row, which exists
+    // whenever there is a body row to flush, and its values are never used), so no
+    // branch surrounds the loads and the wave's load counter stays exact
+    const bool ring = valid && a.S + u < n_before;
+    const char *row = in_h + (size_t)((valid && !ring) ? a.S + u - n_before : 0) * (D * 2);
+    if (__builtin_expect(__any(ring), 0)) {
+      const unsigned slot = (unsigned)u % (unsigned)(a.R + a.C);
+      if (ring) row = ring_h + (size_t)slot * (D * 2);
+    }
+    const u32x4 *src = (const u32x4 *)row + q;
+#pragma unroll
+    for (int i = 0; i < CPL / 8; ++i) s.r[i] = __builtin_nontemporal_load(src + 4 * i);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < CPL * ES / 16; ++i) s.r[i] = (u32x4){0u, 0u, 0u, 0u};
   if (!valid) return;
@@ -511,6 +527,16 @@ __device__ __forceinline__ double pick64(const double (&x)[NL], int i) {
   return r;
 }
 
+// Workgroup barrier that orders LDS only.  The flush's waves share nothing through
+// global memory within a call (every code row, set word and parameter has one writer),
+// so its barriers need not wait for the wave's global loads and stores: the next step's
+// rows stay in flight across them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // DPP quad permutations (gfx9 quad_perm): lane i of a quad reads lane i^2 / i^1.
 __device__ __forceinline__ unsigned quad_xor2(unsigned x) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true);
@@ -634,10 +660,9 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     const int64_t u = tok_of(st, tt);
     load_seg<D, ES>(a, n_before, ring_vh, in_vh, u, tok_valid(u), q, rv[tt]);
   };
-  if (st0 < st1) {   // in flight while T_K is staged
+  // the first step's rows, in flight while T_K is staged
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) { load_k(st0, tt); load_v(st0, tt); }
-  }
+  for (int tt = 0; tt < 2; ++tt) { load_k(st0, tt); load_v(st0, tt); }
   if constexpr (HAD) {
     const _Float16 hp = (_Float16)a.had, hn = (_Float16)(-a.had);
     for (int i = tid; i < D * D; i += kThreads) {
@@ -654,7 +679,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   // quad-transpose selectors of this lane (position e = tok & 3 in its quad)
   const unsigned selA = (tok & 2) ? 0x03020706u : 0x05040100u;
   const unsigned selB = (tok & 1) ? 0x03070105u : 0x06020400u;
-  __syncthreads();
+  lds_barrier();
 
   for (int64_t st = st0; st < st1; ++st) {
     const int64_t set0 = s_first + 2 * st;
@@ -688,7 +713,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       // rows of earlier calls (fp16, from the ring) in the tile: rare outside decode steps
       if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
       else seg_half2<ES, CPL>(rk[tt], false, a.in_dtype, kh);   // (invalid rows are zeros either way)
-      if (st + 1 < st1) load_k(st + 1, tt);
+      load_k(st + 1 < st1 ? st + 1 : st, tt);   // (the last step reloads its own rows: no branch)
       f32x4 acc[NCT];
       if constexpr (HAD) {
         // x = a H k16 by butterflies: element (ct, i) of lane (q, tok) is channel 16 ct + 4 q
@@ -741,6 +766,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       auto key_tile = [&](auto tag) {
         constexpr bool QU = decltype(tag)::value;
         float sc, zp = 0.f;
+        bool kdef = false;   // queued for exact parameters: the queue stores them
         if constexpr (QU) {
           float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -765,7 +791,8 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             const double d64 = quest_pre64(s64, a.clip, Lk, D);
             if (pn) sc = f16_of_f64(d64);
             // still near one: the exact x after the step's tiles
-            defer(pn && near_mid((float)d64, parKB * (float)d64), row, kh, 0u, 0.f, 0.f, 0.f, sc, 0.f);
+            kdef = pn && near_mid((float)d64, parKB * (float)d64);
+            defer(kdef, row, kh, 0u, 0.f, 0.f, 0.f, sc, 0.f);
           }
         } else if constexpr (NL > 0) {
           OrderStats<NL> o;
@@ -803,12 +830,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
                 for (int i = 0; i < 4; ++i)
                   if (acc[ct][i] <= cut_lo + mg || acc[ct][i] >= cut_hi - mg) cmask |= 1u << (4 * ct + i);
             }
+            kdef = pn2;
             defer(pn2, row, kh, cmask, cut_lo, cut_hi, mg, sc, zp);
           }
         } else {
           sc = 0.f;
         }
-        if (q == 0 && vt) {
+        if (q == 0 && vt && !kdef) {
           const int64_t off = body_offset<PAGED>(a.pg, a.Hkv, a.body_cap, b, g, u, 2 * a.kpar_n);
           _Float16 *pk = (_Float16 *)((char *)a.par_k + off);
           if (PAGED && off < 0) {
@@ -905,7 +933,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       float xv[CPL];
       if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_float<ES, CPL>(rv[tt], tok_ring(u), a.in_dtype, xv);
       else seg_float<ES, CPL>(rv[tt], false, a.in_dtype, xv);
-      if (st + 1 < st1) load_v(st + 1, tt);
+      load_v(st + 1 < st1 ? st + 1 : st, tt);
       const int s2 = wave >> 1;                       // set of this wave within the step
       const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
       auto value_tile = [&](auto tag) {
@@ -1024,7 +1052,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     // gets the exact x of all channels (thread group of channel j: x_j in fp64), its exact
     // parameters and the codes of its exact x.
     if (lane == 0) sm.dqn[wave] = ndq;
-    __syncthreads();
+    lds_barrier();
     const int nq0 = sm.dqn[0], nq1 = sm.dqn[1], nq2 = sm.dqn[2], nq3 = sm.dqn[3];
     if (__builtin_expect(nq0 + nq1 + nq2 + nq3 > 0, 0)) {
       auto key_row8 = [&](int64_t u, int m) -> u32x4 {
@@ -1062,7 +1090,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
           } else if (tid < D / 8) {
             *(u32x4 *)&sm.krow[4 * tid] = key_row8(u, tid);
           }
-          __syncthreads();
+          lds_barrier();
           float scx = d.sc, zpx = d.zp;
           bool full = a.quant_k == WUSHKV_Q_QUEST;
           int total = 0;
@@ -1095,7 +1123,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
                 for (int sh = 1; sh < 16; sh <<= 1) part += __shfl_xor(part, sh);
                 if (m == 0 && found) sm.cand[c] = part;
-                __syncthreads();
+                lds_barrier();
                 double lo_s[NL], hi_s[NL];
 #pragma unroll
                 for (int k = 0; k < NL; ++k) { lo_s[k] = INFINITY; hi_s[k] = -INFINITY; }
@@ -1131,7 +1159,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
               for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
               if (lane == 0) sm.red[wave][0] = ss;
-              __syncthreads();
+              lds_barrier();
               ss = ((sm.red[0][0] + sm.red[1][0]) + (sm.red[2][0] + sm.red[3][0])) / (double)TPC;
               scx = f16_of_f64(quest_pre64(ss, a.clip, Lk, D));
             } else if constexpr (NL > 0) {
@@ -1154,7 +1182,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 #pragma unroll
                   for (int k = 0; k < NL; ++k) { sm.red[wave][k] = lo_s[k]; sm.red[wave][NL + k] = hi_s[k]; }
                 }
-                __syncthreads();
+                lds_barrier();
 #pragma unroll
                 for (int k = 0; k < NL; ++k) { lo_s[k] = INFINITY; hi_s[k] = -INFINITY; }
 #pragma unroll
@@ -1189,7 +1217,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
             if (a.quant_k == WUSHKV_Q_QUEST) pk[0] = (_Float16)scx;
             else *(unsigned *)pk = pack_f16(scx, zpx);
           }
-          __syncthreads();
+          lds_barrier();
         }
       }
     }
@@ -1344,7 +1372,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
         else pack_v_words(Bits4{}, Part{});
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
