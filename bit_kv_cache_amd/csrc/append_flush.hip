@@ -171,7 +171,8 @@ __device__ __forceinline__ unsigned raw_word(const RawSeg<ES, CPL> &s, int i) {
 }
 
 // Load the segment of body token u (valid) from the ring if it was appended by an
-// earlier call (an fp16 row), else from the new input; an invalid token reads zeros.
+// earlier call (an fp16 row), else from the new input; an invalid token reads zeros (2-byte
+// input: the head's first input row), values that are never used.
 // Lane group q holds channels 32 i + 8 q .. 32 i + 8 q + 7 (i = 0 .. D/32 - 1), at
 // position 8 i + e of its list: one load instruction then covers 32 contiguous
 // channels of each of its 16 rows.
@@ -643,7 +644,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   RawSeg<ES, CPL> rk[2], rv[2];
   auto tok_of = [&](int64_t st, int tt) { return (s_first + 2 * st) * kSet + 32 * wave + 16 * tt + tok; };
   auto tok_valid = [&](int64_t u) { return u >= u0 && u < u1; };
-  // rows of earlier calls come from the ring (fp16); invalid rows read as fp16 zeros
+  // rows of earlier calls come from the ring (fp16); invalid rows are converted as fp16
   auto tok_ring = [&](int64_t u) { return !tok_valid(u) || a.S + u < n_before; };
   // this KV head's ring and input rows
   const char *ring_kh = (const char *)a.ring_k + (size_t)bg * a.ring_bytes;
@@ -709,10 +710,14 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     for (int tt = 0; tt < 2; ++tt) {
       const int64_t u = ubase + 16 * tt + tok;
       const bool vt = tok_valid(u);
+      if (!__any(vt)) {   // no row of this call's flush in the tile (a decode step's chunk, a call's edges)
+        load_k(st + 1 < st1 ? st + 1 : st, tt);
+        continue;
+      }
       unsigned kh[CPL / 2];
       // rows of earlier calls (fp16, from the ring) in the tile: rare outside decode steps
       if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
-      else seg_half2<ES, CPL>(rk[tt], false, a.in_dtype, kh);   // (invalid rows are zeros either way)
+      else seg_half2<ES, CPL>(rk[tt], false, a.in_dtype, kh);   // (an invalid row's values are never used)
       load_k(st + 1 < st1 ? st + 1 : st, tt);   // (the last step reloads its own rows: no branch)
       f32x4 acc[NCT];
       if constexpr (HAD) {
@@ -930,12 +935,25 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
     for (int tt = 0; tt < 2; ++tt) {
       const int64_t u = ubase + 16 * tt + tok;
       const bool vt = tok_valid(u);
+      const int s2 = wave >> 1;                       // set of this wave within the step
+      const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
+      if (!__any(vt)) {
+        load_v(st + 1 < st1 ? st + 1 : st, tt);
+        if constexpr (B2) {
+          // the quarter's words are OR-ed into whole set words, so they must hold fields
+          // only: zero codes (the set's merge keeps the stored fields of these tokens)
+#pragma unroll
+          for (int g4 = 0; g4 < CPL / 4; ++g4) {
+            const int j = seg_chan(q, 4 * g4 + (tok & 3));
+            sm.vw[s2][col >> 4][(16 * (tok >> 2) + (j & 15)) * (D / 16) + (j >> 4)] = 0u;
+          }
+        }
+        continue;
+      }
       float xv[CPL];
       if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_float<ES, CPL>(rv[tt], tok_ring(u), a.in_dtype, xv);
       else seg_float<ES, CPL>(rv[tt], false, a.in_dtype, xv);
       load_v(st + 1 < st1 ? st + 1 : st, tt);
-      const int s2 = wave >> 1;                       // set of this wave within the step
-      const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
       auto value_tile = [&](auto tag) {
         constexpr bool QU = decltype(tag)::value;
         float sc, zp = 0.f;
