@@ -253,6 +253,10 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
       flush |= n_quantized(seq_nb[b] + n_new, g.S, g.R, g.C) > n_quantized(seq_nb[b], g.S, g.R, g.C);
   }
   (void)hipGetLastError();   // clear an earlier sticky error before launching
+  // A uniform call whose flushed rows all come from the input (every prefill) writes its
+  // window rows from extra workgroups of the flush launch: the flush then reads no ring
+  // slot, so the two may run together, and the call is one launch.
+  const bool fuse_append = flush && !dev_n && !seq_nb && !deferred && g.S + qb >= n_before;
   if (flush) {
     // The flush reads ring rows written by earlier calls, so it runs before this
     // call's ring writes (same stream, in order).
@@ -274,6 +278,11 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
     f.pg = pg;
     f.body_cap = g.body_cap;
     f.had = had;
+    if (fuse_append) {
+      f.append_x = append_workgroups(n_before, n_new, qa, g.S, g.d);
+      f.sink_k = (_Float16 *)c->sink_k; f.sink_v = (_Float16 *)c->sink_v;
+      f.sink_bytes = g.sink_bytes;
+    }
     if (dev_n) {
       f.ragged = kRaggedDevice;
       f.dev_n = dev_n;
@@ -282,6 +291,7 @@ int append_flush_impl(const wushkv_cache *c, const wushkv_pages *pages, int64_t 
       for (int b = 0; b < g.B; ++b) f.seq_nb[b] = (int32_t)seq_nb[b];
     }
     if (launch_flush(f, s) != hipSuccess) return WUSHKV_ERR_HIP;
+    if (fuse_append) return hip_status();
   }
   AppendArgs a;
   memset(&a, 0, sizeof a);

@@ -34,30 +34,28 @@ __host__ __device__ inline int64_t window_tokens(int64_t n_before, int64_t n_new
   return ns + (n_new - tr);
 }
 
-__global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
-  // one thread per (window token, 8-channel group); blockIdx.y = b * Hkv + g.  The grid
-  // covers the most window tokens any sequence has, not all n_new tokens.
-  const int bg = blockIdx.y;
+// Element (window token i, 8-channel group) idx of KV head bg: its fp16 copy into the
+// sink or its ring slot.
+template <class A>
+__device__ __forceinline__ void append_group(const A &a, _Float16 *sink_k, _Float16 *sink_v, _Float16 *ring_k,
+                                             _Float16 *ring_v, size_t sink_bytes, int bg, int64_t n_before,
+                                             int64_t q_after, int64_t idx) {
   const int b = bg / a.Hkv, g = bg % a.Hkv;
   const int groups = a.d / 8;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t i = idx / groups;
   const int j0 = (int)(idx % groups) * 8;
-  const int64_t n_before = seq_before(a, b);
-  if (n_before < 0) return;
-  const int64_t q_after = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.q_after;
   int64_t ns, tr;
   if (i >= window_tokens(n_before, a.n_new, q_after, a.S, ns, tr)) return;
   const int64_t t = i < ns ? i : tr + (i - ns);
   const int64_t p = n_before + t;
   _Float16 *dk, *dv;
   if (p < a.S) {
-    dk = (_Float16 *)((char *)a.sink_k + bg * a.sink_bytes) + p * a.d;
-    dv = (_Float16 *)((char *)a.sink_v + bg * a.sink_bytes) + p * a.d;
+    dk = (_Float16 *)((char *)sink_k + bg * sink_bytes) + p * a.d;
+    dv = (_Float16 *)((char *)sink_v + bg * sink_bytes) + p * a.d;
   } else {
     const int64_t slot = (p - a.S) % (a.R + a.C);
-    dk = (_Float16 *)((char *)a.ring_k + bg * a.ring_bytes) + slot * a.d;
-    dv = (_Float16 *)((char *)a.ring_v + bg * a.ring_bytes) + slot * a.d;
+    dk = (_Float16 *)((char *)ring_k + bg * a.ring_bytes) + slot * a.d;
+    dv = (_Float16 *)((char *)ring_v + bg * a.ring_bytes) + slot * a.d;
   }
   const size_t src = (((size_t)b * a.Hkv + g) * a.n_new + t) * a.d + j0;
   half8 hk, hv;
@@ -68,6 +66,17 @@ __global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
   }
   *(half8 *)(dk + j0) = hk;
   *(half8 *)(dv + j0) = hv;
+}
+
+__global__ void __launch_bounds__(kThreads) append_kernel(AppendArgs a) {
+  // one thread per (window token, 8-channel group); blockIdx.y = b * Hkv + g.  The grid
+  // covers the most window tokens any sequence has, not all n_new tokens.
+  const int bg = blockIdx.y;
+  const int64_t n_before = seq_before(a, bg / a.Hkv);
+  if (n_before < 0) return;
+  const int64_t q_after = a.ragged ? n_quantized(n_before + a.n_new, a.S, a.R, a.C) : a.q_after;
+  append_group(a, a.sink_k, a.sink_v, a.ring_k, a.ring_v, a.sink_bytes, bg, n_before, q_after,
+               (int64_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 // ------------------------------------------------------------------ flush
@@ -622,6 +631,12 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   using QuestTag = std::integral_constant<bool, true>;
   using AffineTag = std::integral_constant<bool, false>;
   __shared__ FlushSmem<D> sm;
+  if (a.append_x > 0 && (int)blockIdx.x >= (int)gridDim.x - a.append_x) {
+    // fused window append (uniform counts; no flushed row comes from the ring)
+    append_group(a, a.sink_k, a.sink_v, (_Float16 *)a.ring_k, (_Float16 *)a.ring_v, a.sink_bytes, blockIdx.y,
+                 a.n_before, a.u1, (int64_t)(blockIdx.x - (gridDim.x - a.append_x)) * kThreads + threadIdx.x);
+    return;
+  }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = lane >> 4, tok = lane & 15;
   const int bg = blockIdx.y, b = bg / a.Hkv, g = bg % a.Hkv;
@@ -1396,6 +1411,13 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
 
 }  // namespace
 
+// Workgroups of the window append for a uniform call (0 if it writes no window row).
+int append_workgroups(int64_t n_before, int64_t n_new, int64_t q_after, int S, int d) {
+  int64_t ns, tr;
+  const int64_t most = window_tokens(n_before, n_new, q_after, S, ns, tr);
+  return (int)((most * (d / 8) + kThreads - 1) / kThreads);
+}
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   // window tokens of the sequence with the most: exact for host counts; device counts
   // are unknown here, and a sequence never has more than S + R + C - 1 (the sink, and
@@ -1483,7 +1505,7 @@ hipError_t launch_flush(const FlushArgs &a, hipStream_t s) {
   // runs measured ~4% slower on the bulk flush)
   int64_t spw = (steps * heads + 511) / 512;
   if (spw < 2) spw = 2;
-  dim3 grid((unsigned)((steps + spw - 1) / spw), (unsigned)heads);
+  dim3 grid((unsigned)((steps + spw - 1) / spw + a.append_x), (unsigned)heads);
   int need = 0;
   if (a.quant_k == WUSHKV_Q_AFFINE_PCT || a.quant_v == WUSHKV_Q_AFFINE_PCT)
     need = a.need_lo > a.need_hi ? a.need_lo : a.need_hi;

@@ -77,6 +77,12 @@ struct FlushArgs {
   PageTable pg;
   int64_t body_cap;
   float had;                      // nonzero: T_K = had * H (Sylvester-Hadamard), tk unused
+  // Fused window append (uniform counts, every flushed row from the input, so no ring
+  // slot the flush reads is written): the last append_x workgroups of the grid's x
+  // dimension write the call's sink and ring rows, as append_kernel would; 0: none.
+  int append_x;
+  _Float16 *sink_k, *sink_v;
+  size_t sink_bytes;
 };
 
 struct AppendArgs {
@@ -146,6 +152,8 @@ int decode_attention_checked(const wushkv_cache *c, int64_t n_tokens, const void
                              float *out, void *stream, bool validate_only);
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+// Workgroups of the window append of a uniform call (FlushArgs::append_x).
+int append_workgroups(int64_t n_before, int64_t n_new, int64_t q_after, int S, int d);
 hipError_t launch_advance(int32_t *dev_n, int B, int n_new, int64_t cap, hipStream_t s);
 hipError_t launch_calib(const CalibArgs &a, hipStream_t s);
 int calib_batch_per_wg(int B, int groups);
