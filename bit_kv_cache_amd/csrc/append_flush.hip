@@ -667,14 +667,19 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
   const size_t in_off = (size_t)bg * (size_t)a.n_new * (D * ES);
   const char *in_kh = (const char *)a.k_new + in_off;
   const char *in_vh = (const char *)a.v_new + in_off;
+  // Refill of a tile with step st's rows.  After the run's last step (st == st1) the
+  // refill loads rows that are never used: as for invalid tokens, every lane then reads
+  // the head's first input row (one cached row, no HBM traffic to speak of) with the
+  // same load instructions, so the wave's load count stays uniform.
   auto load_k = [&](int64_t st, int tt) {
     const int64_t u = tok_of(st, tt);
-    if constexpr (HAD) load_seg_ct<D, ES>(a, n_before, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
-    else load_seg<D, ES>(a, n_before, ring_kh, in_kh, u, tok_valid(u), q, rk[tt]);
+    const bool valid = st < st1 && tok_valid(u);
+    if constexpr (HAD) load_seg_ct<D, ES>(a, n_before, ring_kh, in_kh, u, valid, q, rk[tt]);
+    else load_seg<D, ES>(a, n_before, ring_kh, in_kh, u, valid, q, rk[tt]);
   };
   auto load_v = [&](int64_t st, int tt) {
     const int64_t u = tok_of(st, tt);
-    load_seg<D, ES>(a, n_before, ring_vh, in_vh, u, tok_valid(u), q, rv[tt]);
+    load_seg<D, ES>(a, n_before, ring_vh, in_vh, u, st < st1 && tok_valid(u), q, rv[tt]);
   };
   // the first step's rows, in flight while T_K is staged
 #pragma unroll
@@ -726,14 +731,14 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       const int64_t u = ubase + 16 * tt + tok;
       const bool vt = tok_valid(u);
       if (!__any(vt)) {   // no row of this call's flush in the tile (a decode step's chunk, a call's edges)
-        load_k(st + 1 < st1 ? st + 1 : st, tt);
+        load_k(st + 1, tt);
         continue;
       }
       unsigned kh[CPL / 2];
       // rows of earlier calls (fp16, from the ring) in the tile: rare outside decode steps
       if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_half2<ES, CPL>(rk[tt], tok_ring(u), a.in_dtype, kh);
       else seg_half2<ES, CPL>(rk[tt], false, a.in_dtype, kh);   // (an invalid row's values are never used)
-      load_k(st + 1 < st1 ? st + 1 : st, tt);   // (the last step reloads its own rows: no branch)
+      load_k(st + 1, tt);
       f32x4 acc[NCT];
       if constexpr (HAD) {
         // x = a H k16 by butterflies: element (ct, i) of lane (q, tok) is channel 16 ct + 4 q
@@ -953,7 +958,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       const int s2 = wave >> 1;                       // set of this wave within the step
       const int col = 32 * (wave & 1) + 16 * tt;      // first token of the tile in its set
       if (!__any(vt)) {
-        load_v(st + 1 < st1 ? st + 1 : st, tt);
+        load_v(st + 1, tt);
         if constexpr (B2) {
           // the quarter's words are OR-ed into whole set words, so they must hold fields
           // only: zero codes (the set's merge keeps the stored fields of these tokens)
@@ -968,7 +973,7 @@ __global__ void __launch_bounds__(kThreads, 2) flush_kernel(FlushArgs a, int ste
       float xv[CPL];
       if (__builtin_expect(__any(vt && a.S + u < n_before), 0)) seg_float<ES, CPL>(rv[tt], tok_ring(u), a.in_dtype, xv);
       else seg_float<ES, CPL>(rv[tt], false, a.in_dtype, xv);
-      load_v(st + 1 < st1 ? st + 1 : st, tt);
+      load_v(st + 1, tt);
       auto value_tile = [&](auto tag) {
         constexpr bool QU = decltype(tag)::value;
         float sc, zp = 0.f;
