@@ -950,8 +950,8 @@ def main():
         if 2 in fl:
             # HBM bytes per append_flush call (one layer) from the committed counter summary,
             # beside the call's algorithmic bytes
-            ft = traffic_from_profile("flush_bulk_counters.json", ["flush_kernel<128, 2, 0, false, false>",
-                                                                   "append_kernel"])
+            # (one launch per layer: the same flush kernel also writes the window rows)
+            ft = traffic_from_profile("flush_bulk_counters.json", ["flush_kernel<128, 2, 0, false, false, true>"])
             line["flush"]["2bit"]["algorithmic_bytes_per_layer"] = fl[2]["bytes_layer"]
             line["flush"]["2bit"]["traffic_bytes_per_layer"] = ft
         if had:
