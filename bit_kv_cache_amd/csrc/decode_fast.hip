@@ -497,7 +497,7 @@ __device__ void body_wave(const DecodeArgs &a, FastSmem<G, BK, BV, NW> &sm, int 
   const int ns = (int)(sl.n < a.S ? sl.n : a.S);
   const int nw = ns + (int)(sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
   const unsigned rsz = (unsigned)(a.R + a.C);
-  const unsigned first_slot = (unsigned)(sl.nq % rsz);
+  const unsigned first_slot = sl.nq < 0x80000000ll ? (unsigned)sl.nq % rsz : (unsigned)(sl.nq % rsz);
   const uint8_t *sinkk = (const uint8_t *)a.sink_k + (size_t)bg * a.sink_bytes;
   const uint8_t *sinkv = (const uint8_t *)a.sink_v + (size_t)bg * a.sink_bytes;
   const uint8_t *ringk = (const uint8_t *)a.ring_k + (size_t)bg * a.ring_bytes;
@@ -1063,10 +1063,12 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
     const int64_t ns = sl.n < a.S ? sl.n : a.S;
     const int64_t nw = ns + (sl.n - a.S - sl.nq > 0 ? sl.n - a.S - sl.nq : 0);
     const int64_t nws = (nw + 7) / 8;
-    ws0 = (int)(nws * part / a.P);
-    ws1 = (int)(nws * (part + 1) / a.P);
+    // (the whole layout runs only with P = kWholeWaves: a constant divisor there)
+    const int64_t P = NW == kWholeWaves ? (int64_t)kWholeWaves : (int64_t)a.P;
+    ws0 = (int)(nws * part / P);
+    ws1 = (int)(nws * (part + 1) / P);
     const int64_t items = nsets + nws;
-    if (NW == kWholeWaves && nsets >= a.P && items >= 3 * nws + a.P) {
+    if (NW == kWholeWaves && nsets >= P && items >= 3 * nws + P) {
       // Whole layout: every wave takes an equal share of all items, but the window
       // stages all go to waves 0-3, the first wave of each SIMD, which the SIMD's
       // instruction arbiter favours (those finish their share first, the SIMD's last
@@ -1076,25 +1078,39 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
       auto wb = [&](int p) { return nws * (p < 4 ? p : 4) / 4; };
       ws0 = (int)wb(part);
       ws1 = (int)wb(part + 1);
-      s0 = items * part / a.P - ws0;
-      s1 = items * (part + 1) / a.P - ws1;
-    } else if (nsets >= a.P) {
+      s0 = items * part / P - ws0;
+      s1 = items * (part + 1) / P - ws1;
+    } else if (nsets >= P) {
       // an equal share of all items (window stages and sets) per partition: its window
       // stages as above, sets for the rest (the two shares rounded apart left the
       // partitions 45-47 items long on the serving shape, now 46 each)
-      s0 = items * part / a.P - ws0;
-      s1 = items * (part + 1) / a.P - ws1;
+      s0 = items * part / P - ws0;
+      s1 = items * (part + 1) / P - ws1;
     } else {
-      s0 = nsets * part / a.P;
-      s1 = nsets * (part + 1) / a.P;
+      s0 = nsets * part / P;
+      s1 = nsets * (part + 1) / P;
     }
   }
   body_wave<G, BK, BV, NW, PAGED, APPEND>(a, sm, bg, s0, s1, ws0, ws1, O, bm, bl, bz, wm, wl, wacc);
-  __syncthreads();  // every wave is done with its ring, which u.o and u.wo alias
+  // A wave's partial (PV rows, then window values) goes to its own ring slots when they
+  // hold it (the whole layout: no wave reads another's slots and the wave's own loads
+  // have all landed), so a wave writes it as soon as it is done; otherwise to u.o / u.wo,
+  // which alias every wave's ring, after all waves are done.
+  constexpr bool kOwnSlots = NW == kWholeWaves && kStages * Stage<BK, BV>::SIZE >= 3 * G * kD * 4;
+  auto part_o = [&](int ww) -> float * {
+    if constexpr (kOwnSlots) return (float *)&sm.u.ring[ww][0][0];
+    else return &sm.u.o[ww][0][0];
+  };
+  auto part_w = [&](int ww) -> float * {
+    if constexpr (kOwnSlots) return (float *)&sm.u.ring[ww][0][0] + 2 * G * kD;
+    else return &sm.u.wo[ww][0][0];
+  };
+  if constexpr (!kOwnSlots) __syncthreads();  // every wave is done with its ring
+  float *po = part_o(w), *pw = part_w(w);
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    sm.u.wo[w][h][2 * lane] = wacc[h][0];
-    sm.u.wo[w][h][2 * lane + 1] = wacc[h][1];
+    pw[h * kD + 2 * lane] = wacc[h][0];
+    pw[h * kD + 2 * lane + 1] = wacc[h][1];
     if (lane == 0) { sm.wmx[w][h] = wm[h]; sm.wls[w][h] = wl[h]; }
   }
   {
@@ -1112,7 +1128,7 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
 #pragma unroll
       for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.u.o[w][4 * q4 + i][16 * ct + col] = O[ct][i];
+        for (int i = 0; i < 4; ++i) po[(4 * q4 + i) * kD + 16 * ct + col] = O[ct][i];
     }
   }
   __syncthreads();
@@ -1140,8 +1156,9 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
       const float fw = sm.wls[ww][hh] > 0.f ? __builtin_amdgcn_exp2f(sm.wmx[ww][hh] - mstar) : 0.f;
       den = fmaf(fb, sm.l[ww][hh], den);
       den = fmaf(fw, sm.wls[ww][hh], den);
-      num = fmaf(fb, sm.z[ww][hh] + (sm.u.o[ww][hh][j] + sm.u.o[ww][G + hh][j]), num);
-      num = fmaf(fw, sm.u.wo[ww][hh][j], num);
+      const float *o = part_o(ww);
+      num = fmaf(fb, sm.z[ww][hh] + (o[hh * kD + j] + o[(G + hh) * kD + j]), num);
+      num = fmaf(fw, part_w(ww)[hh * kD + j], num);
     }
     if (direct) {
       a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / den;
