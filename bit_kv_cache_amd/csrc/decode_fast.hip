@@ -91,7 +91,10 @@ template <int G, int BK, int BV, int NW>
 struct __align__(16) FastSmem {
   unsigned qi[G][kD];             // q~ in fixed point, offset to unsigned (balanced digits)
   float q[G][kD];
-  unsigned wb[NW][G][kWbPitch];   // body set: W as fp16 (hi | lo << 16) [head][token]
+  union {
+    unsigned wb[NW][G][kWbPitch];   // body set: W as fp16 (hi | lo << 16) [head][token]
+    float qT[kD][G];              // query setup: q transposed (a channel's G heads in one read)
+  };
   unsigned wzero[kSet];           // zeros: the PV A rows past 2 G read these
   int qe[16];                     // per head: q~ = (qi - kDigitBias) 2^(e - 21)
   float wp[NW][G][8];             // window stage: probabilities [head][token]
@@ -370,7 +373,9 @@ __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BK, BV, NW> &sm, 
     const int hh = i / kD, j = i % kD;
     const size_t off = ((size_t)b * a.Hq + h0 + hh) * kD + j;
     if (!fused) sm.qi[hh][j] = __float_as_uint(a.qt[off]);
-    sm.q[hh][j] = load_in(a.q, a.q_dtype, off);
+    const float qv = load_in(a.q, a.q_dtype, off);
+    sm.q[hh][j] = qv;
+    sm.qT[j][hh] = qv;
   }
   __syncthreads();
   if (fused) {
@@ -385,9 +390,13 @@ __device__ void setup_queries(const DecodeArgs &a, FastSmem<G, BK, BV, NW> &sm, 
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) s[hh] = 0.f;
 #pragma unroll 2
-      for (int m = 0; m < kD / 4; ++m)
+      for (int m = 0; m < kD / 4; ++m) {
+        float qv[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(mv[m], sm.q[hh][4 * m + k], s[hh]);
+        for (int c = 0; c < G; c += 4) *(f32x4 *)&qv[c] = *(const f32x4 *)&sm.qT[4 * m + k][c];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s[hh] = fmaf(mv[m], qv[hh], s[hh]);
+      }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         // (s0 + s1) + (s2 + s3) in lane k = 0 of the row's quad
