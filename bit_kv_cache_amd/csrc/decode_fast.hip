@@ -98,7 +98,8 @@ struct __align__(16) FastSmem {
   unsigned wzero[kSet];           // zeros: the PV A rows past 2 G read these
   int qe[16];                     // per head: q~ = (qi - kDigitBias) 2^(e - 21)
   float wp[NW][G][8];             // window stage: probabilities [head][token]
-  float wmx[NW][16], wls[NW][16]; // window partial: max and sum per head
+  alignas(16) float wmx[16][NW];  // window partial: max and sum [head][wave]
+  alignas(16) float wls[16][NW];
   union {
     uint8_t ring[NW][kStages][Stage<BK, BV>::SIZE];
     struct {
@@ -107,7 +108,9 @@ struct __align__(16) FastSmem {
     };
   } u;
   float sq[16];                   // per head: sum of q~ (the zero-point term)
-  float m[NW][16], l[NW][16], z[NW][16];
+  alignas(16) float m[16][NW];    // body partial: max, sum, zero term [head][wave]
+  alignas(16) float l[16][NW];
+  alignas(16) float z[16][NW];
   unsigned aqw[G / 2][4][64];     // q~ digit operands [operand][register][lane], shared by the waves
 };
 
@@ -1120,7 +1123,7 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
   for (int h = 0; h < G; ++h) {
     pw[h * kD + 2 * lane] = wacc[h][0];
     pw[h * kD + 2 * lane + 1] = wacc[h][1];
-    if (lane == 0) { sm.wmx[w][h] = wm[h]; sm.wls[w][h] = wl[h]; }
+    if (lane == 0) { sm.wmx[h][w] = wm[h]; sm.wls[h][w] = wl[h]; }
   }
   {
     // rows of O are heads; lane 16 hh + t of head quad qd carries head 4 qd + hh's totals
@@ -1128,9 +1131,9 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
     if (col == 0) {
 #pragma unroll
       for (int qd = 0; qd < G / 4; ++qd) {
-        sm.m[w][4 * qd + q4] = bm[qd];
-        sm.l[w][4 * qd + q4] = bl[qd];
-        sm.z[w][4 * qd + q4] = bz[qd];
+        sm.m[4 * qd + q4][w] = bm[qd];
+        sm.l[4 * qd + q4][w] = bl[qd];
+        sm.z[4 * qd + q4][w] = bz[qd];
       }
     }
     if (4 * q4 < 2 * G) {
@@ -1143,37 +1146,55 @@ __global__ void __launch_bounds__(64 * NW) decode_fast_kernel(DecodeArgs a, int 
   __syncthreads();
 
   // ---- merge the workgroup's waves: its partial, or the output when it is the only
-  // workgroup of its KV head.  Each thread takes one (head, channel) output and forms its
-  // head's merge itself (a head's 128 channels are two whole waves): the max over the
-  // waves' non-empty body and window partials, each partial's factor 2^(m - max) (0 when
-  // empty), the denominator and the weighted sum of the partials.
+  // workgroup of its KV head.  Each thread takes four adjacent channels of one head and
+  // forms its head's merge itself: the max over the waves' non-empty body and window
+  // partials, each partial's factor 2^(m - max) (0 when empty), the denominator and the
+  // weighted sums of the partials (per channel in the same order as one channel a thread).
   const int P1 = a.P + 1;
   const bool direct = nwg_body == 1;
-  for (int i = tid; i < G * kD; i += NT) {
-    const int hh = i / kD, j = i % kD;
+  for (int i = tid; i < G * kD / 4; i += NT) {
+    const int hh = i / (kD / 4), j = 4 * (i % (kD / 4));
+    float mv[NW], lv[NW], zv[NW], wmv[NW], wlv[NW];
+#pragma unroll
+    for (int c = 0; c < NW; c += 4) {
+      *(f32x4 *)&mv[c] = *(const f32x4 *)&sm.m[hh][c];
+      *(f32x4 *)&lv[c] = *(const f32x4 *)&sm.l[hh][c];
+      *(f32x4 *)&zv[c] = *(const f32x4 *)&sm.z[hh][c];
+      *(f32x4 *)&wmv[c] = *(const f32x4 *)&sm.wmx[hh][c];
+      *(f32x4 *)&wlv[c] = *(const f32x4 *)&sm.wls[hh][c];
+    }
     float mstar = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
-      if (sm.l[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.m[ww][hh]);
-      if (sm.wls[ww][hh] > 0.f) mstar = fmaxf(mstar, sm.wmx[ww][hh]);
+      if (lv[ww] > 0.f) mstar = fmaxf(mstar, mv[ww]);
+      if (wlv[ww] > 0.f) mstar = fmaxf(mstar, wmv[ww]);
     }
-    float den = 0.f, num = 0.f;
+    float den = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       // an empty partial has factor 0 and finite (zero) sums
-      const float fb = sm.l[ww][hh] > 0.f ? __builtin_amdgcn_exp2f(sm.m[ww][hh] - mstar) : 0.f;
-      const float fw = sm.wls[ww][hh] > 0.f ? __builtin_amdgcn_exp2f(sm.wmx[ww][hh] - mstar) : 0.f;
-      den = fmaf(fb, sm.l[ww][hh], den);
-      den = fmaf(fw, sm.wls[ww][hh], den);
+      const float fb = lv[ww] > 0.f ? __builtin_amdgcn_exp2f(mv[ww] - mstar) : 0.f;
+      const float fw = wlv[ww] > 0.f ? __builtin_amdgcn_exp2f(wmv[ww] - mstar) : 0.f;
+      den = fmaf(fb, lv[ww], den);
+      den = fmaf(fw, wlv[ww], den);
       const float *o = part_o(ww);
-      num = fmaf(fb, sm.z[ww][hh] + (o[hh * kD + j] + o[(G + hh) * kD + j]), num);
-      num = fmaf(fw, part_w(ww)[hh * kD + j], num);
+      const f32x4 oh = *(const f32x4 *)&o[hh * kD + j], ol = *(const f32x4 *)&o[(G + hh) * kD + j];
+      const f32x4 wv = *(const f32x4 *)&part_w(ww)[hh * kD + j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        num[e] = fmaf(fb, zv[ww] + (oh[e] + ol[e]), num[e]);
+        num[e] = fmaf(fw, wv[e], num[e]);
+      }
     }
     if (direct) {
-      a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = num / den;
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = num[e] / den;
+      *(f32x4 *)&a.out[((size_t)b * a.Hq + h0 + hh) * kD + j] = r;
     } else {
       const size_t row = ((size_t)b * a.Hq + h0 + hh) * P1 + blockIdx.x;
-      a.part_o[row * kD + j] = num;
+      *(f32x4 *)&a.part_o[row * kD + j] = num;
       if (j == 0) {
         a.part_ml[row * 2] = mstar;
         a.part_ml[row * 2 + 1] = den;
